@@ -1,0 +1,259 @@
+/* slide.h — C ABI of the layer-sliding offloaded fine-tuning hot path for AMD MI355X (gfx950).
+ *
+ * The method (SlideFormer: "An Efficient Heterogeneous Co-Design for Fine-Tuning on a Single
+ * GPU", Yang & Wen; abstract and the gist.science technical summary, section 2) treats the GPU
+ * as a sliding window over the decoder layers: a layer's weights are streamed into a fixed queue
+ * of pre-allocated GPU buffers, its forward and backward run there, its gradients go back to host
+ * memory asynchronously, and a CPU optimizer updates the layer while the GPU runs the backward of
+ * the layer below (summary, sections 2A and 2B; figure 3 and figure 4 of the paper page, whose
+ * caption states the overlap condition T_bwd >= T_grad_d2h + T_update).
+ *
+ * Conventions shared by every call
+ *  - Return value: SLIDE_OK (0) or a negative SLIDE_E_* code. slide_last_error() returns a
+ *    thread-local message describing the last failure on the calling thread. No C++ exception
+ *    crosses this boundary.
+ *  - Ownership: every device buffer, workspace and pinned host buffer is allocated and owned by
+ *    the caller. The library never allocates device memory. It owns only host bookkeeping and
+ *    the HIP events inside a ring handle and the profiler.
+ *  - Streams and events are passed as `void*` holding a hipStream_t / hipEvent_t (NULL = the
+ *    default stream). GPU calls are asynchronous on the given stream; launch failures return
+ *    SLIDE_E_HIP. Arguments and shapes are validated on the host before anything is launched.
+ *  - Element types: SLIDE_BF16 tensors are uint16 bf16 bit patterns; SLIDE_F32 tensors are
+ *    float. Accumulation, softmax, log-sum-exp and norm statistics are always fp32.
+ *  - Layouts are row-major. A weight matrix W is [out, in] and a projection is y = x W^T.
+ *    Activations are [N, features] with N = B*S tokens, token t = b*S + s at position s.
+ *  - Device pointers must be 16-byte aligned; feature sizes must be multiples of 8.
+ *  - No aliasing between inputs and outputs unless a call says otherwise.
+ */
+#ifndef SLIDE_H
+#define SLIDE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SLIDE_OK = 0,
+  SLIDE_E_ARG = -1,          /* null pointer, bad enum or hyper-parameter */
+  SLIDE_E_SHAPE = -2,        /* unsupported or inconsistent sizes */
+  SLIDE_E_WORKSPACE = -3,    /* workspace too small (see the *_workspace_bytes query) */
+  SLIDE_E_HIP = -4,          /* a HIP runtime call or a kernel launch failed */
+  SLIDE_E_STATE = -5,        /* slot-ring call not allowed in the slot's current state */
+  SLIDE_E_TIMEOUT = -6,      /* a bounded host wait ran out */
+  SLIDE_E_UNSUPPORTED = -7,  /* valid request this build does not implement */
+  SLIDE_E_NONFINITE = -8     /* reserved: non-finite value detected where checked */
+};
+
+typedef enum { SLIDE_F32 = 0, SLIDE_BF16 = 1 } slide_dtype;
+
+const char* slide_last_error(void);
+const char* slide_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Decoder layer (pre-norm Llama block; the pages name Llama-3, Qwen and Mistral as the models
+ * the system fine-tunes, summary section 4, and RoPE / RMSNorm / SwiGLU as its kernels,
+ * summary section 2C):
+ *   r  = RMSNorm(x; w_attn)               r_t = w * x_t / sqrt(mean(x_t^2) + eps)
+ *   q,k,v = split(r Wqkv^T)               rows of Wqkv: n_heads*d q rows, then k, then v
+ *   q,k = RoPE(q,k)                       rotate-half pairs (i, i+d/2), angle s*theta^(-2i/d)
+ *   o  = softmax(q k^T / sqrt(d) + causal) v   query head h reads kv head h/(n_heads/n_kv_heads)
+ *   x2 = x + o Wo^T
+ *   r2 = RMSNorm(x2; w_mlp)
+ *   g,u = split(r2 Wgu^T)                 rows of Wgu: ffn gate rows, then ffn up rows
+ *   y  = x2 + (silu(g) * u) Wd^T
+ * Slot packing (one contiguous buffer per layer, elements of cfg.dtype, in this order):
+ *   w_attn[H] | Wqkv[(nq+2nkv)d, H] | Wo[H, nq d] | w_mlp[H] | Wgu[2F, H] | Wd[H, F]
+ * The gradient buffer of a layer uses the same packing.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t hidden;      /* H, multiple of 8 */
+  int32_t n_heads;     /* nq */
+  int32_t n_kv_heads;  /* nkv, divides nq */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t ffn;         /* F, multiple of 8 */
+  int32_t dtype;       /* slide_dtype of weights, activations and gradients */
+  float rms_eps;
+  float rope_theta;
+} slide_layer_cfg;
+
+/* Number of elements in one layer's packed parameters (0 if cfg is invalid). */
+size_t slide_layer_param_count(const slide_layer_cfg* cfg);
+/* Element offsets of the six packed tensors, in packing order. */
+int slide_layer_param_offsets(const slide_layer_cfg* cfg, size_t off[6]);
+/* Workspace bytes needed by slide_layer_fwd (bwd = 0) or slide_layer_bwd (bwd = 1). */
+size_t slide_layer_workspace_bytes(const slide_layer_cfg* cfg, int B, int S, int bwd);
+
+/* Forward of one layer. w_slot: packed weights (device). x, y: [B*S, H] (device), y != x.
+ * ws: device workspace of at least slide_layer_workspace_bytes(cfg, B, S, 0) bytes. */
+int slide_layer_fwd(const slide_layer_cfg* cfg, const void* w_slot, const void* x, void* y,
+                    int B, int S, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one layer from its input checkpoint x: the layer's forward is recomputed inside
+ * the workspace (only layer inputs are kept between the sweeps), then dx = dL/dx and the packed
+ * parameter gradients g_slot = dL/dw are written (g_slot is overwritten, not accumulated).
+ * dy may alias dx (dy is fully read before dx is written). ws: at least
+ * slide_layer_workspace_bytes(cfg, B, S, 1) bytes. */
+int slide_layer_bwd(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
+                    const void* dy, void* dx, void* g_slot, int B, int S, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Fused LM-head cross-entropy in vocabulary chunks (summary, section 2C: projection and loss
+ * fused so that the [N, V] logit tensor never exists).
+ *   z = h W^T (chunk by chunk), loss = mean over valid t of (logsumexp(z_t) - z_t[y_t]),
+ *   dz = (softmax(z) - onehot(y)) / N_valid, dh = dz W, dW = dz^T h.
+ * Targets < 0 are ignored; with no valid target the loss and both gradients are 0.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t hidden;  /* H, multiple of 8 */
+  int32_t vocab;   /* V, multiple of 8 */
+  int32_t chunk;   /* vocabulary chunk C (multiple of 8); 0 selects 8192 */
+  int32_t dtype;   /* slide_dtype of h, W, dh, dW */
+} slide_ce_cfg;
+
+size_t slide_lmhead_ce_workspace_bytes(const slide_ce_cfg* cfg, int N);
+/* h [N, H], w [V, H], targets int32 [N] (device). loss_dev: one float on the device.
+ * dh [N, H] and dw [V, H] may each be NULL to skip that gradient. */
+int slide_lmhead_ce(const slide_ce_cfg* cfg, const void* h, const void* w,
+                    const int32_t* targets, int N, float* loss_dev, void* dh, void* dw,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Model glue around the layers: token embedding and the final RMSNorm.
+ * ------------------------------------------------------------------------------------------ */
+/* x[t] = E[tokens[t]]; E [V, H], x [N, H]. Tokens outside [0, V) -> SLIDE_E_ARG is not
+ * detectable on the host; such rows are written as zeros. */
+int slide_embed_fwd(const void* E, const int32_t* tokens, void* x, int N, int H, int V,
+                    int dtype, void* stream);
+size_t slide_embed_bwd_workspace_bytes(int N, int V);
+/* dE = sum over positions of dx rows, grouped by token, summed in position order (so the
+ * result is deterministic). dE [V, H] is fully overwritten (rows of absent tokens are 0). */
+int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,
+                    int dtype, void* ws, size_t ws_bytes, void* stream);
+/* y = RMSNorm(x; w). x, y [N, H]; rstd_out: optional fp32 [N] (may be NULL). */
+int slide_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out, int N, int H,
+                      float eps, int dtype, void* stream);
+size_t slide_rmsnorm_bwd_workspace_bytes(int N, int H);
+/* dx = dres + dRMSNorm/dx (dres may be NULL), dw = sum over rows. dw is written, not added. */
+int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, void* dx,
+                      void* dw, int N, int H, float eps, int dtype, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel-level entry points (the building blocks of the layer; used by tests and benches).
+ * ------------------------------------------------------------------------------------------ */
+/* C[M,N] = alpha * sum_k A(m,k) B(k,n)  (+ R[M,N] if R != NULL) (+ C if accumulate).
+ * a_kmajor = 1: A(m,k) = A[m*lda + k] else A[k*lda + m]
+ * b_kmajor = 1: B(k,n) = B[n*ldb + k] else B[k*ldb + n]
+ * A, B, R in dtype; C in c_dtype (accumulate requires c_dtype = SLIDE_F32). */
+int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
+               int ldb, int b_kmajor, void* C, int ldc, int c_dtype, const void* R, int ldr,
+               float alpha, int accumulate, int dtype, void* stream);
+/* Causal GQA attention on a packed qkv buffer [B*S, (nq+2nkv)*d] (RoPE already applied).
+ * o [B*S, nq*d]; lse fp32 [B, nq, S]. */
+int slide_attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv,
+                        int d, int dtype, void* stream);
+size_t slide_attention_bwd_workspace_bytes(int B, int S, int nq);
+/* dqkv [B*S, (nq+2nkv)*d] fully written (dq, dk, dv before the inverse RoPE). */
+int slide_attention_bwd(const void* qkv, const void* o, const float* lse, const void* d_o,
+                        void* dqkv, int B, int S, int nq, int nkv, int d, int dtype, void* ws,
+                        size_t ws_bytes, void* stream);
+/* In-place RoPE on the q and k parts of a packed qkv buffer; inverse = 1 rotates by -angle. */
+int slide_rope(void* qkv, int B, int S, int nq, int nkv, int d, float theta, int inverse,
+               int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Slot ring: the pre-allocated GPU cache queue (summary, section 2B: a fixed queue of
+ * identical buffers holding only the active layers' parameters and gradients, reused as soon
+ * as they are free). Slot k occupies [dev_base + k*(w_bytes+g_bytes), +w_bytes) for weights
+ * and the following g_bytes for gradients.
+ * Slot states: FREE -> LOADING (load) -> IN_USE (acquire) -> FLUSHING (flush) -> FREE (release)
+ *              IN_USE -> FREE (release without a flush, e.g. after a forward).
+ * Every transition is stream-ordered: a release records an event on the compute stream and
+ * the next load into that slot makes the copy stream wait for it (and for a pending flush), so
+ * no call here blocks the host except slide_slot_ring_wait_flush.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct slide_ring slide_ring;
+enum { SLIDE_SLOT_FREE = 0, SLIDE_SLOT_LOADING = 1, SLIDE_SLOT_IN_USE = 2,
+       SLIDE_SLOT_FLUSHING = 3 };
+/* engine: SLIDE_ENGINE_HIP moves data with hipMemcpyAsync on the h2d / d2h streams;
+ * SLIDE_ENGINE_HOST treats dev_base as host memory and copies with memcpy on a host thread
+ * (events become host flags), which lets the state machine run and be tested without a GPU. */
+enum { SLIDE_ENGINE_HIP = 0, SLIDE_ENGINE_HOST = 1 };
+int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_bytes, size_t g_bytes,
+                           void* dev_base, void* h2d_stream, void* d2h_stream, int engine);
+/* Pick the next FREE slot (round-robin), start the copy host_w -> slot weights, mark LOADING.
+ * SLIDE_E_STATE if no slot is FREE. */
+int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot_out);
+/* Make `compute_stream` wait for the slot's load; LOADING -> IN_USE. Also returns the slot's
+ * weight and gradient device addresses (either out pointer may be NULL). */
+int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_stream, void** w_dev,
+                            void** g_dev);
+/* After the work on compute_stream that writes the slot's gradients: copy them to host_g on
+ * the d2h stream; IN_USE -> FLUSHING. *ticket identifies this flush for wait_flush. */
+int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
+                          uint64_t* ticket);
+/* Block until the flush named by ticket has landed in host memory; SLIDE_E_TIMEOUT after
+ * timeout_ms milliseconds (a negative value waits without a limit). */
+int slide_slot_ring_wait_flush(slide_ring* r, uint64_t ticket, int timeout_ms);
+/* Return the slot to FREE once the work queued so far on compute_stream is done with it
+ * (stream-ordered; from IN_USE or FLUSHING). */
+int slide_slot_ring_release(slide_ring* r, int slot, void* compute_stream);
+/* Re-claim a FREE slot whose weights still hold `layer` (nothing was loaded over them since its
+ * release) without copying; FREE -> LOADING. SLIDE_E_STATE if no such slot. Used at the turn
+ * from the forward to the backward sweep, where the last layers are still resident. The caller
+ * must know that the host copy of those weights has not changed since they were loaded. */
+int slide_slot_ring_reuse(slide_ring* r, int layer, int* slot_out);
+int slide_slot_ring_state(slide_ring* r, int slot, int* state, int* layer);
+/* Find the slot currently holding `layer` (LOADING / IN_USE / FLUSHING), or -1. */
+int slide_slot_ring_find(slide_ring* r, int layer, int* slot_out);
+int slide_slot_ring_destroy(slide_ring* r);
+/* Host engine only: make the next `count` copies fail (fail_mode 1) or never complete
+ * (fail_mode 2). Returns SLIDE_E_UNSUPPORTED for the HIP engine. */
+int slide_slot_ring_inject_fault(slide_ring* r, int fail_mode, int count);
+
+/* ------------------------------------------------------------------------------------------
+ * CPU AdamW (the per-layer host optimizer, "Layer-Adam": summary, section 2B).
+ * Decoupled weight decay, bias correction, step t >= 1, fixed float32 operation order:
+ *   scalars (double, each cast once to float): b1t = beta1^t, b2t = beta2^t (t repeated
+ *   multiplications), c_dec = 1 - lr*wd, c_1b1 = 1 - beta1, c_1b2 = 1 - beta2,
+ *   c_step = lr / (1 - b1t), c_bc2 = sqrt(1 - b2t)
+ *   per element (float32, round to nearest-even, no fused multiply-add):
+ *   p1 = p*c_dec; m = beta1*m + c_1b1*g; v = beta2*v + c_1b2*(g*g);
+ *   den = sqrt(v)/c_bc2 + eps; p = p1 - c_step*(m/den); p_bf16 = bf16_rne(p)
+ * p, m, v: float [n] host memory, updated in place. g: [n] of g_dtype (SLIDE_BF16 or
+ * SLIDE_F32). p_bf16_out: optional uint16 [n]; it may alias g when g_dtype is SLIDE_BF16
+ * (the gradient landing buffer and the bf16 weight copy are one shared host buffer).
+ * n_threads <= 0 uses the available cores. Blocks until done.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+} slide_adamw_hp;
+int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
+                    uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
+                    int n_threads);
+
+/* The scalar (non-vector) code path of slide_cpu_adamw on one thread; same contract. Exposed so
+ * that tests can check both code paths give identical bits. */
+int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dtype, float* m, float* v,
+                                    uint16_t* p_bf16_out, size_t n, int64_t step,
+                                    const slide_adamw_hp* hp);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing: when enabled, every kernel the library launches is bracketed by HIP events
+ * on its own stream; slide_prof_read synchronizes them and returns, per kernel name, the
+ * launch count and total milliseconds since the last reset.
+ * ------------------------------------------------------------------------------------------ */
+int slide_prof_enable(int on);
+int slide_prof_reset(void);
+/* Writes up to max_entries records; *n_out = number written. name buffers are 64 bytes. */
+int slide_prof_read(char (*names)[64], int64_t* counts, double* total_ms, int max_entries,
+                    int* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLIDE_H */

@@ -1,0 +1,115 @@
+"""ctypes declarations of libslide's C ABI (include/slide.h). Argument marshalling only."""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libslide.so")
+
+SLIDE_OK = 0
+SLIDE_E_ARG, SLIDE_E_SHAPE, SLIDE_E_WORKSPACE, SLIDE_E_HIP = -1, -2, -3, -4
+SLIDE_E_STATE, SLIDE_E_TIMEOUT, SLIDE_E_UNSUPPORTED, SLIDE_E_NONFINITE = -5, -6, -7, -8
+SLIDE_F32, SLIDE_BF16 = 0, 1
+SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST = 0, 1
+SLOT_FREE, SLOT_LOADING, SLOT_IN_USE, SLOT_FLUSHING = 0, 1, 2, 3
+ERROR_NAMES = {0: "SLIDE_OK", -1: "SLIDE_E_ARG", -2: "SLIDE_E_SHAPE", -3: "SLIDE_E_WORKSPACE",
+               -4: "SLIDE_E_HIP", -5: "SLIDE_E_STATE", -6: "SLIDE_E_TIMEOUT",
+               -7: "SLIDE_E_UNSUPPORTED", -8: "SLIDE_E_NONFINITE"}
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class CeCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class AdamWHp(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+SZ = ctypes.c_size_t
+F = ctypes.c_float
+LCP = ctypes.POINTER(LayerCfg)
+CCP = ctypes.POINTER(CeCfg)
+
+SIGNATURES = {
+    "slide_last_error": (ctypes.c_char_p, []),
+    "slide_version": (ctypes.c_char_p, []),
+    "slide_layer_param_count": (SZ, [LCP]),
+    "slide_layer_param_offsets": (I, [LCP, ctypes.POINTER(SZ)]),
+    "slide_layer_workspace_bytes": (SZ, [LCP, I, I, I]),
+    "slide_layer_fwd": (I, [LCP, P, P, P, I, I, P, SZ, P]),
+    "slide_layer_bwd": (I, [LCP, P, P, P, P, P, I, I, P, SZ, P]),
+    "slide_lmhead_ce_workspace_bytes": (SZ, [CCP, I]),
+    "slide_lmhead_ce": (I, [CCP, P, P, P, I, P, P, P, P, SZ, P]),
+    "slide_embed_fwd": (I, [P, P, P, I, I, I, I, P]),
+    "slide_embed_bwd_workspace_bytes": (SZ, [I, I]),
+    "slide_embed_bwd": (I, [P, P, P, I, I, I, I, P, SZ, P]),
+    "slide_rmsnorm_fwd": (I, [P, P, P, P, I, I, F, I, P]),
+    "slide_rmsnorm_bwd_workspace_bytes": (SZ, [I, I]),
+    "slide_rmsnorm_bwd": (I, [P, P, P, P, P, P, I, I, F, I, P, SZ, P]),
+    "slide_gemm": (I, [I, I, I, P, I, I, P, I, I, P, I, I, P, I, F, I, I, P]),
+    "slide_attention_fwd": (I, [P, P, P, I, I, I, I, I, I, P]),
+    "slide_attention_bwd_workspace_bytes": (SZ, [I, I, I]),
+    "slide_attention_bwd": (I, [P, P, P, P, P, I, I, I, I, I, I, P, SZ, P]),
+    "slide_rope": (I, [P, I, I, I, I, I, F, I, I, P, SZ, P]),
+    "slide_slot_ring_create": (I, [ctypes.POINTER(P), I, SZ, SZ, P, P, P, I]),
+    "slide_slot_ring_load": (I, [P, I, P, ctypes.POINTER(I)]),
+    "slide_slot_ring_reuse": (I, [P, I, ctypes.POINTER(I)]),
+    "slide_slot_ring_acquire": (I, [P, I, P, ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "slide_slot_ring_flush": (I, [P, I, P, P, ctypes.POINTER(ctypes.c_uint64)]),
+    "slide_slot_ring_wait_flush": (I, [P, ctypes.c_uint64, I]),
+    "slide_slot_ring_release": (I, [P, I, P]),
+    "slide_slot_ring_state": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
+    "slide_slot_ring_find": (I, [P, I, ctypes.POINTER(I)]),
+    "slide_slot_ring_destroy": (I, [P]),
+    "slide_slot_ring_inject_fault": (I, [P, I, I]),
+    "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
+    "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,
+                                            ctypes.POINTER(AdamWHp)]),
+    "slide_prof_enable": (I, [I]),
+    "slide_prof_reset": (I, []),
+    "slide_prof_read": (I, [P, P, P, I, ctypes.POINTER(I)]),
+}
+
+_lib = None
+
+
+class SlideError(RuntimeError):
+    def __init__(self, code, func, message):
+        super().__init__(f"{func} -> {ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.func = func
+
+
+def lib():
+    """Load libslide.so (built in-tree). There is no fallback: without the library the
+    product path cannot run."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m layer_sliding_offloaded_fwd_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def call(name, *args):
+    """Call an int-returning entry point; raise SlideError on a non-zero status."""
+    L = lib()
+    rc = getattr(L, name)(*args)
+    if rc != SLIDE_OK:
+        raise SlideError(rc, name, L.slide_last_error().decode(errors="replace"))
+    return rc

@@ -1,0 +1,239 @@
+"""Thin Python binding of libslide with the C ABI's names (include/slide.h).
+
+Argument marshalling only: tensors are passed by address (torch tensors, or plain integers
+holding an address), streams as torch streams or raw hipStream_t integers. Every computation
+runs in libslide's kernels; a non-zero status raises SlideError carrying slide_last_error().
+"""
+import ctypes
+
+from ._capi import (AdamWHp, CeCfg, LayerCfg, SlideError, call, lib, SLIDE_BF16, SLIDE_F32,
+                    SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST)
+
+__all__ = [
+    "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F32", "SLIDE_ENGINE_HIP",
+    "SLIDE_ENGINE_HOST", "slide_layer_param_count", "slide_layer_param_offsets",
+    "slide_layer_workspace_bytes", "slide_layer_fwd", "slide_layer_bwd",
+    "slide_lmhead_ce_workspace_bytes", "slide_lmhead_ce", "slide_embed_fwd",
+    "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
+    "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
+    "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
+    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_prof_enable", "slide_prof_reset",
+    "slide_prof_read", "dtype_code", "layer_cfg",
+]
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    if hasattr(t, "data_ptr"):
+        return ctypes.c_void_p(t.data_ptr())
+    if hasattr(t, "ctypes"):           # numpy array
+        return ctypes.c_void_p(t.ctypes.data)
+    raise TypeError(f"cannot pass {type(t)} as a pointer")
+
+
+def _s(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dtype_code(dt):
+    """'bf16' / 'f32' / torch dtype -> SLIDE_BF16 / SLIDE_F32."""
+    s = str(dt)
+    if "bf16" in s or "bfloat16" in s:
+        return SLIDE_BF16
+    if "f32" in s or "float32" in s:
+        return SLIDE_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def layer_cfg(hidden, n_heads, n_kv_heads, head_dim, ffn, dtype, rms_eps=1e-5,
+              rope_theta=10000.0):
+    return LayerCfg(hidden, n_heads, n_kv_heads, head_dim, ffn, dtype_code(dtype), rms_eps,
+                    rope_theta)
+
+
+# ------------------------------------------------------------------------------ layer
+def slide_layer_param_count(cfg):
+    return int(lib().slide_layer_param_count(ctypes.byref(cfg)))
+
+
+def slide_layer_param_offsets(cfg):
+    off = (ctypes.c_size_t * 6)()
+    call("slide_layer_param_offsets", ctypes.byref(cfg), off)
+    return list(off)
+
+
+def slide_layer_workspace_bytes(cfg, B, S, bwd):
+    return int(lib().slide_layer_workspace_bytes(ctypes.byref(cfg), B, S, int(bwd)))
+
+
+def slide_layer_fwd(cfg, w_slot, x, y, B, S, ws, ws_bytes, stream=None):
+    call("slide_layer_fwd", ctypes.byref(cfg), _p(w_slot), _p(x), _p(y), B, S, _p(ws),
+         ws_bytes, _s(stream))
+
+
+def slide_layer_bwd(cfg, w_slot, x, dy, dx, g_slot, B, S, ws, ws_bytes, stream=None):
+    call("slide_layer_bwd", ctypes.byref(cfg), _p(w_slot), _p(x), _p(dy), _p(dx), _p(g_slot),
+         B, S, _p(ws), ws_bytes, _s(stream))
+
+
+# ------------------------------------------------------------------------------ LM head CE
+def slide_lmhead_ce_workspace_bytes(cfg, N):
+    return int(lib().slide_lmhead_ce_workspace_bytes(ctypes.byref(cfg), N))
+
+
+def slide_lmhead_ce(cfg, h, w, targets, N, loss_dev, dh, dw, ws, ws_bytes, stream=None):
+    call("slide_lmhead_ce", ctypes.byref(cfg), _p(h), _p(w), _p(targets), N, _p(loss_dev),
+         _p(dh), _p(dw), _p(ws), ws_bytes, _s(stream))
+
+
+# ------------------------------------------------------------------------------ glue
+def slide_embed_fwd(E, tokens, x, N, H, V, dtype, stream=None):
+    call("slide_embed_fwd", _p(E), _p(tokens), _p(x), N, H, V, dtype, _s(stream))
+
+
+def slide_embed_bwd_workspace_bytes(N, V):
+    return int(lib().slide_embed_bwd_workspace_bytes(N, V))
+
+
+def slide_embed_bwd(dx, tokens, dE, N, H, V, dtype, ws, ws_bytes, stream=None):
+    call("slide_embed_bwd", _p(dx), _p(tokens), _p(dE), N, H, V, dtype, _p(ws), ws_bytes,
+         _s(stream))
+
+
+def slide_rmsnorm_fwd(x, w, y, rstd, N, H, eps, dtype, stream=None):
+    call("slide_rmsnorm_fwd", _p(x), _p(w), _p(y), _p(rstd), N, H, ctypes.c_float(eps), dtype,
+         _s(stream))
+
+
+def slide_rmsnorm_bwd_workspace_bytes(N, H):
+    return int(lib().slide_rmsnorm_bwd_workspace_bytes(N, H))
+
+
+def slide_rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ws, ws_bytes, stream=None):
+    call("slide_rmsnorm_bwd", _p(dy), _p(x), _p(w), _p(dres), _p(dx), _p(dw), N, H,
+         ctypes.c_float(eps), dtype, _p(ws), ws_bytes, _s(stream))
+
+
+# ------------------------------------------------------------------------------ kernels
+def slide_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, c_dtype, R=None, ldr=0,
+               alpha=1.0, accumulate=False, dtype=SLIDE_BF16, stream=None):
+    call("slide_gemm", M, N, K, _p(A), lda, int(a_kmajor), _p(B), ldb, int(b_kmajor), _p(C), ldc,
+         c_dtype, _p(R), ldr, ctypes.c_float(alpha), int(accumulate), dtype, _s(stream))
+
+
+def slide_attention_fwd(qkv, o, lse, B, S, nq, nkv, d, dtype, stream=None):
+    call("slide_attention_fwd", _p(qkv), _p(o), _p(lse), B, S, nq, nkv, d, dtype, _s(stream))
+
+
+def slide_attention_bwd_workspace_bytes(B, S, nq):
+    return int(lib().slide_attention_bwd_workspace_bytes(B, S, nq))
+
+
+def slide_attention_bwd(qkv, o, lse, d_o, dqkv, B, S, nq, nkv, d, dtype, ws, ws_bytes,
+                        stream=None):
+    call("slide_attention_bwd", _p(qkv), _p(o), _p(lse), _p(d_o), _p(dqkv), B, S, nq, nkv, d,
+         dtype, _p(ws), ws_bytes, _s(stream))
+
+
+def slide_rope(qkv, B, S, nq, nkv, d, theta, inverse, dtype, ws, ws_bytes, stream=None):
+    call("slide_rope", _p(qkv), B, S, nq, nkv, d, ctypes.c_float(theta), int(inverse), dtype,
+         _p(ws), ws_bytes, _s(stream))
+
+
+# ------------------------------------------------------------------------------ slot ring
+class SlotRing:
+    """Handle around slide_slot_ring_*: the fixed queue of identical HBM slots."""
+
+    def __init__(self, n_slots, w_bytes, g_bytes, dev_base, h2d_stream=None, d2h_stream=None,
+                 engine=SLIDE_ENGINE_HIP):
+        self._h = ctypes.c_void_p()
+        call("slide_slot_ring_create", ctypes.byref(self._h), n_slots, w_bytes, g_bytes,
+             _p(dev_base), _s(h2d_stream), _s(d2h_stream), engine)
+
+    def load(self, layer, host_w):
+        s = ctypes.c_int()
+        call("slide_slot_ring_load", self._h, layer, _p(host_w), ctypes.byref(s))
+        return s.value
+
+    def reuse(self, layer):
+        s = ctypes.c_int()
+        call("slide_slot_ring_reuse", self._h, layer, ctypes.byref(s))
+        return s.value
+
+    def acquire(self, slot, compute_stream=None):
+        w = ctypes.c_void_p()
+        g = ctypes.c_void_p()
+        call("slide_slot_ring_acquire", self._h, slot, _s(compute_stream), ctypes.byref(w),
+             ctypes.byref(g))
+        return w.value, g.value
+
+    def flush(self, slot, host_g, compute_stream=None):
+        t = ctypes.c_uint64()
+        call("slide_slot_ring_flush", self._h, slot, _p(host_g), _s(compute_stream),
+             ctypes.byref(t))
+        return t.value
+
+    def wait_flush(self, ticket, timeout_ms=-1):
+        call("slide_slot_ring_wait_flush", self._h, ctypes.c_uint64(ticket), timeout_ms)
+
+    def release(self, slot, compute_stream=None):
+        call("slide_slot_ring_release", self._h, slot, _s(compute_stream))
+
+    def state(self, slot):
+        st = ctypes.c_int()
+        ly = ctypes.c_int()
+        call("slide_slot_ring_state", self._h, slot, ctypes.byref(st), ctypes.byref(ly))
+        return st.value, ly.value
+
+    def find(self, layer):
+        s = ctypes.c_int()
+        call("slide_slot_ring_find", self._h, layer, ctypes.byref(s))
+        return s.value
+
+    def inject_fault(self, mode, count):
+        call("slide_slot_ring_inject_fault", self._h, mode, count)
+
+    def close(self):
+        if self._h:
+            call("slide_slot_ring_destroy", self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------ AdamW
+def slide_cpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, n_threads=0):
+    """p, m, v: float32 host buffers; g: host bf16 (uint16) or float32; hp: AdamWHp."""
+    call("slide_cpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
+         ctypes.byref(hp), n_threads)
+
+
+# ------------------------------------------------------------------------------ profiler
+def slide_prof_enable(on=True):
+    call("slide_prof_enable", int(on))
+
+
+def slide_prof_reset():
+    call("slide_prof_reset")
+
+
+def slide_prof_read(max_entries=256):
+    """{kernel name: (launches, total_ms)} since the last reset (synchronizes the events)."""
+    names = (ctypes.c_char * 64 * max_entries)()
+    counts = (ctypes.c_int64 * max_entries)()
+    ms = (ctypes.c_double * max_entries)()
+    n = ctypes.c_int()
+    call("slide_prof_read", ctypes.cast(names, ctypes.c_void_p), counts, ms, max_entries,
+         ctypes.byref(n))
+    return {bytes(names[i]).split(b"\0")[0].decode(): (counts[i], ms[i]) for i in range(n.value)}

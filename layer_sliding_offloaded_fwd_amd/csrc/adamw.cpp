@@ -1,0 +1,207 @@
+// CPU AdamW: the per-layer host optimizer of the layer-sliding method ("Layer-Adam": optimizer
+// state kept in host memory and updated on the CPU layer by layer while the GPU runs the next
+// layer's backward; SlideFormer summary, sections 2A and 2B).
+//
+// Fixed float32 operation order, every operation rounded to nearest-even and no fused
+// multiply-add, so that the result is reproducible bit for bit on any x86-64 host:
+//   p1 = p*c_dec; m' = c_b1*m + c_1b1*g; v' = c_b2*v + c_1b2*(g*g);
+//   den = sqrt(v')/c_bc2 + c_eps; p' = p1 - c_step*(m'/den); bf16 copy = rne(p').
+// The AVX-512 path and the scalar path perform the same IEEE operations element by element.
+// This file must be compiled with -ffp-contract=off and without fast-math.
+#include <immintrin.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "../../include/slide.h"
+
+namespace slide {
+int fail(int code, const char* fmt, ...);
+}
+
+namespace {
+
+struct Consts {
+  float c_dec, c_b1, c_1b1, c_b2, c_1b2, c_step, c_bc2, c_eps;
+};
+
+Consts make_consts(const slide_adamw_hp& hp, int64_t t) {
+  double b1t = 1.0, b2t = 1.0;
+  for (int64_t i = 0; i < t; ++i) {
+    b1t *= hp.beta1;
+    b2t *= hp.beta2;
+  }
+  Consts c;
+  c.c_dec = (float)(1.0 - hp.lr * hp.weight_decay);
+  c.c_b1 = (float)hp.beta1;
+  c.c_1b1 = (float)(1.0 - hp.beta1);
+  c.c_b2 = (float)hp.beta2;
+  c.c_1b2 = (float)(1.0 - hp.beta2);
+  c.c_step = (float)(hp.lr / (1.0 - b1t));
+  c.c_bc2 = (float)sqrt(1.0 - b2t);
+  c.c_eps = (float)hp.eps;
+  return c;
+}
+
+inline float widen_bf16(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+inline uint16_t bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// One element; g is already widened to float.
+inline void step1(float& p, float g, float& m, float& v, uint16_t* out, const Consts& c) {
+  float p1 = p * c.c_dec;
+  float a = c.c_b1 * m;
+  float b = c.c_1b1 * g;
+  float m2 = a + b;
+  float gg = g * g;
+  float e = c.c_b2 * v;
+  float f = c.c_1b2 * gg;
+  float v2 = e + f;
+  float sq = sqrtf(v2);
+  float q = sq / c.c_bc2;
+  float den = q + c.c_eps;
+  float r = m2 / den;
+  float s = c.c_step * r;
+  float p2 = p1 - s;
+  p = p2;
+  m = m2;
+  v = v2;
+  if (out) *out = bf16_rne(p2);
+}
+
+void range_scalar(float* p, const void* g, int gdt, float* m, float* v, uint16_t* out,
+                  size_t lo, size_t hi, const Consts& c) {
+  for (size_t i = lo; i < hi; ++i) {
+    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
+    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
+  }
+}
+
+__attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const void* g, int gdt,
+                                                                float* m, float* v,
+                                                                uint16_t* out, size_t lo,
+                                                                size_t hi, const Consts& c) {
+  const __m512 c_dec = _mm512_set1_ps(c.c_dec), c_b1 = _mm512_set1_ps(c.c_b1),
+               c_1b1 = _mm512_set1_ps(c.c_1b1), c_b2 = _mm512_set1_ps(c.c_b2),
+               c_1b2 = _mm512_set1_ps(c.c_1b2), c_step = _mm512_set1_ps(c.c_step),
+               c_bc2 = _mm512_set1_ps(c.c_bc2), c_eps = _mm512_set1_ps(c.c_eps);
+  const __m512i exp_mask = _mm512_set1_epi32(0x7fffffff), inf_bits = _mm512_set1_epi32(0x7f800000),
+                bias = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1),
+                quiet = _mm512_set1_epi32(0x40);
+  size_t i = lo;
+  // scalar head up to 64-byte alignment of p
+  while (i < hi && (((uintptr_t)(p + i)) & 63u)) {
+    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
+    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
+    ++i;
+  }
+  for (; i + 16 <= hi; i += 16) {
+    __m512 gv;
+    if (gdt == SLIDE_BF16) {
+      __m256i gb = _mm256_loadu_si256((const __m256i*)((const uint16_t*)g + i));
+      gv = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(gb), 16));
+    } else {
+      gv = _mm512_loadu_ps((const float*)g + i);
+    }
+    __m512 pv = _mm512_load_ps(p + i);
+    __m512 mv = _mm512_loadu_ps(m + i);
+    __m512 vv = _mm512_loadu_ps(v + i);
+    __m512 p1 = _mm512_mul_ps(pv, c_dec);
+    __m512 m2 = _mm512_add_ps(_mm512_mul_ps(c_b1, mv), _mm512_mul_ps(c_1b1, gv));
+    __m512 v2 = _mm512_add_ps(_mm512_mul_ps(c_b2, vv), _mm512_mul_ps(c_1b2, _mm512_mul_ps(gv, gv)));
+    __m512 den = _mm512_add_ps(_mm512_div_ps(_mm512_sqrt_ps(v2), c_bc2), c_eps);
+    __m512 p2 = _mm512_sub_ps(p1, _mm512_mul_ps(c_step, _mm512_div_ps(m2, den)));
+    _mm512_store_ps(p + i, p2);
+    _mm512_storeu_ps(m + i, m2);
+    _mm512_storeu_ps(v + i, v2);
+    if (out) {
+      __m512i u = _mm512_castps_si512(p2);
+      __mmask16 isnan = _mm512_cmpgt_epu32_mask(_mm512_and_si512(u, exp_mask), inf_bits);
+      __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), one);
+      __m512i rnd = _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, bias), lsb), 16);
+      __m512i qn = _mm512_or_si512(_mm512_srli_epi32(u, 16), quiet);
+      __m512i res = _mm512_mask_mov_epi32(rnd, isnan, qn);
+      _mm256_storeu_si256((__m256i*)(out + i), _mm512_cvtepi32_epi16(res));
+    }
+  }
+  for (; i < hi; ++i) {
+    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
+    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
+  }
+}
+
+}  // namespace
+
+extern "C" int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
+                               uint16_t* p_bf16_out, size_t n, int64_t step,
+                               const slide_adamw_hp* hp, int n_threads) {
+  using slide::fail;
+  if (n == 0) return SLIDE_OK;
+  if (!p || !g || !m || !v || !hp) return fail(SLIDE_E_ARG, "slide_cpu_adamw: null pointer");
+  if (g_dtype != SLIDE_BF16 && g_dtype != SLIDE_F32)
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw: g_dtype must be SLIDE_BF16 or SLIDE_F32");
+  if (step < 1) return fail(SLIDE_E_ARG, "slide_cpu_adamw: step must be >= 1 (got %lld)",
+                            (long long)step);
+  if (!(hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && hp->eps > 0 &&
+        hp->lr >= 0 && hp->weight_decay >= 0))
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw: hyper-parameters out of range");
+  if (p_bf16_out && (void*)p_bf16_out != g) {
+    // overlapping but not identical buffers would read already-written values
+    const char* a = (const char*)p_bf16_out;
+    const char* b = (const char*)g;
+    size_t gb = n * (g_dtype == SLIDE_BF16 ? 2 : 4);
+    if (a < b + gb && b < a + n * 2)
+      return fail(SLIDE_E_ARG, "slide_cpu_adamw: p_bf16_out partially overlaps g");
+  }
+  if (p_bf16_out && (void*)p_bf16_out == g && g_dtype != SLIDE_BF16)
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw: p_bf16_out may alias g only for bf16 g");
+  const Consts c = make_consts(*hp, step);
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  size_t min_per = 1 << 16;
+  nt = (int)std::max<size_t>(1, std::min<size_t>((size_t)nt, (n + min_per - 1) / min_per));
+  const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+  auto work = [&](size_t lo, size_t hi) {
+    if (avx512)
+      range_avx512(p, g, g_dtype, m, v, p_bf16_out, lo, hi, c);
+    else
+      range_scalar(p, g, g_dtype, m, v, p_bf16_out, lo, hi, c);
+  };
+  if (nt == 1) {
+    work(0, n);
+    return SLIDE_OK;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  size_t per = (n + nt - 1) / nt;
+  per = (per + 15) / 16 * 16;
+  for (int t = 0; t < nt; ++t) {
+    size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
+    if (lo >= hi) break;
+    th.emplace_back(work, lo, hi);
+  }
+  for (auto& x : th) x.join();
+  return SLIDE_OK;
+}
+
+// Scalar-only entry used by tests to check that both code paths agree bit for bit.
+extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dtype, float* m,
+                                               float* v, uint16_t* out, size_t n, int64_t step,
+                                               const slide_adamw_hp* hp) {
+  if (!p || !g || !m || !v || !hp || step < 1) return SLIDE_E_ARG;
+  range_scalar(p, g, g_dtype, m, v, out, 0, n, make_consts(*hp, step));
+  return SLIDE_OK;
+}

@@ -1,0 +1,715 @@
+// Causal grouped-query attention, forward and backward, on the packed qkv buffer of a layer
+// (rows of (nq + 2 nkv) * d: q heads, then k heads, then v heads). Query head h reads kv head
+// h / (nq / nkv); scores are scaled by 1/sqrt(d); key j is visible to query i iff j <= i.
+// The pages leave attention itself unspecified (they optimise RoPE, RMSNorm and SwiGLU around
+// it: SlideFormer summary, section 2C); this is the standard definition for the Llama family.
+//
+// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, flash-style, no [S, S]
+// tensor in memory):
+//  * forward and dQ: 128 queries per workgroup (32 per wave), keys in blocks of 64. Each wave
+//    computes S^T = K Q^T so that a lane owns one query: row max / row sum are in-lane plus one
+//    exchange with the lane 32 away. O^T += V^T P^T (and dQ^T += K^T dS^T) take P (dS) straight
+//    from the score accumulators as the B operand: the 16 keys an MFMA consumes are ordered the
+//    way the accumulator holds them, and V (K) is staged transposed in LDS in that same order.
+//  * dK/dV: 128 keys per workgroup, looping over the G query heads of the kv group and over the
+//    query blocks on or after the diagonal, so dK and dV are summed without atomics (the result
+//    is deterministic). dQ runs as its own kernel.
+//  * D_i = rowsum(dO_i * O_i) is precomputed by a small kernel.
+// fp32 path (the small fp32 configuration): straightforward SIMT kernels, one thread per query
+// (forward, dQ) or per key (dK/dV).
+#include "attention.h"
+
+namespace slide {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int LDT = 68;  // row length (elements) of transposed tiles: 64 keys + 4 padding
+// LDS elements needed to stage four waves' 32 x D output tiles (rows padded to D + 8)
+template <int D> constexpr int stage_elems() { return 128 * (D + 8); }
+template <int D> constexpr int at_least_stage(int n) { return n > stage_elems<D>() ? n : stage_elems<D>(); }
+
+__device__ __forceinline__ bf16x8_t pack8(const float* v) {
+  uint4 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ bf16x8_t zero8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+
+// [64 rows][D] tile, 16-byte chunk c of row r stored at chunk c ^ (r & 7).
+template <int D>
+__device__ __forceinline__ void rows_to_lds(bf16_t* s, const bf16_t* g, int stride, int row0,
+                                            int nvalid) {
+  constexpr int KCH = D / 8;
+  for (int id = threadIdx.x; id < 64 * KCH; id += 256) {
+    const int r = id / KCH, c = id % KCH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nvalid) v = *(const uint4*)(g + (size_t)(row0 + r) * stride + c * 8);
+    *(uint4*)(s + r * D + ((c ^ (r & 7)) << 3)) = v;
+  }
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t rows_read(const bf16_t* s, int r, int c) {
+  return *(const bf16x8_t*)(s + r * D + ((c ^ (r & 7)) << 3));
+}
+
+__device__ __forceinline__ uint32_t dwsel(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Transposed tile [D][LDT]: element (d, r) = row r, column d of the 64-row source tile.
+template <int D>
+__device__ __forceinline__ void rows_to_lds_t(bf16_t* st, const bf16_t* g, int stride, int row0,
+                                              int nvalid) {
+  constexpr int DB = D / 8;  // 8-wide d blocks
+  const int t = threadIdx.x;
+  if (t >= 8 * DB) return;
+  const int kb = t / DB, db = t % DB;
+  uint4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = kb * 8 + j;
+    v[j] = r < nvalid ? *(const uint4*)(g + (size_t)(row0 + r) * stride + db * 8)
+                      : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t o0 = __builtin_amdgcn_perm(dwsel(v[1], i >> 1), dwsel(v[0], i >> 1), sel);
+    const uint32_t o1 = __builtin_amdgcn_perm(dwsel(v[3], i >> 1), dwsel(v[2], i >> 1), sel);
+    const uint32_t o2 = __builtin_amdgcn_perm(dwsel(v[5], i >> 1), dwsel(v[4], i >> 1), sel);
+    const uint32_t o3 = __builtin_amdgcn_perm(dwsel(v[7], i >> 1), dwsel(v[6], i >> 1), sel);
+    bf16_t* p = st + (db * 8 + i) * LDT + kb * 8;
+    *(uint2*)p = make_uint2(o0, o1);
+    *(uint2*)(p + 4) = make_uint2(o2, o3);
+  }
+}
+// A operand from a transposed tile for the key-ordered MFMA step ks: keys 16ks + 4hf + {0..3}
+// and 16ks + 8 + 4hf + {0..3} of row d.
+__device__ __forceinline__ bf16x8_t t_read(const bf16_t* st, int d, int ks, int hf) {
+  const bf16_t* p = st + d * LDT + ks * 16 + hf * 4;
+  const uint2 a = *(const uint2*)p, b = *(const uint2*)(p + 8);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// score accumulator element i of sub-block kb (32 keys) -> key offset within the 64-key block
+__device__ __forceinline__ int acc_key(int kb, int i, int hf) {
+  return kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+}
+
+// Stage a wave's 32 x D output tile (held transposed in accumulators) through LDS and write
+// 16-byte row chunks: out row r (0..31) of this wave goes to dst + row_index(r) * stride.
+template <int D>
+__device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc, float scale,
+                                             bf16_t* dst, int stride, int row0, int nvalid,
+                                             int lane) {
+  constexpr int LS = D + 8;
+  const int lr = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = db * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
+      stage[lr * LS + d] = f2bf(acc[db][e] * scale);
+    }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  for (int id = lane; id < 32 * (D / 8); id += 64) {
+    const int r = id / (D / 8), c = id % (D / 8);
+    if (r < nvalid) *(uint4*)(dst + (size_t)(row0 + r) * stride + c * 8) = *(const uint4*)(stage + r * LS + c * 8);
+  }
+}
+
+// ------------------------------------------------------------------ forward
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
+                                                       bf16_t* __restrict__ out,
+                                                       float* __restrict__ lse, int S, int nq,
+                                                       int nkv, float scale) {
+  constexpr int NKK = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(64 * D + D * LDT)];
+  bf16_t* sK = smem;
+  bf16_t* sVt = smem + 64 * D;
+
+  const int nqb = (S + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (nq / nkv);
+  const int QS = (nq + 2 * nkv) * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int wq0 = qb * 128 + wave * 32;
+  const int q = wq0 + lr;
+  const bf16_t* base = qkv + (size_t)b * S * QS;
+  const float sl2 = scale * kLog2e;
+
+  bf16x8_t qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = q < S ? *(const bf16x8_t*)(base + (size_t)q * QS + h * D + kk * 16 + hf * 8) : zero8();
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m2 = -INFINITY, l = 0.f;
+
+  const int q_last = min(S - 1, qb * 128 + 127);
+  const int nkvb = q_last / 64 + 1;
+  const bf16_t* kbase = base + (nq + g) * D;
+  const bf16_t* vbase = base + (nq + nkv + g) * D;
+  for (int jb = 0; jb < nkvb; ++jb) {
+    const int kv0 = jb * 64, nvalid = min(64, S - kv0);
+    __syncthreads();
+    rows_to_lds<D>(sK, kbase, QS, kv0, nvalid);
+    rows_to_lds_t<D>(sVt, vbase, QS, kv0, nvalid);
+    __syncthreads();
+    if (kv0 > wq0 + 31) continue;  // every key of this block is after every query of the wave
+
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + acc_key(kb, i, hf);
+        float s = sacc[kb][i] * sl2;
+        if (key > q || key >= S) s = -INFINITY;
+        sacc[kb][i] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m2, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m2 - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(sacc[kb][i] - m_use);
+        sacc[kb][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32, 64);
+    l = l * alpha + rs;
+    m2 = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
+      const bf16x8_t pf = pack8(pv);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sVt, db * 32 + lr, ks, hf), pf,
+                                                           oacc[db], 0, 0, 0);
+    }
+  }
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+  if (hf == 0 && q < S) lse[((size_t)b * nq + h) * S + q] = m2 * kLn2 + logf(l);
+  __syncthreads();
+  bf16_t* stage = smem + wave * 32 * (D + 8);
+  store_tile_t<D>(stage, oacc, inv_l, out + (size_t)b * S * nq * D + h * D, nq * D, wq0,
+                  min(32, S - wq0), lane);
+}
+
+// ------------------------------------------------------------------ D = rowsum(dO * O)
+template <typename T>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
+                                                         const T* __restrict__ dout,
+                                                         float* __restrict__ delta, int B, int S,
+                                                         int nq, int D) {
+  // one 64-lane wave per (token, head) row
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= (size_t)B * S * nq) return;
+  const size_t t = row / nq;
+  const int h = (int)(row % nq);
+  const T* a = o + t * nq * D + (size_t)h * D;
+  const T* c = dout + t * nq * D + (size_t)h * D;
+  float s = 0.f;
+  for (int i = lane; i < D; i += 64) s += Elem<T>::load(a + i) * Elem<T>::load(c + i);
+  s = warp_sum(s);
+  if (lane == 0) {
+    const int b = (int)(t / S), sp = (int)(t % S);
+    delta[((size_t)b * nq + h) * S + sp] = s;
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+                                                      const bf16_t* __restrict__ dout,
+                                                      const float* __restrict__ lse,
+                                                      const float* __restrict__ delta,
+                                                      bf16_t* __restrict__ dqkv, int S, int nq,
+                                                      int nkv, float scale) {
+  constexpr int NKK = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(2 * 64 * D + D * LDT)];
+  bf16_t* sK = smem;
+  bf16_t* sV = smem + 64 * D;
+  bf16_t* sKt = smem + 2 * 64 * D;
+
+  const int nqb = (S + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (nq / nkv);
+  const int QS = (nq + 2 * nkv) * D, OS = nq * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int wq0 = qb * 128 + wave * 32;
+  const int q = wq0 + lr;
+  const bf16_t* base = qkv + (size_t)b * S * QS;
+  const bf16_t* dobase = dout + (size_t)b * S * OS;
+  const float sl2 = scale * kLog2e;
+
+  bf16x8_t qf[NKK], df[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qf[kk] = q < S ? *(const bf16x8_t*)(base + (size_t)q * QS + h * D + kk * 16 + hf * 8) : zero8();
+    df[kk] = q < S ? *(const bf16x8_t*)(dobase + (size_t)q * OS + h * D + kk * 16 + hf * 8) : zero8();
+  }
+  const float lse2 = q < S ? lse[((size_t)b * nq + h) * S + q] * kLog2e : 0.f;
+  const float dl = q < S ? delta[((size_t)b * nq + h) * S + q] : 0.f;
+
+  f32x16_t dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+
+  const int q_last = min(S - 1, qb * 128 + 127);
+  const int nkvb = q_last / 64 + 1;
+  const bf16_t* kbase = base + (nq + g) * D;
+  const bf16_t* vbase = base + (nq + nkv + g) * D;
+  for (int jb = 0; jb < nkvb; ++jb) {
+    const int kv0 = jb * 64, nvalid = min(64, S - kv0);
+    __syncthreads();
+    rows_to_lds<D>(sK, kbase, QS, kv0, nvalid);
+    rows_to_lds<D>(sV, vbase, QS, kv0, nvalid);
+    rows_to_lds_t<D>(sKt, kbase, QS, kv0, nvalid);
+    __syncthreads();
+    if (kv0 > wq0 + 31) continue;
+
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[kb][e] = 0.f;
+        pacc[kb][e] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb], 0, 0, 0);
+      }
+    }
+    // dS = P * (dP - D), P = exp(s*scale - lse)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + acc_key(kb, i, hf);
+        float p = exp2f(sacc[kb][i] * sl2 - lse2);
+        if (key > q || key >= S || q >= S) p = 0.f;
+        sacc[kb][i] = p * (pacc[kb][i] - dl);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float sv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
+      const bf16x8_t sf = pack8(sv);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sKt, db * 32 + lr, ks, hf), sf,
+                                                         dq[db], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  bf16_t* stage = smem + wave * 32 * (D + 8);
+  store_tile_t<D>(stage, dq, scale, dqkv + (size_t)b * S * QS + h * D, QS, wq0, min(32, S - wq0),
+                  lane);
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+__global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+                                                       const bf16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ delta,
+                                                       bf16_t* __restrict__ dqkv, int S, int nq,
+                                                       int nkv, float scale) {
+  constexpr int NKK = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(2 * 64 * D + 2 * D * LDT)];
+  __shared__ float sL[64], sDl[64];
+  bf16_t* sQ = smem;
+  bf16_t* sO = smem + 64 * D;  // dO rows
+  bf16_t* sQt = smem + 2 * 64 * D;
+  bf16_t* sOt = sQt + D * LDT;
+
+  const int nkb = (S + 127) / 128;
+  const int kblk = blockIdx.x;  // key blocks: earliest keys have the most query blocks; go first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = nq / nkv;
+  const int QS = (nq + 2 * nkv) * D, OS = nq * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int k0 = kblk * 128;
+  const int wk0 = k0 + wave * 32;
+  const int key = wk0 + lr;
+  const bf16_t* base = qkv + (size_t)b * S * QS;
+  const bf16_t* dobase = dout + (size_t)b * S * OS;
+  const float sl2 = scale * kLog2e;
+  (void)nkb;
+
+  bf16x8_t kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    kf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + g) * D + kk * 16 + hf * 8) : zero8();
+    vf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + nkv + g) * D + kk * 16 + hf * 8) : zero8();
+  }
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[db][e] = 0.f;
+      dv[db][e] = 0.f;
+    }
+
+  const int nqblk = (S + 63) / 64;
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    for (int jb = k0 / 64; jb < nqblk; ++jb) {
+      const int q0 = jb * 64, nvalid = min(64, S - q0);
+      __syncthreads();
+      rows_to_lds<D>(sQ, base + h * D, QS, q0, nvalid);
+      rows_to_lds<D>(sO, dobase + h * D, OS, q0, nvalid);
+      rows_to_lds_t<D>(sQt, base + h * D, QS, q0, nvalid);
+      rows_to_lds_t<D>(sOt, dobase + h * D, OS, q0, nvalid);
+      if (threadIdx.x < 64) {
+        const int qq = q0 + threadIdx.x;
+        sL[threadIdx.x] = qq < S ? lse[((size_t)b * nq + h) * S + qq] * kLog2e : 0.f;
+        sDl[threadIdx.x] = qq < S ? delta[((size_t)b * nq + h) * S + qq] : 0.f;
+      }
+      __syncthreads();
+      if (q0 + 63 < wk0) continue;  // every query of this block precedes every key of the wave
+
+      f32x16_t sacc[2], pacc[2];
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[qb2][e] = 0.f;
+          pacc[qb2][e] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc[qb2], 0, 0, 0);
+          pacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc[qb2], 0, 0, 0);
+        }
+      }
+      // element i of sub-block qb2 is (query q0 + acc_key(qb2, i), this lane's key)
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = acc_key(qb2, i, hf);
+          const int qq = q0 + ql;
+          float p = exp2f(sacc[qb2][i] * sl2 - sL[ql]);
+          if (key > qq || qq >= S) p = 0.f;
+          sacc[qb2][i] = p;
+          pacc[qb2][i] = p * (pacc[qb2][i] - sDl[ql]);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float pv[8], sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
+          sv[j] = pacc[ks >> 1][8 * (ks & 1) + j];
+        }
+        const bf16x8_t pf = pack8(pv), sf = pack8(sv);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sOt, db * 32 + lr, ks, hf), pf,
+                                                           dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sQt, db * 32 + lr, ks, hf), sf,
+                                                           dk[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  bf16_t* stage = smem + wave * 32 * (D + 8);
+  const int nv = min(32, S - wk0);
+  if (nv > 0) {
+    store_tile_t<D>(stage, dk, scale, dqkv + (size_t)b * S * QS + (nq + g) * D, QS, wk0, nv, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    store_tile_t<D>(stage, dv, 1.0f, dqkv + (size_t)b * S * QS + (nq + nkv + g) * D, QS, wk0, nv,
+                    lane);
+  }
+}
+
+// ------------------------------------------------------------------ fp32 SIMT kernels
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ qkv,
+                                                          float* __restrict__ out,
+                                                          float* __restrict__ lse, int S, int nq,
+                                                          int nkv, float scale) {
+  const int q = blockIdx.x * 64 + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (q >= S) return;
+  const int g = h / (nq / nkv), QS = (nq + 2 * nkv) * D;
+  const float* base = qkv + (size_t)b * S * QS;
+  float qv[D], o[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qv[i] = base[(size_t)q * QS + h * D + i] * scale;
+    o[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= q; ++j) {
+    const float* kr = base + (size_t)j * QS + (nq + g) * D;
+    const float* vr = base + (size_t)j * QS + (nq + nkv + g) * D;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) s += qv[i] * kr[i];
+    const float mn = fmaxf(m, s);
+    const float a = expf(m - mn), p = expf(s - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] = o[i] * a + p * vr[i];
+    m = mn;
+  }
+  float* orow = out + ((size_t)b * S + q) * nq * D + h * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) orow[i] = o[i] / l;
+  lse[((size_t)b * nq + h) * S + q] = m + logf(l);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_dq_f32_kernel(const float* __restrict__ qkv,
+                                                         const float* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ delta,
+                                                         float* __restrict__ dqkv, int S, int nq,
+                                                         int nkv, float scale) {
+  const int q = blockIdx.x * 64 + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (q >= S) return;
+  const int g = h / (nq / nkv), QS = (nq + 2 * nkv) * D, OS = nq * D;
+  const float* base = qkv + (size_t)b * S * QS;
+  float qv[D], dov[D], dq[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qv[i] = base[(size_t)q * QS + h * D + i];
+    dov[i] = dout[((size_t)b * S + q) * OS + h * D + i];
+    dq[i] = 0.f;
+  }
+  const float L = lse[((size_t)b * nq + h) * S + q], Dl = delta[((size_t)b * nq + h) * S + q];
+  for (int j = 0; j <= q; ++j) {
+    const float* kr = base + (size_t)j * QS + (nq + g) * D;
+    const float* vr = base + (size_t)j * QS + (nq + nkv + g) * D;
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      s += qv[i] * kr[i];
+      dp += dov[i] * vr[i];
+    }
+    const float p = expf(s * scale - L);
+    const float ds = p * (dp - Dl);
+#pragma unroll
+    for (int i = 0; i < D; ++i) dq[i] += ds * kr[i];
+  }
+  float* out = dqkv + ((size_t)b * S + q) * QS + h * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) out[i] = dq[i] * scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_dkv_f32_kernel(const float* __restrict__ qkv,
+                                                          const float* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta,
+                                                          float* __restrict__ dqkv, int S, int nq,
+                                                          int nkv, float scale) {
+  const int j = blockIdx.x * 64 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (j >= S) return;
+  const int G = nq / nkv, QS = (nq + 2 * nkv) * D, OS = nq * D;
+  const float* base = qkv + (size_t)b * S * QS;
+  float kv[D], vv[D], dk[D], dv[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    kv[i] = base[(size_t)j * QS + (nq + g) * D + i];
+    vv[i] = base[(size_t)j * QS + (nq + nkv + g) * D + i];
+    dk[i] = 0.f;
+    dv[i] = 0.f;
+  }
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    for (int q = j; q < S; ++q) {
+      const float* qr = base + (size_t)q * QS + h * D;
+      const float* dor = dout + ((size_t)b * S + q) * OS + h * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        s += qr[i] * kv[i];
+        dp += dor[i] * vv[i];
+      }
+      const float p = expf(s * scale - lse[((size_t)b * nq + h) * S + q]);
+      const float ds = p * (dp - delta[((size_t)b * nq + h) * S + q]);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        dv[i] += p * dor[i];
+        dk[i] += ds * qr[i];
+      }
+    }
+  }
+  float* ok = dqkv + ((size_t)b * S + j) * QS + (nq + g) * D;
+  float* ov = dqkv + ((size_t)b * S + j) * QS + (nq + nkv + g) * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    ok[i] = dk[i] * scale;
+    ov[i] = dv[i];
+  }
+}
+
+}  // namespace
+
+int attention_check(int B, int S, int nq, int nkv, int d, int dtype) {
+  SLIDE_REQUIRE(B >= 0 && S >= 0, SLIDE_E_SHAPE, "attention: negative batch or sequence");
+  SLIDE_REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0, SLIDE_E_SHAPE,
+                "attention: n_heads %d must be a positive multiple of n_kv_heads %d", nq, nkv);
+  SLIDE_REQUIRE(d == 64 || d == 128, SLIDE_E_SHAPE, "attention: head_dim %d (64 or 128)", d);
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "attention: bad dtype");
+  return SLIDE_OK;
+}
+
+int attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv, int d,
+                  int dtype, hipStream_t st) {
+  if (B == 0 || S == 0) return SLIDE_OK;
+  ProfScope ps("attn_fwd", st);
+  const float scale = 1.0f / sqrtf((float)d);
+  if (dtype == SLIDE_BF16) {
+    dim3 grid((S + 127) / 128, nq, B), block(256);
+    if (d == 128)
+      hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse, S, nq, nkv, scale);
+  } else {
+    dim3 grid((S + 63) / 64, nq, B), block(64);
+    if (d == 128)
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, block, 0, st, (const float*)qkv, (float*)o, lse, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, block, 0, st, (const float*)qkv, (float*)o, lse, S, nq, nkv, scale);
+  }
+  return check_launch("attn_fwd");
+}
+
+size_t attention_bwd_ws(int B, int S, int nq) { return align_up((size_t)B * nq * S * 4, 256); }
+
+int attention_bwd(const void* qkv, const void* o, const float* lse, const void* dout, void* dqkv,
+                  int B, int S, int nq, int nkv, int d, int dtype, void* ws, hipStream_t st) {
+  if (B == 0 || S == 0) return SLIDE_OK;
+  float* delta = (float*)ws;
+  const float scale = 1.0f / sqrtf((float)d);
+  {
+    ProfScope ps("attn_delta", st);
+    const size_t rows = (size_t)B * S * nq;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (dtype == SLIDE_BF16)
+      hipLaunchKernelGGL(attn_delta_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq, d);
+    else
+      hipLaunchKernelGGL(attn_delta_kernel<float>, grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq, d);
+  }
+  SLIDE_TRY(check_launch("attn_delta"));
+  if (dtype == SLIDE_BF16) {
+    {
+      ProfScope ps("attn_bwd_dq", st);
+      dim3 grid((S + 127) / 128, nq, B), block(256);
+      if (d == 128)
+        hipLaunchKernelGGL(attn_dq_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+      else
+        hipLaunchKernelGGL(attn_dq_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+    }
+    SLIDE_TRY(check_launch("attn_bwd_dq"));
+    {
+      ProfScope ps("attn_bwd_dkv", st);
+      dim3 grid((S + 127) / 128, nkv, B), block(256);
+      if (d == 128)
+        hipLaunchKernelGGL(attn_dkv_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+      else
+        hipLaunchKernelGGL(attn_dkv_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+    }
+    return check_launch("attn_bwd_dkv");
+  }
+  {
+    ProfScope ps("attn_bwd_dq", st);
+    dim3 grid((S + 63) / 64, nq, B), block(64);
+    if (d == 128)
+      hipLaunchKernelGGL(attn_dq_f32_kernel<128>, grid, block, 0, st, (const float*)qkv, (const float*)dout, lse, delta, (float*)dqkv, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL(attn_dq_f32_kernel<64>, grid, block, 0, st, (const float*)qkv, (const float*)dout, lse, delta, (float*)dqkv, S, nq, nkv, scale);
+  }
+  {
+    ProfScope ps("attn_bwd_dkv", st);
+    dim3 grid((S + 63) / 64, nkv, B), block(64);
+    if (d == 128)
+      hipLaunchKernelGGL(attn_dkv_f32_kernel<128>, grid, block, 0, st, (const float*)qkv, (const float*)dout, lse, delta, (float*)dqkv, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL(attn_dkv_f32_kernel<64>, grid, block, 0, st, (const float*)qkv, (const float*)dout, lse, delta, (float*)dqkv, S, nq, nkv, scale);
+  }
+  return check_launch("attn_bwd");
+}
+
+}  // namespace slide
+
+extern "C" int slide_attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq,
+                                   int nkv, int d, int dtype, void* stream) {
+  SLIDE_TRY(slide::attention_check(B, S, nq, nkv, d, dtype));
+  SLIDE_REQUIRE(qkv && o && lse, SLIDE_E_ARG, "slide_attention_fwd: null pointer");
+  return slide::attention_fwd(qkv, o, lse, B, S, nq, nkv, d, dtype, (hipStream_t)stream);
+}
+
+extern "C" size_t slide_attention_bwd_workspace_bytes(int B, int S, int nq) {
+  return slide::attention_bwd_ws(B, S, nq);
+}
+
+extern "C" int slide_attention_bwd(const void* qkv, const void* o, const float* lse,
+                                   const void* d_o, void* dqkv, int B, int S, int nq, int nkv,
+                                   int d, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(slide::attention_check(B, S, nq, nkv, d, dtype));
+  SLIDE_REQUIRE(qkv && o && lse && d_o && dqkv && ws, SLIDE_E_ARG,
+                "slide_attention_bwd: null pointer");
+  SLIDE_REQUIRE(ws_bytes >= slide::attention_bwd_ws(B, S, nq), SLIDE_E_WORKSPACE,
+                "slide_attention_bwd: workspace %zu < %zu", ws_bytes,
+                slide::attention_bwd_ws(B, S, nq));
+  return slide::attention_bwd(qkv, o, lse, d_o, dqkv, B, S, nq, nkv, d, dtype, ws,
+                              (hipStream_t)stream);
+}

@@ -1,0 +1,287 @@
+// Fused LM-head cross-entropy in vocabulary chunks (SlideFormer summary, section 2C: the
+// projection and the loss are fused so that the [N, V] logit tensor of a large vocabulary never
+// exists, cutting the output layer's memory without changing the result).
+//
+//   pass 1, per chunk c of C vocabulary rows: z_c^T = W_c h^T (MFMA GEMM, fp32 out, [C, N]);
+//           per (token, row split) online max / sum-exp partials and the target logit.
+//   combine: lse_t from the partials in a fixed order; loss = mean over valid t of lse_t - z_t[y_t]
+//   pass 2, per chunk: recompute z_c^T, dz = (exp(z - lse_t) - [v == y_t]) / N_valid,
+//           dh += dz^T W_c (fp32 accumulator), dW_c = dz h.
+// Every reduction has a fixed order, so the results are deterministic. The workspace holds one
+// chunk of logits and gradients, O(C*N), instead of O(V*N).
+#include "ce.h"
+
+#include "gemm.h"
+#include "pointwise.h"
+
+namespace slide {
+namespace {
+
+constexpr int kRowSplits = 32;  // row splits per chunk in the statistics pass
+
+// partial (max, sum exp(z - max)) of rows [r0, r1) of a [rows][ldz] fp32 chunk, per token column
+__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ z, int rows,
+                                                       int N, int ldz, int c0,
+                                                       const int32_t* __restrict__ tgt,
+                                                       float* __restrict__ pm,
+                                                       float* __restrict__ ps,
+                                                       float* __restrict__ zt, int splits) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  const int sp = blockIdx.y;
+  const int per = (rows + splits - 1) / splits;
+  const int r0 = sp * per, r1 = min(rows, r0 + per);
+  float m = -INFINITY, s = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    const float v = z[(size_t)r * ldz + t];
+    if (v > m) {
+      s = s * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      s += __expf(v - m);
+    }
+  }
+  pm[(size_t)sp * N + t] = m;
+  ps[(size_t)sp * N + t] = s;
+  const int y = tgt[t] - c0;
+  if (y >= r0 && y < r1) zt[t] = z[(size_t)y * ldz + t];
+}
+
+// lse_t from all partials (chunk-major, split-minor order) and the per-token loss term
+__global__ __launch_bounds__(256) void ce_lse_kernel(const float* __restrict__ pm,
+                                                     const float* __restrict__ ps, int nparts,
+                                                     int N, const int32_t* __restrict__ tgt,
+                                                     int V, const float* __restrict__ zt,
+                                                     float* __restrict__ lse,
+                                                     float* __restrict__ lt) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  float m = -INFINITY;
+  for (int p = 0; p < nparts; ++p) m = fmaxf(m, pm[(size_t)p * N + t]);
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float pmv = pm[(size_t)p * N + t];
+    if (pmv != -INFINITY) s += ps[(size_t)p * N + t] * __expf(pmv - m);
+  }
+  const float l = m + logf(s);
+  lse[t] = l;
+  const int y = tgt[t];
+  lt[t] = (y >= 0 && y < V) ? l - zt[t] : 0.f;
+}
+
+// loss = sum(lt over valid) / N_valid with a fixed reduction tree; also 1/N_valid for pass 2
+__global__ __launch_bounds__(1024) void ce_loss_kernel(const float* __restrict__ lt,
+                                                       const int32_t* __restrict__ tgt, int N,
+                                                       int V, float* loss, float* inv_nv) {
+  __shared__ float ss[1024];
+  __shared__ int sc[1024];
+  float s = 0.f;
+  int c = 0;
+  for (int t = threadIdx.x; t < N; t += 1024) {
+    const int y = tgt[t];
+    if (y >= 0 && y < V) {
+      s += lt[t];
+      ++c;
+    }
+  }
+  ss[threadIdx.x] = s;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      ss[threadIdx.x] += ss[threadIdx.x + o];
+      sc[threadIdx.x] += sc[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int nv = sc[0];
+    *loss = nv > 0 ? ss[0] / (float)nv : 0.f;
+    *inv_nv = nv > 0 ? 1.0f / (float)nv : 0.f;
+  }
+}
+
+// dz[v][t] = (exp(z[v][t] - lse_t) - [c0 + v == y_t]) / N_valid for valid t, 0 otherwise
+template <typename T>
+__global__ __launch_bounds__(256) void ce_dz_kernel(const float* __restrict__ z,
+                                                    T* __restrict__ dz, int rows, int N, int ldz,
+                                                    int c0, int V, const int32_t* __restrict__ tgt,
+                                                    const float* __restrict__ lse,
+                                                    const float* __restrict__ inv_nv) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)rows * ldz) return;
+  const int r = (int)(idx / ldz), t = (int)(idx % ldz);
+  float g = 0.f;
+  if (t < N) {
+    const int y = tgt[t];
+    if (y >= 0 && y < V) {
+      g = __expf(z[idx] - lse[t]);
+      if (c0 + r == y) g -= 1.f;
+      g *= *inv_nv;
+    }
+  }
+  Elem<T>::store(dz + idx, g);
+}
+
+template <typename T>
+__global__ void fill_zero_kernel(T* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) Elem<T>::store(p + i, 0.f);
+}
+
+__global__ void write_scalar_kernel(float* p, float v) { *p = v; }
+
+struct CeLayout {
+  int C, nchunks, ldz;
+  size_t zbuf, dz, pm, ps, zt, lse, lt, scal, dh, total;
+};
+
+CeLayout ce_layout(const slide_ce_cfg& c, int N, bool want_dh) {
+  CeLayout L{};
+  L.C = c.chunk > 0 ? c.chunk : 8192;
+  if (L.C > c.vocab) L.C = c.vocab;
+  L.nchunks = (c.vocab + L.C - 1) / L.C;
+  L.ldz = ((N + 7) / 8) * 8;
+  const size_t ts = (size_t)dtype_size(c.dtype);
+  size_t off = 0;
+  auto put = [&](size_t bytes) {
+    off = align_up(off, 256);
+    size_t at = off;
+    off += bytes;
+    return at;
+  };
+  L.zbuf = put((size_t)L.C * L.ldz * 4);
+  L.dz = put((size_t)L.C * L.ldz * ts);
+  L.pm = put((size_t)L.nchunks * kRowSplits * N * 4);
+  L.ps = put((size_t)L.nchunks * kRowSplits * N * 4);
+  L.zt = put((size_t)N * 4);
+  L.lse = put((size_t)N * 4);
+  L.lt = put((size_t)N * 4);
+  L.scal = put(256);
+  L.dh = want_dh ? put((size_t)N * c.hidden * 4) : 0;
+  L.total = align_up(off, 256);
+  return L;
+}
+
+inline unsigned nblk(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+size_t ce_workspace_bytes(const slide_ce_cfg& c, int N) { return ce_layout(c, N, true).total; }
+
+int ce_check(const slide_ce_cfg* c, int N) {
+  SLIDE_REQUIRE(c, SLIDE_E_ARG, "lmhead_ce: null cfg");
+  SLIDE_REQUIRE(c->dtype == SLIDE_BF16 || c->dtype == SLIDE_F32, SLIDE_E_ARG, "lmhead_ce: bad dtype");
+  SLIDE_REQUIRE(c->hidden > 0 && c->hidden % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: hidden %d must be a positive multiple of 8", c->hidden);
+  SLIDE_REQUIRE(c->vocab > 0 && c->vocab % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: vocab %d must be a positive multiple of 8", c->vocab);
+  SLIDE_REQUIRE(c->chunk >= 0 && c->chunk % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: chunk %d must be a multiple of 8", c->chunk);
+  SLIDE_REQUIRE(N >= 0, SLIDE_E_SHAPE, "lmhead_ce: negative token count");
+  return SLIDE_OK;
+}
+
+int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* tgt, int N,
+           float* loss, void* dh, void* dw, void* ws, hipStream_t st) {
+  const int H = c.hidden, V = c.vocab, dt = c.dtype;
+  const size_t ts = (size_t)dtype_size(dt);
+  const CeLayout L = ce_layout(c, N, dh != nullptr);
+  char* base = (char*)ws;
+  float* zbuf = (float*)(base + L.zbuf);
+  void* dz = base + L.dz;
+  float* pm = (float*)(base + L.pm);
+  float* ps = (float*)(base + L.ps);
+  float* zt = (float*)(base + L.zt);
+  float* lse = (float*)(base + L.lse);
+  float* lt = (float*)(base + L.lt);
+  float* inv_nv = (float*)(base + L.scal);
+  float* dh_acc = dh ? (float*)(base + L.dh) : nullptr;
+
+  if (N == 0) {
+    hipLaunchKernelGGL(write_scalar_kernel, dim3(1), dim3(1), 0, st, loss, 0.f);
+    if (dw) {
+      const size_t n = (size_t)V * H;
+      if (dt == SLIDE_BF16) hipLaunchKernelGGL(fill_zero_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, (bf16_t*)dw, n);
+      else hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, (float*)dw, n);
+    }
+    return check_launch("lmhead_ce(empty)");
+  }
+
+  auto logits = [&](int c0, int rows, const char* name) {
+    // z^T[v][t] = sum_k W[c0+v][k] h[t][k]
+    GemmArgs g{rows, N, H, (const char*)w + (size_t)c0 * H * ts, H, true, h, H, true, zbuf,
+               L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, dt, name};
+    return gemm_launch(g, st);
+  };
+
+  // ---- pass 1: statistics
+  for (int ci = 0; ci < L.nchunks; ++ci) {
+    const int c0 = ci * L.C, rows = std::min(L.C, V - c0);
+    SLIDE_TRY(logits(c0, rows, "ce_logits_gemm"));
+    ProfScope ps_("ce_stats", st);
+    hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), kRowSplits), dim3(256), 0, st, zbuf,
+                       rows, N, L.ldz, c0, tgt, pm + (size_t)ci * kRowSplits * N,
+                       ps + (size_t)ci * kRowSplits * N, zt, kRowSplits);
+    SLIDE_TRY(check_launch("ce_stats"));
+  }
+  {
+    ProfScope ps_("ce_lse", st);
+    hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 256)), dim3(256), 0, st, pm, ps,
+                       L.nchunks * kRowSplits, N, tgt, V, zt, lse, lt);
+    hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, lt, tgt, N, V, loss, inv_nv);
+  }
+  SLIDE_TRY(check_launch("ce_lse"));
+  if (!dh && !dw) return SLIDE_OK;
+
+  // ---- pass 2: gradients
+  for (int ci = 0; ci < L.nchunks; ++ci) {
+    const int c0 = ci * L.C, rows = std::min(L.C, V - c0);
+    SLIDE_TRY(logits(c0, rows, "ce_logits_gemm"));
+    {
+      ProfScope ps_("ce_dz", st);
+      const size_t n = (size_t)rows * L.ldz;
+      if (dt == SLIDE_BF16)
+        hipLaunchKernelGGL(ce_dz_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, zbuf,
+                           (bf16_t*)dz, rows, N, L.ldz, c0, V, tgt, lse, inv_nv);
+      else
+        hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, zbuf,
+                           (float*)dz, rows, N, L.ldz, c0, V, tgt, lse, inv_nv);
+      SLIDE_TRY(check_launch("ce_dz"));
+    }
+    const void* wc = (const char*)w + (size_t)c0 * H * ts;
+    if (dh) {
+      // dh[t][i] (+)= sum_v dz[v][t] W[c0+v][i]
+      GemmArgs g{N, H, rows, dz, L.ldz, false, wc, H, false, dh_acc, H, SLIDE_F32, nullptr, 0,
+                 1.0f, ci > 0, dt, "ce_dh_gemm"};
+      SLIDE_TRY(gemm_launch(g, st));
+    }
+    if (dw) {
+      // dW[c0+v][i] = sum_t dz[v][t] h[t][i]
+      GemmArgs g{rows, H, N, dz, L.ldz, true, h, H, false, (char*)dw + (size_t)c0 * H * ts, H,
+                 dt, nullptr, 0, 1.0f, false, dt, "ce_dw_gemm"};
+      SLIDE_TRY(gemm_launch(g, st));
+    }
+  }
+  if (dh) SLIDE_TRY(convert_from_f32(dh_acc, dh, (size_t)N * H, dt, st));
+  return SLIDE_OK;
+}
+
+}  // namespace slide
+
+extern "C" size_t slide_lmhead_ce_workspace_bytes(const slide_ce_cfg* cfg, int N) {
+  if (!cfg || slide::ce_check(cfg, N) != SLIDE_OK) return 0;
+  return slide::ce_workspace_bytes(*cfg, N);
+}
+
+extern "C" int slide_lmhead_ce(const slide_ce_cfg* cfg, const void* h, const void* w,
+                               const int32_t* targets, int N, float* loss_dev, void* dh,
+                               void* dw, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(slide::ce_check(cfg, N));
+  SLIDE_REQUIRE(loss_dev && ws && (N == 0 || (h && w && targets)), SLIDE_E_ARG,
+                "slide_lmhead_ce: null pointer");
+  SLIDE_REQUIRE(slide::aligned16(h) && slide::aligned16(w) && (!dh || slide::aligned16(dh)) &&
+                    (!dw || slide::aligned16(dw)),
+                SLIDE_E_ARG, "slide_lmhead_ce: tensors must be 16-byte aligned");
+  const size_t need = slide::ce_workspace_bytes(*cfg, N);
+  SLIDE_REQUIRE(ws_bytes >= need, SLIDE_E_WORKSPACE, "slide_lmhead_ce: workspace %zu < %zu",
+                ws_bytes, need);
+  return slide::ce_run(*cfg, h, w, targets, N, loss_dev, dh, dw, ws, (hipStream_t)stream);
+}

@@ -1,0 +1,301 @@
+// One decoder layer, forward and backward, composed from the GEMM, attention and memory-bound
+// kernels, plus the C-ABI entry points of the model glue (RMSNorm, RoPE, embedding).
+//
+// The layer runs on a weight slot of the sliding window (SlideFormer summary, section 2A: only
+// the active layers live on the GPU). Between the forward and the backward sweep only the
+// layer's input x is kept; the backward recomputes the forward's intermediates into its
+// workspace (the summary's section 2B keeps the activation window small), then runs:
+//   dm = dy Wd, dWd = dy^T m; SwiGLU backward; dr2 = dgu Wgu, dWgu = dgu^T r2;
+//   dx2 = dy + RMSNorm_bwd(dr2); do = dx2 Wo, dWo = dx2^T o; attention backward; inverse RoPE;
+//   dr = dqkv Wqkv, dWqkv = dqkv^T r; dx = dx2 + RMSNorm_bwd(dr).
+#include "attention.h"
+#include "gemm.h"
+#include "pointwise.h"
+
+namespace slide {
+namespace {
+
+struct Dims {
+  int H, nq, nkv, d, F, dt, B, S, N, QR, OD;
+  size_t ts;
+};
+
+int check_cfg(const slide_layer_cfg* c) {
+  SLIDE_REQUIRE(c, SLIDE_E_ARG, "layer: null cfg");
+  SLIDE_REQUIRE(c->dtype == SLIDE_BF16 || c->dtype == SLIDE_F32, SLIDE_E_ARG, "layer: bad dtype %d", c->dtype);
+  SLIDE_REQUIRE(c->hidden > 0 && c->hidden % 8 == 0, SLIDE_E_SHAPE, "layer: hidden %d must be a positive multiple of 8", c->hidden);
+  SLIDE_REQUIRE(c->ffn > 0 && c->ffn % 8 == 0, SLIDE_E_SHAPE, "layer: ffn %d must be a positive multiple of 8", c->ffn);
+  SLIDE_REQUIRE(c->head_dim == 64 || c->head_dim == 128, SLIDE_E_SHAPE, "layer: head_dim %d (64 or 128)", c->head_dim);
+  SLIDE_REQUIRE(c->n_heads > 0 && c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads == 0,
+                SLIDE_E_SHAPE, "layer: n_heads %d must be a positive multiple of n_kv_heads %d",
+                c->n_heads, c->n_kv_heads);
+  SLIDE_REQUIRE(c->rms_eps > 0.f && c->rope_theta > 0.f, SLIDE_E_ARG, "layer: rms_eps and rope_theta must be > 0");
+  return SLIDE_OK;
+}
+
+Dims dims_of(const slide_layer_cfg& c, int B, int S) {
+  Dims d;
+  d.H = c.hidden;
+  d.nq = c.n_heads;
+  d.nkv = c.n_kv_heads;
+  d.d = c.head_dim;
+  d.F = c.ffn;
+  d.dt = c.dtype;
+  d.B = B;
+  d.S = S;
+  d.N = B * S;
+  d.QR = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  d.OD = c.n_heads * c.head_dim;
+  d.ts = (size_t)dtype_size(c.dtype);
+  return d;
+}
+
+void param_offsets(const Dims& d, size_t off[6]) {
+  const size_t H = d.H, F = d.F;
+  off[0] = 0;                             // w_attn [H]
+  off[1] = off[0] + H;                    // Wqkv [QR, H]
+  off[2] = off[1] + (size_t)d.QR * H;     // Wo [H, OD]
+  off[3] = off[2] + H * (size_t)d.OD;     // w_mlp [H]
+  off[4] = off[3] + H;                    // Wgu [2F, H]
+  off[5] = off[4] + 2 * F * H;            // Wd [H, F]
+}
+size_t param_count(const Dims& d) {
+  size_t off[6];
+  param_offsets(d, off);
+  return off[5] + (size_t)d.H * d.F;
+}
+
+// Workspace carving; with a null base only the size is computed.
+struct Ws {
+  void *r, *qkv, *o, *x2, *r2, *gu, *m;
+  float *lse, *cos_t, *sin_t;
+  void *dm, *dgu, *dr2, *dx2, *dO, *dqkv, *dr;
+  void *rms_ws, *attn_ws;
+  size_t bytes;
+};
+
+Ws carve(void* base, const Dims& d, bool bwd) {
+  Carver c(base);
+  Ws w{};
+  const size_t N = d.N;
+  auto T = [&](size_t n) { return (void*)c.take<char>(n * d.ts); };
+  w.cos_t = c.take<float>((size_t)d.S * (d.d / 2));
+  w.sin_t = c.take<float>((size_t)d.S * (d.d / 2));
+  w.r = T(N * d.H);
+  w.qkv = T(N * d.QR);
+  w.o = T(N * d.OD);
+  w.lse = c.take<float>((size_t)d.B * d.nq * d.S);
+  w.x2 = T(N * d.H);
+  w.r2 = T(N * d.H);
+  w.gu = T(N * 2 * (size_t)d.F);
+  w.m = T(N * d.F);
+  if (bwd) {
+    w.dm = T(N * d.F);
+    w.dgu = T(N * 2 * (size_t)d.F);
+    w.dr2 = T(N * d.H);
+    w.dx2 = T(N * d.H);
+    w.dO = T(N * d.OD);
+    w.dqkv = T(N * d.QR);
+    w.dr = T(N * d.H);
+    w.rms_ws = c.take<char>(rmsnorm_bwd_ws(d.N, d.H));
+    w.attn_ws = c.take<char>(attention_bwd_ws(d.B, d.S, d.nq));
+  }
+  w.bytes = align_up(c.used, 256);
+  return w;
+}
+
+inline const void* at(const void* p, size_t elems, size_t ts) { return (const char*)p + elems * ts; }
+inline void* at(void* p, size_t elems, size_t ts) { return (char*)p + elems * ts; }
+
+int gemm(int M, int N, int K, const void* A, int lda, bool ak, const void* B, int ldb, bool bk,
+         void* C, int ldc, const void* R, int dt, const char* name, hipStream_t st) {
+  GemmArgs g{M, N, K, A, lda, ak, B, ldb, bk, C, ldc, dt, R, R ? ldc : 0, 1.0f, false, dt, name};
+  return gemm_launch(g, st);
+}
+
+// forward through SwiGLU (everything the backward needs); y written when y != nullptr
+int forward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* x, void* y,
+            const Ws& ws, hipStream_t st) {
+  size_t off[6];
+  param_offsets(d, off);
+  const size_t ts = d.ts;
+  SLIDE_TRY(rope_tables(ws.cos_t, ws.sin_t, d.S, d.d, c.rope_theta, st));
+  SLIDE_TRY(rmsnorm_fwd(x, at(w, off[0], ts), ws.r, nullptr, d.N, d.H, c.rms_eps, d.dt, st));
+  SLIDE_TRY(gemm(d.N, d.QR, d.H, ws.r, d.H, true, at(w, off[1], ts), d.H, true, ws.qkv, d.QR,
+                 nullptr, d.dt, "gemm_qkv", st));
+  SLIDE_TRY(rope_apply(ws.qkv, ws.cos_t, ws.sin_t, d.B, d.S, d.nq, d.nkv, d.d, 0, d.dt, st));
+  SLIDE_TRY(attention_fwd(ws.qkv, ws.o, ws.lse, d.B, d.S, d.nq, d.nkv, d.d, d.dt, st));
+  SLIDE_TRY(gemm(d.N, d.H, d.OD, ws.o, d.OD, true, at(w, off[2], ts), d.OD, true, ws.x2, d.H, x,
+                 d.dt, "gemm_o", st));
+  SLIDE_TRY(rmsnorm_fwd(ws.x2, at(w, off[3], ts), ws.r2, nullptr, d.N, d.H, c.rms_eps, d.dt, st));
+  SLIDE_TRY(gemm(d.N, 2 * d.F, d.H, ws.r2, d.H, true, at(w, off[4], ts), d.H, true, ws.gu,
+                 2 * d.F, nullptr, d.dt, "gemm_gate_up", st));
+  SLIDE_TRY(swiglu_fwd(ws.gu, ws.m, d.N, d.F, d.dt, st));
+  if (y)
+    SLIDE_TRY(gemm(d.N, d.H, d.F, ws.m, d.F, true, at(w, off[5], ts), d.F, true, y, d.H, ws.x2,
+                   d.dt, "gemm_down", st));
+  return SLIDE_OK;
+}
+
+int backward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* x,
+             const void* dy, void* dx, void* g, const Ws& ws, hipStream_t st) {
+  size_t off[6];
+  param_offsets(d, off);
+  const size_t ts = d.ts;
+  const int N = d.N, H = d.H, F = d.F;
+  SLIDE_TRY(forward(d, c, w, x, nullptr, ws, st));
+  // MLP half
+  SLIDE_TRY(gemm(N, F, H, dy, H, true, at(w, off[5], ts), F, false, ws.dm, F, nullptr, d.dt,
+                 "gemm_down_dx", st));
+  SLIDE_TRY(gemm(H, F, N, dy, H, false, ws.m, F, false, at(g, off[5], ts), F, nullptr, d.dt,
+                 "gemm_down_dw", st));
+  SLIDE_TRY(swiglu_bwd(ws.dm, ws.gu, ws.dgu, N, F, d.dt, st));
+  SLIDE_TRY(gemm(N, H, 2 * F, ws.dgu, 2 * F, true, at(w, off[4], ts), H, false, ws.dr2, H,
+                 nullptr, d.dt, "gemm_gate_up_dx", st));
+  SLIDE_TRY(gemm(2 * F, H, N, ws.dgu, 2 * F, false, ws.r2, H, false, at(g, off[4], ts), H,
+                 nullptr, d.dt, "gemm_gate_up_dw", st));
+  SLIDE_TRY(rmsnorm_bwd(ws.dr2, ws.x2, at(w, off[3], ts), dy, ws.dx2, at(g, off[3], ts), N, H,
+                        c.rms_eps, d.dt, ws.rms_ws, st));
+  // attention half
+  SLIDE_TRY(gemm(N, d.OD, H, ws.dx2, H, true, at(w, off[2], ts), d.OD, false, ws.dO, d.OD,
+                 nullptr, d.dt, "gemm_o_dx", st));
+  SLIDE_TRY(gemm(H, d.OD, N, ws.dx2, H, false, ws.o, d.OD, false, at(g, off[2], ts), d.OD,
+                 nullptr, d.dt, "gemm_o_dw", st));
+  SLIDE_TRY(attention_bwd(ws.qkv, ws.o, ws.lse, ws.dO, ws.dqkv, d.B, d.S, d.nq, d.nkv, d.d,
+                          d.dt, ws.attn_ws, st));
+  SLIDE_TRY(rope_apply(ws.dqkv, ws.cos_t, ws.sin_t, d.B, d.S, d.nq, d.nkv, d.d, 1, d.dt, st));
+  SLIDE_TRY(gemm(N, H, d.QR, ws.dqkv, d.QR, true, at(w, off[1], ts), H, false, ws.dr, H, nullptr,
+                 d.dt, "gemm_qkv_dx", st));
+  SLIDE_TRY(gemm(d.QR, H, N, ws.dqkv, d.QR, false, ws.r, H, false, at(g, off[1], ts), H, nullptr,
+                 d.dt, "gemm_qkv_dw", st));
+  SLIDE_TRY(rmsnorm_bwd(ws.dr, x, at(w, off[0], ts), ws.dx2, dx, at(g, off[0], ts), N, H,
+                        c.rms_eps, d.dt, ws.rms_ws, st));
+  return SLIDE_OK;
+}
+
+int check_ptrs(const Dims& d, std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    SLIDE_REQUIRE(p, SLIDE_E_ARG, "layer: null pointer");
+    SLIDE_REQUIRE(aligned16(p), SLIDE_E_ARG, "layer: pointers must be 16-byte aligned");
+  }
+  (void)d;
+  return SLIDE_OK;
+}
+
+}  // namespace
+}  // namespace slide
+
+using namespace slide;
+
+extern "C" size_t slide_layer_param_count(const slide_layer_cfg* cfg) {
+  if (check_cfg(cfg) != SLIDE_OK) return 0;
+  return param_count(dims_of(*cfg, 0, 0));
+}
+
+extern "C" int slide_layer_param_offsets(const slide_layer_cfg* cfg, size_t off[6]) {
+  SLIDE_TRY(check_cfg(cfg));
+  SLIDE_REQUIRE(off, SLIDE_E_ARG, "slide_layer_param_offsets: null output");
+  param_offsets(dims_of(*cfg, 0, 0), off);
+  return SLIDE_OK;
+}
+
+extern "C" size_t slide_layer_workspace_bytes(const slide_layer_cfg* cfg, int B, int S, int bwd) {
+  if (check_cfg(cfg) != SLIDE_OK || B < 0 || S < 0) return 0;
+  return carve(nullptr, dims_of(*cfg, B, S), bwd != 0).bytes;
+}
+
+extern "C" int slide_layer_fwd(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
+                               void* y, int B, int S, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(check_cfg(cfg));
+  SLIDE_REQUIRE(B >= 0 && S >= 0, SLIDE_E_SHAPE, "slide_layer_fwd: negative B or S");
+  const Dims d = dims_of(*cfg, B, S);
+  if (d.N == 0) return SLIDE_OK;
+  SLIDE_TRY(check_ptrs(d, {w_slot, x, y, ws}));
+  SLIDE_REQUIRE(x != y, SLIDE_E_ARG, "slide_layer_fwd: y must not alias x");
+  const Ws w0 = carve(nullptr, d, false);
+  SLIDE_REQUIRE(ws_bytes >= w0.bytes, SLIDE_E_WORKSPACE, "slide_layer_fwd: workspace %zu < %zu",
+                ws_bytes, w0.bytes);
+  return forward(d, *cfg, w_slot, x, y, carve(ws, d, false), (hipStream_t)stream);
+}
+
+extern "C" int slide_layer_bwd(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
+                               const void* dy, void* dx, void* g_slot, int B, int S, void* ws,
+                               size_t ws_bytes, void* stream) {
+  SLIDE_TRY(check_cfg(cfg));
+  SLIDE_REQUIRE(B >= 0 && S >= 0, SLIDE_E_SHAPE, "slide_layer_bwd: negative B or S");
+  const Dims d = dims_of(*cfg, B, S);
+  SLIDE_TRY(check_ptrs(d, {w_slot, g_slot, ws}));
+  if (d.N == 0)  // no tokens: every parameter gradient is zero
+    return fill_zero(g_slot, param_count(d), d.dt, (hipStream_t)stream);
+  SLIDE_TRY(check_ptrs(d, {x, dy, dx}));
+  SLIDE_REQUIRE(x != dx, SLIDE_E_ARG, "slide_layer_bwd: dx must not alias x");
+  const Ws w0 = carve(nullptr, d, true);
+  SLIDE_REQUIRE(ws_bytes >= w0.bytes, SLIDE_E_WORKSPACE, "slide_layer_bwd: workspace %zu < %zu",
+                ws_bytes, w0.bytes);
+  return backward(d, *cfg, w_slot, x, dy, dx, g_slot, carve(ws, d, true), (hipStream_t)stream);
+}
+
+extern "C" int slide_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out, int N,
+                                 int H, float eps, int dtype, void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
+  SLIDE_REQUIRE(eps > 0.f, SLIDE_E_ARG, "rmsnorm: eps must be > 0");
+  if (N == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(x && w && y && aligned16(x) && aligned16(w) && aligned16(y), SLIDE_E_ARG,
+                "rmsnorm: null or misaligned pointer");
+  return rmsnorm_fwd(x, w, y, rstd_out, N, H, eps, dtype, (hipStream_t)stream);
+}
+
+extern "C" size_t slide_rmsnorm_bwd_workspace_bytes(int N, int H) {
+  return rmsnorm_bwd_ws(N < 0 ? 0 : N, H < 0 ? 0 : H);
+}
+
+extern "C" int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres,
+                                 void* dx, void* dw, int N, int H, float eps, int dtype, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
+  SLIDE_REQUIRE(ws && ws_bytes >= rmsnorm_bwd_ws(N, H), SLIDE_E_WORKSPACE,
+                "rmsnorm_bwd: workspace %zu < %zu", ws_bytes, rmsnorm_bwd_ws(N, H));
+  SLIDE_REQUIRE(N == 0 || (dy && x && w && dx), SLIDE_E_ARG, "rmsnorm_bwd: null pointer");
+  SLIDE_REQUIRE(dy != dx, SLIDE_E_ARG, "rmsnorm_bwd: dx must not alias dy");
+  return rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ws, (hipStream_t)stream);
+}
+
+extern "C" int slide_rope(void* qkv, int B, int S, int nq, int nkv, int d, float theta,
+                          int inverse, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(attention_check(B, S, nq, nkv, d, dtype));
+  SLIDE_REQUIRE(theta > 0.f, SLIDE_E_ARG, "rope: theta must be > 0");
+  const size_t need = 2 * align_up((size_t)S * (d / 2) * 4, 256);
+  SLIDE_REQUIRE(ws && ws_bytes >= need, SLIDE_E_WORKSPACE, "rope: workspace %zu < %zu", ws_bytes, need);
+  if ((size_t)B * S == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(qkv, SLIDE_E_ARG, "rope: null qkv");
+  Carver c(ws);
+  float* cs = c.take<float>((size_t)S * (d / 2));
+  float* sn = c.take<float>((size_t)S * (d / 2));
+  SLIDE_TRY(rope_tables(cs, sn, S, d, theta, (hipStream_t)stream));
+  return rope_apply(qkv, cs, sn, B, S, nq, nkv, d, inverse, dtype, (hipStream_t)stream);
+}
+
+extern "C" int slide_embed_fwd(const void* E, const int32_t* tokens, void* x, int N, int H, int V,
+                               int dtype, void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "embed: bad dtype");
+  SLIDE_REQUIRE(N >= 0 && V > 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "embed: bad sizes N %d H %d V %d", N, H, V);
+  if (N == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(E && tokens && x && aligned16(E) && aligned16(x), SLIDE_E_ARG, "embed: null or misaligned pointer");
+  return embed_fwd(E, tokens, x, N, H, V, dtype, (hipStream_t)stream);
+}
+
+extern "C" size_t slide_embed_bwd_workspace_bytes(int N, int V) { return embed_bwd_ws(N < 0 ? 0 : N, V); }
+
+extern "C" int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,
+                               int dtype, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "embed_bwd: bad dtype");
+  SLIDE_REQUIRE(N >= 0 && N <= (1 << 30) && V > 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE,
+                "embed_bwd: bad sizes N %d H %d V %d", N, H, V);
+  SLIDE_REQUIRE(ws && ws_bytes >= embed_bwd_ws(N, V), SLIDE_E_WORKSPACE, "embed_bwd: workspace %zu < %zu",
+                ws_bytes, embed_bwd_ws(N, V));
+  SLIDE_REQUIRE(dE && aligned16(dE) && (N == 0 || (dx && tokens && aligned16(dx))), SLIDE_E_ARG,
+                "embed_bwd: null or misaligned pointer");
+  return embed_bwd(dx, tokens, dE, N, H, V, dtype, ws, (hipStream_t)stream);
+}

@@ -1,0 +1,497 @@
+// Memory-bound kernels of the layer and the model glue: RMSNorm forward/backward, RoPE,
+// SwiGLU forward/backward, token embedding gather and its deterministic backward, plus small
+// fill/convert helpers. The pages name RoPE, RMSNorm and SwiGLU as the kernels their system
+// rewrote (SlideFormer summary, section 2C); the formulas are the standard ones for the Llama
+// family the summary names in section 4.
+//
+// Layout: rows of H (or 2F) contiguous elements; one 64-lane wavefront per row for the row
+// reductions, 16-byte vector accesses (8 bf16 or 2x4 fp32) so every wave reads whole 128-byte
+// lines. All arithmetic is fp32; bf16 is converted on load and rounded (nearest-even) on store.
+#include "pointwise.h"
+
+namespace slide {
+namespace {
+
+// ---------------------------------------------------------------- 8-element vector I/O
+template <typename T> struct V8;
+template <> struct V8<bf16_t> {
+  __device__ __forceinline__ static void load(const bf16_t* p, float (&v)[8]) {
+    uint4 u = *(const uint4*)p;
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct V8<float> {
+  __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
+    float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[8]) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// ---------------------------------------------------------------- RMSNorm
+// y = w * x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row, 4 rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ x,
+                                                          const T* __restrict__ w,
+                                                          T* __restrict__ y, float* rstd,
+                                                          int N, int H, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const T* xr = x + (size_t)row * H;
+  float ss = 0.f;
+  for (int c = lane * 8; c < H; c += 512) {
+    float v[8];
+    V8<T>::load(xr + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  }
+  ss = warp_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (rstd && lane == 0) rstd[row] = r;
+  T* yr = y + (size_t)row * H;
+  for (int c = lane * 8; c < H; c += 512) {
+    float v[8], g[8];
+    V8<T>::load(xr + c, v);
+    V8<T>::load(w + c, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = g[i] * (v[i] * r);
+    V8<T>::store(yr + c, v);
+  }
+}
+
+// dx = dres + r*g - (r^3/H) * x * sum(g*x), g = w*dy; also stores r per row for the dw pass.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy,
+                                                          const T* __restrict__ x,
+                                                          const T* __restrict__ w,
+                                                          const T* dres, T* dx, float* rstd,
+                                                          int N, int H, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const T* xr = x + (size_t)row * H;
+  const T* dyr = dy + (size_t)row * H;
+  float ss = 0.f, gx = 0.f;
+  for (int c = lane * 8; c < H; c += 512) {
+    float xv[8], dv[8], wv[8];
+    V8<T>::load(xr + c, xv);
+    V8<T>::load(dyr + c, dv);
+    V8<T>::load(w + c, wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ss += xv[i] * xv[i];
+      gx += (wv[i] * dv[i]) * xv[i];
+    }
+  }
+  ss = warp_sum(ss);
+  gx = warp_sum(gx);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  const float coef = r * r * r * gx / (float)H;
+  if (lane == 0) rstd[row] = r;
+  T* dxr = dx + (size_t)row * H;
+  const T* drr = dres ? dres + (size_t)row * H : nullptr;
+  for (int c = lane * 8; c < H; c += 512) {
+    float xv[8], dv[8], wv[8], o[8];
+    V8<T>::load(xr + c, xv);
+    V8<T>::load(dyr + c, dv);
+    V8<T>::load(w + c, wv);
+    if (drr) V8<T>::load(drr + c, o);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] += r * (wv[i] * dv[i]) - coef * xv[i];
+    V8<T>::store(dxr + c, o);
+  }
+}
+
+// dw partials: part[rb][j] = sum over rows of block rb of dy*x*r (rows in increasing order).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_dw_partial_kernel(const T* __restrict__ dy,
+                                                                 const T* __restrict__ x,
+                                                                 const float* __restrict__ rstd,
+                                                                 float* __restrict__ part, int N,
+                                                                 int H, int rows_per_block) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= H) return;
+  const int r0 = blockIdx.y * rows_per_block, r1 = min(N, r0 + rows_per_block);
+  float acc = 0.f;
+  for (int t = r0; t < r1; ++t)
+    acc += Elem<T>::load(dy + (size_t)t * H + j) * Elem<T>::load(x + (size_t)t * H + j) * rstd[t];
+  part[(size_t)blockIdx.y * H + j] = acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, T* out,
+                                                          int nparts, int H) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= H) return;
+  float acc = 0.f;
+  for (int p = 0; p < nparts; ++p) acc += part[(size_t)p * H + j];
+  Elem<T>::store(out + j, acc);
+}
+
+// ---------------------------------------------------------------- RoPE
+__global__ void rope_table_kernel(float* cos_t, float* sin_t, int S, int half, int d, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= S * half) return;
+  const int s = idx / half, i = idx % half;
+  const double inv = pow(theta, -2.0 * (double)i / (double)d);
+  const double a = (double)s * inv;
+  cos_t[idx] = (float)cos(a);
+  sin_t[idx] = (float)sin(a);
+}
+
+// One thread per rotation pair (i, i + d/2) of one (token, head) of the q and k parts.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T* qkv, const float* __restrict__ cos_t,
+                                                   const float* __restrict__ sin_t, int N, int S,
+                                                   int heads, int d, int row_stride, float sgn) {
+  const int half = d >> 1;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)N * heads * half;
+  if (idx >= total) return;
+  const int i = (int)(idx % half);
+  const size_t th = idx / half;
+  const int h = (int)(th % heads);
+  const int t = (int)(th / heads);
+  const int s = t % S;
+  T* p = qkv + (size_t)t * row_stride + (size_t)h * d;
+  const float c = cos_t[s * half + i], sn = sgn * sin_t[s * half + i];
+  const float x1 = Elem<T>::load(p + i), x2 = Elem<T>::load(p + i + half);
+  Elem<T>::store(p + i, x1 * c - x2 * sn);
+  Elem<T>::store(p + i + half, x2 * c + x1 * sn);
+}
+
+// ---------------------------------------------------------------- SwiGLU
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const T* __restrict__ gu,
+                                                         T* __restrict__ m, int N, int F) {
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (idx >= (size_t)N * F) return;
+  const size_t t = idx / F, j = idx % F;
+  float g[8], u[8], o[8];
+  V8<T>::load(gu + t * 2 * F + j, g);
+  V8<T>::load(gu + t * 2 * F + F + j, u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = g[i] * sigmoidf_(g[i]) * u[i];
+  V8<T>::store(m + idx, o);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ dm,
+                                                         const T* __restrict__ gu,
+                                                         T* __restrict__ dgu, int N, int F) {
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (idx >= (size_t)N * F) return;
+  const size_t t = idx / F, j = idx % F;
+  float g[8], u[8], d[8], dg[8], du[8];
+  V8<T>::load(gu + t * 2 * F + j, g);
+  V8<T>::load(gu + t * 2 * F + F + j, u);
+  V8<T>::load(dm + idx, d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sg = sigmoidf_(g[i]);
+    du[i] = d[i] * g[i] * sg;
+    dg[i] = d[i] * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
+  }
+  V8<T>::store(dgu + t * 2 * F + j, dg);
+  V8<T>::store(dgu + t * 2 * F + F + j, du);
+}
+
+// ---------------------------------------------------------------- embedding
+template <typename T>
+__global__ __launch_bounds__(256) void embed_fwd_kernel(const T* __restrict__ E,
+                                                        const int32_t* __restrict__ tok,
+                                                        T* __restrict__ x, int N, int H, int V) {
+  const int row = blockIdx.x;
+  const int v = tok[row];
+  T* xr = x + (size_t)row * H;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float o[8];
+    if (v >= 0 && v < V) V8<T>::load(E + (size_t)v * H + c, o);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = 0.f;
+    V8<T>::store(xr + c, o);
+  }
+}
+
+// keys[t] = (token << 32) | t for valid tokens, all-ones for padding and invalid tokens
+__global__ void embed_keys_kernel(const int32_t* __restrict__ tok, uint64_t* keys, int N, int P,
+                                  int V) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= P) return;
+  uint64_t k = ~0ull;
+  if (t < N) {
+    int v = tok[t];
+    if (v >= 0 && v < V) k = ((uint64_t)(uint32_t)v << 32) | (uint32_t)t;
+  }
+  keys[t] = k;
+}
+
+// one compare-exchange stage of a bitonic sort over P = 2^p keys (ascending)
+__global__ void bitonic_step_kernel(uint64_t* keys, int P, int j, int k) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P) return;
+  const int l = i ^ j;
+  if (l > i) {
+    const uint64_t a = keys[i], b = keys[l];
+    const bool up = (i & k) == 0;
+    if ((a > b) == up) {
+      keys[i] = b;
+      keys[l] = a;
+    }
+  }
+}
+
+// dE[v] = sum of dx rows of the positions holding token v, in position order.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_sum_kernel(const T* __restrict__ dx,
+                                                        const uint64_t* __restrict__ keys, int P,
+                                                        T* __restrict__ dE, int H) {
+  const uint32_t v = blockIdx.x;
+  // lower bound of (v << 32) in the sorted keys
+  int lo = 0, hi = P;
+  const uint64_t target = (uint64_t)v << 32;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (keys[mid] < target) lo = mid + 1;
+    else hi = mid;
+  }
+  T* out = dE + (size_t)v * H;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int p = lo; p < P && (uint32_t)(keys[p] >> 32) == v; ++p) {
+      const uint32_t t = (uint32_t)keys[p];
+      float r[8];
+      V8<T>::load(dx + (size_t)t * H + c, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += r[i];
+    }
+    V8<T>::store(out + c, acc);
+  }
+}
+
+// ---------------------------------------------------------------- helpers
+__global__ void fill_f32_kernel(float* p, size_t n, float v) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+template <typename T>
+__global__ void convert_f32_kernel(const float* __restrict__ src, T* __restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) Elem<T>::store(dst + i, src[i]);
+}
+
+inline unsigned blocks_for(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------ launchers
+int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int N, int H, float eps,
+                int dtype, hipStream_t st) {
+  if (N == 0) return SLIDE_OK;
+  ProfScope ps("rmsnorm_fwd", st);
+  dim3 grid(blocks_for(N, 4)), block(256);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)x,
+                       (const bf16_t*)w, (bf16_t*)y, rstd, N, H, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, block, 0, st, (const float*)x,
+                       (const float*)w, (float*)y, rstd, N, H, eps);
+  return check_launch("rmsnorm_fwd");
+}
+
+size_t rmsnorm_bwd_ws(int N, int H) {
+  const int parts = (N + kRmsRowsPerPart - 1) / kRmsRowsPerPart;
+  return align_up((size_t)N * 4, 256) + align_up((size_t)parts * H * 4, 256);
+}
+
+int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, void* dx,
+                void* dw, int N, int H, float eps, int dtype, void* ws, hipStream_t st) {
+  Carver cv(ws);
+  float* rstd = cv.take<float>((size_t)N);
+  const int parts = (N + kRmsRowsPerPart - 1) / kRmsRowsPerPart;
+  float* part = cv.take<float>((size_t)std::max(parts, 1) * H);
+  {
+    ProfScope ps("rmsnorm_bwd", st);
+    if (N > 0) {
+      dim3 grid(blocks_for(N, 4)), block(256);
+      if (dtype == SLIDE_BF16)
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)dy,
+                           (const bf16_t*)x, (const bf16_t*)w, (const bf16_t*)dres, (bf16_t*)dx,
+                           rstd, N, H, eps);
+      else
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, block, 0, st, (const float*)dy,
+                           (const float*)x, (const float*)w, (const float*)dres, (float*)dx,
+                           rstd, N, H, eps);
+    }
+  }
+  SLIDE_TRY(check_launch("rmsnorm_bwd"));
+  if (!dw) return SLIDE_OK;
+  ProfScope ps("rmsnorm_dw", st);
+  if (N == 0) {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(H, 256)), dim3(256), 0, st, part, (size_t)H, 0.f);
+  } else {
+    dim3 g1(blocks_for(H, 256), parts), b1(256);
+    if (dtype == SLIDE_BF16)
+      hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<bf16_t>, g1, b1, 0, st, (const bf16_t*)dy,
+                         (const bf16_t*)x, rstd, part, N, H, kRmsRowsPerPart);
+    else
+      hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<float>, g1, b1, 0, st, (const float*)dy,
+                         (const float*)x, rstd, part, N, H, kRmsRowsPerPart);
+  }
+  dim3 g2(blocks_for(H, 256)), b2(256);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(reduce_rows_kernel<bf16_t>, g2, b2, 0, st, part, (bf16_t*)dw,
+                       std::max(parts, 1), H);
+  else
+    hipLaunchKernelGGL(reduce_rows_kernel<float>, g2, b2, 0, st, part, (float*)dw,
+                       std::max(parts, 1), H);
+  return check_launch("rmsnorm_dw");
+}
+
+int rope_tables(float* cos_t, float* sin_t, int S, int d, float theta, hipStream_t st) {
+  ProfScope ps("rope_table", st);
+  const int half = d / 2;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for((size_t)S * half, 256)), dim3(256), 0, st,
+                     cos_t, sin_t, S, half, d, (double)theta);
+  return check_launch("rope_table");
+}
+
+int rope_apply(void* qkv, const float* cos_t, const float* sin_t, int B, int S, int nq, int nkv,
+               int d, int inverse, int dtype, hipStream_t st) {
+  const int N = B * S, heads = nq + nkv, stride = (nq + 2 * nkv) * d;
+  const size_t total = (size_t)N * heads * (d / 2);
+  if (total == 0) return SLIDE_OK;
+  ProfScope ps(inverse ? "rope_bwd" : "rope_fwd", st);
+  const float sgn = inverse ? -1.f : 1.f;
+  dim3 grid(blocks_for(total, 256)), block(256);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, block, 0, st, (bf16_t*)qkv, cos_t, sin_t, N, S,
+                       heads, d, stride, sgn);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, block, 0, st, (float*)qkv, cos_t, sin_t, N, S,
+                       heads, d, stride, sgn);
+  return check_launch("rope");
+}
+
+int swiglu_fwd(const void* gu, void* m, int N, int F, int dtype, hipStream_t st) {
+  const size_t n8 = (size_t)N * F / 8;
+  if (n8 == 0) return SLIDE_OK;
+  ProfScope ps("swiglu_fwd", st);
+  dim3 grid(blocks_for(n8, 256)), block(256);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(swiglu_fwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)gu, (bf16_t*)m, N, F);
+  else
+    hipLaunchKernelGGL(swiglu_fwd_kernel<float>, grid, block, 0, st, (const float*)gu, (float*)m, N, F);
+  return check_launch("swiglu_fwd");
+}
+
+int swiglu_bwd(const void* dm, const void* gu, void* dgu, int N, int F, int dtype, hipStream_t st) {
+  const size_t n8 = (size_t)N * F / 8;
+  if (n8 == 0) return SLIDE_OK;
+  ProfScope ps("swiglu_bwd", st);
+  dim3 grid(blocks_for(n8, 256)), block(256);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(swiglu_bwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)dm,
+                       (const bf16_t*)gu, (bf16_t*)dgu, N, F);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_kernel<float>, grid, block, 0, st, (const float*)dm,
+                       (const float*)gu, (float*)dgu, N, F);
+  return check_launch("swiglu_bwd");
+}
+
+int embed_fwd(const void* E, const int32_t* tok, void* x, int N, int H, int V, int dtype,
+              hipStream_t st) {
+  if (N == 0) return SLIDE_OK;
+  ProfScope ps("embed_fwd", st);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(embed_fwd_kernel<bf16_t>, dim3(N), dim3(256), 0, st, (const bf16_t*)E, tok,
+                       (bf16_t*)x, N, H, V);
+  else
+    hipLaunchKernelGGL(embed_fwd_kernel<float>, dim3(N), dim3(256), 0, st, (const float*)E, tok,
+                       (float*)x, N, H, V);
+  return check_launch("embed_fwd");
+}
+
+static int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+size_t embed_bwd_ws(int N, int V) {
+  (void)V;
+  return align_up((size_t)pow2_at_least(std::max(N, 1)) * 8, 256);
+}
+
+int embed_bwd(const void* dx, const int32_t* tok, void* dE, int N, int H, int V, int dtype,
+              void* ws, hipStream_t st) {
+  ProfScope ps("embed_bwd", st);
+  const int P = pow2_at_least(std::max(N, 1));
+  uint64_t* keys = (uint64_t*)ws;
+  hipLaunchKernelGGL(embed_keys_kernel, dim3(blocks_for(P, 256)), dim3(256), 0, st, tok, keys, N,
+                     P, V);
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1)
+      hipLaunchKernelGGL(bitonic_step_kernel, dim3(blocks_for(P, 256)), dim3(256), 0, st, keys, P,
+                         j, k);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, dim3(V), dim3(256), 0, st, (const bf16_t*)dx,
+                       keys, P, (bf16_t*)dE, H);
+  else
+    hipLaunchKernelGGL(embed_sum_kernel<float>, dim3(V), dim3(256), 0, st, (const float*)dx, keys,
+                       P, (float*)dE, H);
+  return check_launch("embed_bwd");
+}
+
+int fill_zero(void* p, size_t n, int dtype, hipStream_t st) {
+  if (n == 0) return SLIDE_OK;
+  if (dtype == SLIDE_BF16) {
+    // bf16 zero is the all-zero bit pattern: fill as fp32 words plus a possible odd tail
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n / 2, 256)), dim3(256), 0, st, (float*)p, n / 2, 0.f);
+    if (n & 1)
+      hipLaunchKernelGGL(convert_f32_kernel<bf16_t>, dim3(1), dim3(1), 0, st, (const float*)p, (bf16_t*)p + (n - 1), (size_t)1);
+  } else {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, (float*)p, n, 0.f);
+  }
+  return check_launch("fill_zero");
+}
+
+int fill_f32(float* p, size_t n, float v, hipStream_t st) {
+  if (n == 0) return SLIDE_OK;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, p, n, v);
+  return check_launch("fill");
+}
+
+int convert_from_f32(const float* src, void* dst, size_t n, int dtype, hipStream_t st) {
+  if (n == 0) return SLIDE_OK;
+  ProfScope ps("convert_f32", st);
+  if (dtype == SLIDE_BF16)
+    hipLaunchKernelGGL(convert_f32_kernel<bf16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, st, src,
+                       (bf16_t*)dst, n);
+  else
+    hipLaunchKernelGGL(convert_f32_kernel<float>, dim3(blocks_for(n, 256)), dim3(256), 0, st, src,
+                       (float*)dst, n);
+  return check_launch("convert_f32");
+}
+
+}  // namespace slide

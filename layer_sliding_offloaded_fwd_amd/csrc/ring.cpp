@@ -1,0 +1,456 @@
+// Slot ring: the pre-allocated GPU cache queue of the layer-sliding method (SlideFormer
+// summary, section 2B: a fixed set of identical buffers holding only the active layers'
+// parameters and gradients, each reused as soon as it is free, so nothing is allocated while
+// training; section 2A: gradients leave asynchronously while the next layer computes and the
+// layer after that is prefetched, on transfer streams separate from the compute stream).
+//
+// All ordering is expressed with events so that the host never blocks on the GPU except in
+// slide_slot_ring_wait_flush (the CPU optimizer needs the gradients in host memory):
+//   load     copy stream waits for the slot's last release event, then copies the weights
+//   acquire  compute stream waits for the load and for any flush still reading the slot
+//   flush    copy stream waits for the compute stream, then copies the gradients out
+//   release  records an event on the compute stream (the next load into the slot waits on it)
+// The host engine runs the same state machine on host memory with a copy thread, so the
+// bookkeeping and its failure paths can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+#include <chrono>
+#include <condition_variable>
+#include <deque>
+#include <functional>
+#include <memory>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "../../include/slide.h"
+
+namespace slide {
+int fail(int code, const char* fmt, ...);
+}
+using slide::fail;
+
+namespace {
+
+constexpr int kTicketPool = 1024;
+
+// ------------------------------------------------------------------ host engine pieces
+struct HostEvent {
+  std::atomic<int> st{1};  // 0 pending, 1 done, 2 failed
+};
+
+struct HostCopyQueue {
+  struct Job {
+    std::vector<std::shared_ptr<HostEvent>> waits;
+    void* dst;
+    const void* src;
+    size_t n;
+    std::shared_ptr<HostEvent> done;
+    int fault;  // 0 none, 1 fail, 2 never complete
+  };
+  std::mutex mu;
+  std::condition_variable cv;
+  std::deque<Job> q;
+  bool stop = false;
+  std::thread th;
+
+  HostCopyQueue() { th = std::thread([this] { run(); }); }
+  ~HostCopyQueue() {
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      stop = true;
+    }
+    cv.notify_all();
+    th.join();
+  }
+  void push(Job j) {
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      q.push_back(std::move(j));
+    }
+    cv.notify_all();
+  }
+  void run() {
+    for (;;) {
+      Job j;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv.wait(lk, [&] { return stop || !q.empty(); });
+        if (stop && q.empty()) return;
+        j = std::move(q.front());
+        q.pop_front();
+      }
+      bool dep_failed = false;
+      for (auto& w : j.waits) {
+        // a dependency that never completes stalls this queue, as a GPU stream would
+        while (w->st.load() == 0) {
+          {
+            std::lock_guard<std::mutex> lk(mu);
+            if (stop) return;
+          }
+          std::this_thread::sleep_for(std::chrono::microseconds(100));
+        }
+        if (w->st.load() == 2) dep_failed = true;
+      }
+      if (j.fault == 2) continue;  // never completes
+      if (j.fault == 1 || dep_failed) {
+        j.done->st.store(2);
+        continue;
+      }
+      memcpy(j.dst, j.src, j.n);
+      j.done->st.store(1);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ slot
+struct Ev {
+  hipEvent_t hip = nullptr;
+  std::shared_ptr<HostEvent> host;
+  bool valid = false;
+};
+
+struct Slot {
+  int state = SLIDE_SLOT_FREE;
+  int layer = -1;
+  bool content_valid = false;
+  uint64_t released_at = 0;
+  Ev load_ev, free_ev, flush_ev;
+};
+
+}  // namespace
+
+struct slide_ring {
+  int n = 0;
+  size_t wb = 0, gb = 0;
+  char* base = nullptr;
+  hipStream_t h2d = nullptr, d2h = nullptr;
+  int engine = SLIDE_ENGINE_HIP;
+  std::vector<Slot> slots;
+  uint64_t clock = 1;
+  std::mutex mu;
+  // flush tickets
+  uint64_t next_ticket = 1;
+  std::vector<Ev> ticket_ev;
+  std::vector<uint64_t> ticket_id;
+  // host engine
+  std::unique_ptr<HostCopyQueue> hq_h2d, hq_d2h;
+  int fault_mode = 0, fault_count = 0;
+
+  char* w_ptr(int s) { return base + (size_t)s * (wb + gb); }
+  char* g_ptr(int s) { return base + (size_t)s * (wb + gb) + wb; }
+
+  int take_fault() {
+    if (fault_count <= 0) return 0;
+    --fault_count;
+    return fault_mode;
+  }
+
+  // record an event "now" on a compute stream (host engine: host compute is synchronous)
+  int record_compute(Ev& e, void* stream) {
+    if (engine == SLIDE_ENGINE_HOST) {
+      e.host = std::make_shared<HostEvent>();
+      e.valid = true;
+      return SLIDE_OK;
+    }
+    if (!e.hip && hipEventCreateWithFlags(&e.hip, hipEventDisableTiming) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring: hipEventCreate failed");
+    if (hipEventRecord(e.hip, (hipStream_t)stream) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring: hipEventRecord failed");
+    e.valid = true;
+    return SLIDE_OK;
+  }
+
+  // host wait for an event with a deadline (ms < 0: no limit)
+  int host_wait(const Ev& e, int timeout_ms, const char* what) {
+    if (!e.valid) return SLIDE_OK;
+    auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+      int st;
+      if (engine == SLIDE_ENGINE_HOST) {
+        st = e.host->st.load();
+        if (st == 2) return fail(SLIDE_E_HIP, "slot ring: %s: copy failed", what);
+        if (st == 1) return SLIDE_OK;
+      } else {
+        hipError_t q = hipEventQuery(e.hip);
+        if (q == hipSuccess) return SLIDE_OK;
+        if (q != hipErrorNotReady)
+          return fail(SLIDE_E_HIP, "slot ring: %s: %s", what, hipGetErrorString(q));
+      }
+      if (timeout_ms >= 0) {
+        auto el = std::chrono::duration_cast<std::chrono::milliseconds>(
+                      std::chrono::steady_clock::now() - t0).count();
+        if (el >= timeout_ms)
+          return fail(SLIDE_E_TIMEOUT, "slot ring: %s: no completion after %d ms", what,
+                      timeout_ms);
+      }
+      std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+  }
+};
+
+namespace {
+int check_ring(slide_ring* r, int slot) {
+  if (!r) return fail(SLIDE_E_ARG, "slot ring: null handle");
+  if (slot < 0 || slot >= r->n) return fail(SLIDE_E_ARG, "slot ring: slot %d out of range", slot);
+  return SLIDE_OK;
+}
+const char* state_name(int s) {
+  switch (s) {
+    case SLIDE_SLOT_FREE: return "FREE";
+    case SLIDE_SLOT_LOADING: return "LOADING";
+    case SLIDE_SLOT_IN_USE: return "IN_USE";
+    case SLIDE_SLOT_FLUSHING: return "FLUSHING";
+  }
+  return "?";
+}
+}  // namespace
+
+extern "C" int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_bytes,
+                                      size_t g_bytes, void* dev_base, void* h2d_stream,
+                                      void* d2h_stream, int engine) {
+  if (!out || !dev_base) return fail(SLIDE_E_ARG, "slot ring create: null pointer");
+  if (n_slots < 1 || n_slots > 4096) return fail(SLIDE_E_ARG, "slot ring create: n_slots %d", n_slots);
+  if (w_bytes == 0) return fail(SLIDE_E_ARG, "slot ring create: w_bytes must be > 0");
+  if ((w_bytes % 256) || (g_bytes % 256))
+    return fail(SLIDE_E_ARG, "slot ring create: w_bytes and g_bytes must be multiples of 256");
+  if (engine != SLIDE_ENGINE_HIP && engine != SLIDE_ENGINE_HOST)
+    return fail(SLIDE_E_ARG, "slot ring create: unknown engine %d", engine);
+  auto* r = new slide_ring();
+  r->n = n_slots;
+  r->wb = w_bytes;
+  r->gb = g_bytes;
+  r->base = (char*)dev_base;
+  r->h2d = (hipStream_t)h2d_stream;
+  r->d2h = (hipStream_t)d2h_stream;
+  r->engine = engine;
+  r->slots.resize(n_slots);
+  r->ticket_ev.resize(kTicketPool);
+  r->ticket_id.assign(kTicketPool, 0);
+  if (engine == SLIDE_ENGINE_HOST) {
+    r->hq_h2d.reset(new HostCopyQueue());
+    r->hq_d2h.reset(new HostCopyQueue());
+  }
+  *out = r;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot_out) {
+  if (!r || !host_w || !slot_out) return fail(SLIDE_E_ARG, "slot ring load: null pointer");
+  std::lock_guard<std::mutex> lk(r->mu);
+  int best = -1;
+  for (int s = 0; s < r->n; ++s)
+    if (r->slots[s].state == SLIDE_SLOT_FREE &&
+        (best < 0 || r->slots[s].released_at < r->slots[best].released_at))
+      best = s;
+  if (best < 0) return fail(SLIDE_E_STATE, "slot ring load(layer %d): no FREE slot", layer);
+  Slot& sl = r->slots[best];
+  if (r->engine == SLIDE_ENGINE_HOST) {
+    HostCopyQueue::Job j;
+    if (sl.free_ev.valid) j.waits.push_back(sl.free_ev.host);
+    j.dst = r->w_ptr(best);
+    j.src = host_w;
+    j.n = r->wb;
+    j.done = std::make_shared<HostEvent>();
+    j.done->st.store(0);
+    j.fault = r->take_fault();
+    sl.load_ev.host = j.done;
+    sl.load_ev.valid = true;
+    r->hq_h2d->push(std::move(j));
+  } else {
+    if (sl.free_ev.valid && hipStreamWaitEvent(r->h2d, sl.free_ev.hip, 0) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring load: hipStreamWaitEvent failed");
+    hipError_t e = hipMemcpyAsync(r->w_ptr(best), host_w, r->wb, hipMemcpyHostToDevice, r->h2d);
+    if (e != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring load: hipMemcpyAsync: %s", hipGetErrorString(e));
+    if (!sl.load_ev.hip &&
+        hipEventCreateWithFlags(&sl.load_ev.hip, hipEventDisableTiming) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring load: hipEventCreate failed");
+    if (hipEventRecord(sl.load_ev.hip, r->h2d) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring load: hipEventRecord failed");
+    sl.load_ev.valid = true;
+  }
+  sl.state = SLIDE_SLOT_LOADING;
+  sl.layer = layer;
+  sl.content_valid = true;
+  *slot_out = best;
+  return SLIDE_OK;
+}
+
+// Re-claim a FREE slot whose weights still hold `layer` (nothing was loaded over them since),
+// without copying. SLIDE_E_STATE if there is none.
+extern "C" int slide_slot_ring_reuse(slide_ring* r, int layer, int* slot_out) {
+  if (!r || !slot_out) return fail(SLIDE_E_ARG, "slot ring reuse: null pointer");
+  std::lock_guard<std::mutex> lk(r->mu);
+  for (int s = 0; s < r->n; ++s) {
+    Slot& sl = r->slots[s];
+    if (sl.state == SLIDE_SLOT_FREE && sl.content_valid && sl.layer == layer) {
+      sl.state = SLIDE_SLOT_LOADING;  // its load event (already complete) still orders it
+      *slot_out = s;
+      return SLIDE_OK;
+    }
+  }
+  return fail(SLIDE_E_STATE, "slot ring reuse: no FREE slot holds layer %d", layer);
+}
+
+extern "C" int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_stream,
+                                       void** w_dev, void** g_dev) {
+  int rc = check_ring(r, slot);
+  if (rc) return rc;
+  std::unique_lock<std::mutex> lk(r->mu);
+  Slot& sl = r->slots[slot];
+  if (sl.state != SLIDE_SLOT_LOADING)
+    return fail(SLIDE_E_STATE, "slot ring acquire: slot %d is %s, expected LOADING", slot,
+                state_name(sl.state));
+  if (r->engine == SLIDE_ENGINE_HOST) {
+    Ev le = sl.load_ev, fe = sl.flush_ev;
+    lk.unlock();
+    // host compute runs synchronously, so the stream-side wait becomes a bounded host wait
+    rc = r->host_wait(le, 10000, "acquire (load)");
+    if (rc == SLIDE_OK) rc = r->host_wait(fe, 10000, "acquire (pending flush)");
+    if (rc) return rc;
+    lk.lock();
+  } else {
+    if (sl.load_ev.valid &&
+        hipStreamWaitEvent((hipStream_t)compute_stream, sl.load_ev.hip, 0) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring acquire: hipStreamWaitEvent failed");
+    if (sl.flush_ev.valid &&
+        hipStreamWaitEvent((hipStream_t)compute_stream, sl.flush_ev.hip, 0) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring acquire: hipStreamWaitEvent failed");
+  }
+  sl.state = SLIDE_SLOT_IN_USE;
+  if (w_dev) *w_dev = r->w_ptr(slot);
+  if (g_dev) *g_dev = r->gb ? r->g_ptr(slot) : nullptr;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
+                                     uint64_t* ticket) {
+  int rc = check_ring(r, slot);
+  if (rc) return rc;
+  if (!host_g || !ticket) return fail(SLIDE_E_ARG, "slot ring flush: null pointer");
+  std::lock_guard<std::mutex> lk(r->mu);
+  Slot& sl = r->slots[slot];
+  if (r->gb == 0) return fail(SLIDE_E_STATE, "slot ring flush: ring has no gradient region");
+  if (sl.state != SLIDE_SLOT_IN_USE)
+    return fail(SLIDE_E_STATE, "slot ring flush: slot %d is %s, expected IN_USE", slot,
+                state_name(sl.state));
+  uint64_t t = r->next_ticket++;
+  Ev& te = r->ticket_ev[t % kTicketPool];
+  if (r->engine == SLIDE_ENGINE_HOST) {
+    HostCopyQueue::Job j;
+    j.dst = host_g;
+    j.src = r->g_ptr(slot);
+    j.n = r->gb;
+    j.done = std::make_shared<HostEvent>();
+    j.done->st.store(0);
+    j.fault = r->take_fault();
+    te.host = j.done;
+    te.valid = true;
+    r->hq_d2h->push(std::move(j));
+  } else {
+    Ev cdone;
+    if ((rc = r->record_compute(cdone, compute_stream))) return rc;
+    hipError_t e = hipStreamWaitEvent(r->d2h, cdone.hip, 0);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(host_g, r->g_ptr(slot), r->gb, hipMemcpyDeviceToHost, r->d2h);
+    if (e == hipSuccess && !te.hip)
+      e = hipEventCreateWithFlags(&te.hip, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(te.hip, r->d2h);
+    hipEventDestroy(cdone.hip);  // destruction is deferred by HIP until the event completes
+    if (e != hipSuccess) return fail(SLIDE_E_HIP, "slot ring flush: %s", hipGetErrorString(e));
+    te.valid = true;
+  }
+  r->ticket_id[t % kTicketPool] = t;
+  sl.flush_ev = te;
+  sl.state = SLIDE_SLOT_FLUSHING;
+  *ticket = t;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_wait_flush(slide_ring* r, uint64_t ticket, int timeout_ms) {
+  if (!r) return fail(SLIDE_E_ARG, "slot ring wait_flush: null handle");
+  Ev e;
+  {
+    std::lock_guard<std::mutex> lk(r->mu);
+    if (ticket == 0 || ticket >= r->next_ticket)
+      return fail(SLIDE_E_ARG, "slot ring wait_flush: unknown ticket %llu",
+                  (unsigned long long)ticket);
+    // If the pool entry was reused by a later flush, waiting on the later one is a safe
+    // over-wait: copies on the d2h queue complete in order.
+    e = r->ticket_ev[ticket % kTicketPool];
+  }
+  return r->host_wait(e, timeout_ms, "wait_flush");
+}
+
+extern "C" int slide_slot_ring_release(slide_ring* r, int slot, void* compute_stream) {
+  int rc = check_ring(r, slot);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(r->mu);
+  Slot& sl = r->slots[slot];
+  if (sl.state != SLIDE_SLOT_IN_USE && sl.state != SLIDE_SLOT_FLUSHING)
+    return fail(SLIDE_E_STATE, "slot ring release: slot %d is %s, expected IN_USE or FLUSHING",
+                slot, state_name(sl.state));
+  if ((rc = r->record_compute(sl.free_ev, compute_stream))) return rc;
+  sl.state = SLIDE_SLOT_FREE;
+  sl.released_at = r->clock++;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_state(slide_ring* r, int slot, int* state, int* layer) {
+  int rc = check_ring(r, slot);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(r->mu);
+  if (state) *state = r->slots[slot].state;
+  if (layer) *layer = r->slots[slot].layer;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_find(slide_ring* r, int layer, int* slot_out) {
+  if (!r || !slot_out) return fail(SLIDE_E_ARG, "slot ring find: null pointer");
+  std::lock_guard<std::mutex> lk(r->mu);
+  *slot_out = -1;
+  for (int s = 0; s < r->n; ++s)
+    if (r->slots[s].state != SLIDE_SLOT_FREE && r->slots[s].layer == layer) *slot_out = s;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_inject_fault(slide_ring* r, int fail_mode, int count) {
+  if (!r) return fail(SLIDE_E_ARG, "slot ring inject_fault: null handle");
+  if (r->engine != SLIDE_ENGINE_HOST)
+    return fail(SLIDE_E_UNSUPPORTED, "slot ring inject_fault: host engine only");
+  if (fail_mode < 0 || fail_mode > 2 || count < 0)
+    return fail(SLIDE_E_ARG, "slot ring inject_fault: bad mode %d / count %d", fail_mode, count);
+  std::lock_guard<std::mutex> lk(r->mu);
+  r->fault_mode = fail_mode;
+  r->fault_count = count;
+  return SLIDE_OK;
+}
+
+extern "C" int slide_slot_ring_destroy(slide_ring* r) {
+  if (!r) return fail(SLIDE_E_ARG, "slot ring destroy: null handle");
+  if (r->engine == SLIDE_ENGINE_HIP) {
+    auto drop = [](Ev& e) {
+      if (e.hip) hipEventDestroy(e.hip);
+      e.hip = nullptr;
+    };
+    for (auto& s : r->slots) {
+      drop(s.load_ev);
+      drop(s.free_ev);
+    }
+    for (auto& e : r->ticket_ev) drop(e);
+  } else {
+    // copies that can never complete (injected faults) would stall the copy threads forever;
+    // mark every pending event failed so the threads can drain and exit
+    for (auto& s : r->slots) {
+      for (Ev* e : {&s.load_ev, &s.free_ev, &s.flush_ev})
+        if (e->host && e->host->st.load() == 0) e->host->st.store(2);
+    }
+    for (auto& e : r->ticket_ev)
+      if (e.host && e.host->st.load() == 0) e.host->st.store(2);
+  }
+  delete r;
+  return SLIDE_OK;
+}

@@ -1,0 +1,262 @@
+"""CPU-side checks of the C ABI: the library loads and exports every declared entry point, the
+host-side validation rejects bad arguments before anything is launched, the CPU AdamW matches the
+oracle's fixed-order float32 contract bit for bit, and the slot ring's state machine (on its host
+engine) enforces its transitions and reports copy failures and time-outs."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import layer_sliding_offloaded_fwd_amd as sl
+from layer_sliding_offloaded_fwd_amd import _capi
+from oracle import adamw as oa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "slide.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slide_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sl.lib()
+    names = _declared_functions()
+    assert len(names) >= 30
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _capi.SIGNATURES, f"{n} has no ctypes signature"
+    assert b"gfx950" in L.slide_version()
+
+
+def test_validation_errors_before_any_launch():
+    cfg = sl.layer_cfg(100, 4, 3, 64, 688, "bf16")          # 4 % 3 != 0 and H % 8 != 0
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_layer_fwd(cfg, 16, 16, 32, 1, 8, 64, 1 << 20)
+    assert e.value.code in (_capi.SLIDE_E_SHAPE,)
+    cfg = sl.layer_cfg(256, 4, 4, 96, 688, "bf16")          # head_dim 96 unsupported
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_layer_fwd(cfg, 16, 16, 32, 1, 8, 64, 1 << 20)
+    assert e.value.code == _capi.SLIDE_E_SHAPE and "head_dim" in str(e.value)
+    cfg = sl.layer_cfg(256, 4, 4, 64, 688, "bf16")
+    need = sl.slide_layer_workspace_bytes(cfg, 2, 128, 0)
+    assert need > 0 and sl.slide_layer_workspace_bytes(cfg, 2, 128, 1) > need
+    with pytest.raises(sl.SlideError) as e:                 # workspace one byte short
+        sl.slide_layer_fwd(cfg, 256, 512, 1024, 2, 128, 2048, need - 1)
+    assert e.value.code == _capi.SLIDE_E_WORKSPACE
+    with pytest.raises(sl.SlideError) as e:                 # misaligned pointer
+        sl.slide_layer_fwd(cfg, 258, 512, 1024, 2, 128, 2048, need)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    with pytest.raises(sl.SlideError) as e:                 # null weight slot
+        sl.slide_layer_bwd(cfg, None, 512, 1024, 2048, 4096, 2, 128, 8192, 1 << 40)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    ce = sl.CeCfg(4096, 1001, 8192, sl.SLIDE_BF16)          # vocab not a multiple of 8
+    assert sl.slide_lmhead_ce_workspace_bytes(ce, 16) == 0
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_gemm(64, 64, 60, 256, 64, True, 512, 64, True, 1024, 64, sl.SLIDE_BF16)
+    assert e.value.code == _capi.SLIDE_E_SHAPE              # K-contiguous K % 8 != 0
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_attention_fwd(256, 512, 1024, 1, 16, 6, 4, 128, sl.SLIDE_BF16)
+    assert e.value.code == _capi.SLIDE_E_SHAPE
+
+
+def test_param_count_and_offsets_match_packing():
+    from seeded_inputs import L8B, TINY
+    for w in (TINY, L8B):
+        c = w.layer
+        cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.dtype)
+        assert sl.slide_layer_param_count(cfg) == c.param_count()
+        off = sl.slide_layer_param_offsets(cfg)
+        sizes = [int(np.prod(s)) for _, s in c.param_shapes()]
+        assert off == list(np.concatenate([[0], np.cumsum(sizes)[:-1]]))
+    assert L8B.layer.param_count() == 218_112_000
+
+
+# ------------------------------------------------------------------------------ AdamW
+HP = oa.AdamWHyper(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+CHP = sl.AdamWHp(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay)
+
+
+def _adversarial(n, rng):
+    g = (rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17e-38, 3e38, -3e38, 1e-20, 65504.0,
+                        np.inf, -np.inf, np.nan], np.float32)
+    g[: len(special)] = special
+    return g
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("threads", [1, 7])
+def test_cpu_adamw_bit_exact_vs_oracle(gdt, threads):
+    rng = np.random.default_rng(11)
+    n = 100_003                       # odd size: scalar head and tail around the vector loop
+    p = rng.standard_normal(n).astype(np.float32)
+    p[:4] = [0.0, -0.0, 1e-40, 3e38]
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    po, mo, vo = p.copy(), m.copy(), v.copy()
+    for t in range(1, 5):
+        g32 = _adversarial(n, rng) if t == 2 else (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        if gdt == "bf16":
+            gbits = oa.bf16_round_bits(g32)
+            g_in, g_or = gbits.copy(), oa.bf16_bits_to_f32(gbits)
+            code = sl.SLIDE_BF16
+        else:
+            g_in, g_or, code = g32.copy(), g32, sl.SLIDE_F32
+        out = np.zeros(n, np.uint16)
+        sl.slide_cpu_adamw(p, g_in, code, m, v, out, n, t, CHP, threads)
+        po, mo, vo, bo = oa.adamw_fp32(po, g_or, mo, vo, t, HP)
+        np.testing.assert_array_equal(p.view(np.uint32), po.view(np.uint32))
+        np.testing.assert_array_equal(m.view(np.uint32), mo.view(np.uint32))
+        np.testing.assert_array_equal(v.view(np.uint32), vo.view(np.uint32))
+        np.testing.assert_array_equal(out, bo)
+
+
+def test_cpu_adamw_shared_grad_and_bf16_buffer_and_scalar_path():
+    """The bf16 gradient landing buffer may double as the bf16 weight output (in place)."""
+    rng = np.random.default_rng(12)
+    n = 4099
+    p = rng.standard_normal(n).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.random(n) * 1e-6).astype(np.float32)
+    g = oa.bf16_round_bits((rng.standard_normal(n) * 1e-2).astype(np.float32))
+    po, mo, vo, bo = oa.adamw_fp32(p, oa.bf16_bits_to_f32(g), m, v, 7, HP)
+    p2, m2, v2, shared = p.copy(), m.copy(), v.copy(), g.copy()
+    sl.slide_cpu_adamw(p2, shared, sl.SLIDE_BF16, m2, v2, shared, n, 7, CHP, 3)
+    np.testing.assert_array_equal(shared, bo)
+    np.testing.assert_array_equal(p2.view(np.uint32), po.view(np.uint32))
+    p3, m3, v3, out3 = p.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16)
+    _capi.call("slide_cpu_adamw_scalar_for_test", p3.ctypes.data, g.ctypes.data, sl.SLIDE_BF16,
+               m3.ctypes.data, v3.ctypes.data, out3.ctypes.data, n, 7, ctypes.byref(CHP))
+    np.testing.assert_array_equal(p3.view(np.uint32), po.view(np.uint32))
+    np.testing.assert_array_equal(out3, bo)
+
+
+def test_cpu_adamw_rejects_bad_arguments():
+    a = np.zeros(64, np.float32)
+    g = np.zeros(64, np.uint16)
+    with pytest.raises(sl.SlideError):
+        sl.slide_cpu_adamw(a, g, sl.SLIDE_BF16, a.copy(), a.copy(), None, 64, 0, CHP)
+    bad = sl.AdamWHp(1e-4, 1.0, 0.999, 1e-8, 0.0)
+    with pytest.raises(sl.SlideError):
+        sl.slide_cpu_adamw(a, g, sl.SLIDE_BF16, a.copy(), a.copy(), None, 64, 1, bad)
+    with pytest.raises(sl.SlideError):     # partially overlapping output
+        sl.slide_cpu_adamw(a, g, sl.SLIDE_BF16, a.copy(), a.copy(), g.ctypes.data + 2, 64, 1, CHP)
+
+
+# ------------------------------------------------------------------------------ slot ring
+def _host_ring(n_slots=3, wb=1024, gb=512):
+    dev = np.zeros(n_slots * (wb + gb), np.uint8)
+    ring = sl.SlotRing(n_slots, wb, gb, dev, engine=sl.SLIDE_ENGINE_HOST)
+    return ring, dev
+
+
+def test_ring_sliding_schedule_moves_the_right_bytes():
+    wb, gb, L = 1024, 512, 7
+    ring, dev = _host_ring(3, wb, gb)
+    host_w = [np.full(wb, 10 + i, np.uint8) for i in range(L)]
+    host_g = [np.zeros(gb, np.uint8) for _ in range(L)]
+    loaded = {}
+    for i in range(min(3, L)):
+        loaded[i] = ring.load(i, host_w[i])
+    for i in range(L):                      # forward sweep, prefetch depth 2
+        s = loaded.pop(i)
+        wptr, gptr = ring.acquire(s)
+        off = wptr - dev.ctypes.data
+        assert np.all(dev[off: off + wb] == 10 + i)
+        ring.release(s)
+        if i + 3 < L:
+            loaded[i + 3] = ring.load(i + 3, host_w[i + 3])
+    # turnaround: the last three layers are still resident
+    for i in (L - 1, L - 2, L - 3):
+        loaded[i] = ring.reuse(i)
+    with pytest.raises(sl.SlideError) as e:
+        ring.reuse(0)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    tickets = []
+    for i in range(L - 1, -1, -1):          # backward sweep
+        s = loaded.pop(i)
+        wptr, gptr = ring.acquire(s)
+        off = wptr - dev.ctypes.data
+        assert np.all(dev[off: off + wb] == 10 + i)
+        goff = gptr - dev.ctypes.data
+        dev[goff: goff + gb] = 100 + i      # "compute" the gradients
+        tickets.append((i, ring.flush(s, host_g[i])))
+        ring.release(s)
+        if i - 3 >= 0:
+            loaded[i - 3] = ring.load(i - 3, host_w[i - 3])
+    for i, t in tickets:
+        ring.wait_flush(t, 5000)
+        assert np.all(host_g[i] == 100 + i)
+    ring.close()
+
+
+def test_ring_state_errors():
+    ring, dev = _host_ring(2)
+    w = np.ones(1024, np.uint8)
+    g = np.zeros(512, np.uint8)
+    a = ring.load(0, w)
+    b = ring.load(1, w)
+    assert {a, b} == {0, 1}
+    with pytest.raises(sl.SlideError) as e:           # no FREE slot left
+        ring.load(2, w)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    with pytest.raises(sl.SlideError) as e:           # release before acquire
+        ring.release(a)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    with pytest.raises(sl.SlideError) as e:           # flush before acquire
+        ring.flush(a, g)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    ring.acquire(a)
+    with pytest.raises(sl.SlideError) as e:           # double acquire
+        ring.acquire(a)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    assert ring.state(a) == (_capi.SLOT_IN_USE, 0)
+    t = ring.flush(a, g)
+    assert ring.state(a)[0] == _capi.SLOT_FLUSHING
+    with pytest.raises(sl.SlideError):                # double flush
+        ring.flush(a, g)
+    ring.release(a)
+    assert ring.state(a)[0] == _capi.SLOT_FREE
+    ring.wait_flush(t, 5000)
+    with pytest.raises(sl.SlideError) as e:
+        ring.wait_flush(t + 100, 10)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    with pytest.raises(sl.SlideError) as e:
+        ring.acquire(7)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    assert ring.find(1) == b and ring.find(5) == -1
+    ring.close()
+
+
+def test_ring_copy_failure_and_timeout_are_reported():
+    ring, dev = _host_ring(2)
+    w = np.ones(1024, np.uint8)
+    g = np.zeros(512, np.uint8)
+    ring.inject_fault(1, 1)                           # next copy fails
+    s = ring.load(0, w)
+    with pytest.raises(sl.SlideError) as e:
+        ring.acquire(s)
+    assert e.value.code == _capi.SLIDE_E_HIP and "copy failed" in str(e.value)
+    s2 = ring.load(1, w)
+    ring.acquire(s2)
+    ring.inject_fault(2, 1)                           # next copy never completes
+    t = ring.flush(s2, g)
+    with pytest.raises(sl.SlideError) as e:
+        ring.wait_flush(t, 50)
+    assert e.value.code == _capi.SLIDE_E_TIMEOUT
+    with pytest.raises(sl.SlideError) as e:
+        sl.SlotRing(2, 1024, 512, dev, engine=sl.SLIDE_ENGINE_HIP).inject_fault(1, 1)
+    assert e.value.code == _capi.SLIDE_E_UNSUPPORTED
+    ring.close()
+
+
+def test_ring_rejects_bad_geometry():
+    dev = np.zeros(4096, np.uint8)
+    for args in [(0, 1024, 512), (2, 1000, 512), (2, 0, 0)]:
+        with pytest.raises(sl.SlideError) as e:
+            sl.SlotRing(*args, dev, engine=sl.SLIDE_ENGINE_HOST)
+        assert e.value.code == _capi.SLIDE_E_ARG

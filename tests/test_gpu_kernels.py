@@ -1,0 +1,171 @@
+"""GPU parity of libslide's kernels against the fp64 oracle (and, for the GEMM, the library
+matrix product the oracle uses), on seeded inputs whose sizes span several tiles and end in a
+ragged tail. Every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import layer_sliding_offloaded_fwd_amd as sl
+from oracle import model as om
+from seeded_inputs import activations
+from tests._gpu import DEV, assert_close, dev, empty, host, stream, ws
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _round(a, dtype):
+    """Values the device tensor will hold (bf16 rounding via torch, as the inputs are made)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16).float()
+    return t.numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, True), (False, False)])
+def test_gemm_layouts_and_ragged_tails(dtype, ak, bk):
+    M, N, K = 328, 200, 136          # 3 x 2 tiles of 128 with ragged edges; K spans 3 k-tiles
+    print(f"gemm {dtype} a_kmajor={ak} b_kmajor={bk} M={M} N={N} K={K}", flush=True)
+    rng = _rng(1)
+    A = _round(rng.standard_normal((M, K)), dtype)
+    B = _round(rng.standard_normal((K, N)), dtype)
+    R = _round(rng.standard_normal((M, N)), dtype)
+    ref = A @ B
+    a_mem = A if ak else A.T.copy()           # ak: [M][K] else [K][M]
+    b_mem = B.T.copy() if bk else B           # bk: [N][K] else [K][N]
+    lda = K if ak else M
+    ldb = K if bk else N
+    dA, dB = dev(a_mem, dtype), dev(b_mem, dtype)
+    code = sl.dtype_code(dtype)
+    C = empty((M, N), dtype)
+    sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C, N, code, dtype=code, stream=stream())
+    torch.cuda.synchronize()
+    assert_close(host(C), ref, dtype, "C = A B", tol=1e-2 if dtype == "bf16" else 1e-5)
+    C2 = empty((M, N), dtype)
+    sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C2, N, code, R=dev(R, dtype), ldr=N,
+                  alpha=0.5, dtype=code, stream=stream())
+    C3 = torch.full((M, N), 1.0, dtype=torch.float32, device=DEV)
+    sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C3, N, sl.SLIDE_F32, accumulate=True,
+                  dtype=code, stream=stream())
+    torch.cuda.synchronize()
+    assert_close(host(C2), 0.5 * ref + R, dtype, "C = R + 0.5 A B", tol=1e-2 if dtype == "bf16" else 1e-5)
+    assert_close(host(C3), 1.0 + ref, "f32", "C += A B (fp32 accumulate)", tol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,H", [("bf16", 4096), ("f32", 256), ("bf16", 264)])
+def test_rmsnorm_fwd_bwd(dtype, H):
+    N = 37
+    print(f"rmsnorm {dtype} N={N} H={H}", flush=True)
+    x = activations((N, H), dtype, 5).f64
+    w = _round(1.0 + 0.1 * _rng(6).standard_normal(H), dtype)
+    dy = activations((N, H), dtype, 7).f64
+    dres = activations((N, H), dtype, 8).f64
+    code = sl.dtype_code(dtype)
+    dx_, x_, w_, dy_, dres_ = (dev(a, dtype) for a in (x, x, w, dy, dres))
+    y = empty((N, H), dtype)
+    rstd = torch.empty(N, dtype=torch.float32, device=DEV)
+    sl.slide_rmsnorm_fwd(x_, w_, y, rstd, N, H, 1e-5, code, stream())
+    dx = empty((N, H), dtype)
+    dw = empty((H,), dtype)
+    wsz = sl.slide_rmsnorm_bwd_workspace_bytes(N, H)
+    sl.slide_rmsnorm_bwd(dy_, x_, w_, dres_, dx, dw, N, H, 1e-5, code, ws(wsz), wsz, stream())
+    torch.cuda.synchronize()
+    ry, rr = om.rmsnorm_fwd(x, w, 1e-5)
+    rdx, rdw = om.rmsnorm_bwd(dy, x, w, rr)
+    assert_close(host(y), ry, dtype, "rmsnorm y")
+    assert_close(host(rstd), rr[:, 0], "f32", "rmsnorm rstd", tol=1e-5)
+    assert_close(host(dx), rdx + dres, dtype, "rmsnorm dx + residual")
+    assert_close(host(dw), rdw, dtype, "rmsnorm dw")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_rope_forward_and_inverse(dtype, d):
+    B, S, nq, nkv = 2, 77, 4, 2
+    print(f"rope {dtype} d={d} S={S}", flush=True)
+    QR = (nq + 2 * nkv) * d
+    qkv = activations((B * S, QR), dtype, 9).f64
+    t = dev(qkv, dtype)
+    code = sl.dtype_code(dtype)
+    wsz = 2 * 4 * S * d + 1024
+    w = ws(wsz)
+    sl.slide_rope(t, B, S, nq, nkv, d, 10000.0, 0, code, w, wsz, stream())
+    torch.cuda.synchronize()
+    out = host(t).reshape(B, S, -1)
+    cos, sin = om.rope_tables(S, d, 10000.0)
+    x = qkv.reshape(B, S, -1)
+    rq = om.rope_rotate(x[..., : nq * d].reshape(B, S, nq, d), cos, sin).reshape(B, S, -1)
+    rk = om.rope_rotate(x[..., nq * d:(nq + nkv) * d].reshape(B, S, nkv, d), cos, sin).reshape(B, S, -1)
+    assert_close(out[..., : nq * d], rq, dtype, "rope q")
+    assert_close(out[..., nq * d:(nq + nkv) * d], rk, dtype, "rope k")
+    assert np.array_equal(out[..., (nq + nkv) * d:], x[..., (nq + nkv) * d:]), "v must be untouched"
+    sl.slide_rope(t, B, S, nq, nkv, d, 10000.0, 1, code, w, wsz, stream())
+    torch.cuda.synchronize()
+    assert_close(host(t), qkv, dtype, "rope inverse restores the input")
+
+
+@pytest.mark.parametrize("dtype,B,S,nq,nkv,d", [
+    ("bf16", 2, 200, 8, 2, 128),     # GQA, ragged sequence (not a multiple of 64 or 128)
+    ("bf16", 1, 128, 4, 4, 64),      # MHA, head_dim 64
+    ("bf16", 1, 1, 4, 1, 128),       # a single token: o = v
+    ("f32", 2, 128, 4, 4, 64),
+])
+def test_attention_fwd_bwd(dtype, B, S, nq, nkv, d):
+    print(f"attention {dtype} B={B} S={S} nq={nq} nkv={nkv} d={d}", flush=True)
+    QR = (nq + 2 * nkv) * d
+    qkv = activations((B * S, QR), dtype, 21).f64
+    do = activations((B * S, nq * d), dtype, 22).f64
+    code = sl.dtype_code(dtype)
+    t_qkv, t_do = dev(qkv, dtype), dev(do, dtype)
+    o = empty((B * S, nq * d), dtype)
+    lse = torch.empty(B * nq * S, dtype=torch.float32, device=DEV)
+    sl.slide_attention_fwd(t_qkv, o, lse, B, S, nq, nkv, d, code, stream())
+    dqkv = torch.full((B * S, QR), float("nan"), dtype=o.dtype, device=DEV)
+    wsz = sl.slide_attention_bwd_workspace_bytes(B, S, nq)
+    sl.slide_attention_bwd(t_qkv, o, lse, t_do, dqkv, B, S, nq, nkv, d, code, ws(wsz), wsz,
+                           stream())
+    torch.cuda.synchronize()
+    x = qkv.reshape(B, S, -1)
+    q = x[..., : nq * d].reshape(B, S, nq, d)
+    k = x[..., nq * d:(nq + nkv) * d].reshape(B, S, nkv, d)
+    v = x[..., (nq + nkv) * d:].reshape(B, S, nkv, d)
+    ro, rlse, P = om.attention_fwd(q, k, v)
+    # the backward consumes the o the GPU stored (bf16-rounded), as the layer does
+    dq, dk, dv = om.attention_bwd(do.reshape(B, S, nq, d), q, k, v, P)
+    assert_close(host(o).reshape(B, S, nq, d), ro, dtype, "attention o")
+    assert_close(host(lse).reshape(B, nq, S), rlse, "f32", "attention lse",
+                 tol=1e-4 if dtype == "f32" else 2e-3)
+    g = host(dqkv).reshape(B, S, -1)
+    assert_close(g[..., : nq * d].reshape(B, S, nq, d), dq, dtype, "attention dq")
+    assert_close(g[..., nq * d:(nq + nkv) * d].reshape(B, S, nkv, d), dk, dtype, "attention dk")
+    assert_close(g[..., (nq + nkv) * d:].reshape(B, S, nkv, d), dv, dtype, "attention dv")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_embedding_fwd_bwd_repeated_tokens(dtype):
+    N, H, V = 300, 264, 40           # small vocabulary: every token repeats several times
+    print(f"embedding {dtype} N={N} H={H} V={V}", flush=True)
+    E = activations((V, H), dtype, 31).f64
+    tok = _rng(32).integers(0, V, N).astype(np.int32)
+    tok[5] = 7
+    tok[6] = 7
+    dx = activations((N, H), dtype, 33).f64
+    code = sl.dtype_code(dtype)
+    t_tok = torch.from_numpy(tok).to(DEV)
+    x = empty((N, H), dtype)
+    sl.slide_embed_fwd(dev(E, dtype), t_tok, x, N, H, V, code, stream())
+    dE = torch.full((V, H), float("nan"), dtype=x.dtype, device=DEV)
+    wsz = sl.slide_embed_bwd_workspace_bytes(N, V)
+    sl.slide_embed_bwd(dev(dx, dtype), t_tok, dE, N, H, V, code, ws(wsz), wsz, stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(host(x), E[tok]), "gather must be exact"
+    assert_close(host(dE), om.embedding_bwd(dx, tok, V), dtype, "embedding dE")
+    # deterministic: a second run gives identical bits
+    dE2 = torch.empty_like(dE)
+    sl.slide_embed_bwd(dev(dx, dtype), t_tok, dE2, N, H, V, code, ws(wsz), wsz, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dE.view(torch.int16) if dtype == "bf16" else dE,
+                       dE2.view(torch.int16) if dtype == "bf16" else dE2)
