@@ -208,7 +208,7 @@ int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* t
   auto logits = [&](int c0, int rows, const char* name) {
     // z^T[v][t] = sum_k W[c0+v][k] h[t][k]
     GemmArgs g{rows, N, H, (const char*)w + (size_t)c0 * H * ts, H, true, h, H, true, zbuf,
-               L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, dt, name};
+               L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, dt, name, SITE_CE_LOGITS};
     return gemm_launch(g, st);
   };
 
@@ -250,13 +250,13 @@ int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* t
     if (dh) {
       // dh[t][i] (+)= sum_v dz[v][t] W[c0+v][i]
       GemmArgs g{N, H, rows, dz, L.ldz, false, wc, H, false, dh_acc, H, SLIDE_F32, nullptr, 0,
-                 1.0f, ci > 0, dt, "ce_dh_gemm"};
+                 1.0f, ci > 0, dt, "ce_dh_gemm", SITE_CE_DH};
       SLIDE_TRY(gemm_launch(g, st));
     }
     if (dw) {
       // dW[c0+v][i] = sum_t dz[v][t] h[t][i]
       GemmArgs g{rows, H, N, dz, L.ldz, true, h, H, false, (char*)dw + (size_t)c0 * H * ts, H,
-                 dt, nullptr, 0, 1.0f, false, dt, "ce_dw_gemm"};
+                 dt, nullptr, 0, 1.0f, false, dt, "ce_dw_gemm", SITE_CE_DW};
       SLIDE_TRY(gemm_launch(g, st));
     }
   }

@@ -87,7 +87,7 @@ __device__ __forceinline__ void store_outerk(const uint4 (&reg)[8], bf16_t* s) {
   }
 }
 
-template <bool AK, bool BKM, int EPI>
+template <bool AK, bool BKM, int EPI, int SITE>
 __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
@@ -262,17 +262,49 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+template <bool AK, bool BKM, int EPI, int SITE>
+void launch_one(const GemmArgs& g, hipStream_t st) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI, SITE>), dim3(tiles), dim3(NT), 0, st, g);
+}
+
 template <bool AK, bool BKM>
-int launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
-  int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  dim3 grid(tiles), block(NT);
+void launch_generic(const GemmArgs& g, hipStream_t st, int epi) {
   switch (epi) {
-    case EPI_STORE_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI_STORE_BF16>), grid, block, 0, st, g); break;
-    case EPI_STORE_F32: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI_STORE_F32>), grid, block, 0, st, g); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI_RESID>), grid, block, 0, st, g); break;
-    default: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI_ACCUM_F32>), grid, block, 0, st, g); break;
+    case EPI_STORE_BF16: launch_one<AK, BKM, EPI_STORE_BF16, SITE_GENERIC>(g, st); break;
+    case EPI_STORE_F32: launch_one<AK, BKM, EPI_STORE_F32, SITE_GENERIC>(g, st); break;
+    case EPI_RESID: launch_one<AK, BKM, EPI_RESID, SITE_GENERIC>(g, st); break;
+    default: launch_one<AK, BKM, EPI_ACCUM_F32, SITE_GENERIC>(g, st); break;
   }
-  return SLIDE_OK;
+}
+
+// (site, a_kmajor, b_kmajor, epilogue) -> dedicated instantiation, else generic
+void launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
+#define SLIDE_SITE(S, AK_, BK_, EPI_)                                              \
+  if (g.site == S && g.a_kmajor == AK_ && g.b_kmajor == BK_ && epi == EPI_) {    \
+    launch_one<AK_, BK_, EPI_, S>(g, st);                                        \
+    return;                                                                      \
+  }
+  SLIDE_SITE(SITE_QKV, true, true, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_O, true, true, EPI_RESID)
+  SLIDE_SITE(SITE_GATE_UP, true, true, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_DOWN, true, true, EPI_RESID)
+  SLIDE_SITE(SITE_DOWN_DX, true, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_DOWN_DW, false, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_GATE_UP_DX, true, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_GATE_UP_DW, false, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_O_DX, true, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_O_DW, false, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_QKV_DX, true, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_QKV_DW, false, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_CE_LOGITS, true, true, EPI_STORE_F32)
+  SLIDE_SITE(SITE_CE_DH, false, false, EPI_ACCUM_F32)
+  SLIDE_SITE(SITE_CE_DW, true, false, EPI_STORE_BF16)
+#undef SLIDE_SITE
+  if (g.a_kmajor && g.b_kmajor) launch_generic<true, true>(g, st, epi);
+  else if (g.a_kmajor) launch_generic<true, false>(g, st, epi);
+  else if (g.b_kmajor) launch_generic<false, true>(g, st, epi);
+  else launch_generic<false, false>(g, st, epi);
 }
 
 }  // namespace
@@ -316,10 +348,7 @@ int gemm_launch(const GemmArgs& g, hipStream_t st) {
   ProfScope ps(g.name ? g.name : "gemm", st);
   const int epi = gemm_epilogue_of(g);
   if (g.dtype == SLIDE_BF16) {
-    if (g.a_kmajor && g.b_kmajor) launch_bf16<true, true>(g, st, epi);
-    else if (g.a_kmajor) launch_bf16<true, false>(g, st, epi);
-    else if (g.b_kmajor) launch_bf16<false, true>(g, st, epi);
-    else launch_bf16<false, false>(g, st, epi);
+    launch_bf16(g, st, epi);
   } else {
     dim3 grid((g.N + SB - 1) / SB, (g.M + SB - 1) / SB), block(256);
     switch (epi) {
@@ -337,7 +366,7 @@ extern "C" int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kma
                           int ldb, int b_kmajor, void* C, int ldc, int c_dtype, const void* R,
                           int ldr, float alpha, int accumulate, int dtype, void* stream) {
   slide::GemmArgs g{M, N, K, A, lda, a_kmajor != 0, B, ldb, b_kmajor != 0, C, ldc, c_dtype,
-                    R, ldr, alpha, accumulate != 0, dtype, "gemm"};
+                    R, ldr, alpha, accumulate != 0, dtype, "gemm", slide::SITE_GENERIC};
   SLIDE_TRY(slide::gemm_check(g));
   return slide::gemm_launch(g, (hipStream_t)stream);
 }

@@ -108,8 +108,9 @@ inline const void* at(const void* p, size_t elems, size_t ts) { return (const ch
 inline void* at(void* p, size_t elems, size_t ts) { return (char*)p + elems * ts; }
 
 int gemm(int M, int N, int K, const void* A, int lda, bool ak, const void* B, int ldb, bool bk,
-         void* C, int ldc, const void* R, int dt, const char* name, hipStream_t st) {
-  GemmArgs g{M, N, K, A, lda, ak, B, ldb, bk, C, ldc, dt, R, R ? ldc : 0, 1.0f, false, dt, name};
+         void* C, int ldc, const void* R, int dt, const char* name, int site, hipStream_t st) {
+  GemmArgs g{M, N, K, A, lda, ak, B, ldb, bk, C, ldc, dt, R, R ? ldc : 0, 1.0f, false, dt, name,
+             site};
   return gemm_launch(g, st);
 }
 
@@ -122,18 +123,18 @@ int forward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* 
   SLIDE_TRY(rope_tables(ws.cos_t, ws.sin_t, d.S, d.d, c.rope_theta, st));
   SLIDE_TRY(rmsnorm_fwd(x, at(w, off[0], ts), ws.r, nullptr, d.N, d.H, c.rms_eps, d.dt, st));
   SLIDE_TRY(gemm(d.N, d.QR, d.H, ws.r, d.H, true, at(w, off[1], ts), d.H, true, ws.qkv, d.QR,
-                 nullptr, d.dt, "gemm_qkv", st));
+                 nullptr, d.dt, "gemm_qkv", SITE_QKV, st));
   SLIDE_TRY(rope_apply(ws.qkv, ws.cos_t, ws.sin_t, d.B, d.S, d.nq, d.nkv, d.d, 0, d.dt, st));
   SLIDE_TRY(attention_fwd(ws.qkv, ws.o, ws.lse, d.B, d.S, d.nq, d.nkv, d.d, d.dt, st));
   SLIDE_TRY(gemm(d.N, d.H, d.OD, ws.o, d.OD, true, at(w, off[2], ts), d.OD, true, ws.x2, d.H, x,
-                 d.dt, "gemm_o", st));
+                 d.dt, "gemm_o", SITE_O, st));
   SLIDE_TRY(rmsnorm_fwd(ws.x2, at(w, off[3], ts), ws.r2, nullptr, d.N, d.H, c.rms_eps, d.dt, st));
   SLIDE_TRY(gemm(d.N, 2 * d.F, d.H, ws.r2, d.H, true, at(w, off[4], ts), d.H, true, ws.gu,
-                 2 * d.F, nullptr, d.dt, "gemm_gate_up", st));
+                 2 * d.F, nullptr, d.dt, "gemm_gate_up", SITE_GATE_UP, st));
   SLIDE_TRY(swiglu_fwd(ws.gu, ws.m, d.N, d.F, d.dt, st));
   if (y)
     SLIDE_TRY(gemm(d.N, d.H, d.F, ws.m, d.F, true, at(w, off[5], ts), d.F, true, y, d.H, ws.x2,
-                   d.dt, "gemm_down", st));
+                   d.dt, "gemm_down", SITE_DOWN, st));
   return SLIDE_OK;
 }
 
@@ -146,28 +147,28 @@ int backward(const Dims& d, const slide_layer_cfg& c, const void* w, const void*
   SLIDE_TRY(forward(d, c, w, x, nullptr, ws, st));
   // MLP half
   SLIDE_TRY(gemm(N, F, H, dy, H, true, at(w, off[5], ts), F, false, ws.dm, F, nullptr, d.dt,
-                 "gemm_down_dx", st));
+                 "gemm_down_dx", SITE_DOWN_DX, st));
   SLIDE_TRY(gemm(H, F, N, dy, H, false, ws.m, F, false, at(g, off[5], ts), F, nullptr, d.dt,
-                 "gemm_down_dw", st));
+                 "gemm_down_dw", SITE_DOWN_DW, st));
   SLIDE_TRY(swiglu_bwd(ws.dm, ws.gu, ws.dgu, N, F, d.dt, st));
   SLIDE_TRY(gemm(N, H, 2 * F, ws.dgu, 2 * F, true, at(w, off[4], ts), H, false, ws.dr2, H,
-                 nullptr, d.dt, "gemm_gate_up_dx", st));
+                 nullptr, d.dt, "gemm_gate_up_dx", SITE_GATE_UP_DX, st));
   SLIDE_TRY(gemm(2 * F, H, N, ws.dgu, 2 * F, false, ws.r2, H, false, at(g, off[4], ts), H,
-                 nullptr, d.dt, "gemm_gate_up_dw", st));
+                 nullptr, d.dt, "gemm_gate_up_dw", SITE_GATE_UP_DW, st));
   SLIDE_TRY(rmsnorm_bwd(ws.dr2, ws.x2, at(w, off[3], ts), dy, ws.dx2, at(g, off[3], ts), N, H,
                         c.rms_eps, d.dt, ws.rms_ws, st));
   // attention half
   SLIDE_TRY(gemm(N, d.OD, H, ws.dx2, H, true, at(w, off[2], ts), d.OD, false, ws.dO, d.OD,
-                 nullptr, d.dt, "gemm_o_dx", st));
+                 nullptr, d.dt, "gemm_o_dx", SITE_O_DX, st));
   SLIDE_TRY(gemm(H, d.OD, N, ws.dx2, H, false, ws.o, d.OD, false, at(g, off[2], ts), d.OD,
-                 nullptr, d.dt, "gemm_o_dw", st));
+                 nullptr, d.dt, "gemm_o_dw", SITE_O_DW, st));
   SLIDE_TRY(attention_bwd(ws.qkv, ws.o, ws.lse, ws.dO, ws.dqkv, d.B, d.S, d.nq, d.nkv, d.d,
                           d.dt, ws.attn_ws, st));
   SLIDE_TRY(rope_apply(ws.dqkv, ws.cos_t, ws.sin_t, d.B, d.S, d.nq, d.nkv, d.d, 1, d.dt, st));
   SLIDE_TRY(gemm(N, H, d.QR, ws.dqkv, d.QR, true, at(w, off[1], ts), H, false, ws.dr, H, nullptr,
-                 d.dt, "gemm_qkv_dx", st));
+                 d.dt, "gemm_qkv_dx", SITE_QKV_DX, st));
   SLIDE_TRY(gemm(d.QR, H, N, ws.dqkv, d.QR, false, ws.r, H, false, at(g, off[1], ts), H, nullptr,
-                 d.dt, "gemm_qkv_dw", st));
+                 d.dt, "gemm_qkv_dw", SITE_QKV_DW, st));
   SLIDE_TRY(rmsnorm_bwd(ws.dr, x, at(w, off[0], ts), ws.dx2, dx, at(g, off[0], ts), N, H,
                         c.rms_eps, d.dt, ws.rms_ws, st));
   return SLIDE_OK;

@@ -1,0 +1,476 @@
+"""Thread-based step engine of the layer-sliding method (SlideFormer summary, section 2A:
+a lightweight thread-based engine with separate streams for transfers and computation; the
+GPU is a sliding window over the layers; while the CPU updates layer i the GPU runs the backward
+of layer i-1 and prefetches layer i-2; figures 3-5 of the paper page).
+
+One training step:
+  forward   embedding gather; layers 0..L-1 through the slot ring (weights loaded ahead on the
+            H2D stream as slots free up); only each layer's input is kept on the GPU.
+  loss      final RMSNorm, chunked LM-head cross-entropy (loss, dh, dW_lm).
+  backward  layers L-1..0: the last n_slots layers are still resident (re-claimed without a
+            copy); every other layer is prefetched n_slots layers ahead; after each layer's
+            backward its gradients are flushed to host memory on the D2H stream and a CPU worker
+            thread runs AdamW on that layer as soon as they land, while the GPU continues.
+  glue      embedding, final gain and LM head are updated the same way; their device copies are
+            refreshed by the worker as soon as their update is done.
+The host keeps fp32 master weights and AdamW moments per layer. For bf16 compute each layer has
+one pinned bf16 buffer that is both the upload source of its weights and the landing buffer of
+its gradients; AdamW reads the gradients from it and writes the new bf16 weights back into it
+(summary, section 2B: gradients and FP32->BF16 conversions share fixed host buffers).
+Every device buffer is allocated once, up front (section 2B: pre-allocated, no fragmentation).
+
+All numerical work runs in libslide (HIP kernels and the C++ AdamW); this module only orders
+calls on streams and threads. PyTorch provides device memory, pinned host memory and streams.
+"""
+import queue
+import threading
+import time
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import binding as B
+from ._capi import SLIDE_BF16, SLIDE_F32
+
+
+@dataclass(frozen=True)
+class ModelSpec:
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    n_layers: int
+    dtype: str = "bf16"          # compute dtype: "bf16" or "f32"
+    rms_eps: float = 1e-5
+    rope_theta: float = 10000.0
+
+
+@dataclass(frozen=True)
+class AdamW:
+    lr: float = 1e-4
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+
+def _align(n, a=256):
+    return (n + a - 1) // a * a
+
+
+class _Job:
+    __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
+                 "t_end", "t_ready", "step")
+
+    def __init__(self, name, wait, p, g, m, v, out, n, step, post=None):
+        self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
+        self.out, self.n, self.post, self.step = out, n, post, step
+        self.done = threading.Event()
+        self.t_start = self.t_end = self.t_ready = 0.0
+
+
+class _Param:
+    """Host state of one parameter block: fp32 master, AdamW moments, the pinned buffer that
+    serves as upload source and gradient landing zone, and (for resident blocks) the device
+    copy and device gradient."""
+
+    def __init__(self, n, dtype, device=None, resident=False):
+        self.n = n
+        self.dtype = dtype
+        if dtype == "bf16":
+            self.master = torch.empty(n, dtype=torch.float32)
+            self.shared = torch.empty(n, dtype=torch.int16, pin_memory=True)   # bf16 bits
+            self.grad_host = self.shared
+        else:
+            self.master = torch.empty(n, dtype=torch.float32, pin_memory=True)
+            self.shared = self.master                                           # upload source
+            self.grad_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+        self.m = torch.zeros(n, dtype=torch.float32)
+        self.v = torch.zeros(n, dtype=torch.float32)
+        self.job = None
+        if resident:
+            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+            self.dev = torch.empty(n, dtype=tdt, device=device)
+            self.grad = torch.empty(n, dtype=tdt, device=device)
+            self.ready_ev = None      # h2d of the current device copy
+            self.flushed_ev = None    # d2h of the last device gradient
+
+
+class SlideEngine:
+    def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
+                 adam_threads=0, device="cuda:0", serialize=False, timeline=False):
+        assert spec.dtype in ("bf16", "f32")
+        self.spec, self.B, self.S, self.N = spec, batch, seq, batch * seq
+        self.L = spec.n_layers
+        self.n_slots = max(1, min(n_slots, self.L))
+        self.hp = B.AdamWHp(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)
+        self.adam_threads = adam_threads
+        self.device = torch.device(device)
+        self.serialize = serialize
+        self.timeline = timeline
+        self.code = SLIDE_BF16 if spec.dtype == "bf16" else SLIDE_F32
+        self.tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        self.ts = 2 if spec.dtype == "bf16" else 4
+        s = spec
+        self.cfg = B.layer_cfg(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.ffn, s.dtype,
+                               s.rms_eps, s.rope_theta)
+        self.ce_cfg = B.CeCfg(s.hidden, s.vocab, ce_chunk, self.code)
+        self.P = B.slide_layer_param_count(self.cfg)
+        self.w_bytes = _align(self.P * self.ts)
+        H, V, N = s.hidden, s.vocab, self.N
+
+        # streams: one for compute, one per copy direction (default priority)
+        self.compute = torch.cuda.Stream(device=self.device)
+        self.h2d = torch.cuda.Stream(device=self.device)
+        self.d2h = torch.cuda.Stream(device=self.device)
+
+        # host parameter blocks
+        self.layers = [_Param(self.P, s.dtype) for _ in range(self.L)]
+        self.embed = _Param(V * H, s.dtype, self.device, resident=True)
+        self.final = _Param(H, s.dtype, self.device, resident=True)
+        self.lm = _Param(V * H, s.dtype, self.device, resident=True)
+
+        # device memory, allocated once
+        dev = self.device
+        self.ring_mem = torch.empty(self.n_slots * 2 * self.w_bytes, dtype=torch.uint8, device=dev)
+        self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
+                               self.h2d, self.d2h)
+        self.xs = torch.empty((self.L + 1, N, H), dtype=self.tdt, device=dev)   # layer inputs
+        self.grad_x = torch.empty((N, H), dtype=self.tdt, device=dev)
+        self.hf = torch.empty((N, H), dtype=self.tdt, device=dev)
+        self.dhf = torch.empty((N, H), dtype=self.tdt, device=dev)
+        self.tok_in = torch.empty(N, dtype=torch.int32, device=dev)
+        self.tok_tgt = torch.empty(N, dtype=torch.int32, device=dev)
+        self.loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+        ws = max(B.slide_layer_workspace_bytes(self.cfg, batch, seq, 1),
+                 B.slide_layer_workspace_bytes(self.cfg, batch, seq, 0),
+                 B.slide_lmhead_ce_workspace_bytes(self.ce_cfg, N),
+                 B.slide_embed_bwd_workspace_bytes(N, V),
+                 B.slide_rmsnorm_bwd_workspace_bytes(N, H))
+        self.ws_bytes = _align(ws)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+
+        # CPU optimizer worker
+        self.jobs = queue.Queue()
+        self.worker_error = None
+        self.worker = threading.Thread(target=self._worker_loop, daemon=True, name="slide-adamw")
+        self.worker.start()
+        self.step_count = 0
+        self.records = []
+
+    # ------------------------------------------------------------------ parameters
+    def load_params(self, embed, layers, w_final, lm_head):
+        """Set fp32 master weights (numpy or torch, any shape; layers in slot packing order)
+        and derive the compute copies. Moments are reset to zero and the step counter to 0."""
+        self.wait_updates()
+
+        def put(prm, arr):
+            t = torch.as_tensor(np.ascontiguousarray(arr, dtype=np.float32)
+                                if isinstance(arr, np.ndarray) else arr).reshape(-1).float()
+            assert t.numel() == prm.n
+            prm.master.copy_(t)
+            self._refresh_shared(prm)
+            prm.m.zero_()
+            prm.v.zero_()
+
+        put(self.embed, embed)
+        put(self.final, w_final)
+        put(self.lm, lm_head)
+        assert len(layers) == self.L
+        for prm, arr in zip(self.layers, layers):
+            put(prm, arr)
+        for prm in (self.embed, self.final, self.lm):
+            self._upload_resident(prm)
+        torch.cuda.synchronize(self.device)
+        self.step_count = 0
+
+    def init_random(self, seed=0, std=0.02):
+        """Seeded synthetic weights drawn on the GPU (matrices N(0, std), norm gains 1)."""
+        self.wait_updates()
+        gen = torch.Generator(device=self.device)
+        gen.manual_seed(seed)
+        offs = B.slide_layer_param_offsets(self.cfg)
+        H = self.spec.hidden
+
+        def draw(prm, gains=()):
+            t = torch.empty(prm.n, dtype=torch.float32, device=self.device)
+            t.normal_(0.0, std, generator=gen)
+            for o in gains:
+                t[o:o + H] = 1.0
+            prm.master.copy_(t, non_blocking=False)
+            if prm.dtype == "bf16":
+                prm.shared.copy_(t.to(torch.bfloat16).view(torch.int16))
+            if self.step_count:          # moments are zero from construction until a step ran
+                prm.m.zero_()
+                prm.v.zero_()
+
+        draw(self.embed)
+        for prm in self.layers:
+            draw(prm, gains=(offs[0], offs[3]))
+        self.final.master.fill_(1.0)
+        self._refresh_shared(self.final)
+        draw(self.lm)
+        for prm in (self.embed, self.final, self.lm):
+            self._upload_resident(prm)
+        torch.cuda.synchronize(self.device)
+        self.step_count = 0
+
+    def _refresh_shared(self, prm):
+        if prm.dtype == "bf16":
+            prm.shared.copy_(prm.master.to(torch.bfloat16).view(torch.int16))
+
+    def _upload_resident(self, prm):
+        with torch.cuda.stream(self.h2d):
+            src = prm.shared.view(torch.bfloat16) if prm.dtype == "bf16" else prm.shared
+            prm.dev.copy_(src, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(self.h2d)
+        prm.ready_ev = ev
+
+    def master_params(self):
+        """fp32 master weights as numpy arrays (after waiting for pending updates)."""
+        self.wait_updates()
+        return dict(embed=self.embed.master.numpy().copy(),
+                    layers=[p.master.numpy().copy() for p in self.layers],
+                    w_final=self.final.master.numpy().copy(),
+                    lm_head=self.lm.master.numpy().copy())
+
+    # ------------------------------------------------------------------ CPU worker
+    def _worker_loop(self):
+        while True:
+            job = self.jobs.get()
+            if job is None:
+                return
+            try:
+                if isinstance(job.wait, int):
+                    self.ring.wait_flush(job.wait, -1)
+                elif job.wait is not None:
+                    job.wait.synchronize()
+                job.t_ready = time.perf_counter()
+                B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
+                                  job.step, self.hp, self.adam_threads)
+                job.t_start = job.t_ready
+                job.t_end = time.perf_counter()
+                if job.post is not None:
+                    job.post()
+            except Exception as e:  # surfaced on the main thread by wait_updates / step
+                self.worker_error = e
+            finally:
+                job.done.set()
+
+    def _submit(self, prm, wait, name, post=None):
+        out = prm.shared if prm.dtype == "bf16" else None
+        job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
+                   self.step_count, post)
+        prm.job = job
+        self.jobs.put(job)
+        if self.serialize:
+            job.done.wait()
+        return job
+
+    def _wait_param(self, prm):
+        if prm.job is not None:
+            prm.job.done.wait()
+            if self.worker_error is not None:
+                raise self.worker_error
+
+    def wait_updates(self):
+        for prm in self.layers + [self.embed, self.final, self.lm]:
+            self._wait_param(prm)
+
+    def close(self):
+        self.wait_updates()
+        self.jobs.put(None)
+        self.worker.join()
+        self.ring.close()
+
+    # ------------------------------------------------------------------ step
+    def _sync(self):
+        if self.serialize:
+            torch.cuda.synchronize(self.device)
+
+    def _ev(self, stream):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        return ev
+
+    def _flush_resident(self, prm, name):
+        """D2H of a resident block's device gradient after the compute stream, then AdamW, then
+        the refreshed device copy goes back up on the H2D stream."""
+        ev_c = torch.cuda.Event()
+        ev_c.record(self.compute)
+        self.d2h.wait_event(ev_c)
+        with torch.cuda.stream(self.d2h):
+            dst = prm.grad_host.view(torch.bfloat16) if prm.dtype == "bf16" else prm.grad_host
+            dst.copy_(prm.grad, non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(self.d2h)
+        prm.flushed_ev = done
+        return self._submit(prm, done, name, post=lambda: self._upload_resident(prm))
+
+    def step(self, tokens):
+        """One training step on int32 tokens [B, S+1] (inputs [:, :S], targets [:, 1:]).
+        Returns the loss (float)."""
+        if self.worker_error is not None:
+            raise self.worker_error
+        spec, N, H, V, L = self.spec, self.N, self.spec.hidden, self.spec.vocab, self.L
+        c = self.compute
+        tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32))
+        assert tok.shape == (self.B, self.S + 1), tok.shape
+        self.step_count += 1
+        rec = dict(step=self.step_count, layers={}, jobs=[])
+        t_step0 = time.perf_counter()
+        ev0 = self._ev(c)          # the compute stream is idle here: ev0 ~ host time t_step0
+        rec["host_t0"] = t_step0
+        with torch.cuda.stream(c):
+            self.tok_in.copy_(tok[:, :-1].reshape(-1), non_blocking=False)
+            self.tok_tgt.copy_(tok[:, 1:].reshape(-1), non_blocking=False)
+
+        # ---- forward
+        self._wait_param(self.embed)
+        c.wait_event(self.embed.ready_ev)
+        if self.embed.flushed_ev is not None:
+            c.wait_event(self.embed.flushed_ev)
+        B.slide_embed_fwd(self.embed.dev, self.tok_in, self.xs[0], N, H, V, self.code, c)
+        slots = {}
+        for i in range(self.n_slots):
+            self._wait_param(self.layers[i])
+            slots[i] = self.ring.load(i, self.layers[i].shared)
+        for i in range(L):
+            s = slots.pop(i)
+            w, _ = self.ring.acquire(s, c)
+            e_a = self._ev(c) if self.timeline else None
+            B.slide_layer_fwd(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S, self.ws,
+                              self.ws_bytes, c)
+            if self.timeline:
+                rec["layers"].setdefault(i, {})["fwd"] = (e_a, self._ev(c))
+            self.ring.release(s, c)
+            self._sync()
+            j = i + self.n_slots
+            if j < L:
+                self._wait_param(self.layers[j])
+                slots[j] = self.ring.load(j, self.layers[j].shared)
+
+        # ---- loss
+        self._wait_param(self.final)
+        c.wait_event(self.final.ready_ev)
+        self._wait_param(self.lm)
+        c.wait_event(self.lm.ready_ev)
+        if self.lm.flushed_ev is not None:
+            c.wait_event(self.lm.flushed_ev)
+        if self.final.flushed_ev is not None:
+            c.wait_event(self.final.flushed_ev)
+        B.slide_rmsnorm_fwd(self.xs[L], self.final.dev, self.hf, None, N, H, spec.rms_eps,
+                            self.code, c)
+        e_ce = self._ev(c) if self.timeline else None
+        B.slide_lmhead_ce(self.ce_cfg, self.hf, self.lm.dev, self.tok_tgt, N, self.loss_dev,
+                          self.dhf, self.lm.grad, self.ws, self.ws_bytes, c)
+        if self.timeline:
+            rec["ce"] = (e_ce, self._ev(c))
+        self._flush_resident(self.lm, "lm_head")
+        B.slide_rmsnorm_bwd(self.dhf, self.xs[L], self.final.dev, None, self.grad_x,
+                            self.final.grad, N, H, spec.rms_eps, self.code, self.ws,
+                            self.ws_bytes, c)
+        self._flush_resident(self.final, "w_final")
+        self._sync()
+
+        # ---- backward: the last n_slots layers are still in their slots; claim them all
+        # before the first prefetch so that no load can pick one of their slots
+        for i in range(L - 1, L - 1 - self.n_slots, -1):
+            slots[i] = self.ring.reuse(i)
+        for i in range(L - 1, -1, -1):
+            s = slots.pop(i)
+            w, g = self.ring.acquire(s, c)
+            e_a = self._ev(c) if self.timeline else None
+            B.slide_layer_bwd(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g, self.B,
+                              self.S, self.ws, self.ws_bytes, c)
+            e_b = self._ev(c) if self.timeline else None
+            ticket = self.ring.flush(s, self.layers[i].grad_host, c)
+            if self.timeline:
+                rec["layers"].setdefault(i, {})["bwd"] = (e_a, e_b)
+                rec["layers"][i]["d2h_end"] = self._ev(self.d2h)
+            rec["jobs"].append(self._submit(self.layers[i], ticket, f"layer{i}"))
+            self.ring.release(s, c)
+            self._sync()
+            j = i - self.n_slots
+            if j >= 0:
+                slots[j] = self.ring.load(j, self.layers[j].shared)
+
+        # ---- embedding gradient
+        B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
+                          self.ws, self.ws_bytes, c)
+        self._flush_resident(self.embed, "embed")
+        e_end = self._ev(c)
+        e_end.synchronize()
+        rec["ev0"], rec["ev_end"] = ev0, e_end
+        rec["host_gpu_done"] = time.perf_counter()
+        self._sync()
+        self.records.append(rec)
+        return rec
+
+    def loss(self):
+        return float(self.loss_dev.item())
+
+    # ------------------------------------------------------------------ timeline analysis
+    def analyse(self, rec, d2h_gbps=None):
+        """Per-layer backward time, gradient D2H time and CPU update time of one recorded step
+        (timeline=True), the pages' overlap predicate T_bwd >= T_d2h + T_update per layer
+        (figure 4 caption of the paper page), and the share of the D2H + update work that ran
+        while the GPU was computing the backward sweep."""
+        for j in rec["jobs"]:
+            j.done.wait()
+        ev0, t0 = rec["ev0"], rec["host_t0"]
+        L = self.L
+        out = dict(layers=[])
+        bwd_iv = []
+        for i in range(L - 1, -1, -1):
+            lr = rec["layers"][i]
+            a, b = lr["bwd"]
+            s_ms, e_ms = ev0.elapsed_time(a), ev0.elapsed_time(b)
+            d2h_end = ev0.elapsed_time(lr["d2h_end"])
+            bwd_iv.append((t0 + s_ms / 1e3, t0 + e_ms / 1e3))
+            out["layers"].append(dict(layer=i, t_bwd_ms=e_ms - s_ms, bwd_end_ms=e_ms,
+                                      d2h_end_ms=d2h_end))
+        # D2H intervals: each copy starts when its layer's backward ends or when the previous
+        # copy on the D2H stream ends, whichever is later
+        prev_end = -1.0
+        for li in out["layers"]:
+            start = max(li["bwd_end_ms"], prev_end)
+            li["t_d2h_ms"] = max(0.0, li["d2h_end_ms"] - start)
+            li["d2h_iv"] = (t0 + start / 1e3, t0 + li["d2h_end_ms"] / 1e3)
+            prev_end = li["d2h_end_ms"]
+        jobs = {j.name: j for j in rec["jobs"]}
+        for li in out["layers"]:
+            j = jobs[f"layer{li['layer']}"]
+            li["t_update_ms"] = (j.t_end - j.t_start) * 1e3
+            li["upd_iv"] = (j.t_start, j.t_end)
+        # predicate: the update of layer i is hidden by the backward of layer i-1
+        by = {li["layer"]: li for li in out["layers"]}
+        for i in range(L):
+            nxt = by.get(i - 1)
+            li = by[i]
+            li["hidden_by_next_bwd"] = (nxt is not None and
+                                        nxt["t_bwd_ms"] >= li["t_d2h_ms"] + li["t_update_ms"])
+
+        def covered(iv, ivs):
+            tot = 0.0
+            for a, b in ivs:
+                lo, hi = max(iv[0], a), min(iv[1], b)
+                if hi > lo:
+                    tot += hi - lo
+            return tot
+
+        work = sum((li["d2h_iv"][1] - li["d2h_iv"][0]) + (li["upd_iv"][1] - li["upd_iv"][0])
+                   for li in out["layers"])
+        hid = sum(covered(li["d2h_iv"], bwd_iv) + covered(li["upd_iv"], bwd_iv)
+                  for li in out["layers"])
+        out["overlap_pct"] = 100.0 * hid / work if work > 0 else 100.0
+        out["t_bwd_total_ms"] = sum(li["t_bwd_ms"] for li in out["layers"])
+        out["t_update_total_ms"] = sum(li["t_update_ms"] for li in out["layers"])
+        out["t_d2h_total_ms"] = sum(li["t_d2h_ms"] for li in out["layers"])
+        out["predicate_layers_met"] = sum(1 for li in out["layers"] if li["hidden_by_next_bwd"])
+        out["gpu_ms"] = ev0.elapsed_time(rec["ev_end"])
+        return out

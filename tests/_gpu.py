@@ -24,16 +24,21 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def rel_err(a, r):
+def rel_err(a, r, scale=None):
+    """max|a - r| / max|r|; `scale` replaces max|r| for a reference that is identically zero
+    (then the error is measured against the size of a sibling output of the same op)."""
     a = np.asarray(a, np.float64)
     r = np.asarray(r, np.float64)
     assert a.shape == r.shape, (a.shape, r.shape)
     assert np.all(np.isfinite(a)), "non-finite values in the GPU result"
-    return float(np.max(np.abs(a - r)) / max(float(np.max(np.abs(r))), 1e-30))
+    den = float(np.max(np.abs(r))) if r.size else 0.0
+    if den == 0.0 and scale is not None:
+        den = scale
+    return float(np.max(np.abs(a - r)) / max(den, 1e-30)) if a.size else 0.0
 
 
-def assert_close(a, r, dtype, what, tol=None):
-    e = rel_err(a, r)
+def assert_close(a, r, dtype, what, tol=None, scale=None):
+    e = rel_err(a, r, scale)
     lim = TOL[dtype] if tol is None else tol
     print(f"  {what}: rel err {e:.3e} (limit {lim:.0e})", flush=True)
     assert e <= lim, f"{what}: rel err {e:.3e} > {lim:.0e}"

@@ -1,0 +1,137 @@
+"""GPU tests of the whole training step (embedding, layers through the slot ring, final norm,
+chunked CE, backward with gradient flushes and the CPU AdamW worker) against the oracle, and
+the scheduler-invariance property: offloading and overlap must not change a single bit of the
+result (the pages' offloaded training keeps the semantics of plain training)."""
+import numpy as np
+import pytest
+import torch
+
+from layer_sliding_offloaded_fwd_amd.engine import AdamW, ModelSpec, SlideEngine
+from oracle import adamw as oa
+from oracle import model as om
+from seeded_inputs import TINY, LayerCfg, Workload, model_params, tokens
+from tests._gpu import assert_close
+
+pytestmark = pytest.mark.gpu
+
+HP = AdamW()
+OHP = oa.AdamWHyper(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay)
+
+
+def _spec(w: Workload):
+    c = w.layer
+    return ModelSpec(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.vocab, w.n_layers,
+                     w.dtype, c.rms_eps, c.rope_theta)
+
+
+def _flat_layers(params, w):
+    return [np.concatenate([lp[n].f32.reshape(-1) for n, _ in w.layer.param_shapes()])
+            for lp in params["layers"]]
+
+
+def _oracle_params(params):
+    return dict(embed=params["embed"].f64,
+                layers=[{k: v.f64 for k, v in lp.items()} for lp in params["layers"]],
+                w_final=params["w_final"].f64, lm_head=params["lm_head"].f64)
+
+
+def _flat_grads(g, w):
+    return [np.concatenate([lg[n].reshape(-1) for n, _ in w.layer.param_shapes()])
+            for lg in g["layers"]]
+
+
+def test_tiny_fp32_step_matches_oracle():
+    w = TINY
+    print(f"engine step {w.name}: L={w.n_layers} H={w.layer.hidden} V={w.vocab} "
+          f"B={w.batch} S={w.seq}", flush=True)
+    params = model_params(w, seed=0)
+    tok = tokens(w.batch, w.seq, w.vocab, seed=1)
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=HP, adam_threads=4)
+    try:
+        eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
+                        params["lm_head"].f32)
+        eng.step(tok)
+        loss = eng.loss()
+        eng.wait_updates()
+        sh = om.ModelShape(om.LayerShape(256, 4, 4, 64, 688), w.n_layers, w.vocab)
+        rloss, rg = om.model_loss_and_grads(_oracle_params(params), tok, sh)
+        print(f"  loss gpu {loss:.7f} oracle {rloss:.7f}", flush=True)
+        assert abs(loss - rloss) <= 1e-4 * abs(rloss)
+        # gradients landed in the pinned host buffers (fp32 compute keeps them separate)
+        assert_close(eng.embed.grad_host.numpy(), rg["embed"].reshape(-1), "f32", "grad embed")
+        assert_close(eng.final.grad_host.numpy(), rg["w_final"], "f32", "grad w_final")
+        assert_close(eng.lm.grad_host.numpy(), rg["lm_head"].reshape(-1), "f32", "grad lm_head")
+        for i, (gg, rr) in enumerate(zip([p.grad_host.numpy() for p in eng.layers],
+                                         _flat_grads(rg, w))):
+            assert_close(gg, rr, "f32", f"grad layer {i}")
+        # the update applied on the host is the fixed-order fp32 AdamW of those gradients
+        got = eng.master_params()
+        for name, prm, p0 in [("embed", eng.embed, params["embed"].f32),
+                              ("lm_head", eng.lm, params["lm_head"].f32)]:
+            ref = oa.adamw_fp32(p0.reshape(-1), prm.grad_host.numpy(), np.zeros(prm.n, np.float32),
+                                np.zeros(prm.n, np.float32), 1, OHP)[0]
+            assert np.array_equal(got[name].view(np.uint32), ref.view(np.uint32)), name
+        # a second step sees the updated parameters (synchronous semantics)
+        eng.step(tokens(w.batch, w.seq, w.vocab, seed=2))
+        loss2 = eng.loss()
+        print(f"  step 2 loss {loss2:.7f}", flush=True)
+        assert np.isfinite(loss2) and loss2 < loss + 1e-3
+    finally:
+        eng.close()
+
+
+SMALL = Workload("small-bf16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "bf16")
+
+
+def _run(n_slots, serialize, steps=2):
+    w = SMALL
+    params = model_params(w, seed=0, gain_std=0.1)
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=n_slots, hp=HP, adam_threads=3,
+                      serialize=serialize)
+    try:
+        eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
+                        params["lm_head"].f32)
+        losses = []
+        for s in range(steps):
+            eng.step(tokens(w.batch, w.seq, w.vocab, seed=10 + s))
+            losses.append(eng.loss())
+        return losses, eng.master_params()
+    finally:
+        eng.close()
+
+
+def test_offload_and_overlap_do_not_change_results():
+    print("scheduler invariance: 3 slots overlapped vs serialized vs one slot per layer",
+          flush=True)
+    la, pa = _run(3, False)
+    lb, pb = _run(3, True)
+    lc, pc = _run(SMALL.n_layers, False)
+    lone, pone = _run(1, False)
+    print(f"  losses {la} {lb} {lc} {lone}", flush=True)
+    assert la == lb == lc == lone
+    for other in (pb, pc, pone):
+        for k in ("embed", "w_final", "lm_head"):
+            assert np.array_equal(pa[k].view(np.uint32), other[k].view(np.uint32)), k
+        for x, y in zip(pa["layers"], other["layers"]):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_bf16_model_loss_matches_oracle():
+    w = SMALL
+    print(f"engine step {w.name}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    tok = tokens(w.batch, w.seq, w.vocab, seed=10)
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=HP, adam_threads=3)
+    try:
+        eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
+                        params["lm_head"].f32)
+        eng.step(tok)
+        loss = eng.loss()
+    finally:
+        eng.close()
+    c = w.layer
+    sh = om.ModelShape(om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn),
+                       w.n_layers, w.vocab)
+    rloss, _ = om.model_loss_and_grads(_oracle_params(params), tok, sh)
+    print(f"  loss gpu {loss:.6f} oracle {rloss:.6f}", flush=True)
+    assert abs(loss - rloss) <= 2e-3 * abs(rloss)
