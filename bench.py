@@ -144,7 +144,9 @@ def main():
     t_init = time.perf_counter()
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True)
-    eng.init_random(seed=0, std=0.02)
+    print("[bench] allocating host and device state", file=sys.stderr, flush=True)
+    eng.init_random(seed=0, std=0.02,
+                    progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
             for i in range(args.warmup + args.steps)]
     t_init = time.perf_counter() - t_init

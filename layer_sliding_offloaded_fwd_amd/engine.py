@@ -187,8 +187,9 @@ class SlideEngine:
         torch.cuda.synchronize(self.device)
         self.step_count = 0
 
-    def init_random(self, seed=0, std=0.02):
-        """Seeded synthetic weights drawn on the GPU (matrices N(0, std), norm gains 1)."""
+    def init_random(self, seed=0, std=0.02, progress=None):
+        """Seeded synthetic weights drawn on the GPU (matrices N(0, std), norm gains 1).
+        progress(msg) is called every few layers."""
         self.wait_updates()
         gen = torch.Generator(device=self.device)
         gen.manual_seed(seed)
@@ -208,8 +209,10 @@ class SlideEngine:
                 prm.v.zero_()
 
         draw(self.embed)
-        for prm in self.layers:
+        for i, prm in enumerate(self.layers):
             draw(prm, gains=(offs[0], offs[3]))
+            if progress is not None and (i + 1) % 8 == 0:
+                progress(f"initialised {i + 1}/{self.L} layers")
         self.final.master.fill_(1.0)
         self._refresh_shared(self.final)
         draw(self.lm)

@@ -139,10 +139,11 @@ def test_attention_fwd_bwd(dtype, B, S, nq, nkv, d):
     assert_close(host(lse).reshape(B, nq, S), rlse, "f32", "attention lse",
                  tol=1e-4 if dtype == "f32" else 2e-3)
     g = host(dqkv).reshape(B, S, -1)
-    # with one token dS = P (dP - D) is exactly zero: measure dq against the size of dv
+    # with one token dS = P (dP - D) is exactly zero: measure dq, dk against the size of dv
     assert_close(g[..., : nq * d].reshape(B, S, nq, d), dq, dtype, "attention dq",
                  scale=float(np.max(np.abs(dv))))
-    assert_close(g[..., nq * d:(nq + nkv) * d].reshape(B, S, nkv, d), dk, dtype, "attention dk")
+    assert_close(g[..., nq * d:(nq + nkv) * d].reshape(B, S, nkv, d), dk, dtype, "attention dk",
+                 scale=float(np.max(np.abs(dv))))
     assert_close(g[..., (nq + nkv) * d:].reshape(B, S, nkv, d), dv, dtype, "attention dv")
 
 
