@@ -1,15 +1,21 @@
 // GEMMs of the decoder layer and the LM head (projections y = x W^T, their input gradients
 // dX = dY W and weight gradients dW = dY^T X).
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation. One workgroup of 256
-// threads (4 waves, 2x2) computes a 128x128 tile of C; each wave owns 64x64 = 2x2 MFMA blocks.
-// K is consumed in 64-wide tiles staged through LDS (double buffered: the next tile is fetched
-// into registers while the current one feeds the MFMAs). In LDS both operands are stored
-// K-contiguous, one 128-byte row (64 bf16) per M (or N) index, with the 16-byte chunk index
-// XOR-swizzled by (row + row/8) & 7 so that both the MFMA reads (8 consecutive rows, same chunk)
-// and the transposed writes (8 rows spaced 8 apart) hit distinct banks. An operand whose K is
-// the outer dimension in memory (dW = dY^T X, dX = dY W) is loaded as 8x8 blocks and transposed
-// in registers before the LDS write, so every layout shares the same inner loop.
+// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation. A workgroup computes a
+// BM x BN tile of C with its waves in a WGM x (waves/WGM) grid; K is consumed in 64-wide tiles
+// staged through LDS (double buffered: the next tile is fetched into registers while the current
+// one feeds the MFMAs, one barrier per tile). Two tile shapes:
+//   large: 256 x 256, 8 waves (2 x 4), wave tile 128 x 64 (4 x 2 MFMA blocks), 128 KB of LDS;
+//          half the LDS and L2 traffic per flop of the small tile
+//   small: 128 x 128, 4 waves (2 x 2), wave tile 64 x 64, 64 KB of LDS, for problems with too
+//          few large tiles to fill the 256 compute units
+// In LDS both operands are stored K-contiguous, one 128-byte row (64 bf16) per M (or N) index,
+// with the 16-byte chunk index XOR-swizzled by (row + row/8) & 7 so that both the MFMA reads
+// (8 consecutive rows, same chunk) and the transposed writes (8 rows spaced 8 apart) hit distinct
+// banks. An operand whose K is the outer dimension in memory (dW = dY^T X, dX = dY W) is loaded
+// as 8x8 blocks and transposed in registers before the LDS write (A by the first BM threads, B by
+// the last BN threads, so both transposes run in parallel), so every layout shares one inner
+// loop. Tiles are ordered XCD-aware and grouped along M for L2 reuse.
 // fp32 path (the small fp32 configuration): a plain LDS-tiled SIMT kernel, 64x64 per workgroup.
 #include "gemm.h"
 
@@ -20,75 +26,86 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+constexpr int BK = 64;
 
 __device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
 // element offset of (row, 16-byte chunk) in a [rows][64] bf16 LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
-// ---- K-major operand: rows x 64 k, 16-byte chunks, 4 per thread
-__device__ __forceinline__ void load_kmajor(uint4 (&reg)[4], const bf16_t* __restrict__ P, int ld,
-                                            int row0, int rows_total, int k0, int K) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int id = t + NT * i;
-    int r = id >> 3, c = id & 7;
-    int gr = row0 + r, gk = k0 + c * 8;
-    if (gr < rows_total && gk < K)
-      reg[i] = *(const uint4*)(P + (size_t)gr * ld + gk);
-    else
-      reg[i] = make_uint4(0, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void store_kmajor(const uint4 (&reg)[4], bf16_t* s) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int id = t + NT * i;
-    int r = id >> 3, c = id & 7;
-    *(uint4*)(s + lds_off(r, c)) = reg[i];
-  }
-}
-
-// ---- outer-K operand: memory holds [k][row], row contiguous. Thread t < 128 owns the 8x8
-// block (k-block kb = t/16, row-block rb = t%16) and transposes it in registers.
-__device__ __forceinline__ void load_outerk(uint4 (&reg)[8], const bf16_t* __restrict__ P, int ld,
-                                            int row0, int rows_total, int k0, int K) {
-  const int t = threadIdx.x;
-  if (t >= 128) return;
-  int kb = t >> 4, rb = t & 15;
-  int gr = row0 + rb * 8;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int gk = k0 + kb * 8 + j;
-    if (gr < rows_total && gk < K)
-      reg[j] = *(const uint4*)(P + (size_t)gk * ld + gr);
-    else
-      reg[j] = make_uint4(0, 0, 0, 0);
-  }
-}
 __device__ __forceinline__ uint32_t dw(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
-__device__ __forceinline__ void store_outerk(const uint4 (&reg)[8], bf16_t* s) {
-  const int t = threadIdx.x;
-  if (t >= 128) return;
-  int kb = t >> 4, rb = t & 15;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // row rb*8+i gets k = kb*8 .. kb*8+7: dword w = (k=2w, k=2w+1) from element i of v[2w], v[2w+1]
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o0 = __builtin_amdgcn_perm(dw(reg[1], i >> 1), dw(reg[0], i >> 1), sel);
-    uint32_t o1 = __builtin_amdgcn_perm(dw(reg[3], i >> 1), dw(reg[2], i >> 1), sel);
-    uint32_t o2 = __builtin_amdgcn_perm(dw(reg[5], i >> 1), dw(reg[4], i >> 1), sel);
-    uint32_t o3 = __builtin_amdgcn_perm(dw(reg[7], i >> 1), dw(reg[6], i >> 1), sel);
-    *(uint4*)(s + lds_off(rb * 8 + i, kb)) = make_uint4(o0, o1, o2, o3);
-  }
-}
 
-template <bool AK, bool BKM, int EPI, int SITE>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
+// Operand staging. Threads [0, NT/2) stage the A tile and threads [NT/2, NT) the B tile, each
+// through the same 8 x 16-byte registers: a K-major operand (memory row = M or N index) as 8
+// chunks per thread (8 consecutive threads cover one 128-byte row segment), an outer-K operand
+// (memory holds [k][row]) as one 8x8 block per thread (k-block kb, row-block rb), transposed in
+// registers before the LDS write. Requires ROWS * 8 == 8 * (NT / 2), i.e. ROWS == NT / 2.
+struct Stage {
+  uint4 r[8];
+
+  template <int ROWS, bool KMAJ>
+  __device__ __forceinline__ void load(int u, const bf16_t* __restrict__ P, int ld, int row0,
+                                       int rows_total, int k0, int K) {
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int id = u + ROWS * i;
+        const int rr = id >> 3, c = id & 7;
+        const int gr = row0 + rr, gk = k0 + c * 8;
+        r[i] = (gr < rows_total && gk < K) ? *(const uint4*)(P + (size_t)gr * ld + gk)
+                                           : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int kb = u / (ROWS / 8), rb = u % (ROWS / 8);
+      const int gr = row0 + rb * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int gk = k0 + kb * 8 + j;
+        r[j] = (gr < rows_total && gk < K) ? *(const uint4*)(P + (size_t)gk * ld + gr)
+                                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  template <int ROWS, bool KMAJ>
+  __device__ __forceinline__ void store(int u, bf16_t* s) const {
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int id = u + ROWS * i;
+        *(uint4*)(s + lds_off(id >> 3, id & 7)) = r[i];
+      }
+    } else {
+      const int kb = u / (ROWS / 8), rb = u % (ROWS / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // row rb*8+i gets k = kb*8 .. kb*8+7: dword w = (k=2w, k=2w+1), element i of r[2w], r[2w+1]
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t o0 = __builtin_amdgcn_perm(dw(r[1], i >> 1), dw(r[0], i >> 1), sel);
+        const uint32_t o1 = __builtin_amdgcn_perm(dw(r[3], i >> 1), dw(r[2], i >> 1), sel);
+        const uint32_t o2 = __builtin_amdgcn_perm(dw(r[5], i >> 1), dw(r[4], i >> 1), sel);
+        const uint32_t o3 = __builtin_amdgcn_perm(dw(r[7], i >> 1), dw(r[6], i >> 1), sel);
+        *(uint4*)(s + lds_off(rb * 8 + i, kb)) = make_uint4(o0, o1, o2, o3);
+      }
+    }
+  }
+};
+
+template <int BM_, int BN_, int NT_, int WGM_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, NT = NT_, WGM = WGM_;
+  static constexpr int NW = NT / 64, WGN = NW / WGM;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
+  static constexpr int MI = WTM / 32, NJ = WTN / 32;     // 32x32 MFMA blocks per wave
+  static constexpr int MIN_WAVES = NT >= 512 ? 2 : 2;
+};
+using TileL = Tile<256, 256, 512, 2>;
+using TileS = Tile<128, 128, 256, 2>;
+
+template <class TL, bool AK, bool BKM, int EPI, int SITE>
+__global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BM = TL::BM, BN = TL::BN, NT = TL::NT, MI = TL::MI, NJ = TL::NJ;
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
 
@@ -98,40 +115,38 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
   int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
   if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
   constexpr int GM = 8;
-  int group = logical / (GM * tiles_n);
-  int first_m = group * GM;
-  int gsize = min(tiles_m - first_m, GM);
-  int in_group = logical % (GM * tiles_n);
-  int tm = first_m + in_group % gsize, tn = in_group / gsize;
+  const int group = logical / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = logical % (GM * tiles_n);
+  const int tm = first_m + in_group % gsize, tn = in_group / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const bf16_t* A = (const bf16_t*)g.A;
   const bf16_t* B = (const bf16_t*)g.B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave % TL::WGM, wn = wave / TL::WGM;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[AK ? 4 : 8], rb[BKM ? 4 : 8];
+  static_assert(BM == NT / 2 && BN == NT / 2, "staging splits the threads evenly between A and B");
+  Stage st;
+  const bool is_a = threadIdx.x < NT / 2;
+  const int u = is_a ? threadIdx.x : threadIdx.x - NT / 2;
   auto gload = [&](int k0) {
-    if constexpr (AK) load_kmajor(ra, A, g.lda, m0, g.M, k0, g.K);
-    else load_outerk(ra, A, g.lda, m0, g.M, k0, g.K);
-    if constexpr (BKM) load_kmajor(rb, B, g.ldb, n0, g.N, k0, g.K);
-    else load_outerk(rb, B, g.ldb, n0, g.N, k0, g.K);
+    if (is_a) st.load<BM, AK>(u, A, g.lda, m0, g.M, k0, g.K);
+    else st.load<BN, BKM>(u, B, g.ldb, n0, g.N, k0, g.K);
   };
   auto lstore = [&](int buf) {
-    if constexpr (AK) store_kmajor(ra, sA[buf]);
-    else store_outerk(ra, sA[buf]);
-    if constexpr (BKM) store_kmajor(rb, sB[buf]);
-    else store_outerk(rb, sB[buf]);
+    if (is_a) st.store<BM, AK>(u, sA[buf]);
+    else st.store<BN, BKM>(u, sB[buf]);
   };
-
   const int nk = (g.K + BK - 1) / BK;
   gload(0);
   lstore(0);
@@ -144,21 +159,17 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t af[MI], bfr[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int r = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8_t*)(a_s + lds_off(r, ch));
-      }
+      for (int i = 0; i < MI; ++i)
+        af[i] = *(const bf16x8_t*)(a_s + lds_off(wm * TL::WTM + i * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int r = wn * 64 + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8_t*)(b_s + lds_off(r, ch));
-      }
+      for (int j = 0; j < NJ; ++j)
+        bfr[j] = *(const bf16x8_t*)(b_s + lds_off(wn * TL::WTN + j * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) lstore(cur ^ 1);
@@ -167,14 +178,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 
   // epilogue: acc[i][j][e] is C(row, col) with col = lane%32, row = (e/4)*8 + (lane/32)*4 + e%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
       if (col >= g.N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int row = m0 + wm * TL::WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (row >= g.M) continue;
         float v = acc[i][j][e] * g.alpha;
         if constexpr (EPI == EPI_STORE_BF16) {
@@ -185,6 +196,188 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
           v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
           ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
         } else {  // EPI_ACCUM_F32
+          float* c = (float*)g.C + (size_t)row * g.ldc + col;
+          *c = *c + v;
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------ pipelined bf16 GEMM
+// 256 x 256 tile, 8 waves (2 x 4, wave tile 128 x 64), k-tiles of 32 in 4 LDS stages fed by
+// direct global -> LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS
+// destination + 16 l), so three k-tiles are in flight without holding registers. Each wave
+// issues exactly 2 loads per operand per stage whatever the layout:
+//   K-major operand: stage = [256 rows][32 k] (64-byte rows, 4 chunks); a wave load covers 16
+//     rows; the chunk order inside a row is swizzled by ((r >> 1) ^ (r >> 3)) & 3.
+//   outer-K operand: stage = [32 k][256 rows] (512-byte rows, 32 chunks); a wave load covers 2
+//     k-rows; chunks swizzled by (0, 4, 10, 14)[k % 4]. MFMA fragments come out through the LDS
+//     transpose read ds_read_b64_tr_b16 (16-lane groups: lanes addressing 4 consecutive k-rows x
+//     16 rows deliver 4 consecutive k of one row per lane).
+// The swizzles keep both the 16-byte fragment reads and the transpose reads free of bank
+// conflicts (checked for 32 and 64 banks). Out-of-range lanes load from a zero page.
+namespace pipe {
+
+constexpr int BM = 256, BN = 256, BKP = 32, NS = 4, NT = 512, WGM = 2;
+constexpr int WTM = 128, WTN = 64, MI = 4, NJ = 2;
+constexpr int STAGE_ELEMS = 256 * 32;  // per operand
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_s4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+__device__ uint4 zero_page[4];
+
+__device__ __forceinline__ int swzk(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swzt(int k) {
+  const int t = k & 3;
+  return t == 0 ? 0 : t == 1 ? 4 : t == 2 ? 10 : 14;
+}
+
+// Issue this wave's two loads of one operand for one stage.
+template <bool KMAJ>
+__device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ P, int ld,
+                                      int row0, int rows_total, int k0, int K, int wave,
+                                      int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int instr = wave + 8 * q;          // 16 wave-loads of 1 KB cover the 16 KB stage
+    const void* src = zero_page;
+    if constexpr (KMAJ) {
+      const int r = instr * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swzk(r);
+      const int gr = row0 + r, gk = k0 + c * 8;
+      if (gr < rows_total && gk < K) src = P + (size_t)gr * ld + gk;
+    } else {
+      const int kr = instr * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swzt(kr);
+      const int gk = k0 + kr, gr = row0 + c * 8;
+      if (gk < K && gr < rows_total) src = P + (size_t)gk * ld + gr;
+    }
+    __builtin_amdgcn_global_load_lds((glob_void_t*)src, (lds_void_t*)(stage + instr * 512), 16,
+                                     0, 0);
+  }
+}
+
+// 8 bf16 of MFMA fragment row `r` (0..255 within the stage), k = 16 kk + 8 h .. + 7
+template <bool KMAJ>
+__device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk, int lane) {
+  if constexpr (KMAJ) {
+    const int r = rbase + (lane & 31);
+    const int c = (kk * 2 + (lane >> 5)) ^ swzk(r);
+    return *(const bf16x8_t*)(stage + r * BKP + c * 8);
+  } else {
+    const int g = lane >> 4, i = lane & 15;
+    const int m = rbase + 16 * (g & 1) + 4 * (i & 3);
+    const int k = kk * 16 + 8 * (g >> 1) + (i >> 2);
+    const bf16_t* p0 = stage + k * 256 + (((m >> 3) ^ swzt(k)) << 3) + (m & 7);
+    const bf16_t* p1 = stage + (k + 4) * 256 + (((m >> 3) ^ swzt(k + 4)) << 3) + (m & 7);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)p0);
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)p1);
+    typedef short short8_t __attribute__((ext_vector_type(8)));
+    const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt with vmcnt = N, expcnt and lgkmcnt left at their maxima (no wait on them)
+  static_assert(N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+}  // namespace pipe
+
+template <bool AK, bool BKM, int EPI, int SITE>
+__global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
+  using namespace pipe;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * 2 * STAGE_ELEMS];
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
+  if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  constexpr int GM = 8;
+  const int group = logical / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = logical % (GM * tiles_n);
+  const int tm = first_m + in_group % gsize, tn = in_group / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const bf16_t* A = (const bf16_t*)g.A;
+  const bf16_t* B = (const bf16_t*)g.B;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = (g.K + BKP - 1) / BKP;
+  auto stage_a = [&](int b) { return smem + b * 2 * STAGE_ELEMS; };
+  auto stage_b = [&](int b) { return smem + b * 2 * STAGE_ELEMS + STAGE_ELEMS; };
+  auto issue_stage = [&](int kt) {
+    const int b = kt % NS;
+    issue<AK>(stage_a(b), A, g.lda, m0, g.M, kt * BKP, g.K, wave, lane);
+    issue<BKM>(stage_b(b), B, g.ldb, n0, g.N, kt * BKP, g.K, wave, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue_stage(s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most the loads of the later issued stages are outstanding
+    const int later = min(nk - 1, kt + NS - 2) - kt;
+    if (later >= 2) wait_vm<8>();
+    else if (later == 1) wait_vm<4>();
+    else wait_vm<0>();
+    // Plain barrier: the explicit vmcnt wait above already covers this stage's loads, and the
+    // later stages' loads must stay in flight across it.
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + NS - 1 < nk) issue_stage(kt + NS - 1);
+    const bf16_t* sa = stage_a(kt % NS);
+    const bf16_t* sb = stage_b(kt % NS);
+#pragma unroll
+    for (int kk = 0; kk < BKP / 16; ++kk) {
+      bf16x8_t af[MI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) af[i] = frag<AK>(sa, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = frag<BKM>(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (row >= g.M) continue;
+        float v = acc[i][j][e] * g.alpha;
+        if constexpr (EPI == EPI_STORE_BF16) {
+          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          ((float*)g.C)[(size_t)row * g.ldc + col] = v;
+        } else if constexpr (EPI == EPI_RESID) {
+          v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
+          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+        } else {
           float* c = (float*)g.C + (size_t)row * g.ldc + col;
           *c = *c + v;
         }
@@ -262,10 +455,32 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+// GEMM path for large problems: 1 = register-staged 256 x 256 tile, 2 = pipelined DMA-fed tile.
+int g_gemm_path = 2;
+
+// Large tiles when they alone give at least half a wave of workgroups per compute unit.
+inline bool use_large(const GemmArgs& g) {
+  const long tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  return tiles >= 128;
+}
+
 template <bool AK, bool BKM, int EPI, int SITE>
 void launch_one(const GemmArgs& g, hipStream_t st) {
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI, SITE>), dim3(tiles), dim3(NT), 0, st, g);
+  // The pipelined kernel wins when both operands are K-major; with an outer-K operand its
+  // transpose reads are slower than the register transpose of the staged kernel.
+  if (use_large(g) && AK && BKM && g_gemm_path == 2) {
+    const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKM, EPI, SITE>), dim3(tiles), dim3(pipe::NT), 0, st,
+                       g);
+  } else if (use_large(g)) {
+    const int tiles = ((g.M + TileL::BM - 1) / TileL::BM) * ((g.N + TileL::BN - 1) / TileL::BN);
+    hipLaunchKernelGGL((gemm_bf16_kernel<TileL, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileL::NT),
+                       0, st, g);
+  } else {
+    const int tiles = ((g.M + TileS::BM - 1) / TileS::BM) * ((g.N + TileS::BN - 1) / TileS::BN);
+    hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileS::NT),
+                       0, st, g);
+  }
 }
 
 template <bool AK, bool BKM>
