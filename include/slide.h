@@ -83,7 +83,8 @@ typedef struct {
 size_t slide_layer_param_count(const slide_layer_cfg* cfg);
 /* Element offsets of the six packed tensors, in packing order. */
 int slide_layer_param_offsets(const slide_layer_cfg* cfg, size_t off[6]);
-/* Workspace bytes needed by slide_layer_fwd (bwd = 0) or slide_layer_bwd (bwd = 1). */
+/* Workspace bytes needed by slide_layer_fwd (bwd = 0), slide_layer_bwd (bwd = 1) or
+ * slide_layer_bwd_saved (bwd = 2). */
 size_t slide_layer_workspace_bytes(const slide_layer_cfg* cfg, int B, int S, int bwd);
 
 /* Forward of one layer. w_slot: packed weights (device). x, y: [B*S, H] (device), y != x.
@@ -99,6 +100,22 @@ int slide_layer_fwd(const slide_layer_cfg* cfg, const void* w_slot, const void* 
 int slide_layer_bwd(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
                     const void* dy, void* dx, void* g_slot, int B, int S, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* Keeping the forward's intermediates instead of recomputing them. The pages keep only a small
+ * window of activations on the GPU (summary, section 2B, "sliding activations"); with 288 GB of
+ * HBM the window can hold every layer's intermediates, which removes the backward's recompute.
+ * slide_layer_saved_bytes: bytes of one layer's forward intermediates for B x S tokens.
+ * slide_layer_fwd_save: slide_layer_fwd that leaves them in `saved` (caller-owned, per layer).
+ * slide_layer_bwd_saved: slide_layer_bwd that reads them from `saved` instead of recomputing;
+ * ws needs slide_layer_workspace_bytes(cfg, B, S, 2) bytes. Results are identical to the
+ * recompute path given the same inputs. */
+size_t slide_layer_saved_bytes(const slide_layer_cfg* cfg, int B, int S);
+int slide_layer_fwd_save(const slide_layer_cfg* cfg, const void* w_slot, const void* x, void* y,
+                         int B, int S, void* saved, size_t saved_bytes, void* stream);
+int slide_layer_bwd_saved(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
+                          const void* dy, void* dx, void* g_slot, int B, int S,
+                          const void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Fused LM-head cross-entropy in vocabulary chunks (summary, section 2C: projection and loss

@@ -47,6 +47,9 @@ SIGNATURES = {
     "slide_layer_workspace_bytes": (SZ, [LCP, I, I, I]),
     "slide_layer_fwd": (I, [LCP, P, P, P, I, I, P, SZ, P]),
     "slide_layer_bwd": (I, [LCP, P, P, P, P, P, I, I, P, SZ, P]),
+    "slide_layer_saved_bytes": (SZ, [LCP, I, I]),
+    "slide_layer_fwd_save": (I, [LCP, P, P, P, I, I, P, SZ, P]),
+    "slide_layer_bwd_saved": (I, [LCP, P, P, P, P, P, I, I, P, SZ, P, SZ, P]),
     "slide_lmhead_ce_workspace_bytes": (SZ, [CCP, I]),
     "slide_lmhead_ce": (I, [CCP, P, P, P, I, P, P, P, P, SZ, P]),
     "slide_embed_fwd": (I, [P, P, P, I, I, I, I, P]),

@@ -13,6 +13,7 @@ __all__ = [
     "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F32", "SLIDE_ENGINE_HIP",
     "SLIDE_ENGINE_HOST", "slide_layer_param_count", "slide_layer_param_offsets",
     "slide_layer_workspace_bytes", "slide_layer_fwd", "slide_layer_bwd",
+    "slide_layer_saved_bytes", "slide_layer_fwd_save", "slide_layer_bwd_saved",
     "slide_lmhead_ce_workspace_bytes", "slide_lmhead_ce", "slide_embed_fwd",
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
@@ -81,6 +82,21 @@ def slide_layer_fwd(cfg, w_slot, x, y, B, S, ws, ws_bytes, stream=None):
 def slide_layer_bwd(cfg, w_slot, x, dy, dx, g_slot, B, S, ws, ws_bytes, stream=None):
     call("slide_layer_bwd", ctypes.byref(cfg), _p(w_slot), _p(x), _p(dy), _p(dx), _p(g_slot),
          B, S, _p(ws), ws_bytes, _s(stream))
+
+
+def slide_layer_saved_bytes(cfg, B, S):
+    return int(lib().slide_layer_saved_bytes(ctypes.byref(cfg), B, S))
+
+
+def slide_layer_fwd_save(cfg, w_slot, x, y, B, S, saved, saved_bytes, stream=None):
+    call("slide_layer_fwd_save", ctypes.byref(cfg), _p(w_slot), _p(x), _p(y), B, S, _p(saved),
+         saved_bytes, _s(stream))
+
+
+def slide_layer_bwd_saved(cfg, w_slot, x, dy, dx, g_slot, B, S, saved, saved_bytes, ws,
+                          ws_bytes, stream=None):
+    call("slide_layer_bwd_saved", ctypes.byref(cfg), _p(w_slot), _p(x), _p(dy), _p(dx),
+         _p(g_slot), B, S, _p(saved), saved_bytes, _p(ws), ws_bytes, _s(stream))
 
 
 # ------------------------------------------------------------------------------ LM head CE

@@ -74,9 +74,10 @@ struct Ws {
   size_t bytes;
 };
 
-Ws carve(void* base, const Dims& d, bool bwd) {
+// Forward intermediates (everything the backward reads): the forward workspace, or the
+// per-layer "saved" buffer that lets the backward skip the recompute.
+size_t carve_fwd(void* base, const Dims& d, Ws& w) {
   Carver c(base);
-  Ws w{};
   const size_t N = d.N;
   auto T = [&](size_t n) { return (void*)c.take<char>(n * d.ts); };
   w.cos_t = c.take<float>((size_t)d.S * (d.d / 2));
@@ -89,18 +90,32 @@ Ws carve(void* base, const Dims& d, bool bwd) {
   w.r2 = T(N * d.H);
   w.gu = T(N * 2 * (size_t)d.F);
   w.m = T(N * d.F);
-  if (bwd) {
-    w.dm = T(N * d.F);
-    w.dgu = T(N * 2 * (size_t)d.F);
-    w.dr2 = T(N * d.H);
-    w.dx2 = T(N * d.H);
-    w.dO = T(N * d.OD);
-    w.dqkv = T(N * d.QR);
-    w.dr = T(N * d.H);
-    w.rms_ws = c.take<char>(rmsnorm_bwd_ws(d.N, d.H));
-    w.attn_ws = c.take<char>(attention_bwd_ws(d.B, d.S, d.nq));
-  }
-  w.bytes = align_up(c.used, 256);
+  return align_up(c.used, 256);
+}
+
+// Backward-only buffers.
+size_t carve_bwd(void* base, const Dims& d, Ws& w) {
+  Carver c(base);
+  const size_t N = d.N;
+  auto T = [&](size_t n) { return (void*)c.take<char>(n * d.ts); };
+  w.dm = T(N * d.F);
+  w.dgu = T(N * 2 * (size_t)d.F);
+  w.dr2 = T(N * d.H);
+  w.dx2 = T(N * d.H);
+  w.dO = T(N * d.OD);
+  w.dqkv = T(N * d.QR);
+  w.dr = T(N * d.H);
+  w.rms_ws = c.take<char>(rmsnorm_bwd_ws(d.N, d.H));
+  w.attn_ws = c.take<char>(attention_bwd_ws(d.B, d.S, d.nq));
+  return align_up(c.used, 256);
+}
+
+// Recompute layout: forward intermediates followed by the backward buffers in one workspace.
+Ws carve(void* base, const Dims& d, bool bwd) {
+  Ws w{};
+  const size_t fb = carve_fwd(base, d, w);
+  w.bytes = fb;
+  if (bwd) w.bytes += carve_bwd(base ? (char*)base + fb : nullptr, d, w);
   return w;
 }
 
@@ -139,12 +154,12 @@ int forward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* 
 }
 
 int backward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* x,
-             const void* dy, void* dx, void* g, const Ws& ws, hipStream_t st) {
+             const void* dy, void* dx, void* g, const Ws& ws, bool recompute, hipStream_t st) {
   size_t off[6];
   param_offsets(d, off);
   const size_t ts = d.ts;
   const int N = d.N, H = d.H, F = d.F;
-  SLIDE_TRY(forward(d, c, w, x, nullptr, ws, st));
+  if (recompute) SLIDE_TRY(forward(d, c, w, x, nullptr, ws, st));
   // MLP half
   SLIDE_TRY(gemm(N, F, H, dy, H, true, at(w, off[5], ts), F, false, ws.dm, F, nullptr, d.dt,
                  "gemm_down_dx", SITE_DOWN_DX, st));
@@ -202,6 +217,10 @@ extern "C" int slide_layer_param_offsets(const slide_layer_cfg* cfg, size_t off[
 
 extern "C" size_t slide_layer_workspace_bytes(const slide_layer_cfg* cfg, int B, int S, int bwd) {
   if (check_cfg(cfg) != SLIDE_OK || B < 0 || S < 0) return 0;
+  if (bwd == 2) {  // slide_layer_bwd_saved: the backward-only buffers
+    Ws w{};
+    return carve_bwd(nullptr, dims_of(*cfg, B, S), w);
+  }
   return carve(nullptr, dims_of(*cfg, B, S), bwd != 0).bytes;
 }
 
@@ -233,7 +252,43 @@ extern "C" int slide_layer_bwd(const slide_layer_cfg* cfg, const void* w_slot, c
   const Ws w0 = carve(nullptr, d, true);
   SLIDE_REQUIRE(ws_bytes >= w0.bytes, SLIDE_E_WORKSPACE, "slide_layer_bwd: workspace %zu < %zu",
                 ws_bytes, w0.bytes);
-  return backward(d, *cfg, w_slot, x, dy, dx, g_slot, carve(ws, d, true), (hipStream_t)stream);
+  return backward(d, *cfg, w_slot, x, dy, dx, g_slot, carve(ws, d, true), true,
+                  (hipStream_t)stream);
+}
+
+extern "C" size_t slide_layer_saved_bytes(const slide_layer_cfg* cfg, int B, int S) {
+  if (check_cfg(cfg) != SLIDE_OK || B < 0 || S < 0) return 0;
+  Ws w{};
+  return carve_fwd(nullptr, dims_of(*cfg, B, S), w);
+}
+
+extern "C" int slide_layer_fwd_save(const slide_layer_cfg* cfg, const void* w_slot, const void* x,
+                                    void* y, int B, int S, void* saved, size_t saved_bytes,
+                                    void* stream) {
+  return slide_layer_fwd(cfg, w_slot, x, y, B, S, saved, saved_bytes, stream);
+}
+
+extern "C" int slide_layer_bwd_saved(const slide_layer_cfg* cfg, const void* w_slot,
+                                     const void* x, const void* dy, void* dx, void* g_slot,
+                                     int B, int S, const void* saved, size_t saved_bytes,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(check_cfg(cfg));
+  SLIDE_REQUIRE(B >= 0 && S >= 0, SLIDE_E_SHAPE, "slide_layer_bwd_saved: negative B or S");
+  const Dims d = dims_of(*cfg, B, S);
+  SLIDE_TRY(check_ptrs(d, {w_slot, g_slot}));
+  if (d.N == 0) return fill_zero(g_slot, param_count(d), d.dt, (hipStream_t)stream);
+  SLIDE_TRY(check_ptrs(d, {x, dy, dx, saved, ws}));
+  SLIDE_REQUIRE(x != dx, SLIDE_E_ARG, "slide_layer_bwd_saved: dx must not alias x");
+  Ws w{};
+  const size_t fb = carve_fwd(nullptr, d, w);
+  const size_t bb = carve_bwd(nullptr, d, w);
+  SLIDE_REQUIRE(saved_bytes >= fb, SLIDE_E_WORKSPACE, "slide_layer_bwd_saved: saved %zu < %zu",
+                saved_bytes, fb);
+  SLIDE_REQUIRE(ws_bytes >= bb, SLIDE_E_WORKSPACE, "slide_layer_bwd_saved: workspace %zu < %zu",
+                ws_bytes, bb);
+  carve_fwd(const_cast<void*>(saved), d, w);
+  carve_bwd(ws, d, w);
+  return backward(d, *cfg, w_slot, x, dy, dx, g_slot, w, false, (hipStream_t)stream);
 }
 
 extern "C" int slide_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out, int N,

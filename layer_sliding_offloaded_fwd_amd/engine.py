@@ -5,7 +5,8 @@ of layer i-1 and prefetches layer i-2; figures 3-5 of the paper page).
 
 One training step:
   forward   embedding gather; layers 0..L-1 through the slot ring (weights loaded ahead on the
-            H2D stream as slots free up); only each layer's input is kept on the GPU.
+            H2D stream as slots free up); each layer's input and (by default) its forward
+            intermediates stay in HBM, so the backward does not recompute the forward.
   loss      final RMSNorm, chunked LM-head cross-entropy (loss, dh, dW_lm).
   backward  layers L-1..0: the last n_slots layers are still resident (re-claimed without a
             copy); every other layer is prefetched n_slots layers ahead; after each layer's
@@ -101,7 +102,8 @@ class _Param:
 
 class SlideEngine:
     def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
-                 adam_threads=0, device="cuda:0", serialize=False, timeline=False):
+                 adam_threads=0, device="cuda:0", serialize=False, timeline=False,
+                 save_activations=True):
         assert spec.dtype in ("bf16", "f32")
         self.spec, self.B, self.S, self.N = spec, batch, seq, batch * seq
         self.L = spec.n_layers
@@ -111,6 +113,7 @@ class SlideEngine:
         self.device = torch.device(device)
         self.serialize = serialize
         self.timeline = timeline
+        self.save_activations = save_activations
         self.code = SLIDE_BF16 if spec.dtype == "bf16" else SLIDE_F32
         self.tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
         self.ts = 2 if spec.dtype == "bf16" else 4
@@ -145,8 +148,17 @@ class SlideEngine:
         self.tok_in = torch.empty(N, dtype=torch.int32, device=dev)
         self.tok_tgt = torch.empty(N, dtype=torch.int32, device=dev)
         self.loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
-        ws = max(B.slide_layer_workspace_bytes(self.cfg, batch, seq, 1),
-                 B.slide_layer_workspace_bytes(self.cfg, batch, seq, 0),
+        # forward intermediates of every layer stay in HBM (no recompute in the backward), or
+        # only the layer inputs are kept and the backward recomputes the forward
+        if save_activations:
+            self.saved_bytes = _align(B.slide_layer_saved_bytes(self.cfg, batch, seq))
+            self.saved = torch.empty((self.L, self.saved_bytes), dtype=torch.uint8, device=dev)
+            layer_ws = B.slide_layer_workspace_bytes(self.cfg, batch, seq, 2)
+        else:
+            self.saved_bytes, self.saved = 0, None
+            layer_ws = max(B.slide_layer_workspace_bytes(self.cfg, batch, seq, 1),
+                           B.slide_layer_workspace_bytes(self.cfg, batch, seq, 0))
+        ws = max(layer_ws,
                  B.slide_lmhead_ce_workspace_bytes(self.ce_cfg, N),
                  B.slide_embed_bwd_workspace_bytes(N, V),
                  B.slide_rmsnorm_bwd_workspace_bytes(N, H))
@@ -346,8 +358,12 @@ class SlideEngine:
             s = slots.pop(i)
             w, _ = self.ring.acquire(s, c)
             e_a = self._ev(c) if self.timeline else None
-            B.slide_layer_fwd(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S, self.ws,
-                              self.ws_bytes, c)
+            if self.save_activations:
+                B.slide_layer_fwd_save(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S,
+                                       self.saved[i], self.saved_bytes, c)
+            else:
+                B.slide_layer_fwd(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S,
+                                  self.ws, self.ws_bytes, c)
             if self.timeline:
                 rec["layers"].setdefault(i, {})["fwd"] = (e_a, self._ev(c))
             self.ring.release(s, c)
@@ -388,8 +404,13 @@ class SlideEngine:
             s = slots.pop(i)
             w, g = self.ring.acquire(s, c)
             e_a = self._ev(c) if self.timeline else None
-            B.slide_layer_bwd(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g, self.B,
-                              self.S, self.ws, self.ws_bytes, c)
+            if self.save_activations:
+                B.slide_layer_bwd_saved(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g,
+                                        self.B, self.S, self.saved[i], self.saved_bytes, self.ws,
+                                        self.ws_bytes, c)
+            else:
+                B.slide_layer_bwd(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g, self.B,
+                                  self.S, self.ws, self.ws_bytes, c)
             e_b = self._ev(c) if self.timeline else None
             ticket = self.ring.flush(s, self.layers[i].grad_host, c)
             if self.timeline:

@@ -96,11 +96,11 @@ def test_tiny_fp32_step_matches_oracle():
 SMALL = Workload("small-bf16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "bf16")
 
 
-def _run(n_slots, serialize, steps=2):
+def _run(n_slots, serialize, steps=2, save=True):
     w = SMALL
     params = model_params(w, seed=0, gain_std=0.1)
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=n_slots, hp=HP, adam_threads=3,
-                      serialize=serialize)
+                      serialize=serialize, save_activations=save)
     try:
         eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
                         params["lm_head"].f32)
@@ -120,9 +120,10 @@ def test_offload_and_overlap_do_not_change_results():
     lb, pb = _run(3, True)
     lc, pc = _run(SMALL.n_layers, False)
     lone, pone = _run(1, False)
-    print(f"  losses {la} {lb} {lc} {lone}", flush=True)
-    assert la == lb == lc == lone
-    for other in (pb, pc, pone):
+    lrec, prec = _run(3, False, save=False)       # backward recomputes the forward instead
+    print(f"  losses {la} {lb} {lc} {lone} {lrec}", flush=True)
+    assert la == lb == lc == lone == lrec
+    for other in (pb, pc, pone, prec):
         for k in ("embed", "w_final", "lm_head"):
             assert np.array_equal(pa[k].view(np.uint32), other[k].view(np.uint32)), k
         for x, y in zip(pa["layers"], other["layers"]):

@@ -71,6 +71,35 @@ def test_layer_fwd_bwd_matches_oracle(name, c, dtype, B, S, gain_std):
         assert_close(gg[n], rg[n], dtype, f"grad {n}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_saved_intermediates_give_identical_results(dtype):
+    c, B, S = (LayerCfg(512, 8, 2, 64, 1376), 2, 200) if dtype == "bf16" else (TINY.layer, 2, 128)
+    print(f"layer fwd_save / bwd_saved vs recompute, {dtype}", flush=True)
+    N = B * S
+    params = layer_params(c, dtype, seed=7, gain_std=0.1)
+    x = activations((N, c.hidden), dtype, 8)
+    dy = activations((N, c.hidden), dtype, 9)
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, dtype)
+    w = _packed_to_device(params, c, dtype)
+    tx, tdy = dev(x.f32, dtype), dev(dy.f32, dtype)
+    wb = sl.slide_layer_workspace_bytes(cfg, B, S, 1)
+    y1, dx1, g1 = empty((N, c.hidden), dtype), empty((N, c.hidden), dtype), torch.empty_like(w)
+    sl.slide_layer_fwd(cfg, w, tx, y1, B, S, ws(wb), wb, stream())
+    sl.slide_layer_bwd(cfg, w, tx, tdy, dx1, g1, B, S, ws(wb), wb, stream())
+    sb = sl.slide_layer_saved_bytes(cfg, B, S)
+    w2 = sl.slide_layer_workspace_bytes(cfg, B, S, 2)
+    assert 0 < w2 < wb and sb < wb
+    saved = ws(sb)
+    y2, dx2, g2 = empty((N, c.hidden), dtype), empty((N, c.hidden), dtype), torch.empty_like(w)
+    sl.slide_layer_fwd_save(cfg, w, tx, y2, B, S, saved, sb, stream())
+    sl.slide_layer_bwd_saved(cfg, w, tx, tdy, dx2, g2, B, S, saved, sb, ws(w2), w2, stream())
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(bits(y1), bits(y2))
+    assert torch.equal(bits(dx1), bits(dx2))
+    assert torch.equal(bits(g1), bits(g2))
+
+
 def test_layer_bwd_dy_may_alias_dx():
     c, dtype, B, S = LayerCfg(256, 4, 2, 64, 688), "bf16", 1, 96
     print("layer bwd with dy aliasing dx", flush=True)
