@@ -6,11 +6,18 @@
 //
 // bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, flash-style, no [S, S]
 // tensor in memory):
+//  * every operand tile is [64 rows][d] of q, k, v or dO rows, copied global -> LDS by
+//    direct-to-LDS loads into 3 pipelined stages (two blocks in flight while one is computed).
+//    A tile is read either as rows (16-byte reads: MFMA fragments of q, k, v or dO) or, through
+//    the LDS transpose read ds_read_b64_tr_b16, as columns (fragments of v^T, k^T, q^T, dO^T),
+//    so no operand is ever transposed in registers. The 16-byte chunks of row r are XOR-swizzled
+//    by f(r) (d = 64: 2(r&3) ^ ((r>>2)&3); d = 128: 2(r&3) ^ 5((r>>2)&3)), which keeps both read
+//    kinds free of bank conflicts.
 //  * forward and dQ: 128 queries per workgroup (32 per wave), keys in blocks of 64. Each wave
 //    computes S^T = K Q^T so that a lane owns one query: row max / row sum are in-lane plus one
 //    exchange with the lane 32 away. O^T += V^T P^T (and dQ^T += K^T dS^T) take P (dS) straight
-//    from the score accumulators as the B operand: the 16 keys an MFMA consumes are ordered the
-//    way the accumulator holds them, and V (K) is staged transposed in LDS in that same order.
+//    from the score accumulators as the B operand; the 16 keys an MFMA consumes are ordered the
+//    way the accumulator holds them, and the transpose reads fetch V^T (K^T) in that order.
 //  * dK/dV: 128 keys per workgroup, looping over the G query heads of the kv group and over the
 //    query blocks on or after the diagonal, so dK and dV are summed without atomics (the result
 //    is deterministic). dQ runs as its own kernel.
@@ -28,76 +35,84 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int LDT = 68;  // row length (elements) of transposed tiles: 64 keys + 4 padding
-// LDS elements needed to stage four waves' 32 x D output tiles (rows padded to D + 8)
-template <int D> constexpr int stage_elems() { return 128 * (D + 8); }
-template <int D> constexpr int at_least_stage(int n) { return n > stage_elems<D>() ? n : stage_elems<D>(); }
+constexpr int NSTAGE = 3;  // LDS stages of the key (or query) block pipeline
 
-__device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  uint4 u;
-  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_s4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
 
-__device__ __forceinline__ bf16x8_t zero8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+__device__ uint4 attn_zero_page[4];
 
-// [64 rows][D] tile, 16-byte chunk c of row r stored at chunk c ^ (r & 7).
 template <int D>
-__device__ __forceinline__ void rows_to_lds(bf16_t* s, const bf16_t* g, int stride, int row0,
-                                            int nvalid) {
-  constexpr int KCH = D / 8;
-  for (int id = threadIdx.x; id < 64 * KCH; id += 256) {
-    const int r = id / KCH, c = id % KCH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nvalid) v = *(const uint4*)(g + (size_t)(row0 + r) * stride + c * 8);
-    *(uint4*)(s + r * D + ((c ^ (r & 7)) << 3)) = v;
-  }
+__device__ __forceinline__ int fsw(int r) {
+  return D == 128 ? ((2 * (r & 3)) ^ (5 * ((r >> 2) & 3))) : ((2 * (r & 3)) ^ ((r >> 2) & 3));
 }
 template <int D>
-__device__ __forceinline__ bf16x8_t rows_read(const bf16_t* s, int r, int c) {
-  return *(const bf16x8_t*)(s + r * D + ((c ^ (r & 7)) << 3));
+__device__ __forceinline__ int tile_off(int r, int c) {  // element offset of (row, 16-B chunk c)
+  return r * D + ((c ^ fsw<D>(r)) << 3);
 }
 
-__device__ __forceinline__ uint32_t dwsel(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// Transposed tile [D][LDT]: element (d, r) = row r, column d of the 64-row source tile.
+// Per-wave direct-to-LDS loads of a [64][D] tile (rows row0.. of a strided global matrix). The
+// tile's D*128 bytes are split into 1 KB wave loads; wave w issues loads w, w+4, ...
 template <int D>
-__device__ __forceinline__ void rows_to_lds_t(bf16_t* st, const bf16_t* g, int stride, int row0,
-                                              int nvalid) {
-  constexpr int DB = D / 8;  // 8-wide d blocks
-  const int t = threadIdx.x;
-  if (t >= 8 * DB) return;
-  const int kb = t / DB, db = t % DB;
-  uint4 v[8];
+__device__ __forceinline__ void tile_issue(bf16_t* tile, const bf16_t* g, int stride, int row0,
+                                           int nvalid, int wave, int lane) {
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;          // rows per 1 KB wave load
+  constexpr int LOADS = 64 / RPL;       // wave loads per tile
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = kb * 8 + j;
-    v[j] = r < nvalid ? *(const uint4*)(g + (size_t)(row0 + r) * stride + db * 8)
-                      : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t o0 = __builtin_amdgcn_perm(dwsel(v[1], i >> 1), dwsel(v[0], i >> 1), sel);
-    const uint32_t o1 = __builtin_amdgcn_perm(dwsel(v[3], i >> 1), dwsel(v[2], i >> 1), sel);
-    const uint32_t o2 = __builtin_amdgcn_perm(dwsel(v[5], i >> 1), dwsel(v[4], i >> 1), sel);
-    const uint32_t o3 = __builtin_amdgcn_perm(dwsel(v[7], i >> 1), dwsel(v[6], i >> 1), sel);
-    bf16_t* p = st + (db * 8 + i) * LDT + kb * 8;
-    *(uint2*)p = make_uint2(o0, o1);
-    *(uint2*)(p + 4) = make_uint2(o2, o3);
+  for (int q = wave; q < LOADS; q += 4) {
+    const int r = q * RPL + lane / CH;
+    const int c = (lane % CH) ^ fsw<D>(r);
+    const void* src = attn_zero_page;
+    if (r < nvalid) src = g + (size_t)(row0 + r) * stride + c * 8;
+    __builtin_amdgcn_global_load_lds((glob_void_t*)src, (lds_void_t*)(tile + q * 512), 16, 0, 0);
   }
 }
-// A operand from a transposed tile for the key-ordered MFMA step ks: keys 16ks + 4hf + {0..3}
-// and 16ks + 8 + 4hf + {0..3} of row d.
-__device__ __forceinline__ bf16x8_t t_read(const bf16_t* st, int d, int ks, int hf) {
-  const bf16_t* p = st + d * LDT + ks * 16 + hf * 4;
-  const uint2 a = *(const uint2*)p, b = *(const uint2*)(p + 8);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+template <int D> constexpr int tile_loads_per_wave() { return (64 / (64 / (D / 8))) / 4; }
+
+// 16-byte row read: row r, chunk c (8 consecutive columns)
+template <int D>
+__device__ __forceinline__ bf16x8_t rows_read(const bf16_t* t, int r, int c) {
+  return *(const bf16x8_t*)(t + tile_off<D>(r, c));
+}
+
+// LDS transpose read ds_read_b64_tr_b16 issued through inline asm. (With direct-to-LDS loads in
+// flight the compiler would otherwise drain every outstanding load before each transpose read,
+// including the next stages', which serializes the pipeline.) The result is only valid after
+// tr_wait() on it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ short4_t tr_issue(const bf16_t* p) {
+  short4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr(p)));
+  return v;
+}
+// Wait for all outstanding LDS reads of this wave, then pin the N values after the wait so that
+// no use of them can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void tr_wait(bf16x8_t (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// Column fragment through two transpose reads: A operand of an MFMA whose row index is the tile
+// column d0 + lane%32 and whose 8 k values are tile rows 16ks + 4h + {0..3} and
+// 16ks + 8 + 4h + {0..3} (h = lane/32), i.e. the key order of a score accumulator.
+template <int D>
+__device__ __forceinline__ bf16x8_t t_read(const bf16_t* t, int d0, int ks, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = d0 + 16 * (g & 1) + 4 * (i & 3);
+  const int r0 = ks * 16 + 4 * (g >> 1) + (i >> 2);
+  const int r1 = r0 + 8;
+  const short4_t lo = tr_issue(t + tile_off<D>(r0, col >> 3) + (col & 7));
+  const short4_t hi = tr_issue(t + tile_off<D>(r1, col >> 3) + (col & 7));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // score accumulator element i of sub-block kb (32 keys) -> key offset within the 64-key block
@@ -105,8 +120,22 @@ __device__ __forceinline__ int acc_key(int kb, int i, int hf) {
   return kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// Wait until at most `later` stages of `per` loads each are still outstanding.
+template <int PER>
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= 2) wait_vm<(2 * PER < 16 ? 2 * PER : 15)>();
+  else if (later == 1) wait_vm<PER>();
+  else wait_vm<0>();
+}
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Stage a wave's 32 x D output tile (held transposed in accumulators) through LDS and write
-// 16-byte row chunks: out row r (0..31) of this wave goes to dst + row_index(r) * stride.
+// 16-byte row chunks: out row r (0..31) of this wave goes to dst + (row0 + r) * stride.
 template <int D>
 __device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc, float scale,
                                              bf16_t* dst, int stride, int row0, int nvalid,
@@ -128,23 +157,37 @@ __device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc,
   }
 }
 
+__device__ __forceinline__ bf16x8_t pack8(const float* v) {
+  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 b8;
+  b8 r = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3],
+          (__bf16)v[4], (__bf16)v[5], (__bf16)v[6], (__bf16)v[7]};
+  return r;
+}
+__device__ __forceinline__ bf16x8_t zero8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+
+template <int D> constexpr int stage_elems() { return 128 * (D + 8); }
+template <int D> constexpr int smem_elems(int tiles) {
+  return NSTAGE * tiles * 64 * D > stage_elems<D>() ? NSTAGE * tiles * 64 * D : stage_elems<D>();
+}
+
 // ------------------------------------------------------------------ forward
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                        bf16_t* __restrict__ out,
                                                        float* __restrict__ lse, int S, int nq,
                                                        int nkv, float scale) {
-  constexpr int NKK = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(64 * D + D * LDT)];
-  bf16_t* sK = smem;
-  bf16_t* sVt = smem + 64 * D;
+  constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
+  auto tK = [&](int b) { return smem + b * 2 * 64 * D; };
+  auto tV = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };
 
   const int nqb = (S + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
   const int h = blockIdx.y, b = blockIdx.z;
   const int g = h / (nq / nkv);
   const int QS = (nq + 2 * nkv) * D;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wq0 = qb * 128 + wave * 32;
   const int q = wq0 + lr;
   const bf16_t* base = qkv + (size_t)b * S * QS;
@@ -166,13 +209,23 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict_
   const int nkvb = q_last / 64 + 1;
   const bf16_t* kbase = base + (nq + g) * D;
   const bf16_t* vbase = base + (nq + nkv + g) * D;
+  auto issue = [&](int jb) {
+    const int kv0 = jb * 64, st = jb % NSTAGE;
+    tile_issue<D>(tK(st), kbase, QS, kv0, min(64, S - kv0), wave, lane);
+    tile_issue<D>(tV(st), vbase, QS, kv0, min(64, S - kv0), wave, lane);
+  };
+#pragma unroll
+  for (int j = 0; j < NSTAGE - 1; ++j)
+    if (j < nkvb) issue(j);
+
   for (int jb = 0; jb < nkvb; ++jb) {
-    const int kv0 = jb * 64, nvalid = min(64, S - kv0);
-    __syncthreads();
-    rows_to_lds<D>(sK, kbase, QS, kv0, nvalid);
-    rows_to_lds_t<D>(sVt, vbase, QS, kv0, nvalid);
-    __syncthreads();
+    const int kv0 = jb * 64;
+    wait_stage<PER>(min(nkvb - 1, jb + NSTAGE - 2) - jb);
+    plain_barrier();
+    if (jb + NSTAGE - 1 < nkvb) issue(jb + NSTAGE - 1);
     if (kv0 > wq0 + 31) continue;  // every key of this block is after every query of the wave
+    const bf16_t* sK = tK(jb % NSTAGE);
+    const bf16_t* sV = tV(jb % NSTAGE);
 
     f32x16_t sacc[2];
 #pragma unroll
@@ -184,14 +237,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict_
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
     }
+    const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + acc_key(kb, i, hf);
         float s = sacc[kb][i] * sl2;
-        if (key > q || key >= S) s = -INFINITY;
+        if (need_mask) {
+          const int key = kv0 + acc_key(kb, i, hf);
+          if (key > q || key >= S) s = -INFINITY;
+        }
         sacc[kb][i] = s;
         mx = fmaxf(mx, s);
       }
@@ -221,14 +277,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
       const bf16x8_t pf = pack8(pv);
+      bf16x8_t vt[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vt[db] = t_read<D>(sV, db * 32, ks, lane);
+      tr_wait(vt);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sVt, db * 32 + lr, ks, hf), pf,
-                                                           oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[db], pf, oacc[db], 0, 0, 0);
     }
   }
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   if (hf == 0 && q < S) lse[((size_t)b * nq + h) * S + q] = m2 * kLn2 + logf(l);
+  wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
   store_tile_t<D>(stage, oacc, inv_l, out + (size_t)b * S * nq * D + h * D, nq * D, wq0,
@@ -266,18 +326,18 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__
                                                       const float* __restrict__ delta,
                                                       bf16_t* __restrict__ dqkv, int S, int nq,
                                                       int nkv, float scale) {
-  constexpr int NKK = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(2 * 64 * D + D * LDT)];
-  bf16_t* sK = smem;
-  bf16_t* sV = smem + 64 * D;
-  bf16_t* sKt = smem + 2 * 64 * D;
+  constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
+  auto tK = [&](int b) { return smem + b * 2 * 64 * D; };
+  auto tV = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };
 
   const int nqb = (S + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int g = h / (nq / nkv);
   const int QS = (nq + 2 * nkv) * D, OS = nq * D;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wq0 = qb * 128 + wave * 32;
   const int q = wq0 + lr;
   const bf16_t* base = qkv + (size_t)b * S * QS;
@@ -303,14 +363,23 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__
   const int nkvb = q_last / 64 + 1;
   const bf16_t* kbase = base + (nq + g) * D;
   const bf16_t* vbase = base + (nq + nkv + g) * D;
+  auto issue = [&](int jb) {
+    const int kv0 = jb * 64, st = jb % NSTAGE;
+    tile_issue<D>(tK(st), kbase, QS, kv0, min(64, S - kv0), wave, lane);
+    tile_issue<D>(tV(st), vbase, QS, kv0, min(64, S - kv0), wave, lane);
+  };
+#pragma unroll
+  for (int j = 0; j < NSTAGE - 1; ++j)
+    if (j < nkvb) issue(j);
+
   for (int jb = 0; jb < nkvb; ++jb) {
-    const int kv0 = jb * 64, nvalid = min(64, S - kv0);
-    __syncthreads();
-    rows_to_lds<D>(sK, kbase, QS, kv0, nvalid);
-    rows_to_lds<D>(sV, vbase, QS, kv0, nvalid);
-    rows_to_lds_t<D>(sKt, kbase, QS, kv0, nvalid);
-    __syncthreads();
+    const int kv0 = jb * 64;
+    wait_stage<PER>(min(nkvb - 1, jb + NSTAGE - 2) - jb);
+    plain_barrier();
+    if (jb + NSTAGE - 1 < nkvb) issue(jb + NSTAGE - 1);
     if (kv0 > wq0 + 31) continue;
+    const bf16_t* sK = tK(jb % NSTAGE);
+    const bf16_t* sV = tV(jb % NSTAGE);
 
     f32x16_t sacc[2], pacc[2];
 #pragma unroll
@@ -328,14 +397,16 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__
             rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb], 0, 0, 0);
       }
     }
-    // dS = P * (dP - D), P = exp(s*scale - lse)
+    const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S) || (wq0 + 32 > S);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + acc_key(kb, i, hf);
         float p = exp2f(sacc[kb][i] * sl2 - lse2);
-        if (key > q || key >= S || q >= S) p = 0.f;
+        if (need_mask) {
+          const int key = kv0 + acc_key(kb, i, hf);
+          if (key > q || key >= S || q >= S) p = 0.f;
+        }
         sacc[kb][i] = p * (pacc[kb][i] - dl);
       }
 #pragma unroll
@@ -344,12 +415,16 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 8; ++j) sv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
       const bf16x8_t sf = pack8(sv);
+      bf16x8_t kt[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) kt[db] = t_read<D>(sK, db * 32, ks, lane);
+      tr_wait(kt);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sKt, db * 32 + lr, ks, hf), sf,
-                                                         dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db], sf, dq[db], 0, 0, 0);
     }
   }
+  wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
   store_tile_t<D>(stage, dq, scale, dqkv + (size_t)b * S * QS + h * D, QS, wq0, min(32, S - wq0),
@@ -364,27 +439,24 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
                                                        const float* __restrict__ delta,
                                                        bf16_t* __restrict__ dqkv, int S, int nq,
                                                        int nkv, float scale) {
-  constexpr int NKK = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[at_least_stage<D>(2 * 64 * D + 2 * D * LDT)];
-  __shared__ float sL[64], sDl[64];
-  bf16_t* sQ = smem;
-  bf16_t* sO = smem + 64 * D;  // dO rows
-  bf16_t* sQt = smem + 2 * 64 * D;
-  bf16_t* sOt = sQt + D * LDT;
+  constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
+  __shared__ float sL[NSTAGE][64], sDl[NSTAGE][64];
+  auto tQ = [&](int b) { return smem + b * 2 * 64 * D; };
+  auto tO = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };  // dO rows
 
-  const int nkb = (S + 127) / 128;
-  const int kblk = blockIdx.x;  // key blocks: earliest keys have the most query blocks; go first
+  const int kblk = blockIdx.x;  // earliest keys have the most query blocks: launched first
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = nq / nkv;
   const int QS = (nq + 2 * nkv) * D, OS = nq * D;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, lr = lane & 31;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int k0 = kblk * 128;
   const int wk0 = k0 + wave * 32;
   const int key = wk0 + lr;
   const bf16_t* base = qkv + (size_t)b * S * QS;
   const bf16_t* dobase = dout + (size_t)b * S * OS;
   const float sl2 = scale * kLog2e;
-  (void)nkb;
 
   bf16x8_t kf[NKK], vf[NKK];
 #pragma unroll
@@ -401,71 +473,96 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
       dv[db][e] = 0.f;
     }
 
-  const int nqblk = (S + 63) / 64;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    for (int jb = k0 / 64; jb < nqblk; ++jb) {
-      const int q0 = jb * 64, nvalid = min(64, S - q0);
-      __syncthreads();
-      rows_to_lds<D>(sQ, base + h * D, QS, q0, nvalid);
-      rows_to_lds<D>(sO, dobase + h * D, OS, q0, nvalid);
-      rows_to_lds_t<D>(sQt, base + h * D, QS, q0, nvalid);
-      rows_to_lds_t<D>(sOt, dobase + h * D, OS, q0, nvalid);
-      if (threadIdx.x < 64) {
-        const int qq = q0 + threadIdx.x;
-        sL[threadIdx.x] = qq < S ? lse[((size_t)b * nq + h) * S + qq] * kLog2e : 0.f;
-        sDl[threadIdx.x] = qq < S ? delta[((size_t)b * nq + h) * S + qq] : 0.f;
-      }
-      __syncthreads();
-      if (q0 + 63 < wk0) continue;  // every query of this block precedes every key of the wave
+  // flattened (head of the group, query block on or after the diagonal) sequence
+  const int qb0 = k0 / 64, nqblk = (S + 63) / 64, per_head = nqblk - qb0;
+  const int total = G * per_head;
+  auto issue = [&](int it) {
+    const int hh = it / per_head, jb = qb0 + it % per_head, st = it % NSTAGE;
+    const int h = g * G + hh, q0 = jb * 64, nvalid = min(64, S - q0);
+    tile_issue<D>(tQ(st), base + h * D, QS, q0, nvalid, wave, lane);
+    tile_issue<D>(tO(st), dobase + h * D, OS, q0, nvalid, wave, lane);
+    // the block's log-sum-exp (wave 0) and D = rowsum(dO * O) (wave 1), 4 bytes per lane
+    if (wave < 2) {
+      const float* src = (const float*)attn_zero_page;
+      if (q0 + lane < S)
+        src = (wave == 0 ? lse : delta) + ((size_t)b * nq + h) * S + q0 + lane;
+      __builtin_amdgcn_global_load_lds((glob_void_t*)src,
+                                       (lds_void_t*)(wave == 0 ? sL[st] : sDl[st]), 4, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NSTAGE - 1; ++j)
+    if (j < total) issue(j);
 
-      f32x16_t sacc[2], pacc[2];
+  for (int it = 0; it < total; ++it) {
+    const int hh = it / per_head, jb = qb0 + it % per_head, st = it % NSTAGE;
+    const int q0 = jb * 64;
+    (void)hh;
+    const int later = min(total - 1, it + NSTAGE - 2) - it;
+    if (wave < 2) wait_stage<PER + 1>(later);  // waves 0 and 1 issue one extra load per stage
+    else wait_stage<PER>(later);
+    plain_barrier();
+    if (it + NSTAGE - 1 < total) issue(it + NSTAGE - 1);
+    if (q0 + 63 < wk0) continue;  // every query of this block precedes every key of the wave
+    const bf16_t* sQ = tQ(st);
+    const bf16_t* sO = tO(st);
+
+    f32x16_t sacc[2], pacc[2];
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sacc[qb2][e] = 0.f;
-          pacc[qb2][e] = 0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          sacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc[qb2], 0, 0, 0);
-          pacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc[qb2], 0, 0, 0);
-        }
+      for (int e = 0; e < 16; ++e) {
+        sacc[qb2][e] = 0.f;
+        pacc[qb2][e] = 0.f;
       }
-      // element i of sub-block qb2 is (query q0 + acc_key(qb2, i), this lane's key)
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = acc_key(qb2, i, hf);
-          const int qq = q0 + ql;
-          float p = exp2f(sacc[qb2][i] * sl2 - sL[ql]);
-          if (key > qq || qq >= S) p = 0.f;
-          sacc[qb2][i] = p;
-          pacc[qb2][i] = p * (pacc[qb2][i] - sDl[ql]);
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float pv[8], sv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-          sv[j] = pacc[ks >> 1][8 * (ks & 1) + j];
-        }
-        const bf16x8_t pf = pack8(pv), sf = pack8(sv);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sOt, db * 32 + lr, ks, hf), pf,
-                                                           dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_read(sQt, db * 32 + lr, ks, hf), sf,
-                                                           dk[db], 0, 0, 0);
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        sacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc[qb2], 0, 0, 0);
+        pacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc[qb2], 0, 0, 0);
       }
     }
+    const bool need_mask = (q0 < wk0 + 31) || (q0 + 64 > S) || (wk0 + 32 > S);
+    // element i of sub-block qb2 is (query q0 + acc_key(qb2, i), this lane's key)
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ql = acc_key(qb2, i, hf);
+        float p = exp2f(sacc[qb2][i] * sl2 - sL[st][ql] * kLog2e);
+        if (need_mask) {
+          const int qq = q0 + ql;
+          if (key > qq || qq >= S) p = 0.f;
+        }
+        sacc[qb2][i] = p;
+        pacc[qb2][i] = p * (pacc[qb2][i] - sDl[st][ql]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pv[8], sv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
+        sv[j] = pacc[ks >> 1][8 * (ks & 1) + j];
+      }
+      const bf16x8_t pf = pack8(pv), sf = pack8(sv);
+      bf16x8_t ot[NDB], qt[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) ot[db] = t_read<D>(sO, db * 32, ks, lane);
+      tr_wait(ot);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[db], pf, dv[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) qt[db] = t_read<D>(sQ, db * 32, ks, lane);
+      tr_wait(qt);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], sf, dk[db], 0, 0, 0);
+    }
   }
+  wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
   const int nv = min(32, S - wk0);

@@ -260,6 +260,17 @@ __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ 
   }
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Wait for this wave's outstanding LDS reads and pin the fragments after the wait.
+template <int N>
+__device__ __forceinline__ void tr_wait(bf16x8_t (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
 // 8 bf16 of MFMA fragment row `r` (0..255 within the stage), k = 16 kk + 8 h .. + 7
 template <bool KMAJ>
 __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk, int lane) {
@@ -273,8 +284,11 @@ __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk,
     const int k = kk * 16 + 8 * (g >> 1) + (i >> 2);
     const bf16_t* p0 = stage + k * 256 + (((m >> 3) ^ swzt(k)) << 3) + (m & 7);
     const bf16_t* p1 = stage + (k + 4) * 256 + (((m >> 3) ^ swzt(k + 4)) << 3) + (m & 7);
-    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)p0);
-    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)p1);
+    // inline asm: the compiler would drain all in-flight direct-to-LDS loads before each
+    // builtin transpose read; the caller waits on the results with tr_wait()
+    short4_t lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(lds_addr(p0)));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(lds_addr(p1)));
     typedef short short8_t __attribute__((ext_vector_type(8)));
     const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
@@ -351,6 +365,8 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
       for (int i = 0; i < MI; ++i) af[i] = frag<AK>(sa, wm * WTM + i * 32, kk, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[j] = frag<BKM>(sb, wn * WTN + j * 32, kk, lane);
+      if constexpr (!AK) tr_wait(af);
+      if constexpr (!BKM) tr_wait(bfr);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -466,9 +482,9 @@ inline bool use_large(const GemmArgs& g) {
 
 template <bool AK, bool BKM, int EPI, int SITE>
 void launch_one(const GemmArgs& g, hipStream_t st) {
-  // The pipelined kernel wins when both operands are K-major; with an outer-K operand its
-  // transpose reads are slower than the register transpose of the staged kernel.
-  if (use_large(g) && AK && BKM && g_gemm_path == 2) {
+  // The pipelined kernel is faster whenever A is K-major (forward projections, dX); for dW
+  // (both operands outer-K) the register-transposing staged kernel is faster.
+  if (use_large(g) && AK && g_gemm_path == 2) {
     const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
     hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKM, EPI, SITE>), dim3(tiles), dim3(pipe::NT), 0, st,
                        g);

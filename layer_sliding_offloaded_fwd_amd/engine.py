@@ -23,7 +23,6 @@ Every device buffer is allocated once, up front (section 2B: pre-allocated, no f
 All numerical work runs in libslide (HIP kernels and the C++ AdamW); this module only orders
 calls on streams and threads. PyTorch provides device memory, pinned host memory and streams.
 """
-import queue
 import threading
 import time
 from dataclasses import dataclass, field
@@ -64,11 +63,12 @@ def _align(n, a=256):
 
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step")
+                 "t_end", "t_ready", "step", "priority", "seq")
 
-    def __init__(self, name, wait, p, g, m, v, out, n, step, post=None):
+    def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None):
         self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
-        self.out, self.n, self.post, self.step = out, n, post, step
+        self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
+        self.seq = 0
         self.done = threading.Event()
         self.t_start = self.t_end = self.t_ready = 0.0
 
@@ -165,8 +165,13 @@ class SlideEngine:
         self.ws_bytes = _align(ws)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
 
-        # CPU optimizer worker
-        self.jobs = queue.Queue()
+        # CPU optimizer worker: runs, among the updates whose gradients have landed, the one the
+        # next forward needs first (embedding, then layers in forward order, LM head last), so
+        # the updates still pending at the end of a backward overlap the next forward
+        self.jobs = []
+        self.jobs_cv = threading.Condition()
+        self.job_seq = 0
+        self.worker_stop = False
         self.worker_error = None
         self.worker = threading.Thread(target=self._worker_loop, daemon=True, name="slide-adamw")
         self.worker.start()
@@ -254,34 +259,63 @@ class SlideEngine:
                     lm_head=self.lm.master.numpy().copy())
 
     # ------------------------------------------------------------------ CPU worker
+    def _landed(self, job):
+        """Non-blocking: have this job's gradients arrived in host memory?"""
+        if job.wait is None:
+            return True
+        if isinstance(job.wait, int):
+            try:
+                self.ring.wait_flush(job.wait, 0)
+                return True
+            except B.SlideError as e:
+                if e.code == -6:   # SLIDE_E_TIMEOUT: still in flight
+                    return False
+                raise
+        return job.wait.query()
+
     def _worker_loop(self):
         while True:
-            job = self.jobs.get()
-            if job is None:
-                return
+            with self.jobs_cv:
+                while not self.jobs and not self.worker_stop:
+                    self.jobs_cv.wait()
+                if not self.jobs and self.worker_stop:
+                    return
+                pending = list(self.jobs)
             try:
-                if isinstance(job.wait, int):
-                    self.ring.wait_flush(job.wait, -1)
-                elif job.wait is not None:
-                    job.wait.synchronize()
-                job.t_ready = time.perf_counter()
-                B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
-                                  job.step, self.hp, self.adam_threads)
-                job.t_start = job.t_ready
-                job.t_end = time.perf_counter()
-                if job.post is not None:
-                    job.post()
+                ready = [j for j in pending if self._landed(j)]
+            except Exception as e:
+                self.worker_error = e
+                ready = pending
+            if not ready:
+                time.sleep(50e-6)
+                continue
+            job = min(ready, key=lambda j: (j.priority, j.seq))
+            with self.jobs_cv:
+                self.jobs.remove(job)
+            try:
+                if self.worker_error is None:
+                    job.t_ready = time.perf_counter()
+                    B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
+                                      job.step, self.hp, self.adam_threads)
+                    job.t_start = job.t_ready
+                    job.t_end = time.perf_counter()
+                    if job.post is not None:
+                        job.post()
             except Exception as e:  # surfaced on the main thread by wait_updates / step
                 self.worker_error = e
             finally:
                 job.done.set()
 
-    def _submit(self, prm, wait, name, post=None):
+    def _submit(self, prm, wait, name, priority, post=None):
         out = prm.shared if prm.dtype == "bf16" else None
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
-                   self.step_count, post)
+                   self.step_count, priority, post)
         prm.job = job
-        self.jobs.put(job)
+        with self.jobs_cv:
+            self.job_seq += 1
+            job.seq = self.job_seq
+            self.jobs.append(job)
+            self.jobs_cv.notify()
         if self.serialize:
             job.done.wait()
         return job
@@ -298,7 +332,9 @@ class SlideEngine:
 
     def close(self):
         self.wait_updates()
-        self.jobs.put(None)
+        with self.jobs_cv:
+            self.worker_stop = True
+            self.jobs_cv.notify()
         self.worker.join()
         self.ring.close()
 
@@ -312,7 +348,7 @@ class SlideEngine:
         ev.record(stream)
         return ev
 
-    def _flush_resident(self, prm, name):
+    def _flush_resident(self, prm, name, priority):
         """D2H of a resident block's device gradient after the compute stream, then AdamW, then
         the refreshed device copy goes back up on the H2D stream."""
         ev_c = torch.cuda.Event()
@@ -324,7 +360,7 @@ class SlideEngine:
             done = torch.cuda.Event()
             done.record(self.d2h)
         prm.flushed_ev = done
-        return self._submit(prm, done, name, post=lambda: self._upload_resident(prm))
+        return self._submit(prm, done, name, priority, post=lambda: self._upload_resident(prm))
 
     def step(self, tokens):
         """One training step on int32 tokens [B, S+1] (inputs [:, :S], targets [:, 1:]).
@@ -350,11 +386,28 @@ class SlideEngine:
         if self.embed.flushed_ev is not None:
             c.wait_event(self.embed.flushed_ev)
         B.slide_embed_fwd(self.embed.dev, self.tok_in, self.xs[0], N, H, V, self.code, c)
+        # Prefetch: load layers in order into free slots as soon as their update is done,
+        # without blocking; block only for the layer the forward needs next.
         slots = {}
-        for i in range(self.n_slots):
-            self._wait_param(self.layers[i])
-            slots[i] = self.ring.load(i, self.layers[i].shared)
+        nxt = [0]
+        free = [self.n_slots]
+
+        def prefetch(need=None):
+            while nxt[0] < L and free[0] > 0:
+                j = nxt[0]
+                job = self.layers[j].job
+                if job is not None and not job.done.is_set():
+                    if need != j:
+                        return
+                    self._wait_param(self.layers[j])
+                slots[j] = self.ring.load(j, self.layers[j].shared)
+                nxt[0] += 1
+                free[0] -= 1
+
+        prefetch()
         for i in range(L):
+            if i not in slots:
+                prefetch(need=i)
             s = slots.pop(i)
             w, _ = self.ring.acquire(s, c)
             e_a = self._ev(c) if self.timeline else None
@@ -367,11 +420,9 @@ class SlideEngine:
             if self.timeline:
                 rec["layers"].setdefault(i, {})["fwd"] = (e_a, self._ev(c))
             self.ring.release(s, c)
+            free[0] += 1
             self._sync()
-            j = i + self.n_slots
-            if j < L:
-                self._wait_param(self.layers[j])
-                slots[j] = self.ring.load(j, self.layers[j].shared)
+            prefetch()
 
         # ---- loss
         self._wait_param(self.final)
@@ -389,11 +440,11 @@ class SlideEngine:
                           self.dhf, self.lm.grad, self.ws, self.ws_bytes, c)
         if self.timeline:
             rec["ce"] = (e_ce, self._ev(c))
-        self._flush_resident(self.lm, "lm_head")
+        self._flush_resident(self.lm, "lm_head", L + 1)
         B.slide_rmsnorm_bwd(self.dhf, self.xs[L], self.final.dev, None, self.grad_x,
                             self.final.grad, N, H, spec.rms_eps, self.code, self.ws,
                             self.ws_bytes, c)
-        self._flush_resident(self.final, "w_final")
+        self._flush_resident(self.final, "w_final", L)
         self._sync()
 
         # ---- backward: the last n_slots layers are still in their slots; claim them all
@@ -416,7 +467,7 @@ class SlideEngine:
             if self.timeline:
                 rec["layers"].setdefault(i, {})["bwd"] = (e_a, e_b)
                 rec["layers"][i]["d2h_end"] = self._ev(self.d2h)
-            rec["jobs"].append(self._submit(self.layers[i], ticket, f"layer{i}"))
+            rec["jobs"].append(self._submit(self.layers[i], ticket, f"layer{i}", i))
             self.ring.release(s, c)
             self._sync()
             j = i - self.n_slots
@@ -426,7 +477,7 @@ class SlideEngine:
         # ---- embedding gradient
         B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
                           self.ws, self.ws_bytes, c)
-        self._flush_resident(self.embed, "embed")
+        self._flush_resident(self.embed, "embed", -1)
         e_end = self._ev(c)
         e_end.synchronize()
         rec["ev0"], rec["ev_end"] = ev0, e_end
@@ -439,62 +490,72 @@ class SlideEngine:
         return float(self.loss_dev.item())
 
     # ------------------------------------------------------------------ timeline analysis
-    def analyse(self, rec, d2h_gbps=None):
-        """Per-layer backward time, gradient D2H time and CPU update time of one recorded step
-        (timeline=True), the pages' overlap predicate T_bwd >= T_d2h + T_update per layer
-        (figure 4 caption of the paper page), and the share of the D2H + update work that ran
-        while the GPU was computing the backward sweep."""
-        for j in rec["jobs"]:
-            j.done.wait()
-        ev0, t0 = rec["ev0"], rec["host_t0"]
+    def analyse(self, recs):
+        """Timeline of recorded steps (timeline=True): per-layer backward, gradient D2H and CPU
+        update times; the pages' per-layer overlap predicate T_bwd >= T_d2h + T_update (figure 4
+        caption of the paper page), checked as: the update of layer i is hidden by the backward
+        of layer i-1; and the share of the D2H + update work that ran while the GPU was busy with
+        layer or loss kernels (of the same step or the next one)."""
+        if isinstance(recs, dict):
+            recs = [recs]
         L = self.L
-        out = dict(layers=[])
-        bwd_iv = []
-        for i in range(L - 1, -1, -1):
-            lr = rec["layers"][i]
-            a, b = lr["bwd"]
-            s_ms, e_ms = ev0.elapsed_time(a), ev0.elapsed_time(b)
-            d2h_end = ev0.elapsed_time(lr["d2h_end"])
-            bwd_iv.append((t0 + s_ms / 1e3, t0 + e_ms / 1e3))
-            out["layers"].append(dict(layer=i, t_bwd_ms=e_ms - s_ms, bwd_end_ms=e_ms,
-                                      d2h_end_ms=d2h_end))
-        # D2H intervals: each copy starts when its layer's backward ends or when the previous
-        # copy on the D2H stream ends, whichever is later
-        prev_end = -1.0
-        for li in out["layers"]:
-            start = max(li["bwd_end_ms"], prev_end)
-            li["t_d2h_ms"] = max(0.0, li["d2h_end_ms"] - start)
-            li["d2h_iv"] = (t0 + start / 1e3, t0 + li["d2h_end_ms"] / 1e3)
-            prev_end = li["d2h_end_ms"]
-        jobs = {j.name: j for j in rec["jobs"]}
-        for li in out["layers"]:
-            j = jobs[f"layer{li['layer']}"]
-            li["t_update_ms"] = (j.t_end - j.t_start) * 1e3
-            li["upd_iv"] = (j.t_start, j.t_end)
-        # predicate: the update of layer i is hidden by the backward of layer i-1
-        by = {li["layer"]: li for li in out["layers"]}
-        for i in range(L):
-            nxt = by.get(i - 1)
-            li = by[i]
-            li["hidden_by_next_bwd"] = (nxt is not None and
-                                        nxt["t_bwd_ms"] >= li["t_d2h_ms"] + li["t_update_ms"])
+        gpu_iv, work_iv, per_layer = [], [], []
+        for rec in recs:
+            for j in rec["jobs"]:
+                j.done.wait()
+            ev0, t0 = rec["ev0"], rec["host_t0"]
+            to_host = lambda e: t0 + ev0.elapsed_time(e) / 1e3
+            for i, lr in rec["layers"].items():
+                for key in ("fwd", "bwd"):
+                    if key in lr:
+                        gpu_iv.append((to_host(lr[key][0]), to_host(lr[key][1])))
+            if "ce" in rec:
+                gpu_iv.append((to_host(rec["ce"][0]), to_host(rec["ce"][1])))
+            jobs = {j.name: j for j in rec["jobs"]}
+            prev_end = -1e30
+            for i in range(L - 1, -1, -1):
+                lr = rec["layers"][i]
+                bs, be = to_host(lr["bwd"][0]), to_host(lr["bwd"][1])
+                d_end = to_host(lr["d2h_end"])
+                d_start = max(be, prev_end)   # the copy starts after its backward and the
+                prev_end = d_end              # previous copy on the D2H stream
+                j = jobs[f"layer{i}"]
+                work_iv.append((d_start, d_end))
+                work_iv.append((j.t_start, j.t_end))
+                per_layer.append(dict(step=rec["step"], layer=i, t_bwd_ms=(be - bs) * 1e3,
+                                      t_d2h_ms=max(0.0, d_end - d_start) * 1e3,
+                                      t_update_ms=(j.t_end - j.t_start) * 1e3))
+        # merge GPU intervals
+        gpu_iv.sort()
+        merged = []
+        for a, b in gpu_iv:
+            if merged and a <= merged[-1][1]:
+                merged[-1][1] = max(merged[-1][1], b)
+            else:
+                merged.append([a, b])
 
-        def covered(iv, ivs):
+        def covered(iv):
             tot = 0.0
-            for a, b in ivs:
+            for a, b in merged:
                 lo, hi = max(iv[0], a), min(iv[1], b)
                 if hi > lo:
                     tot += hi - lo
             return tot
 
-        work = sum((li["d2h_iv"][1] - li["d2h_iv"][0]) + (li["upd_iv"][1] - li["upd_iv"][0])
-                   for li in out["layers"])
-        hid = sum(covered(li["d2h_iv"], bwd_iv) + covered(li["upd_iv"], bwd_iv)
-                  for li in out["layers"])
-        out["overlap_pct"] = 100.0 * hid / work if work > 0 else 100.0
-        out["t_bwd_total_ms"] = sum(li["t_bwd_ms"] for li in out["layers"])
-        out["t_update_total_ms"] = sum(li["t_update_ms"] for li in out["layers"])
-        out["t_d2h_total_ms"] = sum(li["t_d2h_ms"] for li in out["layers"])
-        out["predicate_layers_met"] = sum(1 for li in out["layers"] if li["hidden_by_next_bwd"])
-        out["gpu_ms"] = ev0.elapsed_time(rec["ev_end"])
-        return out
+        work = sum(b - a for a, b in work_iv)
+        hid = sum(covered(iv) for iv in work_iv)
+        by = {(li["step"], li["layer"]): li for li in per_layer}
+        met = 0
+        for li in per_layer:
+            nxt = by.get((li["step"], li["layer"] - 1))
+            if nxt is not None and nxt["t_bwd_ms"] >= li["t_d2h_ms"] + li["t_update_ms"]:
+                met += 1
+        n = max(len(recs), 1)
+        return dict(
+            overlap_pct=100.0 * hid / work if work > 0 else 100.0,
+            t_bwd_total_ms=sum(li["t_bwd_ms"] for li in per_layer) / n,
+            t_update_total_ms=sum(li["t_update_ms"] for li in per_layer) / n,
+            t_d2h_total_ms=sum(li["t_d2h_ms"] for li in per_layer) / n,
+            predicate_layers_met=met / n,
+            gpu_ms=sum(r["ev0"].elapsed_time(r["ev_end"]) for r in recs) / n,
+            layers=per_layer)
