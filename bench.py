@@ -112,39 +112,74 @@ def cpu_baseline(w, budget_note=True):
             "sample_seconds": round(t_layer + t_ce + t_ad, 2)}
 
 
-def main():
+def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3-8b-shaped",
+                    choices=["llama3-8b-shaped", "123b-shaped-slice", "lmhead-ce-128k",
+                             "critical-batch-sweep", "layer-kernels-8b"],
+                    help="llama3-8b-shaped (default: the headline step), 123b-shaped-slice, "
+                         "lmhead-ce-128k (the chunked CE alone), critical-batch-sweep, "
+                         "layer-kernels-8b (one 8B-shaped layer's kernels alone, plus a 1 GiB "
+                         "device copy that calibrates HBM byte counters)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers of the 123b slice (default 12, fewer if host RAM is short)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
                     help="CPU AdamW threads (default: cores - 1)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        _die_multi_gpu(max(args.gpus, world))
+    return ap.parse_args()
 
+
+def _kernel_table(prof, alg, exe, byt):
+    kernels = {}
+    for name, (cnt, ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        avg_ms = ms / max(cnt, 1)
+        k = {"launches": cnt, "total_ms": round(ms, 3), "avg_ms": round(avg_ms, 4)}
+        if name in alg:
+            k["tflops_alg"] = round(alg[name] / (avg_ms * 1e-3) / 1e12, 1)
+            k["tflops_exec"] = round(exe[name] / (avg_ms * 1e-3) / 1e12, 1)
+        if name in byt:
+            k["gbs"] = round(byt[name] / (avg_ms * 1e-3) / 1e9, 1)
+        kernels[name] = k
+    return kernels
+
+
+def _roofline(kernels, alg):
+    mfma_names = [n for n in kernels if n in alg]
+    dom = max(mfma_names, key=lambda n: kernels[n]["total_ms"])
+    dk = kernels[dom]
+    achieved = alg[dom] / (dk["avg_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom]}
+
+
+def _host_bytes_needed(w):
+    c = w.layer
+    n = w.n_layers * c.param_count() + 2 * w.vocab * c.hidden + c.hidden
+    return n * 14          # fp32 master + m + v (12 B) and the pinned bf16 buffer (2 B)
+
+
+def run_step(w, args):
     import torch
     import layer_sliding_offloaded_fwd_amd as sl
     from layer_sliding_offloaded_fwd_amd.engine import AdamW, ModelSpec, SlideEngine
-    from seeded_inputs import L8B, tokens as draw_tokens
+    from seeded_inputs import tokens as draw_tokens
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    sl.lib()  # fail loudly if libslide.so is missing
-    w = L8B
     c = w.layer
     spec = ModelSpec(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.vocab, w.n_layers,
                      "bf16", c.rms_eps, c.rope_theta)
     cores = len(os.sched_getaffinity(0))
     threads = args.adam_threads or max(1, cores - 1)
     t_init = time.perf_counter()
+    print(f"[bench] {w.name}: {w.n_layers} layers, host state {_host_bytes_needed(w) / 1e9:.1f} GB;"
+          f" allocating", file=sys.stderr, flush=True)
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True)
-    print("[bench] allocating host and device state", file=sys.stderr, flush=True)
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
@@ -172,40 +207,23 @@ def main():
     print(f"[bench] {args.steps} steps: {step_s * 1e3:.1f} ms/step, {tok_s:.0f} tokens/s, "
           f"loss {loss:.4f}", file=sys.stderr, flush=True)
 
-    # ---- kernels
     alg, exe = kernel_flops(spec, w.batch, w.seq, w.ce_chunk)
-    byt = kernel_bytes(spec, w.batch, w.seq)
-    kernels = {}
-    for name, (cnt, ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
-        avg_ms = ms / max(cnt, 1)
-        k = {"launches": cnt, "total_ms": round(ms, 3), "avg_ms": round(avg_ms, 4)}
-        if name in alg:
-            k["tflops_alg"] = round(alg[name] / (avg_ms * 1e-3) / 1e12, 1)
-            k["tflops_exec"] = round(exe[name] / (avg_ms * 1e-3) / 1e12, 1)
-        if name in byt:
-            k["gbs"] = round(byt[name] / (avg_ms * 1e-3) / 1e9, 1)
-        kernels[name] = k
-    mfma_names = [n for n in kernels if n in alg]
-    dom = max(mfma_names, key=lambda n: kernels[n]["total_ms"])
-    dk = kernels[dom]
-    achieved = alg[dom] / (dk["avg_ms"] * 1e-3) / 1e12
-    # forward projections and attention run twice per step (forward and recompute in the
-    # backward): the algorithmic count takes them once
+    kernels = _kernel_table(prof, alg, exe, kernel_bytes(spec, w.batch, w.seq))
+    # forward projections and attention run once per step when the forward's intermediates are
+    # kept (the engine's default); with the recompute they would run twice
     fwd_names = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attn_fwd"}
-    layer_names = [n for n in mfma_names if n.startswith(("gemm_", "attn_"))]
+    layer_names = [n for n in kernels if n in alg and n.startswith(("gemm_", "attn_"))]
     lt = sum(kernels[n]["total_ms"] for n in layer_names) * 1e-3
-    l_alg = sum(alg[n] * kernels[n]["launches"] * (0.5 if n in fwd_names else 1.0)
+    fwd_runs = 1 if eng.save_activations else 2
+    l_alg = sum(alg[n] * kernels[n]["launches"] / (fwd_runs if n in fwd_names else 1)
                 for n in layer_names)
     l_exe = sum(exe[n] * kernels[n]["launches"] for n in layer_names)
     mfma_util_alg = 100.0 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     mfma_util_exec = 100.0 * l_exe / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
-
-    # ---- overlap (timed steps)
     ana = eng.analyse(eng.records[-args.steps:])
-    gpu_ms = ana["gpu_ms"]
     eng.close()
-
-    result = {
+    layer_bytes = w.n_layers * c.param_count() * 28
+    return {
         "metric": "train tokens/sec (1 GPU) + layer MFMA util % + backward/update overlap %",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
@@ -223,7 +241,7 @@ def main():
                    "ffn": c.ffn, "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
                    "ring_slots": w.ring_slots, "ce_chunk": w.ce_chunk,
                    "parallelism": "single GPU, layers streamed from host",
-                   "adam_threads": threads},
+                   "adam_threads": threads, "activations": "kept in HBM (no recompute)"},
         "layer_mfma_util_pct": round(mfma_util_alg, 2),
         "layer_mfma_util_exec_pct": round(mfma_util_exec, 2),
         "overlap_pct": round(ana["overlap_pct"], 1),
@@ -231,15 +249,285 @@ def main():
                     "t_d2h_total_ms": round(ana["t_d2h_total_ms"], 1),
                     "t_update_total_ms": round(ana["t_update_total_ms"], 1),
                     "layers_meeting_T_bwd_ge_T_d2h_plus_T_update": ana["predicate_layers_met"],
-                    "gpu_span_ms_per_step": round(gpu_ms, 1)},
+                    "gpu_span_ms_per_step": round(ana["gpu_ms"], 1)},
+        # CPU AdamW of the layer parameters: fp32 master, m, v read and written (24 B), the
+        # bf16 gradient read and the bf16 weight written (4 B)
+        "host_adamw_gbs": round(layer_bytes / (ana["t_update_total_ms"] * 1e-3) / 1e9, 1)
+        if ana["t_update_total_ms"] else None,
         "loss_last_step": round(loss, 4),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom]},
+        "roofline": _roofline(kernels, alg),
         "kernels": kernels,
         "init_s": round(t_init, 1),
     }
+
+
+def run_ce(args):
+    """The chunked LM-head CE alone: 16384 tokens, hidden 4096, vocab 128256, chunks of 8192."""
+    import torch
+    import layer_sliding_offloaded_fwd_amd as sl
+    from seeded_inputs import CE_ONLY
+    N, H, V, C = CE_ONLY["tokens"], CE_ONLY["hidden"], CE_ONLY["vocab"], CE_ONLY["chunk"]
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    h = torch.empty(N, H, device=dev, dtype=torch.float32).normal_(0, 1, generator=gen).bfloat16()
+    w = torch.empty(V, H, device=dev, dtype=torch.float32).normal_(0, 0.02, generator=gen).bfloat16()
+    t = torch.randint(0, V, (N,), device=dev, dtype=torch.int32, generator=gen)
+    cfg = sl.CeCfg(H, V, C, sl.SLIDE_BF16)
+    wsz = sl.slide_lmhead_ce_workspace_bytes(cfg, N)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    dh = torch.empty_like(h)
+    dw = torch.empty_like(w)
+    st = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sl.slide_lmhead_ce(cfg, h, w, t, N, loss, dh, dw, ws, wsz, st)
+    torch.cuda.synchronize()
+    sl.slide_prof_reset()
+    sl.slide_prof_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        sl.slide_lmhead_ce(cfg, h, w, t, N, loss, dh, dw, ws, wsz, st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    sl.slide_prof_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    flops_alg = 3 * 2 * N * H * V
+    flops_exec = 4 * 2 * N * H * V
+    nch = (V + C - 1) // C
+    per = 2 * N * V * H / nch
+    alg = {"ce_logits_gemm": per / 2, "ce_dh_gemm": per, "ce_dw_gemm": per}
+    exe = {"ce_logits_gemm": per, "ce_dh_gemm": per, "ce_dw_gemm": per}
+    kernels = _kernel_table(sl.slide_prof_read(), alg, exe, {})
+    return {
+        "metric": "chunked LM-head cross-entropy fwd+bwd tokens/sec (1 GPU)",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "lmhead-ce-128k", "tokens": N, "hidden": H, "vocab": V, "chunk": C},
+        "tflops_alg": round(flops_alg / (ms * 1e-3) / 1e12, 1),
+        "tflops_exec": round(flops_exec / (ms * 1e-3) / 1e12, 1),
+        "mfma_util_alg_pct": round(100 * flops_alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "workspace_bytes": wsz, "dense_fp32_logits_bytes": N * V * 4,
+        "workspace_vs_dense_logits_pct": round(100.0 * wsz / (N * V * 4), 1),
+        "loss": round(float(loss.item()), 5),
+        "roofline": _roofline(kernels, alg), "kernels": kernels,
+    }
+
+
+def run_sweep(args):
+    """The pages' critical batch (figure 4 of the paper page): for one 8B-shaped layer at
+    S = 1024 and B = 1..32, the layer backward time on the GPU against the D2H time of its
+    gradients plus the CPU AdamW time of its parameters."""
+    import torch
+    import layer_sliding_offloaded_fwd_amd as sl
+    from seeded_inputs import L8B
+    c, S = L8B.layer, 1024
+    dev = "cuda:0"
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, "bf16")
+    P = sl.slide_layer_param_count(cfg)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    w = (torch.empty(P, device=dev).normal_(0, 0.02, generator=gen)).bfloat16()
+    offs = sl.slide_layer_param_offsets(cfg)
+    w[offs[0]:offs[0] + c.hidden] = 1.0
+    w[offs[3]:offs[3] + c.hidden] = 1.0
+    g = torch.empty_like(w)
+    st = torch.cuda.current_stream()
+    # T_grad_d2h: the layer's bf16 gradients to pinned host memory
+    cores = len(os.sched_getaffinity(0))
+    threads = args.adam_threads or max(1, cores - 1)
+    host_g = torch.empty(P, dtype=torch.bfloat16, pin_memory=True)
+    for _ in range(2):
+        host_g.copy_(g, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(5):
+        host_g.copy_(g, non_blocking=True)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_d2h = e0.elapsed_time(e1) / 5
+    # T_update: the CPU AdamW of the layer's parameters
+    pm = np.random.default_rng(0).standard_normal(P).astype(np.float32)
+    mm = np.zeros(P, np.float32)
+    vv = np.zeros(P, np.float32)
+    gb = host_g.view(torch.int16).numpy()
+    hp = sl.AdamWHp(1e-4, 0.9, 0.999, 1e-8, 0.01)
+    ts = []
+    for k in range(4):
+        a = time.perf_counter()
+        # in place, as in the step: the bf16 gradient buffer receives the new bf16 weights
+        sl.slide_cpu_adamw(pm, gb, sl.SLIDE_BF16, mm, vv, gb, P, k + 1, hp, threads)
+        ts.append(time.perf_counter() - a)
+    t_upd = min(ts[1:]) * 1e3
+    rows = []
+    crit = None
+    for Bb in (1, 2, 4, 8, 16, 32):
+        N = Bb * S
+        x = torch.empty(N, c.hidden, device=dev).normal_(0, 1, generator=gen).bfloat16()
+        dy = torch.empty_like(x).normal_(0, 1, generator=gen)
+        y = torch.empty_like(x)
+        dx = torch.empty_like(x)
+        sb = sl.slide_layer_saved_bytes(cfg, Bb, S)
+        wb = sl.slide_layer_workspace_bytes(cfg, Bb, S, 2)
+        saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+        ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+        sl.slide_layer_fwd_save(cfg, w, x, y, Bb, S, saved, sb, st)
+        sl.slide_layer_bwd_saved(cfg, w, x, dy, dx, g, Bb, S, saved, sb, ws, wb, st)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(3):
+            sl.slide_layer_bwd_saved(cfg, w, x, dy, dx, g, Bb, S, saved, sb, ws, wb, st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        t_bwd = e0.elapsed_time(e1) / 3
+        ok = t_bwd >= t_d2h + t_upd
+        if ok and crit is None:
+            crit = Bb
+        rows.append({"batch": Bb, "tokens": N, "t_bwd_ms": round(t_bwd, 3),
+                     "t_grad_d2h_ms": round(t_d2h, 3), "t_update_ms": round(t_upd, 3),
+                     "full_overlap": ok})
+        print(f"[bench] B={Bb}: T_bwd {t_bwd:.2f} ms vs T_d2h {t_d2h:.2f} + T_update "
+              f"{t_upd:.2f} ms", file=sys.stderr, flush=True)
+        del x, dy, y, dx, saved, ws
+    per_seq = rows[-1]["t_bwd_ms"] / rows[-1]["batch"]
+    extrap = int(np.ceil((t_d2h + t_upd) / per_seq))
+    return {
+        "metric": "critical batch size: smallest B with T_bwd >= T_grad_d2h + T_update",
+        "value": crit if crit is not None else extrap, "unit": "sequences of 1024 tokens",
+        "n_gpus": 1, "higher_is_better": False, "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "measured": crit is not None,
+        "config": {"workload": "critical-batch-sweep", "layer": "llama3-8b-shaped", "seq_len": S,
+                   "params_per_layer": P, "adam_threads": threads},
+        "rows": rows,
+        "d2h_gbs": round(P * 2 / (t_d2h * 1e-3) / 1e9, 1),
+        "adamw_host_gbs": round(P * 28 / (t_upd * 1e-3) / 1e9, 1),
+    }
+
+
+def run_layer_kernels(args):
+    """One 8B-shaped layer's forward (keeping its intermediates) and backward at batch 8 x 1024,
+    alone on the GPU: the same kernels at the same shapes as in the step, without the host
+    traffic. Then a plain 1 GiB device-to-device copy, the reference a byte counter is scaled
+    by."""
+    import torch
+    import layer_sliding_offloaded_fwd_amd as sl
+    from seeded_inputs import L8B
+    c, Bb, S = L8B.layer, L8B.batch, L8B.seq
+    N = Bb * S
+    dev = "cuda:0"
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, "bf16")
+    P = sl.slide_layer_param_count(cfg)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    w = torch.empty(P, device=dev).normal_(0, 0.02, generator=gen).bfloat16()
+    offs = sl.slide_layer_param_offsets(cfg)
+    w[offs[0]:offs[0] + c.hidden] = 1.0
+    w[offs[3]:offs[3] + c.hidden] = 1.0
+    g = torch.empty_like(w)
+    x = torch.empty(N, c.hidden, device=dev).normal_(0, 1, generator=gen).bfloat16()
+    dy = torch.empty_like(x).normal_(0, 1, generator=gen)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    sb = sl.slide_layer_saved_bytes(cfg, Bb, S)
+    wb = sl.slide_layer_workspace_bytes(cfg, Bb, S, 2)
+    saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+
+    def one():
+        sl.slide_layer_fwd_save(cfg, w, x, y, Bb, S, saved, sb, st)
+        sl.slide_layer_bwd_saved(cfg, w, x, dy, dx, g, Bb, S, saved, sb, ws, wb, st)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    sl.slide_prof_reset()
+    sl.slide_prof_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        one()
+    e1.record(st)
+    torch.cuda.synchronize()
+    sl.slide_prof_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    spec = type("Spec", (), dict(hidden=c.hidden, ffn=c.ffn, head_dim=c.head_dim,
+                                 n_heads=c.n_heads, n_kv_heads=c.n_kv_heads, vocab=L8B.vocab))
+    alg, exe = kernel_flops(spec, Bb, S, L8B.ce_chunk)
+    kernels = _kernel_table(sl.slide_prof_read(), alg, exe, kernel_bytes(spec, Bb, S))
+    lt = sum(k["total_ms"] for n, k in kernels.items() if n in alg) * 1e-3
+    l_alg = sum(alg[n] * k["launches"] for n, k in kernels.items() if n in alg)
+    # the calibration copy: 1 GiB read and 1 GiB written by the runtime's copy kernel
+    del saved, ws
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record(st)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / 3
+    return {
+        "metric": "one decoder layer fwd+bwd, kernels alone (1 GPU)",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer-kernels-8b", "hidden": c.hidden, "heads": c.n_heads,
+                   "kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "ffn": c.ffn,
+                   "global_batch": Bb, "seq_len": S},
+        "layer_mfma_util_pct": round(100 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": _roofline(kernels, alg), "kernels": kernels,
+        "copy_ref": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(copy_ms, 4),
+                     "gbs_read_plus_write": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)},
+    }
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        _die_multi_gpu(max(args.gpus, world))
+    import torch
+    import layer_sliding_offloaded_fwd_amd as sl
+    from seeded_inputs import L8B, L123B
+    import dataclasses
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sl.lib()  # fail loudly if libslide.so is missing
+    if args.workload == "lmhead-ce-128k":
+        print(json.dumps(run_ce(args)))
+        return
+    if args.workload == "critical-batch-sweep":
+        print(json.dumps(run_sweep(args)))
+        return
+    if args.workload == "layer-kernels-8b":
+        print(json.dumps(run_layer_kernels(args)))
+        return
+    if args.workload == "123b-shaped-slice":
+        layers = args.layers or L123B.n_layers
+        w = dataclasses.replace(L123B, n_layers=layers)
+        try:
+            import psutil
+            avail = psutil.virtual_memory().available
+            while layers > 1 and _host_bytes_needed(w) > 0.85 * avail:
+                layers -= 1
+                w = dataclasses.replace(L123B, n_layers=layers)
+        except ImportError:
+            pass
+        result = run_step(w, args)
+        print(json.dumps(result))
+        return
+    w = L8B
+    result = run_step(w, args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w)

@@ -23,6 +23,7 @@ Every device buffer is allocated once, up front (section 2B: pre-allocated, no f
 All numerical work runs in libslide (HIP kernels and the C++ AdamW); this module only orders
 calls on streams and threads. PyTorch provides device memory, pinned host memory and streams.
 """
+import mmap
 import threading
 import time
 from dataclasses import dataclass, field
@@ -73,24 +74,68 @@ class _Job:
         self.t_start = self.t_end = self.t_ready = 0.0
 
 
+class _PinnedPool:
+    """Exact-size pinned host buffers from hipHostMalloc (PyTorch's pinned allocator rounds each
+    request up to a power of two, which wastes up to half of the host RAM the method needs)."""
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                            ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        self._ptrs = []
+
+    def tensor(self, n, dtype):
+        ct = self._ct
+        esize = torch.empty(0, dtype=dtype).element_size()
+        nbytes = max(n * esize, 64)
+        ptr = ct.c_void_p()
+        rc = self._hip.hipHostMalloc(ct.byref(ptr), nbytes, 0)
+        if rc != 0 or not ptr.value:
+            raise MemoryError(f"hipHostMalloc({nbytes}) failed with {rc}")
+        self._ptrs.append(ptr.value)
+        buf = (ct.c_uint8 * nbytes).from_address(ptr.value)
+        return torch.frombuffer(buf, dtype=dtype, count=n)
+
+    def free(self):
+        for p in self._ptrs:
+            self._hip.hipHostFree(self._ct.c_void_p(p))
+        self._ptrs = []
+
+
+def _host_f32(n):
+    """Zero-filled pageable fp32 host array on transparent huge pages where the kernel allows
+    (fewer TLB misses for the CPU optimizer's streaming passes)."""
+    nbytes = max(4 * n, 4)
+    try:
+        mm = mmap.mmap(-1, nbytes, flags=mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS)
+        if hasattr(mmap, "MADV_HUGEPAGE"):
+            mm.madvise(mmap.MADV_HUGEPAGE)
+        return torch.from_numpy(np.frombuffer(mm, dtype=np.float32, count=n))
+    except (OSError, ValueError):
+        return torch.zeros(n, dtype=torch.float32)
+
+
 class _Param:
     """Host state of one parameter block: fp32 master, AdamW moments, the pinned buffer that
     serves as upload source and gradient landing zone, and (for resident blocks) the device
     copy and device gradient."""
 
-    def __init__(self, n, dtype, device=None, resident=False):
+    def __init__(self, n, dtype, pinned, device=None, resident=False):
         self.n = n
         self.dtype = dtype
         if dtype == "bf16":
-            self.master = torch.empty(n, dtype=torch.float32)
-            self.shared = torch.empty(n, dtype=torch.int16, pin_memory=True)   # bf16 bits
+            self.master = _host_f32(n)
+            self.shared = pinned.tensor(n, torch.int16)        # bf16 bits
             self.grad_host = self.shared
         else:
-            self.master = torch.empty(n, dtype=torch.float32, pin_memory=True)
-            self.shared = self.master                                           # upload source
-            self.grad_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
-        self.m = torch.zeros(n, dtype=torch.float32)
-        self.v = torch.zeros(n, dtype=torch.float32)
+            self.master = pinned.tensor(n, torch.float32)      # upload source
+            self.shared = self.master
+            self.grad_host = pinned.tensor(n, torch.float32)
+        self.m = _host_f32(n)
+        self.v = _host_f32(n)
         self.job = None
         if resident:
             tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -131,10 +176,11 @@ class SlideEngine:
         self.d2h = torch.cuda.Stream(device=self.device)
 
         # host parameter blocks
-        self.layers = [_Param(self.P, s.dtype) for _ in range(self.L)]
-        self.embed = _Param(V * H, s.dtype, self.device, resident=True)
-        self.final = _Param(H, s.dtype, self.device, resident=True)
-        self.lm = _Param(V * H, s.dtype, self.device, resident=True)
+        self.pinned = _PinnedPool()
+        self.layers = [_Param(self.P, s.dtype, self.pinned) for _ in range(self.L)]
+        self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
+        self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
+        self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
 
         # device memory, allocated once
         dev = self.device
@@ -337,6 +383,10 @@ class SlideEngine:
             self.jobs_cv.notify()
         self.worker.join()
         self.ring.close()
+        torch.cuda.synchronize(self.device)
+        for prm in self.layers + [self.embed, self.final, self.lm]:
+            prm.master = prm.shared = prm.grad_host = None
+        self.pinned.free()
 
     # ------------------------------------------------------------------ step
     def _sync(self):
