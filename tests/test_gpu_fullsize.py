@@ -1,0 +1,156 @@
+"""GPU parity at the full sizes the step runs: one Llama-3-8B-shaped layer at batch 8 x 1024
+through the same entry points the engine calls (slide_layer_fwd_save / slide_layer_bwd_saved),
+and the chunked LM-head CE at the full 128256-row vocabulary with 8192 and 16384 tokens.
+
+The oracle cannot run the whole launch in seconds, so each test compares what it can compute
+exactly on a sample, plus properties that hold at any size:
+- layer: a sequence's outputs depend only on that sequence and the weights, so one sequence of
+  the batch is checked against the oracle row by row; the batch's weight gradients are the sum
+  of the per-sequence ones (checked against eight single-sequence launches), and one
+  single-sequence weight gradient is checked against the oracle;
+- CE: with every target but a sample ignored, the full-size launch computes exactly the oracle's
+  CE of the sample (loss, dh and the whole dW); without the mask, sampled dh rows equal the
+  sample's dh rescaled by the number of valid targets, and the loss and dW of the whole batch
+  are the token-weighted combination of its two halves.
+"""
+import numpy as np
+import pytest
+import torch
+
+import layer_sliding_offloaded_fwd_amd as sl
+from oracle import model as om
+from seeded_inputs import L8B, CE_ONLY, activations, ce_inputs, layer_params, pack_layer
+from tests._gpu import DEV, assert_close, dev, empty, host, rel_err, stream, ws
+
+pytestmark = pytest.mark.gpu
+
+
+def _unpack(g, c):
+    out, o = {}, 0
+    for name, shape in c.param_shapes():
+        n = int(np.prod(shape))
+        out[name] = g[o:o + n].reshape(shape)
+        o += n
+    return out
+
+
+def test_layer_8b_at_bench_launch():
+    c, B, S, dtype = L8B.layer, L8B.batch, L8B.seq, "bf16"
+    N, H = B * S, c.hidden
+    print(f"8B layer at B={B} S={S}: H={H} nq={c.n_heads} nkv={c.n_kv_heads} d={c.head_dim} "
+          f"F={c.ffn} bf16 (fwd_save / bwd_saved)", flush=True)
+    params = layer_params(c, dtype, seed=0, gain_std=0.1)
+    x = activations((N, H), dtype, 1)
+    dy = activations((N, H), dtype, 2)
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, dtype)
+    w = torch.from_numpy(pack_layer(params, c, dtype).view(np.int16)).to(DEV).view(torch.bfloat16)
+    tx, tdy = dev(x.f32, dtype), dev(dy.f32, dtype)
+
+    def run(xs, dys, nb):
+        sb = sl.slide_layer_saved_bytes(cfg, nb, S)
+        wb = sl.slide_layer_workspace_bytes(cfg, nb, S, 2)
+        saved, work = ws(sb), ws(wb)
+        y = torch.empty_like(xs)
+        dx = torch.empty_like(xs)
+        g = torch.full_like(w, float("nan"))
+        sl.slide_layer_fwd_save(cfg, w, xs, y, nb, S, saved, sb, stream())
+        sl.slide_layer_bwd_saved(cfg, w, xs, dys, dx, g, nb, S, saved, sb, work, wb, stream())
+        return y, dx, g
+
+    y, dx, g = run(tx, tdy, B)
+    # the batch's weight gradient against the sum of eight single-sequence gradients
+    g_sum = torch.zeros(w.numel(), dtype=torch.float32, device=DEV)
+    g_seq = {}
+    for b in range(B):
+        rows = slice(b * S, (b + 1) * S)
+        _, _, gb = run(tx[rows].contiguous(), tdy[rows].contiguous(), 1)
+        g_sum += gb.float()
+        if b == 5:
+            g_seq[b] = gb
+    torch.cuda.synchronize()
+    gh, gs = _unpack(host(g), c), _unpack(g_sum.double().cpu().numpy(), c)
+    for n in om.LAYER_PARAM_NAMES:
+        assert_close(gh[n], gs[n], dtype, f"batch grad {n} vs sum over sequences")
+
+    # sequence 5 against the oracle, row by row
+    b = 5
+    rows = slice(b * S, (b + 1) * S)
+    shape = om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, c.rms_eps,
+                          c.rope_theta)
+    p64 = {k: v.f64 for k, v in params.items()}
+    ry, cache = om.layer_fwd(p64, x.f64[rows].reshape(1, S, H), shape)
+    rdx, rg = om.layer_bwd(p64, dy.f64[rows].reshape(1, S, H), cache, shape)
+    assert_close(host(y[rows]).reshape(1, S, H), ry, dtype, f"y, sequence {b}")
+    assert_close(host(dx[rows]).reshape(1, S, H), rdx, dtype, f"dx, sequence {b}")
+    g5 = _unpack(host(g_seq[b]), c)
+    for n in om.LAYER_PARAM_NAMES:
+        assert_close(g5[n], rg[n], dtype, f"grad {n}, sequence {b} alone")
+
+
+@pytest.fixture(scope="module")
+def ce_full():
+    N, H, V = CE_ONLY["tokens"], CE_ONLY["hidden"], CE_ONLY["vocab"]
+    print(f"drawing CE inputs N={N} H={H} V={V}", flush=True)
+    h, w, t = ce_inputs(N, H, V, "bf16")
+    return h, w, t, dev(h.f32, "bf16"), dev(w.f32, "bf16")
+
+
+def _ce_gpu(th, tw, t, chunk):
+    N, H = th.shape
+    V = tw.shape[0]
+    cfg = sl.CeCfg(H, V, chunk, sl.SLIDE_BF16)
+    wsz = sl.slide_lmhead_ce_workspace_bytes(cfg, N)
+    loss = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
+    dh = empty((N, H), "bf16")
+    dw = empty((V, H), "bf16")
+    sl.slide_lmhead_ce(cfg, th, tw, torch.from_numpy(np.ascontiguousarray(t)).to(DEV), N, loss,
+                       dh, dw, ws(wsz), wsz, stream())
+    torch.cuda.synchronize()
+    return float(loss.item()), dh, dw
+
+
+SAMPLE = np.array([0, 1, 777, 4095, 4096, 8191, 8192, 9000, 12345, 16000, 16382, 16383])
+
+
+@pytest.mark.parametrize("N", [8192, 16384])
+def test_lmhead_ce_full_vocab_masked_sample(ce_full, N):
+    h, w, t, th, tw = ce_full
+    chunk = CE_ONLY["chunk"]
+    sample = SAMPLE[SAMPLE < N]
+    tm = np.full(N, -1, np.int32)
+    tm[sample] = t[sample]
+    print(f"CE N={N} V={w.f32.shape[0]} chunk={chunk}, all targets but {len(sample)} ignored",
+          flush=True)
+    loss, dh, dw = _ce_gpu(th[:N], tw, tm, chunk)
+    rl, rdh, rdw, _ = om.ce_dense(h.f64[sample], w.f64, t[sample])
+    print(f"  loss gpu {loss:.6f} oracle {rl:.6f}", flush=True)
+    assert abs(loss - rl) <= 2e-3 * max(1.0, abs(rl))
+    dhh = host(dh)
+    assert_close(dhh[sample], rdh, "bf16", "dh, sampled rows")
+    rest = np.ones(N, bool)
+    rest[sample] = False
+    assert float(np.max(np.abs(dhh[rest]))) == 0.0, "dh of ignored rows must be exactly 0"
+    assert_close(host(dw), rdw, "bf16", "dW (all vocabulary rows)")
+
+
+def test_lmhead_ce_full_vocab_unmasked(ce_full):
+    h, w, t, th, tw = ce_full
+    N, chunk = CE_ONLY["tokens"], CE_ONLY["chunk"]
+    print(f"CE N={N} V={w.f32.shape[0]} chunk={chunk}, every target valid", flush=True)
+    loss, dh, dw = _ce_gpu(th, tw, t, chunk)
+    # sampled dh rows: the sample's own CE rescaled from its mean to the batch's mean
+    rl, rdh, _, _ = om.ce_dense(h.f64[SAMPLE], w.f64, t[SAMPLE])
+    assert_close(host(dh)[SAMPLE], rdh * (len(SAMPLE) / N), "bf16", "dh, sampled rows")
+    # halves: mean loss and dW combine with weights n_i / N
+    half = N // 2
+    l1, _, dw1 = _ce_gpu(th[:half], tw, t[:half], chunk)
+    l2, _, dw2 = _ce_gpu(th[half:], tw, t[half:], chunk)
+    comb = 0.5 * (l1 + l2)
+    print(f"  loss {loss:.6f}, halves combined {comb:.6f}", flush=True)
+    assert abs(loss - comb) <= 1e-5 * abs(loss)
+    e = rel_err(host(dw), 0.5 * (host(dw1) + host(dw2)))
+    print(f"  dW vs halves combined: rel err {e:.3e}", flush=True)
+    assert e <= 2e-2
+    # statistics at this init: z ~ N(0, 0.02^2 H) per logit, loss near ln V + var / 2
+    expect = np.log(w.f32.shape[0]) + 0.5 * 0.02 ** 2 * h.f32.shape[1]
+    assert abs(loss - expect) < 0.05, (loss, expect)
