@@ -1,21 +1,18 @@
 // GEMMs of the decoder layer and the LM head (projections y = x W^T, their input gradients
 // dX = dY W and weight gradients dW = dY^T X).
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation. A workgroup computes a
-// BM x BN tile of C with its waves in a WGM x (waves/WGM) grid; K is consumed in 64-wide tiles
-// staged through LDS (double buffered: the next tile is fetched into registers while the current
-// one feeds the MFMAs, one barrier per tile). Two tile shapes:
-//   large: 256 x 256, 8 waves (2 x 4), wave tile 128 x 64 (4 x 2 MFMA blocks), 128 KB of LDS;
-//          half the LDS and L2 traffic per flop of the small tile
-//   small: 128 x 128, 4 waves (2 x 2), wave tile 64 x 64, 64 KB of LDS, for problems with too
-//          few large tiles to fill the 256 compute units
-// In LDS both operands are stored K-contiguous, one 128-byte row (64 bf16) per M (or N) index,
-// with the 16-byte chunk index XOR-swizzled by (row + row/8) & 7 so that both the MFMA reads
-// (8 consecutive rows, same chunk) and the transposed writes (8 rows spaced 8 apart) hit distinct
-// banks. An operand whose K is the outer dimension in memory (dW = dY^T X, dX = dY W) is loaded
-// as 8x8 blocks and transposed in registers before the LDS write (A by the first BM threads, B by
-// the last BN threads, so both transposes run in parallel), so every layout shares one inner
-// loop. Tiles are ordered XCD-aware and grouped along M for L2 reuse.
+// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, two kernels:
+//   pipelined (problems with at least 128 tiles of 256 x 256, i.e. every projection of the
+//     step): 256 x 256 tile, 8 waves, k-tiles streamed global -> LDS by direct loads; see the
+//     comment above gemm_pipe_kernel.
+//   register-staged (smaller problems): 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64,
+//     K consumed in 64-wide tiles staged through registers into LDS (double buffered, one
+//     barrier per tile). Both operands are stored K-contiguous in LDS, one 128-byte row per M
+//     (or N) index, the 16-byte chunk index XOR-swizzled by (row + row/8) & 7 so that both the
+//     MFMA reads (8 consecutive rows, same chunk) and the transposed writes (8 rows spaced 8
+//     apart) hit distinct banks. An operand whose K is the outer dimension in memory is loaded as
+//     8x8 blocks and transposed in registers before the LDS write.
+// Tiles are ordered XCD-aware and grouped along M for L2 reuse.
 // fp32 path (the small fp32 configuration): a plain LDS-tiled SIMT kernel, 64x64 per workgroup.
 #include "gemm.h"
 
@@ -98,9 +95,7 @@ struct Tile {
   static constexpr int NW = NT / 64, WGN = NW / WGM;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   static constexpr int MI = WTM / 32, NJ = WTN / 32;     // 32x32 MFMA blocks per wave
-  static constexpr int MIN_WAVES = NT >= 512 ? 2 : 2;
 };
-using TileL = Tile<256, 256, 512, 2>;
 using TileS = Tile<128, 128, 256, 2>;
 
 template <class TL, bool AK, bool BKM, int EPI, int SITE>
@@ -204,23 +199,37 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ pipelined bf16 GEMM
-// 256 x 256 tile, 8 waves (2 x 4, wave tile 128 x 64), k-tiles of 32 in 4 LDS stages fed by
-// direct global -> LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS
-// destination + 16 l), so three k-tiles are in flight without holding registers. Each wave
-// issues exactly 2 loads per operand per stage whatever the layout:
-//   K-major operand: stage = [256 rows][32 k] (64-byte rows, 4 chunks); a wave load covers 16
-//     rows; the chunk order inside a row is swizzled by ((r >> 1) ^ (r >> 3)) & 3.
-//   outer-K operand: stage = [32 k][256 rows] (512-byte rows, 32 chunks); a wave load covers 2
+// 256 x 256 tile, 8 waves (2 x 4, wave tile 128 x 64), k-tiles of 64 in 2 LDS stages of 64 KB
+// fed by direct global -> LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at the
+// wave's LDS destination + 16 l), so the next k-tile streams in without holding registers.
+// Each wave issues 4 loads per operand per stage whatever the layout:
+//   K-major operand: stage = [256 rows][64 k] (128-byte rows, 8 chunks, whole cache lines); a
+//     wave load covers 8 rows; the chunk order inside a row is swizzled by (r ^ (r >> 3)) & 7.
+//   outer-K operand: stage = [64 k][256 rows] (512-byte rows, 32 chunks); a wave load covers 2
 //     k-rows; chunks swizzled by (0, 4, 10, 14)[k % 4]. MFMA fragments come out through the LDS
 //     transpose read ds_read_b64_tr_b16 (16-lane groups: lanes addressing 4 consecutive k-rows x
 //     16 rows deliver 4 consecutive k of one row per lane).
 // The swizzles keep both the 16-byte fragment reads and the transpose reads free of bank
-// conflicts (checked for 32 and 64 banks). Out-of-range lanes load from a zero page.
+// conflicts (checked for 32 and 64 banks). Out-of-range lanes load from a zero page. MFMA
+// fragments are double buffered in registers: the LDS reads of the next 16-k step are in flight
+// while the MFMAs of the current one run, and the one barrier per stage sits where the last
+// step's MFMAs can cover it. Every layout (forward, dX, dW) runs this kernel.
 namespace pipe {
 
-constexpr int BM = 256, BN = 256, BKP = 32, NS = 4, NT = 512, WGM = 2;
-constexpr int WTM = 128, WTN = 64, MI = 4, NJ = 2;
-constexpr int STAGE_ELEMS = 256 * 32;  // per operand
+constexpr int BM = 256, BN = 256;
+
+// NT threads in a WGM x (waves / WGM) wave grid; NS stages of BK-deep k-tiles in LDS
+// (BK = 32: 32 KB per stage, BK = 64: 64 KB).
+template <int NT_, int WGM_, int NS_, int BK_>
+struct PCfg {
+  static constexpr int NT = NT_, NW = NT / 64, WGM = WGM_, WGN = NW / WGM, NS = NS_, BK = BK_;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 32, NJ = WTN / 32;
+  static constexpr int SE = 256 * BK;         // elements per operand and stage
+  static constexpr int LPS = BK / NW;         // this wave's loads per stage (both operands)
+  static constexpr int KS = BK / 16;          // MFMA k steps per stage
+  static_assert(NS * 2 * SE * 2 <= 160 * 1024, "LDS");
+  static_assert(KS % 2 == 0, "fragment sets alternate within a stage");
+};
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_s4_t;
@@ -229,24 +238,29 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 
 __device__ uint4 zero_page[4];
 
-__device__ __forceinline__ int swzk(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int swzt(int k) {
-  const int t = k & 3;
-  return t == 0 ? 0 : t == 1 ? 4 : t == 2 ? 10 : 14;
+// chunk swizzle of K-major rows: 4 chunks of 16 bytes per row (BK = 32) or 8 (BK = 64)
+template <int BK>
+__device__ __forceinline__ int swzk(int r) {
+  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r ^ (r >> 3)) & 7;
 }
+// (0, 4, 10, 14)[k % 4], branch-free (k differs between lanes)
+__device__ __forceinline__ int swzt(int k) { return (0xEA40 >> ((k & 3) << 2)) & 15; }
 
-// Issue this wave's two loads of one operand for one stage.
-template <bool KMAJ>
+// Issue this wave's loads of one operand for one stage: BK / 2 wave-loads of 1 KB cover the
+// stage, BK / 2 / NW of them per wave.
+template <bool KMAJ, int NW, int BK>
 __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ P, int ld,
                                       int row0, int rows_total, int k0, int K, int wave,
                                       int lane) {
+  constexpr int LPR = BK / 8;       // lanes per K-major row (16 bytes each)
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int instr = wave + 8 * q;          // 16 wave-loads of 1 KB cover the 16 KB stage
+  for (int q = 0; q < BK / 2 / NW; ++q) {
+    const int instr = wave + NW * q;
     const void* src = zero_page;
     if constexpr (KMAJ) {
-      const int r = instr * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swzk(r);
+      const int r = instr * (64 / LPR) + lane / LPR;
+      const int c = (lane % LPR) ^ swzk<BK>(r);
       const int gr = row0 + r, gk = k0 + c * 8;
       if (gr < rows_total && gk < K) src = P + (size_t)gr * ld + gk;
     } else {
@@ -263,21 +277,13 @@ __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// Wait for this wave's outstanding LDS reads and pin the fragments after the wait.
-template <int N>
-__device__ __forceinline__ void tr_wait(bf16x8_t (&v)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
-}
-
 // 8 bf16 of MFMA fragment row `r` (0..255 within the stage), k = 16 kk + 8 h .. + 7
-template <bool KMAJ>
+template <bool KMAJ, int BK>
 __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk, int lane) {
   if constexpr (KMAJ) {
     const int r = rbase + (lane & 31);
-    const int c = (kk * 2 + (lane >> 5)) ^ swzk(r);
-    return *(const bf16x8_t*)(stage + r * BKP + c * 8);
+    const int c = (kk * 2 + (lane >> 5)) ^ swzk<BK>(r);
+    return *(const bf16x8_t*)(stage + r * BK + c * 8);
   } else {
     const int g = lane >> 4, i = lane & 15;
     const int m = rbase + 16 * (g & 1) + 4 * (i & 3);
@@ -285,7 +291,7 @@ __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk,
     const bf16_t* p0 = stage + k * 256 + (((m >> 3) ^ swzt(k)) << 3) + (m & 7);
     const bf16_t* p1 = stage + (k + 4) * 256 + (((m >> 3) ^ swzt(k + 4)) << 3) + (m & 7);
     // inline asm: the compiler would drain all in-flight direct-to-LDS loads before each
-    // builtin transpose read; the caller waits on the results with tr_wait()
+    // builtin transpose read; the caller waits on the results with frag_wait()
     short4_t lo, hi;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(lds_addr(p0)));
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(lds_addr(p1)));
@@ -297,22 +303,50 @@ __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int rbase, int kk,
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  // s_waitcnt with vmcnt = N, expcnt and lgkmcnt left at their maxima (no wait on them)
-  static_assert(N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima (no wait)
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// vmcnt wait that leaves the loads of `later` stages (LPS loads each) in flight, later <= L
+template <int L, int LPS>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (L == 0) {
+    wait_vm<0>();
+  } else {
+    if (later >= L) wait_vm<L * LPS>();
+    else wait_later<L - 1, LPS>(later);
+  }
+}
+
+// Wait for this wave's LDS reads into fragment sets a, b and pin the registers after the wait:
+// one statement, so no read of the set can be scheduled after the wait.
+__device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1])
+               :
+               : "memory");
+}
+__device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                 "+v"(b[2]), "+v"(b[3])
+               :
+               : "memory");
 }
 
 }  // namespace pipe
 
-template <bool AK, bool BKM, int EPI, int SITE>
-__global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
+template <class PC, bool AK, bool BKM, int EPI, int SITE>
+__global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   using namespace pipe;
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * 2 * STAGE_ELEMS];
+  constexpr int NS = PC::NS, NW = PC::NW, WGM = PC::WGM, WTM = PC::WTM, WTN = PC::WTN;
+  constexpr int MI = PC::MI, NJ = PC::NJ, BK = PC::BK, SE = PC::SE, KS = PC::KS;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * 2 * SE];
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
   if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int group = logical / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
@@ -334,44 +368,79 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = (g.K + BKP - 1) / BKP;
-  auto stage_a = [&](int b) { return smem + b * 2 * STAGE_ELEMS; };
-  auto stage_b = [&](int b) { return smem + b * 2 * STAGE_ELEMS + STAGE_ELEMS; };
+  const int nk = (g.K + BK - 1) / BK;
+  auto stage_a = [&](int b) { return smem + b * 2 * SE; };
+  auto stage_b = [&](int b) { return smem + b * 2 * SE + SE; };
   auto issue_stage = [&](int kt) {
     const int b = kt % NS;
-    issue<AK>(stage_a(b), A, g.lda, m0, g.M, kt * BKP, g.K, wave, lane);
-    issue<BKM>(stage_b(b), B, g.ldb, n0, g.N, kt * BKP, g.K, wave, lane);
+    issue<AK, NW, BK>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
+    issue<BKM, NW, BK>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
   };
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue_stage(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the loads of the later issued stages are outstanding
-    const int later = min(nk - 1, kt + NS - 2) - kt;
-    if (later >= 2) wait_vm<8>();
-    else if (later == 1) wait_vm<4>();
-    else wait_vm<0>();
-    // Plain barrier: the explicit vmcnt wait above already covers this stage's loads, and the
-    // later stages' loads must stay in flight across it.
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + NS - 1 < nk) issue_stage(kt + NS - 1);
+  // Wait until stage kt has landed (this wave's loads; the barrier that follows covers the
+  // other waves'): the loads of the stages issued after it, up to stage `last`, may stay in
+  // flight.
+  auto wait_stage = [&](int kt, int last) {
+    wait_later<NS - 1, PC::LPS>(min(nk - 1, last) - kt);
+  };
+  // Fragments of one 16-wide k step, double buffered: the LDS reads of the next step are in
+  // flight while the MFMAs of the current one run.
+  bf16x8_t fa[2][MI], fb[2][NJ];
+  auto load_frags = [&](int buf, int kt, int kk) {
     const bf16_t* sa = stage_a(kt % NS);
     const bf16_t* sb = stage_b(kt % NS);
 #pragma unroll
-    for (int kk = 0; kk < BKP / 16; ++kk) {
-      bf16x8_t af[MI], bfr[NJ];
+    for (int i = 0; i < MI; ++i) fa[buf][i] = frag<AK, BK>(sa, wm * WTM + i * 32, kk, lane);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = frag<AK>(sa, wm * WTM + i * 32, kk, lane);
+    for (int j = 0; j < NJ; ++j) fb[buf][j] = frag<BKM, BK>(sb, wn * WTN + j * 32, kk, lane);
+  };
+  // Wait for this wave's LDS reads of fragment set `buf` and pin the registers after the wait:
+  // one statement, so no read of the set can be scheduled after the wait. Required before a
+  // barrier that lets other waves overwrite the stage, and before inline-asm (transpose) reads
+  // are consumed.
+  auto wait_frags = [&](int buf) { frag_wait(fa[buf], fb[buf]); };
+  auto mfmas = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = frag<BKM>(sb, wn * WTN + j * 32, kk, lane);
-      if constexpr (!AK) tr_wait(af);
-      if constexpr (!BKM) tr_wait(bfr);
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
+                                                             0, 0, 0);
+  };
+
+  // All NS stages start in flight; stage kt + NS reuses stage kt's buffer once every wave has
+  // read stage kt (the barrier in iteration kt).
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  for (int s = 0; s < NS; ++s)
+    if (s < nk) issue_stage(s);
+  if (nk > 0) {
+    wait_stage(0, NS - 1);
+    asm volatile("s_barrier" ::: "memory");
+    load_frags(0, 0, 0);
+  }
+  // Steps of 16 k alternate between the two fragment sets. The last step of a stage passes the
+  // barrier after which stage kt's buffer is refilled and stage kt + 1's first fragments are
+  // read, then runs its MFMAs while those reads are in flight. sched_barrier(0) keeps the
+  // compiler from moving MFMAs across these points.
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int cur = kk & 1;
+      wait_frags(cur);
+      if (kk + 1 < KS) {
+        load_frags(cur ^ 1, kt, kk + 1);
+      } else if (kt + 1 < nk) {
+        wait_stage(kt + 1, kt + NS - 1);
+        // Plain barrier: the explicit vmcnt wait covers this wave's loads of stage kt + 1, and
+        // the later stages' loads stay in flight across it.
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + NS < nk) issue_stage(kt + NS);
+        load_frags(cur ^ 1, kt + 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);   // favour the wave issuing MFMAs on its SIMD
+      mfmas(cur);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -471,8 +540,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-// GEMM path for large problems: 1 = register-staged 256 x 256 tile, 2 = pipelined DMA-fed tile.
-int g_gemm_path = 2;
+using PipeL = pipe::PCfg<512, 2, 2, 64>;
 
 // Large tiles when they alone give at least half a wave of workgroups per compute unit.
 inline bool use_large(const GemmArgs& g) {
@@ -482,16 +550,10 @@ inline bool use_large(const GemmArgs& g) {
 
 template <bool AK, bool BKM, int EPI, int SITE>
 void launch_one(const GemmArgs& g, hipStream_t st) {
-  // The pipelined kernel is faster whenever A is K-major (forward projections, dX); for dW
-  // (both operands outer-K) the register-transposing staged kernel is faster.
-  if (use_large(g) && AK && g_gemm_path == 2) {
-    const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-    hipLaunchKernelGGL((gemm_pipe_kernel<AK, BKM, EPI, SITE>), dim3(tiles), dim3(pipe::NT), 0, st,
-                       g);
-  } else if (use_large(g)) {
-    const int tiles = ((g.M + TileL::BM - 1) / TileL::BM) * ((g.N + TileL::BN - 1) / TileL::BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<TileL, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileL::NT),
-                       0, st, g);
+  if (use_large(g)) {
+    const int tiles = ((g.M + pipe::BM - 1) / pipe::BM) * ((g.N + pipe::BN - 1) / pipe::BN);
+    hipLaunchKernelGGL((gemm_pipe_kernel<PipeL, AK, BKM, EPI, SITE>), dim3(tiles),
+                       dim3(PipeL::NT), 0, st, g);
   } else {
     const int tiles = ((g.M + TileS::BM - 1) / TileS::BM) * ((g.N + TileS::BN - 1) / TileS::BN);
     hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileS::NT),
