@@ -138,6 +138,32 @@ int slide_lmhead_ce(const slide_ce_cfg* cfg, const void* h, const void* w,
                     const int32_t* targets, int N, float* loss_dev, void* dh, void* dw,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The same computation in host-driven phases over one workspace and one stream, so that a
+ * caller can start each vocabulary chunk as soon as that chunk's weights are on the device and
+ * ship each chunk of dW as soon as it is computed (the chunked fused cross-entropy of the
+ * SlideFormer summary, section 2C, with the chunks exposed). Chunk ci covers vocabulary rows
+ * [ci * C, min((ci + 1) * C, V)) with C = cfg->chunk (8192 if 0, at most V).
+ *   1. slide_lmhead_ce_stats for every chunk, in any order (pass 1: logits and softmax partials);
+ *   2. slide_lmhead_ce_loss (lse per token, the mean loss into loss_dev);
+ *   3. slide_lmhead_ce_grad for every chunk in increasing order (pass 2: recomputed logits,
+ *      dz, the fp32 dh accumulator in the workspace if with_dh, and rows of dw if dw != NULL;
+ *      chunk 0 initialises the accumulator);
+ *   4. slide_lmhead_ce_dh once if with_dh was set (dh in the storage type).
+ * Arguments mean what they mean for slide_lmhead_ce; ws must hold
+ * slide_lmhead_ce_workspace_bytes(cfg, N) bytes and stays owned by the caller. The results are
+ * bit-identical to slide_lmhead_ce's. A chunk index outside [0, n_chunks) is SLIDE_E_ARG. */
+int slide_lmhead_ce_n_chunks(const slide_ce_cfg* cfg);   /* >= 1, or a negative status */
+int slide_lmhead_ce_stats(const slide_ce_cfg* cfg, const void* h, const void* w,
+                          const int32_t* targets, int N, int chunk, void* ws, size_t ws_bytes,
+                          void* stream);
+int slide_lmhead_ce_loss(const slide_ce_cfg* cfg, const int32_t* targets, int N, float* loss_dev,
+                         void* ws, size_t ws_bytes, void* stream);
+int slide_lmhead_ce_grad(const slide_ce_cfg* cfg, const void* h, const void* w,
+                         const int32_t* targets, int N, int chunk, int with_dh, void* dw,
+                         void* ws, size_t ws_bytes, void* stream);
+int slide_lmhead_ce_dh(const slide_ce_cfg* cfg, int N, void* dh, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Model glue around the layers: token embedding and the final RMSNorm.
  * ------------------------------------------------------------------------------------------ */

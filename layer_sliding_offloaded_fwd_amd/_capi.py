@@ -52,6 +52,11 @@ SIGNATURES = {
     "slide_layer_bwd_saved": (I, [LCP, P, P, P, P, P, I, I, P, SZ, P, SZ, P]),
     "slide_lmhead_ce_workspace_bytes": (SZ, [CCP, I]),
     "slide_lmhead_ce": (I, [CCP, P, P, P, I, P, P, P, P, SZ, P]),
+    "slide_lmhead_ce_n_chunks": (I, [CCP]),
+    "slide_lmhead_ce_stats": (I, [CCP, P, P, P, I, I, P, SZ, P]),
+    "slide_lmhead_ce_loss": (I, [CCP, P, I, P, P, SZ, P]),
+    "slide_lmhead_ce_grad": (I, [CCP, P, P, P, I, I, I, P, P, SZ, P]),
+    "slide_lmhead_ce_dh": (I, [CCP, I, P, P, SZ, P]),
     "slide_embed_fwd": (I, [P, P, P, I, I, I, I, P]),
     "slide_embed_bwd_workspace_bytes": (SZ, [I, I]),
     "slide_embed_bwd": (I, [P, P, P, I, I, I, I, P, SZ, P]),

@@ -14,7 +14,9 @@ __all__ = [
     "SLIDE_ENGINE_HOST", "slide_layer_param_count", "slide_layer_param_offsets",
     "slide_layer_workspace_bytes", "slide_layer_fwd", "slide_layer_bwd",
     "slide_layer_saved_bytes", "slide_layer_fwd_save", "slide_layer_bwd_saved",
-    "slide_lmhead_ce_workspace_bytes", "slide_lmhead_ce", "slide_embed_fwd",
+    "slide_lmhead_ce_workspace_bytes", "slide_lmhead_ce", "slide_lmhead_ce_n_chunks",
+    "slide_lmhead_ce_stats", "slide_lmhead_ce_loss", "slide_lmhead_ce_grad", "slide_lmhead_ce_dh",
+    "slide_embed_fwd",
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
@@ -107,6 +109,33 @@ def slide_lmhead_ce_workspace_bytes(cfg, N):
 def slide_lmhead_ce(cfg, h, w, targets, N, loss_dev, dh, dw, ws, ws_bytes, stream=None):
     call("slide_lmhead_ce", ctypes.byref(cfg), _p(h), _p(w), _p(targets), N, _p(loss_dev),
          _p(dh), _p(dw), _p(ws), ws_bytes, _s(stream))
+
+
+def slide_lmhead_ce_n_chunks(cfg):
+    n = int(lib().slide_lmhead_ce_n_chunks(ctypes.byref(cfg)))
+    if n < 1:
+        raise SlideError(n, "slide_lmhead_ce_n_chunks",
+                         lib().slide_last_error().decode(errors="replace"))
+    return n
+
+
+def slide_lmhead_ce_stats(cfg, h, w, targets, N, chunk, ws, ws_bytes, stream=None):
+    call("slide_lmhead_ce_stats", ctypes.byref(cfg), _p(h), _p(w), _p(targets), N, chunk, _p(ws),
+         ws_bytes, _s(stream))
+
+
+def slide_lmhead_ce_loss(cfg, targets, N, loss_dev, ws, ws_bytes, stream=None):
+    call("slide_lmhead_ce_loss", ctypes.byref(cfg), _p(targets), N, _p(loss_dev), _p(ws),
+         ws_bytes, _s(stream))
+
+
+def slide_lmhead_ce_grad(cfg, h, w, targets, N, chunk, with_dh, dw, ws, ws_bytes, stream=None):
+    call("slide_lmhead_ce_grad", ctypes.byref(cfg), _p(h), _p(w), _p(targets), N, chunk,
+         int(with_dh), _p(dw), _p(ws), ws_bytes, _s(stream))
+
+
+def slide_lmhead_ce_dh(cfg, N, dh, ws, ws_bytes, stream=None):
+    call("slide_lmhead_ce_dh", ctypes.byref(cfg), N, _p(dh), _p(ws), ws_bytes, _s(stream))
 
 
 # ------------------------------------------------------------------------------ glue

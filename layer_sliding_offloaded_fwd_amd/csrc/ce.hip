@@ -179,88 +179,138 @@ int ce_check(const slide_ce_cfg* c, int N) {
   return SLIDE_OK;
 }
 
-int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* tgt, int N,
-           float* loss, void* dh, void* dw, void* ws, hipStream_t st) {
-  const int H = c.hidden, V = c.vocab, dt = c.dtype;
-  const size_t ts = (size_t)dtype_size(dt);
-  const CeLayout L = ce_layout(c, N, dh != nullptr);
-  char* base = (char*)ws;
-  float* zbuf = (float*)(base + L.zbuf);
-  void* dz = base + L.dz;
-  float* pm = (float*)(base + L.pm);
-  float* ps = (float*)(base + L.ps);
-  float* zt = (float*)(base + L.zt);
-  float* lse = (float*)(base + L.lse);
-  float* lt = (float*)(base + L.lt);
-  float* inv_nv = (float*)(base + L.scal);
-  float* dh_acc = dh ? (float*)(base + L.dh) : nullptr;
+// Workspace views shared by the phases below.
+struct CeBufs {
+  CeLayout L;
+  float *zbuf, *pm, *ps, *zt, *lse, *lt, *inv_nv, *dh_acc;
+  void* dz;
+};
 
+CeBufs ce_bufs(const slide_ce_cfg& c, int N, void* ws) {
+  CeBufs b;
+  b.L = ce_layout(c, N, true);
+  char* base = (char*)ws;
+  b.zbuf = (float*)(base + b.L.zbuf);
+  b.dz = base + b.L.dz;
+  b.pm = (float*)(base + b.L.pm);
+  b.ps = (float*)(base + b.L.ps);
+  b.zt = (float*)(base + b.L.zt);
+  b.lse = (float*)(base + b.L.lse);
+  b.lt = (float*)(base + b.L.lt);
+  b.inv_nv = (float*)(base + b.L.scal);
+  b.dh_acc = (float*)(base + b.L.dh);
+  return b;
+}
+
+int ce_n_chunks(const slide_ce_cfg& c) { return ce_layout(c, 0, false).nchunks; }
+
+namespace {
+
+int ce_logits(const slide_ce_cfg& c, const CeBufs& b, const void* h, const void* w, int N, int ci,
+              hipStream_t st) {
+  // z^T[v][t] = sum_k W[c0+v][k] h[t][k]
+  const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
+  const size_t ts = (size_t)dtype_size(c.dtype);
+  GemmArgs g{rows, N, c.hidden, (const char*)w + (size_t)c0 * c.hidden * ts, c.hidden, true, h,
+             c.hidden, true, b.zbuf, b.L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, c.dtype,
+             "ce_logits_gemm", SITE_CE_LOGITS};
+  return gemm_launch(g, st);
+}
+
+}  // namespace
+
+// pass 1 for vocabulary chunk ci: logits, then per (token, row split) max / sum-exp partials and
+// the target logit of targets inside the chunk
+int ce_stats(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* tgt, int N,
+             int ci, void* ws, hipStream_t st) {
+  if (N == 0) return SLIDE_OK;
+  const CeBufs b = ce_bufs(c, N, ws);
+  const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
+  SLIDE_TRY(ce_logits(c, b, h, w, N, ci, st));
+  ProfScope ps_("ce_stats", st);
+  hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), kRowSplits), dim3(256), 0, st, b.zbuf,
+                     rows, N, b.L.ldz, c0, tgt, b.pm + (size_t)ci * kRowSplits * N,
+                     b.ps + (size_t)ci * kRowSplits * N, b.zt, kRowSplits);
+  return check_launch("ce_stats");
+}
+
+// lse_t from the partials of every chunk (fixed order), the per-token loss and the mean
+int ce_loss(const slide_ce_cfg& c, const int32_t* tgt, int N, float* loss, void* ws,
+            hipStream_t st) {
   if (N == 0) {
     hipLaunchKernelGGL(write_scalar_kernel, dim3(1), dim3(1), 0, st, loss, 0.f);
+    return check_launch("lmhead_ce(empty)");
+  }
+  const CeBufs b = ce_bufs(c, N, ws);
+  ProfScope ps_("ce_lse", st);
+  hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 256)), dim3(256), 0, st, b.pm, b.ps,
+                     b.L.nchunks * kRowSplits, N, tgt, c.vocab, b.zt, b.lse, b.lt);
+  hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, b.lt, tgt, N, c.vocab, loss,
+                     b.inv_nv);
+  return check_launch("ce_lse");
+}
+
+// pass 2 for vocabulary chunk ci: recomputed logits, dz, dh (fp32 accumulator in the workspace;
+// chunk 0 initialises it) and the chunk's rows of dW
+int ce_grad(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* tgt, int N,
+            int ci, bool with_dh, void* dw, void* ws, hipStream_t st) {
+  const int H = c.hidden, V = c.vocab, dt = c.dtype;
+  const size_t ts = (size_t)dtype_size(dt);
+  const CeBufs b = ce_bufs(c, N, ws);
+  const int c0 = ci * b.L.C, rows = std::min(b.L.C, V - c0);
+  if (N == 0) {
     if (dw) {
-      const size_t n = (size_t)V * H;
-      if (dt == SLIDE_BF16) hipLaunchKernelGGL(fill_zero_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, (bf16_t*)dw, n);
-      else hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, (float*)dw, n);
+      const size_t n = (size_t)rows * H;
+      char* d = (char*)dw + (size_t)c0 * H * ts;
+      if (dt == SLIDE_BF16) hipLaunchKernelGGL(fill_zero_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, (bf16_t*)d, n);
+      else hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, (float*)d, n);
     }
     return check_launch("lmhead_ce(empty)");
   }
-
-  auto logits = [&](int c0, int rows, const char* name) {
-    // z^T[v][t] = sum_k W[c0+v][k] h[t][k]
-    GemmArgs g{rows, N, H, (const char*)w + (size_t)c0 * H * ts, H, true, h, H, true, zbuf,
-               L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, dt, name, SITE_CE_LOGITS};
-    return gemm_launch(g, st);
-  };
-
-  // ---- pass 1: statistics
-  for (int ci = 0; ci < L.nchunks; ++ci) {
-    const int c0 = ci * L.C, rows = std::min(L.C, V - c0);
-    SLIDE_TRY(logits(c0, rows, "ce_logits_gemm"));
-    ProfScope ps_("ce_stats", st);
-    hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), kRowSplits), dim3(256), 0, st, zbuf,
-                       rows, N, L.ldz, c0, tgt, pm + (size_t)ci * kRowSplits * N,
-                       ps + (size_t)ci * kRowSplits * N, zt, kRowSplits);
-    SLIDE_TRY(check_launch("ce_stats"));
-  }
+  SLIDE_TRY(ce_logits(c, b, h, w, N, ci, st));
   {
-    ProfScope ps_("ce_lse", st);
-    hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 256)), dim3(256), 0, st, pm, ps,
-                       L.nchunks * kRowSplits, N, tgt, V, zt, lse, lt);
-    hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, lt, tgt, N, V, loss, inv_nv);
+    ProfScope ps_("ce_dz", st);
+    const size_t n = (size_t)rows * b.L.ldz;
+    if (dt == SLIDE_BF16)
+      hipLaunchKernelGGL(ce_dz_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,
+                         (bf16_t*)b.dz, rows, N, b.L.ldz, c0, V, tgt, b.lse, b.inv_nv);
+    else
+      hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,
+                         (float*)b.dz, rows, N, b.L.ldz, c0, V, tgt, b.lse, b.inv_nv);
+    SLIDE_TRY(check_launch("ce_dz"));
   }
-  SLIDE_TRY(check_launch("ce_lse"));
-  if (!dh && !dw) return SLIDE_OK;
+  const void* wc = (const char*)w + (size_t)c0 * H * ts;
+  if (with_dh) {
+    // dh[t][i] (+)= sum_v dz[v][t] W[c0+v][i]
+    GemmArgs g{N, H, rows, b.dz, b.L.ldz, false, wc, H, false, b.dh_acc, H, SLIDE_F32, nullptr,
+               0, 1.0f, ci > 0, dt, "ce_dh_gemm", SITE_CE_DH};
+    SLIDE_TRY(gemm_launch(g, st));
+  }
+  if (dw) {
+    // dW[c0+v][i] = sum_t dz[v][t] h[t][i]
+    GemmArgs g{rows, H, N, b.dz, b.L.ldz, true, h, H, false, (char*)dw + (size_t)c0 * H * ts, H,
+               dt, nullptr, 0, 1.0f, false, dt, "ce_dw_gemm", SITE_CE_DW};
+    SLIDE_TRY(gemm_launch(g, st));
+  }
+  return SLIDE_OK;
+}
 
-  // ---- pass 2: gradients
-  for (int ci = 0; ci < L.nchunks; ++ci) {
-    const int c0 = ci * L.C, rows = std::min(L.C, V - c0);
-    SLIDE_TRY(logits(c0, rows, "ce_logits_gemm"));
-    {
-      ProfScope ps_("ce_dz", st);
-      const size_t n = (size_t)rows * L.ldz;
-      if (dt == SLIDE_BF16)
-        hipLaunchKernelGGL(ce_dz_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, zbuf,
-                           (bf16_t*)dz, rows, N, L.ldz, c0, V, tgt, lse, inv_nv);
-      else
-        hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, zbuf,
-                           (float*)dz, rows, N, L.ldz, c0, V, tgt, lse, inv_nv);
-      SLIDE_TRY(check_launch("ce_dz"));
-    }
-    const void* wc = (const char*)w + (size_t)c0 * H * ts;
-    if (dh) {
-      // dh[t][i] (+)= sum_v dz[v][t] W[c0+v][i]
-      GemmArgs g{N, H, rows, dz, L.ldz, false, wc, H, false, dh_acc, H, SLIDE_F32, nullptr, 0,
-                 1.0f, ci > 0, dt, "ce_dh_gemm", SITE_CE_DH};
-      SLIDE_TRY(gemm_launch(g, st));
-    }
-    if (dw) {
-      // dW[c0+v][i] = sum_t dz[v][t] h[t][i]
-      GemmArgs g{rows, H, N, dz, L.ldz, true, h, H, false, (char*)dw + (size_t)c0 * H * ts, H,
-                 dt, nullptr, 0, 1.0f, false, dt, "ce_dw_gemm", SITE_CE_DW};
-      SLIDE_TRY(gemm_launch(g, st));
-    }
-  }
-  if (dh) SLIDE_TRY(convert_from_f32(dh_acc, dh, (size_t)N * H, dt, st));
+// dh in the storage type from the fp32 accumulator
+int ce_dh(const slide_ce_cfg& c, int N, void* dh, void* ws, hipStream_t st) {
+  if (N == 0) return SLIDE_OK;
+  const CeBufs b = ce_bufs(c, N, ws);
+  return convert_from_f32(b.dh_acc, dh, (size_t)N * c.hidden, c.dtype, st);
+}
+
+int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* tgt, int N,
+           float* loss, void* dh, void* dw, void* ws, hipStream_t st) {
+  const int nch = ce_n_chunks(c);
+  if (N > 0)
+    for (int ci = 0; ci < nch; ++ci) SLIDE_TRY(ce_stats(c, h, w, tgt, N, ci, ws, st));
+  SLIDE_TRY(ce_loss(c, tgt, N, loss, ws, st));
+  if (!dh && !dw) return SLIDE_OK;
+  for (int ci = 0; ci < nch; ++ci) SLIDE_TRY(ce_grad(c, h, w, tgt, N, ci, dh != nullptr, dw, ws, st));
+  if (dh) SLIDE_TRY(ce_dh(c, N, dh, ws, st));
   return SLIDE_OK;
 }
 
@@ -269,6 +319,64 @@ int ce_run(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* t
 extern "C" size_t slide_lmhead_ce_workspace_bytes(const slide_ce_cfg* cfg, int N) {
   if (!cfg || slide::ce_check(cfg, N) != SLIDE_OK) return 0;
   return slide::ce_workspace_bytes(*cfg, N);
+}
+
+namespace {
+int ce_common_check(const slide_ce_cfg* cfg, int N, const void* ws, size_t ws_bytes,
+                    const char* fn) {
+  SLIDE_TRY(slide::ce_check(cfg, N));
+  SLIDE_REQUIRE(ws, SLIDE_E_ARG, "%s: null workspace", fn);
+  const size_t need = slide::ce_workspace_bytes(*cfg, N);
+  SLIDE_REQUIRE(ws_bytes >= need, SLIDE_E_WORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, need);
+  return SLIDE_OK;
+}
+int ce_chunk_check(const slide_ce_cfg* cfg, int chunk, const char* fn) {
+  const int n = slide::ce_n_chunks(*cfg);
+  SLIDE_REQUIRE(chunk >= 0 && chunk < n, SLIDE_E_ARG, "%s: chunk %d outside [0, %d)", fn, chunk, n);
+  return SLIDE_OK;
+}
+}  // namespace
+
+extern "C" int slide_lmhead_ce_n_chunks(const slide_ce_cfg* cfg) {
+  if (slide::ce_check(cfg, 0) != SLIDE_OK) return slide::fail(SLIDE_E_ARG, "slide_lmhead_ce_n_chunks: bad cfg");
+  return slide::ce_n_chunks(*cfg);
+}
+
+extern "C" int slide_lmhead_ce_stats(const slide_ce_cfg* cfg, const void* h, const void* w,
+                                     const int32_t* targets, int N, int chunk, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  SLIDE_TRY(ce_common_check(cfg, N, ws, ws_bytes, "slide_lmhead_ce_stats"));
+  SLIDE_TRY(ce_chunk_check(cfg, chunk, "slide_lmhead_ce_stats"));
+  SLIDE_REQUIRE(N == 0 || (h && w && targets), SLIDE_E_ARG, "slide_lmhead_ce_stats: null pointer");
+  SLIDE_REQUIRE(slide::aligned16(h) && slide::aligned16(w), SLIDE_E_ARG,
+                "slide_lmhead_ce_stats: tensors must be 16-byte aligned");
+  return slide::ce_stats(*cfg, h, w, targets, N, chunk, ws, (hipStream_t)stream);
+}
+
+extern "C" int slide_lmhead_ce_loss(const slide_ce_cfg* cfg, const int32_t* targets, int N,
+                                    float* loss_dev, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(ce_common_check(cfg, N, ws, ws_bytes, "slide_lmhead_ce_loss"));
+  SLIDE_REQUIRE(loss_dev && (N == 0 || targets), SLIDE_E_ARG, "slide_lmhead_ce_loss: null pointer");
+  return slide::ce_loss(*cfg, targets, N, loss_dev, ws, (hipStream_t)stream);
+}
+
+extern "C" int slide_lmhead_ce_grad(const slide_ce_cfg* cfg, const void* h, const void* w,
+                                    const int32_t* targets, int N, int chunk, int with_dh,
+                                    void* dw, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_TRY(ce_common_check(cfg, N, ws, ws_bytes, "slide_lmhead_ce_grad"));
+  SLIDE_TRY(ce_chunk_check(cfg, chunk, "slide_lmhead_ce_grad"));
+  SLIDE_REQUIRE(N == 0 || (h && w && targets), SLIDE_E_ARG, "slide_lmhead_ce_grad: null pointer");
+  SLIDE_REQUIRE(slide::aligned16(h) && slide::aligned16(w) && (!dw || slide::aligned16(dw)),
+                SLIDE_E_ARG, "slide_lmhead_ce_grad: tensors must be 16-byte aligned");
+  return slide::ce_grad(*cfg, h, w, targets, N, chunk, with_dh != 0, dw, ws, (hipStream_t)stream);
+}
+
+extern "C" int slide_lmhead_ce_dh(const slide_ce_cfg* cfg, int N, void* dh, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  SLIDE_TRY(ce_common_check(cfg, N, ws, ws_bytes, "slide_lmhead_ce_dh"));
+  SLIDE_REQUIRE(dh || N == 0, SLIDE_E_ARG, "slide_lmhead_ce_dh: null dh");
+  SLIDE_REQUIRE(slide::aligned16(dh), SLIDE_E_ARG, "slide_lmhead_ce_dh: dh must be 16-byte aligned");
+  return slide::ce_dh(*cfg, N, dh, ws, (hipStream_t)stream);
 }
 
 extern "C" int slide_lmhead_ce(const slide_ce_cfg* cfg, const void* h, const void* w,

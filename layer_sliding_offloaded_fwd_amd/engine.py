@@ -181,6 +181,15 @@ class SlideEngine:
         self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
+        # The LM head is updated, uploaded and flushed per vocabulary chunk of the fused CE, so
+        # the CE's first pass starts on chunk c as soon as that chunk is updated, and the CPU
+        # starts on chunk c's next update as soon as the second pass has produced its dW.
+        self.lm_nch = B.slide_lmhead_ce_n_chunks(self.ce_cfg)
+        C = min(ce_chunk if ce_chunk > 0 else 8192, V)
+        self.lm_rows = [(ci * C, min((ci + 1) * C, V)) for ci in range(self.lm_nch)]
+        self.lm_job = [None] * self.lm_nch        # pending CPU update per chunk
+        self.lm_ready = [None] * self.lm_nch      # H2D of the chunk's current device copy
+        self.lm_flushed = [None] * self.lm_nch    # D2H of the chunk's last device gradient
 
         # device memory, allocated once
         dev = self.device
@@ -245,9 +254,7 @@ class SlideEngine:
         assert len(layers) == self.L
         for prm, arr in zip(self.layers, layers):
             put(prm, arr)
-        for prm in (self.embed, self.final, self.lm):
-            self._upload_resident(prm)
-        torch.cuda.synchronize(self.device)
+        self._upload_all_resident()
         self.step_count = 0
 
     def init_random(self, seed=0, std=0.02, progress=None):
@@ -279,14 +286,19 @@ class SlideEngine:
         self.final.master.fill_(1.0)
         self._refresh_shared(self.final)
         draw(self.lm)
-        for prm in (self.embed, self.final, self.lm):
-            self._upload_resident(prm)
-        torch.cuda.synchronize(self.device)
+        self._upload_all_resident()
         self.step_count = 0
 
     def _refresh_shared(self, prm):
         if prm.dtype == "bf16":
             prm.shared.copy_(prm.master.to(torch.bfloat16).view(torch.int16))
+
+    def _upload_all_resident(self):
+        for prm in (self.embed, self.final, self.lm):
+            self._upload_resident(prm)
+        self.lm_ready = [self.lm.ready_ev] * self.lm_nch
+        self.lm_job = [None] * self.lm_nch
+        torch.cuda.synchronize(self.device)
 
     def _upload_resident(self, prm):
         with torch.cuda.stream(self.h2d):
@@ -357,6 +369,9 @@ class SlideEngine:
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
                    self.step_count, priority, post)
         prm.job = job
+        return self._enqueue(job)
+
+    def _enqueue(self, job):
         with self.jobs_cv:
             self.job_seq += 1
             job.seq = self.job_seq
@@ -367,14 +382,19 @@ class SlideEngine:
         return job
 
     def _wait_param(self, prm):
-        if prm.job is not None:
-            prm.job.done.wait()
+        self._wait_job(prm.job)
+
+    def _wait_job(self, job):
+        if job is not None:
+            job.done.wait()
             if self.worker_error is not None:
                 raise self.worker_error
 
     def wait_updates(self):
         for prm in self.layers + [self.embed, self.final, self.lm]:
             self._wait_param(prm)
+        for ci in range(self.lm_nch):
+            self._wait_job(self.lm_job[ci])
 
     def close(self):
         self.wait_updates()
@@ -412,6 +432,40 @@ class SlideEngine:
         prm.flushed_ev = done
         return self._submit(prm, done, name, priority, post=lambda: self._upload_resident(prm))
 
+    def _flush_lm_chunk(self, ci, rec):
+        """D2H of LM-head chunk ci's gradient rows once the compute stream has produced them,
+        then that chunk's AdamW, then its refreshed rows go back up on the H2D stream."""
+        prm, H = self.lm, self.spec.hidden
+        r0, r1 = self.lm_rows[ci]
+        sl = slice(r0 * H, r1 * H)
+        ev_c = torch.cuda.Event()
+        ev_c.record(self.compute)
+        self.d2h.wait_event(ev_c)
+        with torch.cuda.stream(self.d2h):
+            dst = prm.grad_host[sl]
+            dst = dst.view(torch.bfloat16) if prm.dtype == "bf16" else dst
+            dst.copy_(prm.grad[sl], non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(self.d2h)
+        self.lm_flushed[ci] = done
+
+        def upload():
+            with torch.cuda.stream(self.h2d):
+                src = prm.shared[sl]
+                src = src.view(torch.bfloat16) if prm.dtype == "bf16" else src
+                prm.dev[sl].copy_(src, non_blocking=True)
+                ev = torch.cuda.Event()
+                ev.record(self.h2d)
+            self.lm_ready[ci] = ev
+
+        out = prm.shared[sl] if prm.dtype == "bf16" else None
+        job = _Job(f"lm_head{ci}", done, prm.master[sl], prm.grad_host[sl], prm.m[sl],
+                   prm.v[sl], out, r1 * H - r0 * H, self.step_count,
+                   self.L + 1 + ci / self.lm_nch, upload)
+        self.lm_job[ci] = job
+        rec["other_jobs"].append(job)
+        return self._enqueue(job)
+
     def step(self, tokens):
         """One training step on int32 tokens [B, S+1] (inputs [:, :S], targets [:, 1:]).
         Returns the loss (float)."""
@@ -422,7 +476,7 @@ class SlideEngine:
         tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32))
         assert tok.shape == (self.B, self.S + 1), tok.shape
         self.step_count += 1
-        rec = dict(step=self.step_count, layers={}, jobs=[])
+        rec = dict(step=self.step_count, layers={}, jobs=[], other_jobs=[])
         t_step0 = time.perf_counter()
         ev0 = self._ev(c)          # the compute stream is idle here: ev0 ~ host time t_step0
         rec["host_t0"] = t_step0
@@ -474,27 +528,38 @@ class SlideEngine:
             self._sync()
             prefetch()
 
-        # ---- loss
+        # ---- loss: the fused CE in its phases, chunk by chunk of the LM head
         self._wait_param(self.final)
         c.wait_event(self.final.ready_ev)
-        self._wait_param(self.lm)
-        c.wait_event(self.lm.ready_ev)
-        if self.lm.flushed_ev is not None:
-            c.wait_event(self.lm.flushed_ev)
         if self.final.flushed_ev is not None:
             c.wait_event(self.final.flushed_ev)
         B.slide_rmsnorm_fwd(self.xs[L], self.final.dev, self.hf, None, N, H, spec.rms_eps,
                             self.code, c)
+        ce, lm = self.ce_cfg, self.lm
+        ce_iv = rec["ce_iv"] = []         # GPU intervals of the CE, without its waits
+        for ci in range(self.lm_nch):
+            self._wait_job(self.lm_job[ci])       # this chunk's previous update, then its upload
+            c.wait_event(self.lm_ready[ci])
+            e_a = self._ev(c) if self.timeline else None
+            B.slide_lmhead_ce_stats(ce, self.hf, lm.dev, self.tok_tgt, N, ci, self.ws,
+                                    self.ws_bytes, c)
+            if self.timeline:
+                ce_iv.append((e_a, self._ev(c)))
         e_ce = self._ev(c) if self.timeline else None
-        B.slide_lmhead_ce(self.ce_cfg, self.hf, self.lm.dev, self.tok_tgt, N, self.loss_dev,
-                          self.dhf, self.lm.grad, self.ws, self.ws_bytes, c)
+        B.slide_lmhead_ce_loss(ce, self.tok_tgt, N, self.loss_dev, self.ws, self.ws_bytes, c)
+        for ci in range(self.lm_nch):
+            if self.lm_flushed[ci] is not None:   # the previous gradient of these rows is out
+                c.wait_event(self.lm_flushed[ci])
+            B.slide_lmhead_ce_grad(ce, self.hf, lm.dev, self.tok_tgt, N, ci, True, lm.grad,
+                                   self.ws, self.ws_bytes, c)
+            self._flush_lm_chunk(ci, rec)
+        B.slide_lmhead_ce_dh(ce, N, self.dhf, self.ws, self.ws_bytes, c)
         if self.timeline:
-            rec["ce"] = (e_ce, self._ev(c))
-        self._flush_resident(self.lm, "lm_head", L + 1)
+            ce_iv.append((e_ce, self._ev(c)))
         B.slide_rmsnorm_bwd(self.dhf, self.xs[L], self.final.dev, None, self.grad_x,
                             self.final.grad, N, H, spec.rms_eps, self.code, self.ws,
                             self.ws_bytes, c)
-        self._flush_resident(self.final, "w_final", L)
+        rec["other_jobs"].append(self._flush_resident(self.final, "w_final", L))
         self._sync()
 
         # ---- backward: the last n_slots layers are still in their slots; claim them all
@@ -527,7 +592,7 @@ class SlideEngine:
         # ---- embedding gradient
         B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
                           self.ws, self.ws_bytes, c)
-        self._flush_resident(self.embed, "embed", -1)
+        rec["other_jobs"].append(self._flush_resident(self.embed, "embed", -1))
         e_end = self._ev(c)
         e_end.synchronize()
         rec["ev0"], rec["ev_end"] = ev0, e_end
@@ -559,8 +624,8 @@ class SlideEngine:
                 for key in ("fwd", "bwd"):
                     if key in lr:
                         gpu_iv.append((to_host(lr[key][0]), to_host(lr[key][1])))
-            if "ce" in rec:
-                gpu_iv.append((to_host(rec["ce"][0]), to_host(rec["ce"][1])))
+            for a, b in rec.get("ce_iv", []):
+                gpu_iv.append((to_host(a), to_host(b)))
             jobs = {j.name: j for j in rec["jobs"]}
             prev_end = -1e30
             for i in range(L - 1, -1, -1):

@@ -63,6 +63,29 @@ def test_validation_errors_before_any_launch():
     assert e.value.code == _capi.SLIDE_E_SHAPE
 
 
+def test_ce_phase_validation():
+    ce = sl.CeCfg(4096, 128256, 8192, sl.SLIDE_BF16)
+    assert sl.slide_lmhead_ce_n_chunks(ce) == 16            # 15 full chunks and one of 5376 rows
+    assert sl.slide_lmhead_ce_n_chunks(sl.CeCfg(256, 1024, 0, sl.SLIDE_F32)) == 1
+    assert sl.slide_lmhead_ce_n_chunks(sl.CeCfg(256, 1024, 256, sl.SLIDE_F32)) == 4
+    need = sl.slide_lmhead_ce_workspace_bytes(ce, 64)
+    for chunk in (-1, 16):                                  # chunk index out of range
+        with pytest.raises(sl.SlideError) as e:
+            sl.slide_lmhead_ce_stats(ce, 256, 512, 1024, 64, chunk, 2048, need)
+        assert e.value.code == _capi.SLIDE_E_ARG and "chunk" in str(e.value)
+        with pytest.raises(sl.SlideError) as e:
+            sl.slide_lmhead_ce_grad(ce, 256, 512, 1024, 64, chunk, 1, 4096, 2048, need)
+        assert e.value.code == _capi.SLIDE_E_ARG
+    with pytest.raises(sl.SlideError) as e:                 # workspace one byte short
+        sl.slide_lmhead_ce_loss(ce, 1024, 64, 4096, 2048, need - 1)
+    assert e.value.code == _capi.SLIDE_E_WORKSPACE
+    with pytest.raises(sl.SlideError) as e:                 # null dh
+        sl.slide_lmhead_ce_dh(ce, 64, None, 2048, need)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    with pytest.raises(sl.SlideError) as e:                 # bad cfg
+        sl.slide_lmhead_ce_n_chunks(sl.CeCfg(4096, 1001, 8192, sl.SLIDE_BF16))
+
+
 def test_param_count_and_offsets_match_packing():
     from seeded_inputs import L8B, TINY
     for w in (TINY, L8B):

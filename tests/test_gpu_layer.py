@@ -153,3 +153,35 @@ def test_lmhead_ce_matches_oracle(name, dtype, N, H, V, chunk, ign):
     assert abs(got - rl) <= (1e-5 if dtype == "f32" else 2e-3) * max(1.0, abs(rl))
     assert_close(host(dh), rdh, dtype, "ce dh")
     assert_close(host(dw), rdw, dtype, "ce dw")
+
+
+@pytest.mark.parametrize("dtype,N,H,V,chunk,ign", [("bf16", 300, 256, 1000, 256, 0.1),
+                                                  ("f32", 200, 256, 1024, 384, 0.0)])
+def test_lmhead_ce_phases_equal_single_call(dtype, N, H, V, chunk, ign):
+    """The host-driven phases (stats per chunk in reverse order, loss, grad per chunk, dh) give
+    the single call's results bit for bit."""
+    print(f"lmhead ce phases {dtype}: N={N} H={H} V={V} chunk={chunk}", flush=True)
+    h, w, t = ce_inputs(N, H, V, dtype, ignore_frac=ign)
+    cfg = sl.CeCfg(H, V, chunk, sl.dtype_code(dtype))
+    wsz = sl.slide_lmhead_ce_workspace_bytes(cfg, N)
+    th, tw, tt = dev(h.f32, dtype), dev(w.f32, dtype), torch.from_numpy(t).to(DEV)
+    loss1 = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
+    dh1, dw1 = empty((N, H), dtype), empty((V, H), dtype)
+    sl.slide_lmhead_ce(cfg, th, tw, tt, N, loss1, dh1, dw1, ws(wsz), wsz, stream())
+    nch = sl.slide_lmhead_ce_n_chunks(cfg)
+    assert nch == (V + chunk - 1) // chunk
+    W2 = ws(wsz)
+    loss2 = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
+    dh2, dw2 = empty((N, H), dtype), torch.full((V, H), float("nan"), device=DEV,
+                                               dtype=dh1.dtype)
+    for ci in reversed(range(nch)):
+        sl.slide_lmhead_ce_stats(cfg, th, tw, tt, N, ci, W2, wsz, stream())
+    sl.slide_lmhead_ce_loss(cfg, tt, N, loss2, W2, wsz, stream())
+    for ci in range(nch):
+        sl.slide_lmhead_ce_grad(cfg, th, tw, tt, N, ci, True, dw2, W2, wsz, stream())
+    sl.slide_lmhead_ce_dh(cfg, N, dh2, W2, wsz, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(loss1, loss2)
+    bits = (lambda x: x.view(torch.int16)) if dtype == "bf16" else (lambda x: x.view(torch.int32))
+    assert torch.equal(bits(dh1), bits(dh2))
+    assert torch.equal(bits(dw1), bits(dw2))
