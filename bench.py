@@ -115,7 +115,7 @@ def cpu_baseline(w, budget_note=True):
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3-8b-shaped",
                     choices=["llama3-8b-shaped", "123b-shaped-slice", "lmhead-ce-128k",
@@ -164,6 +164,44 @@ def _host_bytes_needed(w):
     return n * 14          # fp32 master + m + v (12 B) and the pinned bf16 buffer (2 B)
 
 
+def host_roofline(w, threads, step_s):
+    """The step's host-memory bound: every parameter's CPU AdamW moves 28 bytes through host
+    DRAM (fp32 master, m, v read and written, the bf16 gradient read and the bf16 weight
+    written), and the weight uploads and gradient flushes cross it once more. Bound = those
+    bytes at the rate slide_cpu_adamw reaches alone on this host (one layer's worth of state on
+    huge pages, same thread count), which is what the host sustains for this access pattern."""
+    import layer_sliding_offloaded_fwd_amd as sl
+    from layer_sliding_offloaded_fwd_amd.engine import _host_f32
+    import torch
+    c = w.layer
+    n = c.param_count()
+    p, m, v = _host_f32(n), _host_f32(n), _host_f32(n)
+    for t in (p, m, v):
+        t.fill_(0.0)                 # touch every page before timing
+    p.fill_(0.01)
+    # the gradient / bf16-weight buffer is pinned, as the engine's shared buffers are
+    g = torch.zeros(n, dtype=torch.int16, pin_memory=True).numpy()
+    hp = sl.AdamWHp(1e-4, 0.9, 0.999, 1e-8, 0.01)
+    ts = []
+    for k in range(6):
+        a = time.perf_counter()
+        sl.slide_cpu_adamw(p, g, sl.SLIDE_BF16, m, v, g, n, k + 1, hp, threads)
+        ts.append(time.perf_counter() - a)
+    bw = 28 * n / min(ts[1:])        # best of the timed calls: the host's DRAM is shared
+    n_all = w.n_layers * n + 2 * w.vocab * c.hidden + c.hidden
+    adam_bytes = 28 * n_all
+    # uploads: every layer twice except the ring's slots reused at the turnaround; the resident
+    # embedding and LM head once; flushes: every gradient once (bf16)
+    h2d = 2 * (2 * w.n_layers - w.ring_slots) * n + 2 * (2 * w.vocab * c.hidden + c.hidden)
+    d2h = 2 * n_all
+    bound_s = adam_bytes / bw
+    return {"bound": "host_dram", "adamw_bytes": adam_bytes, "h2d_bytes": h2d, "d2h_bytes": d2h,
+            "adamw_alone_gbs": round(bw / 1e9, 1),
+            "step_bound_ms": round(bound_s * 1e3, 1),
+            "frac": round(bound_s / step_s, 4),
+            "note": "bound counts the AdamW bytes only; the PCIe copies load the same DRAM"}
+
+
 def run_step(w, args):
     import torch
     import layer_sliding_offloaded_fwd_amd as sl
@@ -194,9 +232,11 @@ def run_step(w, args):
     sl.slide_prof_reset()
     sl.slide_prof_enable(True)
     t0 = time.perf_counter()
+    t_ret = []
     for i in range(args.steps):
         eng.step(toks[args.warmup + i])
-    eng.wait_updates()
+        t_ret.append(time.perf_counter())
+    eng.wait_updates()       # the last step's pending CPU updates are part of the timed work
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sl.slide_prof_enable(False)
@@ -204,8 +244,10 @@ def run_step(w, args):
     loss = eng.loss()
     step_s = (t1 - t0) / args.steps
     tok_s = w.batch * w.seq / step_s
-    print(f"[bench] {args.steps} steps: {step_s * 1e3:.1f} ms/step, {tok_s:.0f} tokens/s, "
-          f"loss {loss:.4f}", file=sys.stderr, flush=True)
+    periods = np.diff(np.asarray(t_ret)) * 1e3
+    steady_ms = float(np.median(periods)) if len(periods) else step_s * 1e3
+    print(f"[bench] {args.steps} steps: {step_s * 1e3:.1f} ms/step ({steady_ms:.1f} ms steady), "
+          f"{tok_s:.0f} tokens/s, loss {loss:.4f}", file=sys.stderr, flush=True)
 
     alg, exe = kernel_flops(spec, w.batch, w.seq, w.ce_chunk)
     kernels = _kernel_table(prof, alg, exe, kernel_bytes(spec, w.batch, w.seq))
@@ -222,6 +264,7 @@ def run_step(w, args):
     mfma_util_exec = 100.0 * l_exe / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     ana = eng.analyse(eng.records[-args.steps:])
     eng.close()
+    host = host_roofline(w, threads, step_s)
     layer_bytes = w.n_layers * c.param_count() * 28
     return {
         "metric": "train tokens/sec (1 GPU) + layer MFMA util % + backward/update overlap %",
@@ -255,6 +298,8 @@ def run_step(w, args):
         "host_adamw_gbs": round(layer_bytes / (ana["t_update_total_ms"] * 1e-3) / 1e9, 1)
         if ana["t_update_total_ms"] else None,
         "loss_last_step": round(loss, 4),
+        "ms_per_step_steady": round(steady_ms, 2),
+        "host_roofline": host,
         "roofline": _roofline(kernels, alg),
         "kernels": kernels,
         "init_s": round(t_init, 1),
@@ -351,9 +396,9 @@ def run_sweep(args):
     torch.cuda.synchronize()
     t_d2h = e0.elapsed_time(e1) / 5
     # T_update: the CPU AdamW of the layer's parameters
-    pm = np.random.default_rng(0).standard_normal(P).astype(np.float32)
-    mm = np.zeros(P, np.float32)
-    vv = np.zeros(P, np.float32)
+    from layer_sliding_offloaded_fwd_amd.engine import _host_f32
+    pm, mm, vv = _host_f32(P), _host_f32(P), _host_f32(P)     # as the engine holds them
+    pm.fill_(0.01)
     gb = host_g.view(torch.int16).numpy()
     hp = sl.AdamWHp(1e-4, 0.9, 0.999, 1e-8, 0.01)
     ts = []
