@@ -147,14 +147,43 @@ def _kernel_table(prof, alg, exe, byt):
     return kernels
 
 
-def _roofline(kernels, alg):
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_8b_layer_hbm_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "layer_sliding_offloaded_fwd_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm.h")]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` at the 8B layer shapes, from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy), or None when there is no
+    figure for it or the GEMM sources changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    sha, table = None, {}
+    for line in open(TRAFFIC_FILE):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "source_sha256":
+            sha = parts[1]
+        elif len(parts) == 3 and parts[0] == "traffic":
+            table[parts[1]] = int(parts[2])
+    if sha != h.hexdigest():
+        return None
+    return table.get(kernel)
+
+
+def _roofline(kernels, alg, traffic_ok=False):
     mfma_names = [n for n in kernels if n in alg]
     dom = max(mfma_names, key=lambda n: kernels[n]["total_ms"])
     dk = kernels[dom]
     achieved = alg[dom] / (dk["avg_ms"] * 1e-3) / 1e12
     return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(dom) if traffic_ok else None,
             "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom]}
 
 
@@ -300,7 +329,7 @@ def run_step(w, args):
         "loss_last_step": round(loss, 4),
         "ms_per_step_steady": round(steady_ms, 2),
         "host_roofline": host,
-        "roofline": _roofline(kernels, alg),
+        "roofline": _roofline(kernels, alg, traffic_ok=(w.name == "llama3-8b-shaped")),
         "kernels": kernels,
         "init_s": round(t_init, 1),
     }
@@ -528,7 +557,7 @@ def run_layer_kernels(args):
                    "kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "ffn": c.ffn,
                    "global_batch": Bb, "seq_len": S},
         "layer_mfma_util_pct": round(100 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": _roofline(kernels, alg), "kernels": kernels,
+        "roofline": _roofline(kernels, alg, traffic_ok=True), "kernels": kernels,
         "copy_ref": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(copy_ms, 4),
                      "gbs_read_plus_write": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)},
     }
