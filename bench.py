@@ -65,25 +65,25 @@ def kernel_bytes(spec, B, S):
             "rope_bwd": 2 * N * (QR - spec.n_kv_heads * d) * 2}
 
 
-def cpu_baseline(w, budget_note=True):
+def cpu_baseline(w):
     """The oracle (NumPy fp64) timed on a bounded sample of the same workload, scaled to the
-    workload's tokens/s: one layer fwd+bwd at B=1 x S=1024, the LM-head CE on 256 tokens at the
-    full vocabulary, and the fp32 AdamW on 1/8 of one layer's parameters."""
+    workload's tokens/s: one layer fwd+bwd at B=2 x S=1024, the LM-head CE on 1024 tokens at the
+    full vocabulary, and the fp32 AdamW on one layer's parameters (about 10 s of CPU work)."""
     from oracle import adamw as oa
     from oracle import model as om
     from seeded_inputs import activations, layer_params
     c = w.layer
     shape = om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn)
-    S1 = 1024
+    B1, S1 = 2, 1024
     p = {k: v.f64 for k, v in layer_params(c, "bf16", seed=0).items()}
-    x = activations((1, S1, c.hidden), "bf16", 1).f64
-    dy = activations((1, S1, c.hidden), "bf16", 2).f64
+    x = activations((B1, S1, c.hidden), "bf16", 1).f64
+    dy = activations((B1, S1, c.hidden), "bf16", 2).f64
     t0 = time.perf_counter()
     y, cache = om.layer_fwd(p, x, shape)
     om.layer_bwd(p, dy, cache, shape)
     t_layer = time.perf_counter() - t0
     del p, cache
-    n_ce = 256
+    n_ce = 1024
     rng = np.random.default_rng(3)
     h = rng.standard_normal((n_ce, c.hidden))
     wl = rng.standard_normal((w.vocab, c.hidden)) * 0.02
@@ -92,7 +92,7 @@ def cpu_baseline(w, budget_note=True):
     om.ce_chunked(h, wl, t, w.ce_chunk)
     t_ce = time.perf_counter() - t0
     del wl
-    n_ad = c.param_count() // 8
+    n_ad = c.param_count()
     pa = rng.standard_normal(n_ad).astype(np.float32)
     ga = (rng.standard_normal(n_ad) * 1e-3).astype(np.float32)
     z = np.zeros(n_ad, np.float32)
@@ -101,14 +101,19 @@ def cpu_baseline(w, budget_note=True):
     t_ad = time.perf_counter() - t0
     n_params = w.n_layers * c.param_count() + 2 * w.vocab * c.hidden + c.hidden
     tokens = w.batch * w.seq
-    step_s = (tokens / S1) * w.n_layers * t_layer + (tokens / n_ce) * t_ce + \
+    step_s = (tokens / (B1 * S1)) * w.n_layers * t_layer + (tokens / n_ce) * t_ce + \
         (n_params / n_ad) * t_ad
-    cores = len(os.sched_getaffinity(0))
-    return {"value": tokens / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"fp64 oracle: one {w.name} layer fwd+bwd at B=1 S=1024 ({t_layer:.2f} s), "
-                       f"LM-head CE on {n_ce} tokens at V={w.vocab} ({t_ce:.2f} s), fp32 AdamW on "
-                       f"{n_ad} params ({t_ad:.2f} s); scaled to {w.n_layers} layers, "
-                       f"{tokens} tokens and {n_params} parameters per step"),
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = len(os.sched_getaffinity(0))
+    return {"value": tokens / step_s, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "sample": (f"fp64 oracle: one {w.name} layer fwd+bwd at B={B1} S={S1} "
+                       f"({t_layer:.2f} s), LM-head CE on {n_ce} tokens at V={w.vocab} "
+                       f"({t_ce:.2f} s), fp32 AdamW on one layer's {n_ad} params ({t_ad:.2f} s, "
+                       f"one thread); scaled to {w.n_layers} layers, {tokens} tokens and "
+                       f"{n_params} parameters per step; cores = BLAS threads"),
             "sample_seconds": round(t_layer + t_ce + t_ad, 2)}
 
 
