@@ -7,7 +7,9 @@
 // bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, flash-style, no [S, S]
 // tensor in memory):
 //  * every operand tile is [64 rows][d] of q, k, v or dO rows, copied global -> LDS by
-//    direct-to-LDS loads into 3 pipelined stages (two blocks in flight while one is computed).
+//    direct-to-LDS loads into 2 pipelined stages (the next block in flight while one is
+//    computed). The forward and dQ kernels are held to 256 registers per lane so that two
+//    workgroups share a compute unit: one wave's softmax runs beside the other's MFMAs.
 //    A tile is read either as rows (16-byte reads: MFMA fragments of q, k, v or dO) or, through
 //    the LDS transpose read ds_read_b64_tr_b16, as columns (fragments of v^T, k^T, q^T, dO^T),
 //    so no operand is ever transposed in registers. The 16-byte chunks of row r are XOR-swizzled
@@ -35,7 +37,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int NSTAGE = 3;  // LDS stages of the key (or query) block pipeline
+// LDS stages of the key (or query) block pipeline: two (64 KB at d = 128), so that two
+// workgroups (two waves per SIMD) fit a compute unit
+constexpr int NSTAGE = 2;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -172,7 +176,7 @@ template <int D> constexpr int smem_elems(int tiles) {
 
 // ------------------------------------------------------------------ forward
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                        bf16_t* __restrict__ out,
                                                        float* __restrict__ lse, int S, int nq,
                                                        int nkv, float scale) {
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 
 // ------------------------------------------------------------------ dQ
 template <int D>
-__global__ __launch_bounds__(256) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                       const bf16_t* __restrict__ dout,
                                                       const float* __restrict__ lse,
                                                       const float* __restrict__ delta,
@@ -507,59 +511,60 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
     const bf16_t* sQ = tQ(st);
     const bf16_t* sO = tO(st);
 
-    f32x16_t sacc[2], pacc[2];
+    const bool need_mask = (q0 < wk0 + 31) || (q0 + 64 > S) || (wk0 + 32 > S);
+    // the 64 queries in two halves of 32, one after the other, so that only one half's score
+    // and dP accumulators are live (keeps the kernel within 256 registers)
 #pragma unroll
     for (int qb2 = 0; qb2 < 2; ++qb2) {
+      f32x16_t sacc, pacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sacc[qb2][e] = 0.f;
-        pacc[qb2][e] = 0.f;
+        sacc[e] = 0.f;
+        pacc[e] = 0.f;
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc[qb2], 0, 0, 0);
-        pacc[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc[qb2], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc, 0, 0, 0);
       }
-    }
-    const bool need_mask = (q0 < wk0 + 31) || (q0 + 64 > S) || (wk0 + 32 > S);
-    // element i of sub-block qb2 is (query q0 + acc_key(qb2, i), this lane's key)
-#pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2)
+      // element i is (query q0 + acc_key(qb2, i), this lane's key)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ql = acc_key(qb2, i, hf);
-        float p = exp2f(sacc[qb2][i] * sl2 - sL[st][ql] * kLog2e);
+        float p = exp2f(sacc[i] * sl2 - sL[st][ql] * kLog2e);
         if (need_mask) {
           const int qq = q0 + ql;
           if (key > qq || qq >= S) p = 0.f;
         }
-        sacc[qb2][i] = p;
-        pacc[qb2][i] = p * (pacc[qb2][i] - sDl[st][ql]);
+        sacc[i] = p;
+        pacc[i] = p * (pacc[i] - sDl[st][ql]);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float pv[8], sv[8];
+      for (int kh = 0; kh < 2; ++kh) {
+        const int ks = 2 * qb2 + kh;
+        float pv[8], sv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-        sv[j] = pacc[ks >> 1][8 * (ks & 1) + j];
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = sacc[8 * kh + j];
+          sv[j] = pacc[8 * kh + j];
+        }
+        const bf16x8_t pf = pack8(pv), sf = pack8(sv);
+        bf16x8_t ot[NDB], qt[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) ot[db] = t_read<D>(sO, db * 32, ks, lane);
+        tr_wait(ot);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[db], pf, dv[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) qt[db] = t_read<D>(sQ, db * 32, ks, lane);
+        tr_wait(qt);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], sf, dk[db], 0, 0, 0);
       }
-      const bf16x8_t pf = pack8(pv), sf = pack8(sv);
-      bf16x8_t ot[NDB], qt[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) ot[db] = t_read<D>(sO, db * 32, ks, lane);
-      tr_wait(ot);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[db], pf, dv[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) qt[db] = t_read<D>(sQ, db * 32, ks, lane);
-      tr_wait(qt);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], sf, dk[db], 0, 0, 0);
     }
   }
   wait_vm<0>();
