@@ -131,6 +131,10 @@ def _parse():
                          "device copy that calibrates HBM byte counters)")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers of the 123b slice (default 12, fewer if host RAM is short)")
+    ap.add_argument("--activations", default="hbm", choices=["hbm", "recompute", "host"],
+                    help="forward state for the backward: intermediates kept in HBM (default), "
+                         "layer inputs kept and the forward recomputed, or layer inputs slid to "
+                         "host memory and back (with recompute)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
@@ -251,7 +255,8 @@ def run_step(w, args):
     print(f"[bench] {w.name}: {w.n_layers} layers, host state {_host_bytes_needed(w) / 1e9:.1f} GB;"
           f" allocating", file=sys.stderr, flush=True)
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
-                      hp=AdamW(), adam_threads=threads, timeline=True)
+                      hp=AdamW(), adam_threads=threads, timeline=True,
+                      activations=args.activations)
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
@@ -318,7 +323,11 @@ def run_step(w, args):
                    "ffn": c.ffn, "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
                    "ring_slots": w.ring_slots, "ce_chunk": w.ce_chunk,
                    "parallelism": "single GPU, layers streamed from host",
-                   "adam_threads": threads, "activations": "kept in HBM (no recompute)"},
+                   "adam_threads": threads,
+                   "activations": {"hbm": "intermediates kept in HBM (no recompute)",
+                                   "recompute": "layer inputs kept in HBM, forward recomputed",
+                                   "host": "layer inputs slid to host memory, forward "
+                                           "recomputed"}[args.activations]},
         "layer_mfma_util_pct": round(mfma_util_alg, 2),
         "layer_mfma_util_exec_pct": round(mfma_util_exec, 2),
         "overlap_pct": round(ana["overlap_pct"], 1),

@@ -148,8 +148,20 @@ class _Param:
 class SlideEngine:
     def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
-                 save_activations=True):
+                 save_activations=True, activations=None, x_slots=4):
+        """activations: where the forward's state for the backward lives.
+          "hbm" (default): every layer's intermediates stay in HBM; no recompute.
+          "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
+          "host": layer inputs slide to pinned host memory after the forward and come back
+            before the backward (the pages' sliding activations), with recompute; only
+            x_slots layer-input buffers stay on the device.
+        save_activations=False is the older spelling of activations="recompute"."""
         assert spec.dtype in ("bf16", "f32")
+        if activations is None:
+            activations = "hbm" if save_activations else "recompute"
+        assert activations in ("hbm", "recompute", "host"), activations
+        self.activations = activations
+        save_activations = activations == "hbm"
         self.spec, self.B, self.S, self.N = spec, batch, seq, batch * seq
         self.L = spec.n_layers
         self.n_slots = max(1, min(n_slots, self.L))
@@ -196,7 +208,18 @@ class SlideEngine:
         self.ring_mem = torch.empty(self.n_slots * 2 * self.w_bytes, dtype=torch.uint8, device=dev)
         self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
                                self.h2d, self.d2h)
-        self.xs = torch.empty((self.L + 1, N, H), dtype=self.tdt, device=dev)   # layer inputs
+        if activations == "host":
+            # a ring of x_slots device buffers: layer input i lives in slot i % x_slots; the
+            # inputs a later layer's output would overwrite are copied to pinned host memory
+            self.x_slots = max(3, min(x_slots, self.L + 1))
+            self.xs = torch.empty((self.x_slots, N, H), dtype=self.tdt, device=dev)
+            self.x_host = self.pinned.tensor((self.L + 1) * N * H,
+                                             torch.int16 if s.dtype == "bf16" else torch.float32)
+            self.x_d2h_ev = [None] * (self.L + 1)
+            self.x_h2d_ev = [None] * (self.L + 1)
+        else:
+            self.x_slots = self.L + 1
+            self.xs = torch.empty((self.L + 1, N, H), dtype=self.tdt, device=dev)   # layer inputs
         self.grad_x = torch.empty((N, H), dtype=self.tdt, device=dev)
         self.hf = torch.empty((N, H), dtype=self.tdt, device=dev)
         self.dhf = torch.empty((N, H), dtype=self.tdt, device=dev)
@@ -432,6 +455,41 @@ class SlideEngine:
         prm.flushed_ev = done
         return self._submit(prm, done, name, priority, post=lambda: self._upload_resident(prm))
 
+    # ------------------------------------------------------------------ sliding activations
+    def _x(self, i):
+        """Device buffer of layer input i (i = L: the last layer's output)."""
+        return self.xs[i % self.x_slots]
+
+    def _x_host(self, i):
+        n = self.N * self.spec.hidden
+        t = self.x_host[i * n:(i + 1) * n]
+        return (t.view(torch.bfloat16) if self.spec.dtype == "bf16" else t).view(self.N, -1)
+
+    def _x_offload(self, i):
+        """After the compute stream's work so far (the forward of layer i), copy layer input i
+        to host memory; its slot may be overwritten once the copy is done."""
+        ev = torch.cuda.Event()
+        ev.record(self.compute)
+        self.d2h.wait_event(ev)
+        with torch.cuda.stream(self.d2h):
+            self._x_host(i).copy_(self._x(i), non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(self.d2h)
+        self.x_d2h_ev[i] = done
+
+    def _x_reload(self, i):
+        """After the compute stream's work so far (which last used slot i % x_slots), bring
+        layer input i back from host memory into its slot."""
+        ev = torch.cuda.Event()
+        ev.record(self.compute)
+        self.h2d.wait_event(ev)
+        self.h2d.wait_event(self.x_d2h_ev[i])
+        with torch.cuda.stream(self.h2d):
+            self._x(i).copy_(self._x_host(i), non_blocking=True)
+            done = torch.cuda.Event()
+            done.record(self.h2d)
+        self.x_h2d_ev[i] = done
+
     def _flush_lm_chunk(self, ci, rec):
         """D2H of LM-head chunk ci's gradient rows once the compute stream has produced them,
         then that chunk's AdamW, then its refreshed rows go back up on the H2D stream."""
@@ -489,7 +547,9 @@ class SlideEngine:
         c.wait_event(self.embed.ready_ev)
         if self.embed.flushed_ev is not None:
             c.wait_event(self.embed.flushed_ev)
-        B.slide_embed_fwd(self.embed.dev, self.tok_in, self.xs[0], N, H, V, self.code, c)
+        host_x = self.activations == "host"
+        K = self.x_slots
+        B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
         # Prefetch: load layers in order into free slots as soon as their update is done,
         # without blocking; block only for the layer the forward needs next.
         slots = {}
@@ -514,15 +574,19 @@ class SlideEngine:
                 prefetch(need=i)
             s = slots.pop(i)
             w, _ = self.ring.acquire(s, c)
+            if host_x and i + 1 >= K:          # the output overwrites input i + 1 - K: copied?
+                c.wait_event(self.x_d2h_ev[i + 1 - K])
             e_a = self._ev(c) if self.timeline else None
             if self.save_activations:
-                B.slide_layer_fwd_save(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S,
+                B.slide_layer_fwd_save(self.cfg, w, self._x(i), self._x(i + 1), self.B, self.S,
                                        self.saved[i], self.saved_bytes, c)
             else:
-                B.slide_layer_fwd(self.cfg, w, self.xs[i], self.xs[i + 1], self.B, self.S,
+                B.slide_layer_fwd(self.cfg, w, self._x(i), self._x(i + 1), self.B, self.S,
                                   self.ws, self.ws_bytes, c)
             if self.timeline:
                 rec["layers"].setdefault(i, {})["fwd"] = (e_a, self._ev(c))
+            if host_x and i <= L - K:          # inputs L-K+1 .. L stay in their slots
+                self._x_offload(i)
             self.ring.release(s, c)
             free[0] += 1
             self._sync()
@@ -533,7 +597,7 @@ class SlideEngine:
         c.wait_event(self.final.ready_ev)
         if self.final.flushed_ev is not None:
             c.wait_event(self.final.flushed_ev)
-        B.slide_rmsnorm_fwd(self.xs[L], self.final.dev, self.hf, None, N, H, spec.rms_eps,
+        B.slide_rmsnorm_fwd(self._x(L), self.final.dev, self.hf, None, N, H, spec.rms_eps,
                             self.code, c)
         ce, lm = self.ce_cfg, self.lm
         ce_iv = rec["ce_iv"] = []         # GPU intervals of the CE, without its waits
@@ -556,7 +620,7 @@ class SlideEngine:
         B.slide_lmhead_ce_dh(ce, N, self.dhf, self.ws, self.ws_bytes, c)
         if self.timeline:
             ce_iv.append((e_ce, self._ev(c)))
-        B.slide_rmsnorm_bwd(self.dhf, self.xs[L], self.final.dev, None, self.grad_x,
+        B.slide_rmsnorm_bwd(self.dhf, self._x(L), self.final.dev, None, self.grad_x,
                             self.final.grad, N, H, spec.rms_eps, self.code, self.ws,
                             self.ws_bytes, c)
         rec["other_jobs"].append(self._flush_resident(self.final, "w_final", L))
@@ -566,17 +630,23 @@ class SlideEngine:
         # before the first prefetch so that no load can pick one of their slots
         for i in range(L - 1, L - 1 - self.n_slots, -1):
             slots[i] = self.ring.reuse(i)
+        if host_x and L - K >= 0:             # slot of x_L is free after the final norm
+            self._x_reload(L - K)
         for i in range(L - 1, -1, -1):
             s = slots.pop(i)
             w, g = self.ring.acquire(s, c)
+            if host_x and i <= L - K:
+                c.wait_event(self.x_h2d_ev[i])
             e_a = self._ev(c) if self.timeline else None
             if self.save_activations:
-                B.slide_layer_bwd_saved(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g,
+                B.slide_layer_bwd_saved(self.cfg, w, self._x(i), self.grad_x, self.grad_x, g,
                                         self.B, self.S, self.saved[i], self.saved_bytes, self.ws,
                                         self.ws_bytes, c)
             else:
-                B.slide_layer_bwd(self.cfg, w, self.xs[i], self.grad_x, self.grad_x, g, self.B,
+                B.slide_layer_bwd(self.cfg, w, self._x(i), self.grad_x, self.grad_x, g, self.B,
                                   self.S, self.ws, self.ws_bytes, c)
+            if host_x and i - K >= 0:          # slot i % K is free again: input i - K comes back
+                self._x_reload(i - K)
             e_b = self._ev(c) if self.timeline else None
             ticket = self.ring.flush(s, self.layers[i].grad_host, c)
             if self.timeline:

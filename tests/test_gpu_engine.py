@@ -100,11 +100,12 @@ def test_tiny_fp32_step_matches_oracle(ce_chunk):
 SMALL = Workload("small-bf16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "bf16")
 
 
-def _run(n_slots, serialize, steps=2, save=True, ce_chunk=256):
+def _run(n_slots, serialize, steps=2, save=True, ce_chunk=256, activations=None, x_slots=4):
     w = SMALL
     params = model_params(w, seed=0, gain_std=0.1)
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=n_slots, hp=HP, adam_threads=3,
-                      serialize=serialize, save_activations=save, ce_chunk=ce_chunk)
+                      serialize=serialize, save_activations=save, ce_chunk=ce_chunk,
+                      activations=activations, x_slots=x_slots)
     try:
         eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
                         params["lm_head"].f32)
@@ -126,14 +127,17 @@ def test_offload_and_overlap_do_not_change_results():
     lone, pone = _run(1, False)
     lrec, prec = _run(3, False, save=False)       # backward recomputes the forward instead
     lsteps, psteps = _run(3, False, steps=3)
-    print(f"  losses {la} {lb} {lc} {lone} {lrec} {lsteps}", flush=True)
-    assert la == lb == lc == lone == lrec == lsteps[:2]
+    # layer inputs slide to host memory (3 device slots for 5 layers) and come back
+    lhost, phost = _run(3, False, activations="host", x_slots=3)
+    lhost1, phost1 = _run(1, True, activations="host", x_slots=3)
+    print(f"  losses {la} {lb} {lc} {lone} {lrec} {lsteps} {lhost} {lhost1}", flush=True)
+    assert la == lb == lc == lone == lrec == lsteps[:2] == lhost == lhost1
     # one LM-head chunk instead of four: the same step up to rounding (an AdamW step moves a
     # weight by at most about lr, so rounding-level gradient differences stay below 2 lr)
     l_ch, p_ch = _run(3, True, ce_chunk=1024)
     assert all(abs(x - y) <= 2e-3 * abs(y) for x, y in zip(l_ch, la))
     assert float(np.max(np.abs(p_ch["lm_head"] - pa["lm_head"]))) <= 2.5 * HP.lr
-    for other in (pb, pc, pone, prec):
+    for other in (pb, pc, pone, prec, phost, phost1):
         for k in ("embed", "w_final", "lm_head"):
             assert np.array_equal(pa[k].view(np.uint32), other[k].view(np.uint32)), k
         for x, y in zip(pa["layers"], other["layers"]):
