@@ -274,6 +274,51 @@ __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ 
   }
 }
 
+// The same loads with the per-lane addressing computed once: each lane keeps one source pointer
+// per load of the stage and advances it by a per-load byte step (0 for a lane outside the
+// matrix, which keeps reading the zero page) each time a stage is issued. Stages are issued in
+// order; a stage that reaches past K goes through the bounds-checked issue() instead.
+template <bool KMAJ, int NW, int BK>
+struct Streamer {
+  static constexpr int NL = BK / 2 / NW;   // this wave's loads per stage of one operand
+  const char* ptr[NL];
+  int step[NL];
+  int dst0;                                // element offset of this wave's first load in a stage
+
+  __device__ __forceinline__ void init(const bf16_t* __restrict__ P, int ld, int row0,
+                                       int rows_total, int wave, int lane) {
+    constexpr int LPR = BK / 8;
+    dst0 = wave * 512;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int instr = wave + NW * q;
+      bool ok;
+      size_t off;
+      if constexpr (KMAJ) {
+        const int r = instr * (64 / LPR) + lane / LPR;
+        const int c = (lane % LPR) ^ swzk<BK>(r);
+        ok = row0 + r < rows_total;
+        off = (size_t)(row0 + r) * ld + c * 8;
+      } else {
+        const int kr = instr * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swzt(kr);
+        ok = row0 + c * 8 < rows_total;
+        off = (size_t)kr * ld + row0 + c * 8;
+      }
+      ptr[q] = ok ? (const char*)(P + off) : (const char*)zero_page;
+      step[q] = ok ? (KMAJ ? BK * 2 : BK * ld * 2) : 0;
+    }
+  }
+  __device__ __forceinline__ void issue_next(bf16_t* stage) {
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      __builtin_amdgcn_global_load_lds((glob_void_t*)ptr[q],
+                                       (lds_void_t*)(stage + dst0 + NW * 512 * q), 16, 0, 0);
+      ptr[q] += step[q];
+    }
+  }
+};
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -371,10 +416,19 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   const int nk = (g.K + BK - 1) / BK;
   auto stage_a = [&](int b) { return smem + b * 2 * SE; };
   auto stage_b = [&](int b) { return smem + b * 2 * SE + SE; };
-  auto issue_stage = [&](int kt) {
+  Streamer<AK, NW, BK> sta;
+  Streamer<BKM, NW, BK> stb;
+  sta.init(A, g.lda, m0, g.M, wave, lane);
+  stb.init(B, g.ldb, n0, g.N, wave, lane);
+  auto issue_stage = [&](int kt) {   // stages are issued in order 0, 1, 2, ...
     const int b = kt % NS;
-    issue<AK, NW, BK>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
-    issue<BKM, NW, BK>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
+    if ((kt + 1) * BK <= g.K) {
+      sta.issue_next(stage_a(b));
+      stb.issue_next(stage_b(b));
+    } else {                         // the last, partial stage: bounds-checked per lane
+      issue<AK, NW, BK>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
+      issue<BKM, NW, BK>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
+    }
   };
   // Wait until stage kt has landed (this wave's loads; the barrier that follows covers the
   // other waves'): the loads of the stages issued after it, up to stage `last`, may stay in
