@@ -138,7 +138,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
-                    help="CPU AdamW threads (default: cores - 1)")
+                    help="CPU AdamW threads (default: cores - 3, leaving cores to the engine thread and the HIP runtime)")
     return ap.parse_args()
 
 
@@ -250,7 +250,7 @@ def run_step(w, args):
     spec = ModelSpec(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.vocab, w.n_layers,
                      "bf16", c.rms_eps, c.rope_theta)
     cores = len(os.sched_getaffinity(0))
-    threads = args.adam_threads or max(1, cores - 1)
+    threads = args.adam_threads or max(1, cores - 3)
     t_init = time.perf_counter()
     print(f"[bench] {w.name}: {w.n_layers} layers, host state {_host_bytes_needed(w) / 1e9:.1f} GB;"
           f" allocating", file=sys.stderr, flush=True)
@@ -426,7 +426,7 @@ def run_sweep(args):
     st = torch.cuda.current_stream()
     # T_grad_d2h: the layer's bf16 gradients to pinned host memory
     cores = len(os.sched_getaffinity(0))
-    threads = args.adam_threads or max(1, cores - 1)
+    threads = args.adam_threads or max(1, cores - 3)
     host_g = torch.empty(P, dtype=torch.bfloat16, pin_memory=True)
     for _ in range(2):
         host_g.copy_(g, non_blocking=True)

@@ -663,7 +663,10 @@ class SlideEngine:
         B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
                           self.ws, self.ws_bytes, c)
         rec["other_jobs"].append(self._flush_resident(self.embed, "embed", -1))
-        e_end = self._ev(c)
+        # the host sleeps until the GPU is done (a blocking event), leaving every core to the
+        # CPU optimizer instead of spinning on one
+        e_end = torch.cuda.Event(enable_timing=True, blocking=True)
+        e_end.record(c)
         e_end.synchronize()
         rec["ev0"], rec["ev_end"] = ev0, e_end
         rec["host_gpu_done"] = time.perf_counter()
