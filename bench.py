@@ -50,8 +50,11 @@ def kernel_flops(spec, B, S, ce_chunk):
     exe.update(attn_fwd=2 * U, attn_bwd_dkv=4 * U, attn_bwd_dq=3 * U)
     nch = (V + ce_chunk - 1) // ce_chunk
     per = 2 * N * V * H / nch           # average per chunk launch
-    alg.update(ce_logits_gemm=per / 2, ce_dh_gemm=per, ce_dw_gemm=per)   # logits recomputed
-    exe.update(ce_logits_gemm=per, ce_dh_gemm=per, ce_dw_gemm=per)
+    # the logits run twice (statistics pass, then recomputed with dz fused); algorithmically once
+    alg.update(ce_stats_gemm=per / 2, ce_dz_gemm=per / 2, ce_logits_gemm=per / 2, ce_dh_gemm=per,
+               ce_dw_gemm=per)
+    exe.update(ce_stats_gemm=per, ce_dz_gemm=per, ce_logits_gemm=per, ce_dh_gemm=per,
+               ce_dw_gemm=per)
     return alg, exe
 
 
@@ -65,16 +68,16 @@ def kernel_bytes(spec, B, S):
             "rope_bwd": 2 * N * (QR - spec.n_kv_heads * d) * 2}
 
 
-def cpu_baseline(w):
+def cpu_baseline(w, B1=2, S1=1024, n_ce=1024, ad_frac=1.0):
     """The oracle (NumPy fp64) timed on a bounded sample of the same workload, scaled to the
-    workload's tokens/s: one layer fwd+bwd at B=2 x S=1024, the LM-head CE on 1024 tokens at the
-    full vocabulary, and the fp32 AdamW on one layer's parameters (about 10 s of CPU work)."""
+    workload's tokens/s: one layer fwd+bwd at B1 x S1 tokens, the LM-head CE on n_ce tokens at
+    the full vocabulary, and the fp32 AdamW on ad_frac of one layer's parameters (about 10 s of
+    CPU work for the 8B shapes)."""
     from oracle import adamw as oa
     from oracle import model as om
     from seeded_inputs import activations, layer_params
     c = w.layer
     shape = om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn)
-    B1, S1 = 2, 1024
     p = {k: v.f64 for k, v in layer_params(c, "bf16", seed=0).items()}
     x = activations((B1, S1, c.hidden), "bf16", 1).f64
     dy = activations((B1, S1, c.hidden), "bf16", 2).f64
@@ -83,7 +86,6 @@ def cpu_baseline(w):
     om.layer_bwd(p, dy, cache, shape)
     t_layer = time.perf_counter() - t0
     del p, cache
-    n_ce = 1024
     rng = np.random.default_rng(3)
     h = rng.standard_normal((n_ce, c.hidden))
     wl = rng.standard_normal((w.vocab, c.hidden)) * 0.02
@@ -92,7 +94,7 @@ def cpu_baseline(w):
     om.ce_chunked(h, wl, t, w.ce_chunk)
     t_ce = time.perf_counter() - t0
     del wl
-    n_ad = c.param_count()
+    n_ad = int(c.param_count() * ad_frac)
     pa = rng.standard_normal(n_ad).astype(np.float32)
     ga = (rng.standard_normal(n_ad) * 1e-3).astype(np.float32)
     z = np.zeros(n_ad, np.float32)
@@ -111,7 +113,7 @@ def cpu_baseline(w):
     return {"value": tokens / step_s, "unit": "tokens/s", "cores": blas, "kind": "oracle",
             "sample": (f"fp64 oracle: one {w.name} layer fwd+bwd at B={B1} S={S1} "
                        f"({t_layer:.2f} s), LM-head CE on {n_ce} tokens at V={w.vocab} "
-                       f"({t_ce:.2f} s), fp32 AdamW on one layer's {n_ad} params ({t_ad:.2f} s, "
+                       f"({t_ce:.2f} s), fp32 AdamW on {n_ad} params ({t_ad:.2f} s, "
                        f"one thread); scaled to {w.n_layers} layers, {tokens} tokens and "
                        f"{n_params} parameters per step; cores = BLAS threads"),
             "sample_seconds": round(t_layer + t_ce + t_ad, 2)}
@@ -237,6 +239,10 @@ def host_roofline(w, threads, step_s):
             "adamw_alone_gbs": round(bw / 1e9, 1),
             "step_bound_ms": round(bound_s * 1e3, 1),
             "frac": round(bound_s / step_s, 4),
+            # achieved rates over the whole step (bytes per step / time per step)
+            "host_dram_gbs": round((adam_bytes + h2d + d2h) / step_s / 1e9, 1),
+            "h2d_link_gbs": round(h2d / step_s / 1e9, 1),
+            "d2h_link_gbs": round(d2h / step_s / 1e9, 1),
             "note": "bound counts the AdamW bytes only; the PCIe copies load the same DRAM"}
 
 
@@ -305,6 +311,8 @@ def run_step(w, args):
     eng.close()
     host = host_roofline(w, threads, step_s)
     layer_bytes = w.n_layers * c.param_count() * 28
+    n_all = w.n_layers * c.param_count() + 2 * w.vocab * c.hidden + c.hidden
+    gpu_kernel_ms = sum(k["total_ms"] for k in kernels.values()) / args.steps
     return {
         "metric": "train tokens/sec (1 GPU) + layer MFMA util % + backward/update overlap %",
         "value": round(tok_s, 1),
@@ -343,6 +351,14 @@ def run_step(w, args):
         "loss_last_step": round(loss, 4),
         "ms_per_step_steady": round(steady_ms, 2),
         "host_roofline": host,
+        # the pages compare offloaded training with training whose state stays on the GPU; this
+        # build has no such variant, so the comparison is against a lower bound of it: the
+        # step's GPU kernel time plus the AdamW bytes at HBM bandwidth
+        "hbm_resident_estimate": {
+            "gpu_kernel_ms_per_step": round(gpu_kernel_ms, 1),
+            "adamw_on_hbm_ms": round(28 * n_all / (PEAK_HBM_GBS * 1e9) * 1e3, 1),
+            "offloaded_fraction_of_resident": round(
+                (gpu_kernel_ms + 28 * n_all / (PEAK_HBM_GBS * 1e9) * 1e3) / (step_s * 1e3), 4)},
         "roofline": _roofline(kernels, alg, traffic_ok=(w.name == "llama3-8b-shaped")),
         "kernels": kernels,
         "init_s": round(t_init, 1),
@@ -385,8 +401,8 @@ def run_ce(args):
     flops_exec = 4 * 2 * N * H * V
     nch = (V + C - 1) // C
     per = 2 * N * V * H / nch
-    alg = {"ce_logits_gemm": per / 2, "ce_dh_gemm": per, "ce_dw_gemm": per}
-    exe = {"ce_logits_gemm": per, "ce_dh_gemm": per, "ce_dw_gemm": per}
+    alg = {"ce_stats_gemm": per / 2, "ce_dz_gemm": per / 2, "ce_dh_gemm": per, "ce_dw_gemm": per}
+    exe = {"ce_stats_gemm": per, "ce_dz_gemm": per, "ce_dh_gemm": per, "ce_dw_gemm": per}
     kernels = _kernel_table(sl.slide_prof_read(), alg, exe, {})
     return {
         "metric": "chunked LM-head cross-entropy fwd+bwd tokens/sec (1 GPU)",
@@ -402,7 +418,30 @@ def run_ce(args):
         "workspace_vs_dense_logits_pct": round(100.0 * wsz / (N * V * 4), 1),
         "loss": round(float(loss.item()), 5),
         "roofline": _roofline(kernels, alg), "kernels": kernels,
+        "cpu_baseline": None if args.no_cpu_baseline else ce_cpu_baseline(N, H, V, C),
     }
+
+
+def ce_cpu_baseline(N, H, V, C, n_s=1024):
+    """The oracle's chunked CE (fwd+bwd, fp64) on n_s of the N tokens at the full vocabulary,
+    scaled to N tokens (the CE is linear in the token count)."""
+    from oracle import model as om
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((n_s, H))
+    w = rng.standard_normal((V, H)) * 0.02
+    t = rng.integers(0, V, n_s)
+    t0 = time.perf_counter()
+    om.ce_chunked(h, w, t, C)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = len(os.sched_getaffinity(0))
+    return {"value": N / (dt * N / n_s), "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "sample": f"fp64 oracle chunked CE fwd+bwd on {n_s} tokens at V={V}, H={H} "
+                      f"({dt:.2f} s), scaled to {N} tokens; cores = BLAS threads",
+            "sample_seconds": round(dt, 2)}
 
 
 def run_sweep(args):
@@ -612,6 +651,11 @@ def main():
         except ImportError:
             pass
         result = run_step(w, args)
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = cpu_baseline(w, B1=1, S1=512, n_ce=1024, ad_frac=0.125)
+        else:
+            result["cpu_baseline"] = None
         print(json.dumps(result))
         return
     w = L8B

@@ -2,13 +2,15 @@
 // projection and the loss are fused so that the [N, V] logit tensor of a large vocabulary never
 // exists, cutting the output layer's memory without changing the result).
 //
-//   pass 1, per chunk c of C vocabulary rows: z_c^T = W_c h^T (MFMA GEMM, fp32 out, [C, N]);
-//           per (token, row split) online max / sum-exp partials and the target logit.
+//   pass 1, per chunk c of C vocabulary rows: z_c^T = W_c h^T (MFMA GEMM); per token and block
+//           of 64 vocabulary rows the max and sum of exp(z - max), and the target logit.
 //   combine: lse_t from the partials in a fixed order; loss = mean over valid t of lse_t - z_t[y_t]
 //   pass 2, per chunk: recompute z_c^T, dz = (exp(z - lse_t) - [v == y_t]) / N_valid,
 //           dh += dz^T W_c (fp32 accumulator), dW_c = dz h.
-// Every reduction has a fixed order, so the results are deterministic. The workspace holds one
-// chunk of logits and gradients, O(C*N), instead of O(V*N).
+// bf16: the statistics of pass 1 and the dz of pass 2 are computed in the logits GEMM's
+// epilogue, so no logit is ever stored; fp32 (the small configuration): the logits of one chunk
+// go to an fp32 buffer that small kernels then reduce. Every reduction has a fixed order, so the
+// results are deterministic. The workspace holds one chunk's dz, O(C*N), instead of O(V*N).
 #include "ce.h"
 
 #include "gemm.h"
@@ -17,7 +19,9 @@
 namespace slide {
 namespace {
 
-constexpr int kRowSplits = 32;  // row splits per chunk in the statistics pass
+// The statistics pass keeps one (max, sum-exp) partial per token and block of kCeRowsPerPart
+// vocabulary rows of a chunk (the bf16 path computes them in the logits GEMM's epilogue).
+__host__ __device__ inline int ce_parts(int rows) { return (rows + kCeRowsPerPart - 1) / kCeRowsPerPart; }
 
 // partial (max, sum exp(z - max)) of rows [r0, r1) of a [rows][ldz] fp32 chunk, per token column
 __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ z, int rows,
@@ -47,23 +51,48 @@ __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__
   if (y >= r0 && y < r1) zt[t] = z[(size_t)y * ldz + t];
 }
 
-// lse_t from all partials (chunk-major, split-minor order) and the per-token loss term
+// lse_t from the partials of every chunk (chunk c holds ce_parts(rows of c) partials starting
+// at slot c * ppc) and the per-token loss term. Thread (t, g) of a 32 x 8 block folds the slots
+// g, g + 8, ... of every chunk for token t (running max, rescaled sum), then the 8 folds of each
+// token are combined in the order g = 0..7: a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void ce_lse_kernel(const float* __restrict__ pm,
-                                                     const float* __restrict__ ps, int nparts,
-                                                     int N, const int32_t* __restrict__ tgt,
-                                                     int V, const float* __restrict__ zt,
+                                                     const float* __restrict__ ps, int nchunks,
+                                                     int C, int ppc, int N,
+                                                     const int32_t* __restrict__ tgt, int V,
+                                                     const float* __restrict__ zt,
                                                      float* __restrict__ lse,
                                                      float* __restrict__ lt) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= N) return;
-  float m = -INFINITY;
-  for (int p = 0; p < nparts; ++p) m = fmaxf(m, pm[(size_t)p * N + t]);
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float pmv = pm[(size_t)p * N + t];
-    if (pmv != -INFINITY) s += ps[(size_t)p * N + t] * __expf(pmv - m);
+  __shared__ float sm[8][32], ss[8][32];
+  const int tl = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int t = blockIdx.x * 32 + tl;
+  float m = -INFINITY, s = 0.f;
+  if (t < N) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int np = ce_parts(min(C, V - c * C));
+      for (int p = g; p < np; p += 8) {
+        const size_t at = (size_t)(c * ppc + p) * N + t;
+        const float pmv = pm[at];
+        if (pmv == -INFINITY) continue;
+        const float psv = ps[at];
+        if (pmv > m) {
+          s = s * __expf(m - pmv) + psv;
+          m = pmv;
+        } else {
+          s += psv * __expf(pmv - m);
+        }
+      }
+    }
   }
-  const float l = m + logf(s);
+  sm[g][tl] = m;
+  ss[g][tl] = s;
+  __syncthreads();
+  if (g != 0 || t >= N) return;
+  float mm = -INFINITY;
+  for (int k = 0; k < 8; ++k) mm = fmaxf(mm, sm[k][tl]);
+  float sum = 0.f;
+  for (int k = 0; k < 8; ++k)
+    if (sm[k][tl] != -INFINITY) sum += ss[k][tl] * __expf(sm[k][tl] - mm);
+  const float l = mm + logf(sum);
   lse[t] = l;
   const int y = tgt[t];
   lt[t] = (y >= 0 && y < V) ? l - zt[t] : 0.f;
@@ -132,7 +161,7 @@ __global__ void fill_zero_kernel(T* p, size_t n) {
 __global__ void write_scalar_kernel(float* p, float v) { *p = v; }
 
 struct CeLayout {
-  int C, nchunks, ldz;
+  int C, nchunks, ldz, ppc;   // ppc: partial slots per chunk
   size_t zbuf, dz, pm, ps, zt, lse, lt, scal, dh, total;
 };
 
@@ -150,10 +179,13 @@ CeLayout ce_layout(const slide_ce_cfg& c, int N, bool want_dh) {
     off += bytes;
     return at;
   };
-  L.zbuf = put((size_t)L.C * L.ldz * 4);
+  L.ppc = ce_parts(L.C);
+  // fp32 logits of one chunk: only the fp32 path stores them (the bf16 path fuses the
+  // statistics and dz into the logits GEMM)
+  L.zbuf = c.dtype == SLIDE_F32 ? put((size_t)L.C * L.ldz * 4) : 0;
   L.dz = put((size_t)L.C * L.ldz * ts);
-  L.pm = put((size_t)L.nchunks * kRowSplits * N * 4);
-  L.ps = put((size_t)L.nchunks * kRowSplits * N * 4);
+  L.pm = put((size_t)L.nchunks * L.ppc * N * 4);
+  L.ps = put((size_t)L.nchunks * L.ppc * N * 4);
   L.zt = put((size_t)N * 4);
   L.lse = put((size_t)N * 4);
   L.lt = put((size_t)N * 4);
@@ -206,14 +238,37 @@ int ce_n_chunks(const slide_ce_cfg& c) { return ce_layout(c, 0, false).nchunks; 
 
 namespace {
 
-int ce_logits(const slide_ce_cfg& c, const CeBufs& b, const void* h, const void* w, int N, int ci,
-              hipStream_t st) {
-  // z^T[v][t] = sum_k W[c0+v][k] h[t][k]
+// z^T[v][t] = sum_k W[c0+v][k] h[t][k] for the rows of chunk ci. fp32: stored in the chunk
+// buffer. bf16: the epilogue `special` consumes it (statistics or dz) and nothing is stored.
+int ce_logits(const slide_ce_cfg& c, const CeBufs& b, const void* h, const void* w,
+              const int32_t* tgt, int N, int ci, int special, hipStream_t st) {
   const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
   const size_t ts = (size_t)dtype_size(c.dtype);
+  const bool fused = c.dtype == SLIDE_BF16;
   GemmArgs g{rows, N, c.hidden, (const char*)w + (size_t)c0 * c.hidden * ts, c.hidden, true, h,
              c.hidden, true, b.zbuf, b.L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, c.dtype,
-             "ce_logits_gemm", SITE_CE_LOGITS};
+             "ce_logits_gemm", SITE_GENERIC};
+  if (fused) {
+    g.special = special;
+    g.tgt = tgt;
+    g.c0 = c0;
+    g.V = c.vocab;
+    if (special == SPECIAL_CE_STATS) {
+      g.site = SITE_CE_STATS;
+      g.name = "ce_stats_gemm";
+      g.C = b.pm;                 // not written; any non-null pointer
+      g.pm = b.pm + (size_t)ci * b.L.ppc * N;
+      g.ps = b.ps + (size_t)ci * b.L.ppc * N;
+      g.zt = b.zt;
+    } else {
+      g.site = SITE_CE_DZ;
+      g.name = "ce_dz_gemm";
+      g.C = b.dz;
+      g.c_dtype = c.dtype;
+      g.lse = b.lse;
+      g.inv_nv = b.inv_nv;
+    }
+  }
   return gemm_launch(g, st);
 }
 
@@ -226,11 +281,13 @@ int ce_stats(const slide_ce_cfg& c, const void* h, const void* w, const int32_t*
   if (N == 0) return SLIDE_OK;
   const CeBufs b = ce_bufs(c, N, ws);
   const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
-  SLIDE_TRY(ce_logits(c, b, h, w, N, ci, st));
+  SLIDE_TRY(ce_logits(c, b, h, w, tgt, N, ci, SPECIAL_CE_STATS, st));
+  if (c.dtype == SLIDE_BF16) return SLIDE_OK;   // the partials came out of the GEMM
   ProfScope ps_("ce_stats", st);
-  hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), kRowSplits), dim3(256), 0, st, b.zbuf,
-                     rows, N, b.L.ldz, c0, tgt, b.pm + (size_t)ci * kRowSplits * N,
-                     b.ps + (size_t)ci * kRowSplits * N, b.zt, kRowSplits);
+  const int parts = ce_parts(rows);
+  hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), parts), dim3(256), 0, st, b.zbuf,
+                     rows, N, b.L.ldz, c0, tgt, b.pm + (size_t)ci * b.L.ppc * N,
+                     b.ps + (size_t)ci * b.L.ppc * N, b.zt, parts);
   return check_launch("ce_stats");
 }
 
@@ -243,8 +300,8 @@ int ce_loss(const slide_ce_cfg& c, const int32_t* tgt, int N, float* loss, void*
   }
   const CeBufs b = ce_bufs(c, N, ws);
   ProfScope ps_("ce_lse", st);
-  hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 256)), dim3(256), 0, st, b.pm, b.ps,
-                     b.L.nchunks * kRowSplits, N, tgt, c.vocab, b.zt, b.lse, b.lt);
+  hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 32)), dim3(256), 0, st, b.pm, b.ps,
+                     b.L.nchunks, b.L.C, b.L.ppc, N, tgt, c.vocab, b.zt, b.lse, b.lt);
   hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, b.lt, tgt, N, c.vocab, loss,
                      b.inv_nv);
   return check_launch("ce_lse");
@@ -267,16 +324,12 @@ int ce_grad(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* 
     }
     return check_launch("lmhead_ce(empty)");
   }
-  SLIDE_TRY(ce_logits(c, b, h, w, N, ci, st));
-  {
+  SLIDE_TRY(ce_logits(c, b, h, w, tgt, N, ci, SPECIAL_CE_DZ, st));
+  if (dt == SLIDE_F32) {   // the bf16 path computed dz in the logits GEMM's epilogue
     ProfScope ps_("ce_dz", st);
     const size_t n = (size_t)rows * b.L.ldz;
-    if (dt == SLIDE_BF16)
-      hipLaunchKernelGGL(ce_dz_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,
-                         (bf16_t*)b.dz, rows, N, b.L.ldz, c0, V, tgt, b.lse, b.inv_nv);
-    else
-      hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,
-                         (float*)b.dz, rows, N, b.L.ldz, c0, V, tgt, b.lse, b.inv_nv);
+    hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,
+                       (float*)b.dz, rows, N, b.L.ldz, c0, V, tgt, b.lse, b.inv_nv);
     SLIDE_TRY(check_launch("ce_dz"));
   }
   const void* wc = (const char*)w + (size_t)c0 * H * ts;

@@ -4,7 +4,17 @@
 
 namespace slide {
 
-enum { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_ACCUM_F32 = 3 };
+enum { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_ACCUM_F32 = 3,
+       EPI_CE_STATS = 4, EPI_CE_DZ = 5 };
+
+// Fused epilogues of the LM-head cross-entropy's logits GEMM (C = z^T, [vocab rows][tokens]):
+//   CE_STATS: per token column, the max and sum of exp(z - max) over each block of kCeRowsPerPart
+//     vocabulary rows, into pm / ps[(row / kCeRowsPerPart) * N + t]; the target logit into zt[t].
+//     z itself is not stored.
+//   CE_DZ: dz = (exp(z - lse_t) - [c0 + row == y_t]) * inv_nv for valid targets, else 0, stored
+//     in C (the storage type) for columns up to ldc (columns past N get 0).
+constexpr int kCeRowsPerPart = 64;
+enum { SPECIAL_NONE = 0, SPECIAL_CE_STATS = 1, SPECIAL_CE_DZ = 2 };
 
 // Call sites of the layer and the LM head. Each site with its usual layout gets its own kernel
 // symbol (the site is a template tag with no effect on the code), so that profilers report the
@@ -12,7 +22,7 @@ enum { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_ACCUM_F32 = 3 }
 enum GemmSite {
   SITE_GENERIC = 0, SITE_QKV, SITE_O, SITE_GATE_UP, SITE_DOWN,
   SITE_DOWN_DX, SITE_DOWN_DW, SITE_GATE_UP_DX, SITE_GATE_UP_DW, SITE_O_DX, SITE_O_DW,
-  SITE_QKV_DX, SITE_QKV_DW, SITE_CE_LOGITS, SITE_CE_DH, SITE_CE_DW
+  SITE_QKV_DX, SITE_QKV_DW, SITE_CE_STATS, SITE_CE_DZ, SITE_CE_DH, SITE_CE_DW
 };
 
 // C[M,N] = alpha * A(m,k) B(k,n) (+ R) (or C += ... when accumulate); see slide_gemm in slide.h.
@@ -34,6 +44,16 @@ struct GemmArgs {
   int dtype;
   const char* name;  // kernel-timer label
   int site;          // GemmSite (0 = generic)
+  // cross-entropy epilogues (special != SPECIAL_NONE; A and B K-major)
+  int special;
+  const int32_t* tgt;    // [N] targets (vocabulary index, < 0 ignored)
+  const float* lse;      // [N] (CE_DZ)
+  const float* inv_nv;   // 1 / number of valid targets (CE_DZ)
+  float* pm;             // [parts][N] (CE_STATS)
+  float* ps;
+  float* zt;             // [N] target logit (CE_STATS)
+  int c0;                // first vocabulary row of this chunk
+  int V;                 // vocabulary size
 };
 
 int gemm_check(const GemmArgs& g);

@@ -33,6 +33,109 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Epilogue of a wave tile of MI x NJ 32x32 MFMA blocks whose top-left element is (rw0, cw0):
+// acc[i][j][e] is C(row, col) with col = cw0 + 32 j + lane%32,
+// row = rw0 + 32 i + (e/4)*8 + (lane/32)*4 + e%4.
+template <int EPI, int MI, int NJ>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)[MI][NJ],
+                                              int rw0, int cw0, int lane) {
+  if constexpr (EPI == EPI_CE_STATS) {
+    static_assert((MI * 32) % kCeRowsPerPart == 0, "whole row blocks per wave");
+    constexpr int PARTS = MI * 32 / kCeRowsPerPart;
+    const int hl = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = cw0 + j * 32 + (lane & 31);
+      const bool cok = col < g.N;
+      const int y = cok ? g.tgt[col] - g.c0 : -1;
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) {
+        // rows of part p: blocks i in [p * MI / PARTS, (p + 1) * MI / PARTS)
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = p * MI / PARTS; i < (p + 1) * MI / PARTS; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = rw0 + i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+            const float v = acc[i][j][e] * g.alpha;
+            if (row < g.M) m = fmaxf(m, v);
+            if (row == y && row < g.M) g.zt[col] = v;
+          }
+        float s = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int i = p * MI / PARTS; i < (p + 1) * MI / PARTS; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = rw0 + i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+              if (row < g.M) s += __expf(acc[i][j][e] * g.alpha - m);
+            }
+        }
+        // combine with the other half of the rows (lane +- 32)
+        const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64);
+        const float mm = fmaxf(m, m2);
+        float ss = 0.f;
+        if (mm != -INFINITY) ss = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+        if (hl == 0 && cok) {
+          const size_t at = (size_t)((rw0 + p * kCeRowsPerPart) / kCeRowsPerPart) * g.N + col;
+          g.pm[at] = mm;
+          g.ps[at] = ss;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = cw0 + j * 32 + (lane & 31);
+        if constexpr (EPI == EPI_CE_DZ) {
+          if (col >= g.ldc) continue;
+        } else {
+          if (col >= g.N) continue;
+        }
+        float dzs = 0.f, lse_t = 0.f;
+        int y = -1;
+        if constexpr (EPI == EPI_CE_DZ) {
+          if (col < g.N) {
+            const int yt = g.tgt[col];
+            if (yt >= 0 && yt < g.V) {
+              y = yt;
+              lse_t = g.lse[col];
+              dzs = *g.inv_nv;
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rw0 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          if (row >= g.M) continue;
+          float v = acc[i][j][e] * g.alpha;
+          if constexpr (EPI == EPI_STORE_BF16) {
+            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+          } else if constexpr (EPI == EPI_STORE_F32) {
+            ((float*)g.C)[(size_t)row * g.ldc + col] = v;
+          } else if constexpr (EPI == EPI_RESID) {
+            v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
+            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+          } else if constexpr (EPI == EPI_ACCUM_F32) {
+            float* c = (float*)g.C + (size_t)row * g.ldc + col;
+            *c = *c + v;
+          } else {  // EPI_CE_DZ
+            float d = 0.f;
+            if (y >= 0) {
+              d = __expf(v - lse_t);
+              if (g.c0 + row == y) d -= 1.f;
+              d *= dzs;
+            }
+            if (g.c_dtype == SLIDE_BF16) ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(d);
+            else ((float*)g.C)[(size_t)row * g.ldc + col] = d;
+          }
+        }
+      }
+  }
+}
+
 // Operand staging. Threads [0, NT/2) stage the A tile and threads [NT/2, NT) the B tile, each
 // through the same 8 x 16-byte registers: a K-major operand (memory row = M or N index) as 8
 // chunks per thread (8 consecutive threads cover one 128-byte row segment), an outer-K operand
@@ -171,31 +274,7 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][e] is C(row, col) with col = lane%32, row = (e/4)*8 + (lane/32)*4 + e%4
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + wn * TL::WTN + j * 32 + (lane & 31);
-      if (col >= g.N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * TL::WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row >= g.M) continue;
-        float v = acc[i][j][e] * g.alpha;
-        if constexpr (EPI == EPI_STORE_BF16) {
-          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          ((float*)g.C)[(size_t)row * g.ldc + col] = v;
-        } else if constexpr (EPI == EPI_RESID) {
-          v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
-          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
-        } else {  // EPI_ACCUM_F32
-          float* c = (float*)g.C + (size_t)row * g.ldc + col;
-          *c = *c + v;
-        }
-      }
-    }
+  gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, lane);
 }
 
 // ------------------------------------------------------------------ pipelined bf16 GEMM
@@ -498,30 +577,7 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
     }
   }
 
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-      if (col >= g.N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row >= g.M) continue;
-        float v = acc[i][j][e] * g.alpha;
-        if constexpr (EPI == EPI_STORE_BF16) {
-          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          ((float*)g.C)[(size_t)row * g.ldc + col] = v;
-        } else if constexpr (EPI == EPI_RESID) {
-          v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
-          ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
-        } else {
-          float* c = (float*)g.C + (size_t)row * g.ldc + col;
-          *c = *c + v;
-        }
-      }
-    }
+  gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT GEMM
@@ -644,7 +700,8 @@ void launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
   SLIDE_SITE(SITE_O_DW, false, false, EPI_STORE_BF16)
   SLIDE_SITE(SITE_QKV_DX, true, false, EPI_STORE_BF16)
   SLIDE_SITE(SITE_QKV_DW, false, false, EPI_STORE_BF16)
-  SLIDE_SITE(SITE_CE_LOGITS, true, true, EPI_STORE_F32)
+  SLIDE_SITE(SITE_CE_STATS, true, true, EPI_CE_STATS)
+  SLIDE_SITE(SITE_CE_DZ, true, true, EPI_CE_DZ)
   SLIDE_SITE(SITE_CE_DH, false, false, EPI_ACCUM_F32)
   SLIDE_SITE(SITE_CE_DW, true, false, EPI_STORE_BF16)
 #undef SLIDE_SITE
@@ -657,6 +714,8 @@ void launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
 }  // namespace
 
 int gemm_epilogue_of(const GemmArgs& g) {
+  if (g.special == SPECIAL_CE_STATS) return EPI_CE_STATS;
+  if (g.special == SPECIAL_CE_DZ) return EPI_CE_DZ;
   if (g.accumulate) return EPI_ACCUM_F32;
   if (g.R) return EPI_RESID;
   return g.c_dtype == SLIDE_F32 ? EPI_STORE_F32 : EPI_STORE_BF16;
@@ -692,6 +751,11 @@ int gemm_check(const GemmArgs& g) {
 
 int gemm_launch(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return SLIDE_OK;
+  // the cross-entropy epilogues exist for the logits GEMM's own instantiation only
+  SLIDE_REQUIRE(g.special == SPECIAL_NONE ||
+                    (g.dtype == SLIDE_BF16 && g.a_kmajor && g.b_kmajor &&
+                     g.site == (g.special == SPECIAL_CE_STATS ? SITE_CE_STATS : SITE_CE_DZ)),
+                SLIDE_E_ARG, "gemm: cross-entropy epilogue with another site or layout");
   ProfScope ps(g.name ? g.name : "gemm", st);
   const int epi = gemm_epilogue_of(g);
   if (g.dtype == SLIDE_BF16) {
