@@ -291,8 +291,10 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
 // The swizzles keep both the 16-byte fragment reads and the transpose reads free of bank
 // conflicts (checked for 32 and 64 banks). Out-of-range lanes load from a zero page. MFMA
 // fragments are double buffered in registers: the LDS reads of the next 16-k step are in flight
-// while the MFMAs of the current one run, and the one barrier per stage sits where the last
-// step's MFMAs can cover it. Every layout (forward, dX, dW) runs this kernel.
+// while the MFMAs of the current one run, and are interleaved with them instruction by
+// instruction; the one barrier per stage sits where the last step's MFMAs can cover it. Each
+// lane's load addresses are computed once and advanced per stage. Every layout (forward, dX,
+// dW) runs this kernel.
 namespace pipe {
 
 constexpr int BM = 256, BN = 256;
@@ -569,10 +571,17 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
         if (kt + NS < nk) issue_stage(kt + NS);
         load_frags(cur ^ 1, kt + 1, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);   // favour the wave issuing MFMAs on its SIMD
       mfmas(cur);
-      __builtin_amdgcn_s_setprio(0);
+      // Interleave this step's MFMAs with the other work (the next set's LDS reads, a stage's
+      // direct-to-LDS loads, address arithmetic): each MFMA is followed by one memory
+      // instruction and up to five ALU instructions, which issue while it runs.
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100 | 0x020, 1, 0);   // LDS read, VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, 5, 0);   // VALU, SALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
