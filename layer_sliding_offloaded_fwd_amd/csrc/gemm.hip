@@ -460,6 +460,12 @@ __device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
                : "memory");
 }
 
+// compile-time selector of the steady-state or the checked stage body
+template <bool V>
+struct StageTag {
+  static constexpr bool value = V;
+};
+
 }  // namespace pipe
 
 template <class PC, bool AK, bool BKM, int EPI, int SITE>
@@ -555,14 +561,26 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   // Steps of 16 k alternate between the two fragment sets. The last step of a stage passes the
   // barrier after which stage kt's buffer is refilled and stage kt + 1's first fragments are
   // read, then runs its MFMAs while those reads are in flight. sched_barrier(0) keeps the
-  // compiler from moving MFMAs across these points.
-  for (int kt = 0; kt < nk; ++kt) {
+  // compiler from moving MFMAs across steps.
+  //
+  // A steady-state stage (stage kt + NS is a full stage, issued in this iteration) is
+  // straight-line code: its last step's MFMAs interleave with the barrier, the stage loads and
+  // the next fragment reads. The last NS stages take the same steps with runtime checks.
+  auto run_stage = [&](int kt, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int cur = kk & 1;
       wait_frags(cur);
       if (kk + 1 < KS) {
         load_frags(cur ^ 1, kt, kk + 1);
+      } else if constexpr (STEADY) {
+        // stages kt + 2 .. kt + NS - 1 stay in flight
+        wait_vm<(NS - 2) * PC::LPS>();
+        asm volatile("s_barrier" ::: "memory");
+        sta.issue_next(stage_a(kt % NS));
+        stb.issue_next(stage_b(kt % NS));
+        load_frags(cur ^ 1, kt + 1, 0);
       } else if (kt + 1 < nk) {
         wait_stage(kt + 1, kt + NS - 1);
         // Plain barrier: the explicit vmcnt wait covers this wave's loads of stage kt + 1, and
@@ -573,10 +591,23 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
       }
       mfmas(cur);
       // Interleave this step's MFMAs with the other work (the next set's LDS reads, a stage's
-      // direct-to-LDS loads, address arithmetic): each MFMA is followed by one memory
-      // instruction and up to five ALU instructions, which issue while it runs.
+      // direct-to-LDS loads, address arithmetic): each MFMA is followed by one or two memory
+      // instructions and a few ALU instructions, which issue while it runs.
+      if constexpr (STEADY) {
+        if (kk + 1 == KS) {
 #pragma unroll
-      for (int q = 0; q < 6; ++q) {
+          for (int q = 0; q < MI * NJ - 1; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100 | 0x020, 2, 0);   // LDS read, VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, 4, 0);   // VALU, SALU
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < MI * NJ - 2; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100 | 0x020, 1, 0);   // LDS read, VMEM read
         __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, 5, 0);   // VALU, SALU
@@ -584,7 +615,12 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  // iterations whose stage kt + NS is a full stage
+  const int n_steady = max(0, g.K / BK - NS);
+  int kt = 0;
+  for (; kt < n_steady; ++kt) run_stage(kt, StageTag<true>{});
+  for (; kt < nk; ++kt) run_stage(kt, StageTag<false>{});
 
   gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
