@@ -460,6 +460,79 @@ __device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
                : "memory");
 }
 
+// bf16 output (optionally plus a bf16 residual) through LDS. The accumulators of a 32 x 32 MFMA
+// block give each lane one column, so direct stores are 2 bytes per lane. Instead, in pass h the
+// waves of wave row h write alpha * acc as fp32 into LDS (WTM x BN floats; the 32-column half is
+// flipped for rows with bit 2 set, so the two half-waves of a write hit different banks), and
+// then every thread reads 4 consecutive values of a row and stores them as 8 bytes: one wave
+// instruction covers a whole 256-column row. Ragged or unaligned edges fall back to per-element
+// stores.
+template <int EPI, class PC>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
+                                                f32x16_t (&acc)[PC::MI][PC::NJ], float* lds,
+                                                int m0, int n0, int wm, int wn, int lane) {
+  constexpr int WTM = PC::WTM, WTN = PC::WTN, MI = PC::MI, NJ = PC::NJ, NT = PC::NT;
+  constexpr int CPR = BN / 4;                 // 4-column chunks per row
+  constexpr int PER = WTM * CPR / NT;         // chunks per thread and pass
+  static_assert(WTM * CPR % NT == 0, "whole chunks per thread");
+  static_assert(WTM * BN * 4 <= PC::NS * 2 * PC::SE * 2, "one wave row of fp32 fits the stages");
+  const int hl = lane >> 5;
+  const bool vec = (g.ldc % 4 == 0) && ((uintptr_t)g.C % 8 == 0) &&
+                   (EPI != EPI_RESID || ((g.ldr % 4 == 0) && ((uintptr_t)g.R % 8 == 0)));
+  bf16_t* C = (bf16_t*)g.C;
+  const bf16_t* R = (const bf16_t*)g.R;
+#pragma unroll
+  for (int h = 0; h < PC::WGM; ++h) {
+    __syncthreads();   // the main loop's (or the previous pass's) LDS reads are done
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+            const int c = (wn * WTN + j * 32 + (lane & 31)) ^ (hl << 5);
+            lds[r * BN + c] = acc[i][j][e] * g.alpha;
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int k = threadIdx.x + NT * q;
+      const int r = k / CPR, cc = k % CPR;
+      const int gr = m0 + h * WTM + r, gc = n0 + cc * 4;
+      if (gr >= g.M || gc >= g.N) continue;
+      const float4 v = *(const float4*)(lds + r * BN + ((cc * 4) ^ (((r >> 2) & 1) << 5)));
+      float o[4] = {v.x, v.y, v.z, v.w};
+      const size_t at = (size_t)gr * g.ldc + gc;
+      if (vec && gc + 3 < g.N) {
+        if constexpr (EPI == EPI_RESID) {
+          const uint2 rr = *(const uint2*)(R + (size_t)gr * g.ldr + gc);
+          o[0] += __uint_as_float(rr.x << 16);
+          o[1] += __uint_as_float(rr.x & 0xffff0000u);
+          o[2] += __uint_as_float(rr.y << 16);
+          o[3] += __uint_as_float(rr.y & 0xffff0000u);
+        }
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[0])) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[1])) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[2])) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[3])) << 16);
+        *(uint2*)(C + at) = w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (gc + t >= g.N) break;
+          float x = o[t];
+          if constexpr (EPI == EPI_RESID) x += bf2f(R[(size_t)gr * g.ldr + gc + t]);
+          C[at + t] = f2bf(x);
+        }
+      }
+    }
+  }
+}
+
 // compile-time selector of the steady-state or the checked stage body
 template <bool V>
 struct StageTag {
@@ -622,7 +695,10 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   for (; kt < n_steady; ++kt) run_stage(kt, StageTag<true>{});
   for (; kt < nk; ++kt) run_stage(kt, StageTag<false>{});
 
-  gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_RESID)
+    staged_epilogue<EPI, PC>(g, acc, (float*)smem, m0, n0, wm, wn, lane);
+  else
+    gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT GEMM
