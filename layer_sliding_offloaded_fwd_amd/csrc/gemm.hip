@@ -460,13 +460,15 @@ __device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
                : "memory");
 }
 
-// bf16 output (optionally plus a bf16 residual) through LDS. The accumulators of a 32 x 32 MFMA
-// block give each lane one column, so direct stores are 2 bytes per lane. Instead, in pass h the
-// waves of wave row h write alpha * acc as fp32 into LDS (WTM x BN floats; the 32-column half is
-// flipped for rows with bit 2 set, so the two half-waves of a write hit different banks), and
-// then every thread reads 4 consecutive values of a row and stores them as 8 bytes: one wave
-// instruction covers a whole 256-column row. Ragged or unaligned edges fall back to per-element
-// stores.
+// Stores through LDS. The accumulators of a 32 x 32 MFMA block give each lane one column, so
+// direct stores are one element per lane. Instead, in pass h the waves of wave row h write
+// alpha * acc as fp32 into LDS (WTM x BN floats; the 32-column half is flipped for rows with bit 2
+// set, so the two half-waves of a write hit different banks), and then every thread reads 4
+// consecutive values of a row and stores them with one vector access (8 bytes of bf16, 16 of
+// fp32): one wave instruction covers a whole 256-column row. The residual (bf16) and the fp32
+// accumulation target are read the same way. Ragged or unaligned edges fall back to per-element
+// accesses. The cross-entropy dz (softmax - onehot of a vocabulary chunk, per token column) is
+// formed from the same staged values.
 template <int EPI, class PC>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
                                                 f32x16_t (&acc)[PC::MI][PC::NJ], float* lds,
@@ -474,13 +476,32 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
   constexpr int WTM = PC::WTM, WTN = PC::WTN, MI = PC::MI, NJ = PC::NJ, NT = PC::NT;
   constexpr int CPR = BN / 4;                 // 4-column chunks per row
   constexpr int PER = WTM * CPR / NT;         // chunks per thread and pass
+  constexpr bool F32 = EPI == EPI_STORE_F32 || EPI == EPI_ACCUM_F32;
   static_assert(WTM * CPR % NT == 0, "whole chunks per thread");
   static_assert(WTM * BN * 4 <= PC::NS * 2 * PC::SE * 2, "one wave row of fp32 fits the stages");
   const int hl = lane >> 5;
-  const bool vec = (g.ldc % 4 == 0) && ((uintptr_t)g.C % 8 == 0) &&
+  const bool c_f32 = F32 || (EPI == EPI_CE_DZ && g.c_dtype == SLIDE_F32);
+  const bool vec = (g.ldc % 4 == 0) && ((uintptr_t)g.C % (c_f32 ? 16 : 8) == 0) &&
                    (EPI != EPI_RESID || ((g.ldr % 4 == 0) && ((uintptr_t)g.R % 8 == 0)));
-  bf16_t* C = (bf16_t*)g.C;
-  const bf16_t* R = (const bf16_t*)g.R;
+  // A thread's chunks all lie in the same 4 columns (NT is a multiple of the chunks per row):
+  // for dz, their targets and log-sum-exps are read once.
+  static_assert(NT % CPR == 0, "fixed chunk column per thread");
+  int dz_y[4] = {-1, -1, -1, -1};
+  float dz_lse[4] = {0.f, 0.f, 0.f, 0.f}, inv_nv = 0.f;
+  if constexpr (EPI == EPI_CE_DZ) {
+    inv_nv = *g.inv_nv;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = n0 + (threadIdx.x % CPR) * 4 + t;
+      if (col < g.N) {
+        const int yt = g.tgt[col];
+        if (yt >= 0 && yt < g.V) {
+          dz_y[t] = yt;
+          dz_lse[t] = g.lse[col];
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int h = 0; h < PC::WGM; ++h) {
     __syncthreads();   // the main loop's (or the previous pass's) LDS reads are done
@@ -502,31 +523,81 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
       const int k = threadIdx.x + NT * q;
       const int r = k / CPR, cc = k % CPR;
       const int gr = m0 + h * WTM + r, gc = n0 + cc * 4;
-      if (gr >= g.M || gc >= g.N) continue;
+      // the cross-entropy dz also writes zeros into the padding columns [N, ldc)
+      if (gr >= g.M || gc >= (EPI == EPI_CE_DZ ? g.ldc : g.N)) continue;
       const float4 v = *(const float4*)(lds + r * BN + ((cc * 4) ^ (((r >> 2) & 1) << 5)));
       float o[4] = {v.x, v.y, v.z, v.w};
       const size_t at = (size_t)gr * g.ldc + gc;
-      if (vec && gc + 3 < g.N) {
-        if constexpr (EPI == EPI_RESID) {
-          const uint2 rr = *(const uint2*)(R + (size_t)gr * g.ldr + gc);
-          o[0] += __uint_as_float(rr.x << 16);
-          o[1] += __uint_as_float(rr.x & 0xffff0000u);
-          o[2] += __uint_as_float(rr.y << 16);
-          o[3] += __uint_as_float(rr.y & 0xffff0000u);
+      if constexpr (EPI == EPI_CE_DZ) {
+        // dz = (softmax - onehot) / N_valid of vocabulary row c0 + gr for tokens gc .. gc + 3;
+        // 0 for ignored targets and padding columns
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float d = 0.f;
+          if (dz_y[t] >= 0) {
+            d = __expf(o[t] - dz_lse[t]);
+            if (g.c0 + gr == dz_y[t]) d -= 1.f;
+            d *= inv_nv;
+          }
+          o[t] = d;
         }
-        uint2 w;
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[0])) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[1])) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[2])) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, f2bf(o[3])) << 16);
-        *(uint2*)(C + at) = w;
+        if (vec && gc + 3 < g.ldc) {
+          if (g.c_dtype == SLIDE_BF16) {
+            uint2 w;
+            w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+            w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            *(uint2*)((bf16_t*)g.C + at) = w;
+          } else {
+            *(float4*)((float*)g.C + at) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (gc + t >= g.ldc) break;
+            if (g.c_dtype == SLIDE_BF16) ((bf16_t*)g.C)[at + t] = f2bf(o[t]);
+            else ((float*)g.C)[at + t] = o[t];
+          }
+        }
+        continue;
+      }
+      if (vec && gc + 3 < g.N) {
+        if constexpr (F32) {
+          float4* c = (float4*)((float*)g.C + at);
+          if constexpr (EPI == EPI_ACCUM_F32) {
+            const float4 old = *c;
+            o[0] += old.x;
+            o[1] += old.y;
+            o[2] += old.z;
+            o[3] += old.w;
+          }
+          *c = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          if constexpr (EPI == EPI_RESID) {
+            const uint2 rr = *(const uint2*)((const bf16_t*)g.R + (size_t)gr * g.ldr + gc);
+            o[0] += __uint_as_float(rr.x << 16);
+            o[1] += __uint_as_float(rr.x & 0xffff0000u);
+            o[2] += __uint_as_float(rr.y << 16);
+            o[3] += __uint_as_float(rr.y & 0xffff0000u);
+          }
+          uint2 w;
+          w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+          w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+          *(uint2*)((bf16_t*)g.C + at) = w;
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (gc + t >= g.N) break;
           float x = o[t];
-          if constexpr (EPI == EPI_RESID) x += bf2f(R[(size_t)gr * g.ldr + gc + t]);
-          C[at + t] = f2bf(x);
+          if constexpr (EPI == EPI_STORE_F32) {
+            ((float*)g.C)[at + t] = x;
+          } else if constexpr (EPI == EPI_ACCUM_F32) {
+            ((float*)g.C)[at + t] += x;
+          } else {
+            if constexpr (EPI == EPI_RESID)
+              x += bf2f(((const bf16_t*)g.R)[(size_t)gr * g.ldr + gc + t]);
+            ((bf16_t*)g.C)[at + t] = f2bf(x);
+          }
         }
       }
     }
@@ -695,7 +766,7 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   for (; kt < n_steady; ++kt) run_stage(kt, StageTag<true>{});
   for (; kt < nk; ++kt) run_stage(kt, StageTag<false>{});
 
-  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_RESID)
+  if constexpr (EPI != EPI_CE_STATS)
     staged_epilogue<EPI, PC>(g, acc, (float*)smem, m0, n0, wm, wn, lane);
   else
     gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);

@@ -28,7 +28,12 @@ def _round(a, dtype):
 GEMM_SHAPES = [
     (328, 200, 136),      # small-tile path: 3 x 2 tiles of 128 with ragged edges, 3 k-tiles
     (2088, 4120, 136),    # large-tile path: 9 x 17 tiles of 256 with ragged edges
+    (2090, 4121, 136),    # large-tile path, odd N and ldc: per-element stores at every row
 ]
+
+
+def _r8(v):
+    return (v + 7) // 8 * 8
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -43,10 +48,11 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     B = _round(rng.standard_normal((K, N)), dtype)
     R = _round(rng.standard_normal((M, N)), dtype)
     ref = A @ B
-    a_mem = A if ak else A.T.copy()           # ak: [M][K] else [K][M]
-    b_mem = B.T.copy() if bk else B           # bk: [N][K] else [K][N]
-    lda = K if ak else M
-    ldb = K if bk else N
+    # ak: [M][K] else [K][M]; bk: [N][K] else [K][N]; an outer-K operand's rows are padded to 8
+    lda = K if ak else _r8(M)
+    ldb = K if bk else _r8(N)
+    a_mem = A if ak else np.pad(A.T, ((0, 0), (0, lda - M)))
+    b_mem = B.T.copy() if bk else np.pad(B, ((0, 0), (0, ldb - N)))
     dA, dB = dev(a_mem, dtype), dev(b_mem, dtype)
     code = sl.dtype_code(dtype)
     C = empty((M, N), dtype)
@@ -59,9 +65,13 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     C3 = torch.full((M, N), 1.0, dtype=torch.float32, device=DEV)
     sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C3, N, sl.SLIDE_F32, accumulate=True,
                   dtype=code, stream=stream())
+    C4 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C4, N, sl.SLIDE_F32, dtype=code,
+                  stream=stream())
     torch.cuda.synchronize()
     assert_close(host(C2), 0.5 * ref + R, dtype, "C = R + 0.5 A B", tol=1e-2 if dtype == "bf16" else 1e-5)
     assert_close(host(C3), 1.0 + ref, "f32", "C += A B (fp32 accumulate)", tol=1e-5)
+    assert_close(host(C4), ref, "f32", "C = A B (fp32 output)", tol=1e-5)
 
 
 @pytest.mark.parametrize("dtype,H", [("bf16", 4096), ("f32", 256), ("bf16", 264)])
