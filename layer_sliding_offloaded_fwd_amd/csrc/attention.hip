@@ -20,9 +20,10 @@
 //    exchange with the lane 32 away. O^T += V^T P^T (and dQ^T += K^T dS^T) take P (dS) straight
 //    from the score accumulators as the B operand; the 16 keys an MFMA consumes are ordered the
 //    way the accumulator holds them, and the transpose reads fetch V^T (K^T) in that order.
-//  * dK/dV: 128 keys per workgroup, looping over the G query heads of the kv group and over the
-//    query blocks on or after the diagonal, so dK and dV are summed without atomics (the result
-//    is deterministic). dQ runs as its own kernel.
+//  * dK and dV: two kernels (one accumulator each, so each fits 256 registers), 128 keys per
+//    workgroup, looping over the G query heads of the kv group and over the query blocks on or
+//    after the diagonal, so dK and dV are summed without atomics (the result is deterministic).
+//    dQ runs as its own kernel.
 //  * D_i = rowsum(dO_i * O_i) is precomputed by a small kernel.
 // fp32 path (the small fp32 configuration): straightforward SIMT kernels, one thread per query
 // (forward, dQ) or per key (dK/dV).
@@ -441,13 +442,20 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <int D>
-__global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
-                                                       const bf16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse,
-                                                       const float* __restrict__ delta,
-                                                       bf16_t* __restrict__ dqkv, int S, int nq,
-                                                       int nkv, float scale) {
+// One kernel per output: MODE_DV accumulates dV = sum P^T dO, MODE_DK accumulates
+// dK = scale * sum dS^T Q with dS = P (dP - D). Each recomputes the scores it needs; split this
+// way a wave holds one 32 x d accumulator instead of two, and both stay within 256 registers
+// per lane, so two workgroups share a compute unit.
+constexpr int MODE_DV = 0, MODE_DK = 1;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
+                                                          const bf16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta,
+                                                          bf16_t* __restrict__ dqkv, int S, int nq,
+                                                          int nkv, float scale) {
+  constexpr bool DK = MODE == MODE_DK;
   constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
   __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
   __shared__ float sL[NSTAGE][64], sDl[NSTAGE][64];
@@ -467,20 +475,18 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
   const bf16_t* dobase = dout + (size_t)b * S * OS;
   const float sl2 = scale * kLog2e;
 
-  bf16x8_t kf[NKK], vf[NKK];
+  bf16x8_t kf[NKK], vf[DK ? NKK : 1];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     kf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + g) * D + kk * 16 + hf * 8) : zero8();
-    vf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + nkv + g) * D + kk * 16 + hf * 8) : zero8();
+    if constexpr (DK)
+      vf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + nkv + g) * D + kk * 16 + hf * 8) : zero8();
   }
-  f32x16_t dk[NDB], dv[NDB];
+  f32x16_t acc[NDB];   // dK or dV, transposed: [d][key]
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dk[db][e] = 0.f;
-      dv[db][e] = 0.f;
-    }
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
 
   // flattened (head of the group, query block on or after the diagonal) sequence
   const int qb0 = k0 / 64, nqblk = (S + 63) / 64, per_head = nqblk - qb0;
@@ -504,9 +510,8 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
     if (j < total) issue(j);
 
   for (int it = 0; it < total; ++it) {
-    const int hh = it / per_head, jb = qb0 + it % per_head, st = it % NSTAGE;
+    const int jb = qb0 + it % per_head, st = it % NSTAGE;
     const int q0 = jb * 64;
-    (void)hh;
     const int later = min(total - 1, it + NSTAGE - 2) - it;
     if (wave < 2) wait_stage<PER + 1>(later);  // waves 0 and 1 issue one extra load per stage
     else wait_stage<PER>(later);
@@ -517,8 +522,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
     const bf16_t* sO = tO(st);
 
     const bool need_mask = (q0 < wk0 + 31) || (q0 + 64 > S) || (wk0 + 32 > S);
-    // the 64 queries in two halves of 32, one after the other, so that only one half's score
-    // and dP accumulators are live (keeps the kernel within 256 registers)
+    // the 64 queries in two halves of 32
 #pragma unroll
     for (int qb2 = 0; qb2 < 2; ++qb2) {
       f32x16_t sacc, pacc;
@@ -531,8 +535,20 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
       for (int kk = 0; kk < NKK; ++kk) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc, 0, 0, 0);
+        if constexpr (DK)
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc, 0, 0, 0);
+      }
+      // dV += P^T dO (columns of dO), dK += dS^T Q (columns of Q), in two steps of 16 queries.
+      // The column reads do not depend on the scores: the first step's (both steps' for dV,
+      // which has the registers) are issued before the softmax so that it covers their latency.
+      const bf16_t* sT = DK ? sQ : sO;
+      bf16x8_t tf0[NDB], tf1[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) tf0[db] = t_read<D>(sT, db * 32, 2 * qb2, lane);
+      if constexpr (!DK) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) tf1[db] = t_read<D>(sT, db * 32, 2 * qb2 + 1, lane);
       }
       // element i is (query q0 + acc_key(qb2, i), this lane's key)
 #pragma unroll
@@ -543,46 +559,37 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const bf16_t* __restrict_
           const int qq = q0 + ql;
           if (key > qq || qq >= S) p = 0.f;
         }
-        sacc[i] = p;
-        pacc[i] = p * (pacc[i] - sDl[st][ql]);
+        if constexpr (DK) sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
+        else sacc[i] = p;                                           // P
+      }
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = sacc[j];
+      const bf16x8_t wf0 = pack8(w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = sacc[8 + j];
+      const bf16x8_t wf1 = pack8(w);
+      tr_wait(tf0);
+      if constexpr (DK) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) tf1[db] = t_read<D>(sT, db * 32, 2 * qb2 + 1, lane);
       }
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int ks = 2 * qb2 + kh;
-        float pv[8], sv[8];
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf0[db], wf0, acc[db], 0, 0, 0);
+      tr_wait(tf1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = sacc[8 * kh + j];
-          sv[j] = pacc[8 * kh + j];
-        }
-        const bf16x8_t pf = pack8(pv), sf = pack8(sv);
-        bf16x8_t ot[NDB], qt[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) ot[db] = t_read<D>(sO, db * 32, ks, lane);
-        tr_wait(ot);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[db], pf, dv[db], 0, 0, 0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) qt[db] = t_read<D>(sQ, db * 32, ks, lane);
-        tr_wait(qt);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db], sf, dk[db], 0, 0, 0);
-      }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf1[db], wf1, acc[db], 0, 0, 0);
     }
   }
   wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
   const int nv = min(32, S - wk0);
-  if (nv > 0) {
-    store_tile_t<D>(stage, dk, scale, dqkv + (size_t)b * S * QS + (nq + g) * D, QS, wk0, nv, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    store_tile_t<D>(stage, dv, 1.0f, dqkv + (size_t)b * S * QS + (nq + nkv + g) * D, QS, wk0, nv,
-                    lane);
-  }
+  if (nv > 0)
+    store_tile_t<D>(stage, acc, DK ? scale : 1.0f,
+                    dqkv + (size_t)b * S * QS + (nq + (DK ? 0 : nkv) + g) * D, QS, wk0, nv, lane);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT kernels
@@ -767,14 +774,23 @@ int attention_bwd(const void* qkv, const void* o, const float* lse, const void* 
     }
     SLIDE_TRY(check_launch("attn_bwd_dq"));
     {
-      ProfScope ps("attn_bwd_dkv", st);
+      ProfScope ps("attn_bwd_dv", st);
       dim3 grid((S + 127) / 128, nkv, B), block(256);
       if (d == 128)
-        hipLaunchKernelGGL(attn_dkv_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+        hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DV>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
       else
-        hipLaunchKernelGGL(attn_dkv_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+        hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DV>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
     }
-    return check_launch("attn_bwd_dkv");
+    SLIDE_TRY(check_launch("attn_bwd_dv"));
+    {
+      ProfScope ps("attn_bwd_dk", st);
+      dim3 grid((S + 127) / 128, nkv, B), block(256);
+      if (d == 128)
+        hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DK>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+      else
+        hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DK>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
+    }
+    return check_launch("attn_bwd_dk");
   }
   {
     ProfScope ps("attn_bwd_dq", st);
