@@ -842,7 +842,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+// Two 64-deep stages where an operand is K-major (its 128-byte rows swizzle conflict-free); when
+// both operands are read through transpose reads (the weight-gradient GEMMs), four 32-deep
+// stages, which keep more loads in flight.
 using PipeL = pipe::PCfg<512, 2, 2, 64>;
+using PipeT = pipe::PCfg<512, 2, 4, 32>;
+template <bool AK, bool BKM>
+struct PipeFor {
+  using type = PipeL;
+};
+template <>
+struct PipeFor<false, false> {
+  using type = PipeT;
+};
 
 // Large tiles when they alone give at least half a wave of workgroups per compute unit.
 inline bool use_large(const GemmArgs& g) {
@@ -854,8 +866,9 @@ template <bool AK, bool BKM, int EPI, int SITE>
 void launch_one(const GemmArgs& g, hipStream_t st) {
   if (use_large(g)) {
     const int tiles = ((g.M + pipe::BM - 1) / pipe::BM) * ((g.N + pipe::BN - 1) / pipe::BN);
-    hipLaunchKernelGGL((gemm_pipe_kernel<PipeL, AK, BKM, EPI, SITE>), dim3(tiles),
-                       dim3(PipeL::NT), 0, st, g);
+    using PC = typename PipeFor<AK, BKM>::type;
+    hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE>), dim3(tiles), dim3(PC::NT), 0,
+                       st, g);
   } else {
     const int tiles = ((g.M + TileS::BM - 1) / TileS::BM) * ((g.N + TileS::BN - 1) / TileS::BN);
     hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileS::NT),
