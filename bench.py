@@ -352,6 +352,9 @@ def run_step(w, args):
         if ana["t_update_total_ms"] else None,
         "loss_last_step": round(loss, 4),
         "ms_per_step_steady": round(steady_ms, 2),
+        "step_periods_ms": [round(float(x), 1) for x in periods],
+        "first_step_ms": round((t_ret[0] - t0) * 1e3, 1) if t_ret else None,
+        "drain_ms": round((t1 - t_ret[-1]) * 1e3, 1) if t_ret else None,
         "host_roofline": host,
         # the pages compare offloaded training with training whose state stays on the GPU; this
         # build has no such variant, so the comparison is against a lower bound of it: the
