@@ -307,22 +307,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
 
 // ------------------------------------------------------------------ D = rowsum(dO * O)
 template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  const uint4 u = *(const uint4*)p;
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// D_i = rowsum(dO_i * O_i): the (token, head) rows of o and dO are contiguous runs of D values;
+// D / 8 lanes per row, 8 values (one 16- or 32-byte load) per lane, then a shuffle tree.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
                                                          const T* __restrict__ dout,
                                                          float* __restrict__ delta, int B, int S,
-                                                         int nq, int D) {
-  // one 64-lane wave per (token, head) row
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= (size_t)B * S * nq) return;
-  const size_t t = row / nq;
-  const int h = (int)(row % nq);
-  const T* a = o + t * nq * D + (size_t)h * D;
-  const T* c = dout + t * nq * D + (size_t)h * D;
+                                                         int nq) {
+  constexpr int LPR = D / 8;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / LPR;
+  const int sub = (int)(gid % LPR);
+  const bool ok = row < (size_t)B * S * nq;
   float s = 0.f;
-  for (int i = lane; i < D; i += 64) s += Elem<T>::load(a + i) * Elem<T>::load(c + i);
-  s = warp_sum(s);
-  if (lane == 0) {
+  if (ok) {
+    float a[8], c[8];
+    load8<T>(o + row * D + sub * 8, a);
+    load8<T>(dout + row * D + sub * 8, c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += a[i] * c[i];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (ok && sub == 0) {
+    const size_t t = row / nq;
+    const int h = (int)(row % nq);
     const int b = (int)(t / S), sp = (int)(t % S);
     delta[((size_t)b * nq + h) * S + sp] = s;
   }
@@ -756,11 +783,15 @@ int attention_bwd(const void* qkv, const void* o, const float* lse, const void* 
   {
     ProfScope ps("attn_delta", st);
     const size_t rows = (size_t)B * S * nq;
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    if (dtype == SLIDE_BF16)
-      hipLaunchKernelGGL(attn_delta_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq, d);
+    dim3 grid((unsigned)((rows * (d / 8) + 255) / 256)), block(256);
+    if (dtype == SLIDE_BF16 && d == 128)
+      hipLaunchKernelGGL((attn_delta_kernel<bf16_t, 128>), grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq);
+    else if (dtype == SLIDE_BF16)
+      hipLaunchKernelGGL((attn_delta_kernel<bf16_t, 64>), grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq);
+    else if (d == 128)
+      hipLaunchKernelGGL((attn_delta_kernel<float, 128>), grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq);
     else
-      hipLaunchKernelGGL(attn_delta_kernel<float>, grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq, d);
+      hipLaunchKernelGGL((attn_delta_kernel<float, 64>), grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq);
   }
   SLIDE_TRY(check_launch("attn_delta"));
   if (dtype == SLIDE_BF16) {

@@ -135,14 +135,20 @@ __global__ __launch_bounds__(256) void rmsnorm_dw_partial_kernel(const T* __rest
   part[(size_t)blockIdx.y * H + j] = acc;
 }
 
+// Sum of nparts rows of H floats, per column: 64 columns per workgroup, the parts split over 4
+// slices (slice s takes parts s, s + 4, ...), combined in slice order (deterministic).
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, T* out,
                                                           int nparts, int H) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= H) return;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
   float acc = 0.f;
-  for (int p = 0; p < nparts; ++p) acc += part[(size_t)p * H + j];
-  Elem<T>::store(out + j, acc);
+  if (j < H)
+    for (int p = sl; p < nparts; p += 4) acc += part[(size_t)p * H + j];
+  red[sl][c] = acc;
+  __syncthreads();
+  if (sl == 0 && j < H) Elem<T>::store(out + j, ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
 // ---------------------------------------------------------------- RoPE
@@ -156,25 +162,35 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int S, int half, i
   sin_t[idx] = (float)sin(a);
 }
 
-// One thread per rotation pair (i, i + d/2) of one (token, head) of the q and k parts.
+// One thread per 8 consecutive rotation pairs (i .. i+7, i+d/2 .. i+d/2+7) of one (token, head)
+// of the q and k parts: 16-byte loads and stores of both halves.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(T* qkv, const float* __restrict__ cos_t,
                                                    const float* __restrict__ sin_t, int N, int S,
                                                    int heads, int d, int row_stride, float sgn) {
-  const int half = d >> 1;
+  const int half = d >> 1, groups = half >> 3;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)N * heads * half;
+  const size_t total = (size_t)N * heads * groups;
   if (idx >= total) return;
-  const int i = (int)(idx % half);
-  const size_t th = idx / half;
+  const int i0 = (int)(idx % groups) * 8;
+  const size_t th = idx / groups;
   const int h = (int)(th % heads);
   const int t = (int)(th / heads);
   const int s = t % S;
   T* p = qkv + (size_t)t * row_stride + (size_t)h * d;
-  const float c = cos_t[s * half + i], sn = sgn * sin_t[s * half + i];
-  const float x1 = Elem<T>::load(p + i), x2 = Elem<T>::load(p + i + half);
-  Elem<T>::store(p + i, x1 * c - x2 * sn);
-  Elem<T>::store(p + i + half, x2 * c + x1 * sn);
+  float x1[8], x2[8], c[8], sn[8], o1[8], o2[8];
+  V8<T>::load(p + i0, x1);
+  V8<T>::load(p + i0 + half, x2);
+  V8<float>::load(cos_t + (size_t)s * half + i0, c);
+  V8<float>::load(sin_t + (size_t)s * half + i0, sn);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float sk = sgn * sn[k];
+    o1[k] = x1[k] * c[k] - x2[k] * sk;
+    o2[k] = x2[k] * c[k] + x1[k] * sk;
+  }
+  V8<T>::store(p + i0, o1);
+  V8<T>::store(p + i0 + half, o2);
 }
 
 // ---------------------------------------------------------------- SwiGLU
@@ -358,7 +374,7 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
       hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<float>, g1, b1, 0, st, (const float*)dy,
                          (const float*)x, rstd, part, N, H, kRmsRowsPerPart);
   }
-  dim3 g2(blocks_for(H, 256)), b2(256);
+  dim3 g2(blocks_for(H, 64)), b2(256);
   if (dtype == SLIDE_BF16)
     hipLaunchKernelGGL(reduce_rows_kernel<bf16_t>, g2, b2, 0, st, part, (bf16_t*)dw,
                        std::max(parts, 1), H);
@@ -379,7 +395,7 @@ int rope_tables(float* cos_t, float* sin_t, int S, int d, float theta, hipStream
 int rope_apply(void* qkv, const float* cos_t, const float* sin_t, int B, int S, int nq, int nkv,
                int d, int inverse, int dtype, hipStream_t st) {
   const int N = B * S, heads = nq + nkv, stride = (nq + 2 * nkv) * d;
-  const size_t total = (size_t)N * heads * (d / 2);
+  const size_t total = (size_t)N * heads * (d / 16);   // threads: 8 pairs each (d % 16 == 0)
   if (total == 0) return SLIDE_OK;
   ProfScope ps(inverse ? "rope_bwd" : "rope_fwd", st);
   const float sgn = inverse ? -1.f : 1.f;
