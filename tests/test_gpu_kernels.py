@@ -74,9 +74,10 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     assert_close(host(C4), ref, "f32", "C = A B (fp32 output)", tol=1e-5)
 
 
-@pytest.mark.parametrize("dtype,H", [("bf16", 4096), ("f32", 256), ("bf16", 264)])
-def test_rmsnorm_fwd_bwd(dtype, H):
-    N = 37
+# N = 300 and 517: several 64-row partial sums of the weight gradient, the last one ragged
+@pytest.mark.parametrize("dtype,H,N", [("bf16", 4096, 37), ("f32", 256, 37), ("bf16", 264, 300),
+                                       ("f32", 200, 517)])
+def test_rmsnorm_fwd_bwd(dtype, H, N):
     print(f"rmsnorm {dtype} N={N} H={H}", flush=True)
     x = activations((N, H), dtype, 5).f64
     w = _round(1.0 + 0.1 * _rng(6).standard_normal(H), dtype)
