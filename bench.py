@@ -237,6 +237,9 @@ def host_roofline(w, threads, step_s):
     h2d = 2 * (2 * w.n_layers - w.ring_slots) * n + 2 * (2 * w.vocab * c.hidden + c.hidden)
     d2h = 2 * n_all
     bound_s = adam_bytes / bw
+    link = host_link(2 * n)
+    link_s = max(h2d / (link["h2d_both_gbs"] * 1e9), d2h / (link["d2h_both_gbs"] * 1e9))
+    link.update(step_bound_ms=round(link_s * 1e3, 1), frac=round(link_s / step_s, 4))
     return {"bound": "host_dram", "adamw_bytes": adam_bytes, "h2d_bytes": h2d, "d2h_bytes": d2h,
             "adamw_alone_gbs": round(bw / 1e9, 1),
             "step_bound_ms": round(bound_s * 1e3, 1),
@@ -245,7 +248,43 @@ def host_roofline(w, threads, step_s):
             "host_dram_gbs": round((adam_bytes + h2d + d2h) / step_s / 1e9, 1),
             "h2d_link_gbs": round(h2d / step_s / 1e9, 1),
             "d2h_link_gbs": round(d2h / step_s / 1e9, 1),
+            "link": link,
             "note": "bound counts the AdamW bytes only; the PCIe copies load the same DRAM"}
+
+
+def host_link(nbytes, reps=3):
+    """Host-link rates of the slot-ring copies, measured alone: one layer's bf16 weights
+    (nbytes) between pinned host memory and HBM with hipMemcpyAsync on side streams, each
+    direction alone and both at once (the backward's weight reloads run beside its gradient
+    flushes). Best of `reps`. The step's link bound is its upload and flush bytes at the rates of
+    both directions at once."""
+    import torch
+    h_src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h_dst = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d_dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d_src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    up, down = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(h2d, d2h):
+        best = float("inf")
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            if h2d:
+                with torch.cuda.stream(up):
+                    d_dst.copy_(h_src, non_blocking=True)
+            if d2h:
+                with torch.cuda.stream(down):
+                    h_dst.copy_(d_src, non_blocking=True)
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - a)
+        return nbytes / best / 1e9
+
+    timed(True, True)   # warm-up
+    h2d_alone, d2h_alone, both = timed(True, False), timed(False, True), timed(True, True)
+    return {"bytes_per_copy": nbytes, "h2d_alone_gbs": round(h2d_alone, 1),
+            "d2h_alone_gbs": round(d2h_alone, 1), "h2d_both_gbs": round(both, 1),
+            "d2h_both_gbs": round(both, 1)}
 
 
 def run_step(w, args):
