@@ -202,6 +202,17 @@ class SlideEngine:
         self.lm_job = [None] * self.lm_nch        # pending CPU update per chunk
         self.lm_ready = [None] * self.lm_nch      # H2D of the chunk's current device copy
         self.lm_flushed = [None] * self.lm_nch    # D2H of the chunk's last device gradient
+        # The embedding is flushed, updated and uploaded in row chunks too: at the step boundary
+        # its gradient's D2H, CPU update and upload overlap chunk by chunk instead of running one
+        # after the other before the next forward can start.
+        self.emb_nch = min(8, V)
+        er = -(-V // self.emb_nch)
+        self.emb_rows = [(ci * er, min((ci + 1) * er, V)) for ci in range(self.emb_nch)
+                         if ci * er < V]
+        self.emb_nch = len(self.emb_rows)
+        self.emb_job = [None] * self.emb_nch
+        self.emb_ready = [None] * self.emb_nch
+        self.emb_flushed = [None] * self.emb_nch
 
         # device memory, allocated once
         dev = self.device
@@ -321,6 +332,8 @@ class SlideEngine:
             self._upload_resident(prm)
         self.lm_ready = [self.lm.ready_ev] * self.lm_nch
         self.lm_job = [None] * self.lm_nch
+        self.emb_ready = [self.embed.ready_ev] * self.emb_nch
+        self.emb_job = [None] * self.emb_nch
         torch.cuda.synchronize(self.device)
 
     def _upload_resident(self, prm):
@@ -418,6 +431,8 @@ class SlideEngine:
             self._wait_param(prm)
         for ci in range(self.lm_nch):
             self._wait_job(self.lm_job[ci])
+        for ci in range(self.emb_nch):
+            self._wait_job(self.emb_job[ci])
 
     def close(self):
         self.wait_updates()
@@ -490,11 +505,12 @@ class SlideEngine:
             done.record(self.h2d)
         self.x_h2d_ev[i] = done
 
-    def _flush_lm_chunk(self, ci, rec):
-        """D2H of LM-head chunk ci's gradient rows once the compute stream has produced them,
-        then that chunk's AdamW, then its refreshed rows go back up on the H2D stream."""
-        prm, H = self.lm, self.spec.hidden
-        r0, r1 = self.lm_rows[ci]
+    def _flush_chunk(self, prm, r0, r1, name, priority, rec, on_ready):
+        """D2H of rows [r0, r1) of a resident block's gradient once the compute stream has
+        produced them, then those rows' AdamW, then the refreshed rows go back up on the H2D
+        stream (on_ready(event) is called with the upload's event). Returns (job, flush
+        event)."""
+        H = self.spec.hidden
         sl = slice(r0 * H, r1 * H)
         ev_c = torch.cuda.Event()
         ev_c.record(self.compute)
@@ -505,7 +521,6 @@ class SlideEngine:
             dst.copy_(prm.grad[sl], non_blocking=True)
             done = torch.cuda.Event()
             done.record(self.d2h)
-        self.lm_flushed[ci] = done
 
         def upload():
             with torch.cuda.stream(self.h2d):
@@ -514,15 +529,37 @@ class SlideEngine:
                 prm.dev[sl].copy_(src, non_blocking=True)
                 ev = torch.cuda.Event()
                 ev.record(self.h2d)
-            self.lm_ready[ci] = ev
+            on_ready(ev)
 
         out = prm.shared[sl] if prm.dtype == "bf16" else None
-        job = _Job(f"lm_head{ci}", done, prm.master[sl], prm.grad_host[sl], prm.m[sl],
-                   prm.v[sl], out, r1 * H - r0 * H, self.step_count,
-                   self.L + 1 + ci / self.lm_nch, upload)
-        self.lm_job[ci] = job
+        job = _Job(name, done, prm.master[sl], prm.grad_host[sl], prm.m[sl], prm.v[sl], out,
+                   (r1 - r0) * H, self.step_count, priority, upload)
         rec["other_jobs"].append(job)
+        return job, done
+
+    def _flush_lm_chunk(self, ci, rec):
+        """LM-head chunk ci: flushed, updated and uploaded on its own (see _flush_chunk)."""
+        r0, r1 = self.lm_rows[ci]
+
+        def ready(ev):
+            self.lm_ready[ci] = ev
+        job, done = self._flush_chunk(self.lm, r0, r1, f"lm_head{ci}",
+                                      self.L + 1 + ci / self.lm_nch, rec, ready)
+        self.lm_flushed[ci] = done
+        self.lm_job[ci] = job
         return self._enqueue(job)
+
+    def _flush_embed(self, rec):
+        """The embedding's gradient in row chunks, each flushed, updated (before every layer:
+        priorities -1 .. -1/n) and uploaded on its own."""
+        for ci, (r0, r1) in enumerate(self.emb_rows):
+            def ready(ev, ci=ci):
+                self.emb_ready[ci] = ev
+            job, done = self._flush_chunk(self.embed, r0, r1, f"embed{ci}",
+                                          -1 + ci / self.emb_nch, rec, ready)
+            self.emb_flushed[ci] = done
+            self.emb_job[ci] = job
+            self._enqueue(job)
 
     def step(self, tokens):
         """One training step on int32 tokens [B, S+1] (inputs [:, :S], targets [:, 1:]).
@@ -543,13 +580,8 @@ class SlideEngine:
             self.tok_tgt.copy_(tok[:, 1:].reshape(-1), non_blocking=False)
 
         # ---- forward
-        self._wait_param(self.embed)
-        c.wait_event(self.embed.ready_ev)
-        if self.embed.flushed_ev is not None:
-            c.wait_event(self.embed.flushed_ev)
         host_x = self.activations == "host"
         K = self.x_slots
-        B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
         # Prefetch: load layers in order into free slots as soon as their update is done,
         # without blocking; block only for the layer the forward needs next.
         slots = {}
@@ -568,7 +600,17 @@ class SlideEngine:
                 nxt[0] += 1
                 free[0] -= 1
 
+        # layers already updated start uploading while the embedding's chunks are still being
+        # updated; the gather waits for every chunk's upload
         prefetch()
+        for ci in range(self.emb_nch):
+            self._wait_job(self.emb_job[ci])
+            prefetch()
+        for ci in range(self.emb_nch):
+            c.wait_event(self.emb_ready[ci])
+            if self.emb_flushed[ci] is not None:
+                c.wait_event(self.emb_flushed[ci])
+        B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
         for i in range(L):
             if i not in slots:
                 prefetch(need=i)
@@ -662,7 +704,7 @@ class SlideEngine:
         # ---- embedding gradient
         B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
                           self.ws, self.ws_bytes, c)
-        rec["other_jobs"].append(self._flush_resident(self.embed, "embed", -1))
+        self._flush_embed(rec)
         # the host sleeps until the GPU is done (a blocking event), leaving every core to the
         # CPU optimizer instead of spinning on one
         e_end = torch.cuda.Event(enable_timing=True, blocking=True)
