@@ -518,13 +518,83 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
           }
     }
     __syncthreads();
+    // the cross-entropy dz also writes zeros into the padding columns [N, ldc)
+    const int col_lim = EPI == EPI_CE_DZ ? g.ldc : g.N;
+    if (vec && n0 + BN <= col_lim && m0 + h * WTM + WTM <= g.M) {
+      // the whole pass is inside the matrix: groups of GRP chunks with no per-chunk checks, so
+      // a group's global reads (residual, accumulation target) and LDS reads are all issued
+      // before the first of them is waited for
+      constexpr int GRP = 8;
+      static_assert(PER % GRP == 0, "whole groups per pass");
+#pragma unroll
+      for (int q0 = 0; q0 < PER; q0 += GRP) {
+        uint2 rres[GRP];
+        float4 cold[GRP], v[GRP];
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          const int k = threadIdx.x + NT * (q0 + j);
+          const int gr = m0 + h * WTM + k / CPR, gc = n0 + (k % CPR) * 4;
+          if constexpr (EPI == EPI_RESID)
+            rres[j] = *(const uint2*)((const bf16_t*)g.R + (size_t)gr * g.ldr + gc);
+          if constexpr (EPI == EPI_ACCUM_F32)
+            cold[j] = *(const float4*)((const float*)g.C + (size_t)gr * g.ldc + gc);
+        }
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          const int k = threadIdx.x + NT * (q0 + j);
+          const int r = k / CPR, cc = k % CPR;
+          v[j] = *(const float4*)(lds + r * BN + ((cc * 4) ^ (((r >> 2) & 1) << 5)));
+        }
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {
+          const int k = threadIdx.x + NT * (q0 + j);
+          const int gr = m0 + h * WTM + k / CPR, gc = n0 + (k % CPR) * 4;
+          const size_t at = (size_t)gr * g.ldc + gc;
+          float o[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+          bool f32_out = F32;
+          if constexpr (EPI == EPI_RESID) {
+            o[0] += __uint_as_float(rres[j].x << 16);
+            o[1] += __uint_as_float(rres[j].x & 0xffff0000u);
+            o[2] += __uint_as_float(rres[j].y << 16);
+            o[3] += __uint_as_float(rres[j].y & 0xffff0000u);
+          }
+          if constexpr (EPI == EPI_ACCUM_F32) {
+            o[0] += cold[j].x;
+            o[1] += cold[j].y;
+            o[2] += cold[j].z;
+            o[3] += cold[j].w;
+          }
+          if constexpr (EPI == EPI_CE_DZ) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              float d = 0.f;
+              if (dz_y[t] >= 0) {
+                d = __expf(o[t] - dz_lse[t]);
+                if (g.c0 + gr == dz_y[t]) d -= 1.f;
+                d *= inv_nv;
+              }
+              o[t] = d;
+            }
+            f32_out = c_f32;
+          }
+          if (f32_out) {
+            *(float4*)((float*)g.C + at) = make_float4(o[0], o[1], o[2], o[3]);
+          } else {
+            uint2 w;
+            w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+            w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            *(uint2*)((bf16_t*)g.C + at) = w;
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int k = threadIdx.x + NT * q;
       const int r = k / CPR, cc = k % CPR;
       const int gr = m0 + h * WTM + r, gc = n0 + cc * 4;
-      // the cross-entropy dz also writes zeros into the padding columns [N, ldc)
-      if (gr >= g.M || gc >= (EPI == EPI_CE_DZ ? g.ldc : g.N)) continue;
+      if (gr >= g.M || gc >= col_lim) continue;
       const float4 v = *(const float4*)(lds + r * BN + ((cc * 4) ^ (((r >> 2) & 1) << 5)));
       float o[4] = {v.x, v.y, v.z, v.w};
       const size_t at = (size_t)gr * g.ldc + gc;
