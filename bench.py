@@ -64,10 +64,13 @@ def kernel_bytes(spec, B, S):
     """Algorithmic HBM bytes per launch of the memory-bound kernels (bf16 tensors)."""
     N, H, F, d = B * S, spec.hidden, spec.ffn, spec.head_dim
     QR = (spec.n_heads + 2 * spec.n_kv_heads) * d
+    OD = spec.n_heads * d
     return {"rmsnorm_fwd": 2 * N * H * 2, "rmsnorm_bwd": 4 * N * H * 2,
+            "rmsnorm_dw": 2 * N * H * 2,             # dy and x read; the partials are small
             "swiglu_fwd": 3 * N * F * 2, "swiglu_bwd": 5 * N * F * 2,
             "rope_fwd": 2 * N * (QR - spec.n_kv_heads * d) * 2,
-            "rope_bwd": 2 * N * (QR - spec.n_kv_heads * d) * 2}
+            "rope_bwd": 2 * N * (QR - spec.n_kv_heads * d) * 2,
+            "attn_delta": 2 * N * OD * 2 + N * spec.n_heads * 4}
 
 
 def cpu_baseline(w, B1=2, S1=1024, n_ce=1024, ad_frac=1.0):
@@ -644,6 +647,10 @@ def run_layer_kernels(args):
     e1.record(st)
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / 3
+    copy_gbs = 2 * nbytes / (copy_ms * 1e-3) / 1e9
+    for k in kernels.values():   # the HBM-bound kernels against the measured copy rate
+        if "gbs" in k:
+            k["frac_of_copy"] = round(k["gbs"] / copy_gbs, 3)
     return {
         "metric": "one decoder layer fwd+bwd, kernels alone (1 GPU)",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -656,7 +663,7 @@ def run_layer_kernels(args):
         "layer_mfma_util_pct": round(100 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": _roofline(kernels, alg, traffic_ok=True), "kernels": kernels,
         "copy_ref": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(copy_ms, 4),
-                     "gbs_read_plus_write": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)},
+                     "gbs_read_plus_write": round(copy_gbs, 1)},
     }
 
 
