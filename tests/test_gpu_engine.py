@@ -163,3 +163,44 @@ def test_bf16_model_loss_matches_oracle():
     rloss, _ = om.model_loss_and_grads(_oracle_params(params), tok, sh)
     print(f"  loss gpu {loss:.6f} oracle {rloss:.6f}", flush=True)
     assert abs(loss - rloss) <= 2e-3 * abs(rloss)
+
+
+RAGGED = Workload("ragged-vocab-bf16", LayerCfg(256, 4, 2, 64, 688), 3, 1000, 2, 64, "bf16")
+
+
+def test_ragged_vocab_chunks_match_oracle_and_serialized_run():
+    """A vocabulary of 1000 rows: LM-head chunks of 256 with a ragged last one (232 rows) and
+    embedding row chunks of 125 rows, each flushed, updated and uploaded on its own. Step 1's
+    loss matches the oracle; two overlapped steps equal two serialized ones bit for bit."""
+    w = RAGGED
+    print(f"engine step {w.name}: V={w.vocab}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    toks = [tokens(w.batch, w.seq, w.vocab, seed=20 + s) for s in range(2)]
+
+    def run(serialize):
+        eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=2, hp=HP, adam_threads=3,
+                          serialize=serialize, ce_chunk=256)
+        try:
+            eng.load_params(params["embed"].f32, _flat_layers(params, w),
+                            params["w_final"].f32, params["lm_head"].f32)
+            losses = []
+            for t in toks:
+                eng.step(t)
+                losses.append(eng.loss())
+            return losses, eng.master_params()
+        finally:
+            eng.close()
+
+    la, pa = run(False)
+    lb, pb = run(True)
+    c = w.layer
+    sh = om.ModelShape(om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn),
+                       w.n_layers, w.vocab)
+    rloss, _ = om.model_loss_and_grads(_oracle_params(params), toks[0], sh)
+    print(f"  losses overlapped {la} serialized {lb}, oracle step 1 {rloss:.6f}", flush=True)
+    assert abs(la[0] - rloss) <= 2e-3 * abs(rloss)
+    assert la == lb
+    for k in ("embed", "w_final", "lm_head"):
+        assert np.array_equal(pa[k].view(np.uint32), pb[k].view(np.uint32)), k
+    for x, y in zip(pa["layers"], pb["layers"]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
