@@ -237,16 +237,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
     const bf16_t* sK = tK(jb % NSTAGE);
     const bf16_t* sV = tV(jb % NSTAGE);
 
+    // the two 32-key halves alternate, so consecutive MFMAs do not depend on each other and
+    // each K-row read has a step more to arrive
     f32x16_t sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
-    }
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
     float mx = -INFINITY;
 #pragma unroll
