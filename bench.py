@@ -209,6 +209,18 @@ def _host_bytes_needed(w):
     return n * 14          # fp32 master + m + v (12 B) and the pinned bf16 buffer (2 B)
 
 
+def step_host_bytes(w):
+    """Host bytes of one offloaded step: the CPU AdamW's 28 B per parameter (fp32 master, m, v
+    read and written, the bf16 gradient read and the bf16 weight written); the uploads (every
+    layer twice except the ring's slots reused at the turnaround, the resident embedding, final
+    gain and LM head once); the gradient flushes (every parameter once, bf16)."""
+    c = w.layer
+    n = c.param_count()
+    n_all = w.n_layers * n + 2 * w.vocab * c.hidden + c.hidden
+    h2d = 2 * (2 * w.n_layers - w.ring_slots) * n + 2 * (2 * w.vocab * c.hidden + c.hidden)
+    return 28 * n_all, h2d, 2 * n_all
+
+
 def host_roofline(w, threads, step_s):
     """The step's host-memory bound: every parameter's CPU AdamW moves 28 bytes through host
     DRAM (fp32 master, m, v read and written, the bf16 gradient read and the bf16 weight
@@ -233,12 +245,7 @@ def host_roofline(w, threads, step_s):
         sl.slide_cpu_adamw(p, g, sl.SLIDE_BF16, m, v, g, n, k + 1, hp, threads)
         ts.append(time.perf_counter() - a)
     bw = 28 * n / min(ts[1:])        # best of the timed calls: the host's DRAM is shared
-    n_all = w.n_layers * n + 2 * w.vocab * c.hidden + c.hidden
-    adam_bytes = 28 * n_all
-    # uploads: every layer twice except the ring's slots reused at the turnaround; the resident
-    # embedding and LM head once; flushes: every gradient once (bf16)
-    h2d = 2 * (2 * w.n_layers - w.ring_slots) * n + 2 * (2 * w.vocab * c.hidden + c.hidden)
-    d2h = 2 * n_all
+    adam_bytes, h2d, d2h = step_host_bytes(w)
     bound_s = adam_bytes / bw
     link = host_link(2 * n)
     link_s = max(h2d / (link["h2d_both_gbs"] * 1e9), d2h / (link["d2h_both_gbs"] * 1e9))

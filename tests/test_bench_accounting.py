@@ -1,0 +1,71 @@
+"""The bench's work accounting against the algorithmic totals worked out independently for the
+Llama-3-8B-shaped step (hot-path scope table): a wrong flop or byte count would misstate every
+reported rate, so these are pinned on the CPU."""
+import types
+
+import pytest
+
+import bench
+from seeded_inputs import L8B
+
+LAYER_FWD = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attn_fwd")
+LAYER_BWD = ("gemm_qkv_dx", "gemm_qkv_dw", "gemm_o_dx", "gemm_o_dw", "gemm_gate_up_dx",
+             "gemm_gate_up_dw", "gemm_down_dx", "gemm_down_dw", "attn_bwd_dv", "attn_bwd_dk",
+             "attn_bwd_dq")
+
+
+def _spec():
+    c = L8B.layer
+    return types.SimpleNamespace(hidden=c.hidden, ffn=c.ffn, head_dim=c.head_dim,
+                                 n_heads=c.n_heads, n_kv_heads=c.n_kv_heads, vocab=L8B.vocab)
+
+
+def test_layer_flops_match_the_algorithmic_totals():
+    alg, exe = bench.kernel_flops(_spec(), L8B.batch, L8B.seq, L8B.ce_chunk)
+    # one causal S x S x d product over all heads: d * S(S+1) * B * nq (2 flops per pair / 2)
+    U = 128 * 1024 * 1025 * 8 * 32
+    assert alg["attn_fwd"] == 2 * U
+    assert alg["attn_bwd_dv"] + alg["attn_bwd_dk"] + alg["attn_bwd_dq"] == 4 * U
+    fwd = sum(alg[k] for k in LAYER_FWD)
+    bwd = sum(alg[k] for k in LAYER_BWD)
+    assert fwd == pytest.approx(3.642e12, rel=1e-3)        # 444.6 MF/token at N = 8192
+    assert bwd == pytest.approx(2 * fwd, rel=1e-12)         # every product twice
+    assert fwd + bwd == pytest.approx(1333.8e6 * 8192, rel=1e-3)
+    # projections: 2 M N K
+    assert alg["gemm_gate_up"] == 2 * 8192 * 2 * 14336 * 4096
+    assert alg["gemm_qkv"] == 2 * 8192 * (32 + 16) * 128 * 4096
+    # executed attention work includes the recomputed scores (and dP in the dK and dQ kernels)
+    assert exe["attn_bwd_dv"] == 2 * U and exe["attn_bwd_dk"] == 3 * U and exe["attn_bwd_dq"] == 3 * U
+
+
+def test_cross_entropy_flops_per_chunk():
+    alg, exe = bench.kernel_flops(_spec(), L8B.batch, L8B.seq, L8B.ce_chunk)
+    nch = -(-L8B.vocab // L8B.ce_chunk)
+    per = 2 * 8192 * L8B.vocab * 4096 / nch
+    # algorithmically the logits once, dh and dW once; the logits GEMM runs twice
+    assert alg["ce_stats_gemm"] + alg["ce_dz_gemm"] == pytest.approx(per)
+    assert exe["ce_stats_gemm"] == exe["ce_dz_gemm"] == pytest.approx(per)
+    assert alg["ce_dh_gemm"] == alg["ce_dw_gemm"] == pytest.approx(per)
+    # the 8B step's CE: three 2 N V H products = 25.8 TF
+    assert 3 * per * nch == pytest.approx(25.8e12, rel=2e-3)
+
+
+def test_hbm_bytes_of_the_memory_bound_kernels():
+    b = bench.kernel_bytes(_spec(), L8B.batch, L8B.seq)
+    N, H, F = 8192, 4096, 14336
+    assert b["rmsnorm_fwd"] == 2 * N * H * 2                 # read x, write y
+    assert b["swiglu_fwd"] == 3 * N * F * 2                  # read g, u; write m
+    assert b["swiglu_bwd"] == 5 * N * F * 2                  # read dm, g, u; write dg, du
+    assert b["rope_fwd"] == 2 * N * 40 * 128 * 2             # q and k heads, read and written
+    assert b["attn_delta"] == 2 * N * 4096 * 2 + N * 32 * 4
+
+
+def test_step_host_bytes():
+    """Per step: AdamW moves 28 B per parameter (224.8 GB), the uploads are 28.7 GB and the
+    gradient flushes 16.1 GB."""
+    assert L8B.layer.param_count() == 218_112_000
+    adam, h2d, d2h = bench.step_host_bytes(L8B)
+    assert adam == 28 * 8_030_261_248
+    assert adam == pytest.approx(224.8e9, rel=1e-3)
+    assert h2d == pytest.approx(28.7e9, rel=2e-3)
+    assert d2h == pytest.approx(16.06e9, rel=1e-3)
