@@ -502,6 +502,36 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
       }
     }
   }
+  // A plain bf16 store of a tile inside an aligned matrix: one pass. The whole 256 x 256 tile,
+  // rounded to bf16 (the only rounding either way), fits the 128 KB of stages, so every wave
+  // writes at once and each thread then stores 16-byte row chunks.
+  if constexpr (EPI == EPI_STORE_BF16) {
+    if (g.ldc % 8 == 0 && (uintptr_t)g.C % 16 == 0 && m0 + BM <= g.M && n0 + BN <= g.N) {
+      static_assert(BM * BN * 2 <= PC::NS * 2 * PC::SE * 2, "a bf16 tile fits the stages");
+      constexpr int CPR8 = BN / 8, PER8 = BM * CPR8 / NT;
+      bf16_t* lb = (bf16_t*)lds;
+      __syncthreads();   // the main loop's LDS reads are done
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = wm * WTM + i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+            const int c = (wn * WTN + j * 32 + (lane & 31)) ^ (hl << 5);
+            lb[r * BN + c] = f2bf(acc[i][j][e] * g.alpha);
+          }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < PER8; ++q) {
+        const int k = threadIdx.x + NT * q;
+        const int r = k / CPR8, cc = k % CPR8;
+        const uint4 v = *(const uint4*)(lb + r * BN + ((cc * 8) ^ (((r >> 2) & 1) << 5)));
+        *(uint4*)((bf16_t*)g.C + (size_t)(m0 + r) * g.ldc + n0 + cc * 8) = v;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int h = 0; h < PC::WGM; ++h) {
     __syncthreads();   // the main loop's (or the previous pass's) LDS reads are done
