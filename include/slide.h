@@ -44,7 +44,8 @@ enum {
   SLIDE_E_STATE = -5,        /* slot-ring call not allowed in the slot's current state */
   SLIDE_E_TIMEOUT = -6,      /* a bounded host wait ran out */
   SLIDE_E_UNSUPPORTED = -7,  /* valid request this build does not implement */
-  SLIDE_E_NONFINITE = -8     /* reserved: non-finite value detected where checked */
+  SLIDE_E_NONFINITE = -8,    /* reserved: non-finite value detected where checked */
+  SLIDE_E_IO = -9            /* a file operation of the disk tier failed (errno in the message) */
 };
 
 typedef enum { SLIDE_F32 = 0, SLIDE_BF16 = 1 } slide_dtype;
@@ -284,6 +285,50 @@ int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
 int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dtype, float* m, float* v,
                                     uint16_t* p_bf16_out, size_t n, int64_t step,
                                     const slide_adamw_hp* hp);
+
+/* ------------------------------------------------------------------------------------------
+ * Disk tier of the optimizer state (the method's CPU optimizer keeps its state in host memory
+ * and can move it to NVMe: summary, section 2B, "Layer-Adam"; for models larger than host memory
+ * the optimizer state goes to NVMe first: summary, section 3, and the paper page's "Analysis of
+ * NVMe Offloading").
+ * A tier is one file of capacity_bytes holding fp32 arrays at offsets that are multiples of 4096.
+ * The caller places the arrays; an array of n floats takes slide_tier_region_bytes(n) bytes (n*4
+ * rounded up to 4096). Every transfer goes through the tier's page-aligned bounce buffers
+ * (3 sets x 3 arrays x chunk_elems floats, owned by the tier) in 1 MiB requests served by
+ * n_io_threads threads (<= 0: 8).
+ * flags: SLIDE_TIER_DIRECT opens the file with O_DIRECT (the page cache is bypassed, so the
+ *   bytes reach the device); where the file system refuses O_DIRECT the file is opened buffered
+ *   and slide_tier_info reports direct = 0. SLIDE_TIER_UNLINK removes the file's name right
+ *   after it is created, so its space is returned when the tier is destroyed or the process ends.
+ * The file is created (or truncated) and sized to capacity_bytes; it reads as zeros until
+ * written. Calls on one tier are serialized by the tier. File errors return SLIDE_E_IO;
+ * offsets that are not page multiples or regions past the capacity return SLIDE_E_ARG.
+ * ------------------------------------------------------------------------------------------ */
+enum { SLIDE_TIER_DIRECT = 1, SLIDE_TIER_UNLINK = 2 };
+typedef struct slide_tier slide_tier;
+size_t slide_tier_region_bytes(size_t n_floats);
+int slide_tier_create(slide_tier** out, const char* path, uint64_t capacity_bytes,
+                      size_t chunk_elems /* 0: 4Mi; rounded up to a multiple of 1024 */,
+                      int n_io_threads, int flags);
+int slide_tier_destroy(slide_tier* t);
+int slide_tier_info(slide_tier* t, int* direct, uint64_t* capacity_bytes, size_t* chunk_elems);
+/* Totals since creation: bytes moved to and from the file, seconds spent inside tier calls and
+ * seconds of those spent waiting for I/O. */
+int slide_tier_stats(slide_tier* t, uint64_t* bytes_read, uint64_t* bytes_written,
+                     double* busy_s, double* stall_s);
+/* Blocking copies between host memory and the tier. src == NULL writes zeros. Whole pages are
+ * written: the bytes from off + bytes up to the next multiple of 4096 become zero. */
+int slide_tier_write(slide_tier* t, uint64_t off, const void* src, size_t bytes);
+int slide_tier_read(slide_tier* t, uint64_t off, void* dst, size_t bytes);
+/* slide_cpu_adamw on one parameter block whose p, m and v each live either in host memory (a
+ * non-NULL pointer; the offset is ignored) or in the tier at the given offset (a NULL pointer).
+ * The block is streamed in chunks of chunk_elems: while chunk k is updated, chunk k+1's tier
+ * arrays are read and chunk k-1's written back. Every element gets exactly slide_cpu_adamw's
+ * operations, so the results are bit-identical to that call with the arrays in memory. g and
+ * p_bf16_out are host memory as for slide_cpu_adamw (p_bf16_out may alias a bf16 g). Blocks. */
+int slide_tier_adamw(slide_tier* t, float* p, uint64_t p_off, float* m, uint64_t m_off, float* v,
+                     uint64_t v_off, const void* g, int g_dtype, uint16_t* p_bf16_out, size_t n,
+                     int64_t step, const slide_adamw_hp* hp, int n_threads);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel timing: when enabled, every kernel the library launches is bracketed by HIP events

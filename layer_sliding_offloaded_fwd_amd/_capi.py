@@ -7,12 +7,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libslide.so
 SLIDE_OK = 0
 SLIDE_E_ARG, SLIDE_E_SHAPE, SLIDE_E_WORKSPACE, SLIDE_E_HIP = -1, -2, -3, -4
 SLIDE_E_STATE, SLIDE_E_TIMEOUT, SLIDE_E_UNSUPPORTED, SLIDE_E_NONFINITE = -5, -6, -7, -8
+SLIDE_E_IO = -9
+SLIDE_TIER_DIRECT, SLIDE_TIER_UNLINK = 1, 2
 SLIDE_F32, SLIDE_BF16 = 0, 1
 SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST = 0, 1
 SLOT_FREE, SLOT_LOADING, SLOT_IN_USE, SLOT_FLUSHING = 0, 1, 2, 3
 ERROR_NAMES = {0: "SLIDE_OK", -1: "SLIDE_E_ARG", -2: "SLIDE_E_SHAPE", -3: "SLIDE_E_WORKSPACE",
                -4: "SLIDE_E_HIP", -5: "SLIDE_E_STATE", -6: "SLIDE_E_TIMEOUT",
-               -7: "SLIDE_E_UNSUPPORTED", -8: "SLIDE_E_NONFINITE"}
+               -7: "SLIDE_E_UNSUPPORTED", -8: "SLIDE_E_NONFINITE", -9: "SLIDE_E_IO"}
 
 
 class LayerCfg(ctypes.Structure):
@@ -82,6 +84,17 @@ SIGNATURES = {
     "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,
                                             ctypes.POINTER(AdamWHp)]),
+    "slide_tier_region_bytes": (SZ, [SZ]),
+    "slide_tier_create": (I, [ctypes.POINTER(P), ctypes.c_char_p, ctypes.c_uint64, SZ, I, I]),
+    "slide_tier_destroy": (I, [P]),
+    "slide_tier_info": (I, [P, ctypes.POINTER(I), ctypes.POINTER(ctypes.c_uint64),
+                            ctypes.POINTER(SZ)]),
+    "slide_tier_stats": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
+                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+    "slide_tier_write": (I, [P, ctypes.c_uint64, P, SZ]),
+    "slide_tier_read": (I, [P, ctypes.c_uint64, P, SZ]),
+    "slide_tier_adamw": (I, [P, P, ctypes.c_uint64, P, ctypes.c_uint64, P, ctypes.c_uint64, P, I,
+                             P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_prof_enable": (I, [I]),
     "slide_prof_reset": (I, []),
     "slide_prof_read": (I, [P, P, P, I, ctypes.POINTER(I)]),

@@ -7,7 +7,7 @@ runs in libslide's kernels; a non-zero status raises SlideError carrying slide_l
 import ctypes
 
 from ._capi import (AdamWHp, CeCfg, LayerCfg, SlideError, call, lib, SLIDE_BF16, SLIDE_F32,
-                    SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST)
+                    SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_TIER_DIRECT, SLIDE_TIER_UNLINK)
 
 __all__ = [
     "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F32", "SLIDE_ENGINE_HIP",
@@ -20,7 +20,8 @@ __all__ = [
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
-    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_prof_enable", "slide_prof_reset",
+    "slide_rope", "SlotRing", "slide_cpu_adamw", "StateTier", "slide_tier_region_bytes",
+    "SLIDE_TIER_DIRECT", "SLIDE_TIER_UNLINK", "slide_prof_enable", "slide_prof_reset",
     "slide_prof_read", "dtype_code", "layer_cfg",
 ]
 
@@ -262,6 +263,63 @@ def slide_cpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, n_threads=0):
     """p, m, v: float32 host buffers; g: host bf16 (uint16) or float32; hp: AdamWHp."""
     call("slide_cpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
          ctypes.byref(hp), n_threads)
+
+
+# ------------------------------------------------------------------------------ disk tier
+def slide_tier_region_bytes(n_floats):
+    return lib().slide_tier_region_bytes(n_floats)
+
+
+class StateTier:
+    """Handle of a disk tier of fp32 optimizer state (slide_tier_*). Offsets are bytes, multiples
+    of 4096; arrays are host buffers (numpy or CPU torch)."""
+
+    def __init__(self, path, capacity_bytes, chunk_elems=0, io_threads=8,
+                 flags=SLIDE_TIER_DIRECT | SLIDE_TIER_UNLINK):
+        h = ctypes.c_void_p()
+        call("slide_tier_create", ctypes.byref(h), str(path).encode(), capacity_bytes,
+             chunk_elems, io_threads, flags)
+        self.h = h
+
+    def info(self):
+        d, cap, ch = ctypes.c_int(), ctypes.c_uint64(), ctypes.c_size_t()
+        call("slide_tier_info", self.h, ctypes.byref(d), ctypes.byref(cap), ctypes.byref(ch))
+        return dict(direct=bool(d.value), capacity=cap.value, chunk=ch.value)
+
+    def stats(self):
+        r, w = ctypes.c_uint64(), ctypes.c_uint64()
+        busy, stall = ctypes.c_double(), ctypes.c_double()
+        call("slide_tier_stats", self.h, ctypes.byref(r), ctypes.byref(w), ctypes.byref(busy),
+             ctypes.byref(stall))
+        return dict(bytes_read=r.value, bytes_written=w.value, busy_s=busy.value,
+                    stall_s=stall.value)
+
+    def write(self, off, src, nbytes=None):
+        """src: host array, or None to write nbytes of zeros."""
+        if nbytes is None:
+            nbytes = src.nbytes if hasattr(src, "nbytes") else src.numel() * src.element_size()
+        call("slide_tier_write", self.h, off, _p(src), nbytes)
+
+    def read(self, off, dst):
+        nbytes = dst.nbytes if hasattr(dst, "nbytes") else dst.numel() * dst.element_size()
+        call("slide_tier_read", self.h, off, _p(dst), nbytes)
+
+    def adamw(self, p, p_off, m, m_off, v, v_off, g, g_dtype, p_bf16_out, n, step, hp,
+              n_threads=0):
+        """p, m, v: a host float32 buffer, or None for the array at the given tier offset."""
+        call("slide_tier_adamw", self.h, _p(p), p_off, _p(m), m_off, _p(v), v_off, _p(g), g_dtype,
+             _p(p_bf16_out), n, step, ctypes.byref(hp), n_threads)
+
+    def close(self):
+        if self.h is not None and self.h.value:
+            call("slide_tier_destroy", self.h)
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------------------ profiler

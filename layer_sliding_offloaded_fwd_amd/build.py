@@ -20,7 +20,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "pointwise.hip", "ce.hip", "layer.hip"]
 HIP_HOST_SOURCES = ["common.cpp", "ring.cpp"]   # host code that calls the HIP runtime
-CPU_SOURCES = ["adamw.cpp"]
+CPU_SOURCES = ["adamw.cpp", "tier.cpp"]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
