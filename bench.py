@@ -142,6 +142,13 @@ def _parse():
                     help="forward state for the backward: intermediates kept in HBM (default), "
                          "layer inputs kept and the forward recomputed, or layer inputs slid to "
                          "host memory and back (with recompute)")
+    ap.add_argument("--state-tier", default=None, metavar="DIR",
+                    help="keep the optimizer state (fp32 master, m, v) of --tier-layers layers in "
+                         "a file under DIR (O_DIRECT where the file system allows; unlinked at "
+                         "once) instead of host memory: the pages' optional NVMe tier")
+    ap.add_argument("--tier-layers", type=int, default=0,
+                    help="with --state-tier: how many layers (the last ones) keep their state "
+                         "in the file (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
@@ -203,10 +210,15 @@ def _roofline(kernels, alg, traffic_ok=False):
             "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom]}
 
 
-def _host_bytes_needed(w):
+def _host_bytes_needed(w, args=None):
+    """fp32 master + m + v (12 B) and the pinned bf16 buffer (2 B) per parameter; layers whose
+    optimizer state is in the disk tier keep only the bf16 buffer in host memory."""
     c = w.layer
     n = w.n_layers * c.param_count() + 2 * w.vocab * c.hidden + c.hidden
-    return n * 14          # fp32 master + m + v (12 B) and the pinned bf16 buffer (2 B)
+    tiered = 0
+    if args is not None and getattr(args, "state_tier", None):
+        tiered = min(args.tier_layers or w.n_layers, w.n_layers) * c.param_count()
+    return n * 14 - tiered * 12
 
 
 def step_host_bytes(w):
@@ -309,11 +321,24 @@ def run_step(w, args):
     cores = len(os.sched_getaffinity(0))
     threads = args.adam_threads or max(1, cores - 3)
     t_init = time.perf_counter()
-    print(f"[bench] {w.name}: {w.n_layers} layers, host state {_host_bytes_needed(w) / 1e9:.1f} GB;"
+    print(f"[bench] {w.name}: {w.n_layers} layers, host state {_host_bytes_needed(w, args) / 1e9:.1f} GB;"
           f" allocating", file=sys.stderr, flush=True)
+    tier_kw = {}
+    if args.state_tier:
+        # the last layers: their gradients land first in the backward and the next forward
+        # needs them last, so their slower updates have the most time to hide
+        k = min(args.tier_layers or w.n_layers, w.n_layers)
+        tier_kw = dict(state_tier=os.path.join(args.state_tier, f"slide-state-{os.getpid()}.bin"),
+                       tier_layers=list(range(w.n_layers - k, w.n_layers)))
+        need = k * 3 * sl.slide_tier_region_bytes(c.param_count())
+        st = os.statvfs(args.state_tier)
+        if need > 0.95 * st.f_bavail * st.f_frsize:
+            print(f"[bench] --state-tier {args.state_tier}: {k} layers need {need / 1e9:.1f} GB, "
+                  f"only {st.f_bavail * st.f_frsize / 1e9:.1f} GB free", file=sys.stderr)
+            sys.exit(1)
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True,
-                      activations=args.activations)
+                      activations=args.activations, **tier_kw)
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
@@ -325,6 +350,7 @@ def run_step(w, args):
         print(f"[bench] warmup step {i + 1}: loss {eng.loss():.4f}", file=sys.stderr, flush=True)
     eng.wait_updates()
     torch.cuda.synchronize()
+    tier0 = eng.tier_stats()
     sl.slide_prof_reset()
     sl.slide_prof_enable(True)
     t0 = time.perf_counter()
@@ -359,6 +385,7 @@ def run_step(w, args):
     mfma_util_alg = 100.0 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     mfma_util_exec = 100.0 * l_exe / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     ana = eng.analyse(eng.records[-args.steps:])
+    tier = _tier_report(eng, tier0, args.steps, step_s) if eng.tier is not None else None
     eng.close()
     host = host_roofline(w, threads, step_s)
     layer_bytes = w.n_layers * c.param_count() * 28
@@ -414,9 +441,29 @@ def run_step(w, args):
             "offloaded_fraction_of_resident": round(
                 (gpu_kernel_ms + 28 * n_all / (PEAK_HBM_GBS * 1e9) * 1e3) / (step_s * 1e3), 4)},
         "roofline": _roofline(kernels, alg, traffic_ok=(w.name == "llama3-8b-shaped")),
+        **({"state_tier": tier} if tier is not None else {}),
         "kernels": kernels,
         "init_s": round(t_init, 1),
     }
+
+
+def _tier_report(eng, before, steps, step_s):
+    """Disk-tier traffic of the timed steps: the optimizer state of each tiered layer (fp32
+    master, m and v for bf16 compute: 12 B per parameter) is read and written once per step,
+    streamed through the update; the rate is those bytes over the time the tier's calls took,
+    and the bound is the step's tier bytes at that rate."""
+    after = eng.tier_stats()
+    rd = after["bytes_read"] - before["bytes_read"]
+    wr = after["bytes_written"] - before["bytes_written"]
+    busy = after["busy_s"] - before["busy_s"]
+    stall = after["stall_s"] - before["stall_s"]
+    return {"layers": len(eng.tier_layers), "direct_io": after["direct"],
+            "chunk_elems": after["chunk"], "file_bytes": after["capacity"],
+            "read_bytes_per_step": rd // steps, "write_bytes_per_step": wr // steps,
+            "update_s_per_step": round(busy / steps, 3),
+            "io_wait_s_per_step": round(stall / steps, 3),
+            "read_plus_write_gbs": round((rd + wr) / busy / 1e9, 2) if busy else None,
+            "frac_of_step": round(busy / steps / step_s, 4)}
 
 
 def run_ce(args):
@@ -703,7 +750,7 @@ def main():
         try:
             import psutil
             avail = psutil.virtual_memory().available
-            while layers > 1 and _host_bytes_needed(w) > 0.85 * avail:
+            while layers > 1 and _host_bytes_needed(w, args) > 0.85 * avail:
                 layers -= 1
                 w = dataclasses.replace(L123B, n_layers=layers)
         except ImportError:

@@ -64,11 +64,12 @@ def _align(n, a=256):
 
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step", "priority", "seq")
+                 "t_end", "t_ready", "step", "priority", "seq", "tier")
 
-    def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None):
+    def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None):
         self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
         self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
+        self.tier = tier      # (p, m, v) offsets in the disk tier (None: in host memory)
         self.seq = 0
         self.done = threading.Event()
         self.t_start = self.t_end = self.t_ready = 0.0
@@ -121,21 +122,25 @@ def _host_f32(n):
 class _Param:
     """Host state of one parameter block: fp32 master, AdamW moments, the pinned buffer that
     serves as upload source and gradient landing zone, and (for resident blocks) the device
-    copy and device gradient."""
+    copy and device gradient.
+    tier: (p, m, v) byte offsets of the arrays that live in the disk tier instead of host memory
+    (the moments always; the master too for bf16 compute, where the pinned bf16 buffer is the
+    upload source; None where an array stays in host memory)."""
 
-    def __init__(self, n, dtype, pinned, device=None, resident=False):
+    def __init__(self, n, dtype, pinned, device=None, resident=False, tier=None):
         self.n = n
         self.dtype = dtype
+        self.tier = tier
         if dtype == "bf16":
-            self.master = _host_f32(n)
+            self.master = _host_f32(n) if tier is None or tier[0] is None else None
             self.shared = pinned.tensor(n, torch.int16)        # bf16 bits
             self.grad_host = self.shared
         else:
             self.master = pinned.tensor(n, torch.float32)      # upload source
             self.shared = self.master
             self.grad_host = pinned.tensor(n, torch.float32)
-        self.m = _host_f32(n)
-        self.v = _host_f32(n)
+        self.m = _host_f32(n) if tier is None else None
+        self.v = _host_f32(n) if tier is None else None
         self.job = None
         if resident:
             tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -148,14 +153,22 @@ class _Param:
 class SlideEngine:
     def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
-                 save_activations=True, activations=None, x_slots=4):
+                 save_activations=True, activations=None, x_slots=4, state_tier=None,
+                 tier_layers=None, tier_chunk=0, tier_io_threads=8):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
           "host": layer inputs slide to pinned host memory after the forward and come back
             before the backward (the pages' sliding activations), with recompute; only
             x_slots layer-input buffers stay on the device.
-        save_activations=False is the older spelling of activations="recompute"."""
+        save_activations=False is the older spelling of activations="recompute".
+        state_tier: path of a file that holds the optimizer state (AdamW moments, and the fp32
+          master for bf16 compute) of the layers in tier_layers (default: every layer) instead
+          of host memory (the pages' optional NVMe tier of the CPU optimizer's state). The file
+          is opened with O_DIRECT where the file system allows and unlinked at once, so it
+          takes disk space only while the engine lives. tier_chunk (elements) and
+          tier_io_threads size its streaming.
+        """
         assert spec.dtype in ("bf16", "f32")
         if activations is None:
             activations = "hbm" if save_activations else "recompute"
@@ -189,7 +202,26 @@ class SlideEngine:
 
         # host parameter blocks
         self.pinned = _PinnedPool()
-        self.layers = [_Param(self.P, s.dtype, self.pinned) for _ in range(self.L)]
+        self.tier = None
+        tiered = set()
+        if state_tier is not None:
+            tiered = set(range(self.L) if tier_layers is None else tier_layers)
+            assert tiered <= set(range(self.L)), tier_layers
+            reg = B.slide_tier_region_bytes(self.P)
+            arrays = 3 if s.dtype == "bf16" else 2
+            self.tier = B.StateTier(state_tier, max(arrays * reg * len(tiered), 4096),
+                                    tier_chunk, tier_io_threads)
+        self.tier_layers = sorted(tiered)
+        self.layers = []
+        o = 0
+        for i in range(self.L):
+            offs = None
+            if i in tiered:
+                if s.dtype == "bf16":
+                    offs, o = (o, o + reg, o + 2 * reg), o + 3 * reg
+                else:
+                    offs, o = (None, o, o + reg), o + 2 * reg
+            self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs))
         self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
@@ -262,8 +294,15 @@ class SlideEngine:
         self.job_seq = 0
         self.worker_stop = False
         self.worker_error = None
-        self.worker = threading.Thread(target=self._worker_loop, daemon=True, name="slide-adamw")
-        self.worker.start()
+        self.workers = [threading.Thread(target=self._worker_loop, daemon=True, name="slide-adamw")]
+        if self.tier is not None:
+            # the tier's updates stream their state through the file; their arithmetic needs few
+            # cores, so they get a share of the optimizer threads and run beside the others
+            self.tier_threads = max(2, (adam_threads or 12) // 3)
+            self.workers.append(threading.Thread(target=self._worker_loop, args=(True,),
+                                                 daemon=True, name="slide-adamw-tier"))
+        for t in self.workers:
+            t.start()
         self.step_count = 0
         self.records = []
 
@@ -277,10 +316,8 @@ class SlideEngine:
             t = torch.as_tensor(np.ascontiguousarray(arr, dtype=np.float32)
                                 if isinstance(arr, np.ndarray) else arr).reshape(-1).float()
             assert t.numel() == prm.n
-            prm.master.copy_(t)
-            self._refresh_shared(prm)
-            prm.m.zero_()
-            prm.v.zero_()
+            self._set_master(prm, t)
+            self._zero_moments(prm)
 
         put(self.embed, embed)
         put(self.final, w_final)
@@ -305,12 +342,9 @@ class SlideEngine:
             t.normal_(0.0, std, generator=gen)
             for o in gains:
                 t[o:o + H] = 1.0
-            prm.master.copy_(t, non_blocking=False)
-            if prm.dtype == "bf16":
-                prm.shared.copy_(t.to(torch.bfloat16).view(torch.int16))
+            self._set_master(prm, t)
             if self.step_count:          # moments are zero from construction until a step ran
-                prm.m.zero_()
-                prm.v.zero_()
+                self._zero_moments(prm)
 
         draw(self.embed)
         for i, prm in enumerate(self.layers):
@@ -326,6 +360,35 @@ class SlideEngine:
     def _refresh_shared(self, prm):
         if prm.dtype == "bf16":
             prm.shared.copy_(prm.master.to(torch.bfloat16).view(torch.int16))
+
+    def _set_master(self, prm, t):
+        """fp32 master weights of a block (a float32 tensor of prm.n elements, any device), and
+        the bf16 compute copy derived from them."""
+        if prm.master is not None:
+            prm.master.copy_(t)
+        else:
+            self.tier.write(prm.tier[0], t.detach().to("cpu").contiguous())
+        if prm.dtype == "bf16":
+            prm.shared.copy_(t.to(torch.bfloat16).view(torch.int16).to("cpu"))
+
+    def _zero_moments(self, prm):
+        if prm.tier is None:
+            prm.m.zero_()
+            prm.v.zero_()
+        else:
+            self.tier.write(prm.tier[1], None, 4 * prm.n)
+            self.tier.write(prm.tier[2], None, 4 * prm.n)
+
+    def _get_master(self, prm):
+        if prm.master is not None:
+            return prm.master.numpy().copy()
+        out = np.empty(prm.n, np.float32)
+        self.tier.read(prm.tier[0], out)
+        return out
+
+    def tier_stats(self):
+        """Traffic and time of the disk tier so far (None without a tier)."""
+        return None if self.tier is None else dict(self.tier.stats(), **self.tier.info())
 
     def _upload_all_resident(self):
         for prm in (self.embed, self.final, self.lm):
@@ -348,7 +411,7 @@ class SlideEngine:
         """fp32 master weights as numpy arrays (after waiting for pending updates)."""
         self.wait_updates()
         return dict(embed=self.embed.master.numpy().copy(),
-                    layers=[p.master.numpy().copy() for p in self.layers],
+                    layers=[self._get_master(p) for p in self.layers],
                     w_final=self.final.master.numpy().copy(),
                     lm_head=self.lm.master.numpy().copy())
 
@@ -367,14 +430,20 @@ class SlideEngine:
                 raise
         return job.wait.query()
 
-    def _worker_loop(self):
+    def _worker_loop(self, tiered=False):
+        """One CPU worker: the updates of blocks whose state is in host memory, or (tiered)
+        those whose state is in the disk tier, which wait mostly on the file and so run beside
+        the in-memory ones instead of holding them up."""
+        def mine():
+            return [j for j in self.jobs if (j.tier is not None) == tiered]
+
         while True:
             with self.jobs_cv:
-                while not self.jobs and not self.worker_stop:
+                while not mine() and not self.worker_stop:
                     self.jobs_cv.wait()
-                if not self.jobs and self.worker_stop:
+                pending = mine()
+                if not pending and self.worker_stop:
                     return
-                pending = list(self.jobs)
             try:
                 ready = [j for j in pending if self._landed(j)]
             except Exception as e:
@@ -389,8 +458,13 @@ class SlideEngine:
             try:
                 if self.worker_error is None:
                     job.t_ready = time.perf_counter()
-                    B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
-                                      job.step, self.hp, self.adam_threads)
+                    if job.tier is None:
+                        B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
+                                          job.step, self.hp, self.adam_threads)
+                    else:
+                        po, mo, vo = job.tier
+                        self.tier.adamw(job.p, po or 0, job.m, mo, job.v, vo, job.g, self.code,
+                                        job.out, job.n, job.step, self.hp, self.tier_threads)
                     job.t_start = job.t_ready
                     job.t_end = time.perf_counter()
                     if job.post is not None:
@@ -403,7 +477,7 @@ class SlideEngine:
     def _submit(self, prm, wait, name, priority, post=None):
         out = prm.shared if prm.dtype == "bf16" else None
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
-                   self.step_count, priority, post)
+                   self.step_count, priority, post, prm.tier)
         prm.job = job
         return self._enqueue(job)
 
@@ -412,7 +486,7 @@ class SlideEngine:
             self.job_seq += 1
             job.seq = self.job_seq
             self.jobs.append(job)
-            self.jobs_cv.notify()
+            self.jobs_cv.notify_all()
         if self.serialize:
             job.done.wait()
         return job
@@ -438,13 +512,16 @@ class SlideEngine:
         self.wait_updates()
         with self.jobs_cv:
             self.worker_stop = True
-            self.jobs_cv.notify()
-        self.worker.join()
+            self.jobs_cv.notify_all()
+        for t in self.workers:
+            t.join()
         self.ring.close()
         torch.cuda.synchronize(self.device)
         for prm in self.layers + [self.embed, self.final, self.lm]:
             prm.master = prm.shared = prm.grad_host = None
         self.pinned.free()
+        if self.tier is not None:
+            self.tier.close()
 
     # ------------------------------------------------------------------ step
     def _sync(self):

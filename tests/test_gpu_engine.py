@@ -100,12 +100,12 @@ def test_tiny_fp32_step_matches_oracle(ce_chunk):
 SMALL = Workload("small-bf16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "bf16")
 
 
-def _run(n_slots, serialize, steps=2, save=True, ce_chunk=256, activations=None, x_slots=4):
-    w = SMALL
+def _run(n_slots, serialize, steps=2, save=True, ce_chunk=256, activations=None, x_slots=4,
+         w=SMALL, **kw):
     params = model_params(w, seed=0, gain_std=0.1)
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=n_slots, hp=HP, adam_threads=3,
                       serialize=serialize, save_activations=save, ce_chunk=ce_chunk,
-                      activations=activations, x_slots=x_slots)
+                      activations=activations, x_slots=x_slots, **kw)
     try:
         eng.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
                         params["lm_head"].f32)
@@ -204,3 +204,22 @@ def test_ragged_vocab_chunks_match_oracle_and_serialized_run():
         assert np.array_equal(pa[k].view(np.uint32), pb[k].view(np.uint32)), k
     for x, y in zip(pa["layers"], pb["layers"]):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", [SMALL, TINY], ids=["bf16", "f32"])
+def test_disk_tier_of_optimizer_state_changes_no_bit(tmp_path, w):
+    """The optimizer state of some or all layers lives in a file (O_DIRECT where the file system
+    allows; for bf16 the fp32 master too, for fp32 the moments only): three steps give the same
+    losses and master weights, bit for bit, as with every state in host memory."""
+    print(f"disk tier: {w.name} L={w.n_layers}", flush=True)
+    la, pa = _run(3, False, steps=3, w=w)
+    for layers in (None, [0, w.n_layers - 1]):
+        lt, pt = _run(3, False, steps=3, w=w, state_tier=str(tmp_path / "state.bin"),
+                      tier_layers=layers, tier_chunk=4096 * 3)
+        print(f"  tier layers {layers}: losses {lt} (host memory {la})", flush=True)
+        assert lt == la
+        for k in ("embed", "w_final", "lm_head"):
+            assert np.array_equal(pa[k].view(np.uint32), pt[k].view(np.uint32)), k
+        for x, y in zip(pa["layers"], pt["layers"]):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert not (tmp_path / "state.bin").exists()
