@@ -1,6 +1,7 @@
 """GPU parity at the full sizes the step runs: one Llama-3-8B-shaped layer at batch 8 x 1024
-through the same entry points the engine calls (slide_layer_fwd_save / slide_layer_bwd_saved),
-and the chunked LM-head CE at the full 128256-row vocabulary with 8192 and 16384 tokens.
+and one 123B-class layer at batch 4 x 2048 through the same entry points the engine calls
+(slide_layer_fwd_save / slide_layer_bwd_saved), and the chunked LM-head CE at the full
+128256-row vocabulary with 8192 and 16384 tokens.
 
 The oracle cannot run the whole launch in seconds, so each test compares what it can compute
 exactly on a sample, plus properties that hold at any size:
@@ -8,6 +9,10 @@ exactly on a sample, plus properties that hold at any size:
   the batch is checked against the oracle row by row; the batch's weight gradients are the sum
   of the per-sequence ones (checked against eight single-sequence launches), and one
   single-sequence weight gradient is checked against the oracle;
+- 123B-class layer: the upstream gradient is zero except on the first P positions of one
+  sequence; by causality only those positions receive or pass on gradient, so the launch's
+  weight gradients, those positions' dx and y rows equal the oracle's layer on the P-token
+  prefix, and every other dx row is exactly zero;
 - CE: with every target but a sample ignored, the full-size launch computes exactly the oracle's
   CE of the sample (loss, dh and the whole dW); without the mask, sampled dh rows equal the
   sample's dh rescaled by the number of valid targets, and the loss and dW of the whole batch
@@ -19,7 +24,7 @@ import torch
 
 import layer_sliding_offloaded_fwd_amd as sl
 from oracle import model as om
-from seeded_inputs import L8B, CE_ONLY, activations, ce_inputs, layer_params, pack_layer
+from seeded_inputs import L8B, L123B, CE_ONLY, activations, ce_inputs, layer_params, pack_layer
 from tests._gpu import DEV, assert_close, dev, empty, host, rel_err, stream, ws
 
 pytestmark = pytest.mark.gpu
@@ -85,6 +90,47 @@ def test_layer_8b_at_bench_launch():
     g5 = _unpack(host(g_seq[b]), c)
     for n in om.LAYER_PARAM_NAMES:
         assert_close(g5[n], rg[n], dtype, f"grad {n}, sequence {b} alone")
+
+
+def test_layer_123b_at_bench_launch_prefix():
+    c, B, S, dtype = L123B.layer, L123B.batch, L123B.seq, "bf16"
+    N, H, P, b = B * S, c.hidden, 48, 2
+    print(f"123B-class layer at B={B} S={S}: H={H} nq={c.n_heads} nkv={c.n_kv_heads} "
+          f"d={c.head_dim} F={c.ffn} bf16; upstream gradient on the first {P} positions of "
+          f"sequence {b} only", flush=True)
+    params = layer_params(c, dtype, seed=0, gain_std=0.1)
+    x = activations((N, H), dtype, 1)
+    dyp = activations((P, H), dtype, 2)
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, dtype)
+    w = torch.from_numpy(pack_layer(params, c, dtype).view(np.int16)).to(DEV).view(torch.bfloat16)
+    tx = dev(x.f32, dtype)
+    rows = slice(b * S, b * S + P)
+    tdy = torch.zeros_like(tx)
+    tdy[rows] = dev(dyp.f32, dtype)
+    sb = sl.slide_layer_saved_bytes(cfg, B, S)
+    wb = sl.slide_layer_workspace_bytes(cfg, B, S, 2)
+    saved, work = ws(sb), ws(wb)
+    y = torch.empty_like(tx)
+    dx = torch.empty_like(tx)
+    g = torch.full_like(w, float("nan"))
+    sl.slide_layer_fwd_save(cfg, w, tx, y, B, S, saved, sb, stream())
+    sl.slide_layer_bwd_saved(cfg, w, tx, tdy, dx, g, B, S, saved, sb, work, wb, stream())
+    torch.cuda.synchronize()
+    del saved, work
+    shape = om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, c.rms_eps,
+                          c.rope_theta)
+    p64 = {k: v.f64 for k, v in params.items()}
+    ry, cache = om.layer_fwd(p64, x.f64[rows].reshape(1, P, H), shape)
+    rdx, rg = om.layer_bwd(p64, dyp.f64.reshape(1, P, H), cache, shape)
+    del p64, cache
+    assert_close(host(y[rows]).reshape(1, P, H), ry, dtype, f"y, first {P} rows of sequence {b}")
+    dxh = host(dx)
+    assert_close(dxh[rows].reshape(1, P, H), rdx, dtype, f"dx, first {P} rows of sequence {b}")
+    dxh[rows] = 0.0
+    assert float(np.max(np.abs(dxh))) == 0.0, "dx rows without upstream gradient must be 0"
+    gh = _unpack(host(g), c)
+    for n in om.LAYER_PARAM_NAMES:
+        assert_close(gh[n], rg[n], dtype, f"grad {n}")
 
 
 @pytest.fixture(scope="module")
