@@ -136,6 +136,10 @@ def _parse():
                          "lmhead-ce-128k (the chunked CE alone), critical-batch-sweep, "
                          "layer-kernels-8b (one 8B-shaped layer's kernels alone, plus a 1 GiB "
                          "device copy that calibrates HBM byte counters)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences of 1024 tokens per step of the llama3-8b-shaped workload "
+                         "(default 8); at the critical batch the CPU updates hide behind the "
+                         "backward")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers of the 123b slice (default 12, fewer if host RAM is short)")
     ap.add_argument("--activations", default="hbm", choices=["hbm", "recompute", "host"],
@@ -763,7 +767,7 @@ def main():
             result["cpu_baseline"] = None
         print(json.dumps(result))
         return
-    w = L8B
+    w = dataclasses.replace(L8B, batch=args.batch) if args.batch else L8B
     result = run_step(w, args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
