@@ -23,7 +23,10 @@ Every device buffer is allocated once, up front (section 2B: pre-allocated, no f
 All numerical work runs in libslide (HIP kernels and the C++ AdamW); this module only orders
 calls on streams and threads. PyTorch provides device memory, pinned host memory and streams.
 """
+import dataclasses
+import json
 import mmap
+import os
 import threading
 import time
 from dataclasses import dataclass, field
@@ -385,6 +388,65 @@ class SlideEngine:
         out = np.empty(prm.n, np.float32)
         self.tier.read(prm.tier[0], out)
         return out
+
+    # ------------------------------------------------------------------ checkpoint
+    def _blocks(self):
+        out = {"embed": self.embed, "w_final": self.final, "lm_head": self.lm}
+        out.update({f"layer{i}": p for i, p in enumerate(self.layers)})
+        return out
+
+    def _state(self, prm, kind):
+        """fp32 master ("master"), first ("m") or second ("v") moment of a block as a numpy copy,
+        from host memory or the disk tier."""
+        arr = {"master": prm.master, "m": prm.m, "v": prm.v}[kind]
+        if arr is not None:
+            return arr.numpy().copy()
+        out = np.empty(prm.n, np.float32)
+        self.tier.read(prm.tier[{"master": 0, "m": 1, "v": 2}[kind]], out)
+        return out
+
+    def save_checkpoint(self, path):
+        """Write the host state after every pending update: each block's fp32 master weights and
+        AdamW moments as .npy files under `path`, and a manifest with the step count, the model
+        shape and the hyper-parameters. The bf16 compute copies are not saved; they are the
+        rounding of the master weights."""
+        self.wait_updates()
+        os.makedirs(path, exist_ok=True)
+        blocks = self._blocks()
+        for name, prm in blocks.items():
+            for kind in ("master", "m", "v"):
+                np.save(os.path.join(path, f"{name}.{kind}.npy"), self._state(prm, kind),
+                        allow_pickle=False)
+        manifest = dict(step=self.step_count, spec=dataclasses.asdict(self.spec),
+                        hp=dict(lr=self.hp.lr, beta1=self.hp.beta1, beta2=self.hp.beta2,
+                                eps=self.hp.eps, weight_decay=self.hp.weight_decay),
+                        blocks={name: prm.n for name, prm in blocks.items()})
+        with open(os.path.join(path, "manifest.json"), "w") as f:
+            json.dump(manifest, f, indent=1)
+
+    def load_checkpoint(self, path):
+        """Restore what save_checkpoint wrote (same model shape): master weights, moments, the
+        derived compute copies and the step count. The next step continues exactly as the
+        saved run would have."""
+        self.wait_updates()
+        with open(os.path.join(path, "manifest.json")) as f:
+            manifest = json.load(f)
+        if manifest["spec"] != dataclasses.asdict(self.spec):
+            raise ValueError(f"checkpoint of {manifest['spec']}, engine is {self.spec}")
+        blocks = self._blocks()
+        if manifest["blocks"] != {name: prm.n for name, prm in blocks.items()}:
+            raise ValueError("checkpoint block sizes differ from the engine's")
+        for name, prm in blocks.items():
+            ld = lambda kind: np.load(os.path.join(path, f"{name}.{kind}.npy"), allow_pickle=False)
+            self._set_master(prm, torch.from_numpy(ld("master")))
+            for kind, idx in (("m", 1), ("v", 2)):
+                arr = ld(kind)
+                if prm.tier is None:
+                    getattr(prm, kind).copy_(torch.from_numpy(arr))
+                else:
+                    self.tier.write(prm.tier[idx], arr)
+        self._upload_all_resident()
+        self.step_count = int(manifest["step"])
 
     def tier_stats(self):
         """Traffic and time of the disk tier so far (None without a tier)."""

@@ -223,3 +223,55 @@ def test_disk_tier_of_optimizer_state_changes_no_bit(tmp_path, w):
         for x, y in zip(pa["layers"], pt["layers"]):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
     assert not (tmp_path / "state.bin").exists()
+
+
+def test_checkpoint_resume_is_bit_exact(tmp_path):
+    """Two steps in one run equal one step, a checkpoint, a new engine that loads it and one more
+    step, bit for bit; also when the resumed engine keeps its optimizer state in the disk tier."""
+    w = SMALL
+    print(f"checkpoint/resume: {w.name}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    toks = [tokens(w.batch, w.seq, w.vocab, seed=30 + s) for s in range(2)]
+
+    def engine(**kw):
+        return SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=HP, adam_threads=3,
+                           ce_chunk=256, **kw)
+
+    def load(e):
+        e.load_params(params["embed"].f32, _flat_layers(params, w), params["w_final"].f32,
+                      params["lm_head"].f32)
+
+    ref = engine()
+    try:
+        load(ref)
+        losses = []
+        for t in toks:
+            ref.step(t)
+            losses.append(ref.loss())
+        pref = ref.master_params()
+    finally:
+        ref.close()
+    first = engine()
+    try:
+        load(first)
+        first.step(toks[0])
+        l0 = first.loss()
+        first.save_checkpoint(tmp_path / "ck")
+    finally:
+        first.close()
+    for kw in ({}, {"state_tier": str(tmp_path / "state.bin")}):
+        e = engine(**kw)
+        try:
+            e.load_checkpoint(tmp_path / "ck")
+            assert e.step_count == 1
+            e.step(toks[1])
+            l1 = e.loss()
+            pe = e.master_params()
+        finally:
+            e.close()
+        print(f"  {sorted(kw)}: losses {[l0, l1]} vs uninterrupted {losses}", flush=True)
+        assert [l0, l1] == losses
+        for k in ("embed", "w_final", "lm_head"):
+            assert np.array_equal(pref[k].view(np.uint32), pe[k].view(np.uint32)), k
+        for x, y in zip(pref["layers"], pe["layers"]):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
