@@ -44,7 +44,7 @@ enum {
   SLIDE_E_STATE = -5,        /* slot-ring call not allowed in the slot's current state */
   SLIDE_E_TIMEOUT = -6,      /* a bounded host wait ran out */
   SLIDE_E_UNSUPPORTED = -7,  /* valid request this build does not implement */
-  SLIDE_E_NONFINITE = -8,    /* reserved: non-finite value detected where checked */
+  SLIDE_E_NONFINITE = -8,    /* non-finite gradient found where checked (engine option) */
   SLIDE_E_IO = -9            /* a file operation of the disk tier failed (errno in the message) */
 };
 
@@ -258,6 +258,13 @@ int slide_slot_ring_destroy(slide_ring* r);
 /* Host engine only: make the next `count` copies fail (fail_mode 1) or never complete
  * (fail_mode 2). Returns SLIDE_E_UNSUPPORTED for the HIP engine. */
 int slide_slot_ring_inject_fault(slide_ring* r, int fail_mode, int count);
+
+/* Non-finite check of a gradient before it leaves the GPU: *count_dev (device memory, 4 bytes,
+ * overwritten) receives the number of NaN or infinite elements of x[n] (dtype SLIDE_BF16 or
+ * SLIDE_F32; x 16-byte aligned). The pages leave failure handling open; an update computed from
+ * such a gradient would corrupt the fp32 master weights, so the engine checks each layer's
+ * gradient with this call and refuses the update (SLIDE_E_NONFINITE) instead of applying it. */
+int slide_nonfinite_count(const void* x, int dtype, size_t n, uint32_t* count_dev, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * CPU AdamW (the per-layer host optimizer, "Layer-Adam": summary, section 2B).

@@ -21,6 +21,7 @@ __all__ = [
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "StateTier", "slide_tier_region_bytes",
+    "slide_nonfinite_count",
     "SLIDE_TIER_DIRECT", "SLIDE_TIER_UNLINK", "slide_prof_enable", "slide_prof_reset",
     "slide_prof_read", "dtype_code", "layer_cfg",
 ]
@@ -263,6 +264,12 @@ def slide_cpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, n_threads=0):
     """p, m, v: float32 host buffers; g: host bf16 (uint16) or float32; hp: AdamWHp."""
     call("slide_cpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
          ctypes.byref(hp), n_threads)
+
+
+def slide_nonfinite_count(x, dtype, n, count_dev, stream=None):
+    """count_dev: a 4-byte device buffer (e.g. an int32 tensor element) that receives the number
+    of NaN or infinite elements of x[:n]."""
+    call("slide_nonfinite_count", _p(x), dtype, n, _p(count_dev), _s(stream))
 
 
 # ------------------------------------------------------------------------------ disk tier

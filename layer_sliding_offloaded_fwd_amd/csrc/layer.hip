@@ -318,6 +318,15 @@ extern "C" int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, c
   return rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ws, (hipStream_t)stream);
 }
 
+extern "C" int slide_nonfinite_count(const void* x, int dtype, size_t n, uint32_t* count_dev,
+                                     void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "nonfinite_count: bad dtype");
+  SLIDE_REQUIRE(count_dev && (n == 0 || x), SLIDE_E_ARG, "nonfinite_count: null pointer");
+  SLIDE_REQUIRE(n == 0 || aligned16(x), SLIDE_E_ARG, "nonfinite_count: x must be 16-byte aligned");
+  SLIDE_REQUIRE(((uintptr_t)count_dev & 3) == 0, SLIDE_E_ARG, "nonfinite_count: count must be 4-byte aligned");
+  return nonfinite_count(x, n, dtype, count_dev, (hipStream_t)stream);
+}
+
 extern "C" int slide_rope(void* qkv, int B, int S, int nq, int nkv, int d, float theta,
                           int inverse, int dtype, void* ws, size_t ws_bytes, void* stream) {
   SLIDE_TRY(attention_check(B, S, nq, nkv, d, dtype));

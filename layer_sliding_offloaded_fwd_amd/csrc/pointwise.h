@@ -25,6 +25,8 @@ int embed_fwd(const void* E, const int32_t* tok, void* x, int N, int H, int V, i
 size_t embed_bwd_ws(int N, int V);
 int embed_bwd(const void* dx, const int32_t* tok, void* dE, int N, int H, int V, int dtype,
               void* ws, hipStream_t st);
+// *count (device) = number of NaN or infinite elements of x[n]
+int nonfinite_count(const void* x, size_t n, int dtype, uint32_t* count, hipStream_t st);
 int fill_f32(float* p, size_t n, float v, hipStream_t st);
 int fill_zero(void* p, size_t n, int dtype, hipStream_t st);
 int convert_from_f32(const float* src, void* dst, size_t n, int dtype, hipStream_t st);

@@ -306,6 +306,41 @@ __global__ __launch_bounds__(256) void embed_sum_kernel(const T* __restrict__ dx
 }
 
 // ---------------------------------------------------------------- helpers
+// ---------------------------------------------------------------- non-finite count
+// Number of NaN or infinite elements (exponent bits all ones): 8 elements per thread and step
+// (one 16-byte load for bf16, two for fp32) in a grid-stride loop, a wave sum, one integer atomic
+// per wave (exact, whatever the order).
+template <typename T>
+__global__ __launch_bounds__(256) void nonfinite_count_kernel(const T* __restrict__ x, size_t n,
+                                                              uint32_t* __restrict__ count) {
+  const size_t n8 = n / 8;
+  uint32_t c = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    if constexpr (sizeof(T) == 2) {
+      const uint4 u = *(const uint4*)(x + i * 8);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        c += ((w[k] & 0x7F80u) == 0x7F80u) + ((w[k] & 0x7F800000u) == 0x7F800000u);
+    } else {
+      const uint4 a = *(const uint4*)(x + i * 8), b = *(const uint4*)(x + i * 8 + 4);
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c += (w[k] & 0x7F800000u) == 0x7F800000u;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {   // the last n % 8 elements
+    const size_t i = n8 * 8 + threadIdx.x;
+    if constexpr (sizeof(T) == 2) c += (((const uint16_t*)x)[i] & 0x7F80u) == 0x7F80u;
+    else c += (((const uint32_t*)x)[i] & 0x7F800000u) == 0x7F800000u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(count, c);
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -382,6 +417,21 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
     hipLaunchKernelGGL(reduce_rows_kernel<float>, g2, b2, 0, st, part, (float*)dw,
                        std::max(parts, 1), H);
   return check_launch("rmsnorm_dw");
+}
+
+int nonfinite_count(const void* x, size_t n, int dtype, uint32_t* count, hipStream_t st) {
+  ProfScope ps("nonfinite_count", st);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, count);
+  if (n > 0) {
+    const unsigned grid = std::min<size_t>(std::max<size_t>(blocks_for(n / 8, 256), 1), 2048);
+    if (dtype == SLIDE_BF16)
+      hipLaunchKernelGGL(nonfinite_count_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
+                         (const bf16_t*)x, n, count);
+    else
+      hipLaunchKernelGGL(nonfinite_count_kernel<float>, dim3(grid), dim3(256), 0, st,
+                         (const float*)x, n, count);
+  }
+  return check_launch("nonfinite_count");
 }
 
 int rope_tables(float* cos_t, float* sin_t, int S, int d, float theta, hipStream_t st) {

@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from ._capi import SLIDE_BF16, SLIDE_F32
+from ._capi import SLIDE_BF16, SLIDE_E_NONFINITE, SLIDE_F32
 
 
 @dataclass(frozen=True)
@@ -67,12 +67,13 @@ def _align(n, a=256):
 
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step", "priority", "seq", "tier")
+                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite")
 
     def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None):
         self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
         self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
         self.tier = tier      # (p, m, v) offsets in the disk tier (None: in host memory)
+        self.nonfinite = None  # (pinned count array, index) when the gradient is checked
         self.seq = 0
         self.done = threading.Event()
         self.t_start = self.t_end = self.t_ready = 0.0
@@ -157,7 +158,7 @@ class SlideEngine:
     def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
-                 tier_layers=None, tier_chunk=0, tier_io_threads=8):
+                 tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -171,6 +172,10 @@ class SlideEngine:
           is opened with O_DIRECT where the file system allows and unlinked at once, so it
           takes disk space only while the engine lives. tier_chunk (elements) and
           tier_io_threads size its streaming.
+        check_finite: count the NaN / infinite elements of every gradient on the GPU before it
+          is flushed; the CPU worker then refuses the update of a block whose gradient is not
+          finite (SlideError SLIDE_E_NONFINITE, raised by the next wait), so the fp32 master
+          weights are never overwritten from it.
         """
         assert spec.dtype in ("bf16", "f32")
         if activations is None:
@@ -251,6 +256,14 @@ class SlideEngine:
 
         # device memory, allocated once
         dev = self.device
+        self.check_finite = check_finite
+        if check_finite:
+            names = ([f"layer{i}" for i in range(self.L)] + ["w_final"]
+                     + [f"lm_head{ci}" for ci in range(self.lm_nch)]
+                     + [f"embed{ci}" for ci in range(self.emb_nch)])
+            self.nf_index = {n: k for k, n in enumerate(names)}
+            self.nf_dev = torch.zeros(len(names), dtype=torch.int32, device=dev)
+            self.nf_host = self.pinned.tensor(len(names), torch.int32)
         self.ring_mem = torch.empty(self.n_slots * 2 * self.w_bytes, dtype=torch.uint8, device=dev)
         self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
                                self.h2d, self.d2h)
@@ -519,6 +532,14 @@ class SlideEngine:
                 self.jobs.remove(job)
             try:
                 if self.worker_error is None:
+                    if job.nonfinite is not None:
+                        arr, k = job.nonfinite
+                        bad = int(arr[k])
+                        if bad:
+                            raise B.SlideError(
+                                SLIDE_E_NONFINITE, "slide_nonfinite_count",
+                                f"{job.name}: {bad} NaN or infinite gradient elements in step "
+                                f"{job.step}; its update was not applied")
                     job.t_ready = time.perf_counter()
                     if job.tier is None:
                         B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
@@ -540,8 +561,28 @@ class SlideEngine:
         out = prm.shared if prm.dtype == "bf16" else None
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
                    self.step_count, priority, post, prm.tier)
+        self._nf_attach(job)
         prm.job = job
         return self._enqueue(job)
+
+    # ------------------------------------------------------------------ non-finite check
+    def _nf_count(self, grad, n, name):
+        """On the compute stream, after the gradient is complete: count its non-finite
+        elements into the block's device counter (check_finite only)."""
+        if self.check_finite:
+            k = self.nf_index[name]
+            B.slide_nonfinite_count(grad, self.code, n, self.nf_dev[k:k + 1], self.compute)
+
+    def _nf_fetch(self, name):
+        """On the D2H stream, ahead of the gradient copy: the counter to pinned host memory, so
+        the gradient's arrival implies the count's."""
+        if self.check_finite:
+            k = self.nf_index[name]
+            self.nf_host[k:k + 1].copy_(self.nf_dev[k:k + 1], non_blocking=True)
+
+    def _nf_attach(self, job):
+        if self.check_finite and job.name in self.nf_index:
+            job.nonfinite = (self.nf_host, self.nf_index[job.name])
 
     def _enqueue(self, job):
         with self.jobs_cv:
@@ -598,10 +639,12 @@ class SlideEngine:
     def _flush_resident(self, prm, name, priority):
         """D2H of a resident block's device gradient after the compute stream, then AdamW, then
         the refreshed device copy goes back up on the H2D stream."""
+        self._nf_count(prm.grad, prm.n, name)
         ev_c = torch.cuda.Event()
         ev_c.record(self.compute)
         self.d2h.wait_event(ev_c)
         with torch.cuda.stream(self.d2h):
+            self._nf_fetch(name)
             dst = prm.grad_host.view(torch.bfloat16) if prm.dtype == "bf16" else prm.grad_host
             dst.copy_(prm.grad, non_blocking=True)
             done = torch.cuda.Event()
@@ -651,10 +694,12 @@ class SlideEngine:
         event)."""
         H = self.spec.hidden
         sl = slice(r0 * H, r1 * H)
+        self._nf_count(prm.grad[sl], (r1 - r0) * H, name)
         ev_c = torch.cuda.Event()
         ev_c.record(self.compute)
         self.d2h.wait_event(ev_c)
         with torch.cuda.stream(self.d2h):
+            self._nf_fetch(name)
             dst = prm.grad_host[sl]
             dst = dst.view(torch.bfloat16) if prm.dtype == "bf16" else dst
             dst.copy_(prm.grad[sl], non_blocking=True)
@@ -673,6 +718,7 @@ class SlideEngine:
         out = prm.shared[sl] if prm.dtype == "bf16" else None
         job = _Job(name, done, prm.master[sl], prm.grad_host[sl], prm.m[sl], prm.v[sl], out,
                    (r1 - r0) * H, self.step_count, priority, upload)
+        self._nf_attach(job)
         rec["other_jobs"].append(job)
         return job, done
 
@@ -829,6 +875,11 @@ class SlideEngine:
             if host_x and i - K >= 0:          # slot i % K is free again: input i - K comes back
                 self._x_reload(i - K)
             e_b = self._ev(c) if self.timeline else None
+            if self.check_finite:
+                self._nf_count(g, self.P, f"layer{i}")
+                self.d2h.wait_event(self._ev(c))
+                with torch.cuda.stream(self.d2h):
+                    self._nf_fetch(f"layer{i}")
             ticket = self.ring.flush(s, self.layers[i].grad_host, c)
             if self.timeline:
                 rec["layers"].setdefault(i, {})["bwd"] = (e_a, e_b)

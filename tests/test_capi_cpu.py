@@ -63,6 +63,17 @@ def test_validation_errors_before_any_launch():
     assert e.value.code == _capi.SLIDE_E_SHAPE
 
 
+def test_nonfinite_count_validation():
+    cnt = np.zeros(1, np.int32)
+    for args, code in [((None, sl.SLIDE_BF16, 16, cnt.ctypes.data), _capi.SLIDE_E_ARG),
+                       ((cnt.ctypes.data, 7, 16, cnt.ctypes.data), _capi.SLIDE_E_ARG),
+                       ((cnt.ctypes.data + 2, sl.SLIDE_F32, 16, cnt.ctypes.data), _capi.SLIDE_E_ARG),
+                       ((cnt.ctypes.data, sl.SLIDE_F32, 16, None), _capi.SLIDE_E_ARG)]:
+        with pytest.raises(sl.SlideError) as e:
+            sl.slide_nonfinite_count(*args)
+        assert e.value.code == code
+
+
 def test_ce_phase_validation():
     ce = sl.CeCfg(4096, 128256, 8192, sl.SLIDE_BF16)
     assert sl.slide_lmhead_ce_n_chunks(ce) == 16            # 15 full chunks and one of 5376 rows

@@ -275,3 +275,41 @@ def test_checkpoint_resume_is_bit_exact(tmp_path):
             assert np.array_equal(pref[k].view(np.uint32), pe[k].view(np.uint32)), k
         for x, y in zip(pref["layers"], pe["layers"]):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_nonfinite_gradient_check(tmp_path):
+    """With check_finite the results are the same bits as without; a layer weight set to
+    infinity makes that step's gradients non-finite, and the engine refuses their updates with
+    SLIDE_E_NONFINITE instead of writing them into the fp32 master weights."""
+    from layer_sliding_offloaded_fwd_amd._capi import SLIDE_E_NONFINITE, SlideError
+    w = SMALL
+    print(f"non-finite check: {w.name}", flush=True)
+    la, pa = _run(3, False)
+    lc, pc = _run(3, False, check_finite=True)
+    assert la == lc
+    for k in ("embed", "w_final", "lm_head"):
+        assert np.array_equal(pa[k].view(np.uint32), pc[k].view(np.uint32)), k
+    for x, y in zip(pa["layers"], pc["layers"]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+    params = model_params(w, seed=0, gain_std=0.1)
+    layers = _flat_layers(params, w)
+    layers[2] = layers[2].copy()
+    layers[2][w.layer.hidden + 5] = np.inf          # one entry of layer 2's Wqkv
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=HP, adam_threads=3, ce_chunk=256,
+                      check_finite=True)
+    try:
+        eng.load_params(params["embed"].f32, layers, params["w_final"].f32,
+                        params["lm_head"].f32)
+        eng.step(tokens(w.batch, w.seq, w.vocab, seed=10))
+        with pytest.raises(SlideError) as e:
+            eng.wait_updates()
+        print(f"  raised: {e.value}", flush=True)
+        assert e.value.code == SLIDE_E_NONFINITE
+        # every update was refused: each master is still the loaded value (or its infinity)
+        for i, prm in enumerate(eng.layers):
+            assert np.array_equal(prm.master.numpy().view(np.uint32),
+                                  layers[i].astype(np.float32).view(np.uint32)), i
+    finally:
+        eng.worker_error = None
+        eng.close()

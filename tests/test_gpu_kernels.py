@@ -191,3 +191,26 @@ def test_embedding_fwd_bwd_repeated_tokens(dtype):
     torch.cuda.synchronize()
     assert torch.equal(dE.view(torch.int16) if dtype == "bf16" else dE,
                        dE2.view(torch.int16) if dtype == "bf16" else dE2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [0, 5, 8, 1000003])
+def test_nonfinite_count_exact(dtype, n):
+    """Exact count of NaN / +inf / -inf among finite values of every size class (including the
+    largest finite value and denormals), with a ragged tail; the counter is overwritten."""
+    print(f"nonfinite count {dtype} n={n}", flush=True)
+    rng = _rng(40)
+    a = rng.standard_normal(n).astype(np.float32)
+    big = 3.3e38 if dtype == "bf16" else 3.4e38
+    special = np.array([np.nan, np.inf, -np.inf, big, -big, 1e-40, 0.0, -0.0], np.float32)
+    if n:
+        idx = rng.choice(n, size=min(n, 64), replace=False)
+        a[idx] = special[rng.integers(0, len(special), len(idx))]
+        a[-1] = np.inf                                  # the last element sits in the tail
+    t = dev(a, dtype) if n else empty((8,), dtype)
+    want = int(np.sum(~np.isfinite(_round(a, dtype)))) if n else 0
+    cnt = torch.full((1,), 12345, dtype=torch.int32, device=DEV)
+    sl.slide_nonfinite_count(t, sl.dtype_code(dtype), n, cnt, stream())
+    torch.cuda.synchronize()
+    print(f"  count {int(cnt.item())} expected {want}", flush=True)
+    assert int(cnt.item()) == want
