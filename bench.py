@@ -153,6 +153,9 @@ def _parse():
     ap.add_argument("--tier-layers", type=int, default=0,
                     help="with --state-tier: how many layers (the last ones) keep their state "
                          "in the file (default: all)")
+    ap.add_argument("--overlap-table", default=None, metavar="PATH",
+                    help="write the last timed step's per-layer T_bwd, T_d2h and T_update (the "
+                         "pages' overlap condition, layer by layer) as a CSV file")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
@@ -389,6 +392,8 @@ def run_step(w, args):
     mfma_util_alg = 100.0 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     mfma_util_exec = 100.0 * l_exe / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     ana = eng.analyse(eng.records[-args.steps:])
+    if args.overlap_table:
+        _write_overlap_table(args.overlap_table, ana["layers"])
     tier = _tier_report(eng, tier0, args.steps, step_s) if eng.tier is not None else None
     eng.close()
     host = host_roofline(w, threads, step_s)
@@ -449,6 +454,22 @@ def run_step(w, args):
         "kernels": kernels,
         "init_s": round(t_init, 1),
     }
+
+
+def _write_overlap_table(path, per_layer):
+    """Per layer of the last timed step: its backward time, the D2H of its gradients, its CPU
+    update, and whether the backward of the layer below covers them (the pages' condition)."""
+    last = max(li["step"] for li in per_layer)
+    rows = sorted((li for li in per_layer if li["step"] == last), key=lambda li: -li["layer"])
+    by = {li["layer"]: li for li in rows}
+    with open(path, "w") as f:
+        f.write("layer,t_bwd_ms,t_d2h_ms,t_update_ms,t_bwd_next_layer_ms,covered\n")
+        for li in rows:
+            nxt = by.get(li["layer"] - 1)
+            tb = nxt["t_bwd_ms"] if nxt else float("nan")
+            ok = nxt is not None and tb >= li["t_d2h_ms"] + li["t_update_ms"]
+            f.write(f"{li['layer']},{li['t_bwd_ms']:.3f},{li['t_d2h_ms']:.3f},"
+                    f"{li['t_update_ms']:.3f},{tb:.3f},{int(ok)}\n")
 
 
 def _tier_report(eng, before, steps, step_s):
