@@ -612,7 +612,13 @@ class SlideEngine:
             self._wait_job(self.emb_job[ci])
 
     def close(self):
-        self.wait_updates()
+        """Wait for the pending updates and free every resource. A worker error is raised after
+        the clean-up (the updates after it were not applied)."""
+        err = None
+        try:
+            self.wait_updates()
+        except Exception as e:  # noqa: BLE001 - re-raised below, after the clean-up
+            err = e
         with self.jobs_cv:
             self.worker_stop = True
             self.jobs_cv.notify_all()
@@ -625,6 +631,8 @@ class SlideEngine:
         self.pinned.free()
         if self.tier is not None:
             self.tier.close()
+        if err is not None:
+            raise err
 
     # ------------------------------------------------------------------ step
     def _sync(self):

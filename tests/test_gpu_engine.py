@@ -298,6 +298,7 @@ def test_nonfinite_gradient_check(tmp_path):
     layers[2][w.layer.hidden + 5] = np.inf          # one entry of layer 2's Wqkv
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=HP, adam_threads=3, ce_chunk=256,
                       check_finite=True)
+    closed = False
     try:
         eng.load_params(params["embed"].f32, layers, params["w_final"].f32,
                         params["lm_head"].f32)
@@ -310,6 +311,13 @@ def test_nonfinite_gradient_check(tmp_path):
         for i, prm in enumerate(eng.layers):
             assert np.array_equal(prm.master.numpy().view(np.uint32),
                                   layers[i].astype(np.float32).view(np.uint32)), i
+        # close() frees everything and raises the error once more
+        with pytest.raises(SlideError):
+            eng.close()
+        closed = True
     finally:
-        eng.worker_error = None
-        eng.close()
+        if not closed:
+            try:
+                eng.close()
+            except SlideError:
+                pass
