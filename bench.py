@@ -345,7 +345,8 @@ def run_step(w, args):
             sys.exit(1)
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True,
-                      activations=args.activations, **tier_kw)
+                      activations=args.activations, keep_records=args.steps + args.warmup,
+                      **tier_kw)
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
@@ -391,7 +392,7 @@ def run_step(w, args):
     l_exe = sum(exe[n] * kernels[n]["launches"] for n in layer_names)
     mfma_util_alg = 100.0 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
     mfma_util_exec = 100.0 * l_exe / lt / 1e12 / PEAK_BF16_TFLOPS if lt else 0.0
-    ana = eng.analyse(eng.records[-args.steps:])
+    ana = eng.analyse(list(eng.records)[-args.steps:])
     if args.overlap_table:
         _write_overlap_table(args.overlap_table, ana["layers"])
     tier = _tier_report(eng, tier0, args.steps, step_s) if eng.tier is not None else None

@@ -23,6 +23,7 @@ Every device buffer is allocated once, up front (section 2B: pre-allocated, no f
 All numerical work runs in libslide (HIP kernels and the C++ AdamW); this module only orders
 calls on streams and threads. PyTorch provides device memory, pinned host memory and streams.
 """
+import collections
 import dataclasses
 import json
 import mmap
@@ -158,7 +159,8 @@ class SlideEngine:
     def __init__(self, spec: ModelSpec, batch, seq, n_slots=3, ce_chunk=8192, hp=AdamW(),
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
-                 tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False):
+                 tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False,
+                 keep_records=64):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -176,6 +178,8 @@ class SlideEngine:
           is flushed; the CPU worker then refuses the update of a block whose gradient is not
           finite (SlideError SLIDE_E_NONFINITE, raised by the next wait), so the fp32 master
           weights are never overwritten from it.
+        keep_records: how many of the latest steps' records (events, job timings) are kept for
+          analyse(); older ones are dropped, so a long run does not accumulate them.
         """
         assert spec.dtype in ("bf16", "f32")
         if activations is None:
@@ -320,7 +324,7 @@ class SlideEngine:
         for t in self.workers:
             t.start()
         self.step_count = 0
-        self.records = []
+        self.records = collections.deque(maxlen=max(1, keep_records))
 
     # ------------------------------------------------------------------ parameters
     def load_params(self, embed, layers, w_final, lm_head):
