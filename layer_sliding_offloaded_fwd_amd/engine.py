@@ -932,9 +932,11 @@ class SlideEngine:
             recs = [recs]
         L = self.L
         gpu_iv, work_iv, per_layer = [], [], []
+        cpu_all = 0.0
         for rec in recs:
-            for j in rec["jobs"]:
+            for j in rec["jobs"] + rec["other_jobs"]:
                 j.done.wait()
+            cpu_all += sum(j.t_end - j.t_start for j in rec["jobs"] + rec["other_jobs"])
             ev0, t0 = rec["ev0"], rec["host_t0"]
             to_host = lambda e: t0 + ev0.elapsed_time(e) / 1e3
             for i, lr in rec["layers"].items():
@@ -990,4 +992,5 @@ class SlideEngine:
             t_d2h_total_ms=sum(li["t_d2h_ms"] for li in per_layer) / n,
             predicate_layers_met=met / n,
             gpu_ms=sum(r["ev0"].elapsed_time(r["ev_end"]) for r in recs) / n,
+            t_update_all_ms=cpu_all * 1e3 / n,
             layers=per_layer)
