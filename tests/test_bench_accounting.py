@@ -69,3 +69,36 @@ def test_step_host_bytes():
     assert adam == pytest.approx(224.8e9, rel=1e-3)
     assert h2d == pytest.approx(28.7e9, rel=2e-3)
     assert d2h == pytest.approx(16.06e9, rel=1e-3)
+
+
+def test_overlap_table_checks_the_pages_condition(tmp_path):
+    """Layer i is covered when the backward of layer i-1 takes at least T_d2h(i) + T_update(i);
+    only the last step's rows are written, from the last layer down."""
+    rows = []
+    for step in (1, 2):
+        for i, (tb, td, tu) in enumerate([(10.0, 3.0, 6.0), (9.0, 3.0, 6.0), (8.0, 4.0, 5.0)]):
+            rows.append(dict(step=step, layer=i, t_bwd_ms=tb + step, t_d2h_ms=td, t_update_ms=tu))
+    path = tmp_path / "t.csv"
+    bench._write_overlap_table(str(path), rows)
+    lines = path.read_text().strip().split("\n")
+    assert lines[0].startswith("layer,t_bwd_ms")
+    got = [line.split(",") for line in lines[1:]]
+    assert [int(r[0]) for r in got] == [2, 1, 0]
+    # layer 2: below it layer 1 takes 11 >= 4 + 5; layer 1: layer 0 takes 12 >= 3 + 6; layer 0:
+    # nothing below
+    assert [int(r[-1]) for r in got] == [1, 1, 0]
+    assert got[0][4] == "11.000" and got[2][4] == "nan"
+
+
+def test_tier_report_rates():
+    class Eng:
+        tier_layers = [30, 31]
+        def tier_stats(self):
+            return dict(bytes_read=3 * 10**9 + 100, bytes_written=3 * 10**9 + 100, busy_s=2.5,
+                        stall_s=1.0, direct=True, capacity=5 * 10**9, chunk=4 << 20)
+    before = dict(bytes_read=100, bytes_written=100, busy_s=0.5, stall_s=0.0)
+    r = bench._tier_report(Eng(), before, steps=2, step_s=2.0)
+    assert r["read_bytes_per_step"] == r["write_bytes_per_step"] == 1.5e9
+    assert r["update_s_per_step"] == 1.0 and r["io_wait_s_per_step"] == 0.5
+    assert r["read_plus_write_gbs"] == 3.0          # 6 GB over 2 s of tier calls
+    assert r["frac_of_step"] == 0.5 and r["layers"] == 2 and r["direct_io"] is True
