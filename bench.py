@@ -432,6 +432,9 @@ def run_step(w, args):
                     "t_update_total_ms": round(ana["t_update_total_ms"], 1),
                     # every CPU update of the step (layers, embedding, final gain, LM head)
                     "t_update_all_blocks_ms": round(ana["t_update_all_ms"], 1),
+                    # GPU idle between a backward's end and the next layer-0 forward (median)
+                    "step_boundary_gap_ms": (round(ana["boundary_ms"], 1)
+                                             if ana["boundary_ms"] is not None else None),
                     "layers_meeting_T_bwd_ge_T_d2h_plus_T_update": ana["predicate_layers_met"],
                     "gpu_span_ms_per_step": round(ana["gpu_ms"], 1)},
         # CPU AdamW of the layer parameters: fp32 master, m, v read and written (24 B), the

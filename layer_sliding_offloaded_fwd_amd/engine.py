@@ -922,6 +922,19 @@ class SlideEngine:
         return float(self.loss_dev.item())
 
     # ------------------------------------------------------------------ timeline analysis
+    @staticmethod
+    def _boundary_gaps(recs):
+        """Median GPU time between the end of a step's backward and the start of the next step's
+        layer-0 forward (the iteration-boundary bubble: the next forward needs the embedding and
+        layer 0 first, and they are the last to get their gradients), over consecutive records;
+        None with fewer than two."""
+        gaps = []
+        for a, b in zip(recs[:-1], recs[1:]):
+            f0 = b["layers"].get(0, {}).get("fwd")
+            if b["step"] == a["step"] + 1 and f0 is not None:
+                gaps.append(a["ev_end"].elapsed_time(f0[0]))
+        return float(np.median(gaps)) if gaps else None
+
     def analyse(self, recs):
         """Timeline of recorded steps (timeline=True): per-layer backward, gradient D2H and CPU
         update times; the pages' per-layer overlap predicate T_bwd >= T_d2h + T_update (figure 4
@@ -993,4 +1006,5 @@ class SlideEngine:
             predicate_layers_met=met / n,
             gpu_ms=sum(r["ev0"].elapsed_time(r["ev_end"]) for r in recs) / n,
             t_update_all_ms=cpu_all * 1e3 / n,
+            boundary_ms=self._boundary_gaps(recs),
             layers=per_layer)
