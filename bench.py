@@ -156,6 +156,10 @@ def _parse():
     ap.add_argument("--overlap-table", default=None, metavar="PATH",
                     help="write the last timed step's per-layer T_bwd, T_d2h and T_update (the "
                          "pages' overlap condition, layer by layer) as a CSV file")
+    ap.add_argument("--trace", default=None, metavar="PREFIX",
+                    help="write PREFIX.json (Chrome trace of the timed steps: GPU layer and CE "
+                         "intervals, gradient D2H, CPU updates) and PREFIX.txt (text timeline of "
+                         "the last two steps, 10 ms per column)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
     ap.add_argument("--adam-threads", type=int, default=0,
@@ -395,6 +399,10 @@ def run_step(w, args):
     ana = eng.analyse(list(eng.records)[-args.steps:])
     if args.overlap_table:
         _write_overlap_table(args.overlap_table, ana["layers"])
+    if args.trace:
+        recs = list(eng.records)[-args.steps:]
+        eng.export_trace(recs, args.trace + ".json")
+        _write_text_timeline(eng, recs[-3:], args.trace + ".txt")
     tier = _tier_report(eng, tier0, args.steps, step_s) if eng.tier is not None else None
     eng.close()
     host = host_roofline(w, threads, step_s)
@@ -460,6 +468,19 @@ def run_step(w, args):
         "kernels": kernels,
         "init_s": round(t_init, 1),
     }
+
+
+def _write_text_timeline(eng, recs, path, ms_per_col=10.0):
+    """Text lanes from the start of the second of `recs` to the end: GPU (F layer forward, B
+    layer backward, C CE), D2H (# gradient copies) and CPU (u layer, e embedding, l LM head, f
+    final gain updates), with the first step's updates included where they run into the
+    second; ':' marks a partly busy column."""
+    tl = eng.timeline_of(recs)
+    t0 = (recs[1]["host_t0"] - recs[0]["host_t0"]) * 1e3 if len(recs) > 1 else 0.0
+    with open(path, "w") as f:
+        f.write(f"steps {recs[min(1, len(recs) - 1)]['step']}-{recs[-1]['step']}, "
+                f"{ms_per_col:g} ms per column\n")
+        f.write(eng.render_timeline(tl, ms_per_col, t_start=t0) + "\n")
 
 
 def _write_overlap_table(path, per_layer):

@@ -922,6 +922,79 @@ class SlideEngine:
         return float(self.loss_dev.item())
 
     # ------------------------------------------------------------------ timeline analysis
+    def timeline_of(self, recs):
+        """Intervals of consecutive recorded steps (timeline=True), in ms from the first one's
+        start: GPU layer forwards ("F"), backwards ("B") and CE phases ("C"); the layers'
+        gradient D2H copies ("#"); and the CPU updates ("u" layer, "e" embedding, "l" LM head,
+        "f" final gain), each under the step that produced its gradient -- the pages' timeline
+        figures (paper page, figures 3 and 5) for this build."""
+        if isinstance(recs, dict):
+            recs = [recs]
+        origin = recs[0]["host_t0"]
+        gpu, d2h, cpu = [], [], []
+        kind = {"layer": "u", "embed": "e", "lm_head": "l", "w_final": "f"}
+        for rec in recs:
+            for j in rec["jobs"] + rec["other_jobs"]:
+                j.done.wait()
+            ev0, shift = rec["ev0"], (rec["host_t0"] - origin) * 1e3
+            gms = lambda e, ev0=ev0, shift=shift: shift + ev0.elapsed_time(e)
+            for i, lr in sorted(rec["layers"].items()):
+                for key, ch in (("fwd", "F"), ("bwd", "B")):
+                    if key in lr:
+                        gpu.append((ch, f"step{rec['step']} layer{i} {key}", gms(lr[key][0]),
+                                    gms(lr[key][1])))
+            for a, b in rec.get("ce_iv", []):
+                gpu.append(("C", f"step{rec['step']} lm-head CE", gms(a), gms(b)))
+            prev = -1e30
+            for i in range(self.L - 1, -1, -1):
+                lr = rec["layers"].get(i, {})
+                if "bwd" in lr and "d2h_end" in lr:
+                    start, end = max(gms(lr["bwd"][1]), prev), gms(lr["d2h_end"])
+                    prev = end
+                    d2h.append(("#", f"step{rec['step']} layer{i} grads", start, end))
+            for j in rec["jobs"] + rec["other_jobs"]:
+                if j.t_end > j.t_start:
+                    ch = next((v for k, v in kind.items() if j.name.startswith(k)), "?")
+                    cpu.append((ch, f"step{rec['step']} {j.name}", (j.t_start - origin) * 1e3,
+                                (j.t_end - origin) * 1e3))
+        return dict(gpu=gpu, d2h=d2h, cpu=cpu)
+
+    @staticmethod
+    def render_timeline(tl, ms_per_col=10.0, t_end=None, t_start=0.0):
+        """Three text lanes (GPU, D2H, CPU) of a timeline_of(), one column per ms_per_col: each
+        column shows the activity that covers at least half of it, ':' when activities cover
+        10-50% of it, '.' when idle."""
+        lanes = (("GPU", tl["gpu"]), ("D2H", tl["d2h"]), ("CPU", tl["cpu"]))
+        end = t_end or max((iv[3] for _, ivs in lanes for iv in ivs), default=0.0)
+        ncol = max(1, int((end - t_start) / ms_per_col + 0.999))
+        out = []
+        for name, ivs in lanes:
+            row = []
+            for c in range(ncol):
+                lo, hi = t_start + c * ms_per_col, t_start + (c + 1) * ms_per_col
+                cover = {}
+                for ch, _, a, b in ivs:
+                    ov = min(b, hi) - max(a, lo)
+                    if ov > 0:
+                        cover[ch] = cover.get(ch, 0.0) + ov
+                best = max(cover.items(), key=lambda kv: kv[1]) if cover else None
+                busy = sum(cover.values())
+                row.append(best[0] if best and best[1] >= 0.5 * ms_per_col
+                           else ":" if busy >= 0.1 * ms_per_col else ".")
+            out.append(f"{name} |{''.join(row)}|")
+        return "\n".join(out)
+
+    def export_trace(self, recs, path):
+        """Chrome trace-event JSON (chrome://tracing, Perfetto) of recorded steps."""
+        events = []
+        tl = self.timeline_of(recs)
+        for tid, lane in ((1, "gpu"), (2, "d2h"), (3, "cpu")):
+            for _, name, a, b in tl[lane]:
+                events.append(dict(name=name, ph="X", pid=0, tid=tid, ts=a * 1e3,
+                                   dur=max(0.0, (b - a) * 1e3)))
+        with open(path, "w") as f:
+            json.dump({"traceEvents": events}, f)
+
     @staticmethod
     def _boundary_gaps(recs):
         """Median GPU time between the end of a step's backward and the start of the next step's

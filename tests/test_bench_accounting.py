@@ -102,3 +102,16 @@ def test_tier_report_rates():
     assert r["update_s_per_step"] == 1.0 and r["io_wait_s_per_step"] == 0.5
     assert r["read_plus_write_gbs"] == 3.0          # 6 GB over 2 s of tier calls
     assert r["frac_of_step"] == 0.5 and r["layers"] == 2 and r["direct_io"] is True
+
+
+def test_text_timeline_lanes():
+    """A column shows the activity covering at least half of it, ':' when 10-50% of it is
+    busy, '.' when idle."""
+    from layer_sliding_offloaded_fwd_amd.engine import SlideEngine
+    tl = dict(gpu=[("F", "layer0 fwd", 0, 9), ("C", "ce", 30, 45), ("B", "layer0 bwd", 50, 58)],
+              d2h=[("#", "layer0 grads", 58, 66)],
+              cpu=[("e", "embed0", 5, 14), ("u", "layer0", 66, 85)])
+    out = SlideEngine.render_timeline(tl, 5.0).split("\n")
+    assert out[0] == "GPU |FF....CCC.BB.....|"
+    assert out[1] == "D2H |...........:#:...|"      # 58-66 ms: 40%, 100%, 20% of columns
+    assert out[2] == "CPU |.ee..........uuuu|"
