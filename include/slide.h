@@ -230,6 +230,8 @@ enum { SLIDE_ENGINE_HIP = 0, SLIDE_ENGINE_HOST = 1 };
 int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_bytes, size_t g_bytes,
                            void* dev_base, void* h2d_stream, void* d2h_stream, int engine);
 /* Pick the next FREE slot (round-robin), start the copy host_w -> slot weights, mark LOADING.
+ * The copy is w_bytes long: host_w must span w_bytes bytes (pinned memory for an asynchronous
+ * copy), also where the layer's own bytes end before w_bytes.
  * SLIDE_E_STATE if no slot is FREE. */
 int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot_out);
 /* Make `compute_stream` wait for the slot's load; LOADING -> IN_USE. Also returns the slot's
@@ -237,7 +239,8 @@ int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot
 int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_stream, void** w_dev,
                             void** g_dev);
 /* After the work on compute_stream that writes the slot's gradients: copy them to host_g on
- * the d2h stream; IN_USE -> FLUSHING. *ticket identifies this flush for wait_flush. */
+ * the d2h stream; IN_USE -> FLUSHING. The copy is g_bytes long, so host_g must span g_bytes
+ * bytes. *ticket identifies this flush for wait_flush. */
 int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
                           uint64_t* ticket);
 /* Block until the flush named by ticket has landed in host memory; SLIDE_E_TIMEOUT after

@@ -66,12 +66,20 @@ def _align(n, a=256):
     return (n + a - 1) // a * a
 
 
+def pinned_bytes(n, esize, min_bytes=0):
+    """Bytes allocated for a pinned buffer of n elements of esize bytes that the slot ring may
+    copy min_bytes of: the larger of the two, at least 64, rounded up to 256."""
+    return _align(max(n * esize, int(min_bytes), 64))
+
+
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite")
+                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off")
 
-    def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None):
+    def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None,
+                 off=0):
         self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
+        self.off = off        # element offset of this job's part within its block
         self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
         self.tier = tier      # (p, m, v) offsets in the disk tier (None: in host memory)
         self.nonfinite = None  # (pinned count array, index) when the gradient is checked
@@ -93,10 +101,12 @@ class _PinnedPool:
         self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
         self._ptrs = []
 
-    def tensor(self, n, dtype):
+    def tensor(self, n, dtype, min_bytes=0):
+        """n elements of dtype; the allocation spans at least min_bytes and is rounded up to
+        256 bytes, so a copy of a 256-byte-padded size (the slot ring's) stays inside it."""
         ct = self._ct
         esize = torch.empty(0, dtype=dtype).element_size()
-        nbytes = max(n * esize, 64)
+        nbytes = pinned_bytes(n, esize, min_bytes)
         ptr = ct.c_void_p()
         rc = self._hip.hipHostMalloc(ct.byref(ptr), nbytes, 0)
         if rc != 0 or not ptr.value:
@@ -132,18 +142,20 @@ class _Param:
     (the moments always; the master too for bf16 compute, where the pinned bf16 buffer is the
     upload source; None where an array stays in host memory)."""
 
-    def __init__(self, n, dtype, pinned, device=None, resident=False, tier=None):
+    def __init__(self, n, dtype, pinned, device=None, resident=False, tier=None, copy_bytes=0):
+        """copy_bytes: how many bytes the slot ring copies into / out of the pinned buffers
+        (its slot size, n elements rounded up to 256 bytes); they are allocated that large."""
         self.n = n
         self.dtype = dtype
         self.tier = tier
         if dtype == "bf16":
             self.master = _host_f32(n) if tier is None or tier[0] is None else None
-            self.shared = pinned.tensor(n, torch.int16)        # bf16 bits
+            self.shared = pinned.tensor(n, torch.int16, copy_bytes)        # bf16 bits
             self.grad_host = self.shared
         else:
-            self.master = pinned.tensor(n, torch.float32)      # upload source
+            self.master = pinned.tensor(n, torch.float32, copy_bytes)      # upload source
             self.shared = self.master
-            self.grad_host = pinned.tensor(n, torch.float32)
+            self.grad_host = pinned.tensor(n, torch.float32, copy_bytes)
         self.m = _host_f32(n) if tier is None else None
         self.v = _host_f32(n) if tier is None else None
         self.job = None
@@ -160,7 +172,7 @@ class SlideEngine:
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
                  tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False,
-                 keep_records=64):
+                 keep_records=64, on_gradient=None):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -180,6 +192,12 @@ class SlideEngine:
           weights are never overwritten from it.
         keep_records: how many of the latest steps' records (events, job timings) are kept for
           analyse(); older ones are dropped, so a long run does not accumulate them.
+        on_gradient: optional callable(name, step, offset, grad) run on the CPU worker once a
+          gradient has landed in host memory and before the update that consumes it (for bf16
+          compute the update overwrites the gradient with the new weights). name is the block
+          ("layer3", "embed2", "lm_head0", "w_final"), offset the element offset of this part
+          within its block, grad the host tensor (bf16 bits as int16, or fp32). For gradient
+          statistics and inspection; it must not modify grad.
         """
         assert spec.dtype in ("bf16", "f32")
         if activations is None:
@@ -233,7 +251,8 @@ class SlideEngine:
                     offs, o = (o, o + reg, o + 2 * reg), o + 3 * reg
                 else:
                     offs, o = (None, o, o + reg), o + 2 * reg
-            self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs))
+            self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs,
+                                      copy_bytes=self.w_bytes))
         self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
@@ -261,6 +280,7 @@ class SlideEngine:
         # device memory, allocated once
         dev = self.device
         self.check_finite = check_finite
+        self.on_gradient = on_gradient
         if check_finite:
             names = ([f"layer{i}" for i in range(self.L)] + ["w_final"]
                      + [f"lm_head{ci}" for ci in range(self.lm_nch)]
@@ -544,6 +564,8 @@ class SlideEngine:
                                 SLIDE_E_NONFINITE, "slide_nonfinite_count",
                                 f"{job.name}: {bad} NaN or infinite gradient elements in step "
                                 f"{job.step}; its update was not applied")
+                    if self.on_gradient is not None:
+                        self.on_gradient(job.name, job.step, job.off, job.g)
                     job.t_ready = time.perf_counter()
                     if job.tier is None:
                         B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
@@ -729,7 +751,7 @@ class SlideEngine:
 
         out = prm.shared[sl] if prm.dtype == "bf16" else None
         job = _Job(name, done, prm.master[sl], prm.grad_host[sl], prm.m[sl], prm.v[sl], out,
-                   (r1 - r0) * H, self.step_count, priority, upload)
+                   (r1 - r0) * H, self.step_count, priority, upload, off=r0 * H)
         self._nf_attach(job)
         rec["other_jobs"].append(job)
         return job, done

@@ -228,6 +228,36 @@ def test_ring_sliding_schedule_moves_the_right_bytes():
     ring.close()
 
 
+def test_ring_copies_stay_inside_engine_sized_host_buffers():
+    """hidden 520 in bf16: a layer's bytes are not a multiple of 256, the slot ring copies its
+    256-byte-padded slot size, and the engine sizes its pinned layer buffers for that copy.
+    Guard bytes after each buffer must survive a load and a flush."""
+    from layer_sliding_offloaded_fwd_amd.engine import _align, pinned_bytes
+    cfg = sl.layer_cfg(520, 4, 2, 64, 1040, "bf16")
+    P = sl.slide_layer_param_count(cfg)
+    assert (P * 2) % 256 != 0
+    wb = _align(P * 2)
+    nb = pinned_bytes(P, 2, wb)
+    assert nb >= wb and nb % 256 == 0
+    ring, dev = _host_ring(2, wb, wb)
+    guard = 4096
+    hw = np.full(nb + guard, 0xA5, np.uint8)
+    hg = np.full(nb + guard, 0x5A, np.uint8)
+    hw[:P * 2] = np.arange(P * 2, dtype=np.uint64).astype(np.uint8)
+    s = ring.load(0, hw)
+    wptr, gptr = ring.acquire(s)
+    off = wptr - dev.ctypes.data
+    assert np.array_equal(dev[off: off + P * 2], hw[:P * 2])
+    goff = gptr - dev.ctypes.data
+    dev[goff: goff + wb] = 7
+    t = ring.flush(s, hg)
+    ring.release(s)
+    ring.wait_flush(t, 5000)
+    assert np.all(hg[:wb] == 7)
+    assert np.all(hw[nb:] == 0xA5) and np.all(hg[nb:] == 0x5A), "copy ran past the buffer"
+    ring.close()
+
+
 def test_ring_state_errors():
     ring, dev = _host_ring(2)
     w = np.ones(1024, np.uint8)

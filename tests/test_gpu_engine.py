@@ -165,6 +165,121 @@ def test_bf16_model_loss_matches_oracle():
     assert abs(loss - rloss) <= 2e-3 * abs(rloss)
 
 
+def _block_of(name):
+    """Block a CPU job belongs to: "embed3" -> "embed", "lm_head0" -> "lm_head"."""
+    for b in ("embed", "lm_head"):
+        if name.startswith(b):
+            return b
+    return name
+
+
+def _oracle_from_flat(flat, w):
+    """fp64 oracle parameters from flat fp32 blocks (embed, layer0.., w_final, lm_head)."""
+    V, H = w.vocab, w.layer.hidden
+    out = dict(embed=flat["embed"].astype(np.float64).reshape(V, H),
+               w_final=flat["w_final"].astype(np.float64),
+               lm_head=flat["lm_head"].astype(np.float64).reshape(V, H), layers=[])
+    for i in range(w.n_layers):
+        d, o = {}, 0
+        for n, shp in w.layer.param_shapes():
+            k = int(np.prod(shp))
+            d[n] = flat[f"layer{i}"][o:o + k].astype(np.float64).reshape(shp)
+            o += k
+        out["layers"].append(d)
+    return out
+
+
+@pytest.mark.parametrize("activations", ["hbm", "host", "recompute"])
+def test_bf16_step_gradients_updates_and_uploads_match_oracle(activations):
+    """The benchmarked bf16 path, where one pinned buffer per block is both the gradient landing
+    zone and the upload source and the CPU AdamW writes the new bf16 weights into it in place.
+    For two steps (the second on the weights the first produced; a large learning rate makes a
+    stale or misrouted upload visible in the second step's loss and gradients):
+    - the loss matches the oracle's at the bf16 rounding of the current fp32 masters;
+    - every gradient that lands in host memory matches the oracle's gradient (bf16 tolerance);
+    - every fp32 master, first and second moment equals the fixed-order fp32 AdamW of the
+      landed gradient, bit for bit;
+    - every pinned buffer (the next upload source) and every resident device copy holds the
+      bf16 rounding of its master, bit for bit."""
+    w = SMALL
+    c = w.layer
+    hp = AdamW(lr=1e-2)
+    ohp = oa.AdamWHyper(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)
+    print(f"bf16 engine vs oracle after updates: {w.name} activations={activations} "
+          f"lr={hp.lr}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    H, V, P = c.hidden, w.vocab, c.param_count()
+    sizes = dict(embed=V * H, w_final=H, lm_head=V * H, **{f"layer{i}": P
+                                                              for i in range(w.n_layers)})
+    landed = {}
+
+    def on_gradient(name, step, off, g):
+        blk = _block_of(name)
+        arr = landed.setdefault((step, blk), np.full(sizes[blk], np.nan, np.float32))
+        arr[off:off + g.numel()] = oa.bf16_bits_to_f32(g.numpy().view(np.uint16))
+
+    p = dict(embed=params["embed"].f32.reshape(-1), w_final=params["w_final"].f32,
+             lm_head=params["lm_head"].f32.reshape(-1))
+    for i, flat in enumerate(_flat_layers(params, w)):
+        p[f"layer{i}"] = flat.astype(np.float32)
+    m = {k: np.zeros(v.size, np.float32) for k, v in p.items()}
+    vv = {k: np.zeros(v.size, np.float32) for k, v in p.items()}
+    sh = om.ModelShape(om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn),
+                       w.n_layers, w.vocab)
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=hp, adam_threads=3, ce_chunk=256,
+                      activations=activations, x_slots=3, on_gradient=on_gradient)
+    try:
+        eng.load_params(p["embed"], [p[f"layer{i}"] for i in range(w.n_layers)], p["w_final"],
+                        p["lm_head"])
+        prm_of = dict(embed=eng.embed, w_final=eng.final, lm_head=eng.lm,
+                      **{f"layer{i}": eng.layers[i] for i in range(w.n_layers)})
+        for step in (1, 2):
+            tok = tokens(w.batch, w.seq, w.vocab, seed=40 + step)
+            eng.step(tok)
+            loss = eng.loss()
+            eng.wait_updates()
+            torch.cuda.synchronize()
+            # the oracle runs on the bf16 rounding of the masters the GPU computed with
+            cur = {k: oa.bf16_bits_to_f32(oa.bf16_round_bits(a)) for k, a in p.items()}
+            rloss, rg = om.model_loss_and_grads(_oracle_from_flat(cur, w), tok, sh)
+            print(f"  step {step}: loss gpu {loss:.6f} oracle {rloss:.6f}", flush=True)
+            assert abs(loss - rloss) <= 2e-3 * abs(rloss)
+            rflat = dict(embed=rg["embed"].reshape(-1), w_final=rg["w_final"],
+                         lm_head=rg["lm_head"].reshape(-1))
+            for i, fl in enumerate(_flat_grads(rg, w)):
+                rflat[f"layer{i}"] = fl
+            got = eng.master_params()
+            got_flat = dict(embed=got["embed"], w_final=got["w_final"], lm_head=got["lm_head"],
+                            **{f"layer{i}": a for i, a in enumerate(got["layers"])})
+            for blk in sizes:
+                g = landed.pop((step, blk))
+                assert not np.isnan(g).any(), f"step {step} {blk}: a part never landed"
+                if blk.startswith("layer"):
+                    o = 0
+                    for n, shp in c.param_shapes():
+                        k = int(np.prod(shp))
+                        assert_close(g[o:o + k], rflat[blk][o:o + k], "bf16",
+                                     f"step {step} {blk} landed grad {n}")
+                        o += k
+                else:
+                    assert_close(g, rflat[blk], "bf16", f"step {step} {blk} landed grad")
+                pn, mn, vn, bits = oa.adamw_fp32(p[blk], g, m[blk], vv[blk], step, ohp)
+                prm = prm_of[blk]
+                assert np.array_equal(got_flat[blk].view(np.uint32), pn.view(np.uint32)), \
+                    f"step {step} {blk}: master is not AdamW of the landed gradient"
+                assert np.array_equal(prm.m.numpy().view(np.uint32), mn.view(np.uint32)), blk
+                assert np.array_equal(prm.v.numpy().view(np.uint32), vn.view(np.uint32)), blk
+                assert np.array_equal(prm.shared.numpy().view(np.uint16), bits), \
+                    f"step {step} {blk}: upload buffer is not the bf16 rounding of the master"
+                if hasattr(prm, "dev"):
+                    dbits = prm.dev.view(torch.int16).cpu().numpy().view(np.uint16)
+                    assert np.array_equal(dbits, bits), f"step {step} {blk}: device copy"
+                p[blk], m[blk], vv[blk] = pn, mn, vn
+        assert not landed, sorted(landed)
+    finally:
+        eng.close()
+
+
 RAGGED = Workload("ragged-vocab-bf16", LayerCfg(256, 4, 2, 64, 688), 3, 1000, 2, 64, "bf16")
 
 

@@ -24,7 +24,8 @@ import torch
 
 import layer_sliding_offloaded_fwd_amd as sl
 from oracle import model as om
-from seeded_inputs import L8B, L123B, CE_ONLY, activations, ce_inputs, layer_params, pack_layer
+from seeded_inputs import (L8B, L123B, CE_ONLY, LayerCfg, activations, ce_inputs,
+                           layer_params, pack_layer)
 from tests._gpu import DEV, assert_close, dev, empty, host, rel_err, stream, ws
 
 pytestmark = pytest.mark.gpu
@@ -131,6 +132,64 @@ def test_layer_123b_at_bench_launch_prefix():
     gh = _unpack(host(g), c)
     for n in om.LAYER_PARAM_NAMES:
         assert_close(gh[n], rg[n], dtype, f"grad {n}")
+
+
+def test_layer_groups_of_12_full_2048_sequence():
+    """Attention over whole 2048-token rows with 12 query heads per kv head (the 123B-class
+    layer's group size) at the 123B-class launch of 4 x 2048 tokens, with a reduced hidden size
+    so that the oracle runs a whole sequence: every row of y and dx of one sequence against the
+    oracle, the batch's weight gradients against the sum of the four single-sequence launches,
+    and one single-sequence weight gradient against the oracle."""
+    c, B, S, dtype = LayerCfg(1536, 24, 2, 128, 4096), L123B.batch, L123B.seq, "bf16"
+    N, H, b = B * S, c.hidden, 1
+    print(f"layer with groups of {c.n_heads // c.n_kv_heads}: H={H} nq={c.n_heads} "
+          f"nkv={c.n_kv_heads} d={c.head_dim} F={c.ffn} at B={B} S={S} bf16", flush=True)
+    params = layer_params(c, dtype, seed=0, gain_std=0.1)
+    x = activations((N, H), dtype, 1)
+    dy = activations((N, H), dtype, 2)
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, dtype)
+    w = torch.from_numpy(pack_layer(params, c, dtype).view(np.int16)).to(DEV).view(torch.bfloat16)
+    tx, tdy = dev(x.f32, dtype), dev(dy.f32, dtype)
+
+    def run(xs, dys, nb):
+        sb = sl.slide_layer_saved_bytes(cfg, nb, S)
+        wb = sl.slide_layer_workspace_bytes(cfg, nb, S, 2)
+        saved, work = ws(sb), ws(wb)
+        y = torch.empty_like(xs)
+        dx = torch.empty_like(xs)
+        g = torch.full_like(w, float("nan"))
+        sl.slide_layer_fwd_save(cfg, w, xs, y, nb, S, saved, sb, stream())
+        sl.slide_layer_bwd_saved(cfg, w, xs, dys, dx, g, nb, S, saved, sb, work, wb, stream())
+        return y, dx, g
+
+    y, dx, g = run(tx, tdy, B)
+    g_sum = torch.zeros(w.numel(), dtype=torch.float32, device=DEV)
+    for bb in range(B):
+        rows = slice(bb * S, (bb + 1) * S)
+        _, _, gb = run(tx[rows].contiguous(), tdy[rows].contiguous(), 1)
+        g_sum += gb.float()
+        if bb == b:
+            g_one = gb
+    torch.cuda.synchronize()
+    gh, gs = _unpack(host(g), c), _unpack(g_sum.double().cpu().numpy(), c)
+    for n in om.LAYER_PARAM_NAMES:
+        assert_close(gh[n], gs[n], dtype, f"batch grad {n} vs sum over sequences")
+    rows = slice(b * S, (b + 1) * S)
+    shape = om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, c.rms_eps,
+                          c.rope_theta)
+    p64 = {k: v.f64 for k, v in params.items()}
+    ry, cache = om.layer_fwd(p64, x.f64[rows].reshape(1, S, H), shape)
+    rdx, rg = om.layer_bwd(p64, dy.f64[rows].reshape(1, S, H), cache, shape)
+    del cache
+    assert_close(host(y[rows]).reshape(1, S, H), ry, dtype, f"y, all {S} rows of sequence {b}")
+    assert_close(host(dx[rows]).reshape(1, S, H), rdx, dtype, f"dx, all {S} rows of sequence {b}")
+    # the last rows attend over the whole sequence: check them on their own as well
+    tail = slice(b * S + S - 64, (b + 1) * S)
+    assert_close(host(y[tail]).reshape(1, 64, H), ry[:, -64:], dtype, "y, last 64 rows")
+    assert_close(host(dx[tail]).reshape(1, 64, H), rdx[:, -64:], dtype, "dx, last 64 rows")
+    g1 = _unpack(host(g_one), c)
+    for n in om.LAYER_PARAM_NAMES:
+        assert_close(g1[n], rg[n], dtype, f"grad {n}, sequence {b} alone")
 
 
 @pytest.fixture(scope="module")
