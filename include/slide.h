@@ -185,6 +185,18 @@ size_t slide_rmsnorm_bwd_workspace_bytes(int N, int H);
 int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, void* dx,
                       void* dw, int N, int H, float eps, int dtype, void* ws, size_t ws_bytes,
                       void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): slide_rmsnorm_bwd with its scratch in a fixed
+ * device array of the library instead of a caller workspace. Results are bit-identical to
+ * slide_rmsnorm_bwd. Calls no hipMalloc / hipFree. SLIDE_E_WORKSPACE if the call needs more
+ * than slide_rmsnorm_bwd_noalloc_max_bytes() (16 MiB) of scratch, i.e. if
+ * slide_rmsnorm_bwd_workspace_bytes(N, H) exceeds it. Each GPU has one such array, held until
+ * the process ends and shared by every call on that GPU: calls that overlap on one GPU (other
+ * streams, other threads) race on it and must be serialized by the caller. */
+size_t slide_rmsnorm_bwd_noalloc_max_bytes(void);
+int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w, const void* dres,
+                              void* dx, void* dw, int N, int H, float eps, int dtype,
+                              void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel-level entry points (the building blocks of the layer; used by tests and benches).

@@ -65,6 +65,8 @@ SIGNATURES = {
     "slide_rmsnorm_fwd": (I, [P, P, P, P, I, I, F, I, P]),
     "slide_rmsnorm_bwd_workspace_bytes": (SZ, [I, I]),
     "slide_rmsnorm_bwd": (I, [P, P, P, P, P, P, I, I, F, I, P, SZ, P]),
+    "slide_rmsnorm_bwd_noalloc_max_bytes": (SZ, []),
+    "slide_rmsnorm_bwd_noalloc": (I, [P, P, P, P, P, P, I, I, F, I, P]),
     "slide_gemm": (I, [I, I, I, P, I, I, P, I, I, P, I, I, P, I, F, I, I, P]),
     "slide_attention_fwd": (I, [P, P, P, I, I, I, I, I, I, P]),
     "slide_attention_bwd_workspace_bytes": (SZ, [I, I, I]),

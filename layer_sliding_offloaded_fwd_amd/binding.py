@@ -18,7 +18,8 @@ __all__ = [
     "slide_lmhead_ce_stats", "slide_lmhead_ce_loss", "slide_lmhead_ce_grad", "slide_lmhead_ce_dh",
     "slide_embed_fwd",
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
-    "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_gemm",
+    "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
+    "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "StateTier", "slide_tier_region_bytes",
     "slide_nonfinite_count",
@@ -166,6 +167,15 @@ def slide_rmsnorm_bwd_workspace_bytes(N, H):
 def slide_rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ws, ws_bytes, stream=None):
     call("slide_rmsnorm_bwd", _p(dy), _p(x), _p(w), _p(dres), _p(dx), _p(dw), N, H,
          ctypes.c_float(eps), dtype, _p(ws), ws_bytes, _s(stream))
+
+
+def slide_rmsnorm_bwd_noalloc_max_bytes():
+    return int(lib().slide_rmsnorm_bwd_noalloc_max_bytes())
+
+
+def slide_rmsnorm_bwd_noalloc(dy, x, w, dres, dx, dw, N, H, eps, dtype, stream=None):
+    call("slide_rmsnorm_bwd_noalloc", _p(dy), _p(x), _p(w), _p(dres), _p(dx), _p(dw), N, H,
+         ctypes.c_float(eps), dtype, _s(stream))
 
 
 # ------------------------------------------------------------------------------ kernels

@@ -8,6 +8,8 @@
 //   dm = dy Wd, dWd = dy^T m; SwiGLU backward; dr2 = dgu Wgu, dWgu = dgu^T r2;
 //   dx2 = dy + RMSNorm_bwd(dr2); do = dx2 Wo, dWo = dx2^T o; attention backward; inverse RoPE;
 //   dr = dqkv Wqkv, dWqkv = dqkv^T r; dx = dx2 + RMSNorm_bwd(dr).
+#include <mutex>
+
 #include "attention.h"
 #include "gemm.h"
 #include "pointwise.h"
@@ -316,6 +318,68 @@ extern "C" int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, c
   SLIDE_REQUIRE(N == 0 || (dy && x && w && dx), SLIDE_E_ARG, "rmsnorm_bwd: null pointer");
   SLIDE_REQUIRE(dy != dx, SLIDE_E_ARG, "rmsnorm_bwd: dx must not alias dy");
   return rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ws, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+// The RMSNorm backward's scratch (per-row 1/rms and the 64-row partial sums of the weight
+// gradient) in a fixed device array, for callers that cannot allocate. Each GPU holds its own
+// copy of the array; its device address is looked up once per device and kept.
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the current device for the
+// null stream).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(SLIDE_E_HIP, "no-alloc scratch: hipGetDevice: %s", hipGetErrorString(e));
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess)
+      return fail(SLIDE_E_HIP, "no-alloc scratch: hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SLIDE_E_UNSUPPORTED, "no-alloc scratch: device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(SLIDE_E_HIP, "no-alloc scratch: hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(SLIDE_E_HIP, "no-alloc scratch: hipGetSymbolAddress on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SLIDE_OK;
+}
+}  // namespace
+
+extern "C" size_t slide_rmsnorm_bwd_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w,
+                                         const void* dres, void* dx, void* dw, int N, int H,
+                                         float eps, int dtype, void* stream) {
+  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
+  const size_t need = rmsnorm_bwd_ws(N, H);
+  SLIDE_REQUIRE(need <= kNoAllocScratchBytes, SLIDE_E_WORKSPACE,
+                "rmsnorm_bwd_noalloc: N=%d H=%d needs %zu bytes of scratch, the fixed array holds %zu",
+                N, H, need, kNoAllocScratchBytes);
+  SLIDE_REQUIRE(N == 0 || (dy && x && w && dx), SLIDE_E_ARG, "rmsnorm_bwd: null pointer");
+  SLIDE_REQUIRE(dy != dx, SLIDE_E_ARG, "rmsnorm_bwd: dx must not alias dy");
+  void* ptr = nullptr;
+  SLIDE_TRY(scratch_for_stream((hipStream_t)stream, &ptr));
+  // every scratch element the kernels read is written earlier in the same call: nothing needs
+  // clearing, and a previous call's contents are never read
+  return rmsnorm_bwd(dy, x, w, dres, dx, dw, N, H, eps, dtype, ptr, (hipStream_t)stream);
 }
 
 extern "C" int slide_nonfinite_count(const void* x, int dtype, size_t n, uint32_t* count_dev,

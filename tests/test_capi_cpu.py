@@ -63,6 +63,18 @@ def test_validation_errors_before_any_launch():
     assert e.value.code == _capi.SLIDE_E_SHAPE
 
 
+def test_rmsnorm_noalloc_size_limit_checked_before_any_launch():
+    """The no-allocation RMSNorm backward refuses a size whose scratch exceeds its fixed array
+    (16 MiB) with SLIDE_E_WORKSPACE before touching the device."""
+    assert sl.slide_rmsnorm_bwd_noalloc_max_bytes() == 16 << 20
+    N, H = 65536, 8192
+    assert sl.slide_rmsnorm_bwd_workspace_bytes(N, H) > 16 << 20
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_rmsnorm_bwd_noalloc(None, None, None, None, None, None, N, H, 1e-5,
+                                     sl.SLIDE_BF16)
+    assert e.value.code == _capi.SLIDE_E_WORKSPACE
+
+
 def test_nonfinite_count_validation():
     cnt = np.zeros(1, np.int32)
     for args, code in [((None, sl.SLIDE_BF16, 16, cnt.ctypes.data), _capi.SLIDE_E_ARG),
