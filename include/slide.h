@@ -301,6 +301,14 @@ typedef struct {
 int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
                     uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
                     int n_threads);
+/* The host-DRAM roofline of the CPU optimizer (summary, section 2B: the optimizer state lives
+ * in host memory, so the update of a layer is bound by host memory bandwidth): a STREAM triad
+ * a = b + s*c over three float arrays of n elements that the call maps (transparent huge pages)
+ * and unmaps itself, on n_threads threads (<= 0: the available cores) with the same contiguous
+ * per-thread ranges and 64-byte vector accesses as slide_cpu_adamw. 12 bytes per element per
+ * repetition; *gbs_best (and *gbs_median, nullable) receive GB/s over `reps` repetitions.
+ * SLIDE_E_ARG for n < 16, reps < 1 or a failed mapping. Blocks until done. */
+int slide_host_triad(size_t n, int n_threads, int reps, double* gbs_best, double* gbs_median);
 
 /* The scalar (non-vector) code path of slide_cpu_adamw on one thread; same contract. Exposed so
  * that tests can check both code paths give identical bits. */

@@ -86,6 +86,8 @@ SIGNATURES = {
     "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,
                                             ctypes.POINTER(AdamWHp)]),
+    "slide_host_triad": (I, [SZ, I, I, ctypes.POINTER(ctypes.c_double),
+                             ctypes.POINTER(ctypes.c_double)]),
     "slide_nonfinite_count": (I, [P, I, SZ, P, P]),
     "slide_tier_region_bytes": (SZ, [SZ]),
     "slide_tier_create": (I, [ctypes.POINTER(P), ctypes.c_char_p, ctypes.c_uint64, SZ, I, I]),

@@ -21,7 +21,8 @@ __all__ = [
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
     "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
-    "slide_rope", "SlotRing", "slide_cpu_adamw", "StateTier", "slide_tier_region_bytes",
+    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_host_triad", "StateTier",
+    "slide_tier_region_bytes",
     "slide_nonfinite_count",
     "SLIDE_TIER_DIRECT", "SLIDE_TIER_UNLINK", "slide_prof_enable", "slide_prof_reset",
     "slide_prof_read", "dtype_code", "layer_cfg",
@@ -274,6 +275,13 @@ def slide_cpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, n_threads=0):
     """p, m, v: float32 host buffers; g: host bf16 (uint16) or float32; hp: AdamWHp."""
     call("slide_cpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
          ctypes.byref(hp), n_threads)
+
+
+def slide_host_triad(n, n_threads=0, reps=3):
+    """STREAM-triad host-DRAM bandwidth (GB/s): (best, median) over reps repetitions."""
+    best, med = ctypes.c_double(), ctypes.c_double()
+    call("slide_host_triad", n, n_threads, reps, ctypes.byref(best), ctypes.byref(med))
+    return best.value, med.value
 
 
 def slide_nonfinite_count(x, dtype, n, count_dev, stream=None):

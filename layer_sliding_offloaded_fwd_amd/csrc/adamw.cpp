@@ -205,3 +205,85 @@ extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dt
   range_scalar(p, g, g_dtype, m, v, out, 0, n, make_consts(*hp, step));
   return SLIDE_OK;
 }
+
+// ------------------------------------------------------------------ host-DRAM roofline
+// STREAM triad (McCalpin): a[i] = b[i] + s * c[i] over three float arrays, each thread on its
+// own contiguous range, with the same 64-byte vector loads and stores as the AdamW above. The
+// arrays are mapped with transparent huge pages and first touched by the threads that use
+// them, as the optimizer state is. Bytes counted: 12 per element (two reads, one write).
+#include <sys/mman.h>
+
+#include <chrono>
+
+namespace {
+
+__attribute__((target("avx512f"))) void triad_range(float* a, const float* b, const float* c,
+                                                    float s, size_t lo, size_t hi) {
+  const __m512 sv = _mm512_set1_ps(s);
+  size_t i = lo;
+  for (; i + 16 <= hi; i += 16)
+    _mm512_store_ps(a + i, _mm512_add_ps(_mm512_load_ps(b + i),
+                                         _mm512_mul_ps(sv, _mm512_load_ps(c + i))));
+  for (; i < hi; ++i) a[i] = b[i] + s * c[i];
+}
+
+void triad_range_scalar(float* a, const float* b, const float* c, float s, size_t lo, size_t hi) {
+  for (size_t i = lo; i < hi; ++i) a[i] = b[i] + s * c[i];
+}
+
+}  // namespace
+
+extern "C" int slide_host_triad(size_t n, int n_threads, int reps, double* gbs_best,
+                                double* gbs_median) {
+  using slide::fail;
+  if (n < 16 || reps < 1 || !gbs_best)
+    return fail(SLIDE_E_ARG, "slide_host_triad: need n >= 16, reps >= 1 and an output");
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  const size_t bytes = (n * sizeof(float) + 4095) / 4096 * 4096;
+  float* arr[3] = {nullptr, nullptr, nullptr};
+  for (int k = 0; k < 3; ++k) {
+    void* p = mmap(nullptr, bytes, PROT_READ | PROT_WRITE, MAP_PRIVATE | MAP_ANONYMOUS, -1, 0);
+    if (p == MAP_FAILED) {
+      for (int j = 0; j < k; ++j) munmap(arr[j], bytes);
+      return fail(SLIDE_E_ARG, "slide_host_triad: cannot map %zu bytes", bytes);
+    }
+    madvise(p, bytes, MADV_HUGEPAGE);
+    arr[k] = (float*)p;
+  }
+  size_t per = (n + nt - 1) / nt;
+  per = (per + 15) / 16 * 16;
+  const bool avx512 = __builtin_cpu_supports("avx512f");
+  auto parallel = [&](auto&& body) {
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; ++t) {
+      size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
+      if (lo >= hi) break;
+      th.emplace_back(body, lo, hi);
+    }
+    for (auto& x : th) x.join();
+  };
+  parallel([&](size_t lo, size_t hi) {
+    for (size_t i = lo; i < hi; ++i) {
+      arr[0][i] = 0.f;
+      arr[1][i] = 1.f;
+      arr[2][i] = 2.f;
+    }
+  });
+  std::vector<double> rates;
+  for (int r = 0; r < reps; ++r) {
+    const auto t0 = std::chrono::steady_clock::now();
+    parallel([&](size_t lo, size_t hi) {
+      if (avx512) triad_range(arr[0], arr[1], arr[2], 3.f, lo, hi);
+      else triad_range_scalar(arr[0], arr[1], arr[2], 3.f, lo, hi);
+    });
+    const double s = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    rates.push_back(12.0 * (double)n / s / 1e9);
+  }
+  const bool ok = arr[0][n - 1] == 7.f;
+  for (int k = 0; k < 3; ++k) munmap(arr[k], bytes);
+  if (!ok) return fail(SLIDE_E_STATE, "slide_host_triad: wrong result");
+  std::sort(rates.begin(), rates.end());
+  *gbs_best = rates.back();
+  if (gbs_median) *gbs_median = rates[rates.size() / 2];
+  return SLIDE_OK;
+}

@@ -181,6 +181,15 @@ def test_cpu_adamw_shared_grad_and_bf16_buffer_and_scalar_path():
     np.testing.assert_array_equal(out3, bo)
 
 
+def test_host_triad_measures_and_validates():
+    best, med = sl.slide_host_triad(1 << 20, 2, 3)
+    assert best >= med > 0.0
+    with pytest.raises(sl.SlideError):
+        sl.slide_host_triad(8, 1, 1)
+    with pytest.raises(sl.SlideError):
+        sl.slide_host_triad(1 << 20, 1, 0)
+
+
 def test_cpu_adamw_rejects_bad_arguments():
     a = np.zeros(64, np.float32)
     g = np.zeros(64, np.uint16)
