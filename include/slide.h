@@ -301,11 +301,33 @@ typedef struct {
 int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
                     uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
                     int n_threads);
+/* slide_cpu_adamw on a list of rows: row r is elements [r*row_len, (r+1)*row_len) of p, m, v,
+ * g and p_bf16_out (all indexed alike, n_rows_total rows in each). g = NULL means an exactly
+ * zero gradient for every listed row (summary, section 2B, Layer-Adam; for an embedding, the
+ * rows that no token of the batch selected: their update needs no gradient copy and can run
+ * before the backward ends). rows: n_rows distinct indices in [0, n_rows_total), else
+ * SLIDE_E_ARG. Same bits as slide_cpu_adamw over the whole arrays with those gradients. */
+int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float* m, float* v,
+                         uint16_t* p_bf16_out, size_t row_len, size_t n_rows_total,
+                         const int32_t* rows, size_t n_rows, int64_t step,
+                         const slide_adamw_hp* hp, int n_threads);
+
+/* The same AdamW step on the GPU, for training whose optimizer state stays in HBM (the
+ * non-offloaded baseline of the paper page's abstract, which compares the layer-sliding method
+ * with training that keeps everything on the GPU). p, m, v: device float [n]; g: device [n] of
+ * g_dtype; p_bf16_out: optional device uint16 [n], which may alias g for a bf16 g. Same
+ * operation order and rounding as slide_cpu_adamw, so the results are equal bit for bit.
+ * Asynchronous on `stream`; argument errors as slide_cpu_adamw. */
+int slide_gpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
+                    uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
+                    void* stream);
+
 /* The host-DRAM roofline of the CPU optimizer (summary, section 2B: the optimizer state lives
  * in host memory, so the update of a layer is bound by host memory bandwidth): a STREAM triad
  * a = b + s*c over three float arrays of n elements that the call maps (transparent huge pages)
  * and unmaps itself, on n_threads threads (<= 0: the available cores) with the same contiguous
- * per-thread ranges and 64-byte vector accesses as slide_cpu_adamw. 12 bytes per element per
+ * per-thread ranges as slide_cpu_adamw, 64-byte loads and streaming stores (so no written line
+ * is read first and the counted bytes are the bytes moved). 12 bytes per element per
  * repetition; *gbs_best (and *gbs_median, nullable) receive GB/s over `reps` repetitions.
  * SLIDE_E_ARG for n < 16, reps < 1 or a failed mapping. Blocks until done. */
 int slide_host_triad(size_t n, int n_threads, int reps, double* gbs_best, double* gbs_median);

@@ -86,6 +86,9 @@ SIGNATURES = {
     "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,
                                             ctypes.POINTER(AdamWHp)]),
+    "slide_cpu_adamw_rows": (I, [P, P, I, P, P, P, SZ, SZ, P, SZ, ctypes.c_int64,
+                                 ctypes.POINTER(AdamWHp), I]),
+    "slide_gpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), P]),
     "slide_host_triad": (I, [SZ, I, I, ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_double)]),
     "slide_nonfinite_count": (I, [P, I, SZ, P, P]),

@@ -21,7 +21,8 @@ __all__ = [
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
     "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
-    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_host_triad", "StateTier",
+    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows", "slide_gpu_adamw",
+    "slide_host_triad", "StateTier",
     "slide_tier_region_bytes",
     "slide_nonfinite_count",
     "SLIDE_TIER_DIRECT", "SLIDE_TIER_UNLINK", "slide_prof_enable", "slide_prof_reset",
@@ -275,6 +276,19 @@ def slide_cpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, n_threads=0):
     """p, m, v: float32 host buffers; g: host bf16 (uint16) or float32; hp: AdamWHp."""
     call("slide_cpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
          ctypes.byref(hp), n_threads)
+
+
+def slide_cpu_adamw_rows(p, g, g_dtype, m, v, p_bf16_out, row_len, n_rows_total, rows, n_rows,
+                         step, hp, n_threads=0):
+    """Rows of row_len elements (int32 row indices); g None: zero gradient on those rows."""
+    call("slide_cpu_adamw_rows", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), row_len,
+         n_rows_total, _p(rows), n_rows, step, ctypes.byref(hp), n_threads)
+
+
+def slide_gpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, stream=None):
+    """p, m, v: float32 device tensors; g: device bf16 or float32; hp: AdamWHp."""
+    call("slide_gpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
+         ctypes.byref(hp), _s(stream))
 
 
 def slide_host_triad(n, n_threads=0, reps=3):

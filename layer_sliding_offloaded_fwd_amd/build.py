@@ -18,13 +18,16 @@ LIB = os.path.join(HERE, "libslide.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "pointwise.hip", "ce.hip", "layer.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "pointwise.hip", "ce.hip", "layer.hip",
+               "adamw_gpu.hip"]
 HIP_HOST_SOURCES = ["common.cpp", "ring.cpp"]   # host code that calls the HIP runtime
 CPU_SOURCES = ["adamw.cpp", "tier.cpp"]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
+# the GPU AdamW matches the CPU one's rounding only without fused multiply-adds
+PER_FILE_FLAGS = {"adamw_gpu.hip": ["-ffp-contract=off"]}
 CPU_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-pthread",
              "-Wall"]
 
@@ -44,7 +47,7 @@ def _compile(src):
     elif src in HIP_HOST_SOURCES:
         cmd = [HIPCC, "-x", "hip", *HIP_FLAGS, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *HIP_FLAGS, "-c", path, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *PER_FILE_FLAGS.get(src, []), "-c", path, "-o", obj]
     _run(cmd)
     return obj
 

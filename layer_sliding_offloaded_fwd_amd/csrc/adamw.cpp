@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "../../include/slide.h"
+#include "adamw_consts.h"
 
 namespace slide {
 int fail(int code, const char* fmt, ...);
@@ -24,27 +25,9 @@ int fail(int code, const char* fmt, ...);
 
 namespace {
 
-struct Consts {
-  float c_dec, c_b1, c_1b1, c_b2, c_1b2, c_step, c_bc2, c_eps;
-};
+using Consts = slide::AdamConsts;
 
-Consts make_consts(const slide_adamw_hp& hp, int64_t t) {
-  double b1t = 1.0, b2t = 1.0;
-  for (int64_t i = 0; i < t; ++i) {
-    b1t *= hp.beta1;
-    b2t *= hp.beta2;
-  }
-  Consts c;
-  c.c_dec = (float)(1.0 - hp.lr * hp.weight_decay);
-  c.c_b1 = (float)hp.beta1;
-  c.c_1b1 = (float)(1.0 - hp.beta1);
-  c.c_b2 = (float)hp.beta2;
-  c.c_1b2 = (float)(1.0 - hp.beta2);
-  c.c_step = (float)(hp.lr / (1.0 - b1t));
-  c.c_bc2 = (float)sqrt(1.0 - b2t);
-  c.c_eps = (float)hp.eps;
-  return c;
-}
+Consts make_consts(const slide_adamw_hp& hp, int64_t t) { return slide::adam_consts(hp, t); }
 
 inline float widen_bf16(uint16_t b) {
   uint32_t u = ((uint32_t)b) << 16;
@@ -146,29 +129,36 @@ __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const vo
 
 }  // namespace
 
-extern "C" int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
-                               uint16_t* p_bf16_out, size_t n, int64_t step,
-                               const slide_adamw_hp* hp, int n_threads) {
+int slide::adamw_check(const char* who, const void* p, const void* g, int g_dtype,
+                       const void* m, const void* v, const void* p_bf16_out, size_t n,
+                       int64_t step, const slide_adamw_hp* hp) {
   using slide::fail;
-  if (n == 0) return SLIDE_OK;
-  if (!p || !g || !m || !v || !hp) return fail(SLIDE_E_ARG, "slide_cpu_adamw: null pointer");
+  if (!p || !g || !m || !v || !hp) return fail(SLIDE_E_ARG, "%s: null pointer", who);
   if (g_dtype != SLIDE_BF16 && g_dtype != SLIDE_F32)
-    return fail(SLIDE_E_ARG, "slide_cpu_adamw: g_dtype must be SLIDE_BF16 or SLIDE_F32");
-  if (step < 1) return fail(SLIDE_E_ARG, "slide_cpu_adamw: step must be >= 1 (got %lld)",
-                            (long long)step);
+    return fail(SLIDE_E_ARG, "%s: g_dtype must be SLIDE_BF16 or SLIDE_F32", who);
+  if (step < 1) return fail(SLIDE_E_ARG, "%s: step must be >= 1 (got %lld)", who, (long long)step);
   if (!(hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && hp->eps > 0 &&
         hp->lr >= 0 && hp->weight_decay >= 0))
-    return fail(SLIDE_E_ARG, "slide_cpu_adamw: hyper-parameters out of range");
-  if (p_bf16_out && (void*)p_bf16_out != g) {
+    return fail(SLIDE_E_ARG, "%s: hyper-parameters out of range", who);
+  if (p_bf16_out && p_bf16_out != g) {
     // overlapping but not identical buffers would read already-written values
     const char* a = (const char*)p_bf16_out;
     const char* b = (const char*)g;
     size_t gb = n * (g_dtype == SLIDE_BF16 ? 2 : 4);
     if (a < b + gb && b < a + n * 2)
-      return fail(SLIDE_E_ARG, "slide_cpu_adamw: p_bf16_out partially overlaps g");
+      return fail(SLIDE_E_ARG, "%s: p_bf16_out partially overlaps g", who);
   }
-  if (p_bf16_out && (void*)p_bf16_out == g && g_dtype != SLIDE_BF16)
-    return fail(SLIDE_E_ARG, "slide_cpu_adamw: p_bf16_out may alias g only for bf16 g");
+  if (p_bf16_out && p_bf16_out == g && g_dtype != SLIDE_BF16)
+    return fail(SLIDE_E_ARG, "%s: p_bf16_out may alias g only for bf16 g", who);
+  return SLIDE_OK;
+}
+
+extern "C" int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
+                               uint16_t* p_bf16_out, size_t n, int64_t step,
+                               const slide_adamw_hp* hp, int n_threads) {
+  if (n == 0) return SLIDE_OK;
+  int rc = slide::adamw_check("slide_cpu_adamw", p, g, g_dtype, m, v, p_bf16_out, n, step, hp);
+  if (rc != SLIDE_OK) return rc;
   const Consts c = make_consts(*hp, step);
   int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
   size_t min_per = 1 << 16;
@@ -197,6 +187,60 @@ extern "C" int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, f
   return SLIDE_OK;
 }
 
+// The same update on a list of rows of row_len elements (row r = elements [r*row_len,
+// (r+1)*row_len) of p, m, v, g and the bf16 copy); g may be NULL for rows whose gradient is
+// exactly zero (an embedding's rows that no token of the batch selected). Rows are split evenly
+// over the threads; each row runs the element loop of slide_cpu_adamw, so the results are the
+// same bits as a whole-array call with those gradient values.
+extern "C" int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float* m, float* v,
+                                    uint16_t* p_bf16_out, size_t row_len, size_t n_rows_total,
+                                    const int32_t* rows, size_t n_rows, int64_t step,
+                                    const slide_adamw_hp* hp, int n_threads) {
+  using slide::fail;
+  if (n_rows == 0 || row_len == 0) return SLIDE_OK;
+  const size_t n = row_len * n_rows_total;
+  const void* gchk = g ? g : (const void*)p;   // the checks below need a gradient address
+  int rc = slide::adamw_check("slide_cpu_adamw_rows", p, gchk, g ? g_dtype : SLIDE_F32, m, v,
+                              g ? p_bf16_out : nullptr, n, step, hp);
+  if (rc != SLIDE_OK) return rc;
+  if (!rows) return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows: null row list");
+  for (size_t k = 0; k < n_rows; ++k)
+    if (rows[k] < 0 || (size_t)rows[k] >= n_rows_total)
+      return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows: row %d outside [0, %zu)", rows[k],
+                  n_rows_total);
+  const Consts c = make_consts(*hp, step);
+  const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+  const size_t gsz = g_dtype == SLIDE_BF16 ? 2 : 4;
+  auto work = [&](size_t k0, size_t k1) {
+    std::vector<uint16_t> zeros(g ? 0 : row_len, 0);   // bf16 +0.0 widens to +0.0f
+    for (size_t k = k0; k < k1; ++k) {
+      const size_t o = (size_t)rows[k] * row_len;
+      const void* gr = g ? (const void*)((const char*)g + o * gsz) : (const void*)zeros.data();
+      const int gd = g ? g_dtype : SLIDE_BF16;
+      uint16_t* outr = p_bf16_out ? p_bf16_out + o : nullptr;
+      if (avx512) range_avx512(p + o, gr, gd, m + o, v + o, outr, 0, row_len, c);
+      else range_scalar(p + o, gr, gd, m + o, v + o, outr, 0, row_len, c);
+    }
+  };
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::max<size_t>(1, std::min<size_t>((size_t)nt, (n_rows * row_len + 65535) / 65536));
+  nt = (int)std::min<size_t>((size_t)nt, n_rows);
+  if (nt == 1) {
+    work(0, n_rows);
+    return SLIDE_OK;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  const size_t per = (n_rows + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    const size_t k0 = (size_t)t * per, k1 = std::min(n_rows, k0 + per);
+    if (k0 >= k1) break;
+    th.emplace_back(work, k0, k1);
+  }
+  for (auto& x : th) x.join();
+  return SLIDE_OK;
+}
+
 // Scalar-only entry used by tests to check that both code paths agree bit for bit.
 extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dtype, float* m,
                                                float* v, uint16_t* out, size_t n, int64_t step,
@@ -208,9 +252,12 @@ extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dt
 
 // ------------------------------------------------------------------ host-DRAM roofline
 // STREAM triad (McCalpin): a[i] = b[i] + s * c[i] over three float arrays, each thread on its
-// own contiguous range, with the same 64-byte vector loads and stores as the AdamW above. The
-// arrays are mapped with transparent huge pages and first touched by the threads that use
-// them, as the optimizer state is. Bytes counted: 12 per element (two reads, one write).
+// own contiguous range, 64-byte vector loads and streaming (non-temporal) stores. The arrays
+// are mapped with transparent huge pages and first touched by the threads that use them, as
+// the optimizer state is. Bytes counted: 12 per element (two reads, one write). The streaming
+// stores write a line without reading it first, so the counted bytes are the bytes that move;
+// with ordinary stores each written line would also be read (an uncounted third read), while
+// the in-place AdamW reads every line it writes anyway.
 #include <sys/mman.h>
 
 #include <chrono>
@@ -222,9 +269,10 @@ __attribute__((target("avx512f"))) void triad_range(float* a, const float* b, co
   const __m512 sv = _mm512_set1_ps(s);
   size_t i = lo;
   for (; i + 16 <= hi; i += 16)
-    _mm512_store_ps(a + i, _mm512_add_ps(_mm512_load_ps(b + i),
-                                         _mm512_mul_ps(sv, _mm512_load_ps(c + i))));
+    _mm512_stream_ps(a + i, _mm512_add_ps(_mm512_load_ps(b + i),
+                                          _mm512_mul_ps(sv, _mm512_load_ps(c + i))));
   for (; i < hi; ++i) a[i] = b[i] + s * c[i];
+  _mm_sfence();
 }
 
 void triad_range_scalar(float* a, const float* b, const float* c, float s, size_t lo, size_t hi) {

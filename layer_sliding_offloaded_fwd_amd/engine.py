@@ -74,12 +74,16 @@ def pinned_bytes(n, esize, min_bytes=0):
 
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off")
+                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off",
+                 "rows", "row_len")
 
     def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None,
-                 off=0):
+                 off=0, rows=None, row_len=0):
         self.name, self.wait, self.p, self.g, self.m, self.v = name, wait, p, g, m, v
         self.off = off        # element offset of this job's part within its block
+        # rows: update only these rows of row_len elements (int32 indices into p, m, v, out,
+        # which then hold n // row_len rows); g None: their gradient is exactly zero
+        self.rows, self.row_len = rows, row_len
         self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
         self.tier = tier      # (p, m, v) offsets in the disk tier (None: in host memory)
         self.nonfinite = None  # (pinned count array, index) when the gradient is checked
@@ -142,16 +146,21 @@ class _Param:
     (the moments always; the master too for bf16 compute, where the pinned bf16 buffer is the
     upload source; None where an array stays in host memory)."""
 
-    def __init__(self, n, dtype, pinned, device=None, resident=False, tier=None, copy_bytes=0):
+    def __init__(self, n, dtype, pinned, device=None, resident=False, tier=None, copy_bytes=0,
+                 separate_grad=False):
         """copy_bytes: how many bytes the slot ring copies into / out of the pinned buffers
-        (its slot size, n elements rounded up to 256 bytes); they are allocated that large."""
+        (its slot size, n elements rounded up to 256 bytes); they are allocated that large.
+        separate_grad: for bf16, the gradient lands in its own pinned buffer instead of the
+        upload buffer (the embedding: the update of its untouched rows writes the upload buffer
+        while the gradient of the touched rows is still on its way)."""
         self.n = n
         self.dtype = dtype
         self.tier = tier
         if dtype == "bf16":
             self.master = _host_f32(n) if tier is None or tier[0] is None else None
             self.shared = pinned.tensor(n, torch.int16, copy_bytes)        # bf16 bits
-            self.grad_host = self.shared
+            self.grad_host = (pinned.tensor(n, torch.int16) if separate_grad
+                              else self.shared)
         else:
             self.master = pinned.tensor(n, torch.float32, copy_bytes)      # upload source
             self.shared = self.master
@@ -253,7 +262,8 @@ class SlideEngine:
                     offs, o = (None, o, o + reg), o + 2 * reg
             self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs,
                                       copy_bytes=self.w_bytes))
-        self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
+        self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True,
+                            separate_grad=True)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         # The LM head is updated, uploaded and flushed per vocabulary chunk of the fused CE, so
@@ -276,6 +286,12 @@ class SlideEngine:
         self.emb_job = [None] * self.emb_nch
         self.emb_ready = [None] * self.emb_nch
         self.emb_flushed = [None] * self.emb_nch
+        # Rows of the embedding that no input token of a step selects have an exactly zero
+        # gradient: their update needs no gradient copy, so it runs as soon as the step's gather
+        # has been issued (off the step boundary); after the backward only the selected rows
+        # are updated, chunk by chunk.
+        self.emb_zero_job = None
+        self.emb_present = None
 
         # device memory, allocated once
         dev = self.device
@@ -496,6 +512,7 @@ class SlideEngine:
         self.lm_job = [None] * self.lm_nch
         self.emb_ready = [self.embed.ready_ev] * self.emb_nch
         self.emb_job = [None] * self.emb_nch
+        self.emb_zero_job = None
         torch.cuda.synchronize(self.device)
 
     def _upload_resident(self, prm):
@@ -551,7 +568,9 @@ class SlideEngine:
             if not ready:
                 time.sleep(50e-6)
                 continue
-            job = min(ready, key=lambda j: (j.priority, j.seq))
+            # a step's updates before the next step's (every one is needed by that step's
+            # forward), then the one the next forward needs first
+            job = min(ready, key=lambda j: (j.step, j.priority, j.seq))
             with self.jobs_cv:
                 self.jobs.remove(job)
             try:
@@ -564,10 +583,16 @@ class SlideEngine:
                                 SLIDE_E_NONFINITE, "slide_nonfinite_count",
                                 f"{job.name}: {bad} NaN or infinite gradient elements in step "
                                 f"{job.step}; its update was not applied")
-                    if self.on_gradient is not None:
+                    if self.on_gradient is not None and job.g is not None:
                         self.on_gradient(job.name, job.step, job.off, job.g)
                     job.t_ready = time.perf_counter()
-                    if job.tier is None:
+                    if job.rows is not None:
+                        if len(job.rows):
+                            B.slide_cpu_adamw_rows(job.p, job.g, self.code, job.m, job.v,
+                                                   job.out, job.row_len, job.n // job.row_len,
+                                                   job.rows, len(job.rows), job.step, self.hp,
+                                                   self.adam_threads)
+                    elif job.tier is None:
                         B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
                                           job.step, self.hp, self.adam_threads)
                     else:
@@ -636,6 +661,7 @@ class SlideEngine:
             self._wait_job(self.lm_job[ci])
         for ci in range(self.emb_nch):
             self._wait_job(self.emb_job[ci])
+        self._wait_job(self.emb_zero_job)
 
     def close(self):
         """Wait for the pending updates and free every resource. A worker error is raised after
@@ -721,10 +747,11 @@ class SlideEngine:
             done.record(self.h2d)
         self.x_h2d_ev[i] = done
 
-    def _flush_chunk(self, prm, r0, r1, name, priority, rec, on_ready):
+    def _flush_chunk(self, prm, r0, r1, name, priority, rec, on_ready, rows=None):
         """D2H of rows [r0, r1) of a resident block's gradient once the compute stream has
         produced them, then those rows' AdamW, then the refreshed rows go back up on the H2D
-        stream (on_ready(event) is called with the upload's event). Returns (job, flush
+        stream (on_ready(event) is called with the upload's event). rows: update only these
+        rows (int32, relative to r0; the others were updated already). Returns (job, flush
         event)."""
         H = self.spec.hidden
         sl = slice(r0 * H, r1 * H)
@@ -751,7 +778,8 @@ class SlideEngine:
 
         out = prm.shared[sl] if prm.dtype == "bf16" else None
         job = _Job(name, done, prm.master[sl], prm.grad_host[sl], prm.m[sl], prm.v[sl], out,
-                   (r1 - r0) * H, self.step_count, priority, upload, off=r0 * H)
+                   (r1 - r0) * H, self.step_count, priority, upload, off=r0 * H, rows=rows,
+                   row_len=H)
         self._nf_attach(job)
         rec["other_jobs"].append(job)
         return job, done
@@ -768,14 +796,35 @@ class SlideEngine:
         self.lm_job[ci] = job
         return self._enqueue(job)
 
+    def _update_embed_zero_rows(self, rec):
+        """After this step's gather has been issued (and every earlier update of the embedding
+        is done): update the rows that no input token selects, whose gradient this step is
+        exactly zero, with no gradient copy. Their upload goes with the chunks after the
+        backward; this update runs before those chunks' (priority -2)."""
+        V, H = self.spec.vocab, self.spec.hidden
+        zero = np.ones(V, bool)
+        zero[self.emb_present] = False
+        rows = np.flatnonzero(zero).astype(np.int32)
+        prm = self.embed
+        out = prm.shared if prm.dtype == "bf16" else None
+        job = _Job("embed_zero", None, prm.master, None, prm.m, prm.v, out, V * H,
+                   self.step_count, -2, rows=rows, row_len=H)
+        rec["other_jobs"].append(job)
+        self.emb_zero_job = job
+        self._enqueue(job)
+
     def _flush_embed(self, rec):
-        """The embedding's gradient in row chunks, each flushed, updated (before every layer:
-        priorities -1 .. -1/n) and uploaded on its own."""
+        """The embedding's gradient in row chunks, each flushed, updated on the rows that this
+        step's tokens selected (before every layer: priorities -1 .. -1/n; the other rows were
+        updated during the step) and uploaded on its own."""
         for ci, (r0, r1) in enumerate(self.emb_rows):
             def ready(ev, ci=ci):
                 self.emb_ready[ci] = ev
+            pr = self.emb_present
+            sel = pr[(pr >= r0) & (pr < r1)] - r0
             job, done = self._flush_chunk(self.embed, r0, r1, f"embed{ci}",
-                                          -1 + ci / self.emb_nch, rec, ready)
+                                          -1 + ci / self.emb_nch, rec, ready,
+                                          rows=sel.astype(np.int32))
             self.emb_flushed[ci] = done
             self.emb_job[ci] = job
             self._enqueue(job)
@@ -830,6 +879,8 @@ class SlideEngine:
             if self.emb_flushed[ci] is not None:
                 c.wait_event(self.emb_flushed[ci])
         B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
+        self.emb_present = np.unique(np.asarray(tok[:, :-1])).astype(np.int32)
+        self._update_embed_zero_rows(rec)
         for i in range(L):
             if i not in slots:
                 prefetch(need=i)
@@ -1064,7 +1115,10 @@ class SlideEngine:
                 j = jobs[f"layer{i}"]
                 work_iv.append((d_start, d_end))
                 work_iv.append((j.t_start, j.t_end))
-                per_layer.append(dict(step=rec["step"], layer=i, t_bwd_ms=(be - bs) * 1e3,
+                fw = lr.get("fwd")
+                t_fwd = fw[0].elapsed_time(fw[1]) if fw is not None else None
+                per_layer.append(dict(step=rec["step"], layer=i, t_fwd_ms=t_fwd,
+                                      t_bwd_ms=(be - bs) * 1e3,
                                       t_d2h_ms=max(0.0, d_end - d_start) * 1e3,
                                       t_update_ms=(j.t_end - j.t_start) * 1e3))
         # merge GPU intervals

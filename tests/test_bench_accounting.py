@@ -115,3 +115,26 @@ def test_text_timeline_lanes():
     assert out[0] == "GPU |FF....CCC.BB.....|"
     assert out[1] == "D2H |...........:#:...|"      # 58-66 ms: 40%, 100%, 20% of columns
     assert out[2] == "CPU |.ee..........uuuu|"
+
+
+def test_noop_step_replay_worked_example():
+    """4 layers through 2 slots, worked out by hand: loads of layers 0, 1 and the embedding end
+    at 1.5, 3, 4; the forward runs 4.5-9.5 (layer 2 waits for its load until 7, layer 3 until
+    8.5); the head 9.5-12.5; the backward's reloads of layers 1 and 0 end at 16 and 18, so the
+    backward runs 12.5-20.5; the embedding's backward ends the step at 21."""
+    t = bench.noop_step_replay([1, 1, 1, 1], [2, 2, 2, 2], 2, 0.5, 3.0, 0.5, 1.5, 1.0, 1.0)
+    assert t == pytest.approx(21.0, abs=1e-12)
+
+
+def test_noop_step_replay_limits():
+    L, S = 32, 3
+    # uploads free: the step is the GPU's work
+    t = bench.noop_step_replay([2.0] * L, [5.0] * L, S, 0.1, 20.0, 1.0, 0.0, 0.0, 0.0)
+    assert t == pytest.approx(2.0 * L + 5.0 * L + 20.0 + 1.1)
+    # GPU free: the step is the upload link's work (every layer twice except the resident
+    # slots, the embedding and the LM head), plus nothing else
+    t = bench.noop_step_replay([0.0] * L, [0.0] * L, S, 0.0, 0.0, 0.0, 8.0, 18.0, 18.0)
+    assert t == pytest.approx((2 * L - S) * 8.0 + 18.0 + 18.0)
+    # one slot: no load can run ahead of the layer that holds the slot
+    t = bench.noop_step_replay([1.0] * 4, [1.0] * 4, 1, 0.0, 0.0, 0.0, 2.0, 0.0, 0.0)
+    assert t == pytest.approx(4 * (2.0 + 1.0) + 1.0 + 3 * (2.0 + 1.0))

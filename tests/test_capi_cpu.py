@@ -181,6 +181,54 @@ def test_cpu_adamw_shared_grad_and_bf16_buffer_and_scalar_path():
     np.testing.assert_array_equal(out3, bo)
 
 
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("zero_grad", [False, True])
+def test_cpu_adamw_rows_bit_exact_vs_oracle(gdt, zero_grad):
+    """Listed rows get the fixed-order AdamW of their gradient (zero when g is NULL), bit for
+    bit; rows not listed are untouched."""
+    rng = np.random.default_rng(13)
+    R, W = 37, 1000                     # odd row length: vector loop with a scalar tail per row
+    p = rng.standard_normal(R * W).astype(np.float32)
+    m = (rng.standard_normal(R * W) * 1e-3).astype(np.float32)
+    v = (rng.random(R * W) * 1e-6).astype(np.float32)
+    g32 = (rng.standard_normal(R * W) * 1e-2).astype(np.float32)
+    rows = np.array([0, 5, 6, 17, 36], np.int32)
+    if gdt == "bf16":
+        gbits = oa.bf16_round_bits(g32)
+        g_in, g_or, code = gbits, oa.bf16_bits_to_f32(gbits), sl.SLIDE_BF16
+    else:
+        g_in, g_or, code = g32, g32, sl.SLIDE_F32
+    if zero_grad:
+        g_or = np.zeros_like(g32)
+    p2, m2, v2, out = p.copy(), m.copy(), v.copy(), np.full(R * W, 7, np.uint16)
+    sl.slide_cpu_adamw_rows(p2, None if zero_grad else g_in, code, m2, v2, out, W, R, rows,
+                            len(rows), 3, CHP, 4)
+    po, mo, vo, bo = oa.adamw_fp32(p, g_or, m, v, 3, HP)
+    sel = np.zeros(R, bool)
+    sel[rows] = True
+    sel = np.repeat(sel, W)
+    np.testing.assert_array_equal(p2[sel].view(np.uint32), po[sel].view(np.uint32))
+    np.testing.assert_array_equal(m2[sel].view(np.uint32), mo[sel].view(np.uint32))
+    np.testing.assert_array_equal(v2[sel].view(np.uint32), vo[sel].view(np.uint32))
+    np.testing.assert_array_equal(out[sel], bo[sel])
+    np.testing.assert_array_equal(p2[~sel].view(np.uint32), p[~sel].view(np.uint32))
+    assert np.all(out[~sel] == 7)
+    with pytest.raises(sl.SlideError):            # a row outside the arrays
+        sl.slide_cpu_adamw_rows(p2, None, code, m2, v2, None, W, R,
+                                np.array([R], np.int32), 1, 1, CHP)
+
+
+def test_gpu_adamw_validates_before_any_launch():
+    a = np.zeros(16, np.float32)
+    with pytest.raises(sl.SlideError) as e:
+        sl.slide_gpu_adamw(None, a, sl.SLIDE_F32, a, a, None, 16, 1, CHP)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    with pytest.raises(sl.SlideError):            # step 0
+        sl.slide_gpu_adamw(a, a, sl.SLIDE_F32, a, a, None, 16, 0, CHP)
+    with pytest.raises(sl.SlideError):            # fp32 gradient aliasing the bf16 output
+        sl.slide_gpu_adamw(a, a, sl.SLIDE_F32, a.copy(), a.copy(), a, 16, 1, CHP)
+
+
 def test_host_triad_measures_and_validates():
     best, med = sl.slide_host_triad(1 << 20, 2, 3)
     assert best >= med > 0.0

@@ -1,0 +1,155 @@
+"""GPU AdamW and the HBM-resident trainer.
+
+slide_gpu_adamw follows the CPU optimizer's fixed float32 operation order, so it matches the
+oracle's adamw_fp32 bit for bit (NaN results are compared as NaN: their payload bits are not
+part of the contract). The resident trainer runs the offloaded engine's library calls with the
+optimizer on the GPU, so a resident step equals an offloaded step bit for bit: the offload, the
+ring and the overlap change nothing (the pages' offloaded training is plain training, faster)."""
+import numpy as np
+import pytest
+import torch
+
+import layer_sliding_offloaded_fwd_amd as sl
+from layer_sliding_offloaded_fwd_amd.engine import AdamW, ModelSpec, SlideEngine
+from layer_sliding_offloaded_fwd_amd.resident import ResidentTrainer
+from oracle import adamw as oa
+from seeded_inputs import TINY, LayerCfg, Workload, model_params, tokens
+from tests._gpu import DEV
+
+pytestmark = pytest.mark.gpu
+
+HP = oa.AdamWHyper(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+CHP = sl.AdamWHp(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay)
+
+
+def _adversarial(n, rng):
+    g = (rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17e-38, 3e38, -3e38, 1e-20, 65504.0,
+                        np.inf, -np.inf, np.nan], np.float32)
+    g[: len(special)] = special
+    return g
+
+
+def _same_f32(a, b, what):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    assert np.array_equal(na, nb), f"{what}: NaN positions differ"
+    bad = np.flatnonzero((a.view(np.uint32) != b.view(np.uint32)) & ~na)
+    assert bad.size == 0, f"{what}: {bad.size} elements differ, first at {bad[:5]}"
+
+
+def _same_bf16(a, b, what):
+    a, b = np.asarray(a, np.uint16), np.asarray(b, np.uint16)
+    na = ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)
+    nb = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    assert np.array_equal(na, nb), f"{what}: NaN positions differ"
+    bad = np.flatnonzero((a != b) & ~na)
+    assert bad.size == 0, f"{what}: {bad.size} elements differ, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_gpu_adamw_bit_exact_vs_oracle(gdt, offset):
+    """offset 3: the arrays start 12 (6) bytes past an aligned address, so only the per-element
+    path applies; offset 0: 8-element vector groups plus a ragged tail."""
+    print(f"gpu adamw {gdt} offset {offset}", flush=True)
+    rng = np.random.default_rng(11)
+    n = 100_003
+    p = rng.standard_normal(n).astype(np.float32)
+    p[:4] = [0.0, -0.0, 1e-40, 3e38]
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dp, dm, dv = (torch.zeros(n + offset, dtype=torch.float32, device=DEV) for _ in range(3))
+    dp[offset:] = torch.from_numpy(p)
+    out = torch.zeros(n + offset, dtype=torch.int16, device=DEV)
+    po, mo, vo = p.copy(), m.copy(), v.copy()
+    st = torch.cuda.current_stream()
+    for t in range(1, 5):
+        g32 = _adversarial(n, rng) if t == 2 else (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        if gdt == "bf16":
+            gbits = oa.bf16_round_bits(g32)
+            g_or = oa.bf16_bits_to_f32(gbits)
+            dg = torch.zeros(n + offset, dtype=torch.int16, device=DEV)
+            dg[offset:] = torch.from_numpy(gbits.view(np.int16))
+            code = sl.SLIDE_BF16
+        else:
+            g_or = g32
+            dg = torch.zeros(n + offset, dtype=torch.float32, device=DEV)
+            dg[offset:] = torch.from_numpy(g32)
+            code = sl.SLIDE_F32
+        sl.slide_gpu_adamw(dp[offset:], dg[offset:], code, dm[offset:], dv[offset:],
+                           out[offset:], n, t, CHP, st)
+        torch.cuda.synchronize()
+        po, mo, vo, bo = oa.adamw_fp32(po, g_or, mo, vo, t, HP)
+        _same_f32(dp[offset:].cpu().numpy(), po, f"step {t} p")
+        _same_f32(dm[offset:].cpu().numpy(), mo, f"step {t} m")
+        _same_f32(dv[offset:].cpu().numpy(), vo, f"step {t} v")
+        _same_bf16(out[offset:].cpu().numpy().view(np.uint16), bo, f"step {t} bf16 copy")
+
+
+def test_gpu_adamw_in_place_bf16_buffer():
+    """The bf16 gradient buffer may double as the bf16 weight output."""
+    rng = np.random.default_rng(12)
+    n = 4099
+    p = rng.standard_normal(n).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.random(n) * 1e-6).astype(np.float32)
+    g = oa.bf16_round_bits((rng.standard_normal(n) * 1e-2).astype(np.float32))
+    po, mo, vo, bo = oa.adamw_fp32(p, oa.bf16_bits_to_f32(g), m, v, 7, HP)
+    dp, dm, dv = (torch.from_numpy(a.copy()).to(DEV) for a in (p, m, v))
+    shared = torch.from_numpy(g.view(np.int16).copy()).to(DEV)
+    sl.slide_gpu_adamw(dp, shared, sl.SLIDE_BF16, dm, dv, shared, n, 7, CHP,
+                       torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(shared.cpu().numpy().view(np.uint16), bo)
+    assert np.array_equal(dp.cpu().numpy().view(np.uint32), po.view(np.uint32))
+
+
+SMALL = Workload("small-bf16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "bf16")
+RAGGED = Workload("ragged-vocab-bf16", LayerCfg(256, 4, 2, 64, 688), 3, 1000, 2, 64, "bf16")
+
+
+def _spec(w):
+    c = w.layer
+    return ModelSpec(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.vocab, w.n_layers,
+                     w.dtype, c.rms_eps, c.rope_theta)
+
+
+@pytest.mark.parametrize("w,ce_chunk,steps", [(SMALL, 256, 3), (RAGGED, 256, 2),
+                                              (TINY, 8192, 2)], ids=["bf16", "ragged", "f32"])
+def test_resident_step_equals_offloaded_step(w, ce_chunk, steps):
+    print(f"resident vs offloaded: {w.name} steps={steps}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    flat = [np.concatenate([lp[n].f32.reshape(-1) for n, _ in w.layer.param_shapes()])
+            for lp in params["layers"]]
+    toks = [tokens(w.batch, w.seq, w.vocab, seed=50 + s) for s in range(steps)]
+    hp = AdamW(lr=1e-3)
+
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=hp, adam_threads=3,
+                      ce_chunk=ce_chunk)
+    try:
+        eng.load_params(params["embed"].f32, flat, params["w_final"].f32, params["lm_head"].f32)
+        la = []
+        for t in toks:
+            eng.step(t)
+            la.append(eng.loss())
+        pa = eng.master_params()
+    finally:
+        eng.close()
+    res = ResidentTrainer(_spec(w), w.batch, w.seq, ce_chunk=ce_chunk, hp=hp)
+    res.load_params(params["embed"].f32, flat, params["w_final"].f32, params["lm_head"].f32)
+    lb = []
+    for t in toks:
+        res.step(t)
+        lb.append(res.loss())
+    pb = res.master_params()
+    print(f"  losses offloaded {la} resident {lb}", flush=True)
+    assert la == lb
+    for k in ("embed", "w_final", "lm_head"):
+        assert np.array_equal(pa[k].view(np.uint32), pb[k].view(np.uint32)), k
+    for i, (x, y) in enumerate(zip(pa["layers"], pb["layers"])):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"layer {i}"
+    if w.dtype == "bf16":   # compute copies are the bf16 rounding of the masters
+        for i in range(w.n_layers):
+            dbits = res.layers.dev[i].view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(dbits, oa.bf16_round_bits(pb["layers"][i])), f"layer {i}"
