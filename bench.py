@@ -162,6 +162,9 @@ def _parse():
                          "the last two steps, 10 ms per column)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
+    ap.add_argument("--embed-split", action="store_true",
+                    help="update the embedding's rows that no token selects during the step and "
+                         "only the selected rows after the backward")
     ap.add_argument("--adam-threads", type=int, default=0,
                     help="CPU AdamW threads (default: cores - 3, leaving cores to the engine thread and the HIP runtime)")
     return ap.parse_args()
@@ -358,7 +361,7 @@ def run_step(w, args):
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True,
                       activations=args.activations, keep_records=args.steps + args.warmup,
-                      **tier_kw)
+                      embed_split=args.embed_split, **tier_kw)
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)

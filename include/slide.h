@@ -18,8 +18,9 @@
  *  - Streams and events are passed as `void*` holding a hipStream_t / hipEvent_t (NULL = the
  *    default stream). GPU calls are asynchronous on the given stream; launch failures return
  *    SLIDE_E_HIP. Arguments and shapes are validated on the host before anything is launched.
- *  - Element types: SLIDE_BF16 tensors are uint16 bf16 bit patterns; SLIDE_F32 tensors are
- *    float. Accumulation, softmax, log-sum-exp and norm statistics are always fp32.
+ *  - Element types: SLIDE_BF16 tensors are uint16 bf16 bit patterns, SLIDE_F16 tensors IEEE
+ *    binary16, SLIDE_F32 tensors float. Accumulation, softmax, log-sum-exp and norm statistics
+ *    are always fp32.
  *  - Layouts are row-major. A weight matrix W is [out, in] and a projection is y = x W^T.
  *    Activations are [N, features] with N = B*S tokens, token t = b*S + s at position s.
  *  - Device pointers must be 16-byte aligned; feature sizes must be multiples of 8.
@@ -48,7 +49,9 @@ enum {
   SLIDE_E_IO = -9            /* a file operation of the disk tier failed (errno in the message) */
 };
 
-typedef enum { SLIDE_F32 = 0, SLIDE_BF16 = 1 } slide_dtype;
+/* SLIDE_F16: IEEE binary16 compute (the pages name FP16 beside BF16 for the GPU's compute and
+ * the host buffers' conversions, summary section 2B), used with dynamic loss scaling. */
+typedef enum { SLIDE_F32 = 0, SLIDE_BF16 = 1, SLIDE_F16 = 2 } slide_dtype;
 
 const char* slide_last_error(void);
 const char* slide_version(void);
@@ -130,6 +133,9 @@ typedef struct {
   int32_t vocab;   /* V, multiple of 8 */
   int32_t chunk;   /* vocabulary chunk C (multiple of 8); 0 selects 8192 */
   int32_t dtype;   /* slide_dtype of h, W, dh, dW */
+  /* Gradient scale S (dynamic loss scaling of fp16 training): dh and dW are the gradients of S
+   * times the mean loss (dz carries S / N_valid); the reported loss is not scaled. 0 means 1. */
+  float grad_scale;
 } slide_ce_cfg;
 
 size_t slide_lmhead_ce_workspace_bytes(const slide_ce_cfg* cfg, int N);
@@ -290,13 +296,20 @@ int slide_nonfinite_count(const void* x, int dtype, size_t n, uint32_t* count_de
  *   per element (float32, round to nearest-even, no fused multiply-add):
  *   p1 = p*c_dec; m = beta1*m + c_1b1*g; v = beta2*v + c_1b2*(g*g);
  *   den = sqrt(v)/c_bc2 + eps; p = p1 - c_step*(m/den); p_bf16 = bf16_rne(p)
- * p, m, v: float [n] host memory, updated in place. g: [n] of g_dtype (SLIDE_BF16 or
- * SLIDE_F32). p_bf16_out: optional uint16 [n]; it may alias g when g_dtype is SLIDE_BF16
- * (the gradient landing buffer and the bf16 weight copy are one shared host buffer).
+ * with g read as float (exact widening) and multiplied by c_gs = float(1/hp->grad_scale) when
+ * hp->grad_scale is neither 0 nor 1.
+ * p, m, v: float [n] host memory, updated in place. g: [n] of g_dtype (SLIDE_BF16, SLIDE_F16 or
+ * SLIDE_F32). p_bf16_out: optional uint16 [n] 16-bit copy of p, rounded to nearest-even, in
+ * g's type when g is 16-bit (bf16 for an fp32 g); it may alias g when g is 16-bit (the
+ * gradient landing buffer and the 16-bit weight copy are one shared host buffer).
  * n_threads <= 0 uses the available cores. Blocks until done.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   double lr, beta1, beta2, eps, weight_decay;
+  /* The loss scale the gradient was computed at (dynamic loss scaling of fp16 training): the
+   * update uses g * c_gs with c_gs = float(1 / grad_scale), a power of two in practice, so the
+   * product is exact. 0 or 1: unscaled (c_gs = 1, no change to any result). */
+  double grad_scale;
 } slide_adamw_hp;
 int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
                     uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
@@ -321,6 +334,12 @@ int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float* m, float* 
 int slide_gpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
                     uint16_t* p_bf16_out, size_t n, int64_t step, const slide_adamw_hp* hp,
                     void* stream);
+
+/* fp32 -> 16-bit conversion on the host, n_threads threads: dst [n] in dst_dtype (SLIDE_BF16 or
+ * SLIDE_F16), rounded to nearest-even, NaN kept as a quiet NaN; the 16-bit compute copy of
+ * fp32 master weights (summary, section 2B: FP32 -> BF16/FP16 conversion in the shared host
+ * buffers). SLIDE_E_ARG for a null pointer or another dtype. Blocks until done. */
+int slide_cpu_convert_f32(const float* src, void* dst, int dst_dtype, size_t n, int n_threads);
 
 /* The host-DRAM roofline of the CPU optimizer (summary, section 2B: the optimizer state lives
  * in host memory, so the update of a layer is bound by host memory bandwidth): a STREAM triad

@@ -9,7 +9,7 @@ SLIDE_E_ARG, SLIDE_E_SHAPE, SLIDE_E_WORKSPACE, SLIDE_E_HIP = -1, -2, -3, -4
 SLIDE_E_STATE, SLIDE_E_TIMEOUT, SLIDE_E_UNSUPPORTED, SLIDE_E_NONFINITE = -5, -6, -7, -8
 SLIDE_E_IO = -9
 SLIDE_TIER_DIRECT, SLIDE_TIER_UNLINK = 1, 2
-SLIDE_F32, SLIDE_BF16 = 0, 1
+SLIDE_F32, SLIDE_BF16, SLIDE_F16 = 0, 1, 2
 SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST = 0, 1
 SLOT_FREE, SLOT_LOADING, SLOT_IN_USE, SLOT_FLUSHING = 0, 1, 2, 3
 ERROR_NAMES = {0: "SLIDE_OK", -1: "SLIDE_E_ARG", -2: "SLIDE_E_SHAPE", -3: "SLIDE_E_WORKSPACE",
@@ -26,12 +26,14 @@ class LayerCfg(ctypes.Structure):
 
 class CeCfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("grad_scale", ctypes.c_float)]
 
 
 class AdamWHp(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
-                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("grad_scale", ctypes.c_double)]
 
 
 P = ctypes.c_void_p
@@ -89,6 +91,7 @@ SIGNATURES = {
     "slide_cpu_adamw_rows": (I, [P, P, I, P, P, P, SZ, SZ, P, SZ, ctypes.c_int64,
                                  ctypes.POINTER(AdamWHp), I]),
     "slide_gpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), P]),
+    "slide_cpu_convert_f32": (I, [P, P, I, SZ, I]),
     "slide_host_triad": (I, [SZ, I, I, ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_double)]),
     "slide_nonfinite_count": (I, [P, I, SZ, P, P]),

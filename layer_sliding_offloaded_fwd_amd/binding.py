@@ -6,11 +6,13 @@ runs in libslide's kernels; a non-zero status raises SlideError carrying slide_l
 """
 import ctypes
 
-from ._capi import (AdamWHp, CeCfg, LayerCfg, SlideError, call, lib, SLIDE_BF16, SLIDE_F32,
-                    SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_TIER_DIRECT, SLIDE_TIER_UNLINK)
+from ._capi import (AdamWHp, CeCfg, LayerCfg, SlideError, call, lib, SLIDE_BF16, SLIDE_F16,
+                    SLIDE_F32, SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_TIER_DIRECT,
+                    SLIDE_TIER_UNLINK)
 
 __all__ = [
-    "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F32", "SLIDE_ENGINE_HIP",
+    "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F16", "SLIDE_F32",
+    "SLIDE_ENGINE_HIP",
     "SLIDE_ENGINE_HOST", "slide_layer_param_count", "slide_layer_param_offsets",
     "slide_layer_workspace_bytes", "slide_layer_fwd", "slide_layer_bwd",
     "slide_layer_saved_bytes", "slide_layer_fwd_save", "slide_layer_bwd_saved",
@@ -22,7 +24,7 @@ __all__ = [
     "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows", "slide_gpu_adamw",
-    "slide_host_triad", "StateTier",
+    "slide_cpu_convert_f32", "slide_host_triad", "StateTier",
     "slide_tier_region_bytes",
     "slide_nonfinite_count",
     "SLIDE_TIER_DIRECT", "SLIDE_TIER_UNLINK", "slide_prof_enable", "slide_prof_reset",
@@ -51,10 +53,12 @@ def _s(stream):
 
 
 def dtype_code(dt):
-    """'bf16' / 'f32' / torch dtype -> SLIDE_BF16 / SLIDE_F32."""
+    """'bf16' / 'f16' / 'f32' / torch dtype -> SLIDE_BF16 / SLIDE_F16 / SLIDE_F32."""
     s = str(dt)
     if "bf16" in s or "bfloat16" in s:
         return SLIDE_BF16
+    if s in ("f16", "torch.float16", "float16"):
+        return SLIDE_F16
     if "f32" in s or "float32" in s:
         return SLIDE_F32
     raise ValueError(f"unsupported dtype {dt}")
@@ -289,6 +293,11 @@ def slide_gpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, stream=None):
     """p, m, v: float32 device tensors; g: device bf16 or float32; hp: AdamWHp."""
     call("slide_gpu_adamw", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), n, step,
          ctypes.byref(hp), _s(stream))
+
+
+def slide_cpu_convert_f32(src, dst, dst_dtype, n, n_threads=0):
+    """fp32 host array -> bf16 / fp16 bit patterns (round to nearest-even)."""
+    call("slide_cpu_convert_f32", _p(src), _p(dst), dst_dtype, n, n_threads)
 
 
 def slide_host_triad(n, n_threads=0, reps=3):

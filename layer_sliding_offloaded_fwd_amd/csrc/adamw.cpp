@@ -36,6 +36,11 @@ inline float widen_bf16(uint16_t b) {
   return f;
 }
 
+__attribute__((target("f16c"))) inline float widen_f16(uint16_t h) { return _cvtsh_ss(h); }
+__attribute__((target("f16c"))) inline uint16_t f16_rne(float f) {
+  return (uint16_t)_cvtss_sh(f, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+}
+
 inline uint16_t bf16_rne(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
@@ -44,8 +49,20 @@ inline uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// One element; g is already widened to float.
-inline void step1(float& p, float g, float& m, float& v, uint16_t* out, const Consts& c) {
+// Gradient element i of g_dtype as float (exact), unscaled by c_gs when the gradient carries a
+// loss scale.
+inline float grad_at(const void* g, int gdt, size_t i, const Consts& c) {
+  float gi = gdt == SLIDE_BF16   ? widen_bf16(((const uint16_t*)g)[i])
+             : gdt == SLIDE_F16 ? widen_f16(((const uint16_t*)g)[i])
+                                : ((const float*)g)[i];
+  if (c.c_gs != 1.0f) gi = gi * c.c_gs;
+  return gi;
+}
+
+// One element; g is already widened to float. The 16-bit copy is fp16 when the gradient is
+// (f16_out), else bf16.
+inline void step1(float& p, float g, float& m, float& v, uint16_t* out, const Consts& c,
+                  bool f16_out = false) {
   float p1 = p * c.c_dec;
   float a = c.c_b1 * m;
   float b = c.c_1b1 * g;
@@ -63,15 +80,14 @@ inline void step1(float& p, float g, float& m, float& v, uint16_t* out, const Co
   p = p2;
   m = m2;
   v = v2;
-  if (out) *out = bf16_rne(p2);
+  if (out) *out = f16_out ? f16_rne(p2) : bf16_rne(p2);
 }
 
 void range_scalar(float* p, const void* g, int gdt, float* m, float* v, uint16_t* out,
                   size_t lo, size_t hi, const Consts& c) {
-  for (size_t i = lo; i < hi; ++i) {
-    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
-    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
-  }
+  for (size_t i = lo; i < hi; ++i)
+    step1(p[i], grad_at(g, gdt, i, c), m[i], v[i], out ? out + i : nullptr, c,
+          gdt == SLIDE_F16);
 }
 
 __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const void* g, int gdt,
@@ -85,11 +101,12 @@ __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const vo
   const __m512i exp_mask = _mm512_set1_epi32(0x7fffffff), inf_bits = _mm512_set1_epi32(0x7f800000),
                 bias = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1),
                 quiet = _mm512_set1_epi32(0x40);
+  const __m512 c_gs = _mm512_set1_ps(c.c_gs);
+  const bool scaled = c.c_gs != 1.0f, f16 = gdt == SLIDE_F16;
   size_t i = lo;
   // scalar head up to 64-byte alignment of p
   while (i < hi && (((uintptr_t)(p + i)) & 63u)) {
-    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
-    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
+    step1(p[i], grad_at(g, gdt, i, c), m[i], v[i], out ? out + i : nullptr, c, f16);
     ++i;
   }
   for (; i + 16 <= hi; i += 16) {
@@ -97,9 +114,12 @@ __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const vo
     if (gdt == SLIDE_BF16) {
       __m256i gb = _mm256_loadu_si256((const __m256i*)((const uint16_t*)g + i));
       gv = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(gb), 16));
+    } else if (f16) {
+      gv = _mm512_cvtph_ps(_mm256_loadu_si256((const __m256i*)((const uint16_t*)g + i)));
     } else {
       gv = _mm512_loadu_ps((const float*)g + i);
     }
+    if (scaled) gv = _mm512_mul_ps(gv, c_gs);
     __m512 pv = _mm512_load_ps(p + i);
     __m512 mv = _mm512_loadu_ps(m + i);
     __m512 vv = _mm512_loadu_ps(v + i);
@@ -111,7 +131,10 @@ __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const vo
     _mm512_store_ps(p + i, p2);
     _mm512_storeu_ps(m + i, m2);
     _mm512_storeu_ps(v + i, v2);
-    if (out) {
+    if (out && f16) {
+      _mm256_storeu_si256((__m256i*)(out + i),
+                          _mm512_cvtps_ph(p2, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC));
+    } else if (out) {
       __m512i u = _mm512_castps_si512(p2);
       __mmask16 isnan = _mm512_cmpgt_epu32_mask(_mm512_and_si512(u, exp_mask), inf_bits);
       __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), one);
@@ -121,10 +144,8 @@ __attribute__((target("avx512f,avx512bw"))) void range_avx512(float* p, const vo
       _mm256_storeu_si256((__m256i*)(out + i), _mm512_cvtepi32_epi16(res));
     }
   }
-  for (; i < hi; ++i) {
-    float gi = gdt == SLIDE_BF16 ? widen_bf16(((const uint16_t*)g)[i]) : ((const float*)g)[i];
-    step1(p[i], gi, m[i], v[i], out ? out + i : nullptr, c);
-  }
+  for (; i < hi; ++i)
+    step1(p[i], grad_at(g, gdt, i, c), m[i], v[i], out ? out + i : nullptr, c, f16);
 }
 
 }  // namespace
@@ -134,8 +155,10 @@ int slide::adamw_check(const char* who, const void* p, const void* g, int g_dtyp
                        int64_t step, const slide_adamw_hp* hp) {
   using slide::fail;
   if (!p || !g || !m || !v || !hp) return fail(SLIDE_E_ARG, "%s: null pointer", who);
-  if (g_dtype != SLIDE_BF16 && g_dtype != SLIDE_F32)
-    return fail(SLIDE_E_ARG, "%s: g_dtype must be SLIDE_BF16 or SLIDE_F32", who);
+  if (g_dtype != SLIDE_BF16 && g_dtype != SLIDE_F16 && g_dtype != SLIDE_F32)
+    return fail(SLIDE_E_ARG, "%s: g_dtype must be SLIDE_BF16, SLIDE_F16 or SLIDE_F32", who);
+  if (!(hp->grad_scale >= 0))
+    return fail(SLIDE_E_ARG, "%s: grad_scale must be >= 0", who);
   if (step < 1) return fail(SLIDE_E_ARG, "%s: step must be >= 1 (got %lld)", who, (long long)step);
   if (!(hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && hp->eps > 0 &&
         hp->lr >= 0 && hp->weight_decay >= 0))
@@ -144,12 +167,12 @@ int slide::adamw_check(const char* who, const void* p, const void* g, int g_dtyp
     // overlapping but not identical buffers would read already-written values
     const char* a = (const char*)p_bf16_out;
     const char* b = (const char*)g;
-    size_t gb = n * (g_dtype == SLIDE_BF16 ? 2 : 4);
+    size_t gb = n * (g_dtype == SLIDE_F32 ? 4 : 2);
     if (a < b + gb && b < a + n * 2)
       return fail(SLIDE_E_ARG, "%s: p_bf16_out partially overlaps g", who);
   }
-  if (p_bf16_out && p_bf16_out == g && g_dtype != SLIDE_BF16)
-    return fail(SLIDE_E_ARG, "%s: p_bf16_out may alias g only for bf16 g", who);
+  if (p_bf16_out && p_bf16_out == g && g_dtype == SLIDE_F32)
+    return fail(SLIDE_E_ARG, "%s: p_bf16_out may alias g only for a 16-bit g", who);
   return SLIDE_OK;
 }
 
@@ -210,13 +233,14 @@ extern "C" int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float*
                   n_rows_total);
   const Consts c = make_consts(*hp, step);
   const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
-  const size_t gsz = g_dtype == SLIDE_BF16 ? 2 : 4;
+  const size_t gsz = g_dtype == SLIDE_F32 ? 4 : 2;
   auto work = [&](size_t k0, size_t k1) {
     std::vector<uint16_t> zeros(g ? 0 : row_len, 0);   // bf16 +0.0 widens to +0.0f
     for (size_t k = k0; k < k1; ++k) {
       const size_t o = (size_t)rows[k] * row_len;
+      // zero rows: +0.0 in the gradient's 16-bit type (widens to +0.0f), so the copy keeps it
       const void* gr = g ? (const void*)((const char*)g + o * gsz) : (const void*)zeros.data();
-      const int gd = g ? g_dtype : SLIDE_BF16;
+      const int gd = g ? g_dtype : (g_dtype == SLIDE_F16 ? SLIDE_F16 : SLIDE_BF16);
       uint16_t* outr = p_bf16_out ? p_bf16_out + o : nullptr;
       if (avx512) range_avx512(p + o, gr, gd, m + o, v + o, outr, 0, row_len, c);
       else range_scalar(p + o, gr, gd, m + o, v + o, outr, 0, row_len, c);
@@ -247,6 +271,35 @@ extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dt
                                                const slide_adamw_hp* hp) {
   if (!p || !g || !m || !v || !hp || step < 1) return SLIDE_E_ARG;
   range_scalar(p, g, g_dtype, m, v, out, 0, n, make_consts(*hp, step));
+  return SLIDE_OK;
+}
+
+extern "C" int slide_cpu_convert_f32(const float* src, void* dst, int dst_dtype, size_t n,
+                                     int n_threads) {
+  using slide::fail;
+  if (n == 0) return SLIDE_OK;
+  if (!src || !dst) return fail(SLIDE_E_ARG, "slide_cpu_convert_f32: null pointer");
+  if (dst_dtype != SLIDE_BF16 && dst_dtype != SLIDE_F16)
+    return fail(SLIDE_E_ARG, "slide_cpu_convert_f32: dst_dtype must be SLIDE_BF16 or SLIDE_F16");
+  uint16_t* d = (uint16_t*)dst;
+  const bool f16 = dst_dtype == SLIDE_F16;
+  auto work = [&](size_t lo, size_t hi) {
+    for (size_t i = lo; i < hi; ++i) d[i] = f16 ? f16_rne(src[i]) : bf16_rne(src[i]);
+  };
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::max<size_t>(1, std::min<size_t>((size_t)nt, (n + 65535) / 65536));
+  if (nt == 1) {
+    work(0, n);
+    return SLIDE_OK;
+  }
+  std::vector<std::thread> th;
+  const size_t per = (n + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    const size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
+    if (lo >= hi) break;
+    th.emplace_back(work, lo, hi);
+  }
+  for (auto& x : th) x.join();
   return SLIDE_OK;
 }
 

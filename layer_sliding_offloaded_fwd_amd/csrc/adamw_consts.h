@@ -11,6 +11,7 @@ namespace slide {
 
 struct AdamConsts {
   float c_dec, c_b1, c_1b1, c_b2, c_1b2, c_step, c_bc2, c_eps;
+  float c_gs;   // 1 / grad_scale (the loss scale the gradient was computed at), 1 if unscaled
 };
 
 // Computed in double and cast once to float: b1t = beta1^t and b2t = beta2^t by t repeated
@@ -30,6 +31,7 @@ inline AdamConsts adam_consts(const slide_adamw_hp& hp, int64_t t) {
   c.c_step = (float)(hp.lr / (1.0 - b1t));
   c.c_bc2 = (float)sqrt(1.0 - b2t);
   c.c_eps = (float)hp.eps;
+  c.c_gs = (float)(1.0 / (hp.grad_scale > 0 ? hp.grad_scale : 1.0));
   return c;
 }
 

@@ -21,6 +21,17 @@ __device__ __forceinline__ uint16_t rne_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// the 16-bit copy: fp16 for an fp16 gradient, bf16 otherwise (both round to nearest-even)
+template <int GDT>
+__device__ __forceinline__ uint16_t copy16(float f) {
+  if constexpr (GDT == SLIDE_F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
+  else return rne_bf16(f);
+}
+template <int GDT>
+__device__ __forceinline__ float widen16(uint16_t b) {
+  if constexpr (GDT == SLIDE_F16) return (float)__builtin_bit_cast(_Float16, b);
+  else return bf2f(b);
+}
 
 __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, const AdamConsts& c) {
   const float p1 = p * c.c_dec;
@@ -34,7 +45,7 @@ __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, con
 
 // 8 consecutive elements per thread with 16-byte accesses (all pointers 16-byte aligned and
 // n8 = n / 8 groups), or one element per thread (scalar = true) for the rest.
-template <bool BF16G, bool SCALAR>
+template <int GDT, bool SCALAR>
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const void* g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     uint16_t* out, size_t lo, size_t n,
@@ -43,13 +54,14 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
   if constexpr (SCALAR) {
     const size_t i = lo + t;
     if (i >= n) return;
-    float gi = BF16G ? bf2f(((const uint16_t*)g)[i]) : ((const float*)g)[i];
+    float gi = GDT == SLIDE_F32 ? ((const float*)g)[i] : widen16<GDT>(((const uint16_t*)g)[i]);
+    if (c.c_gs != 1.0f) gi = gi * c.c_gs;
     float pi = p[i], mi = m[i], vi = v[i];
     adam1(pi, gi, mi, vi, c);
     p[i] = pi;
     m[i] = mi;
     v[i] = vi;
-    if (out) out[i] = rne_bf16(pi);
+    if (out) out[i] = copy16<GDT>(pi);
   } else {
     const size_t i = t * 8;
     if (i + 8 > n) return;
@@ -60,18 +72,21 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
     *(float4*)&mm[4] = *(const float4*)(m + i + 4);
     *(float4*)&vv[0] = *(const float4*)(v + i);
     *(float4*)&vv[4] = *(const float4*)(v + i + 4);
-    if constexpr (BF16G) {
+    if constexpr (GDT != SLIDE_F32) {
       const uint4 gb = *(const uint4*)((const uint16_t*)g + i);
       const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        gg[2 * k] = __uint_as_float(w[k] << 16);
-        gg[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        gg[2 * k] = widen16<GDT>((uint16_t)(w[k] & 0xffffu));
+        gg[2 * k + 1] = widen16<GDT>((uint16_t)(w[k] >> 16));
       }
     } else {
       *(float4*)&gg[0] = *(const float4*)((const float*)g + i);
       *(float4*)&gg[4] = *(const float4*)((const float*)g + i + 4);
     }
+    if (c.c_gs != 1.0f)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) gg[k] = gg[k] * c.c_gs;
 #pragma unroll
     for (int k = 0; k < 8; ++k) adam1(pp[k], gg[k], mm[k], vv[k], c);
     *(float4*)(p + i) = *(float4*)&pp[0];
@@ -82,16 +97,16 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
     *(float4*)(v + i + 4) = *(float4*)&vv[4];
     if (out) {
       uint4 o;
-      o.x = (uint32_t)rne_bf16(pp[0]) | ((uint32_t)rne_bf16(pp[1]) << 16);
-      o.y = (uint32_t)rne_bf16(pp[2]) | ((uint32_t)rne_bf16(pp[3]) << 16);
-      o.z = (uint32_t)rne_bf16(pp[4]) | ((uint32_t)rne_bf16(pp[5]) << 16);
-      o.w = (uint32_t)rne_bf16(pp[6]) | ((uint32_t)rne_bf16(pp[7]) << 16);
+      o.x = (uint32_t)copy16<GDT>(pp[0]) | ((uint32_t)copy16<GDT>(pp[1]) << 16);
+      o.y = (uint32_t)copy16<GDT>(pp[2]) | ((uint32_t)copy16<GDT>(pp[3]) << 16);
+      o.z = (uint32_t)copy16<GDT>(pp[4]) | ((uint32_t)copy16<GDT>(pp[5]) << 16);
+      o.w = (uint32_t)copy16<GDT>(pp[6]) | ((uint32_t)copy16<GDT>(pp[7]) << 16);
       *(uint4*)(out + i) = o;
     }
   }
 }
 
-template <bool BF16G>
+template <int GDT>
 void launch(float* p, const void* g, float* m, float* v, uint16_t* out, size_t n,
             const AdamConsts& c, hipStream_t st) {
   const bool vec = aligned16(p) && aligned16(g) && aligned16(m) && aligned16(v) &&
@@ -99,12 +114,12 @@ void launch(float* p, const void* g, float* m, float* v, uint16_t* out, size_t n
   size_t done = 0;
   if (vec && n >= 8) {
     const size_t groups = n / 8;
-    hipLaunchKernelGGL((adamw_kernel<BF16G, false>), dim3((unsigned)((groups + 255) / 256)),
+    hipLaunchKernelGGL((adamw_kernel<GDT, false>), dim3((unsigned)((groups + 255) / 256)),
                        dim3(256), 0, st, p, g, m, v, out, (size_t)0, n, c);
     done = groups * 8;
   }
   if (done < n)
-    hipLaunchKernelGGL((adamw_kernel<BF16G, true>), dim3((unsigned)((n - done + 255) / 256)),
+    hipLaunchKernelGGL((adamw_kernel<GDT, true>), dim3((unsigned)((n - done + 255) / 256)),
                        dim3(256), 0, st, p, g, m, v, out, done, n, c);
 }
 
@@ -121,8 +136,10 @@ extern "C" int slide_gpu_adamw(float* p, const void* g, int g_dtype, float* m, f
   const AdamConsts c = adam_consts(*hp, step);
   ProfScope ps("gpu_adamw", (hipStream_t)stream);
   if (g_dtype == SLIDE_BF16)
-    launch<true>(p, g, m, v, p_bf16_out, n, c, (hipStream_t)stream);
+    launch<SLIDE_BF16>(p, g, m, v, p_bf16_out, n, c, (hipStream_t)stream);
+  else if (g_dtype == SLIDE_F16)
+    launch<SLIDE_F16>(p, g, m, v, p_bf16_out, n, c, (hipStream_t)stream);
   else
-    launch<false>(p, g, m, v, p_bf16_out, n, c, (hipStream_t)stream);
+    launch<SLIDE_F32>(p, g, m, v, p_bf16_out, n, c, (hipStream_t)stream);
   return check_launch("slide_gpu_adamw");
 }

@@ -4,8 +4,8 @@
 // The pages leave attention itself unspecified (they optimise RoPE, RMSNorm and SwiGLU around
 // it: SlideFormer summary, section 2C); this is the standard definition for the Llama family.
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, flash-style, no [S, S]
-// tensor in memory):
+// 16-bit path (bf16 or fp16 operands: gfx950 MFMA v_mfma_f32_32x32x16_bf16 / _f16, fp32
+// accumulation, flash-style, no [S, S] tensor in memory):
 //  * every operand tile is [64 rows][d] of q, k, v or dO rows, copied global -> LDS by
 //    direct-to-LDS loads into 2 pipelined stages (the next block in flight while one is
 //    computed). The forward and dQ kernels are held to 256 registers per lane so that two
@@ -30,9 +30,6 @@
 #include "attention.h"
 
 namespace slide {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 namespace {
 
@@ -146,7 +143,7 @@ __device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "
 
 // Stage a wave's 32 x D output tile (held transposed in accumulators) through LDS and write
 // 16-byte row chunks: out row r (0..31) of this wave goes to dst + (row0 + r) * stride.
-template <int D>
+template <int D, int DT>
 __device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc, float scale,
                                              bf16_t* dst, int stride, int row0, int nvalid,
                                              int lane) {
@@ -157,7 +154,7 @@ __device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc,
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int d = db * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-      stage[lr * LS + d] = f2bf(acc[db][e] * scale);
+      stage[lr * LS + d] = Bits16<DT>::from_f(acc[db][e] * scale);
     }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
@@ -167,12 +164,6 @@ __device__ __forceinline__ void store_tile_t(bf16_t* stage, const f32x16_t* acc,
   }
 }
 
-__device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 b8;
-  b8 r = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3],
-          (__bf16)v[4], (__bf16)v[5], (__bf16)v[6], (__bf16)v[7]};
-  return r;
-}
 __device__ __forceinline__ bf16x8_t zero8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
 
 template <int D> constexpr int stage_elems() { return 128 * (D + 8); }
@@ -181,7 +172,7 @@ template <int D> constexpr int smem_elems(int tiles) {
 }
 
 // ------------------------------------------------------------------ forward
-template <int D>
+template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                        bf16_t* __restrict__ out,
                                                        float* __restrict__ lse, int S, int nq,
@@ -248,8 +239,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
+        sacc[kb] = mfma32<DT>(rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb]);
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
     float mx = -INFINITY;
 #pragma unroll
@@ -289,14 +279,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
       float pv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-      const bf16x8_t pf = pack8(pv);
+      const bf16x8_t pf = pack8<DT>(pv);
       bf16x8_t vt[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vt[db] = t_read<D>(sV, db * 32, ks, lane);
       tr_wait(vt);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[db], pf, oacc[db], 0, 0, 0);
+        oacc[db] = mfma32<DT>(vt[db], pf, oacc[db]);
     }
   }
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
@@ -304,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
   wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
-  store_tile_t<D>(stage, oacc, inv_l, out + (size_t)b * S * nq * D + h * D, nq * D, wq0,
+  store_tile_t<D, DT>(stage, oacc, inv_l, out + (size_t)b * S * nq * D + h * D, nq * D, wq0,
                   min(32, S - wq0), lane);
 }
 
@@ -320,6 +310,13 @@ __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&v)[8]) {
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
+}
+template <>
+__device__ __forceinline__ void load8<f16_t>(const f16_t* p, float (&v)[8]) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 h = *(const h8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
 }
 template <>
 __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
@@ -359,7 +356,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 }
 
 // ------------------------------------------------------------------ dQ
-template <int D>
+template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                       const bf16_t* __restrict__ dout,
                                                       const float* __restrict__ lse,
@@ -431,10 +428,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb], 0, 0, 0);
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb], 0, 0, 0);
+        sacc[kb] = mfma32<DT>(rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb]);
+        pacc[kb] = mfma32<DT>(rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb]);
       }
     }
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S) || (wq0 + 32 > S);
@@ -454,20 +449,20 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
       float sv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) sv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
-      const bf16x8_t sf = pack8(sv);
+      const bf16x8_t sf = pack8<DT>(sv);
       bf16x8_t kt[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) kt[db] = t_read<D>(sK, db * 32, ks, lane);
       tr_wait(kt);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db], sf, dq[db], 0, 0, 0);
+        dq[db] = mfma32<DT>(kt[db], sf, dq[db]);
     }
   }
   wait_vm<0>();
   __syncthreads();
   bf16_t* stage = smem + wave * 32 * (D + 8);
-  store_tile_t<D>(stage, dq, scale, dqkv + (size_t)b * S * QS + h * D, QS, wq0, min(32, S - wq0),
+  store_tile_t<D, DT>(stage, dq, scale, dqkv + (size_t)b * S * QS + h * D, QS, wq0, min(32, S - wq0),
                   lane);
 }
 
@@ -478,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
 // per lane, so two workgroups share a compute unit.
 constexpr int MODE_DV = 0, MODE_DK = 1;
 
-template <int D, int MODE>
+template <int D, int MODE, int DT>
 __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
                                                           const bf16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
@@ -563,11 +558,9 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc, 0, 0, 0);
+        sacc = mfma32<DT>(rows_read<D>(sQ, qb2 * 32 + lr, kk * 2 + hf), kf[kk], sacc);
         if constexpr (DK)
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc, 0, 0, 0);
+          pacc = mfma32<DT>(rows_read<D>(sO, qb2 * 32 + lr, kk * 2 + hf), vf[kk], pacc);
       }
       // dV += P^T dO (columns of dO), dK += dS^T Q (columns of Q), in two steps of 16 queries.
       // The column reads do not depend on the scores: the first step's (both steps' for dV,
@@ -595,10 +588,10 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
       float w[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[j] = sacc[j];
-      const bf16x8_t wf0 = pack8(w);
+      const bf16x8_t wf0 = pack8<DT>(w);
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[j] = sacc[8 + j];
-      const bf16x8_t wf1 = pack8(w);
+      const bf16x8_t wf1 = pack8<DT>(w);
       tr_wait(tf0);
       if constexpr (DK) {
 #pragma unroll
@@ -606,11 +599,11 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf0[db], wf0, acc[db], 0, 0, 0);
+        acc[db] = mfma32<DT>(tf0[db], wf0, acc[db]);
       tr_wait(tf1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf1[db], wf1, acc[db], 0, 0, 0);
+        acc[db] = mfma32<DT>(tf1[db], wf1, acc[db]);
     }
   }
   wait_vm<0>();
@@ -618,7 +611,7 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
   bf16_t* stage = smem + wave * 32 * (D + 8);
   const int nv = min(32, S - wk0);
   if (nv > 0)
-    store_tile_t<D>(stage, acc, DK ? scale : 1.0f,
+    store_tile_t<D, DT>(stage, acc, DK ? scale : 1.0f,
                     dqkv + (size_t)b * S * QS + (nq + (DK ? 0 : nkv) + g) * D, QS, wk0, nv, lane);
 }
 
@@ -751,9 +744,80 @@ int attention_check(int B, int S, int nq, int nkv, int d, int dtype) {
   SLIDE_REQUIRE(nq > 0 && nkv > 0 && nq % nkv == 0, SLIDE_E_SHAPE,
                 "attention: n_heads %d must be a positive multiple of n_kv_heads %d", nq, nkv);
   SLIDE_REQUIRE(d == 64 || d == 128, SLIDE_E_SHAPE, "attention: head_dim %d (64 or 128)", d);
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "attention: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "attention: bad dtype");
   return SLIDE_OK;
 }
+
+namespace {
+
+template <int DT>
+void launch_fwd16(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv, int d,
+                  float scale, hipStream_t st) {
+  dim3 grid((S + 127) / 128, nq, B), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((attn_fwd_kernel<128, DT>), grid, block, 0, st, (const bf16_t*)qkv,
+                       (bf16_t*)o, lse, S, nq, nkv, scale);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<64, DT>), grid, block, 0, st, (const bf16_t*)qkv,
+                       (bf16_t*)o, lse, S, nq, nkv, scale);
+}
+
+template <typename T>
+void launch_delta(const void* o, const void* dout, float* delta, int B, int S, int nq, int d,
+                  hipStream_t st) {
+  const size_t rows = (size_t)B * S * nq;
+  dim3 grid((unsigned)((rows * (d / 8) + 255) / 256)), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((attn_delta_kernel<T, 128>), grid, block, 0, st, (const T*)o,
+                       (const T*)dout, delta, B, S, nq);
+  else
+    hipLaunchKernelGGL((attn_delta_kernel<T, 64>), grid, block, 0, st, (const T*)o,
+                       (const T*)dout, delta, B, S, nq);
+}
+
+template <int DT>
+int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv,
+                 const float* delta, int B, int S, int nq, int nkv, int d, float scale,
+                 hipStream_t st) {
+  const bf16_t* q = (const bf16_t*)qkv;
+  const bf16_t* g = (const bf16_t*)dout;
+  bf16_t* out = (bf16_t*)dqkv;
+  {
+    ProfScope ps("attn_bwd_dq", st);
+    dim3 grid((S + 127) / 128, nq, B), block(256);
+    if (d == 128)
+      hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+                         nq, nkv, scale);
+    else
+      hipLaunchKernelGGL((attn_dq_kernel<64, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+                         nq, nkv, scale);
+  }
+  SLIDE_TRY(check_launch("attn_bwd_dq"));
+  {
+    ProfScope ps("attn_bwd_dv", st);
+    dim3 grid((S + 127) / 128, nkv, B), block(256);
+    if (d == 128)
+      hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DV, DT>), grid, block, 0, st, q, g, lse,
+                         delta, out, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DV, DT>), grid, block, 0, st, q, g, lse,
+                         delta, out, S, nq, nkv, scale);
+  }
+  SLIDE_TRY(check_launch("attn_bwd_dv"));
+  {
+    ProfScope ps("attn_bwd_dk", st);
+    dim3 grid((S + 127) / 128, nkv, B), block(256);
+    if (d == 128)
+      hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DK, DT>), grid, block, 0, st, q, g, lse,
+                         delta, out, S, nq, nkv, scale);
+    else
+      hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DK, DT>), grid, block, 0, st, q, g, lse,
+                         delta, out, S, nq, nkv, scale);
+  }
+  return check_launch("attn_bwd_dk");
+}
+
+}  // namespace
 
 int attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv, int d,
                   int dtype, hipStream_t st) {
@@ -761,11 +825,9 @@ int attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, in
   ProfScope ps("attn_fwd", st);
   const float scale = 1.0f / sqrtf((float)d);
   if (dtype == SLIDE_BF16) {
-    dim3 grid((S + 127) / 128, nq, B), block(256);
-    if (d == 128)
-      hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse, S, nq, nkv, scale);
-    else
-      hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse, S, nq, nkv, scale);
+    launch_fwd16<SLIDE_BF16>(qkv, o, lse, B, S, nq, nkv, d, scale, st);
+  } else if (dtype == SLIDE_F16) {
+    launch_fwd16<SLIDE_F16>(qkv, o, lse, B, S, nq, nkv, d, scale, st);
   } else {
     dim3 grid((S + 63) / 64, nq, B), block(64);
     if (d == 128)
@@ -785,47 +847,13 @@ int attention_bwd(const void* qkv, const void* o, const float* lse, const void* 
   const float scale = 1.0f / sqrtf((float)d);
   {
     ProfScope ps("attn_delta", st);
-    const size_t rows = (size_t)B * S * nq;
-    dim3 grid((unsigned)((rows * (d / 8) + 255) / 256)), block(256);
-    if (dtype == SLIDE_BF16 && d == 128)
-      hipLaunchKernelGGL((attn_delta_kernel<bf16_t, 128>), grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq);
-    else if (dtype == SLIDE_BF16)
-      hipLaunchKernelGGL((attn_delta_kernel<bf16_t, 64>), grid, block, 0, st, (const bf16_t*)o, (const bf16_t*)dout, delta, B, S, nq);
-    else if (d == 128)
-      hipLaunchKernelGGL((attn_delta_kernel<float, 128>), grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq);
-    else
-      hipLaunchKernelGGL((attn_delta_kernel<float, 64>), grid, block, 0, st, (const float*)o, (const float*)dout, delta, B, S, nq);
+    SLIDE_DISPATCH(dtype, T, launch_delta<T>(o, dout, delta, B, S, nq, d, st));
   }
   SLIDE_TRY(check_launch("attn_delta"));
-  if (dtype == SLIDE_BF16) {
-    {
-      ProfScope ps("attn_bwd_dq", st);
-      dim3 grid((S + 127) / 128, nq, B), block(256);
-      if (d == 128)
-        hipLaunchKernelGGL(attn_dq_kernel<128>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-      else
-        hipLaunchKernelGGL(attn_dq_kernel<64>, grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-    }
-    SLIDE_TRY(check_launch("attn_bwd_dq"));
-    {
-      ProfScope ps("attn_bwd_dv", st);
-      dim3 grid((S + 127) / 128, nkv, B), block(256);
-      if (d == 128)
-        hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DV>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-      else
-        hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DV>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-    }
-    SLIDE_TRY(check_launch("attn_bwd_dv"));
-    {
-      ProfScope ps("attn_bwd_dk", st);
-      dim3 grid((S + 127) / 128, nkv, B), block(256);
-      if (d == 128)
-        hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DK>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-      else
-        hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DK>), grid, block, 0, st, (const bf16_t*)qkv, (const bf16_t*)dout, lse, delta, (bf16_t*)dqkv, S, nq, nkv, scale);
-    }
-    return check_launch("attn_bwd_dk");
-  }
+  if (dtype == SLIDE_BF16)
+    return launch_bwd16<SLIDE_BF16>(qkv, lse, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
+  if (dtype == SLIDE_F16)
+    return launch_bwd16<SLIDE_F16>(qkv, lse, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
   {
     ProfScope ps("attn_bwd_dq", st);
     dim3 grid((S + 63) / 64, nq, B), block(64);

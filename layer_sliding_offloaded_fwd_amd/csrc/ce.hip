@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void ce_lse_kernel(const float* __restrict__ p
 // loss = sum(lt over valid) / N_valid with a fixed reduction tree; also 1/N_valid for pass 2
 __global__ __launch_bounds__(1024) void ce_loss_kernel(const float* __restrict__ lt,
                                                        const int32_t* __restrict__ tgt, int N,
-                                                       int V, float* loss, float* inv_nv) {
+                                                       int V, float* loss, float* inv_nv,
+                                                       float scale) {
   __shared__ float ss[1024];
   __shared__ int sc[1024];
   float s = 0.f;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(1024) void ce_loss_kernel(const float* __restrict__
   if (threadIdx.x == 0) {
     const int nv = sc[0];
     *loss = nv > 0 ? ss[0] / (float)nv : 0.f;
-    *inv_nv = nv > 0 ? 1.0f / (float)nv : 0.f;
+    *inv_nv = nv > 0 ? scale / (float)nv : 0.f;
   }
 }
 
@@ -203,7 +204,9 @@ size_t ce_workspace_bytes(const slide_ce_cfg& c, int N) { return ce_layout(c, N,
 
 int ce_check(const slide_ce_cfg* c, int N) {
   SLIDE_REQUIRE(c, SLIDE_E_ARG, "lmhead_ce: null cfg");
-  SLIDE_REQUIRE(c->dtype == SLIDE_BF16 || c->dtype == SLIDE_F32, SLIDE_E_ARG, "lmhead_ce: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(c->dtype), SLIDE_E_ARG, "lmhead_ce: bad dtype");
+  SLIDE_REQUIRE(c->grad_scale >= 0.f && c->grad_scale < 3.0e38f, SLIDE_E_ARG,
+                "lmhead_ce: grad_scale must be a finite value >= 0");
   SLIDE_REQUIRE(c->hidden > 0 && c->hidden % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: hidden %d must be a positive multiple of 8", c->hidden);
   SLIDE_REQUIRE(c->vocab > 0 && c->vocab % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: vocab %d must be a positive multiple of 8", c->vocab);
   SLIDE_REQUIRE(c->chunk >= 0 && c->chunk % 8 == 0, SLIDE_E_SHAPE, "lmhead_ce: chunk %d must be a multiple of 8", c->chunk);
@@ -244,7 +247,7 @@ int ce_logits(const slide_ce_cfg& c, const CeBufs& b, const void* h, const void*
               const int32_t* tgt, int N, int ci, int special, hipStream_t st) {
   const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
   const size_t ts = (size_t)dtype_size(c.dtype);
-  const bool fused = c.dtype == SLIDE_BF16;
+  const bool fused = c.dtype != SLIDE_F32;
   GemmArgs g{rows, N, c.hidden, (const char*)w + (size_t)c0 * c.hidden * ts, c.hidden, true, h,
              c.hidden, true, b.zbuf, b.L.ldz, SLIDE_F32, nullptr, 0, 1.0f, false, c.dtype,
              "ce_logits_gemm", SITE_GENERIC};
@@ -282,7 +285,7 @@ int ce_stats(const slide_ce_cfg& c, const void* h, const void* w, const int32_t*
   const CeBufs b = ce_bufs(c, N, ws);
   const int c0 = ci * b.L.C, rows = std::min(b.L.C, c.vocab - c0);
   SLIDE_TRY(ce_logits(c, b, h, w, tgt, N, ci, SPECIAL_CE_STATS, st));
-  if (c.dtype == SLIDE_BF16) return SLIDE_OK;   // the partials came out of the GEMM
+  if (c.dtype != SLIDE_F32) return SLIDE_OK;   // the partials came out of the GEMM
   ProfScope ps_("ce_stats", st);
   const int parts = ce_parts(rows);
   hipLaunchKernelGGL(ce_stats_kernel, dim3(nblk(N, 256), parts), dim3(256), 0, st, b.zbuf,
@@ -302,8 +305,9 @@ int ce_loss(const slide_ce_cfg& c, const int32_t* tgt, int N, float* loss, void*
   ProfScope ps_("ce_lse", st);
   hipLaunchKernelGGL(ce_lse_kernel, dim3(nblk(N, 32)), dim3(256), 0, st, b.pm, b.ps,
                      b.L.nchunks, b.L.C, b.L.ppc, N, tgt, c.vocab, b.zt, b.lse, b.lt);
+  const float scale = c.grad_scale > 0.f ? c.grad_scale : 1.0f;
   hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(1024), 0, st, b.lt, tgt, N, c.vocab, loss,
-                     b.inv_nv);
+                     b.inv_nv, scale);
   return check_launch("ce_lse");
 }
 
@@ -319,13 +323,13 @@ int ce_grad(const slide_ce_cfg& c, const void* h, const void* w, const int32_t* 
     if (dw) {
       const size_t n = (size_t)rows * H;
       char* d = (char*)dw + (size_t)c0 * H * ts;
-      if (dt == SLIDE_BF16) hipLaunchKernelGGL(fill_zero_kernel<bf16_t>, dim3(nblk(n, 256)), dim3(256), 0, st, (bf16_t*)d, n);
-      else hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, (float*)d, n);
+      SLIDE_DISPATCH(dt, T, hipLaunchKernelGGL(fill_zero_kernel<T>, dim3(nblk(n, 256)), dim3(256),
+                                               0, st, (T*)d, n));
     }
     return check_launch("lmhead_ce(empty)");
   }
   SLIDE_TRY(ce_logits(c, b, h, w, tgt, N, ci, SPECIAL_CE_DZ, st));
-  if (dt == SLIDE_F32) {   // the bf16 path computed dz in the logits GEMM's epilogue
+  if (dt == SLIDE_F32) {   // the 16-bit path computed dz in the logits GEMM's epilogue
     ProfScope ps_("ce_dz", st);
     const size_t n = (size_t)rows * b.L.ldz;
     hipLaunchKernelGGL(ce_dz_kernel<float>, dim3(nblk(n, 256)), dim3(256), 0, st, b.zbuf,

@@ -1,7 +1,8 @@
 // GEMMs of the decoder layer and the LM head (projections y = x W^T, their input gradients
 // dX = dY W and weight gradients dW = dY^T X).
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, two kernels:
+// 16-bit path (bf16 or fp16 operands): gfx950 MFMA v_mfma_f32_32x32x16_bf16 / _f16, fp32
+// accumulation, two kernels:
 //   pipelined (problems with at least 128 tiles of 256 x 256, i.e. every projection of the
 //     step): 256 x 256 tile, 8 waves, k-tiles streamed global -> LDS by direct loads; see the
 //     comment above gemm_pipe_kernel.
@@ -18,10 +19,17 @@
 
 namespace slide {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-
 namespace {
+
+// the two 16-bit values of a 32-bit word, widened
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) { return Bits16<DT>::to_f((uint16_t)(w & 0xffffu)); }
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) { return Bits16<DT>::to_f((uint16_t)(w >> 16)); }
+template <int DT>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  return (uint32_t)Bits16<DT>::from_f(a) | ((uint32_t)Bits16<DT>::from_f(b) << 16);
+}
 
 constexpr int BK = 64;
 
@@ -36,7 +44,7 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int i) {
 // Epilogue of a wave tile of MI x NJ 32x32 MFMA blocks whose top-left element is (rw0, cw0):
 // acc[i][j][e] is C(row, col) with col = cw0 + 32 j + lane%32,
 // row = rw0 + 32 i + (e/4)*8 + (lane/32)*4 + e%4.
-template <int EPI, int MI, int NJ>
+template <int EPI, int MI, int NJ, int DT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)[MI][NJ],
                                               int rw0, int cw0, int lane) {
   if constexpr (EPI == EPI_CE_STATS) {
@@ -112,12 +120,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)
           if (row >= g.M) continue;
           float v = acc[i][j][e] * g.alpha;
           if constexpr (EPI == EPI_STORE_BF16) {
-            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = Bits16<DT>::from_f(v);
           } else if constexpr (EPI == EPI_STORE_F32) {
             ((float*)g.C)[(size_t)row * g.ldc + col] = v;
           } else if constexpr (EPI == EPI_RESID) {
-            v += bf2f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
-            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(v);
+            v += Bits16<DT>::to_f(((const bf16_t*)g.R)[(size_t)row * g.ldr + col]);
+            ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = Bits16<DT>::from_f(v);
           } else if constexpr (EPI == EPI_ACCUM_F32) {
             float* c = (float*)g.C + (size_t)row * g.ldc + col;
             *c = *c + v;
@@ -128,7 +136,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16_t (&acc)
               if (g.c0 + row == y) d -= 1.f;
               d *= dzs;
             }
-            if (g.c_dtype == SLIDE_BF16) ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = f2bf(d);
+            if (g.c_dtype != SLIDE_F32) ((bf16_t*)g.C)[(size_t)row * g.ldc + col] = Bits16<DT>::from_f(d);
             else ((float*)g.C)[(size_t)row * g.ldc + col] = d;
           }
         }
@@ -201,7 +209,7 @@ struct Tile {
 };
 using TileS = Tile<128, 128, 256, 2>;
 
-template <class TL, bool AK, bool BKM, int EPI, int SITE>
+template <class TL, bool AK, bool BKM, int EPI, int SITE, int DT>
 __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, NT = TL::NT, MI = TL::MI, NJ = TL::NJ;
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
@@ -268,13 +276,13 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<DT>(af[i], bfr[j], acc[i][j]);
     }
     if (kt + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
   }
 
-  gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, lane);
+  gemm_epilogue<EPI, MI, NJ, DT>(g, acc, m0 + wm * TL::WTM, n0 + wn * TL::WTN, lane);
 }
 
 // ------------------------------------------------------------------ pipelined bf16 GEMM
@@ -469,7 +477,7 @@ __device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
 // accumulation target are read the same way. Ragged or unaligned edges fall back to per-element
 // accesses. The cross-entropy dz (softmax - onehot of a vocabulary chunk, per token column) is
 // formed from the same staged values.
-template <int EPI, class PC>
+template <int EPI, class PC, int DT>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
                                                 f32x16_t (&acc)[PC::MI][PC::NJ], float* lds,
                                                 int m0, int n0, int wm, int wn, int lane) {
@@ -519,7 +527,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
           for (int e = 0; e < 16; ++e) {
             const int r = wm * WTM + i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
             const int c = (wn * WTN + j * 32 + (lane & 31)) ^ (hl << 5);
-            lb[r * BN + c] = f2bf(acc[i][j][e] * g.alpha);
+            lb[r * BN + c] = Bits16<DT>::from_f(acc[i][j][e] * g.alpha);
           }
       __syncthreads();
 #pragma unroll
@@ -583,10 +591,10 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
           float o[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
           bool f32_out = F32;
           if constexpr (EPI == EPI_RESID) {
-            o[0] += __uint_as_float(rres[j].x << 16);
-            o[1] += __uint_as_float(rres[j].x & 0xffff0000u);
-            o[2] += __uint_as_float(rres[j].y << 16);
-            o[3] += __uint_as_float(rres[j].y & 0xffff0000u);
+            o[0] += lo16<DT>(rres[j].x);
+            o[1] += hi16<DT>(rres[j].x);
+            o[2] += lo16<DT>(rres[j].y);
+            o[3] += hi16<DT>(rres[j].y);
           }
           if constexpr (EPI == EPI_ACCUM_F32) {
             o[0] += cold[j].x;
@@ -611,8 +619,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
             *(float4*)((float*)g.C + at) = make_float4(o[0], o[1], o[2], o[3]);
           } else {
             uint2 w;
-            w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-            w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            w.x = pack16<DT>(o[0], o[1]);
+            w.y = pack16<DT>(o[2], o[3]);
             *(uint2*)((bf16_t*)g.C + at) = w;
           }
         }
@@ -642,10 +650,10 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
           o[t] = d;
         }
         if (vec && gc + 3 < g.ldc) {
-          if (g.c_dtype == SLIDE_BF16) {
+          if (g.c_dtype != SLIDE_F32) {
             uint2 w;
-            w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-            w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+            w.x = pack16<DT>(o[0], o[1]);
+            w.y = pack16<DT>(o[2], o[3]);
             *(uint2*)((bf16_t*)g.C + at) = w;
           } else {
             *(float4*)((float*)g.C + at) = make_float4(o[0], o[1], o[2], o[3]);
@@ -654,7 +662,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             if (gc + t >= g.ldc) break;
-            if (g.c_dtype == SLIDE_BF16) ((bf16_t*)g.C)[at + t] = f2bf(o[t]);
+            if (g.c_dtype != SLIDE_F32) ((bf16_t*)g.C)[at + t] = Bits16<DT>::from_f(o[t]);
             else ((float*)g.C)[at + t] = o[t];
           }
         }
@@ -674,14 +682,14 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
         } else {
           if constexpr (EPI == EPI_RESID) {
             const uint2 rr = *(const uint2*)((const bf16_t*)g.R + (size_t)gr * g.ldr + gc);
-            o[0] += __uint_as_float(rr.x << 16);
-            o[1] += __uint_as_float(rr.x & 0xffff0000u);
-            o[2] += __uint_as_float(rr.y << 16);
-            o[3] += __uint_as_float(rr.y & 0xffff0000u);
+            o[0] += lo16<DT>(rr.x);
+            o[1] += hi16<DT>(rr.x);
+            o[2] += lo16<DT>(rr.y);
+            o[3] += hi16<DT>(rr.y);
           }
           uint2 w;
-          w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-          w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+          w.x = pack16<DT>(o[0], o[1]);
+          w.y = pack16<DT>(o[2], o[3]);
           *(uint2*)((bf16_t*)g.C + at) = w;
         }
       } else {
@@ -695,8 +703,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
             ((float*)g.C)[at + t] += x;
           } else {
             if constexpr (EPI == EPI_RESID)
-              x += bf2f(((const bf16_t*)g.R)[(size_t)gr * g.ldr + gc + t]);
-            ((bf16_t*)g.C)[at + t] = f2bf(x);
+              x += Bits16<DT>::to_f(((const bf16_t*)g.R)[(size_t)gr * g.ldr + gc + t]);
+            ((bf16_t*)g.C)[at + t] = Bits16<DT>::from_f(x);
           }
         }
       }
@@ -712,7 +720,7 @@ struct StageTag {
 
 }  // namespace pipe
 
-template <class PC, bool AK, bool BKM, int EPI, int SITE>
+template <class PC, bool AK, bool BKM, int EPI, int SITE, int DT>
 __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   using namespace pipe;
   constexpr int NS = PC::NS, NW = PC::NW, WGM = PC::WGM, WTM = PC::WTM, WTN = PC::WTN;
@@ -788,8 +796,7 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
-                                                             0, 0, 0);
+        acc[i][j] = mfma32<DT>(fa[buf][i], fb[buf][j], acc[i][j]);
   };
 
   // All NS stages start in flight; stage kt + NS reuses stage kt's buffer once every wave has
@@ -867,9 +874,9 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
   for (; kt < nk; ++kt) run_stage(kt, StageTag<false>{});
 
   if constexpr (EPI != EPI_CE_STATS)
-    staged_epilogue<EPI, PC>(g, acc, (float*)smem, m0, n0, wm, wn, lane);
+    staged_epilogue<EPI, PC, DT>(g, acc, (float*)smem, m0, n0, wm, wn, lane);
   else
-    gemm_epilogue<EPI, MI, NJ>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    gemm_epilogue<EPI, MI, NJ, DT>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT GEMM
@@ -962,35 +969,37 @@ inline bool use_large(const GemmArgs& g) {
   return tiles >= 128;
 }
 
-template <bool AK, bool BKM, int EPI, int SITE>
+template <bool AK, bool BKM, int EPI, int SITE, int DT>
 void launch_one(const GemmArgs& g, hipStream_t st) {
   if (use_large(g)) {
     const int tiles = ((g.M + pipe::BM - 1) / pipe::BM) * ((g.N + pipe::BN - 1) / pipe::BN);
     using PC = typename PipeFor<AK, BKM>::type;
-    hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE>), dim3(tiles), dim3(PC::NT), 0,
-                       st, g);
+    hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles), dim3(PC::NT),
+                       0, st, g);
   } else {
     const int tiles = ((g.M + TileS::BM - 1) / TileS::BM) * ((g.N + TileS::BN - 1) / TileS::BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE>), dim3(tiles), dim3(TileS::NT),
-                       0, st, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE, DT>), dim3(tiles),
+                       dim3(TileS::NT), 0, st, g);
   }
 }
 
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, int DT>
 void launch_generic(const GemmArgs& g, hipStream_t st, int epi) {
   switch (epi) {
-    case EPI_STORE_BF16: launch_one<AK, BKM, EPI_STORE_BF16, SITE_GENERIC>(g, st); break;
-    case EPI_STORE_F32: launch_one<AK, BKM, EPI_STORE_F32, SITE_GENERIC>(g, st); break;
-    case EPI_RESID: launch_one<AK, BKM, EPI_RESID, SITE_GENERIC>(g, st); break;
-    default: launch_one<AK, BKM, EPI_ACCUM_F32, SITE_GENERIC>(g, st); break;
+    case EPI_STORE_BF16: launch_one<AK, BKM, EPI_STORE_BF16, SITE_GENERIC, DT>(g, st); break;
+    case EPI_STORE_F32: launch_one<AK, BKM, EPI_STORE_F32, SITE_GENERIC, DT>(g, st); break;
+    case EPI_RESID: launch_one<AK, BKM, EPI_RESID, SITE_GENERIC, DT>(g, st); break;
+    default: launch_one<AK, BKM, EPI_ACCUM_F32, SITE_GENERIC, DT>(g, st); break;
   }
 }
 
-// (site, a_kmajor, b_kmajor, epilogue) -> dedicated instantiation, else generic
-void launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
+// (site, a_kmajor, b_kmajor, epilogue) -> dedicated instantiation, else generic; DT is the
+// 16-bit operand type (SLIDE_BF16 or SLIDE_F16)
+template <int DT>
+void launch_16(const GemmArgs& g, hipStream_t st, int epi) {
 #define SLIDE_SITE(S, AK_, BK_, EPI_)                                              \
   if (g.site == S && g.a_kmajor == AK_ && g.b_kmajor == BK_ && epi == EPI_) {    \
-    launch_one<AK_, BK_, EPI_, S>(g, st);                                        \
+    launch_one<AK_, BK_, EPI_, S, DT>(g, st);                                    \
     return;                                                                      \
   }
   SLIDE_SITE(SITE_QKV, true, true, EPI_STORE_BF16)
@@ -1010,10 +1019,10 @@ void launch_bf16(const GemmArgs& g, hipStream_t st, int epi) {
   SLIDE_SITE(SITE_CE_DH, false, false, EPI_ACCUM_F32)
   SLIDE_SITE(SITE_CE_DW, true, false, EPI_STORE_BF16)
 #undef SLIDE_SITE
-  if (g.a_kmajor && g.b_kmajor) launch_generic<true, true>(g, st, epi);
-  else if (g.a_kmajor) launch_generic<true, false>(g, st, epi);
-  else if (g.b_kmajor) launch_generic<false, true>(g, st, epi);
-  else launch_generic<false, false>(g, st, epi);
+  if (g.a_kmajor && g.b_kmajor) launch_generic<true, true, DT>(g, st, epi);
+  else if (g.a_kmajor) launch_generic<true, false, DT>(g, st, epi);
+  else if (g.b_kmajor) launch_generic<false, true, DT>(g, st, epi);
+  else launch_generic<false, false, DT>(g, st, epi);
 }
 
 }  // namespace
@@ -1029,7 +1038,7 @@ int gemm_epilogue_of(const GemmArgs& g) {
 int gemm_check(const GemmArgs& g) {
   SLIDE_REQUIRE(g.M >= 0 && g.N >= 0 && g.K >= 0, SLIDE_E_SHAPE, "gemm: negative size");
   SLIDE_REQUIRE(g.A && g.B && g.C, SLIDE_E_ARG, "gemm: null operand");
-  SLIDE_REQUIRE(g.dtype == SLIDE_BF16 || g.dtype == SLIDE_F32, SLIDE_E_ARG, "gemm: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(g.dtype), SLIDE_E_ARG, "gemm: bad dtype");
   SLIDE_REQUIRE(!g.accumulate || g.c_dtype == SLIDE_F32, SLIDE_E_ARG,
                 "gemm: accumulate needs an fp32 C");
   SLIDE_REQUIRE(!(g.accumulate && g.R), SLIDE_E_ARG, "gemm: residual and accumulate are exclusive");
@@ -1037,7 +1046,7 @@ int gemm_check(const GemmArgs& g) {
   SLIDE_REQUIRE(g.lda >= (g.a_kmajor ? g.K : g.M) && g.ldb >= (g.b_kmajor ? g.K : g.N) &&
                     g.ldc >= g.N && (!g.R || g.ldr >= g.N),
                 SLIDE_E_SHAPE, "gemm: leading dimension smaller than the row");
-  if (g.dtype == SLIDE_BF16) {
+  if (g.dtype != SLIDE_F32) {
     SLIDE_REQUIRE(aligned16(g.A) && aligned16(g.B), SLIDE_E_ARG, "gemm: operands must be 16-byte aligned");
     SLIDE_REQUIRE(g.lda % 8 == 0 && g.ldb % 8 == 0, SLIDE_E_SHAPE, "gemm: lda/ldb must be multiples of 8");
     // 16-byte vector loads: a K-contiguous operand needs K % 8 == 0; an operand whose rows run
@@ -1047,7 +1056,8 @@ int gemm_check(const GemmArgs& g) {
                       (g.b_kmajor ? g.K % 8 == 0 : g.ldb >= r8(g.N)),
                   SLIDE_E_SHAPE, "gemm: K must be a multiple of 8 for a K-contiguous operand, "
                   "and ld >= M (N) rounded up to 8 otherwise");
-    SLIDE_REQUIRE(g.c_dtype == SLIDE_BF16 || g.c_dtype == SLIDE_F32, SLIDE_E_ARG, "gemm: bad c_dtype");
+    SLIDE_REQUIRE(g.c_dtype == g.dtype || g.c_dtype == SLIDE_F32, SLIDE_E_ARG,
+                  "gemm: c_dtype must be the operands' dtype or SLIDE_F32");
   } else {
     SLIDE_REQUIRE(g.c_dtype == SLIDE_F32, SLIDE_E_ARG, "gemm: fp32 operands need an fp32 C");
   }
@@ -1058,13 +1068,15 @@ int gemm_launch(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return SLIDE_OK;
   // the cross-entropy epilogues exist for the logits GEMM's own instantiation only
   SLIDE_REQUIRE(g.special == SPECIAL_NONE ||
-                    (g.dtype == SLIDE_BF16 && g.a_kmajor && g.b_kmajor &&
+                    (g.dtype != SLIDE_F32 && g.a_kmajor && g.b_kmajor &&
                      g.site == (g.special == SPECIAL_CE_STATS ? SITE_CE_STATS : SITE_CE_DZ)),
                 SLIDE_E_ARG, "gemm: cross-entropy epilogue with another site or layout");
   ProfScope ps(g.name ? g.name : "gemm", st);
   const int epi = gemm_epilogue_of(g);
   if (g.dtype == SLIDE_BF16) {
-    launch_bf16(g, st, epi);
+    launch_16<SLIDE_BF16>(g, st, epi);
+  } else if (g.dtype == SLIDE_F16) {
+    launch_16<SLIDE_F16>(g, st, epi);
   } else {
     dim3 grid((g.N + SB - 1) / SB, (g.M + SB - 1) / SB), block(256);
     switch (epi) {

@@ -24,7 +24,7 @@ struct Dims {
 
 int check_cfg(const slide_layer_cfg* c) {
   SLIDE_REQUIRE(c, SLIDE_E_ARG, "layer: null cfg");
-  SLIDE_REQUIRE(c->dtype == SLIDE_BF16 || c->dtype == SLIDE_F32, SLIDE_E_ARG, "layer: bad dtype %d", c->dtype);
+  SLIDE_REQUIRE(dtype_valid(c->dtype), SLIDE_E_ARG, "layer: bad dtype %d", c->dtype);
   SLIDE_REQUIRE(c->hidden > 0 && c->hidden % 8 == 0, SLIDE_E_SHAPE, "layer: hidden %d must be a positive multiple of 8", c->hidden);
   SLIDE_REQUIRE(c->ffn > 0 && c->ffn % 8 == 0, SLIDE_E_SHAPE, "layer: ffn %d must be a positive multiple of 8", c->ffn);
   SLIDE_REQUIRE(c->head_dim == 64 || c->head_dim == 128, SLIDE_E_SHAPE, "layer: head_dim %d (64 or 128)", c->head_dim);
@@ -295,7 +295,7 @@ extern "C" int slide_layer_bwd_saved(const slide_layer_cfg* cfg, const void* w_s
 
 extern "C" int slide_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out, int N,
                                  int H, float eps, int dtype, void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "rmsnorm: bad dtype");
   SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
   SLIDE_REQUIRE(eps > 0.f, SLIDE_E_ARG, "rmsnorm: eps must be > 0");
   if (N == 0) return SLIDE_OK;
@@ -311,7 +311,7 @@ extern "C" size_t slide_rmsnorm_bwd_workspace_bytes(int N, int H) {
 extern "C" int slide_rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres,
                                  void* dx, void* dw, int N, int H, float eps, int dtype, void* ws,
                                  size_t ws_bytes, void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "rmsnorm: bad dtype");
   SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
   SLIDE_REQUIRE(ws && ws_bytes >= rmsnorm_bwd_ws(N, H), SLIDE_E_WORKSPACE,
                 "rmsnorm_bwd: workspace %zu < %zu", ws_bytes, rmsnorm_bwd_ws(N, H));
@@ -367,7 +367,7 @@ extern "C" size_t slide_rmsnorm_bwd_noalloc_max_bytes(void) { return kNoAllocScr
 extern "C" int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w,
                                          const void* dres, void* dx, void* dw, int N, int H,
                                          float eps, int dtype, void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "rmsnorm: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "rmsnorm: bad dtype");
   SLIDE_REQUIRE(N >= 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "rmsnorm: H %d must be a positive multiple of 8", H);
   const size_t need = rmsnorm_bwd_ws(N, H);
   SLIDE_REQUIRE(need <= kNoAllocScratchBytes, SLIDE_E_WORKSPACE,
@@ -384,7 +384,7 @@ extern "C" int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const vo
 
 extern "C" int slide_nonfinite_count(const void* x, int dtype, size_t n, uint32_t* count_dev,
                                      void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "nonfinite_count: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "nonfinite_count: bad dtype");
   SLIDE_REQUIRE(count_dev && (n == 0 || x), SLIDE_E_ARG, "nonfinite_count: null pointer");
   SLIDE_REQUIRE(n == 0 || aligned16(x), SLIDE_E_ARG, "nonfinite_count: x must be 16-byte aligned");
   SLIDE_REQUIRE(((uintptr_t)count_dev & 3) == 0, SLIDE_E_ARG, "nonfinite_count: count must be 4-byte aligned");
@@ -408,7 +408,7 @@ extern "C" int slide_rope(void* qkv, int B, int S, int nq, int nkv, int d, float
 
 extern "C" int slide_embed_fwd(const void* E, const int32_t* tokens, void* x, int N, int H, int V,
                                int dtype, void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "embed: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "embed: bad dtype");
   SLIDE_REQUIRE(N >= 0 && V > 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE, "embed: bad sizes N %d H %d V %d", N, H, V);
   if (N == 0) return SLIDE_OK;
   SLIDE_REQUIRE(E && tokens && x && aligned16(E) && aligned16(x), SLIDE_E_ARG, "embed: null or misaligned pointer");
@@ -419,7 +419,7 @@ extern "C" size_t slide_embed_bwd_workspace_bytes(int N, int V) { return embed_b
 
 extern "C" int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,
                                int dtype, void* ws, size_t ws_bytes, void* stream) {
-  SLIDE_REQUIRE(dtype == SLIDE_BF16 || dtype == SLIDE_F32, SLIDE_E_ARG, "embed_bwd: bad dtype");
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "embed_bwd: bad dtype");
   SLIDE_REQUIRE(N >= 0 && N <= (1 << 30) && V > 0 && H > 0 && H % 8 == 0, SLIDE_E_SHAPE,
                 "embed_bwd: bad sizes N %d H %d V %d", N, H, V);
   SLIDE_REQUIRE(ws && ws_bytes >= embed_bwd_ws(N, V), SLIDE_E_WORKSPACE, "embed_bwd: workspace %zu < %zu",

@@ -31,6 +31,21 @@ template <> struct V8<bf16_t> {
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
+template <> struct V8<f16_t> {
+  __device__ __forceinline__ static void load(const f16_t* p, float (&v)[8]) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = *(const h8*)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+  }
+  __device__ __forceinline__ static void store(f16_t* p, const float (&v)[8]) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+    *(h8*)p = h;
+  }
+};
 template <> struct V8<float> {
   __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
     float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
@@ -317,11 +332,13 @@ __global__ __launch_bounds__(256) void nonfinite_count_kernel(const T* __restric
   uint32_t c = 0;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
     if constexpr (sizeof(T) == 2) {
+      // exponent field of bf16 (8 bits) or fp16 (5 bits), in both halves of a word
+      constexpr uint32_t e = __is_same(T, f16_t) ? 0x7C00u : 0x7F80u;
       const uint4 u = *(const uint4*)(x + i * 8);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        c += ((w[k] & 0x7F80u) == 0x7F80u) + ((w[k] & 0x7F800000u) == 0x7F800000u);
+        c += ((w[k] & e) == e) + ((w[k] & (e << 16)) == (e << 16));
     } else {
       const uint4 a = *(const uint4*)(x + i * 8), b = *(const uint4*)(x + i * 8 + 4);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -331,7 +348,8 @@ __global__ __launch_bounds__(256) void nonfinite_count_kernel(const T* __restric
   }
   if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {   // the last n % 8 elements
     const size_t i = n8 * 8 + threadIdx.x;
-    if constexpr (sizeof(T) == 2) c += (((const uint16_t*)x)[i] & 0x7F80u) == 0x7F80u;
+    constexpr uint32_t e = __is_same(T, f16_t) ? 0x7C00u : 0x7F80u;
+    if constexpr (sizeof(T) == 2) c += (((const uint16_t*)x)[i] & e) == e;
     else c += (((const uint32_t*)x)[i] & 0x7F800000u) == 0x7F800000u;
   }
 #pragma unroll
@@ -361,12 +379,9 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int N, int H
   if (N == 0) return SLIDE_OK;
   ProfScope ps("rmsnorm_fwd", st);
   dim3 grid(blocks_for(N, 4)), block(256);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)x,
-                       (const bf16_t*)w, (bf16_t*)y, rstd, N, H, eps);
-  else
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, block, 0, st, (const float*)x,
-                       (const float*)w, (float*)y, rstd, N, H, eps);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, grid, block, 0, st, (const T*)x,
+                                    (const T*)w, (T*)y, rstd, N, H, eps));
   return check_launch("rmsnorm_fwd");
 }
 
@@ -385,14 +400,10 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
     ProfScope ps("rmsnorm_bwd", st);
     if (N > 0) {
       dim3 grid(blocks_for(N, 4)), block(256);
-      if (dtype == SLIDE_BF16)
-        hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)dy,
-                           (const bf16_t*)x, (const bf16_t*)w, (const bf16_t*)dres, (bf16_t*)dx,
-                           rstd, N, H, eps);
-      else
-        hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, block, 0, st, (const float*)dy,
-                           (const float*)x, (const float*)w, (const float*)dres, (float*)dx,
-                           rstd, N, H, eps);
+      SLIDE_DISPATCH(dtype, T,
+                     hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, grid, block, 0, st,
+                                        (const T*)dy, (const T*)x, (const T*)w,
+                                        (const T*)dres, (T*)dx, rstd, N, H, eps));
     }
   }
   SLIDE_TRY(check_launch("rmsnorm_bwd"));
@@ -402,20 +413,15 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
     hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(H, 256)), dim3(256), 0, st, part, (size_t)H, 0.f);
   } else {
     dim3 g1(blocks_for(H, 256), parts), b1(256);
-    if (dtype == SLIDE_BF16)
-      hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<bf16_t>, g1, b1, 0, st, (const bf16_t*)dy,
-                         (const bf16_t*)x, rstd, part, N, H, kRmsRowsPerPart);
-    else
-      hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<float>, g1, b1, 0, st, (const float*)dy,
-                         (const float*)x, rstd, part, N, H, kRmsRowsPerPart);
+    SLIDE_DISPATCH(dtype, T,
+                   hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<T>, g1, b1, 0, st,
+                                      (const T*)dy, (const T*)x, rstd, part, N, H,
+                                      kRmsRowsPerPart));
   }
   dim3 g2(blocks_for(H, 64)), b2(256);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(reduce_rows_kernel<bf16_t>, g2, b2, 0, st, part, (bf16_t*)dw,
-                       std::max(parts, 1), H);
-  else
-    hipLaunchKernelGGL(reduce_rows_kernel<float>, g2, b2, 0, st, part, (float*)dw,
-                       std::max(parts, 1), H);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(reduce_rows_kernel<T>, g2, b2, 0, st, part, (T*)dw,
+                                    std::max(parts, 1), H));
   return check_launch("rmsnorm_dw");
 }
 
@@ -424,12 +430,9 @@ int nonfinite_count(const void* x, size_t n, int dtype, uint32_t* count, hipStre
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, count);
   if (n > 0) {
     const unsigned grid = std::min<size_t>(std::max<size_t>(blocks_for(n / 8, 256), 1), 2048);
-    if (dtype == SLIDE_BF16)
-      hipLaunchKernelGGL(nonfinite_count_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
-                         (const bf16_t*)x, n, count);
-    else
-      hipLaunchKernelGGL(nonfinite_count_kernel<float>, dim3(grid), dim3(256), 0, st,
-                         (const float*)x, n, count);
+    SLIDE_DISPATCH(dtype, T,
+                   hipLaunchKernelGGL(nonfinite_count_kernel<T>, dim3(grid), dim3(256), 0, st,
+                                      (const T*)x, n, count));
   }
   return check_launch("nonfinite_count");
 }
@@ -450,12 +453,9 @@ int rope_apply(void* qkv, const float* cos_t, const float* sin_t, int B, int S, 
   ProfScope ps(inverse ? "rope_bwd" : "rope_fwd", st);
   const float sgn = inverse ? -1.f : 1.f;
   dim3 grid(blocks_for(total, 256)), block(256);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, block, 0, st, (bf16_t*)qkv, cos_t, sin_t, N, S,
-                       heads, d, stride, sgn);
-  else
-    hipLaunchKernelGGL(rope_kernel<float>, grid, block, 0, st, (float*)qkv, cos_t, sin_t, N, S,
-                       heads, d, stride, sgn);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(rope_kernel<T>, grid, block, 0, st, (T*)qkv, cos_t, sin_t,
+                                    N, S, heads, d, stride, sgn));
   return check_launch("rope");
 }
 
@@ -464,10 +464,9 @@ int swiglu_fwd(const void* gu, void* m, int N, int F, int dtype, hipStream_t st)
   if (n8 == 0) return SLIDE_OK;
   ProfScope ps("swiglu_fwd", st);
   dim3 grid(blocks_for(n8, 256)), block(256);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(swiglu_fwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)gu, (bf16_t*)m, N, F);
-  else
-    hipLaunchKernelGGL(swiglu_fwd_kernel<float>, grid, block, 0, st, (const float*)gu, (float*)m, N, F);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(swiglu_fwd_kernel<T>, grid, block, 0, st, (const T*)gu,
+                                    (T*)m, N, F));
   return check_launch("swiglu_fwd");
 }
 
@@ -476,12 +475,9 @@ int swiglu_bwd(const void* dm, const void* gu, void* dgu, int N, int F, int dtyp
   if (n8 == 0) return SLIDE_OK;
   ProfScope ps("swiglu_bwd", st);
   dim3 grid(blocks_for(n8, 256)), block(256);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(swiglu_bwd_kernel<bf16_t>, grid, block, 0, st, (const bf16_t*)dm,
-                       (const bf16_t*)gu, (bf16_t*)dgu, N, F);
-  else
-    hipLaunchKernelGGL(swiglu_bwd_kernel<float>, grid, block, 0, st, (const float*)dm,
-                       (const float*)gu, (float*)dgu, N, F);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(swiglu_bwd_kernel<T>, grid, block, 0, st, (const T*)dm,
+                                    (const T*)gu, (T*)dgu, N, F));
   return check_launch("swiglu_bwd");
 }
 
@@ -489,12 +485,9 @@ int embed_fwd(const void* E, const int32_t* tok, void* x, int N, int H, int V, i
               hipStream_t st) {
   if (N == 0) return SLIDE_OK;
   ProfScope ps("embed_fwd", st);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(embed_fwd_kernel<bf16_t>, dim3(N), dim3(256), 0, st, (const bf16_t*)E, tok,
-                       (bf16_t*)x, N, H, V);
-  else
-    hipLaunchKernelGGL(embed_fwd_kernel<float>, dim3(N), dim3(256), 0, st, (const float*)E, tok,
-                       (float*)x, N, H, V);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(embed_fwd_kernel<T>, dim3(N), dim3(256), 0, st,
+                                    (const T*)E, tok, (T*)x, N, H, V));
   return check_launch("embed_fwd");
 }
 
@@ -520,19 +513,16 @@ int embed_bwd(const void* dx, const int32_t* tok, void* dE, int N, int H, int V,
     for (int j = k >> 1; j > 0; j >>= 1)
       hipLaunchKernelGGL(bitonic_step_kernel, dim3(blocks_for(P, 256)), dim3(256), 0, st, keys, P,
                          j, k);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, dim3(V), dim3(256), 0, st, (const bf16_t*)dx,
-                       keys, P, (bf16_t*)dE, H);
-  else
-    hipLaunchKernelGGL(embed_sum_kernel<float>, dim3(V), dim3(256), 0, st, (const float*)dx, keys,
-                       P, (float*)dE, H);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(embed_sum_kernel<T>, dim3(V), dim3(256), 0, st,
+                                    (const T*)dx, keys, P, (T*)dE, H));
   return check_launch("embed_bwd");
 }
 
 int fill_zero(void* p, size_t n, int dtype, hipStream_t st) {
   if (n == 0) return SLIDE_OK;
-  if (dtype == SLIDE_BF16) {
-    // bf16 zero is the all-zero bit pattern: fill as fp32 words plus a possible odd tail
+  if (dtype != SLIDE_F32) {
+    // a 16-bit zero is the all-zero bit pattern: fill as fp32 words plus a possible odd tail
     hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n / 2, 256)), dim3(256), 0, st, (float*)p, n / 2, 0.f);
     if (n & 1)
       hipLaunchKernelGGL(convert_f32_kernel<bf16_t>, dim3(1), dim3(1), 0, st, (const float*)p, (bf16_t*)p + (n - 1), (size_t)1);
@@ -551,12 +541,9 @@ int fill_f32(float* p, size_t n, float v, hipStream_t st) {
 int convert_from_f32(const float* src, void* dst, size_t n, int dtype, hipStream_t st) {
   if (n == 0) return SLIDE_OK;
   ProfScope ps("convert_f32", st);
-  if (dtype == SLIDE_BF16)
-    hipLaunchKernelGGL(convert_f32_kernel<bf16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, st, src,
-                       (bf16_t*)dst, n);
-  else
-    hipLaunchKernelGGL(convert_f32_kernel<float>, dim3(blocks_for(n, 256)), dim3(256), 0, st, src,
-                       (float*)dst, n);
+  SLIDE_DISPATCH(dtype, T,
+                 hipLaunchKernelGGL(convert_f32_kernel<T>, dim3(blocks_for(n, 256)), dim3(256),
+                                    0, st, src, (T*)dst, n));
   return check_launch("convert_f32");
 }
 

@@ -36,7 +36,11 @@ import numpy as np
 import torch
 
 from . import binding as B
-from ._capi import SLIDE_BF16, SLIDE_E_NONFINITE, SLIDE_F32
+from ._capi import SLIDE_BF16, SLIDE_E_NONFINITE, SLIDE_F16, SLIDE_F32
+
+# compute dtype -> (library code, torch dtype of the compute copies, bytes per element)
+_DTYPES = {"bf16": (SLIDE_BF16, torch.bfloat16, 2), "f16": (SLIDE_F16, torch.float16, 2),
+           "f32": (SLIDE_F32, torch.float32, 4)}
 
 
 @dataclass(frozen=True)
@@ -48,7 +52,7 @@ class ModelSpec:
     ffn: int
     vocab: int
     n_layers: int
-    dtype: str = "bf16"          # compute dtype: "bf16" or "f32"
+    dtype: str = "bf16"          # compute dtype: "bf16", "f16" (with loss scaling) or "f32"
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
 
@@ -75,7 +79,7 @@ def pinned_bytes(n, esize, min_bytes=0):
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
                  "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off",
-                 "rows", "row_len")
+                 "rows", "row_len", "adam_t", "hp", "cancelled")
 
     def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None,
                  off=0, rows=None, row_len=0):
@@ -84,6 +88,9 @@ class _Job:
         # rows: update only these rows of row_len elements (int32 indices into p, m, v, out,
         # which then hold n // row_len rows); g None: their gradient is exactly zero
         self.rows, self.row_len = rows, row_len
+        self.adam_t = step     # AdamW's step count (bias correction); the engine sets it
+        self.hp = None         # per-job hyper-parameters (loss-scaled gradients), else the engine's
+        self.cancelled = False  # the step was skipped (fp16 overflow): apply nothing
         self.out, self.n, self.post, self.step, self.priority = out, n, post, step, priority
         self.tier = tier      # (p, m, v) offsets in the disk tier (None: in host memory)
         self.nonfinite = None  # (pinned count array, index) when the gradient is checked
@@ -150,15 +157,15 @@ class _Param:
                  separate_grad=False):
         """copy_bytes: how many bytes the slot ring copies into / out of the pinned buffers
         (its slot size, n elements rounded up to 256 bytes); they are allocated that large.
-        separate_grad: for bf16, the gradient lands in its own pinned buffer instead of the
+        separate_grad: for 16-bit compute, the gradient lands in its own pinned buffer instead of the
         upload buffer (the embedding: the update of its untouched rows writes the upload buffer
         while the gradient of the touched rows is still on its way)."""
         self.n = n
         self.dtype = dtype
         self.tier = tier
-        if dtype == "bf16":
+        if dtype != "f32":
             self.master = _host_f32(n) if tier is None or tier[0] is None else None
-            self.shared = pinned.tensor(n, torch.int16, copy_bytes)        # bf16 bits
+            self.shared = pinned.tensor(n, torch.int16, copy_bytes)        # 16-bit bits
             self.grad_host = (pinned.tensor(n, torch.int16) if separate_grad
                               else self.shared)
         else:
@@ -169,7 +176,7 @@ class _Param:
         self.v = _host_f32(n) if tier is None else None
         self.job = None
         if resident:
-            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+            tdt = _DTYPES[dtype][1]
             self.dev = torch.empty(n, dtype=tdt, device=device)
             self.grad = torch.empty(n, dtype=tdt, device=device)
             self.ready_ev = None      # h2d of the current device copy
@@ -181,7 +188,8 @@ class SlideEngine:
                  adam_threads=0, device="cuda:0", serialize=False, timeline=False,
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
                  tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False,
-                 keep_records=64, on_gradient=None):
+                 keep_records=64, on_gradient=None, embed_split=False, loss_scale=2.0 ** 16,
+                 scale_growth_interval=2000, min_loss_scale=1.0):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -201,6 +209,16 @@ class SlideEngine:
           weights are never overwritten from it.
         keep_records: how many of the latest steps' records (events, job timings) are kept for
           analyse(); older ones are dropped, so a long run does not accumulate them.
+        loss_scale, scale_growth_interval, min_loss_scale: dynamic loss scaling of fp16 compute
+          (spec.dtype "f16"). The gradients are computed for loss_scale times the loss; every
+          block's gradient is checked for NaN / infinity on the GPU, and a step's CPU updates
+          start only once the whole step has passed (they then overlap the next step's forward
+          instead of this step's backward). A step with a non-finite gradient is skipped whole:
+          no parameter, moment or step count changes, and the scale is halved (not below
+          min_loss_scale); after scale_growth_interval good steps in a row it is doubled.
+        embed_split: update the embedding's rows that no input token selects (an exactly zero
+          gradient) while the step runs, and only the selected rows after the backward (False:
+          the whole embedding after the backward, chunk by chunk). Same results either way.
         on_gradient: optional callable(name, step, offset, grad) run on the CPU worker once a
           gradient has landed in host memory and before the update that consumes it (for bf16
           compute the update overwrites the gradient with the new weights). name is the block
@@ -208,7 +226,9 @@ class SlideEngine:
           within its block, grad the host tensor (bf16 bits as int16, or fp32). For gradient
           statistics and inspection; it must not modify grad.
         """
-        assert spec.dtype in ("bf16", "f32")
+        assert spec.dtype in _DTYPES, spec.dtype
+        self.fp16 = spec.dtype == "f16"
+        assert not (self.fp16 and serialize), "serialize is not supported with fp16 compute"
         if activations is None:
             activations = "hbm" if save_activations else "recompute"
         assert activations in ("hbm", "recompute", "host"), activations
@@ -223,9 +243,17 @@ class SlideEngine:
         self.serialize = serialize
         self.timeline = timeline
         self.save_activations = save_activations
-        self.code = SLIDE_BF16 if spec.dtype == "bf16" else SLIDE_F32
-        self.tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
-        self.ts = 2 if spec.dtype == "bf16" else 4
+        self.code, self.tdt, self.ts = _DTYPES[spec.dtype]
+        # dynamic loss scaling (fp16): the scale, good steps in a row, skipped steps; the
+        # optimizer's own step count advances only on applied steps; a step's CPU updates are
+        # released (opened_step) once its gradients have been checked
+        self.loss_scale = float(loss_scale) if self.fp16 else 1.0
+        self.scale_growth_interval = scale_growth_interval
+        self.min_loss_scale = min_loss_scale
+        self.good_steps = 0
+        self.skipped_steps = 0
+        self.opt_step = 0
+        self.opened_step = 0 if self.fp16 else float("inf")
         s = spec
         self.cfg = B.layer_cfg(s.hidden, s.n_heads, s.n_kv_heads, s.head_dim, s.ffn, s.dtype,
                                s.rms_eps, s.rope_theta)
@@ -247,7 +275,7 @@ class SlideEngine:
             tiered = set(range(self.L) if tier_layers is None else tier_layers)
             assert tiered <= set(range(self.L)), tier_layers
             reg = B.slide_tier_region_bytes(self.P)
-            arrays = 3 if s.dtype == "bf16" else 2
+            arrays = 3 if s.dtype != "f32" else 2
             self.tier = B.StateTier(state_tier, max(arrays * reg * len(tiered), 4096),
                                     tier_chunk, tier_io_threads)
         self.tier_layers = sorted(tiered)
@@ -256,14 +284,15 @@ class SlideEngine:
         for i in range(self.L):
             offs = None
             if i in tiered:
-                if s.dtype == "bf16":
+                if s.dtype != "f32":
                     offs, o = (o, o + reg, o + 2 * reg), o + 3 * reg
                 else:
                     offs, o = (None, o, o + reg), o + 2 * reg
             self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs,
                                       copy_bytes=self.w_bytes))
+        self.embed_split = embed_split
         self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True,
-                            separate_grad=True)
+                            separate_grad=embed_split)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         # The LM head is updated, uploaded and flushed per vocabulary chunk of the fused CE, so
@@ -295,9 +324,10 @@ class SlideEngine:
 
         # device memory, allocated once
         dev = self.device
-        self.check_finite = check_finite
+        # fp16 counts every block's non-finite gradient elements for its loss-scale check
+        self.check_finite = check_finite or self.fp16
         self.on_gradient = on_gradient
-        if check_finite:
+        if self.check_finite:
             names = ([f"layer{i}" for i in range(self.L)] + ["w_final"]
                      + [f"lm_head{ci}" for ci in range(self.lm_nch)]
                      + [f"embed{ci}" for ci in range(self.emb_nch)])
@@ -313,7 +343,7 @@ class SlideEngine:
             self.x_slots = max(3, min(x_slots, self.L + 1))
             self.xs = torch.empty((self.x_slots, N, H), dtype=self.tdt, device=dev)
             self.x_host = self.pinned.tensor((self.L + 1) * N * H,
-                                             torch.int16 if s.dtype == "bf16" else torch.float32)
+                                             torch.int16 if s.dtype != "f32" else torch.float32)
             self.x_d2h_ev = [None] * (self.L + 1)
             self.x_h2d_ev = [None] * (self.L + 1)
         else:
@@ -382,7 +412,7 @@ class SlideEngine:
         for prm, arr in zip(self.layers, layers):
             put(prm, arr)
         self._upload_all_resident()
-        self.step_count = 0
+        self._reset_counts()
 
     def init_random(self, seed=0, std=0.02, progress=None):
         """Seeded synthetic weights drawn on the GPU (matrices N(0, std), norm gains 1).
@@ -411,21 +441,32 @@ class SlideEngine:
         self._refresh_shared(self.final)
         draw(self.lm)
         self._upload_all_resident()
-        self.step_count = 0
+        self._reset_counts()
 
-    def _refresh_shared(self, prm):
-        if prm.dtype == "bf16":
-            prm.shared.copy_(prm.master.to(torch.bfloat16).view(torch.int16))
+    def _reset_counts(self, step=0, opt_step=None):
+        self.step_count = step
+        self.opt_step = step if opt_step is None else opt_step
+        if self.fp16:
+            self.opened_step = step
+
+    def _refresh_shared(self, prm, src=None):
+        """The 16-bit compute copy (the upload buffer) of a block from its fp32 master (or from
+        src, a host fp32 tensor of the same values), rounded by the library."""
+        if prm.dtype != "f32":
+            if src is None:
+                src = prm.master if prm.master is not None else torch.from_numpy(
+                    self._get_master(prm))
+            B.slide_cpu_convert_f32(src, prm.shared, self.code, prm.n, self.adam_threads)
 
     def _set_master(self, prm, t):
         """fp32 master weights of a block (a float32 tensor of prm.n elements, any device), and
-        the bf16 compute copy derived from them."""
+        the 16-bit compute copy derived from them."""
+        host = t.detach().to("cpu").float().contiguous()
         if prm.master is not None:
-            prm.master.copy_(t)
+            prm.master.copy_(host)
         else:
-            self.tier.write(prm.tier[0], t.detach().to("cpu").contiguous())
-        if prm.dtype == "bf16":
-            prm.shared.copy_(t.to(torch.bfloat16).view(torch.int16).to("cpu"))
+            self.tier.write(prm.tier[0], host)
+        self._refresh_shared(prm, host)
 
     def _zero_moments(self, prm):
         if prm.tier is None:
@@ -470,7 +511,9 @@ class SlideEngine:
             for kind in ("master", "m", "v"):
                 np.save(os.path.join(path, f"{name}.{kind}.npy"), self._state(prm, kind),
                         allow_pickle=False)
-        manifest = dict(step=self.step_count, spec=dataclasses.asdict(self.spec),
+        manifest = dict(step=self.step_count, opt_step=self.opt_step,
+                        loss_scale=self.loss_scale, good_steps=self.good_steps,
+                        spec=dataclasses.asdict(self.spec),
                         hp=dict(lr=self.hp.lr, beta1=self.hp.beta1, beta2=self.hp.beta2,
                                 eps=self.hp.eps, weight_decay=self.hp.weight_decay),
                         blocks={name: prm.n for name, prm in blocks.items()})
@@ -499,7 +542,10 @@ class SlideEngine:
                 else:
                     self.tier.write(prm.tier[idx], arr)
         self._upload_all_resident()
-        self.step_count = int(manifest["step"])
+        self._reset_counts(int(manifest["step"]), int(manifest.get("opt_step", manifest["step"])))
+        if self.fp16 and "loss_scale" in manifest:
+            self.loss_scale = float(manifest["loss_scale"])
+            self.good_steps = int(manifest.get("good_steps", 0))
 
     def tier_stats(self):
         """Traffic and time of the disk tier so far (None without a tier)."""
@@ -517,7 +563,7 @@ class SlideEngine:
 
     def _upload_resident(self, prm):
         with torch.cuda.stream(self.h2d):
-            src = prm.shared.view(torch.bfloat16) if prm.dtype == "bf16" else prm.shared
+            src = prm.shared.view(self.tdt) if prm.dtype != "f32" else prm.shared
             prm.dev.copy_(src, non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(self.h2d)
@@ -533,7 +579,10 @@ class SlideEngine:
 
     # ------------------------------------------------------------------ CPU worker
     def _landed(self, job):
-        """Non-blocking: have this job's gradients arrived in host memory?"""
+        """Non-blocking: have this job's gradients arrived in host memory (and, for fp16 compute,
+        has its step passed the overflow check)?"""
+        if job.step > self.opened_step:
+            return False
         if job.wait is None:
             return True
         if isinstance(job.wait, int):
@@ -574,7 +623,7 @@ class SlideEngine:
             with self.jobs_cv:
                 self.jobs.remove(job)
             try:
-                if self.worker_error is None:
+                if self.worker_error is None and not job.cancelled:
                     if job.nonfinite is not None:
                         arr, k = job.nonfinite
                         bad = int(arr[k])
@@ -586,19 +635,20 @@ class SlideEngine:
                     if self.on_gradient is not None and job.g is not None:
                         self.on_gradient(job.name, job.step, job.off, job.g)
                     job.t_ready = time.perf_counter()
+                    hp = job.hp if job.hp is not None else self.hp
                     if job.rows is not None:
                         if len(job.rows):
                             B.slide_cpu_adamw_rows(job.p, job.g, self.code, job.m, job.v,
                                                    job.out, job.row_len, job.n // job.row_len,
-                                                   job.rows, len(job.rows), job.step, self.hp,
+                                                   job.rows, len(job.rows), job.adam_t, hp,
                                                    self.adam_threads)
                     elif job.tier is None:
                         B.slide_cpu_adamw(job.p, job.g, self.code, job.m, job.v, job.out, job.n,
-                                          job.step, self.hp, self.adam_threads)
+                                          job.adam_t, hp, self.adam_threads)
                     else:
                         po, mo, vo = job.tier
                         self.tier.adamw(job.p, po or 0, job.m, mo, job.v, vo, job.g, self.code,
-                                        job.out, job.n, job.step, self.hp, self.tier_threads)
+                                        job.out, job.n, job.adam_t, hp, self.tier_threads)
                     job.t_start = job.t_ready
                     job.t_end = time.perf_counter()
                     if job.post is not None:
@@ -609,7 +659,7 @@ class SlideEngine:
                 job.done.set()
 
     def _submit(self, prm, wait, name, priority, post=None):
-        out = prm.shared if prm.dtype == "bf16" else None
+        out = prm.shared if prm.dtype != "f32" else None
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
                    self.step_count, priority, post, prm.tier)
         self._nf_attach(job)
@@ -632,10 +682,16 @@ class SlideEngine:
             self.nf_host[k:k + 1].copy_(self.nf_dev[k:k + 1], non_blocking=True)
 
     def _nf_attach(self, job):
-        if self.check_finite and job.name in self.nf_index:
+        """The worker refuses a non-finite update (check_finite); with fp16 compute the engine
+        decides for the whole step instead."""
+        if self.check_finite and not self.fp16 and job.name in self.nf_index:
             job.nonfinite = (self.nf_host, self.nf_index[job.name])
 
     def _enqueue(self, job):
+        job.adam_t = self.opt_step + 1
+        if self.fp16:
+            h = self.hp
+            job.hp = B.AdamWHp(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, self.loss_scale)
         with self.jobs_cv:
             self.job_seq += 1
             job.seq = self.job_seq
@@ -705,7 +761,7 @@ class SlideEngine:
         self.d2h.wait_event(ev_c)
         with torch.cuda.stream(self.d2h):
             self._nf_fetch(name)
-            dst = prm.grad_host.view(torch.bfloat16) if prm.dtype == "bf16" else prm.grad_host
+            dst = prm.grad_host.view(self.tdt) if prm.dtype != "f32" else prm.grad_host
             dst.copy_(prm.grad, non_blocking=True)
             done = torch.cuda.Event()
             done.record(self.d2h)
@@ -720,7 +776,7 @@ class SlideEngine:
     def _x_host(self, i):
         n = self.N * self.spec.hidden
         t = self.x_host[i * n:(i + 1) * n]
-        return (t.view(torch.bfloat16) if self.spec.dtype == "bf16" else t).view(self.N, -1)
+        return (t.view(self.tdt) if self.spec.dtype != "f32" else t).view(self.N, -1)
 
     def _x_offload(self, i):
         """After the compute stream's work so far (the forward of layer i), copy layer input i
@@ -762,7 +818,7 @@ class SlideEngine:
         with torch.cuda.stream(self.d2h):
             self._nf_fetch(name)
             dst = prm.grad_host[sl]
-            dst = dst.view(torch.bfloat16) if prm.dtype == "bf16" else dst
+            dst = dst.view(self.tdt) if prm.dtype != "f32" else dst
             dst.copy_(prm.grad[sl], non_blocking=True)
             done = torch.cuda.Event()
             done.record(self.d2h)
@@ -770,13 +826,13 @@ class SlideEngine:
         def upload():
             with torch.cuda.stream(self.h2d):
                 src = prm.shared[sl]
-                src = src.view(torch.bfloat16) if prm.dtype == "bf16" else src
+                src = src.view(self.tdt) if prm.dtype != "f32" else src
                 prm.dev[sl].copy_(src, non_blocking=True)
                 ev = torch.cuda.Event()
                 ev.record(self.h2d)
             on_ready(ev)
 
-        out = prm.shared[sl] if prm.dtype == "bf16" else None
+        out = prm.shared[sl] if prm.dtype != "f32" else None
         job = _Job(name, done, prm.master[sl], prm.grad_host[sl], prm.m[sl], prm.v[sl], out,
                    (r1 - r0) * H, self.step_count, priority, upload, off=r0 * H, rows=rows,
                    row_len=H)
@@ -806,7 +862,7 @@ class SlideEngine:
         zero[self.emb_present] = False
         rows = np.flatnonzero(zero).astype(np.int32)
         prm = self.embed
-        out = prm.shared if prm.dtype == "bf16" else None
+        out = prm.shared if prm.dtype != "f32" else None
         job = _Job("embed_zero", None, prm.master, None, prm.m, prm.v, out, V * H,
                    self.step_count, -2, rows=rows, row_len=H)
         rec["other_jobs"].append(job)
@@ -820,11 +876,12 @@ class SlideEngine:
         for ci, (r0, r1) in enumerate(self.emb_rows):
             def ready(ev, ci=ci):
                 self.emb_ready[ci] = ev
-            pr = self.emb_present
-            sel = pr[(pr >= r0) & (pr < r1)] - r0
+            sel = None
+            if self.embed_split:
+                pr = self.emb_present
+                sel = (pr[(pr >= r0) & (pr < r1)] - r0).astype(np.int32)
             job, done = self._flush_chunk(self.embed, r0, r1, f"embed{ci}",
-                                          -1 + ci / self.emb_nch, rec, ready,
-                                          rows=sel.astype(np.int32))
+                                          -1 + ci / self.emb_nch, rec, ready, rows=sel)
             self.emb_flushed[ci] = done
             self.emb_job[ci] = job
             self._enqueue(job)
@@ -879,8 +936,9 @@ class SlideEngine:
             if self.emb_flushed[ci] is not None:
                 c.wait_event(self.emb_flushed[ci])
         B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
-        self.emb_present = np.unique(np.asarray(tok[:, :-1])).astype(np.int32)
-        self._update_embed_zero_rows(rec)
+        if self.embed_split:
+            self.emb_present = np.unique(np.asarray(tok[:, :-1])).astype(np.int32)
+            self._update_embed_zero_rows(rec)
         for i in range(L):
             if i not in slots:
                 prefetch(need=i)
@@ -912,6 +970,7 @@ class SlideEngine:
         B.slide_rmsnorm_fwd(self._x(L), self.final.dev, self.hf, None, N, H, spec.rms_eps,
                             self.code, c)
         ce, lm = self.ce_cfg, self.lm
+        ce.grad_scale = self.loss_scale if self.fp16 else 0.0
         ce_iv = rec["ce_iv"] = []         # GPU intervals of the CE, without its waits
         for ci in range(self.lm_nch):
             self._wait_job(self.lm_job[ci])       # this chunk's previous update, then its upload
@@ -987,9 +1046,43 @@ class SlideEngine:
         e_end.synchronize()
         rec["ev0"], rec["ev_end"] = ev0, e_end
         rec["host_gpu_done"] = time.perf_counter()
+        if self.fp16:
+            self._loss_scale_check(rec)
+        else:
+            self.opt_step += 1
         self._sync()
         self.records.append(rec)
         return rec
+
+    def _loss_scale_check(self, rec):
+        """fp16: once the step's gradients are complete, release its CPU updates if every
+        gradient is finite, or skip the whole step: cancel the updates (none has started: they
+        wait for this release), put the fp32 masters' 16-bit copies back into the upload buffers
+        (where the gradients landed) and halve the loss scale."""
+        bad = int(self.nf_dev.cpu().sum())
+        rec["loss_scale"], rec["nonfinite"] = self.loss_scale, bad
+        jobs = rec["jobs"] + rec["other_jobs"]
+        if bad:
+            for j in jobs:
+                j.cancelled = True
+        with self.jobs_cv:
+            self.opened_step = self.step_count
+            self.jobs_cv.notify_all()
+        if not bad:
+            self.opt_step += 1
+            self.good_steps += 1
+            if self.good_steps >= self.scale_growth_interval:
+                self.loss_scale *= 2.0
+                self.good_steps = 0
+            return
+        for j in jobs:
+            j.done.wait()
+        self.d2h.synchronize()           # every gradient copy has landed
+        for prm in self.layers + [self.embed, self.final, self.lm]:
+            self._refresh_shared(prm)
+        self.loss_scale = max(self.loss_scale * 0.5, self.min_loss_scale)
+        self.good_steps = 0
+        self.skipped_steps += 1
 
     def loss(self):
         return float(self.loss_dev.item())

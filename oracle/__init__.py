@@ -22,12 +22,12 @@ from .model import (LayerShape, rmsnorm_fwd, rmsnorm_bwd, rope_tables, rope_rota
                     layer_bwd, ce_dense, ce_chunked, embedding_fwd, embedding_bwd,
                     ModelShape, model_loss_and_grads, LAYER_PARAM_NAMES)
 from .adamw import (adamw_fp64, adamw_fp32, bf16_round_bits, bf16_bits_to_f32,
-                    AdamWHyper)
+                    f16_round_bits, f16_bits_to_f32, AdamWHyper)
 
 __all__ = [
     "LayerShape", "rmsnorm_fwd", "rmsnorm_bwd", "rope_tables", "rope_rotate",
     "attention_fwd", "attention_bwd", "swiglu_fwd", "swiglu_bwd", "layer_fwd", "layer_bwd",
     "ce_dense", "ce_chunked", "embedding_fwd", "embedding_bwd", "ModelShape",
     "model_loss_and_grads", "LAYER_PARAM_NAMES", "adamw_fp64", "adamw_fp32",
-    "bf16_round_bits", "bf16_bits_to_f32", "AdamWHyper",
+    "bf16_round_bits", "bf16_bits_to_f32", "f16_round_bits", "f16_bits_to_f32", "AdamWHyper",
 ]

@@ -23,9 +23,10 @@ Two forms:
                   v'  = (c_b2 * v) + (c_1b2 * (g * g))
                   den = (sqrt(v') / c_bc2) + c_eps
                   p'  = p1 - c_step * (m' / den)
-              plus the bf16 copy of p' rounded to nearest-even (NaN -> quiet NaN), which is
-              the FP32 -> BF16 conversion the summary places in the shared host buffers
-              (section 2B).
+              plus the bf16 (or fp16) copy of p' rounded to nearest-even (NaN -> quiet NaN),
+              which is the FP32 -> BF16/FP16 conversion the summary places in the shared host
+              buffers (section 2B). With loss scaling (fp16 training) the gradient is first
+              multiplied by float32(1 / scale).
 The two agree to about 1e-6 relative (pinned in the tests).
 """
 from dataclasses import dataclass
@@ -72,10 +73,12 @@ def _scalars_fp32(t, hp: AdamWHyper):
     )
 
 
-def adamw_fp32(p, g, m, v, t, hp: AdamWHyper):
+def adamw_fp32(p, g, m, v, t, hp: AdamWHyper, grad_scale=1.0, copy="bf16"):
     """The fixed-order float32 AdamW step. p, g, m, v: float32 arrays (g may be any float
-    array exactly representable in float32, e.g. widened bf16). Returns new (p, m, v,
-    p_bf16_bits) with the bf16 copy as uint16 bit patterns."""
+    array exactly representable in float32, e.g. widened bf16 or fp16). grad_scale: the loss
+    scale the gradient carries (dynamic loss scaling): g is first multiplied by
+    float32(1 / grad_scale), unless grad_scale is 0 or 1. Returns new (p, m, v, copy_bits) with
+    the 16-bit copy of p ("bf16" or "f16", round to nearest-even) as uint16 bit patterns."""
     c = _scalars_fp32(t, hp)
     f32 = np.float32
     p = np.asarray(p, f32)
@@ -83,12 +86,15 @@ def adamw_fp32(p, g, m, v, t, hp: AdamWHyper):
     m = np.asarray(m, f32)
     v = np.asarray(v, f32)
     with np.errstate(all="ignore"):
+        if grad_scale not in (0, 1, 0.0, 1.0):
+            g = g * f32(1.0 / grad_scale)
         p1 = p * c["c_dec"]
         m2 = (c["c_b1"] * m) + (c["c_1b1"] * g)
         v2 = (c["c_b2"] * v) + (c["c_1b2"] * (g * g))
         den = (np.sqrt(v2) / c["c_bc2"]) + c["c_eps"]
         p2 = p1 - c["c_step"] * (m2 / den)
-    return p2.astype(f32), m2.astype(f32), v2.astype(f32), bf16_round_bits(p2)
+    bits = f16_round_bits(p2) if copy == "f16" else bf16_round_bits(p2)
+    return p2.astype(f32), m2.astype(f32), v2.astype(f32), bits
 
 
 def bf16_round_bits(x):
@@ -101,6 +107,18 @@ def bf16_round_bits(x):
     rounded = ((b + 0x7FFF + lsb) >> 16) & 0xFFFF
     quiet = ((b >> 16) | 0x0040) & 0xFFFF
     return np.where(is_nan, quiet, rounded).astype(np.uint16)
+
+
+def f16_round_bits(x):
+    """float32 -> IEEE binary16 bit pattern (uint16), round to nearest, ties to even, overflow
+    to infinity (NumPy's float16 conversion, which implements the IEEE-754 rounding)."""
+    with np.errstate(all="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits):
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float32)
 
 
 def bf16_bits_to_f32(bits):

@@ -95,6 +95,9 @@ def _finish(a, dtype):
     if dtype == "bf16":
         bits = to_bf16_bits(a)
         return Tensor(bf16_bits_as_f32(bits), bits)
+    if dtype == "f16":     # IEEE binary16, round to nearest-even (NumPy's conversion)
+        h = a.astype(np.float16)
+        return Tensor(h.astype(np.float32), h.view(np.uint16))
     return Tensor(a)
 
 
@@ -118,7 +121,7 @@ def layer_params(cfg: LayerCfg, dtype, seed=0, std=0.02, gain_std=0.0):
 
 def pack_layer(params, cfg: LayerCfg, dtype):
     """Concatenate one layer's parameters in slot packing order (flat array)."""
-    parts = [(params[n].bits if dtype == "bf16" else params[n].f32).reshape(-1)
+    parts = [(params[n].bits if dtype in ("bf16", "f16") else params[n].f32).reshape(-1)
              for n, _ in cfg.param_shapes()]
     return np.concatenate(parts)
 

@@ -5,18 +5,22 @@ import numpy as np
 import torch
 
 DEV = "cuda:0"
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+# fp16 (not stated by the pages or the task): the bf16 bound scaled by the ratio of the unit
+# roundoffs, 2^-11 / 2^-8 = 1/8, since every rounding point is the same and only the format
+# changes
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2.5e-3}
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def dev(arr, dtype):
-    """numpy fp32 (exactly bf16-representable when dtype is bf16) -> device tensor."""
+    """numpy fp32 (exactly representable in dtype) -> device tensor."""
     t = torch.from_numpy(np.ascontiguousarray(arr, np.float32))
-    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    t = t.to(_TORCH[dtype])
     return t.to(DEV)
 
 
 def empty(shape, dtype):
-    return torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+    return torch.empty(shape, dtype=_TORCH[dtype],
                        device=DEV)
 
 
@@ -40,8 +44,8 @@ def rel_err(a, r, scale=None):
 def assert_close(a, r, dtype, what, tol=None, scale=None):
     e = rel_err(a, r, scale)
     lim = TOL[dtype] if tol is None else tol
-    print(f"  {what}: rel err {e:.3e} (limit {lim:.0e})", flush=True)
-    assert e <= lim, f"{what}: rel err {e:.3e} > {lim:.0e}"
+    print(f"  {what}: rel err {e:.3e} (limit {lim:.1e})", flush=True)
+    assert e <= lim, f"{what}: rel err {e:.3e} > {lim:.1e}"
 
 
 def ws(nbytes):

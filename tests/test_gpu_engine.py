@@ -189,7 +189,7 @@ def _oracle_from_flat(flat, w):
     return out
 
 
-@pytest.mark.parametrize("activations", ["hbm", "host", "recompute"])
+@pytest.mark.parametrize("activations", ["hbm", "host", "recompute", "hbm-embed-split"])
 def test_bf16_step_gradients_updates_and_uploads_match_oracle(activations):
     """The benchmarked bf16 path, where one pinned buffer per block is both the gradient landing
     zone and the upload source and the CPU AdamW writes the new bf16 weights into it in place.
@@ -226,8 +226,10 @@ def test_bf16_step_gradients_updates_and_uploads_match_oracle(activations):
     vv = {k: np.zeros(v.size, np.float32) for k, v in p.items()}
     sh = om.ModelShape(om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn),
                        w.n_layers, w.vocab)
+    split = activations.endswith("-embed-split")
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=hp, adam_threads=3, ce_chunk=256,
-                      activations=activations, x_slots=3, on_gradient=on_gradient)
+                      activations=activations.split("-")[0], x_slots=3,
+                      on_gradient=on_gradient, embed_split=split)
     try:
         eng.load_params(p["embed"], [p[f"layer{i}"] for i in range(w.n_layers)], p["w_final"],
                         p["lm_head"])

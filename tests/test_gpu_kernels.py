@@ -22,6 +22,8 @@ def _round(a, dtype):
     t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
     if dtype == "bf16":
         t = t.to(torch.bfloat16).float()
+    elif dtype == "f16":
+        t = t.to(torch.float16).float()
     return t.numpy().astype(np.float64)
 
 
@@ -37,8 +39,9 @@ def _r8(v):
 
 
 # the fp32 kernel (tiny fp32 model) has a single tile shape: only the small shape applies to it
-GEMM_CASES = ([("bf16",) + s for s in GEMM_SHAPES]
+GEMM_CASES = ([("bf16",) + s for s in GEMM_SHAPES] + [("f16",) + s for s in GEMM_SHAPES]
               + [("f32",) + s for s in GEMM_SHAPES if s[0] <= 1000])
+GEMM_TOL = {"bf16": 1e-2, "f16": 2e-3, "f32": 1e-5}
 
 
 @pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, True), (False, False)])
@@ -60,7 +63,7 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     C = empty((M, N), dtype)
     sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C, N, code, dtype=code, stream=stream())
     torch.cuda.synchronize()
-    assert_close(host(C), ref, dtype, "C = A B", tol=1e-2 if dtype == "bf16" else 1e-5)
+    assert_close(host(C), ref, dtype, "C = A B", tol=GEMM_TOL[dtype])
     C2 = empty((M, N), dtype)
     sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C2, N, code, R=dev(R, dtype), ldr=N,
                   alpha=0.5, dtype=code, stream=stream())
@@ -71,14 +74,14 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C4, N, sl.SLIDE_F32, dtype=code,
                   stream=stream())
     torch.cuda.synchronize()
-    assert_close(host(C2), 0.5 * ref + R, dtype, "C = R + 0.5 A B", tol=1e-2 if dtype == "bf16" else 1e-5)
+    assert_close(host(C2), 0.5 * ref + R, dtype, "C = R + 0.5 A B", tol=GEMM_TOL[dtype])
     assert_close(host(C3), 1.0 + ref, "f32", "C += A B (fp32 accumulate)", tol=1e-5)
     assert_close(host(C4), ref, "f32", "C = A B (fp32 output)", tol=1e-5)
 
 
 # N = 300 and 517: several 64-row partial sums of the weight gradient, the last one ragged
 @pytest.mark.parametrize("dtype,H,N", [("bf16", 4096, 37), ("f32", 256, 37), ("bf16", 264, 300),
-                                       ("f32", 200, 517)])
+                                       ("f32", 200, 517), ("f16", 4096, 37), ("f16", 264, 300)])
 def test_rmsnorm_fwd_bwd(dtype, H, N):
     print(f"rmsnorm {dtype} N={N} H={H}", flush=True)
     x = activations((N, H), dtype, 5).f64
@@ -103,7 +106,7 @@ def test_rmsnorm_fwd_bwd(dtype, H, N):
     assert_close(host(dw), rdw, dtype, "rmsnorm dw")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f16", 128)])
 def test_rope_forward_and_inverse(dtype, d):
     B, S, nq, nkv = 2, 77, 4, 2
     print(f"rope {dtype} d={d} S={S}", flush=True)
@@ -133,6 +136,8 @@ def test_rope_forward_and_inverse(dtype, d):
     ("bf16", 1, 128, 4, 4, 64),      # MHA, head_dim 64
     ("bf16", 1, 1, 4, 1, 128),       # a single token: o = v
     ("f32", 2, 128, 4, 4, 64),
+    ("f16", 2, 200, 8, 2, 128),
+    ("f16", 1, 128, 4, 4, 64),
 ])
 def test_attention_fwd_bwd(dtype, B, S, nq, nkv, d):
     print(f"attention {dtype} B={B} S={S} nq={nq} nkv={nkv} d={d}", flush=True)
@@ -168,7 +173,7 @@ def test_attention_fwd_bwd(dtype, B, S, nq, nkv, d):
     assert_close(g[..., (nq + nkv) * d:].reshape(B, S, nkv, d), dv, dtype, "attention dv")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_embedding_fwd_bwd_repeated_tokens(dtype):
     N, H, V = 300, 264, 40           # small vocabulary: every token repeats several times
     print(f"embedding {dtype} N={N} H={H} V={V}", flush=True)
@@ -191,11 +196,11 @@ def test_embedding_fwd_bwd_repeated_tokens(dtype):
     dE2 = torch.empty_like(dE)
     sl.slide_embed_bwd(dev(dx, dtype), t_tok, dE2, N, H, V, code, ws(wsz), wsz, stream())
     torch.cuda.synchronize()
-    assert torch.equal(dE.view(torch.int16) if dtype == "bf16" else dE,
-                       dE2.view(torch.int16) if dtype == "bf16" else dE2)
+    assert torch.equal(dE.view(torch.int16) if dtype != "f32" else dE,
+                       dE2.view(torch.int16) if dtype != "f32" else dE2)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("n", [0, 5, 8, 1000003])
 def test_nonfinite_count_exact(dtype, n):
     """Exact count of NaN / +inf / -inf among finite values of every size class (including the
@@ -203,7 +208,7 @@ def test_nonfinite_count_exact(dtype, n):
     print(f"nonfinite count {dtype} n={n}", flush=True)
     rng = _rng(40)
     a = rng.standard_normal(n).astype(np.float32)
-    big = 3.3e38 if dtype == "bf16" else 3.4e38
+    big = {"bf16": 3.3e38, "f32": 3.4e38, "f16": 65504.0}[dtype]
     special = np.array([np.nan, np.inf, -np.inf, big, -big, 1e-40, 0.0, -0.0], np.float32)
     if n:
         idx = rng.choice(n, size=min(n, 64), replace=False)

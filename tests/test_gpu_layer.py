@@ -7,7 +7,7 @@ import torch
 import layer_sliding_offloaded_fwd_amd as sl
 from oracle import model as om
 from seeded_inputs import LayerCfg, TINY, activations, ce_inputs, layer_params, pack_layer
-from tests._gpu import DEV, assert_close, dev, empty, host, stream, ws
+from tests._gpu import DEV, assert_close, dev, empty, host, rel_err, stream, ws
 
 pytestmark = pytest.mark.gpu
 
@@ -17,10 +17,13 @@ def _oracle_shape(c: LayerCfg):
                          c.rope_theta)
 
 
+_TDT = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def _packed_to_device(params, c, dtype):
     flat = pack_layer(params, c, dtype)
-    t = torch.from_numpy(flat.view(np.int16) if dtype == "bf16" else flat).to(DEV)
-    return t.view(torch.bfloat16) if dtype == "bf16" else t
+    t = torch.from_numpy(flat.view(np.int16) if dtype != "f32" else flat).to(DEV)
+    return t.view(_TDT[dtype]) if dtype != "f32" else t
 
 
 def _unpack(g, c):
@@ -36,6 +39,8 @@ CASES = [
     ("tiny-fp32", TINY.layer, "f32", 2, 128, 0.0),
     ("bf16-gqa-ragged", LayerCfg(512, 8, 2, 64, 1376), "bf16", 2, 200, 0.1),
     ("bf16-d128", LayerCfg(1024, 8, 4, 128, 2816), "bf16", 1, 256, 0.1),
+    ("f16-gqa-ragged", LayerCfg(512, 8, 2, 64, 1376), "f16", 2, 200, 0.1),
+    ("f16-d128", LayerCfg(1024, 8, 4, 128, 2816), "f16", 1, 256, 0.1),
 ]
 
 
@@ -71,9 +76,9 @@ def test_layer_fwd_bwd_matches_oracle(name, c, dtype, B, S, gain_std):
         assert_close(gg[n], rg[n], dtype, f"grad {n}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_saved_intermediates_give_identical_results(dtype):
-    c, B, S = (LayerCfg(512, 8, 2, 64, 1376), 2, 200) if dtype == "bf16" else (TINY.layer, 2, 128)
+    c, B, S = (LayerCfg(512, 8, 2, 64, 1376), 2, 200) if dtype != "f32" else (TINY.layer, 2, 128)
     print(f"layer fwd_save / bwd_saved vs recompute, {dtype}", flush=True)
     N = B * S
     params = layer_params(c, dtype, seed=7, gain_std=0.1)
@@ -94,7 +99,7 @@ def test_saved_intermediates_give_identical_results(dtype):
     sl.slide_layer_fwd_save(cfg, w, tx, y2, B, S, saved, sb, stream())
     sl.slide_layer_bwd_saved(cfg, w, tx, tdy, dx2, g2, B, S, saved, sb, ws(w2), w2, stream())
     torch.cuda.synchronize()
-    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    bits = (lambda t: t.view(torch.int16)) if dtype != "f32" else (lambda t: t.view(torch.int32))
     assert torch.equal(bits(y1), bits(y2))
     assert torch.equal(bits(dx1), bits(dx2))
     assert torch.equal(bits(g1), bits(g2))
@@ -128,6 +133,8 @@ CE_CASES = [
     ("bf16-one-chunk", "bf16", 128, 512, 2048, 8192, 0.0),
     ("f32-tiny", "f32", 256, 256, 1024, 8192, 0.0),
     ("bf16-all-ignored", "bf16", 64, 256, 512, 128, 1.0),
+    ("f16-ragged-chunks", "f16", 300, 256, 1000, 256, 0.1),
+    ("f16-one-chunk", "f16", 128, 512, 2048, 8192, 0.0),
 ]
 
 
@@ -156,7 +163,8 @@ def test_lmhead_ce_matches_oracle(name, dtype, N, H, V, chunk, ign):
 
 
 @pytest.mark.parametrize("dtype,N,H,V,chunk,ign", [("bf16", 300, 256, 1000, 256, 0.1),
-                                                  ("f32", 200, 256, 1024, 384, 0.0)])
+                                                  ("f32", 200, 256, 1024, 384, 0.0),
+                                                  ("f16", 300, 256, 1000, 256, 0.1)])
 def test_lmhead_ce_phases_equal_single_call(dtype, N, H, V, chunk, ign):
     """The host-driven phases (stats per chunk in reverse order, loss, grad per chunk, dh) give
     the single call's results bit for bit."""
@@ -182,6 +190,42 @@ def test_lmhead_ce_phases_equal_single_call(dtype, N, H, V, chunk, ign):
     sl.slide_lmhead_ce_dh(cfg, N, dh2, W2, wsz, stream())
     torch.cuda.synchronize()
     assert torch.equal(loss1, loss2)
-    bits = (lambda x: x.view(torch.int16)) if dtype == "bf16" else (lambda x: x.view(torch.int32))
+    bits = (lambda x: x.view(torch.int16)) if dtype != "f32" else (lambda x: x.view(torch.int32))
     assert torch.equal(bits(dh1), bits(dh2))
     assert torch.equal(bits(dw1), bits(dw2))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_lmhead_ce_gradient_scale(dtype):
+    """With grad_scale S (dynamic loss scaling) the CE returns the same loss and S times the
+    gradients. In bf16 (fp32's exponent range) a power-of-two S scales every rounding point
+    exactly, so dh and dW are S times the unscaled values exactly. In fp16 the unscaled dz
+    (about 1 / (V N)) lies in the subnormal range and loses digits, which S restores: the
+    scaled gradients match the oracle within the fp16 bound and more closely than the unscaled
+    ones."""
+    N, H, V, chunk = 300, 256, 1000, 256
+    S = 1024.0
+    print(f"lmhead ce {dtype} grad_scale {S}", flush=True)
+    h, w, t = ce_inputs(N, H, V, dtype, ignore_frac=0.1)
+    th, tw, tt = dev(h.f32, dtype), dev(w.f32, dtype), torch.from_numpy(t).to(DEV)
+    out = []
+    for scale in (0.0, S):
+        cfg = sl.CeCfg(H, V, chunk, sl.dtype_code(dtype), scale)
+        wsz = sl.slide_lmhead_ce_workspace_bytes(cfg, N)
+        loss = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
+        dh, dw = empty((N, H), dtype), empty((V, H), dtype)
+        sl.slide_lmhead_ce(cfg, th, tw, tt, N, loss, dh, dw, ws(wsz), wsz, stream())
+        torch.cuda.synchronize()
+        out.append((float(loss.item()), host(dh), host(dw)))
+    (l0, dh0, dw0), (l1, dh1, dw1) = out
+    assert l0 == l1
+    rl, rdh, rdw, _ = om.ce_dense(h.f64, w.f64, t)
+    if dtype == "bf16":
+        assert np.array_equal(dh1, S * dh0) and np.array_equal(dw1, S * dw0)
+    else:
+        e0 = rel_err(dw0, rdw)
+        e1 = rel_err(dw1 / S, rdw)
+        print(f"  fp16 dW rel err unscaled {e0:.3e}, scaled by {S:g} {e1:.3e}", flush=True)
+        assert e1 < e0
+    assert_close(dh1 / S, rdh, dtype, "ce dh / S")
+    assert_close(dw1 / S, rdw, dtype, "ce dw / S")

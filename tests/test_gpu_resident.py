@@ -115,9 +115,10 @@ def _spec(w):
                      w.dtype, c.rms_eps, c.rope_theta)
 
 
-@pytest.mark.parametrize("w,ce_chunk,steps", [(SMALL, 256, 3), (RAGGED, 256, 2),
-                                              (TINY, 8192, 2)], ids=["bf16", "ragged", "f32"])
-def test_resident_step_equals_offloaded_step(w, ce_chunk, steps):
+@pytest.mark.parametrize("w,ce_chunk,steps,split", [(SMALL, 256, 3, False), (RAGGED, 256, 2, False),
+                                                    (TINY, 8192, 2, False), (SMALL, 256, 3, True)],
+                         ids=["bf16", "ragged", "f32", "bf16-embed-split"])
+def test_resident_step_equals_offloaded_step(w, ce_chunk, steps, split):
     print(f"resident vs offloaded: {w.name} steps={steps}", flush=True)
     params = model_params(w, seed=0, gain_std=0.1)
     flat = [np.concatenate([lp[n].f32.reshape(-1) for n, _ in w.layer.param_shapes()])
@@ -126,7 +127,7 @@ def test_resident_step_equals_offloaded_step(w, ce_chunk, steps):
     hp = AdamW(lr=1e-3)
 
     eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=hp, adam_threads=3,
-                      ce_chunk=ce_chunk)
+                      ce_chunk=ce_chunk, embed_split=split)
     try:
         eng.load_params(params["embed"].f32, flat, params["w_final"].f32, params["lm_head"].f32)
         la = []
