@@ -161,6 +161,53 @@ def test_cpu_adamw_bit_exact_vs_oracle(gdt, threads):
         np.testing.assert_array_equal(out, bo)
 
 
+def _same_f32_nan(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    assert np.array_equal(na, nb)
+    assert np.array_equal(a.view(np.uint32)[~na], b.view(np.uint32)[~nb])
+
+
+@pytest.mark.parametrize("threads", [1, 5])
+def test_cpu_adamw_fp16_gradient_with_loss_scale_bit_exact_vs_oracle(threads):
+    """fp16 gradients at a loss scale of 2^16 (including values that overflowed to infinity):
+    the update unscales them and writes an fp16 copy, bit for bit as the oracle's contract (NaN
+    results compared as NaN)."""
+    rng = np.random.default_rng(14)
+    n = 50_001
+    S = 2.0 ** 16
+    p = rng.standard_normal(n).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    po, mo, vo = p.copy(), m.copy(), v.copy()
+    hp = sl.AdamWHp(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay, S)
+    for t in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3 * S).astype(np.float32)
+        if t == 2:
+            g[:3] = [np.inf, -np.inf, 70000.0]
+        gbits = oa.f16_round_bits(g)
+        out = np.zeros(n, np.uint16)
+        sl.slide_cpu_adamw(p, gbits.copy(), sl.SLIDE_F16, m, v, out, n, t, hp, threads)
+        po, mo, vo, bo = oa.adamw_fp32(po, oa.f16_bits_to_f32(gbits), mo, vo, t, HP,
+                                       grad_scale=S, copy="f16")
+        _same_f32_nan(p, po)
+        _same_f32_nan(m, mo)
+        _same_f32_nan(v, vo)
+        _same_f32_nan(oa.f16_bits_to_f32(out), oa.f16_bits_to_f32(bo))
+
+
+def test_cpu_convert_f32_matches_oracle_rounding():
+    rng = np.random.default_rng(15)
+    x = (rng.standard_normal(70_001) * 10.0 ** rng.integers(-10, 6, 70_001)).astype(np.float32)
+    x[:4] = [np.inf, -np.inf, 65520.0, 1e-9]
+    for code, ref in ((sl.SLIDE_BF16, oa.bf16_round_bits(x)), (sl.SLIDE_F16, oa.f16_round_bits(x))):
+        out = np.zeros(x.size, np.uint16)
+        sl.slide_cpu_convert_f32(x, out, code, x.size, 3)
+        assert np.array_equal(out, ref)
+    with pytest.raises(sl.SlideError):
+        sl.slide_cpu_convert_f32(x, np.zeros(4, np.float32), sl.SLIDE_F32, 4)
+
+
 def test_cpu_adamw_shared_grad_and_bf16_buffer_and_scalar_path():
     """The bf16 gradient landing buffer may double as the bf16 weight output (in place)."""
     rng = np.random.default_rng(12)

@@ -438,3 +438,129 @@ def test_nonfinite_gradient_check(tmp_path):
                 eng.close()
             except SlideError:
                 pass
+
+
+SMALL16 = Workload("small-f16", LayerCfg(256, 4, 2, 64, 688), 5, 1024, 2, 64, "f16")
+
+
+def test_f16_loss_scaled_steps_match_oracle_and_overflow_skips_the_step():
+    """fp16 compute with dynamic loss scaling (scale 2^16, doubled after 2 good steps):
+    - steps 1 and 2: the loss matches the oracle at the fp16 rounding of the masters; every
+      landed gradient divided by the step's scale matches the oracle's gradient (fp16 bound);
+      masters and moments equal the fp32 AdamW contract of the landed (scaled) gradient with
+      that scale, bit for bit; every upload buffer and resident device copy holds the fp16
+      rounding of its master;
+    - step 3 at a scale of 2^40 overflows (the CE's dz alone exceeds fp16's range): the whole
+      step is skipped, so every master, moment, upload buffer and device copy keeps its bits,
+      the optimizer's step count stays, and the scale is halved;
+    - step 4 at 2^16 applies again, as the optimizer's third step."""
+    w = SMALL16
+    c = w.layer
+    hp = AdamW(lr=1e-2)
+    ohp = oa.AdamWHyper(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)
+    print(f"fp16 engine with loss scaling: {w.name}", flush=True)
+    params = model_params(w, seed=0, gain_std=0.1)
+    H, V, P = c.hidden, w.vocab, c.param_count()
+    sizes = dict(embed=V * H, w_final=H, lm_head=V * H, **{f"layer{i}": P
+                                                              for i in range(w.n_layers)})
+    landed = {}
+
+    def on_gradient(name, step, off, g):
+        blk = _block_of(name)
+        arr = landed.setdefault((step, blk), np.full(sizes[blk], np.nan, np.float32))
+        arr[off:off + g.numel()] = oa.f16_bits_to_f32(g.numpy().view(np.uint16))
+
+    p = dict(embed=params["embed"].f32.reshape(-1), w_final=params["w_final"].f32,
+             lm_head=params["lm_head"].f32.reshape(-1))
+    for i, flat in enumerate(_flat_layers(params, w)):
+        p[f"layer{i}"] = flat.astype(np.float32)
+    m = {k: np.zeros(v.size, np.float32) for k, v in p.items()}
+    vv = {k: np.zeros(v.size, np.float32) for k, v in p.items()}
+    sh = om.ModelShape(om.LayerShape(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn),
+                       w.n_layers, w.vocab)
+    eng = SlideEngine(_spec(w), w.batch, w.seq, n_slots=3, hp=hp, adam_threads=3, ce_chunk=256,
+                      on_gradient=on_gradient, loss_scale=2.0 ** 16, scale_growth_interval=2)
+    try:
+        eng.load_params(p["embed"], [p[f"layer{i}"] for i in range(w.n_layers)], p["w_final"],
+                        p["lm_head"])
+        prm_of = dict(embed=eng.embed, w_final=eng.final, lm_head=eng.lm,
+                      **{f"layer{i}": eng.layers[i] for i in range(w.n_layers)})
+
+        def state_bits():
+            out = {}
+            for blk, prm in prm_of.items():
+                out[blk] = (prm.master.numpy().copy(), prm.m.numpy().copy(),
+                            prm.v.numpy().copy(), prm.shared.numpy().copy(),
+                            prm.dev.view(torch.int16).cpu().numpy() if hasattr(prm, "dev")
+                            else None)
+            return out
+
+        def applied_step(step, seed):
+            scale = eng.loss_scale
+            tok = tokens(w.batch, w.seq, w.vocab, seed=seed)
+            eng.step(tok)
+            loss = eng.loss()
+            eng.wait_updates()
+            torch.cuda.synchronize()
+            cur = {k: oa.f16_bits_to_f32(oa.f16_round_bits(a)) for k, a in p.items()}
+            rloss, rg = om.model_loss_and_grads(_oracle_from_flat(cur, w), tok, sh)
+            print(f"  step {step} (scale {scale:g}): loss gpu {loss:.6f} oracle {rloss:.6f}",
+                  flush=True)
+            assert abs(loss - rloss) <= 2e-3 * abs(rloss)
+            rflat = dict(embed=rg["embed"].reshape(-1), w_final=rg["w_final"],
+                         lm_head=rg["lm_head"].reshape(-1))
+            for i, fl in enumerate(_flat_grads(rg, w)):
+                rflat[f"layer{i}"] = fl
+            got = eng.master_params()
+            got_flat = dict(embed=got["embed"], w_final=got["w_final"], lm_head=got["lm_head"],
+                            **{f"layer{i}": a for i, a in enumerate(got["layers"])})
+            t_adam = eng.opt_step
+            for blk in sizes:
+                g = landed.pop((eng.step_count, blk))
+                assert not np.isnan(g).any(), f"step {step} {blk}: a part never landed"
+                if blk.startswith("layer"):
+                    o = 0
+                    for n, shp in c.param_shapes():
+                        k = int(np.prod(shp))
+                        assert_close(g[o:o + k] / scale, rflat[blk][o:o + k], "f16",
+                                     f"step {step} {blk} landed grad / scale {n}")
+                        o += k
+                else:
+                    assert_close(g / scale, rflat[blk], "f16", f"step {step} {blk} landed grad")
+                pn, mn, vn, bits = oa.adamw_fp32(p[blk], g, m[blk], vv[blk], t_adam, ohp,
+                                                 grad_scale=scale, copy="f16")
+                prm = prm_of[blk]
+                assert np.array_equal(got_flat[blk].view(np.uint32), pn.view(np.uint32)), blk
+                assert np.array_equal(prm.m.numpy().view(np.uint32), mn.view(np.uint32)), blk
+                assert np.array_equal(prm.v.numpy().view(np.uint32), vn.view(np.uint32)), blk
+                assert np.array_equal(prm.shared.numpy().view(np.uint16), bits), blk
+                if hasattr(prm, "dev"):
+                    dbits = prm.dev.view(torch.int16).cpu().numpy().view(np.uint16)
+                    assert np.array_equal(dbits, bits), f"step {step} {blk}: device copy"
+                p[blk], m[blk], vv[blk] = pn, mn, vn
+
+        applied_step(1, 60)
+        assert eng.loss_scale == 2.0 ** 16 and eng.opt_step == 1
+        applied_step(2, 61)
+        assert eng.loss_scale == 2.0 ** 17 and eng.opt_step == 2 and eng.skipped_steps == 0
+        # step 3 overflows
+        before = state_bits()
+        eng.loss_scale = 2.0 ** 40
+        eng.step(tokens(w.batch, w.seq, w.vocab, seed=62))
+        eng.wait_updates()
+        torch.cuda.synchronize()
+        print(f"  step 3 (scale 2^40): skipped {eng.skipped_steps}, scale now "
+              f"{eng.loss_scale:g}", flush=True)
+        assert eng.skipped_steps == 1 and eng.loss_scale == 2.0 ** 39 and eng.opt_step == 2
+        after = state_bits()
+        for blk in before:
+            for a, b in zip(before[blk], after[blk]):
+                if a is not None:
+                    assert np.array_equal(a, b), f"step 3 changed {blk}"
+        assert not [k for k in landed if k[0] == 3], "a skipped step's gradient reached AdamW"
+        # step 4 applies again, as the optimizer's third step
+        eng.loss_scale = 2.0 ** 16
+        applied_step(4, 63)
+        assert eng.opt_step == 3 and eng.step_count == 4
+    finally:
+        eng.close()

@@ -223,9 +223,11 @@ def test_lmhead_ce_gradient_scale(dtype):
     if dtype == "bf16":
         assert np.array_equal(dh1, S * dh0) and np.array_equal(dw1, S * dw0)
     else:
-        e0 = rel_err(dw0, rdw)
-        e1 = rel_err(dw1 / S, rdw)
-        print(f"  fp16 dW rel err unscaled {e0:.3e}, scaled by {S:g} {e1:.3e}", flush=True)
+        # the largest errors sit in the target rows (dz near -1/N, normal range either way);
+        # the underflow shows in the many small entries, so compare root-mean-square errors
+        rms = lambda a: float(np.sqrt(np.mean((a - rdw) ** 2)) / np.sqrt(np.mean(rdw ** 2)))
+        e0, e1 = rms(dw0), rms(dw1 / S)
+        print(f"  fp16 dW rms rel err unscaled {e0:.3e}, scaled by {S:g} {e1:.3e}", flush=True)
         assert e1 < e0
     assert_close(dh1 / S, rdh, dtype, "ce dh / S")
     assert_close(dw1 / S, rdw, dtype, "ce dw / S")

@@ -197,3 +197,40 @@ def test_bf16_rounding_matches_torch():
     assert np.all(np.isnan(oa.bf16_bits_to_f32(nb))) and np.all(nb & 0x0040)
     assert np.array_equal(oa.bf16_bits_to_f32(ours[:5000]).view(np.uint32) & 0xFFFF,
                           np.zeros(5000, np.uint32))
+
+
+def test_f16_rounding_matches_ieee_cases_and_torch():
+    """binary16 round-to-nearest-even: hand-checked encodings (exact values, the halfway ties
+    around 1, the largest finite value and the first value that rounds to infinity, the
+    smallest subnormal), and agreement with torch's conversion over a wide sample."""
+    cases = {1.0: 0x3C00, -2.0: 0xC000, 65504.0: 0x7BFF, 65520.0: 0x7C00, 2.0 ** -24: 0x0001,
+             2.0 ** -14: 0x0400, 1.0 + 2.0 ** -11: 0x3C00, 1.0 + 3 * 2.0 ** -11: 0x3C02,
+             0.0: 0x0000, 1e-9: 0x0000}
+    for x, bits in cases.items():
+        assert int(oa.f16_round_bits(np.float32(x))) == bits, (x, hex(bits))
+    assert float(oa.f16_bits_to_f32(np.uint16(0x3555))) == 0.333251953125
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oa.f16_round_bits(x), ref)
+
+
+def test_adamw_loss_scaled_gradient_closed_form():
+    """A gradient computed at loss scale S is unscaled before the update: at t = 1 from m = v = 0
+    the step is p0 (1 - lr wd) - lr (g/S) / (|g/S| + eps), the same as the unscaled gradient's;
+    with S a power of two the fp32 contract gives the unscaled result bit for bit."""
+    hp = oa.AdamWHyper()
+    rng = np.random.default_rng(4)
+    p0 = rng.standard_normal(1000).astype(np.float32)
+    g = (rng.standard_normal(1000) * 1e-3).astype(np.float32)
+    S = 2.0 ** 16
+    z = np.zeros(1000, np.float32)
+    a = oa.adamw_fp32(p0, g, z, z, 1, hp)
+    b = oa.adamw_fp32(p0, g * np.float32(S), z, z, 1, hp, grad_scale=S)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    ref = p0.astype(np.float64) * (1 - hp.lr * hp.weight_decay) - hp.lr * g / (np.abs(g) + hp.eps)
+    assert np.max(np.abs(b[0] - ref)) <= 1e-6
+    # the 16-bit copy in fp16
+    assert np.array_equal(oa.adamw_fp32(p0, g, z, z, 1, hp, copy="f16")[3],
+                          oa.f16_round_bits(a[0]))
