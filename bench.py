@@ -162,6 +162,9 @@ def _parse():
                          "the last two steps, 10 ms per column)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (e.g. under a profiler)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="compute dtype of the step and layer-kernel workloads (f16: with dynamic "
+                         "loss scaling)")
     ap.add_argument("--embed-split", action="store_true",
                     help="update the embedding's rows that no token selects during the step and "
                          "only the selected rows after the backward")
@@ -212,16 +215,42 @@ def measured_traffic(kernel):
     return table.get(kernel)
 
 
+STEP_PROFILE = os.path.join(ROOT, "profiles", "llama3-8b-shaped_step_kernels.md")
+
+
+def profiled_figures(kernel):
+    """The committed rocprofv3 summaries' averages for `kernel` (ms): under kernel tracing in the
+    step (the runtime then copies gradients with blit kernels on the compute units) and alone on
+    the GPU (layer-kernels workload); None where a summary has no figure for it."""
+    out = {"step_profile_avg_ms": None, "layer_kernels_avg_ms": None}
+    if not os.path.exists(STEP_PROFILE):
+        return out
+    for line in open(STEP_PROFILE):
+        parts = line.split()
+        if len(parts) == 3 and parts[1] == kernel:
+            if parts[0] == "profiled_step_avg_ms":
+                out["step_profile_avg_ms"] = float(parts[2])
+            elif parts[0] == "layer_kernels_avg_ms":
+                out["layer_kernels_avg_ms"] = float(parts[2])
+    return out
+
+
 def _roofline(kernels, alg, traffic_ok=False):
     mfma_names = [n for n in kernels if n in alg]
     dom = max(mfma_names, key=lambda n: kernels[n]["total_ms"])
     dk = kernels[dom]
     achieved = alg[dom] / (dk["avg_ms"] * 1e-3) / 1e12
+    check = profiled_figures(dom)
+    for k in list(check):
+        if check[k] is not None:
+            check[k.replace("avg_ms", "frac")] = round(
+                alg[dom] / (check[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    check["source"] = os.path.relpath(STEP_PROFILE, ROOT)
     return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(dom) if traffic_ok else None,
-            "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom]}
+            "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom], "check": check}
 
 
 def _host_bytes_needed(w, args=None):
@@ -339,7 +368,7 @@ def run_step(w, args):
 
     c = w.layer
     spec = ModelSpec(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, w.vocab, w.n_layers,
-                     "bf16", c.rms_eps, c.rope_theta)
+                     args.dtype, c.rms_eps, c.rope_theta)
     cores = len(os.sched_getaffinity(0))
     threads = args.adam_threads or max(1, cores - 3)
     t_init = time.perf_counter()
@@ -415,13 +444,15 @@ def run_step(w, args):
         eng.export_trace(recs, args.trace + ".json")
         _write_text_timeline(eng, recs[-3:], args.trace + ".txt")
     tier = _tier_report(eng, tier0, args.steps, step_s) if eng.tier is not None else None
+    eng_scale, eng_skipped = eng.loss_scale, eng.skipped_steps
     eng.close()
     del eng
     import gc
     gc.collect()
     torch.cuda.empty_cache()
     print("[bench] resident (non-offloaded) baseline", file=sys.stderr, flush=True)
-    resident = run_resident(w, args)
+    resident = (run_resident(w, args) if args.dtype == "bf16" else
+                {"skipped": "the resident baseline runs the bf16 step"})
     if "tokens_per_s" in resident:
         resident["offloaded_fraction_of_resident"] = round(tok_s / resident["tokens_per_s"], 4)
     host = host_roofline(w, threads, step_s)
@@ -457,7 +488,7 @@ def run_step(w, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "hidden": c.hidden,
                    "heads": c.n_heads, "kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
@@ -498,6 +529,8 @@ def run_step(w, args):
         if ana["t_update_total_ms"] else None,
         "loss_last_step": round(loss, 4),
         "ms_per_step_steady": round(steady_ms, 2),
+        **({"loss_scaling": {"final_scale": eng_scale, "skipped_steps": eng_skipped}}
+           if args.dtype == "f16" else {}),
         "step_periods_ms": [round(float(x), 1) for x in periods],
         "first_step_ms": round((t_ret[0] - t0) * 1e3, 1) if t_ret else None,
         "drain_ms": round((t1 - t_ret[-1]) * 1e3, 1) if t_ret else None,
@@ -836,16 +869,17 @@ def run_layer_kernels(args):
     c, Bb, S = L8B.layer, L8B.batch, L8B.seq
     N = Bb * S
     dev = "cuda:0"
-    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, "bf16")
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, args.dtype)
+    tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
     P = sl.slide_layer_param_count(cfg)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
-    w = torch.empty(P, device=dev).normal_(0, 0.02, generator=gen).bfloat16()
+    w = torch.empty(P, device=dev).normal_(0, 0.02, generator=gen).to(tdt)
     offs = sl.slide_layer_param_offsets(cfg)
     w[offs[0]:offs[0] + c.hidden] = 1.0
     w[offs[3]:offs[3] + c.hidden] = 1.0
     g = torch.empty_like(w)
-    x = torch.empty(N, c.hidden, device=dev).normal_(0, 1, generator=gen).bfloat16()
+    x = torch.empty(N, c.hidden, device=dev).normal_(0, 1, generator=gen).to(tdt)
     dy = torch.empty_like(x).normal_(0, 1, generator=gen)
     y, dx = torch.empty_like(x), torch.empty_like(x)
     sb = sl.slide_layer_saved_bytes(cfg, Bb, S)
@@ -898,7 +932,7 @@ def run_layer_kernels(args):
         "metric": "one decoder layer fwd+bwd, kernels alone (1 GPU)",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": "layer-kernels-8b", "hidden": c.hidden, "heads": c.n_heads,
                    "kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "ffn": c.ffn,
