@@ -235,22 +235,32 @@ def profiled_figures(kernel):
     return out
 
 
-def _roofline(kernels, alg, traffic_ok=False):
+def _roofline(kernels, alg, profiled=False):
+    """Roofline of the dominant MFMA kernel. `profiled`: the launch is the one the committed
+    counter and trace summaries cover (the 8B-shaped layer at 8 x 1024 tokens in bf16), so
+    their HBM traffic and profiled averages apply; otherwise both are null."""
     mfma_names = [n for n in kernels if n in alg]
     dom = max(mfma_names, key=lambda n: kernels[n]["total_ms"])
     dk = kernels[dom]
     achieved = alg[dom] / (dk["avg_ms"] * 1e-3) / 1e12
-    check = profiled_figures(dom)
-    for k in list(check):
-        if check[k] is not None:
-            check[k.replace("avg_ms", "frac")] = round(
-                alg[dom] / (check[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-    check["source"] = os.path.relpath(STEP_PROFILE, ROOT)
+    check = None
+    if profiled:
+        check = profiled_figures(dom)
+        for k in list(check):
+            if check[k] is not None:
+                check[k.replace("avg_ms", "frac")] = round(
+                    alg[dom] / (check[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        check["source"] = os.path.relpath(STEP_PROFILE, ROOT)
     return {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(dom) if traffic_ok else None,
+            "traffic": measured_traffic(dom) if profiled else None,
             "avg_launch_ms": dk["avg_ms"], "flops_per_launch": alg[dom], "check": check}
+
+
+def _is_profiled_launch(layer, tokens, dtype):
+    from seeded_inputs import L8B
+    return layer == L8B.layer and tokens == 8 * 1024 and dtype == "bf16"
 
 
 def _host_bytes_needed(w, args=None):
@@ -281,7 +291,8 @@ def host_roofline(w, threads, step_s):
     DRAM (fp32 master, m, v read and written, the bf16 gradient read and the bf16 weight
     written), and the weight uploads and gradient flushes cross it once more. The peak is a
     STREAM triad (slide_host_triad) on the optimizer's threads over one layer's worth of
-    elements on huge pages; the bound is the step's host bytes (AdamW + copies) at that rate.
+    elements (at most 2^28 per array) on huge pages, the better of one run before and one after
+    the AdamW timing; the bound is the step's host bytes (AdamW + copies) at that rate.
     The AdamW's own rate alone on the same host is reported beside it (its fraction of the
     triad is the optimizer's efficiency)."""
     import layer_sliding_offloaded_fwd_amd as sl
@@ -289,7 +300,8 @@ def host_roofline(w, threads, step_s):
     import torch
     c = w.layer
     n = c.param_count()
-    triad_best, triad_med = sl.slide_host_triad(n, threads, 5)
+    n_triad = min(n, 1 << 28)       # 1 GiB per array, several times the last-level cache
+    triad_best, triad_med = sl.slide_host_triad(n_triad, threads, 5)
     p, m, v = _host_f32(n), _host_f32(n), _host_f32(n)
     for t in (p, m, v):
         t.fill_(0.0)                 # touch every page before timing
@@ -304,6 +316,11 @@ def host_roofline(w, threads, step_s):
         ts.append(time.perf_counter() - a)
     del p, m, v, g
     bw = 28 * n / min(ts[1:])        # best of the timed calls: the host's DRAM is shared
+    # a second triad after the AdamW; the peak is the better of the two (right after a large
+    # engine is torn down the kernel may still be reclaiming its pinned memory)
+    tb2, tm2 = sl.slide_host_triad(n_triad, threads, 5)
+    if tb2 > triad_best:
+        triad_best, triad_med = tb2, tm2
     adam_bytes, h2d, d2h = step_host_bytes(w)
     host_bytes = adam_bytes + h2d + d2h
     bound_s = host_bytes / (triad_best * 1e9)
@@ -538,7 +555,8 @@ def run_step(w, args):
         # the pages compare offloaded training with training whose state stays on the GPU:
         # measured on the same GPU with the same kernels (paper page abstract: over 95%)
         "resident": resident,
-        "roofline": _roofline(kernels, alg, traffic_ok=(w.name == "llama3-8b-shaped")),
+        "roofline": _roofline(kernels, alg, profiled=_is_profiled_launch(
+            w.layer, w.batch * w.seq, args.dtype)),
         **({"state_tier": tier} if tier is not None else {}),
         "kernels": kernels,
         "init_s": round(t_init, 1),
@@ -938,7 +956,8 @@ def run_layer_kernels(args):
                    "kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "ffn": c.ffn,
                    "global_batch": Bb, "seq_len": S},
         "layer_mfma_util_pct": round(100 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": _roofline(kernels, alg, traffic_ok=True), "kernels": kernels,
+        "roofline": _roofline(kernels, alg, profiled=_is_profiled_launch(c, Bb * S, args.dtype)),
+        "kernels": kernels,
         "copy_ref": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(copy_ms, 4),
                      "gbs_read_plus_write": round(copy_gbs, 1)},
     }

@@ -183,6 +183,16 @@ size_t slide_embed_bwd_workspace_bytes(int N, int V);
  * result is deterministic). dE [V, H] is fully overwritten (rows of absent tokens are 0). */
 int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,
                     int dtype, void* ws, size_t ws_bytes, void* stream);
+/* Row gather / scatter in device memory: row (dst_rows ? dst_rows[k] : k) of dst = row
+ * (src_rows ? src_rows[k] : k) of src for k < n_rows, rows of row_bytes (a positive multiple of
+ * 16; src and dst 16-byte aligned). src holds src_n_rows rows and dst dst_n_rows; a listed index
+ * outside them is skipped (it cannot be checked on the host: the lists are device memory), an
+ * implicit one outside them is SLIDE_E_SHAPE. Used to move only the embedding rows a batch
+ * selected between the device table and the host (summary, section 2A: transfers kept off the
+ * compute path; here the step boundary). */
+int slide_copy_rows(const void* src, const int32_t* src_rows, int64_t src_n_rows, void* dst,
+                    const int32_t* dst_rows, int64_t dst_n_rows, int64_t n_rows,
+                    size_t row_bytes, void* stream);
 /* y = RMSNorm(x; w). x, y [N, H]; rstd_out: optional fp32 [N] (may be NULL). */
 int slide_rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd_out, int N, int H,
                       float eps, int dtype, void* stream);
@@ -261,6 +271,25 @@ int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_stream, void*
  * bytes. *ticket identifies this flush for wait_flush. */
 int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
                           uint64_t* ticket);
+/* Part of a load or of a flush, so that a layer's copies, its CPU update and its upload can be
+ * pipelined in pieces (summary, section 2A: transfers and updates overlap one another; here the
+ * step boundary, where the last layer of the backward is the first of the next forward).
+ * load_range: copy weight bytes [offset, offset + nbytes) from host_w + offset (host_w is the
+ *   start of the layer's whole host buffer). *slot_inout < 0 starts a load on the next FREE
+ *   slot (FREE -> LOADING, the slot is written back); otherwise *slot_inout must be LOADING
+ *   with the same layer and the part is appended. The parts must cover the bytes the layer
+ *   needs before slide_slot_ring_acquire, which orders the compute stream after every part
+ *   issued so far (they run in order on the h2d stream).
+ * flush_range: after the work queued so far on compute_stream, copy gradient bytes
+ *   [offset, offset + nbytes) of the slot to host_g + offset; the slot must be IN_USE (the first
+ *   part: -> FLUSHING) or FLUSHING. Each part gets its own ticket; the slot's pending-flush
+ *   event is the last part's.
+ * Both: SLIDE_E_ARG if the bytes fall outside the slot's w_bytes / g_bytes or nbytes is 0,
+ * SLIDE_E_STATE for a slot in the wrong state (nothing is copied then). */
+int slide_slot_ring_load_range(slide_ring* r, int layer, const void* host_w, size_t offset,
+                               size_t nbytes, int* slot_inout);
+int slide_slot_ring_flush_range(slide_ring* r, int slot, void* host_g, size_t offset,
+                                size_t nbytes, void* compute_stream, uint64_t* ticket);
 /* Block until the flush named by ticket has landed in host memory; SLIDE_E_TIMEOUT after
  * timeout_ms milliseconds (a negative value waits without a limit). */
 int slide_slot_ring_wait_flush(slide_ring* r, uint64_t ticket, int timeout_ms);
@@ -324,6 +353,19 @@ int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float* m, float* 
                          uint16_t* p_bf16_out, size_t row_len, size_t n_rows_total,
                          const int32_t* rows, size_t n_rows, int64_t step,
                          const slide_adamw_hp* hp, int n_threads);
+/* slide_cpu_adamw on listed rows whose gradients arrive packed: row k of g_packed (n_rows rows
+ * of row_len elements, g_dtype) is the gradient of row rows[k] of p, m, v (n_rows_total rows;
+ * for an embedding, only the rows the batch selected leave the GPU). For a 16-bit g_dtype the
+ * new row's 16-bit copy (the gradient's type) is written to row rows[k] of out_full and to row
+ * k of out_packed (either may be NULL; out_packed may be g_packed itself, each row is consumed
+ * before it is overwritten), so the packed rows can go back to the device as they are. For
+ * SLIDE_F32 out_full must be NULL and out_packed receives the new fp32 rows. rows: distinct
+ * indices in [0, n_rows_total), else SLIDE_E_ARG. Same bits as slide_cpu_adamw_rows. */
+int slide_cpu_adamw_rows_packed(float* p, float* m, float* v, size_t row_len,
+                                size_t n_rows_total, const int32_t* rows, size_t n_rows,
+                                const void* g_packed, int g_dtype, void* out_full,
+                                void* out_packed, int64_t step, const slide_adamw_hp* hp,
+                                int n_threads);
 
 /* The same AdamW step on the GPU, for training whose optimizer state stays in HBM (the
  * non-offloaded baseline of the paper page's abstract, which compares the layer-sliding method

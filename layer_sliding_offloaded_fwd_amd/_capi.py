@@ -64,6 +64,7 @@ SIGNATURES = {
     "slide_embed_fwd": (I, [P, P, P, I, I, I, I, P]),
     "slide_embed_bwd_workspace_bytes": (SZ, [I, I]),
     "slide_embed_bwd": (I, [P, P, P, I, I, I, I, P, SZ, P]),
+    "slide_copy_rows": (I, [P, P, ctypes.c_int64, P, P, ctypes.c_int64, ctypes.c_int64, SZ, P]),
     "slide_rmsnorm_fwd": (I, [P, P, P, P, I, I, F, I, P]),
     "slide_rmsnorm_bwd_workspace_bytes": (SZ, [I, I]),
     "slide_rmsnorm_bwd": (I, [P, P, P, P, P, P, I, I, F, I, P, SZ, P]),
@@ -76,9 +77,11 @@ SIGNATURES = {
     "slide_rope": (I, [P, I, I, I, I, I, F, I, I, P, SZ, P]),
     "slide_slot_ring_create": (I, [ctypes.POINTER(P), I, SZ, SZ, P, P, P, I]),
     "slide_slot_ring_load": (I, [P, I, P, ctypes.POINTER(I)]),
+    "slide_slot_ring_load_range": (I, [P, I, P, SZ, SZ, ctypes.POINTER(I)]),
     "slide_slot_ring_reuse": (I, [P, I, ctypes.POINTER(I)]),
     "slide_slot_ring_acquire": (I, [P, I, P, ctypes.POINTER(P), ctypes.POINTER(P)]),
     "slide_slot_ring_flush": (I, [P, I, P, P, ctypes.POINTER(ctypes.c_uint64)]),
+    "slide_slot_ring_flush_range": (I, [P, I, P, SZ, SZ, P, ctypes.POINTER(ctypes.c_uint64)]),
     "slide_slot_ring_wait_flush": (I, [P, ctypes.c_uint64, I]),
     "slide_slot_ring_release": (I, [P, I, P]),
     "slide_slot_ring_state": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
@@ -88,6 +91,8 @@ SIGNATURES = {
     "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,
                                             ctypes.POINTER(AdamWHp)]),
+    "slide_cpu_adamw_rows_packed": (I, [P, P, P, SZ, SZ, P, SZ, P, I, P, P, ctypes.c_int64,
+                                        ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_rows": (I, [P, P, I, P, P, P, SZ, SZ, P, SZ, ctypes.c_int64,
                                  ctypes.POINTER(AdamWHp), I]),
     "slide_gpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), P]),

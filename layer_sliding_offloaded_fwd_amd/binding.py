@@ -23,7 +23,8 @@ __all__ = [
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
     "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
-    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows", "slide_gpu_adamw",
+    "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows",
+    "slide_cpu_adamw_rows_packed", "slide_copy_rows", "slide_gpu_adamw",
     "slide_cpu_convert_f32", "slide_host_triad", "StateTier",
     "slide_tier_region_bytes",
     "slide_nonfinite_count",
@@ -161,6 +162,13 @@ def slide_embed_bwd(dx, tokens, dE, N, H, V, dtype, ws, ws_bytes, stream=None):
          _s(stream))
 
 
+def slide_copy_rows(src, src_rows, src_n_rows, dst, dst_rows, dst_n_rows, n_rows, row_bytes,
+                    stream=None):
+    """Row gather / scatter on the device (src_rows / dst_rows: int32 device lists or None)."""
+    call("slide_copy_rows", _p(src), _p(src_rows), src_n_rows, _p(dst), _p(dst_rows),
+         dst_n_rows, n_rows, row_bytes, _s(stream))
+
+
 def slide_rmsnorm_fwd(x, w, y, rstd, N, H, eps, dtype, stream=None):
     call("slide_rmsnorm_fwd", _p(x), _p(w), _p(y), _p(rstd), N, H, ctypes.c_float(eps), dtype,
          _s(stream))
@@ -225,6 +233,14 @@ class SlotRing:
         call("slide_slot_ring_load", self._h, layer, _p(host_w), ctypes.byref(s))
         return s.value
 
+    def load_range(self, layer, host_w, offset, nbytes, slot=-1):
+        """Part [offset, offset + nbytes) of a layer's weights; slot -1 starts the load on the
+        next FREE slot, a slot number continues it. Returns the slot."""
+        s = ctypes.c_int(slot)
+        call("slide_slot_ring_load_range", self._h, layer, _p(host_w), offset, nbytes,
+             ctypes.byref(s))
+        return s.value
+
     def reuse(self, layer):
         s = ctypes.c_int()
         call("slide_slot_ring_reuse", self._h, layer, ctypes.byref(s))
@@ -241,6 +257,12 @@ class SlotRing:
         t = ctypes.c_uint64()
         call("slide_slot_ring_flush", self._h, slot, _p(host_g), _s(compute_stream),
              ctypes.byref(t))
+        return t.value
+
+    def flush_range(self, slot, host_g, offset, nbytes, compute_stream=None):
+        t = ctypes.c_uint64()
+        call("slide_slot_ring_flush_range", self._h, slot, _p(host_g), offset, nbytes,
+             _s(compute_stream), ctypes.byref(t))
         return t.value
 
     def wait_flush(self, ticket, timeout_ms=-1):
@@ -287,6 +309,14 @@ def slide_cpu_adamw_rows(p, g, g_dtype, m, v, p_bf16_out, row_len, n_rows_total,
     """Rows of row_len elements (int32 row indices); g None: zero gradient on those rows."""
     call("slide_cpu_adamw_rows", _p(p), _p(g), g_dtype, _p(m), _p(v), _p(p_bf16_out), row_len,
          n_rows_total, _p(rows), n_rows, step, ctypes.byref(hp), n_threads)
+
+
+def slide_cpu_adamw_rows_packed(p, m, v, row_len, n_rows_total, rows, n_rows, g_packed, g_dtype,
+                                out_full, out_packed, step, hp, n_threads=0):
+    """Rows rows[k] updated from packed gradient rows k; new rows to out_full / out_packed."""
+    call("slide_cpu_adamw_rows_packed", _p(p), _p(m), _p(v), row_len, n_rows_total, _p(rows),
+         n_rows, _p(g_packed), g_dtype, _p(out_full), _p(out_packed), step, ctypes.byref(hp),
+         n_threads)
 
 
 def slide_gpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, stream=None):

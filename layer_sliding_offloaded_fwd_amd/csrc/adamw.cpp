@@ -265,6 +265,76 @@ extern "C" int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float*
   return SLIDE_OK;
 }
 
+// Listed rows whose gradients arrive packed (row k of g_packed belongs to row rows[k]): each row
+// runs the element loop of slide_cpu_adamw with the new 16-bit copy written into out_full's
+// row, then that row is copied into out_packed's row k (which may be g_packed's, already
+// consumed). For fp32 gradients the new fp32 row itself is copied into out_packed.
+extern "C" int slide_cpu_adamw_rows_packed(float* p, float* m, float* v, size_t row_len,
+                                           size_t n_rows_total, const int32_t* rows,
+                                           size_t n_rows, const void* g_packed, int g_dtype,
+                                           void* out_full, void* out_packed, int64_t step,
+                                           const slide_adamw_hp* hp, int n_threads) {
+  using slide::fail;
+  if (n_rows == 0 || row_len == 0) return SLIDE_OK;
+  int rc = slide::adamw_check("slide_cpu_adamw_rows_packed", p, g_packed, g_dtype, m, v,
+                              nullptr, row_len * n_rows, step, hp);
+  if (rc != SLIDE_OK) return rc;
+  if (!rows) return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: null row list");
+  if (n_rows > n_rows_total)
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: %zu rows of %zu", n_rows,
+                n_rows_total);
+  const bool g16 = g_dtype != SLIDE_F32;
+  if (!g16 && out_full)
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: out_full needs a 16-bit gradient");
+  const size_t gsz = g16 ? 2 : 4;
+  if (out_packed && out_packed != g_packed) {
+    const char* a = (const char*)out_packed;
+    const char* b = (const char*)g_packed;
+    const size_t nb = n_rows * row_len * gsz;
+    if (a < b + nb && b < a + nb)
+      return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: out_packed partially overlaps g");
+  }
+  for (size_t k = 0; k < n_rows; ++k)
+    if (rows[k] < 0 || (size_t)rows[k] >= n_rows_total)
+      return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: row %d outside [0, %zu)", rows[k],
+                  n_rows_total);
+  const Consts c = make_consts(*hp, step);
+  const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+  auto work = [&](size_t k0, size_t k1) {
+    std::vector<uint16_t> tmp(g16 && !out_full ? row_len : 0);
+    for (size_t k = k0; k < k1; ++k) {
+      const size_t o = (size_t)rows[k] * row_len;
+      const void* gr = (const char*)g_packed + k * row_len * gsz;
+      uint16_t* o16 = nullptr;
+      if (g16) o16 = out_full ? (uint16_t*)out_full + o : tmp.data();
+      if (avx512) range_avx512(p + o, gr, g_dtype, m + o, v + o, o16, 0, row_len, c);
+      else range_scalar(p + o, gr, g_dtype, m + o, v + o, o16, 0, row_len, c);
+      if (out_packed) {
+        char* dst = (char*)out_packed + k * row_len * gsz;
+        if (g16) memcpy(dst, o16, row_len * 2);
+        else memcpy(dst, p + o, row_len * 4);
+      }
+    }
+  };
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::max<size_t>(1, std::min<size_t>((size_t)nt, (n_rows * row_len + 65535) / 65536));
+  nt = (int)std::min<size_t>((size_t)nt, n_rows);
+  if (nt == 1) {
+    work(0, n_rows);
+    return SLIDE_OK;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  const size_t per = (n_rows + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    const size_t k0 = (size_t)t * per, k1 = std::min(n_rows, k0 + per);
+    if (k0 >= k1) break;
+    th.emplace_back(work, k0, k1);
+  }
+  for (auto& x : th) x.join();
+  return SLIDE_OK;
+}
+
 // Scalar-only entry used by tests to check that both code paths agree bit for bit.
 extern "C" int slide_cpu_adamw_scalar_for_test(float* p, const void* g, int g_dtype, float* m,
                                                float* v, uint16_t* out, size_t n, int64_t step,

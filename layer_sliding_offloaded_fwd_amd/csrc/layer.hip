@@ -415,6 +415,23 @@ extern "C" int slide_embed_fwd(const void* E, const int32_t* tokens, void* x, in
   return embed_fwd(E, tokens, x, N, H, V, dtype, (hipStream_t)stream);
 }
 
+extern "C" int slide_copy_rows(const void* src, const int32_t* src_rows, int64_t src_n_rows,
+                               void* dst, const int32_t* dst_rows, int64_t dst_n_rows,
+                               int64_t n_rows, size_t row_bytes, void* stream) {
+  SLIDE_REQUIRE(n_rows >= 0 && n_rows < (1LL << 31) && src_n_rows >= 0 && dst_n_rows >= 0,
+                SLIDE_E_SHAPE, "copy_rows: bad row counts %lld %lld %lld", (long long)n_rows,
+                (long long)src_n_rows, (long long)dst_n_rows);
+  SLIDE_REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, SLIDE_E_SHAPE,
+                "copy_rows: row_bytes %zu is not a positive multiple of 16", row_bytes);
+  SLIDE_REQUIRE((src_rows || n_rows <= src_n_rows) && (dst_rows || n_rows <= dst_n_rows),
+                SLIDE_E_SHAPE, "copy_rows: %lld rows in order exceed a matrix", (long long)n_rows);
+  if (n_rows == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(src && dst && aligned16(src) && aligned16(dst), SLIDE_E_ARG,
+                "copy_rows: null or misaligned pointer");
+  return copy_rows(src, src_rows, src_n_rows, dst, dst_rows, dst_n_rows, n_rows, row_bytes,
+                   (hipStream_t)stream);
+}
+
 extern "C" size_t slide_embed_bwd_workspace_bytes(int N, int V) { return embed_bwd_ws(N < 0 ? 0 : N, V); }
 
 extern "C" int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,

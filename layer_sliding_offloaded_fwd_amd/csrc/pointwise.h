@@ -23,6 +23,12 @@ int swiglu_bwd(const void* dm, const void* gu, void* dgu, int N, int F, int dtyp
 int embed_fwd(const void* E, const int32_t* tok, void* x, int N, int H, int V, int dtype,
               hipStream_t st);
 size_t embed_bwd_ws(int N, int V);
+// dst row (dst_rows ? dst_rows[k] : k) = src row (src_rows ? src_rows[k] : k), k < n_rows;
+// rows of row_bytes (a multiple of 16); a pair with an index outside [0, src_n) or
+// [0, dst_n) is skipped
+int copy_rows(const void* src, const int32_t* src_rows, long long src_n, void* dst,
+              const int32_t* dst_rows, long long dst_n, long long n_rows, size_t row_bytes,
+              hipStream_t st);
 int embed_bwd(const void* dx, const int32_t* tok, void* dE, int N, int H, int V, int dtype,
               void* ws, hipStream_t st);
 // *count (device) = number of NaN or infinite elements of x[n]

@@ -491,6 +491,32 @@ int embed_fwd(const void* E, const int32_t* tok, void* x, int N, int H, int V, i
   return check_launch("embed_fwd");
 }
 
+// One workgroup per row pair, 16-byte accesses.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ src,
+                                                        const int32_t* __restrict__ src_rows,
+                                                        long long src_n, uint4* __restrict__ dst,
+                                                        const int32_t* __restrict__ dst_rows,
+                                                        long long dst_n, long long row_vec) {
+  const long long k = blockIdx.x;
+  const long long rs = src_rows ? (long long)src_rows[k] : k;
+  const long long rd = dst_rows ? (long long)dst_rows[k] : k;
+  if (rs < 0 || rs >= src_n || rd < 0 || rd >= dst_n) return;
+  const uint4* s = src + rs * row_vec;
+  uint4* d = dst + rd * row_vec;
+  for (long long i = threadIdx.x; i < row_vec; i += 256) d[i] = s[i];
+}
+
+int copy_rows(const void* src, const int32_t* src_rows, long long src_n, void* dst,
+              const int32_t* dst_rows, long long dst_n, long long n_rows, size_t row_bytes,
+              hipStream_t st) {
+  if (n_rows == 0) return SLIDE_OK;
+  ProfScope ps("copy_rows", st);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)n_rows), dim3(256), 0, st,
+                     (const uint4*)src, src_rows, src_n, (uint4*)dst, dst_rows, dst_n,
+                     (long long)(row_bytes / 16));
+  return check_launch("copy_rows");
+}
+
 static int pow2_at_least(int n) {
   int p = 1;
   while (p < n) p <<= 1;

@@ -237,22 +237,41 @@ extern "C" int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_by
   return SLIDE_OK;
 }
 
-extern "C" int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot_out) {
-  if (!r || !host_w || !slot_out) return fail(SLIDE_E_ARG, "slot ring load: null pointer");
+namespace {
+// Start (slot < 0: on the next FREE slot, which becomes LOADING) or continue (slot LOADING with
+// this layer) the copy of weight bytes [off, off + n) from host_w + off into the slot. The
+// slot's load event is re-recorded after every part; the copy stream runs the parts in order,
+// so the last event covers them all.
+int load_part(slide_ring* r, int layer, const void* host_w, size_t off, size_t n, int* slot_io,
+              const char* what) {
+  if (!r || !host_w || !slot_io) return fail(SLIDE_E_ARG, "slot ring %s: null pointer", what);
+  if (n == 0 || off > r->wb || n > r->wb - off)
+    return fail(SLIDE_E_ARG, "slot ring %s(layer %d): bytes [%zu, +%zu) outside the %zu-byte slot",
+                what, layer, off, n, r->wb);
   std::lock_guard<std::mutex> lk(r->mu);
-  int best = -1;
-  for (int s = 0; s < r->n; ++s)
-    if (r->slots[s].state == SLIDE_SLOT_FREE &&
-        (best < 0 || r->slots[s].released_at < r->slots[best].released_at))
-      best = s;
-  if (best < 0) return fail(SLIDE_E_STATE, "slot ring load(layer %d): no FREE slot", layer);
-  Slot& sl = r->slots[best];
+  int s = *slot_io;
+  const bool first = s < 0;
+  if (first) {
+    for (int k = 0; k < r->n; ++k)
+      if (r->slots[k].state == SLIDE_SLOT_FREE &&
+          (s < 0 || r->slots[k].released_at < r->slots[s].released_at))
+        s = k;
+    if (s < 0) return fail(SLIDE_E_STATE, "slot ring %s(layer %d): no FREE slot", what, layer);
+  } else {
+    if (s >= r->n) return fail(SLIDE_E_ARG, "slot ring %s: slot %d out of range", what, s);
+    if (r->slots[s].state != SLIDE_SLOT_LOADING || r->slots[s].layer != layer)
+      return fail(SLIDE_E_STATE, "slot ring %s: slot %d is not LOADING layer %d", what, s,
+                  layer);
+  }
+  Slot& sl = r->slots[s];
+  char* dst = r->w_ptr(s) + off;
+  const char* src = (const char*)host_w + off;
   if (r->engine == SLIDE_ENGINE_HOST) {
     HostCopyQueue::Job j;
-    if (sl.free_ev.valid) j.waits.push_back(sl.free_ev.host);
-    j.dst = r->w_ptr(best);
-    j.src = host_w;
-    j.n = r->wb;
+    if (first && sl.free_ev.valid) j.waits.push_back(sl.free_ev.host);
+    j.dst = dst;
+    j.src = src;
+    j.n = n;
     j.done = std::make_shared<HostEvent>();
     j.done->st.store(0);
     j.fault = r->take_fault();
@@ -260,23 +279,39 @@ extern "C" int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w
     sl.load_ev.valid = true;
     r->hq_h2d->push(std::move(j));
   } else {
-    if (sl.free_ev.valid && hipStreamWaitEvent(r->h2d, sl.free_ev.hip, 0) != hipSuccess)
-      return fail(SLIDE_E_HIP, "slot ring load: hipStreamWaitEvent failed");
-    hipError_t e = hipMemcpyAsync(r->w_ptr(best), host_w, r->wb, hipMemcpyHostToDevice, r->h2d);
+    if (first && sl.free_ev.valid && hipStreamWaitEvent(r->h2d, sl.free_ev.hip, 0) != hipSuccess)
+      return fail(SLIDE_E_HIP, "slot ring %s: hipStreamWaitEvent failed", what);
+    hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, r->h2d);
     if (e != hipSuccess)
-      return fail(SLIDE_E_HIP, "slot ring load: hipMemcpyAsync: %s", hipGetErrorString(e));
+      return fail(SLIDE_E_HIP, "slot ring %s: hipMemcpyAsync: %s", what, hipGetErrorString(e));
     if (!sl.load_ev.hip &&
         hipEventCreateWithFlags(&sl.load_ev.hip, hipEventDisableTiming) != hipSuccess)
-      return fail(SLIDE_E_HIP, "slot ring load: hipEventCreate failed");
+      return fail(SLIDE_E_HIP, "slot ring %s: hipEventCreate failed", what);
     if (hipEventRecord(sl.load_ev.hip, r->h2d) != hipSuccess)
-      return fail(SLIDE_E_HIP, "slot ring load: hipEventRecord failed");
+      return fail(SLIDE_E_HIP, "slot ring %s: hipEventRecord failed", what);
     sl.load_ev.valid = true;
   }
-  sl.state = SLIDE_SLOT_LOADING;
-  sl.layer = layer;
-  sl.content_valid = true;
-  *slot_out = best;
+  if (first) {
+    sl.state = SLIDE_SLOT_LOADING;
+    sl.layer = layer;
+    sl.content_valid = true;
+  }
+  *slot_io = s;
   return SLIDE_OK;
+}
+}  // namespace
+
+extern "C" int slide_slot_ring_load(slide_ring* r, int layer, const void* host_w, int* slot_out) {
+  if (!slot_out) return fail(SLIDE_E_ARG, "slot ring load: null pointer");
+  int s = -1;
+  int rc = load_part(r, layer, host_w, 0, r ? r->wb : 0, &s, "load");
+  if (rc == SLIDE_OK) *slot_out = s;
+  return rc;
+}
+
+extern "C" int slide_slot_ring_load_range(slide_ring* r, int layer, const void* host_w,
+                                          size_t offset, size_t nbytes, int* slot_inout) {
+  return load_part(r, layer, host_w, offset, nbytes, slot_inout, "load_range");
 }
 
 // Re-claim a FREE slot whose weights still hold `layer` (nothing was loaded over them since),
@@ -326,24 +361,33 @@ extern "C" int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_st
   return SLIDE_OK;
 }
 
-extern "C" int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
-                                     uint64_t* ticket) {
+namespace {
+// After the work queued so far on compute_stream: copy gradient bytes [off, off + n) of the
+// slot to host_g + off on the d2h stream. The first part takes the slot from IN_USE to
+// FLUSHING; further parts of the same flush are accepted while it is FLUSHING.
+int flush_part(slide_ring* r, int slot, void* host_g, size_t off, size_t n,
+               void* compute_stream, uint64_t* ticket, const char* what) {
   int rc = check_ring(r, slot);
   if (rc) return rc;
-  if (!host_g || !ticket) return fail(SLIDE_E_ARG, "slot ring flush: null pointer");
+  if (!host_g || !ticket) return fail(SLIDE_E_ARG, "slot ring %s: null pointer", what);
   std::lock_guard<std::mutex> lk(r->mu);
   Slot& sl = r->slots[slot];
-  if (r->gb == 0) return fail(SLIDE_E_STATE, "slot ring flush: ring has no gradient region");
-  if (sl.state != SLIDE_SLOT_IN_USE)
-    return fail(SLIDE_E_STATE, "slot ring flush: slot %d is %s, expected IN_USE", slot,
-                state_name(sl.state));
+  if (r->gb == 0) return fail(SLIDE_E_STATE, "slot ring %s: ring has no gradient region", what);
+  if (n == 0 || off > r->gb || n > r->gb - off)
+    return fail(SLIDE_E_ARG, "slot ring %s: bytes [%zu, +%zu) outside the %zu-byte gradient",
+                what, off, n, r->gb);
+  if (sl.state != SLIDE_SLOT_IN_USE && sl.state != SLIDE_SLOT_FLUSHING)
+    return fail(SLIDE_E_STATE, "slot ring %s: slot %d is %s, expected IN_USE or FLUSHING",
+                what, slot, state_name(sl.state));
   uint64_t t = r->next_ticket++;
   Ev& te = r->ticket_ev[t % kTicketPool];
+  char* dst = (char*)host_g + off;
+  const char* src = r->g_ptr(slot) + off;
   if (r->engine == SLIDE_ENGINE_HOST) {
     HostCopyQueue::Job j;
-    j.dst = host_g;
-    j.src = r->g_ptr(slot);
-    j.n = r->gb;
+    j.dst = dst;
+    j.src = src;
+    j.n = n;
     j.done = std::make_shared<HostEvent>();
     j.done->st.store(0);
     j.fault = r->take_fault();
@@ -354,13 +398,12 @@ extern "C" int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void
     Ev cdone;
     if ((rc = r->record_compute(cdone, compute_stream))) return rc;
     hipError_t e = hipStreamWaitEvent(r->d2h, cdone.hip, 0);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(host_g, r->g_ptr(slot), r->gb, hipMemcpyDeviceToHost, r->d2h);
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToHost, r->d2h);
     if (e == hipSuccess && !te.hip)
       e = hipEventCreateWithFlags(&te.hip, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventRecord(te.hip, r->d2h);
     hipEventDestroy(cdone.hip);  // destruction is deferred by HIP until the event completes
-    if (e != hipSuccess) return fail(SLIDE_E_HIP, "slot ring flush: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(SLIDE_E_HIP, "slot ring %s: %s", what, hipGetErrorString(e));
     te.valid = true;
   }
   r->ticket_id[t % kTicketPool] = t;
@@ -368,6 +411,24 @@ extern "C" int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void
   sl.state = SLIDE_SLOT_FLUSHING;
   *ticket = t;
   return SLIDE_OK;
+}
+}  // namespace
+
+extern "C" int slide_slot_ring_flush(slide_ring* r, int slot, void* host_g, void* compute_stream,
+                                     uint64_t* ticket) {
+  if (r && slot >= 0 && slot < r->n) {
+    std::lock_guard<std::mutex> lk(r->mu);
+    if (r->slots[slot].state != SLIDE_SLOT_IN_USE)
+      return fail(SLIDE_E_STATE, "slot ring flush: slot %d is %s, expected IN_USE", slot,
+                  state_name(r->slots[slot].state));
+  }
+  return flush_part(r, slot, host_g, 0, r ? r->gb : 0, compute_stream, ticket, "flush");
+}
+
+extern "C" int slide_slot_ring_flush_range(slide_ring* r, int slot, void* host_g, size_t offset,
+                                           size_t nbytes, void* compute_stream,
+                                           uint64_t* ticket) {
+  return flush_part(r, slot, host_g, offset, nbytes, compute_stream, ticket, "flush_range");
 }
 
 extern "C" int slide_slot_ring_wait_flush(slide_ring* r, uint64_t ticket, int timeout_ms) {

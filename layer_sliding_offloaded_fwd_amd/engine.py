@@ -79,7 +79,7 @@ def pinned_bytes(n, esize, min_bytes=0):
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
                  "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off",
-                 "rows", "row_len", "adam_t", "hp", "cancelled")
+                 "rows", "row_len", "adam_t", "hp", "cancelled", "packed")
 
     def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None,
                  off=0, rows=None, row_len=0):
@@ -88,6 +88,9 @@ class _Job:
         # rows: update only these rows of row_len elements (int32 indices into p, m, v, out,
         # which then hold n // row_len rows); g None: their gradient is exactly zero
         self.rows, self.row_len = rows, row_len
+        # packed: g holds only the listed rows (row k for rows[k]); the new rows' upload copy
+        # is written over g (and into out, the whole table's upload buffer, for 16-bit)
+        self.packed = False
         self.adam_t = step     # AdamW's step count (bias correction); the engine sets it
         self.hp = None         # per-job hyper-parameters (loss-scaled gradients), else the engine's
         self.cancelled = False  # the step was skipped (fp16 overflow): apply nothing
@@ -175,6 +178,7 @@ class _Param:
         self.m = _host_f32(n) if tier is None else None
         self.v = _host_f32(n) if tier is None else None
         self.job = None
+        self.part_jobs = None   # the last update, when it ran in parts (layer 0)
         if resident:
             tdt = _DTYPES[dtype][1]
             self.dev = torch.empty(n, dtype=tdt, device=device)
@@ -189,7 +193,7 @@ class SlideEngine:
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
                  tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False,
                  keep_records=64, on_gradient=None, embed_split=False, loss_scale=2.0 ** 16,
-                 scale_growth_interval=2000, min_loss_scale=1.0):
+                 scale_growth_interval=2000, min_loss_scale=1.0, boundary_parts=8):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -219,12 +223,19 @@ class SlideEngine:
         embed_split: update the embedding's rows that no input token selects (an exactly zero
           gradient) while the step runs, and only the selected rows after the backward (False:
           the whole embedding after the backward, chunk by chunk). Same results either way.
+        boundary_parts: layer 0, the last layer of the backward and the first the next forward
+          needs, is flushed, updated and uploaded in this many parts (byte ranges of its slot),
+          so that its gradient copy, its CPU update and its upload overlap one another at the
+          step boundary instead of running back to back; 1 moves it whole. (Not for a layer 0
+          whose optimizer state is in the disk tier.)
         on_gradient: optional callable(name, step, offset, grad) run on the CPU worker once a
           gradient has landed in host memory and before the update that consumes it (for bf16
           compute the update overwrites the gradient with the new weights). name is the block
           ("layer3", "embed2", "lm_head0", "w_final"), offset the element offset of this part
-          within its block, grad the host tensor (bf16 bits as int16, or fp32). For gradient
-          statistics and inspection; it must not modify grad.
+          within its block (with embed_split, an embedding part holds only selected rows:
+          offset is then the int32 array of their row numbers, grad their rows in that order),
+          grad the host tensor (bf16 bits as int16, or fp32). For gradient statistics and
+          inspection; it must not modify grad.
         """
         assert spec.dtype in _DTYPES, spec.dtype
         self.fp16 = spec.dtype == "f16"
@@ -290,9 +301,13 @@ class SlideEngine:
                     offs, o = (None, o, o + reg), o + 2 * reg
             self.layers.append(_Param(self.P, s.dtype, self.pinned, tier=offs,
                                       copy_bytes=self.w_bytes))
+        # layer 0 in parts at the step boundary: element ranges starting on 256-byte boundaries
+        self.l0_parts = None
+        if boundary_parts > 1 and 0 not in tiered:
+            step_el = _align(-(-self.P * self.ts // boundary_parts)) // self.ts
+            self.l0_parts = [(a, min(a + step_el, self.P)) for a in range(0, self.P, step_el)]
         self.embed_split = embed_split
-        self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True,
-                            separate_grad=embed_split)
+        self.embed = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         self.final = _Param(H, s.dtype, self.pinned, self.device, resident=True)
         self.lm = _Param(V * H, s.dtype, self.pinned, self.device, resident=True)
         # The LM head is updated, uploaded and flushed per vocabulary chunk of the fused CE, so
@@ -321,6 +336,19 @@ class SlideEngine:
         # are updated, chunk by chunk.
         self.emb_zero_job = None
         self.emb_present = None
+        # With the split, only the selected rows cross the link at the step boundary: their
+        # gradient rows are packed on the device, copied out, updated and copied back packed,
+        # then scattered into the table; the rest of the table goes up after its zero-gradient
+        # update, during the step.
+        self.emb_scatter_n = 0          # selected rows whose new values wait to be scattered
+        self.emb_zero_up_ev = None      # upload of the table after the zero-row update
+        if embed_split:
+            R = min(N, V)
+            self.emb_rows_host = self.pinned.tensor(R, torch.int32)
+            self.emb_rows_dev = torch.empty(R, dtype=torch.int32, device=self.device)
+            self.emb_gc_dev = torch.empty(R * H, dtype=self.tdt, device=self.device)
+            self.emb_gc_host = self.pinned.tensor(
+                R * H, torch.int16 if s.dtype != "f32" else torch.float32)
 
         # device memory, allocated once
         dev = self.device
@@ -558,7 +586,10 @@ class SlideEngine:
         self.lm_job = [None] * self.lm_nch
         self.emb_ready = [self.embed.ready_ev] * self.emb_nch
         self.emb_job = [None] * self.emb_nch
+        self.emb_flushed = [None] * self.emb_nch
         self.emb_zero_job = None
+        self.emb_scatter_n = 0
+        self.emb_zero_up_ev = None
         torch.cuda.synchronize(self.device)
 
     def _upload_resident(self, prm):
@@ -633,10 +664,16 @@ class SlideEngine:
                                 f"{job.name}: {bad} NaN or infinite gradient elements in step "
                                 f"{job.step}; its update was not applied")
                     if self.on_gradient is not None and job.g is not None:
-                        self.on_gradient(job.name, job.step, job.off, job.g)
+                        self.on_gradient(job.name, job.step,
+                                         job.rows if job.packed else job.off, job.g)
                     job.t_ready = time.perf_counter()
                     hp = job.hp if job.hp is not None else self.hp
-                    if job.rows is not None:
+                    if job.packed:
+                        B.slide_cpu_adamw_rows_packed(
+                            job.p, job.m, job.v, job.row_len, job.n // job.row_len, job.rows,
+                            len(job.rows), job.g, self.code, job.out, job.g, job.adam_t, hp,
+                            self.adam_threads)
+                    elif job.rows is not None:
                         if len(job.rows):
                             B.slide_cpu_adamw_rows(job.p, job.g, self.code, job.m, job.v,
                                                    job.out, job.row_len, job.n // job.row_len,
@@ -663,8 +700,21 @@ class SlideEngine:
         job = _Job(name, wait, prm.master, prm.grad_host, prm.m, prm.v, out, prm.n,
                    self.step_count, priority, post, prm.tier)
         self._nf_attach(job)
-        prm.job = job
+        prm.job, prm.part_jobs = job, None
         return self._enqueue(job)
+
+    def _submit_parts(self, prm, tickets, name, priority):
+        """The update of a layer flushed in parts (l0_parts): one job per part, each waiting for
+        its own gradient copy; the parts' uploads follow as each job finishes."""
+        jobs = []
+        for (a, b), t in zip(self.l0_parts, tickets):
+            out = prm.shared[a:b] if prm.dtype != "f32" else None
+            job = _Job(name, t, prm.master[a:b], prm.grad_host[a:b], prm.m[a:b], prm.v[a:b],
+                       out, b - a, self.step_count, priority, off=a)
+            self._nf_attach(job)
+            jobs.append(self._enqueue(job))
+        prm.job, prm.part_jobs = None, jobs
+        return jobs
 
     # ------------------------------------------------------------------ non-finite check
     def _nf_count(self, grad, n, name):
@@ -703,6 +753,8 @@ class SlideEngine:
 
     def _wait_param(self, prm):
         self._wait_job(prm.job)
+        for j in prm.part_jobs or ():
+            self._wait_job(j)
 
     def _wait_job(self, job):
         if job is not None:
@@ -718,6 +770,7 @@ class SlideEngine:
         for ci in range(self.emb_nch):
             self._wait_job(self.emb_job[ci])
         self._wait_job(self.emb_zero_job)
+        self._embed_catch_up()           # the device table holds the updated rows too
 
     def close(self):
         """Wait for the pending updates and free every resource. A worker error is raised after
@@ -863,25 +916,103 @@ class SlideEngine:
         rows = np.flatnonzero(zero).astype(np.int32)
         prm = self.embed
         out = prm.shared if prm.dtype != "f32" else None
+        ev_g = torch.cuda.Event()
+        ev_g.record(self.compute)        # the gather that reads the current table
+
+        def upload():
+            # the whole table goes up (its selected rows still hold the values the device
+            # has; their new values are scattered over them before the next gather)
+            self.h2d.wait_event(ev_g)
+            with torch.cuda.stream(self.h2d):
+                src = prm.shared.view(self.tdt) if prm.dtype != "f32" else prm.shared
+                prm.dev.copy_(src, non_blocking=True)
+                ev = torch.cuda.Event()
+                ev.record(self.h2d)
+            self.emb_zero_up_ev = ev
         job = _Job("embed_zero", None, prm.master, None, prm.m, prm.v, out, V * H,
-                   self.step_count, -2, rows=rows, row_len=H)
+                   self.step_count, -2, post=upload, rows=rows, row_len=H)
         rec["other_jobs"].append(job)
         self.emb_zero_job = job
         self._enqueue(job)
 
+    def _embed_catch_up(self):
+        """Order the compute stream after the embedding's last updates and uploads (its chunks
+        or packed parts, and with embed_split the table after its zero-row update), and
+        scatter the packed rows into the table: from here the device table is current. The
+        updates themselves must be done (their jobs issue the uploads)."""
+        c, H, V = self.compute, self.spec.hidden, self.spec.vocab
+        for ci in range(self.emb_nch):
+            if self.emb_ready[ci] is not None:
+                c.wait_event(self.emb_ready[ci])
+            if self.emb_flushed[ci] is not None:
+                c.wait_event(self.emb_flushed[ci])
+        self._wait_job(self.emb_zero_job)
+        if self.emb_zero_up_ev is not None:
+            c.wait_event(self.emb_zero_up_ev)
+            self.emb_zero_up_ev = None
+        if self.emb_scatter_n:
+            n = self.emb_scatter_n
+            B.slide_copy_rows(self.emb_gc_dev, None, n, self.embed.dev, self.emb_rows_dev, V, n,
+                              H * self.ts, c)
+            self.emb_scatter_n = 0
+
+    def _flush_embed_packed(self, rec):
+        """embed_split: the selected rows' gradient, packed on the device, leaves in parts; each
+        part is updated (priorities -1 .. -1/n, before every layer) and its new rows go back
+        packed; the next forward scatters them into the table before its gather."""
+        prm, H, V = self.embed, self.spec.hidden, self.spec.vocab
+        pres = self.emb_present
+        n = len(pres)
+        c = self.compute
+        B.slide_copy_rows(prm.grad, self.emb_rows_dev, V, self.emb_gc_dev, None, n, n,
+                          H * self.ts, c)
+        nch = self.emb_nch
+        per = -(-n // nch) if n else 0
+        for ci in range(nch):
+            k0, k1 = min(ci * per, n), min((ci + 1) * per, n)
+            self.emb_job[ci] = self.emb_ready[ci] = self.emb_flushed[ci] = None
+            if k0 >= k1:
+                continue
+            sl = slice(k0 * H, k1 * H)
+            self._nf_count(self.emb_gc_dev[sl], (k1 - k0) * H, f"embed{ci}")
+            ev_c = torch.cuda.Event()
+            ev_c.record(c)
+            self.d2h.wait_event(ev_c)
+            gh = self.emb_gc_host[sl]
+            with torch.cuda.stream(self.d2h):
+                self._nf_fetch(f"embed{ci}")
+                (gh.view(self.tdt) if prm.dtype != "f32" else gh).copy_(self.emb_gc_dev[sl],
+                                                                       non_blocking=True)
+                done = torch.cuda.Event()
+                done.record(self.d2h)
+
+            def upload(ci=ci, sl=sl, gh=gh):
+                with torch.cuda.stream(self.h2d):
+                    self.emb_gc_dev[sl].copy_(gh.view(self.tdt) if prm.dtype != "f32" else gh,
+                                              non_blocking=True)
+                    ev = torch.cuda.Event()
+                    ev.record(self.h2d)
+                self.emb_ready[ci] = ev
+            out = prm.shared if prm.dtype != "f32" else None
+            job = _Job(f"embed{ci}", done, prm.master, gh, prm.m, prm.v, out, V * H,
+                       self.step_count, -1 + ci / nch, post=upload, rows=pres[k0:k1],
+                       row_len=H)
+            job.packed = True
+            self._nf_attach(job)
+            rec["other_jobs"].append(job)
+            self.emb_flushed[ci] = done
+            self.emb_job[ci] = job
+            self._enqueue(job)
+        self.emb_scatter_n = n
+
     def _flush_embed(self, rec):
-        """The embedding's gradient in row chunks, each flushed, updated on the rows that this
-        step's tokens selected (before every layer: priorities -1 .. -1/n; the other rows were
-        updated during the step) and uploaded on its own."""
+        """The embedding's gradient in row chunks, each flushed, updated (before every layer:
+        priorities -1 .. -1/n) and uploaded on its own."""
         for ci, (r0, r1) in enumerate(self.emb_rows):
             def ready(ev, ci=ci):
                 self.emb_ready[ci] = ev
-            sel = None
-            if self.embed_split:
-                pr = self.emb_present
-                sel = (pr[(pr >= r0) & (pr < r1)] - r0).astype(np.int32)
             job, done = self._flush_chunk(self.embed, r0, r1, f"embed{ci}",
-                                          -1 + ci / self.emb_nch, rec, ready, rows=sel)
+                                          -1 + ci / self.emb_nch, rec, ready)
             self.emb_flushed[ci] = done
             self.emb_job[ci] = job
             self._enqueue(job)
@@ -912,16 +1043,39 @@ class SlideEngine:
         slots = {}
         nxt = [0]
         free = [self.n_slots]
+        part = dict(slot=-1, k=0)   # progress of a layer uploaded in parts
+
+        def load_parts(j, prm, need):
+            """Upload the parts of layer j whose updates are done, in order; True once all
+            are on their way."""
+            jobs = prm.part_jobs
+            while part["k"] < len(jobs):
+                k = part["k"]
+                if not jobs[k].done.is_set():
+                    if need != j:
+                        return False
+                    self._wait_job(jobs[k])
+                a, b = self.l0_parts[k]
+                part["slot"] = self.ring.load_range(j, prm.shared, a * self.ts, (b - a) * self.ts,
+                                                    part["slot"])
+                part["k"] += 1
+            return True
 
         def prefetch(need=None):
             while nxt[0] < L and free[0] > 0:
                 j = nxt[0]
-                job = self.layers[j].job
-                if job is not None and not job.done.is_set():
-                    if need != j:
+                prm = self.layers[j]
+                if prm.part_jobs:
+                    if not load_parts(j, prm, need):
                         return
-                    self._wait_param(self.layers[j])
-                slots[j] = self.ring.load(j, self.layers[j].shared)
+                    slots[j] = part["slot"]
+                else:
+                    job = prm.job
+                    if job is not None and not job.done.is_set():
+                        if need != j:
+                            return
+                        self._wait_param(prm)
+                    slots[j] = self.ring.load(j, prm.shared)
                 nxt[0] += 1
                 free[0] -= 1
 
@@ -931,13 +1085,15 @@ class SlideEngine:
         for ci in range(self.emb_nch):
             self._wait_job(self.emb_job[ci])
             prefetch()
-        for ci in range(self.emb_nch):
-            c.wait_event(self.emb_ready[ci])
-            if self.emb_flushed[ci] is not None:
-                c.wait_event(self.emb_flushed[ci])
+        self._embed_catch_up()
         B.slide_embed_fwd(self.embed.dev, self.tok_in, self._x(0), N, H, V, self.code, c)
         if self.embed_split:
-            self.emb_present = np.unique(np.asarray(tok[:, :-1])).astype(np.int32)
+            pres = np.unique(np.asarray(tok[:, :-1])).astype(np.int32)
+            self.emb_present = pres
+            self.emb_rows_host[:len(pres)].copy_(torch.from_numpy(pres))
+            with torch.cuda.stream(c):
+                self.emb_rows_dev[:len(pres)].copy_(self.emb_rows_host[:len(pres)],
+                                                    non_blocking=True)
             self._update_embed_zero_rows(rec)
         for i in range(L):
             if i not in slots:
@@ -1024,11 +1180,19 @@ class SlideEngine:
                 self.d2h.wait_event(self._ev(c))
                 with torch.cuda.stream(self.d2h):
                     self._nf_fetch(f"layer{i}")
-            ticket = self.ring.flush(s, self.layers[i].grad_host, c)
+            if i == 0 and self.l0_parts is not None:
+                gh = self.layers[0].grad_host
+                tickets = [self.ring.flush_range(s, gh, a * self.ts, (b - a) * self.ts, c)
+                           for a, b in self.l0_parts]
+            else:
+                ticket = self.ring.flush(s, self.layers[i].grad_host, c)
             if self.timeline:
                 rec["layers"].setdefault(i, {})["bwd"] = (e_a, e_b)
                 rec["layers"][i]["d2h_end"] = self._ev(self.d2h)
-            rec["jobs"].append(self._submit(self.layers[i], ticket, f"layer{i}", i))
+            if i == 0 and self.l0_parts is not None:
+                rec["jobs"].extend(self._submit_parts(self.layers[0], tickets, "layer0", 0))
+            else:
+                rec["jobs"].append(self._submit(self.layers[i], ticket, f"layer{i}", i))
             self.ring.release(s, c)
             self._sync()
             j = i - self.n_slots
@@ -1038,7 +1202,10 @@ class SlideEngine:
         # ---- embedding gradient
         B.slide_embed_bwd(self.grad_x, self.tok_in, self.embed.grad, N, H, V, self.code,
                           self.ws, self.ws_bytes, c)
-        self._flush_embed(rec)
+        if self.embed_split:
+            self._flush_embed_packed(rec)
+        else:
+            self._flush_embed(rec)
         # the host sleeps until the GPU is done (a blocking event), leaving every core to the
         # CPU optimizer instead of spinning on one
         e_end = torch.cuda.Event(enable_timing=True, blocking=True)
@@ -1077,6 +1244,7 @@ class SlideEngine:
             return
         for j in jobs:
             j.done.wait()
+        self.emb_scatter_n = 0           # the device still holds every current row
         self.d2h.synchronize()           # every gradient copy has landed
         for prm in self.layers + [self.embed, self.final, self.lm]:
             self._refresh_shared(prm)
@@ -1197,7 +1365,9 @@ class SlideEngine:
                         gpu_iv.append((to_host(lr[key][0]), to_host(lr[key][1])))
             for a, b in rec.get("ce_iv", []):
                 gpu_iv.append((to_host(a), to_host(b)))
-            jobs = {j.name: j for j in rec["jobs"]}
+            jobs = {}
+            for j in rec["jobs"]:
+                jobs.setdefault(j.name, []).append(j)
             prev_end = -1e30
             for i in range(L - 1, -1, -1):
                 lr = rec["layers"][i]
@@ -1205,15 +1375,15 @@ class SlideEngine:
                 d_end = to_host(lr["d2h_end"])
                 d_start = max(be, prev_end)   # the copy starts after its backward and the
                 prev_end = d_end              # previous copy on the D2H stream
-                j = jobs[f"layer{i}"]
+                parts = jobs[f"layer{i}"]
                 work_iv.append((d_start, d_end))
-                work_iv.append((j.t_start, j.t_end))
+                work_iv.extend((j.t_start, j.t_end) for j in parts)
                 fw = lr.get("fwd")
                 t_fwd = fw[0].elapsed_time(fw[1]) if fw is not None else None
                 per_layer.append(dict(step=rec["step"], layer=i, t_fwd_ms=t_fwd,
                                       t_bwd_ms=(be - bs) * 1e3,
                                       t_d2h_ms=max(0.0, d_end - d_start) * 1e3,
-                                      t_update_ms=(j.t_end - j.t_start) * 1e3))
+                                      t_update_ms=sum(j.t_end - j.t_start for j in parts) * 1e3))
         # merge GPU intervals
         gpu_iv.sort()
         merged = []

@@ -265,6 +265,76 @@ def test_cpu_adamw_rows_bit_exact_vs_oracle(gdt, zero_grad):
                                 np.array([R], np.int32), 1, 1, CHP)
 
 
+@pytest.mark.parametrize("gdt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_cpu_adamw_rows_packed_bit_exact_vs_oracle(gdt, in_place):
+    """Packed gradient rows (row k for row rows[k], rows in any order): the listed rows get the
+    fixed-order AdamW of their gradient bit for bit, the 16-bit copy lands in both the full
+    table's rows and the packed rows (in place over the gradient when asked), fp32 rows are
+    packed as they are; rows not listed are untouched."""
+    rng = np.random.default_rng(17)
+    R, W = 41, 1000
+    p = rng.standard_normal(R * W).astype(np.float32)
+    m = (rng.standard_normal(R * W) * 1e-3).astype(np.float32)
+    v = (rng.random(R * W) * 1e-6).astype(np.float32)
+    rows = np.array([33, 0, 7, 40, 12], np.int32)
+    K = len(rows)
+    g32 = (rng.standard_normal(K * W) * 1e-2).astype(np.float32)
+    if gdt == "bf16":
+        g_in = oa.bf16_round_bits(g32)
+        g_or, code = oa.bf16_bits_to_f32(g_in), sl.SLIDE_BF16
+    elif gdt == "f16":
+        g_in = oa.f16_round_bits(g32)
+        g_or, code = oa.f16_bits_to_f32(g_in), sl.SLIDE_F16
+    else:
+        g_in, g_or, code = g32, g32, sl.SLIDE_F32
+    g_full = np.zeros(R * W, np.float32)
+    for k, r in enumerate(rows):
+        g_full[r * W:(r + 1) * W] = g_or[k * W:(k + 1) * W]
+    p2, m2, v2 = p.copy(), m.copy(), v.copy()
+    full = np.full(R * W, 7, np.uint16) if gdt != "f32" else None
+    g_buf = g_in.copy()
+    packed = g_buf if in_place else np.zeros_like(g_in)
+    sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, rows, K, g_buf, code, full, packed, 3,
+                                   CHP, 4)
+    po, mo, vo, bo = oa.adamw_fp32(p, g_full, m, v, 3, HP, copy="f16" if gdt == "f16" else "bf16")
+    sel = np.zeros(R, bool)
+    sel[rows] = True
+    sel = np.repeat(sel, W)
+    np.testing.assert_array_equal(p2[sel].view(np.uint32), po[sel].view(np.uint32))
+    np.testing.assert_array_equal(m2[sel].view(np.uint32), mo[sel].view(np.uint32))
+    np.testing.assert_array_equal(v2[sel].view(np.uint32), vo[sel].view(np.uint32))
+    np.testing.assert_array_equal(p2[~sel].view(np.uint32), p[~sel].view(np.uint32))
+    for k, r in enumerate(rows):
+        want = bo[r * W:(r + 1) * W] if gdt != "f32" else po[r * W:(r + 1) * W]
+        got = packed[k * W:(k + 1) * W]
+        np.testing.assert_array_equal(got.view(want.dtype), want)
+    if full is not None:
+        np.testing.assert_array_equal(full[sel], bo[sel])
+        assert np.all(full[~sel] == 7)
+    with pytest.raises(sl.SlideError):            # a row outside the table
+        sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, np.array([R], np.int32), 1, g_buf,
+                                       code, None, None, 1, CHP)
+    if gdt == "f32":
+        with pytest.raises(sl.SlideError):        # no 16-bit copy of an fp32 gradient
+            sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, rows, K, g_buf, code,
+                                           np.zeros(R * W, np.uint16), None, 1, CHP)
+    with pytest.raises(sl.SlideError):            # packed output partly over the gradient
+        sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, rows, K, g_buf, code, None,
+                                       g_buf.ctypes.data + 2, 1, CHP)
+
+
+def test_copy_rows_validates_before_any_launch():
+    a = np.zeros(64, np.float32)
+    for args in [(a, None, 4, a, None, 4, 2, 24),       # row_bytes not a multiple of 16
+                 (a, None, 1, a, None, 4, 2, 16),       # two rows in order from a 1-row source
+                 (a, None, 4, a, None, 4, -1, 16)]:     # negative count
+        with pytest.raises(sl.SlideError) as e:
+            sl.slide_copy_rows(*args)
+        assert e.value.code == _capi.SLIDE_E_SHAPE
+    sl.slide_copy_rows(a, None, 4, a, None, 4, 0, 16)     # nothing to copy: no launch
+
+
 def test_gpu_adamw_validates_before_any_launch():
     a = np.zeros(16, np.float32)
     with pytest.raises(sl.SlideError) as e:
@@ -440,3 +510,68 @@ def test_ring_rejects_bad_geometry():
         with pytest.raises(sl.SlideError) as e:
             sl.SlotRing(*args, dev, engine=sl.SLIDE_ENGINE_HOST)
         assert e.value.code == _capi.SLIDE_E_ARG
+
+
+def test_ring_ranged_flush_and_load_move_exactly_their_parts():
+    """A layer flushed and loaded in parts (the step boundary's layer 0): each part's ticket
+    covers its bytes, parts land at their offsets, the slot stays FLUSHING / LOADING between
+    parts, and acquire after the last load part sees the whole layer."""
+    wb, gb = 1024, 1024
+    ring, dev = _host_ring(2, wb, gb)
+    w = np.arange(wb, dtype=np.uint16).astype(np.uint8)
+    s = ring.load(0, w)
+    wptr, gptr = ring.acquire(s)
+    goff = gptr - dev.ctypes.data
+    dev[goff: goff + gb] = (np.arange(gb) % 251).astype(np.uint8)
+    hg = np.zeros(gb + 256, np.uint8)
+    parts = [(0, 256), (256, 512), (768, 256)]
+    tickets = []
+    for off, n in parts:
+        tickets.append(ring.flush_range(s, hg, off, n))
+        assert ring.state(s)[0] == _capi.SLOT_FLUSHING
+    for (off, n), t in zip(parts, tickets):
+        ring.wait_flush(t, 5000)
+        assert np.array_equal(hg[off: off + n], dev[goff + off: goff + off + n])
+    assert np.all(hg[gb:] == 0)
+    ring.release(s)
+    # load layer 1 in parts into the other slot, then acquire
+    w1 = (np.arange(wb) * 7 % 253).astype(np.uint8)
+    slot = -1
+    for off, n in parts:
+        slot = ring.load_range(1, w1, off, n, slot)
+        assert ring.state(slot) == (_capi.SLOT_LOADING, 1)
+    wptr, _ = ring.acquire(slot)
+    woff = wptr - dev.ctypes.data
+    assert np.array_equal(dev[woff: woff + wb], w1)
+    ring.release(slot)
+    ring.close()
+
+
+def test_ring_ranged_copies_validate_before_copying():
+    ring, dev = _host_ring(2, 1024, 512)
+    w = np.ones(1024, np.uint8)
+    g = np.zeros(512, np.uint8)
+    for off, n in [(0, 0), (1024, 1), (1000, 100)]:
+        with pytest.raises(sl.SlideError) as e:
+            ring.load_range(0, w, off, n, -1)
+        assert e.value.code == _capi.SLIDE_E_ARG
+    s = ring.load_range(0, w, 0, 512, -1)
+    with pytest.raises(sl.SlideError) as e:          # continue a load of another layer
+        ring.load_range(1, w, 512, 512, s)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    with pytest.raises(sl.SlideError) as e:          # flush a part of a slot not in use
+        ring.flush_range(s, g, 0, 256)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    ring.load_range(0, w, 512, 512, s)
+    ring.acquire(s)
+    with pytest.raises(sl.SlideError) as e:          # outside the gradient bytes
+        ring.flush_range(s, g, 256, 512)
+    assert e.value.code == _capi.SLIDE_E_ARG
+    t = ring.flush_range(s, g, 0, 256)
+    with pytest.raises(sl.SlideError) as e:          # a whole flush needs an IN_USE slot
+        ring.flush(s, g)
+    assert e.value.code == _capi.SLIDE_E_STATE
+    ring.flush_range(s, g, 256, 256)
+    ring.release(s)
+    ring.wait_flush(t, 5000)
+    ring.close()

@@ -130,14 +130,33 @@ def test_offload_and_overlap_do_not_change_results():
     # layer inputs slide to host memory (3 device slots for 5 layers) and come back
     lhost, phost = _run(3, False, activations="host", x_slots=3)
     lhost1, phost1 = _run(1, True, activations="host", x_slots=3)
-    print(f"  losses {la} {lb} {lc} {lone} {lrec} {lsteps} {lhost} {lhost1}", flush=True)
-    assert la == lb == lc == lone == lrec == lsteps[:2] == lhost == lhost1
+    # layer 0 moved whole at the step boundary instead of in parts, and in 3 uneven parts
+    lwhole, pwhole = _run(3, False, boundary_parts=1)
+    lp3, pp3 = _run(3, True, boundary_parts=3)
+    # only the selected embedding rows cross the link at the step boundary (packed)
+    lsp, psp = _run(3, False, steps=3, embed_split=True)
+    assert lsp == lsteps
+    for k in ("embed", "w_final", "lm_head"):
+        assert np.array_equal(psteps[k].view(np.uint32), psp[k].view(np.uint32)), k
+    for x, y in zip(psteps["layers"], psp["layers"]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    # the same in fp32 (packed fp32 rows), three steps
+    lt, pt = _run(3, False, steps=3, w=TINY)
+    lts, pts = _run(3, False, steps=3, w=TINY, embed_split=True)
+    assert lt == lts
+    for k in ("embed", "w_final", "lm_head"):
+        assert np.array_equal(pt[k].view(np.uint32), pts[k].view(np.uint32)), k
+    for x, y in zip(pt["layers"], pts["layers"]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    print(f"  losses {la} {lb} {lc} {lone} {lrec} {lsteps} {lhost} {lhost1} {lwhole} {lp3}",
+          flush=True)
+    assert la == lb == lc == lone == lrec == lsteps[:2] == lhost == lhost1 == lwhole == lp3
     # one LM-head chunk instead of four: the same step up to rounding (an AdamW step moves a
     # weight by at most about lr, so rounding-level gradient differences stay below 2 lr)
     l_ch, p_ch = _run(3, True, ce_chunk=1024)
     assert all(abs(x - y) <= 2e-3 * abs(y) for x, y in zip(l_ch, la))
     assert float(np.max(np.abs(p_ch["lm_head"] - pa["lm_head"]))) <= 2.5 * HP.lr
-    for other in (pb, pc, pone, prec, phost, phost1):
+    for other in (pb, pc, pone, prec, phost, phost1, pwhole, pp3):
         for k in ("embed", "w_final", "lm_head"):
             assert np.array_equal(pa[k].view(np.uint32), other[k].view(np.uint32)), k
         for x, y in zip(pa["layers"], other["layers"]):
@@ -216,7 +235,12 @@ def test_bf16_step_gradients_updates_and_uploads_match_oracle(activations):
     def on_gradient(name, step, off, g):
         blk = _block_of(name)
         arr = landed.setdefault((step, blk), np.full(sizes[blk], np.nan, np.float32))
-        arr[off:off + g.numel()] = oa.bf16_bits_to_f32(g.numpy().view(np.uint16))
+        vals = oa.bf16_bits_to_f32(g.numpy().view(np.uint16))
+        if isinstance(off, np.ndarray):       # packed rows of the split embedding
+            for k, r in enumerate(off):
+                arr[r * H:(r + 1) * H] = vals[k * H:(k + 1) * H]
+        else:
+            arr[off:off + g.numel()] = vals
 
     p = dict(embed=params["embed"].f32.reshape(-1), w_final=params["w_final"].f32,
              lm_head=params["lm_head"].f32.reshape(-1))
@@ -255,6 +279,13 @@ def test_bf16_step_gradients_updates_and_uploads_match_oracle(activations):
                             **{f"layer{i}": a for i, a in enumerate(got["layers"])})
             for blk in sizes:
                 g = landed.pop((step, blk))
+                if split and blk == "embed":
+                    # only the selected rows leave the GPU; every other row's gradient is
+                    # exactly zero (the oracle's gradient below must agree)
+                    sel = np.zeros(V, bool)
+                    sel[np.unique(tok[:, :-1])] = True
+                    assert not np.isnan(g.reshape(V, H)[sel]).any(), f"step {step}: embed"
+                    g.reshape(V, H)[~sel] = 0.0
                 assert not np.isnan(g).any(), f"step {step} {blk}: a part never landed"
                 if blk.startswith("layer"):
                     o = 0
