@@ -134,20 +134,149 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
   }
 }
 
-// dw partials: part[rb][j] = sum over rows of block rb of dy*x*r (rows in increasing order).
+// Single-pass variants for rows of H = 512 * NI elements: each lane keeps its NI 8-element
+// pieces of the row in registers (as loaded, 16 or 32 bytes each), so the row is read from
+// memory once, with all of a lane's loads in flight together. Same operations in the same
+// order as the two-pass kernels above, so the results are the same bits.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_dw_partial_kernel(const T* __restrict__ dy,
-                                                                 const T* __restrict__ x,
-                                                                 const float* __restrict__ rstd,
-                                                                 float* __restrict__ part, int N,
-                                                                 int H, int rows_per_block) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+struct Raw8 {
+  uint4 u[sizeof(T) / 2];
+  __device__ __forceinline__ void load(const T* p) {
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 2); ++k) u[k] = ((const uint4*)p)[k];
+  }
+  __device__ __forceinline__ void get(float (&v)[8]) const { V8<T>::load((const T*)u, v); }
+};
+
+template <typename T, int NI>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const T* __restrict__ x,
+                                                              const T* __restrict__ w,
+                                                              T* __restrict__ y, float* rstd,
+                                                              int N, float eps) {
+  constexpr int H = NI * 512;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const T* xr = x + (size_t)row * H + lane * 8;
+  Raw8<T> xv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) xv[i].load(xr + i * 512);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float v[8];
+    xv[i].get(v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+  }
+  ss = warp_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (rstd && lane == 0) rstd[row] = r;
+  T* yr = y + (size_t)row * H + lane * 8;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float v[8], g[8];
+    xv[i].get(v);
+    V8<T>::load(w + i * 512 + lane * 8, g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = g[k] * (v[k] * r);
+    V8<T>::store(yr + i * 512, v);
+  }
+}
+
+template <typename T, int NI>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const T* __restrict__ dy,
+                                                              const T* __restrict__ x,
+                                                              const T* __restrict__ w,
+                                                              const T* dres, T* dx, float* rstd,
+                                                              int N, float eps) {
+  constexpr int H = NI * 512;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const size_t o0 = (size_t)row * H + lane * 8;
+  Raw8<T> xv[NI], dv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    xv[i].load(x + o0 + i * 512);
+    dv[i].load(dy + o0 + i * 512);
+  }
+  float ss = 0.f, gx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float a[8], d[8], g[8];
+    xv[i].get(a);
+    dv[i].get(d);
+    V8<T>::load(w + i * 512 + lane * 8, g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ss += a[k] * a[k];
+      gx += (g[k] * d[k]) * a[k];
+    }
+  }
+  ss = warp_sum(ss);
+  gx = warp_sum(gx);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  const float coef = r * r * r * gx / (float)H;
+  if (lane == 0) rstd[row] = r;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float a[8], d[8], g[8], o[8];
+    xv[i].get(a);
+    dv[i].get(d);
+    V8<T>::load(w + i * 512 + lane * 8, g);
+    if (dres) V8<T>::load(dres + o0 + i * 512, o);
+    else
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] += r * (g[k] * d[k]) - coef * a[k];
+    V8<T>::store(dx + o0 + i * 512, o);
+  }
+}
+
+// dw partials: part[rb][j] = sum over rows of block rb of dy*x*r (rows in increasing order).
+// One lane per 8 consecutive columns (16- or 32-byte loads), one wave per workgroup.
+template <typename T>
+__global__ __launch_bounds__(64) void rmsnorm_dw_partial_kernel(const T* __restrict__ dy,
+                                                                const T* __restrict__ x,
+                                                                const float* __restrict__ rstd,
+                                                                float* __restrict__ part, int N,
+                                                                int H, int rows_per_block) {
+  const int j = (blockIdx.x * 64 + threadIdx.x) * 8;
   if (j >= H) return;
   const int r0 = blockIdx.y * rows_per_block, r1 = min(N, r0 + rows_per_block);
-  float acc = 0.f;
-  for (int t = r0; t < r1; ++t)
-    acc += Elem<T>::load(dy + (size_t)t * H + j) * Elem<T>::load(x + (size_t)t * H + j) * rstd[t];
-  part[(size_t)blockIdx.y * H + j] = acc;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  // 16 rows' loads in flight at a time; the sums still run row by row in order
+  constexpr int U = 16;
+  int t = r0;
+  for (; t + U <= r1; t += U) {
+    Raw8<T> a[U], b[U];
+    float r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u].load(dy + (size_t)(t + u) * H + j);
+      b[u].load(x + (size_t)(t + u) * H + j);
+      r[u] = rstd[t + u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float av[8], bv[8];
+      a[u].get(av);
+      b[u].get(bv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += av[k] * bv[k] * r[u];
+    }
+  }
+  for (; t < r1; ++t) {
+    float a[8], b[8];
+    V8<T>::load(dy + (size_t)t * H + j, a);
+    V8<T>::load(x + (size_t)t * H + j, b);
+    const float r = rstd[t];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += a[k] * b[k] * r;
+  }
+  V8<float>::store(part + (size_t)blockIdx.y * H + j, acc);
 }
 
 // Sum of nparts rows of H floats, per column: 64 columns per workgroup, the parts split over 4
@@ -379,6 +508,18 @@ int rmsnorm_fwd(const void* x, const void* w, void* y, float* rstd, int N, int H
   if (N == 0) return SLIDE_OK;
   ProfScope ps("rmsnorm_fwd", st);
   dim3 grid(blocks_for(N, 4)), block(256);
+#define SLIDE_RMS_FWD_REG(NI)                                                                  \
+  case NI:                                                                                     \
+    SLIDE_DISPATCH(dtype, T,                                                                   \
+                   hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, NI>), grid, block, 0, st,     \
+                                      (const T*)x, (const T*)w, (T*)y, rstd, N, eps));         \
+    return check_launch("rmsnorm_fwd");
+  if (H % 512 == 0) switch (H / 512) {
+      SLIDE_RMS_FWD_REG(1) SLIDE_RMS_FWD_REG(2) SLIDE_RMS_FWD_REG(4) SLIDE_RMS_FWD_REG(8)
+      SLIDE_RMS_FWD_REG(16) SLIDE_RMS_FWD_REG(24)
+      default: break;
+    }
+#undef SLIDE_RMS_FWD_REG
   SLIDE_DISPATCH(dtype, T,
                  hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, grid, block, 0, st, (const T*)x,
                                     (const T*)w, (T*)y, rstd, N, H, eps));
@@ -400,10 +541,26 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
     ProfScope ps("rmsnorm_bwd", st);
     if (N > 0) {
       dim3 grid(blocks_for(N, 4)), block(256);
-      SLIDE_DISPATCH(dtype, T,
-                     hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, grid, block, 0, st,
-                                        (const T*)dy, (const T*)x, (const T*)w,
-                                        (const T*)dres, (T*)dx, rstd, N, H, eps));
+      bool done = false;
+#define SLIDE_RMS_BWD_REG(NI)                                                                  \
+  case NI:                                                                                     \
+    SLIDE_DISPATCH(dtype, T,                                                                   \
+                   hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, NI>), grid, block, 0, st,     \
+                                      (const T*)dy, (const T*)x, (const T*)w, (const T*)dres,  \
+                                      (T*)dx, rstd, N, eps));                                  \
+    done = true;                                                                               \
+    break;
+      if (H % 512 == 0) switch (H / 512) {
+          SLIDE_RMS_BWD_REG(1) SLIDE_RMS_BWD_REG(2) SLIDE_RMS_BWD_REG(4) SLIDE_RMS_BWD_REG(8)
+          SLIDE_RMS_BWD_REG(16)
+          default: break;
+        }
+#undef SLIDE_RMS_BWD_REG
+      if (!done)
+        SLIDE_DISPATCH(dtype, T,
+                       hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, grid, block, 0, st,
+                                          (const T*)dy, (const T*)x, (const T*)w,
+                                          (const T*)dres, (T*)dx, rstd, N, H, eps));
     }
   }
   SLIDE_TRY(check_launch("rmsnorm_bwd"));
@@ -412,7 +569,7 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* w, const void* dres, 
   if (N == 0) {
     hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(H, 256)), dim3(256), 0, st, part, (size_t)H, 0.f);
   } else {
-    dim3 g1(blocks_for(H, 256), parts), b1(256);
+    dim3 g1(blocks_for(H / 8, 64), parts), b1(64);
     SLIDE_DISPATCH(dtype, T,
                    hipLaunchKernelGGL(rmsnorm_dw_partial_kernel<T>, g1, b1, 0, st,
                                       (const T*)dy, (const T*)x, rstd, part, N, H,
