@@ -101,6 +101,16 @@ __device__ __forceinline__ void tr_wait(bf16x8_t (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
+// The same with the last K LDS operations of this wave still in flight (the reads of the next
+// step, issued after v's): LDS operations complete in order, so v's have landed. Only for code
+// with no scalar memory loads outstanding, which share the counter and complete out of order.
+template <int K, int N>
+__device__ __forceinline__ void tr_wait_keep(bf16x8_t (&v)[N]) {
+  static_assert(K >= 0 && K < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(K) : "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
 
 // Column fragment through two transpose reads: A operand of an MFMA whose row index is the tile
 // column d0 + lane%32 and whose 8 k values are tile rows 16ks + 4h + {0..3} and
@@ -126,6 +136,21 @@ __device__ __forceinline__ int acc_key(int kb, int i, int hf) {
 // 2^-126 come out as denormals; here such values are weights next to a row maximum of 1 and
 // contribute nothing, so the flush to zero is immaterial.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a value with the one held by the lane 32 away (the other half of a score column):
+// v_permlane32_swap hands every lane the pair (value of lane l mod 32, value of lane l mod 32 +
+// 32) without a trip through the LDS. The pair is combined in the same order in both halves, and
+// max and + are commutative, so every lane gets the same bits as with a shuffle.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -240,21 +265,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma32<DT>(rows_read<D>(sK, kb * 32 + lr, kk * 2 + hf), qf[kk], sacc[kb]);
+    // V^T fragments of the first 16 keys: they do not depend on the scores, so they are read
+    // before the softmax, whose VALU work covers their latency; each later step's are read
+    // while the previous step's MFMAs run
+    bf16x8_t vt[2][NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vt[0][db] = t_read<D>(sV, db * 32, 0, lane);
+    // the mask only on blocks that reach the diagonal or the end (one branch per block, not
+    // one per score)
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
     float mx = -INFINITY;
+    if (need_mask) {
+      // key kv0 + acc_key(kb, i, hf) is masked iff it is past min(q, S - 1); acc_key without
+      // its lane term is a constant of the unrolled loop
+      const int lim = min(q, S - 1) - kv0 - hf * 4;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = sacc[kb][i] * sl2;
-        if (need_mask) {
-          const int key = kv0 + acc_key(kb, i, hf);
-          if (key > q || key >= S) s = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const float s = acc_key(kb, i, 0) > lim ? -INFINITY : sacc[kb][i] * sl2;
+          sacc[kb][i] = s;
+          mx = fmaxf(mx, s);
         }
-        sacc[kb][i] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float s = sacc[kb][i] * sl2;
+          sacc[kb][i] = s;
+          mx = fmaxf(mx, s);
+        }
+    }
+    mx = halves_max(mx);
     const float m_new = fmaxf(m2, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m2 - m_use);
@@ -267,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
         sacc[kb][i] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32, 64);
+    rs = halves_sum(rs);
     l = l * alpha + rs;
     m2 = m_new;
 #pragma unroll
@@ -280,13 +323,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
 #pragma unroll
       for (int j = 0; j < 8; ++j) pv[j] = sacc[ks >> 1][8 * (ks & 1) + j];
       const bf16x8_t pf = pack8<DT>(pv);
-      bf16x8_t vt[NDB];
+      if (ks < 3) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) vt[db] = t_read<D>(sV, db * 32, ks, lane);
-      tr_wait(vt);
+        for (int db = 0; db < NDB; ++db) vt[(ks + 1) & 1][db] = t_read<D>(sV, db * 32, ks + 1, lane);
+        tr_wait_keep<2 * NDB>(vt[ks & 1]);     // two transpose reads per fragment
+      } else {
+        tr_wait(vt[ks & 1]);
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        oacc[db] = mfma32<DT>(vt[db], pf, oacc[db]);
+        oacc[db] = mfma32<DT>(vt[ks & 1][db], pf, oacc[db]);
     }
   }
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
@@ -432,6 +478,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
         pacc[kb] = mfma32<DT>(rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb]);
       }
     }
+    // (a branch-free mask, as in the forward, measured 4% slower here: the compiler's schedule
+    // of this form is the better one at this register budget)
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S) || (wq0 + 32 > S);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -574,16 +622,29 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
         for (int db = 0; db < NDB; ++db) tf1[db] = t_read<D>(sT, db * 32, 2 * qb2 + 1, lane);
       }
       // element i is (query q0 + acc_key(qb2, i), this lane's key)
+      if constexpr (DK) {
+        // (the branch-free mask below spills here, at 256 registers, and measured 10% slower)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ql = acc_key(qb2, i, hf);
-        float p = fast_exp2(sacc[i] * sl2 - sL[st][ql] * kLog2e);
-        if (need_mask) {
-          const int qq = q0 + ql;
-          if (key > qq || qq >= S) p = 0.f;
+        for (int i = 0; i < 16; ++i) {
+          const int ql = acc_key(qb2, i, hf);
+          float p = fast_exp2(sacc[i] * sl2 - sL[st][ql] * kLog2e);
+          if (need_mask) {
+            const int qq = q0 + ql;
+            if (key > qq || qq >= S) p = 0.f;
+          }
+          sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
         }
-        if constexpr (DK) sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
-        else sacc[i] = p;                                           // P
+      } else {
+        // query q0 + acc_key(qb2, i, hf) is masked iff it precedes this lane's key or is past
+        // the end: one compare pair and select per score, selecting nothing off the diagonal
+        const int lo = key - q0 - hf * 4, hi = S - 1 - q0 - hf * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = acc_key(qb2, i, hf);
+          const float p = fast_exp2(sacc[i] * sl2 - sL[st][ql] * kLog2e);
+          const int c = acc_key(qb2, i, 0);
+          sacc[i] = (c < lo || c > hi) ? 0.f : p;                    // P
+        }
       }
       float w[8];
 #pragma unroll
