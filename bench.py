@@ -48,8 +48,10 @@ def kernel_flops(spec, B, S, ce_chunk):
     exe = dict(g)
     # backward, algorithmically dV, dP, dK and dQ once each; the kernels recompute the scores
     # (dV, dK and dQ kernels) and dP (dK and dQ kernels)
-    alg.update(attn_fwd=2 * U, attn_bwd_dv=1 * U, attn_bwd_dk=2 * U, attn_bwd_dq=1 * U)
-    exe.update(attn_fwd=2 * U, attn_bwd_dv=2 * U, attn_bwd_dk=3 * U, attn_bwd_dq=3 * U)
+    # dK and dV run as one launch: 2 causal matmuls for dK (dS^T Q and dP), 1 for dV (P^T dO);
+    # executed, the scores are recomputed in both halves and dP in the dK half
+    alg.update(attn_fwd=2 * U, attn_bwd_dkv=3 * U, attn_bwd_dq=1 * U)
+    exe.update(attn_fwd=2 * U, attn_bwd_dkv=5 * U, attn_bwd_dq=3 * U)
     nch = (V + ce_chunk - 1) // ce_chunk
     per = 2 * N * V * H / nch           # average per chunk launch
     # the logits run twice (statistics pass, then recomputed with dz fused); algorithmically once

@@ -20,10 +20,11 @@
 //    exchange with the lane 32 away. O^T += V^T P^T (and dQ^T += K^T dS^T) take P (dS) straight
 //    from the score accumulators as the B operand; the 16 keys an MFMA consumes are ordered the
 //    way the accumulator holds them, and the transpose reads fetch V^T (K^T) in that order.
-//  * dK and dV: two kernels (one accumulator each, so each fits 256 registers), 128 keys per
-//    workgroup, looping over the G query heads of the kv group and over the query blocks on or
-//    after the diagonal, so dK and dV are summed without atomics (the result is deterministic).
-//    dQ runs as its own kernel.
+//  * dK and dV: two workgroup bodies (one accumulator each, so each fits 256 registers) in one
+//    launch, 128 keys per workgroup, looping over the G query heads of the kv group and over
+//    the query blocks on or after the diagonal, so dK and dV are summed without atomics (the
+//    result is deterministic). dQ runs as its own kernel. Every grid is flat and ordered
+//    heaviest block first.
 //  * D_i = rowsum(dO_i * O_i) is precomputed by a small kernel.
 // fp32 path (the small fp32 configuration): straightforward SIMT kernels, one thread per query
 // (forward, dQ) or per key (dK/dV).
@@ -207,9 +208,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
   auto tK = [&](int b) { return smem + b * 2 * 64 * D; };
   auto tV = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };
 
+  // one flat grid, heaviest (latest) query blocks of every head and sequence first: the
+  // hardware dispatches in order, so the light blocks fill the compute units at the end
   const int nqb = (S + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;  // heaviest (latest) query blocks first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int per = gridDim.x / nqb;       // heads x sequences
+  const int qb = nqb - 1 - (int)blockIdx.x / per;
+  const int h = (int)blockIdx.x % per % nq, b = (int)blockIdx.x % per / nq;
   const int g = h / (nq / nkv);
   const int QS = (nq + 2 * nkv) * D;
   const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
@@ -414,9 +418,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
   auto tK = [&](int b) { return smem + b * 2 * 64 * D; };
   auto tV = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };
 
-  const int nqb = (S + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nqb = (S + 127) / 128;       // flat grid, heaviest first (as in the forward)
+  const int per = gridDim.x / nqb;
+  const int qb = nqb - 1 - (int)blockIdx.x / per;
+  const int h = (int)blockIdx.x % per % nq, b = (int)blockIdx.x % per / nq;
   const int g = h / (nq / nkv);
   const int QS = (nq + 2 * nkv) * D, OS = nq * D;
   const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
@@ -515,28 +520,26 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
 }
 
 // ------------------------------------------------------------------ dK, dV
-// One kernel per output: MODE_DV accumulates dV = sum P^T dO, MODE_DK accumulates
+// One workgroup body per output: MODE_DV accumulates dV = sum P^T dO, MODE_DK accumulates
 // dK = scale * sum dS^T Q with dS = P (dP - D). Each recomputes the scores it needs; split this
 // way a wave holds one 32 x d accumulator instead of two, and both stay within 256 registers
 // per lane, so two workgroups share a compute unit.
 constexpr int MODE_DV = 0, MODE_DK = 1;
 
 template <int D, int MODE, int DT>
-__global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restrict__ qkv,
-                                                          const bf16_t* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          const float* __restrict__ delta,
-                                                          bf16_t* __restrict__ dqkv, int S, int nq,
-                                                          int nkv, float scale) {
+__device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (*sDl)[64],
+                                          int kblk, int g, int b,
+                                          const bf16_t* __restrict__ qkv,
+                                          const bf16_t* __restrict__ dout,
+                                          const float* __restrict__ lse,
+                                          const float* __restrict__ delta,
+                                          bf16_t* __restrict__ dqkv, int S, int nq, int nkv,
+                                          float scale) {
   constexpr bool DK = MODE == MODE_DK;
   constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
-  __shared__ float sL[NSTAGE][64], sDl[NSTAGE][64];
   auto tQ = [&](int b) { return smem + b * 2 * 64 * D; };
   auto tO = [&](int b) { return smem + b * 2 * 64 * D + 64 * D; };  // dO rows
 
-  const int kblk = blockIdx.x;  // earliest keys have the most query blocks: launched first
-  const int g = blockIdx.y, b = blockIdx.z;
   const int G = nq / nkv;
   const int QS = (nq + 2 * nkv) * D, OS = nq * D;
   const int lane = threadIdx.x & 63, hf = lane >> 5, lr = lane & 31;
@@ -674,6 +677,33 @@ __global__ __launch_bounds__(256, 2) void attn_dkv_kernel(const bf16_t* __restri
   if (nv > 0)
     store_tile_t<D, DT>(stage, acc, DK ? scale : 1.0f,
                     dqkv + (size_t)b * S * QS + (nq + (DK ? 0 : nkv) + g) * D, QS, wk0, nv, lane);
+}
+
+// dK and dV in one launch, one workgroup per (key block, output, kv head, sequence), in one
+// flat grid ordered by key block: the earliest keys, which see the most query blocks, of both
+// outputs go first. A key block's work shrinks along the sequence (8 : 1 at S = 1024), so with
+// each output launched alone (512 workgroups, all resident at once) every launch waited for its
+// heaviest blocks; in one grid the lighter blocks of both fill the compute units behind the
+// heavy ones. The two bodies share the LDS and the register budget is their maximum.
+template <int D, int DT>
+__global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
+                                                           const bf16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta,
+                                                           bf16_t* __restrict__ dqkv, int S,
+                                                           int nq, int nkv, float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[smem_elems<D>(2)];
+  __shared__ float sL[NSTAGE][64], sDl[NSTAGE][64];
+  const int nkb = (S + 127) / 128;
+  const int per = gridDim.x / nkb;     // 2 outputs x kv heads x sequences
+  const int kblk = (int)blockIdx.x / per, r = (int)blockIdx.x % per;
+  const int mode = r & 1, g = (r >> 1) % nkv, b = (r >> 1) / nkv;
+  if (mode == MODE_DK)
+    dkv_block<D, MODE_DK, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse, delta, dqkv, S, nq, nkv,
+                              scale);
+  else
+    dkv_block<D, MODE_DV, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse, delta, dqkv, S, nq, nkv,
+                              scale);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT kernels
@@ -814,7 +844,7 @@ namespace {
 template <int DT>
 void launch_fwd16(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv, int d,
                   float scale, hipStream_t st) {
-  dim3 grid((S + 127) / 128, nq, B), block(256);
+  dim3 grid((unsigned)((S + 127) / 128 * nq * B)), block(256);
   if (d == 128)
     hipLaunchKernelGGL((attn_fwd_kernel<128, DT>), grid, block, 0, st, (const bf16_t*)qkv,
                        (bf16_t*)o, lse, S, nq, nkv, scale);
@@ -845,7 +875,7 @@ int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv
   bf16_t* out = (bf16_t*)dqkv;
   {
     ProfScope ps("attn_bwd_dq", st);
-    dim3 grid((S + 127) / 128, nq, B), block(256);
+    dim3 grid((unsigned)((S + 127) / 128 * nq * B)), block(256);
     if (d == 128)
       hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
                          nq, nkv, scale);
@@ -855,27 +885,16 @@ int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv
   }
   SLIDE_TRY(check_launch("attn_bwd_dq"));
   {
-    ProfScope ps("attn_bwd_dv", st);
-    dim3 grid((S + 127) / 128, nkv, B), block(256);
+    ProfScope ps("attn_bwd_dkv", st);
+    dim3 grid((unsigned)((S + 127) / 128 * 2 * nkv * B)), block(256);
     if (d == 128)
-      hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DV, DT>), grid, block, 0, st, q, g, lse,
-                         delta, out, S, nq, nkv, scale);
+      hipLaunchKernelGGL((attn_dkdv_kernel<128, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+                         nq, nkv, scale);
     else
-      hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DV, DT>), grid, block, 0, st, q, g, lse,
-                         delta, out, S, nq, nkv, scale);
+      hipLaunchKernelGGL((attn_dkdv_kernel<64, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+                         nq, nkv, scale);
   }
-  SLIDE_TRY(check_launch("attn_bwd_dv"));
-  {
-    ProfScope ps("attn_bwd_dk", st);
-    dim3 grid((S + 127) / 128, nkv, B), block(256);
-    if (d == 128)
-      hipLaunchKernelGGL((attn_dkv_kernel<128, MODE_DK, DT>), grid, block, 0, st, q, g, lse,
-                         delta, out, S, nq, nkv, scale);
-    else
-      hipLaunchKernelGGL((attn_dkv_kernel<64, MODE_DK, DT>), grid, block, 0, st, q, g, lse,
-                         delta, out, S, nq, nkv, scale);
-  }
-  return check_launch("attn_bwd_dk");
+  return check_launch("attn_bwd_dkv");
 }
 
 }  // namespace
