@@ -200,6 +200,39 @@ def test_embedding_fwd_bwd_repeated_tokens(dtype):
                        dE2.view(torch.int16) if dtype != "f32" else dE2)
 
 
+@pytest.mark.parametrize("row_bytes", [16, 528, 8192])
+def test_copy_rows_gather_scatter_exact(row_bytes):
+    """Row gather (listed source rows into a packed matrix), scatter (packed rows into listed
+    destination rows) and both at once move exactly the listed rows, bit for bit; rows not
+    listed stay as they were; listed indices outside a matrix are skipped."""
+    print(f"copy_rows row_bytes={row_bytes}", flush=True)
+    rng = np.random.default_rng(5)
+    V, n = 37, 12
+    w = row_bytes // 4
+    table = torch.from_numpy(rng.integers(0, 2**31, (V, w), dtype=np.int64).astype(np.int32)).to(DEV)
+    rows = np.array([36, 0, 5, 17, 3, 30, 31, 9, 12, 1, 22, 8], np.int32)
+    t_rows = torch.from_numpy(rows).to(DEV)
+    packed = torch.full((n, w), -1, dtype=torch.int32, device=DEV)
+    sl.slide_copy_rows(table, t_rows, V, packed, None, n, n, row_bytes, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(packed.cpu(), table.cpu()[torch.from_numpy(rows).long()])
+    dst = torch.zeros((V, w), dtype=torch.int32, device=DEV)
+    sl.slide_copy_rows(packed, None, n, dst, t_rows, V, n, row_bytes, stream())
+    torch.cuda.synchronize()
+    want = torch.zeros((V, w), dtype=torch.int32)
+    want[torch.from_numpy(rows).long()] = table.cpu()[torch.from_numpy(rows).long()]
+    assert torch.equal(dst.cpu(), want)
+    # both lists at once, with two indices out of range (skipped, nothing else touched)
+    src_rows = torch.from_numpy(np.array([2, 40, 7, -1], np.int32)).to(DEV)
+    dst_rows = torch.from_numpy(np.array([10, 11, 99, 12], np.int32)).to(DEV)
+    dst2 = torch.zeros((V, w), dtype=torch.int32, device=DEV)
+    sl.slide_copy_rows(table, src_rows, V, dst2, dst_rows, V, 4, row_bytes, stream())
+    torch.cuda.synchronize()
+    want2 = torch.zeros((V, w), dtype=torch.int32)
+    want2[10] = table.cpu()[2]
+    assert torch.equal(dst2.cpu(), want2)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("n", [0, 5, 8, 1000003])
 def test_nonfinite_count_exact(dtype, n):
