@@ -13,6 +13,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -24,6 +27,92 @@ int fail(int code, const char* fmt, ...);
 }
 
 namespace {
+
+// Helper threads kept alive per calling thread: a layer's update is one call, about seventy per
+// training step, and creating and joining a dozen threads for each of them costs more than the
+// dispatch below. Each calling thread (the engine's in-memory and tiered workers, a test) owns
+// its own helpers, so concurrent callers never wait for one another; they end with it.
+class Helpers {
+ public:
+  ~Helpers() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  // Run body(i) for i in [0, n): i = 0 on the caller, the others on helpers; returns when all
+  // are done.
+  void run(int n, const std::function<void(int)>& body) {
+    if (n <= 1) {
+      if (n == 1) body(0);
+      return;
+    }
+    while ((int)th_.size() < n - 1) {
+      const int k = (int)th_.size();
+      th_.emplace_back([this, k] { loop(k + 1); });
+    }
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      body_ = &body;
+      n_ = n;
+      left_ = n - 1;
+      ++gen_;
+    }
+    cv_.notify_all();
+    body(0);
+    std::unique_lock<std::mutex> lk(mu_);
+    done_.wait(lk, [&] { return left_ == 0; });
+    body_ = nullptr;
+  }
+
+ private:
+  void loop(int idx) {
+    uint64_t seen = 0;
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      seen = gen_;   // a helper created for a call joins it below: gen_ already counts it
+      if (body_ && idx < n_) --seen;
+    }
+    for (;;) {
+      const std::function<void(int)>* b;
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        if (idx >= n_) continue;   // not needed in this call
+        b = body_;
+      }
+      (*b)(idx);
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        if (--left_ == 0) done_.notify_all();
+      }
+    }
+  }
+  std::vector<std::thread> th_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_;
+  const std::function<void(int)>* body_ = nullptr;
+  int n_ = 0, left_ = 0;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+thread_local Helpers tl_helpers;
+
+// body(lo, hi) over [0, n) split into at most nt ranges of `align`-multiple length
+void parallel_ranges(size_t n, int nt, size_t align, const std::function<void(size_t, size_t)>& body) {
+  size_t per = (n + nt - 1) / nt;
+  per = (per + align - 1) / align * align;
+  const int parts = (int)((n + per - 1) / per);
+  tl_helpers.run(parts, [&](int i) {
+    const size_t lo = (size_t)i * per, hi = std::min(n, lo + per);
+    if (lo < hi) body(lo, hi);
+  });
+}
 
 using Consts = slide::AdamConsts;
 
@@ -197,16 +286,7 @@ extern "C" int slide_cpu_adamw(float* p, const void* g, int g_dtype, float* m, f
     work(0, n);
     return SLIDE_OK;
   }
-  std::vector<std::thread> th;
-  th.reserve(nt);
-  size_t per = (n + nt - 1) / nt;
-  per = (per + 15) / 16 * 16;
-  for (int t = 0; t < nt; ++t) {
-    size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
-    if (lo >= hi) break;
-    th.emplace_back(work, lo, hi);
-  }
-  for (auto& x : th) x.join();
+  parallel_ranges(n, nt, 16, work);
   return SLIDE_OK;
 }
 
@@ -253,15 +333,7 @@ extern "C" int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float*
     work(0, n_rows);
     return SLIDE_OK;
   }
-  std::vector<std::thread> th;
-  th.reserve(nt);
-  const size_t per = (n_rows + nt - 1) / nt;
-  for (int t = 0; t < nt; ++t) {
-    const size_t k0 = (size_t)t * per, k1 = std::min(n_rows, k0 + per);
-    if (k0 >= k1) break;
-    th.emplace_back(work, k0, k1);
-  }
-  for (auto& x : th) x.join();
+  parallel_ranges(n_rows, nt, 1, work);
   return SLIDE_OK;
 }
 
@@ -323,15 +395,7 @@ extern "C" int slide_cpu_adamw_rows_packed(float* p, float* m, float* v, size_t 
     work(0, n_rows);
     return SLIDE_OK;
   }
-  std::vector<std::thread> th;
-  th.reserve(nt);
-  const size_t per = (n_rows + nt - 1) / nt;
-  for (int t = 0; t < nt; ++t) {
-    const size_t k0 = (size_t)t * per, k1 = std::min(n_rows, k0 + per);
-    if (k0 >= k1) break;
-    th.emplace_back(work, k0, k1);
-  }
-  for (auto& x : th) x.join();
+  parallel_ranges(n_rows, nt, 1, work);
   return SLIDE_OK;
 }
 
@@ -362,14 +426,7 @@ extern "C" int slide_cpu_convert_f32(const float* src, void* dst, int dst_dtype,
     work(0, n);
     return SLIDE_OK;
   }
-  std::vector<std::thread> th;
-  const size_t per = (n + nt - 1) / nt;
-  for (int t = 0; t < nt; ++t) {
-    const size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
-    if (lo >= hi) break;
-    th.emplace_back(work, lo, hi);
-  }
-  for (auto& x : th) x.join();
+  parallel_ranges(n, nt, 1, work);
   return SLIDE_OK;
 }
 
@@ -424,14 +481,9 @@ extern "C" int slide_host_triad(size_t n, int n_threads, int reps, double* gbs_b
   size_t per = (n + nt - 1) / nt;
   per = (per + 15) / 16 * 16;
   const bool avx512 = __builtin_cpu_supports("avx512f");
+  // the optimizer's helper threads, each on the range it first touched
   auto parallel = [&](auto&& body) {
-    std::vector<std::thread> th;
-    for (int t = 0; t < nt; ++t) {
-      size_t lo = (size_t)t * per, hi = std::min(n, lo + per);
-      if (lo >= hi) break;
-      th.emplace_back(body, lo, hi);
-    }
-    for (auto& x : th) x.join();
+    parallel_ranges(n, nt, 16, [&](size_t lo, size_t hi) { body(lo, hi); });
   };
   parallel([&](size_t lo, size_t hi) {
     for (size_t i = lo; i < hi; ++i) {
