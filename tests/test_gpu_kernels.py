@@ -31,6 +31,8 @@ GEMM_SHAPES = [
     (328, 200, 136),      # small-tile path: 3 x 2 tiles of 128 with ragged edges, 3 k-tiles
     (2088, 4120, 136),    # large-tile path: 9 x 17 tiles of 256 with ragged edges
     (2090, 4121, 136),    # large-tile path, odd N and ldc: per-element stores at every row
+    (4608, 4096, 520),    # full 256 x 256 tiles, more than one per compute unit (288): the
+                          # bf16 store walks tiles, each next tile's loads under the last store
 ]
 
 
