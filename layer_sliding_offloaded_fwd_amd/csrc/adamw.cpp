@@ -118,6 +118,21 @@ using Consts = slide::AdamConsts;
 
 Consts make_consts(const slide_adamw_hp& hp, int64_t t) { return slide::adam_consts(hp, t); }
 
+// Every listed row inside [0, n_total) and listed once (a repeated row would be updated twice,
+// by two threads at once); -1 if so, else the position of the first offending entry.
+long long bad_row(const int32_t* rows, size_t n, size_t n_total) {
+  std::vector<uint64_t> seen((n_total + 63) / 64, 0);
+  for (size_t k = 0; k < n; ++k) {
+    const int32_t r = rows[k];
+    if (r < 0 || (size_t)r >= n_total) return (long long)k;
+    uint64_t& w = seen[(size_t)r >> 6];
+    const uint64_t bit = uint64_t(1) << (r & 63);
+    if (w & bit) return (long long)k;
+    w |= bit;
+  }
+  return -1;
+}
+
 inline float widen_bf16(uint16_t b) {
   uint32_t u = ((uint32_t)b) << 16;
   float f;
@@ -307,10 +322,9 @@ extern "C" int slide_cpu_adamw_rows(float* p, const void* g, int g_dtype, float*
                               g ? p_bf16_out : nullptr, n, step, hp);
   if (rc != SLIDE_OK) return rc;
   if (!rows) return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows: null row list");
-  for (size_t k = 0; k < n_rows; ++k)
-    if (rows[k] < 0 || (size_t)rows[k] >= n_rows_total)
-      return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows: row %d outside [0, %zu)", rows[k],
-                  n_rows_total);
+  if (const long long k = bad_row(rows, n_rows, n_rows_total); k >= 0)
+    return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows: row %d (entry %lld) outside [0, %zu) or repeated",
+                rows[k], k, n_rows_total);
   const Consts c = make_consts(*hp, step);
   const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
   const size_t gsz = g_dtype == SLIDE_F32 ? 4 : 2;
@@ -366,10 +380,10 @@ extern "C" int slide_cpu_adamw_rows_packed(float* p, float* m, float* v, size_t 
     if (a < b + nb && b < a + nb)
       return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: out_packed partially overlaps g");
   }
-  for (size_t k = 0; k < n_rows; ++k)
-    if (rows[k] < 0 || (size_t)rows[k] >= n_rows_total)
-      return fail(SLIDE_E_ARG, "slide_cpu_adamw_rows_packed: row %d outside [0, %zu)", rows[k],
-                  n_rows_total);
+  if (const long long k = bad_row(rows, n_rows, n_rows_total); k >= 0)
+    return fail(SLIDE_E_ARG,
+                "slide_cpu_adamw_rows_packed: row %d (entry %lld) outside [0, %zu) or repeated",
+                rows[k], k, n_rows_total);
   const Consts c = make_consts(*hp, step);
   const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
   auto work = [&](size_t k0, size_t k1) {

@@ -263,6 +263,11 @@ def test_cpu_adamw_rows_bit_exact_vs_oracle(gdt, zero_grad):
     with pytest.raises(sl.SlideError):            # a row outside the arrays
         sl.slide_cpu_adamw_rows(p2, None, code, m2, v2, None, W, R,
                                 np.array([R], np.int32), 1, 1, CHP)
+    p3 = p2.copy()
+    with pytest.raises(sl.SlideError):            # a row listed twice: refused, nothing changed
+        sl.slide_cpu_adamw_rows(p3, None, code, m2, v2, None, W, R,
+                                np.array([3, 9, 3], np.int32), 3, 1, CHP)
+    np.testing.assert_array_equal(p3.view(np.uint32), p2.view(np.uint32))
 
 
 @pytest.mark.parametrize("gdt", ["f32", "bf16", "f16"])
@@ -314,6 +319,9 @@ def test_cpu_adamw_rows_packed_bit_exact_vs_oracle(gdt, in_place):
         assert np.all(full[~sel] == 7)
     with pytest.raises(sl.SlideError):            # a row outside the table
         sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, np.array([R], np.int32), 1, g_buf,
+                                       code, None, None, 1, CHP)
+    with pytest.raises(sl.SlideError):            # a row listed twice
+        sl.slide_cpu_adamw_rows_packed(p2, m2, v2, W, R, np.array([5, 5], np.int32), 2, g_buf,
                                        code, None, None, 1, CHP)
     if gdt == "f32":
         with pytest.raises(sl.SlideError):        # no 16-bit copy of an fp32 gradient
