@@ -7,8 +7,9 @@
 // 16-bit path (bf16 or fp16 operands: gfx950 MFMA v_mfma_f32_32x32x16_bf16 / _f16, fp32
 // accumulation, flash-style, no [S, S] tensor in memory):
 //  * every operand tile is [64 rows][d] of q, k, v or dO rows, copied global -> LDS by
-//    direct-to-LDS loads into 2 pipelined stages (the next block in flight while one is
-//    computed). The forward and dQ kernels are held to 256 registers per lane so that two
+//    direct-to-LDS buffer loads into 2 pipelined stages (the next block in flight while one is
+//    computed); the range check of the buffer descriptor turns rows past the sequence into
+//    zeros. The forward and dQ kernels are held to 256 registers per lane so that two
 //    workgroups share a compute unit: one wave's softmax runs beside the other's MFMAs.
 //    A tile is read either as rows (16-byte reads: MFMA fragments of q, k, v or dO) or, through
 //    the LDS transpose read ds_read_b64_tr_b16, as columns (fragments of v^T, k^T, q^T, dO^T),
@@ -44,9 +45,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_s4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
 
-__device__ uint4 attn_zero_page[4];
 
 template <int D>
 __device__ __forceinline__ int fsw(int r) {
@@ -57,22 +56,50 @@ __device__ __forceinline__ int tile_off(int r, int c) {  // element offset of (r
   return r * D + ((c ^ fsw<D>(r)) << 3);
 }
 
-// Per-wave direct-to-LDS loads of a [64][D] tile (rows row0.. of a strided global matrix). The
-// tile's D*128 bytes are split into 1 KB wave loads; wave w issues loads w, w+4, ...
+// Buffer descriptor of nbytes of global memory from p: a raw buffer load whose byte offset
+// reaches nbytes is out of range and returns zeros (the range check of raw buffer accesses).
+// Every field is uniform; readfirstlane keeps the compiler from building the descriptor in
+// vector registers (and looping over lanes to use it). Word 3: 32-bit data format, the value
+// for raw buffer accesses on this architecture family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* p, int nbytes) {
+  const int nrec = __builtin_amdgcn_readfirstlane(nbytes > 0 ? nbytes : 0);
+  const uintptr_t a = (uintptr_t)p;
+  const uintptr_t au = ((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)au, (short)0, nrec, 0x00020000);
+}
+// Rows [row0, row0 + nvalid) of a strided 16-bit matrix whose columns of interest start at g:
+// loads of rows at or past nvalid return zeros, which is how a sequence's partial last block
+// reads as zero rows. Each row's D columns end within its stride, so every in-range row is
+// whole.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* g, int stride, int row0,
+                                                          int nvalid) {
+  return span_rsrc((const char*)g + (size_t)row0 * stride * 2, nvalid * stride * 2);
+}
+
+// Per-wave direct-to-LDS loads of a [64][D] tile (rows row0.. of a strided global matrix; rows
+// at or past nvalid read as zeros). The tile's D*128 bytes are split into 1 KB wave loads; wave
+// w issues loads w, w+4, ... . Across a wave's loads a lane keeps the same row within the load
+// and the same swizzled chunk (the swizzle depends on the row mod 16, and the loads are 16 rows
+// apart for d = 128, 32 for d = 64), so its byte offsets differ by a constant and the base is
+// one descriptor in scalar registers.
 template <int D>
 __device__ __forceinline__ void tile_issue(bf16_t* tile, const bf16_t* g, int stride, int row0,
                                            int nvalid, int wave, int lane) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int RPL = 64 / CH;          // rows per 1 KB wave load
   constexpr int LOADS = 64 / RPL;       // wave loads per tile
+  constexpr int PW = LOADS / 4;         // loads per wave
+  static_assert((4 * RPL) % 16 == 0, "a wave's loads keep the row mod 16");
+  const int rl = wave * RPL + lane / CH;
+  const int c = (lane % CH) ^ fsw<D>(rl);
+  const uint32_t voff = (uint32_t)(rl * stride + c * 8) * 2u;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(g, stride, row0, nvalid);
 #pragma unroll
-  for (int q = wave; q < LOADS; q += 4) {
-    const int r = q * RPL + lane / CH;
-    const int c = (lane % CH) ^ fsw<D>(r);
-    const void* src = attn_zero_page;
-    if (r < nvalid) src = g + (size_t)(row0 + r) * stride + c * 8;
-    __builtin_amdgcn_global_load_lds((glob_void_t*)src, (lds_void_t*)(tile + q * 512), 16, 0, 0);
-  }
+  for (int j = 0; j < PW; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave + 4 * j) * 512), 16,
+                                             voff + (uint32_t)(j * 4 * RPL * stride * 2), 0, 0,
+                                             0);
 }
 template <int D> constexpr int tile_loads_per_wave() { return (64 / (64 / (D / 8))) / 4; }
 
@@ -124,6 +151,42 @@ __device__ __forceinline__ bf16x8_t t_read(const bf16_t* t, int d0, int ks, int 
   const int r1 = r0 + 8;
   const short4_t lo = tr_issue(t + tile_off<D>(r0, col >> 3) + (col & 7));
   const short4_t hi = tr_issue(t + tile_off<D>(r1, col >> 3) + (col & 7));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// The same column fragment from per-lane byte offsets computed once: the swizzle depends on the
+// row mod 16, so a k step (16 rows) moves both reads by 32 D bytes, which the instruction takes
+// as an immediate offset, and only the stage's base is added per block.
+template <int D>
+struct ColOffs {
+  uint32_t o[D / 32][2];
+  __device__ __forceinline__ explicit ColOffs(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int r0 = 4 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 4 * (i & 3);
+      o[db][0] = 2u * (uint32_t)(tile_off<D>(r0, col >> 3) + (col & 7));
+      o[db][1] = 2u * (uint32_t)(tile_off<D>(r0 + 8, col >> 3) + (col & 7));
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ short4_t tr_issue_ks(uint32_t addr, int ks) {
+  short4_t v;
+  switch (ks) {   // ks is a constant of the unrolled caller
+    case 0: asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr)); break;
+    case 1: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(32 * D)); break;
+    case 2: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(64 * D)); break;
+    default: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(96 * D)); break;
+  }
+  return v;
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t t_read_at(uint32_t tile, const ColOffs<D>& co, int db, int ks) {
+  const short4_t lo = tr_issue_ks<D>(tile + co.o[db][0], ks);
+  const short4_t hi = tr_issue_ks<D>(tile + co.o[db][1], ks);
   const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -234,6 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m2 = -INFINITY, l = 0.f;
+  const ColOffs<D> co(lane);
 
   const int q_last = min(S - 1, qb * 128 + 127);
   const int nkvb = q_last / 64 + 1;
@@ -273,8 +337,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
     // before the softmax, whose VALU work covers their latency; each later step's are read
     // while the previous step's MFMAs run
     bf16x8_t vt[2][NDB];
+    const uint32_t aV = lds_addr(sV);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vt[0][db] = t_read<D>(sV, db * 32, 0, lane);
+    for (int db = 0; db < NDB; ++db) vt[0][db] = t_read_at<D>(aV, co, db, 0);
     // the mask only on blocks that reach the diagonal or the end (one branch per block, not
     // one per score)
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
@@ -329,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
       const bf16x8_t pf = pack8<DT>(pv);
       if (ks < 3) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) vt[(ks + 1) & 1][db] = t_read<D>(sV, db * 32, ks + 1, lane);
+        for (int db = 0; db < NDB; ++db) vt[(ks + 1) & 1][db] = t_read_at<D>(aV, co, db, ks + 1);
         tr_wait_keep<2 * NDB>(vt[ks & 1]);     // two transpose reads per fragment
       } else {
         tr_wait(vt[ks & 1]);
@@ -438,6 +503,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
     qf[kk] = q < S ? *(const bf16x8_t*)(base + (size_t)q * QS + h * D + kk * 16 + hf * 8) : zero8();
     df[kk] = q < S ? *(const bf16x8_t*)(dobase + (size_t)q * OS + h * D + kk * 16 + hf * 8) : zero8();
   }
+  const ColOffs<D> co(lane);
   const float lse2 = q < S ? lse[((size_t)b * nq + h) * S + q] * kLog2e : 0.f;
   const float dl = q < S ? delta[((size_t)b * nq + h) * S + q] : 0.f;
 
@@ -505,7 +571,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
       const bf16x8_t sf = pack8<DT>(sv);
       bf16x8_t kt[NDB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) kt[db] = t_read<D>(sK, db * 32, ks, lane);
+      for (int db = 0; db < NDB; ++db) kt[db] = t_read_at<D>(lds_addr(sK), co, db, ks);
       tr_wait(kt);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -558,6 +624,7 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
     if constexpr (DK)
       vf[kk] = key < S ? *(const bf16x8_t*)(base + (size_t)key * QS + (nq + nkv + g) * D + kk * 16 + hf * 8) : zero8();
   }
+  const ColOffs<D> co(lane);
   f32x16_t acc[NDB];   // dK or dV, transposed: [d][key]
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -572,13 +639,13 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
     const int h = g * G + hh, q0 = jb * 64, nvalid = min(64, S - q0);
     tile_issue<D>(tQ(st), base + h * D, QS, q0, nvalid, wave, lane);
     tile_issue<D>(tO(st), dobase + h * D, OS, q0, nvalid, wave, lane);
-    // the block's log-sum-exp (wave 0) and D = rowsum(dO * O) (wave 1), 4 bytes per lane
+    // the block's log-sum-exp (wave 0) and D = rowsum(dO * O) (wave 1), 4 bytes per lane;
+    // queries past the sequence read zeros
     if (wave < 2) {
-      const float* src = (const float*)attn_zero_page;
-      if (q0 + lane < S)
-        src = (wave == 0 ? lse : delta) + ((size_t)b * nq + h) * S + q0 + lane;
-      __builtin_amdgcn_global_load_lds((glob_void_t*)src,
-                                       (lds_void_t*)(wave == 0 ? sL[st] : sDl[st]), 4, 0, 0);
+      const float* src = (wave == 0 ? lse : delta) + ((size_t)b * nq + h) * S + q0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(src, (S - q0) * 4),
+                                               (lds_void_t*)(wave == 0 ? sL[st] : sDl[st]), 4,
+                                               (uint32_t)lane * 4u, 0, 0, 0);
     }
   };
 #pragma unroll
@@ -619,10 +686,11 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
       const bf16_t* sT = DK ? sQ : sO;
       bf16x8_t tf0[NDB], tf1[NDB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) tf0[db] = t_read<D>(sT, db * 32, 2 * qb2, lane);
+      for (int db = 0; db < NDB; ++db) tf0[db] = t_read_at<D>(lds_addr(sT), co, db, 2 * qb2);
       if constexpr (!DK) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) tf1[db] = t_read<D>(sT, db * 32, 2 * qb2 + 1, lane);
+        for (int db = 0; db < NDB; ++db)
+          tf1[db] = t_read_at<D>(lds_addr(sT), co, db, 2 * qb2 + 1);
       }
       // element i is (query q0 + acc_key(qb2, i), this lane's key)
       if constexpr (DK) {
@@ -659,7 +727,8 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
       tr_wait(tf0);
       if constexpr (DK) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) tf1[db] = t_read<D>(sT, db * 32, 2 * qb2 + 1, lane);
+        for (int db = 0; db < NDB; ++db)
+          tf1[db] = t_read_at<D>(lds_addr(sT), co, db, 2 * qb2 + 1);
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
