@@ -37,6 +37,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// the forward's running maximum (log2 units) lags the true one by at most this much
+constexpr float kLazy = 8.0f;
 // LDS stages of the key (or query) block pipeline: two (64 KB at d = 128), so that two
 // workgroups (two waves per SIMD) fit a compute unit
 constexpr int NSTAGE = 2;
@@ -343,6 +345,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
     // the mask only on blocks that reach the diagonal or the end (one branch per block, not
     // one per score)
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S);
+    // The row maximum is taken over the raw scores and scaled once: the scale is positive and
+    // rounding is monotonic, so this is the maximum of the scaled scores, and the scale goes
+    // into each exponent's argument as a fused multiply-add.
     float mx = -INFINITY;
     if (need_mask) {
       // key kv0 + acc_key(kb, i, hf) is masked iff it is past min(q, S - 1); acc_key without
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float s = acc_key(kb, i, 0) > lim ? -INFINITY : sacc[kb][i] * sl2;
+          const float s = acc_key(kb, i, 0) > lim ? -INFINITY : sacc[kb][i];
           sacc[kb][i] = s;
           mx = fmaxf(mx, s);
         }
@@ -360,32 +365,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const bf16_t* __restri
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float s = sacc[kb][i] * sl2;
-          sacc[kb][i] = s;
-          mx = fmaxf(mx, s);
-        }
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     }
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m2, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m2 - m_use);
+    mx = halves_max(mx) * sl2;
+    // The reference maximum m2 of the exponents moves only when some lane's block maximum
+    // exceeds it by more than 2^kLazy: otherwise the weights exp2(s - m2) stay at most 2^kLazy
+    // (no overflow in fp32 or in the 16-bit P), and O and l keep their scale, so the rescale of
+    // O (64 products per lane) is skipped for the wave. O / l and the log-sum-exp m2 + log2 l
+    // do not depend on which reference is used. The first block always moves it (m2 = -inf).
+    if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazy) != 0) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = fast_exp2(m2 - (m_new == -INFINITY ? 0.f : m_new));
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m2 = m_new;
+    }
+    const float m_use = m2 == -INFINITY ? 0.f : m2;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sacc[kb][i] - m_use);
+        const float p = fast_exp2(fmaf(sacc[kb][i], sl2, -m_use));
         sacc[kb][i] = p;
         rs += p;
       }
-    rs = halves_sum(rs);
-    l = l * alpha + rs;
-    m2 = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l += halves_sum(rs);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float pv[8];
