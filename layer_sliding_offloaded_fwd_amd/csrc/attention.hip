@@ -453,7 +453,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
                                                          const T* __restrict__ dout,
-                                                         float* __restrict__ delta, int B, int S,
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ delta,
+                                                         float* __restrict__ lse2, int B, int S,
                                                          int nq) {
   constexpr int LPR = D / 8;
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -474,7 +476,9 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
     const size_t t = row / nq;
     const int h = (int)(row % nq);
     const int b = (int)(t / S), sp = (int)(t % S);
-    delta[((size_t)b * nq + h) * S + sp] = s;
+    const size_t at = ((size_t)b * nq + h) * S + sp;
+    delta[at] = s;
+    lse2[at] = lse[at] * kLog2e;
   }
 }
 
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                       const bf16_t* __restrict__ dout,
-                                                      const float* __restrict__ lse,
+                                                      const float* __restrict__ lse2v,
                                                       const float* __restrict__ delta,
                                                       bf16_t* __restrict__ dqkv, int S, int nq,
                                                       int nkv, float scale) {
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
     df[kk] = q < S ? *(const bf16x8_t*)(dobase + (size_t)q * OS + h * D + kk * 16 + hf * 8) : zero8();
   }
   const ColOffs<D> co(lane);
-  const float lse2 = q < S ? lse[((size_t)b * nq + h) * S + q] * kLog2e : 0.f;
+  const float lse2 = q < S ? lse2v[((size_t)b * nq + h) * S + q] : 0.f;
   const float dl = q < S ? delta[((size_t)b * nq + h) * S + q] : 0.f;
 
   f32x16_t dq[NDB];
@@ -557,20 +561,24 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
         pacc[kb] = mfma32<DT>(rows_read<D>(sV, kb * 32 + lr, kk * 2 + hf), df[kk], pacc[kb]);
       }
     }
-    // (a branch-free mask, as in the forward, measured 4% slower here: the compiler's schedule
-    // of this form is the better one at this register budget)
+    // The mask only in blocks on the diagonal or at the end of the sequence, as one branch per
+    // block that sets masked scores to -inf (exp2 gives 0; every dP is finite, rows past the end
+    // being zeros): key kv0 + acc_key(kb, i, hf) is masked iff it is past the query (which also
+    // covers keys past the end), and every key is masked for a query past the end.
     const bool need_mask = (kv0 + 63 > wq0) || (kv0 + 64 > S) || (wq0 + 32 > S);
+    if (need_mask) {
+      const int lim = (q < S ? q : -1) - kv0 - hf * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_key(kb, i, 0) > lim) sacc[kb][i] = -INFINITY;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(sacc[kb][i] * sl2 - lse2);
-        if (need_mask) {
-          const int key = kv0 + acc_key(kb, i, hf);
-          if (key > q || key >= S || q >= S) p = 0.f;
-        }
-        sacc[kb][i] = p * (pacc[kb][i] - dl);
-      }
+      for (int i = 0; i < 16; ++i)
+        sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], sl2, -lse2)) * (pacc[kb][i] - dl);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float sv[8];
@@ -605,7 +613,7 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
                                           int kblk, int g, int b,
                                           const bf16_t* __restrict__ qkv,
                                           const bf16_t* __restrict__ dout,
-                                          const float* __restrict__ lse,
+                                          const float* __restrict__ lse2,
                                           const float* __restrict__ delta,
                                           bf16_t* __restrict__ dqkv, int S, int nq, int nkv,
                                           float scale) {
@@ -647,10 +655,10 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
     const int h = g * G + hh, q0 = jb * 64, nvalid = min(64, S - q0);
     tile_issue<D>(tQ(st), base + h * D, QS, q0, nvalid, wave, lane);
     tile_issue<D>(tO(st), dobase + h * D, OS, q0, nvalid, wave, lane);
-    // the block's log-sum-exp (wave 0) and D = rowsum(dO * O) (wave 1), 4 bytes per lane;
-    // queries past the sequence read zeros
+    // the block's log-sum-exp in log2 units (wave 0) and D = rowsum(dO * O) (wave 1), 4 bytes
+    // per lane; queries past the sequence read zeros
     if (wave < 2) {
-      const float* src = (wave == 0 ? lse : delta) + ((size_t)b * nq + h) * S + q0;
+      const float* src = (wave == 0 ? lse2 : delta) + ((size_t)b * nq + h) * S + q0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(src, (S - q0) * 4),
                                                (lds_void_t*)(wave == 0 ? sL[st] : sDl[st]), 4,
                                                (uint32_t)lane * 4u, 0, 0, 0);
@@ -700,29 +708,39 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
         for (int db = 0; db < NDB; ++db)
           tf1[db] = t_read_at<D>(lds_addr(sT), co, db, 2 * qb2 + 1);
       }
-      // element i is (query q0 + acc_key(qb2, i), this lane's key)
+      // element i is (query q0 + acc_key(qb2, i), this lane's key). Query q0 + acc_key(qb2, i,
+      // hf) is masked iff it precedes this lane's key or is past the end: a compare pair and a
+      // select per score, only in the blocks on the diagonal or at the end of the sequence.
+      const int lo = key - q0 - hf * 4, hi = S - 1 - q0 - hf * 4;
       if constexpr (DK) {
-        // (the branch-free mask below spills here, at 256 registers, and measured 10% slower)
+        if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = acc_key(qb2, i, hf);
-          float p = fast_exp2(sacc[i] * sl2 - sL[st][ql] * kLog2e);
-          if (need_mask) {
-            const int qq = q0 + ql;
-            if (key > qq || qq >= S) p = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            const int ql = acc_key(qb2, i, hf), c = acc_key(qb2, i, 0);
+            float p = fast_exp2(fmaf(sacc[i], sl2, -sL[st][ql]));
+            p = (c < lo || c > hi) ? 0.f : p;
+            sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
           }
-          sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ql = acc_key(qb2, i, hf);
+            const float p = fast_exp2(fmaf(sacc[i], sl2, -sL[st][ql]));
+            sacc[i] = p * (pacc[i] - sDl[st][ql]);   // dS
+          }
         }
       } else {
-        // query q0 + acc_key(qb2, i, hf) is masked iff it precedes this lane's key or is past
-        // the end: one compare pair and select per score, selecting nothing off the diagonal
-        const int lo = key - q0 - hf * 4, hi = S - 1 - q0 - hf * 4;
+        if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = acc_key(qb2, i, hf);
-          const float p = fast_exp2(sacc[i] * sl2 - sL[st][ql] * kLog2e);
-          const int c = acc_key(qb2, i, 0);
-          sacc[i] = (c < lo || c > hi) ? 0.f : p;                    // P
+          for (int i = 0; i < 16; ++i) {
+            const int ql = acc_key(qb2, i, hf), c = acc_key(qb2, i, 0);
+            const float p = fast_exp2(fmaf(sacc[i], sl2, -sL[st][ql]));
+            sacc[i] = (c < lo || c > hi) ? 0.f : p;                    // P
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[i] = fast_exp2(fmaf(sacc[i], sl2, -sL[st][acc_key(qb2, i, hf)]));   // P
         }
       }
       float w[8];
@@ -765,7 +783,7 @@ __device__ __forceinline__ void dkv_block(bf16_t* smem, float (*sL)[64], float (
 template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
                                                            const bf16_t* __restrict__ dout,
-                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ lse2,
                                                            const float* __restrict__ delta,
                                                            bf16_t* __restrict__ dqkv, int S,
                                                            int nq, int nkv, float scale) {
@@ -776,10 +794,10 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const bf16_t* __restr
   const int kblk = (int)blockIdx.x / per, r = (int)blockIdx.x % per;
   const int mode = r & 1, g = (r >> 1) % nkv, b = (r >> 1) / nkv;
   if (mode == MODE_DK)
-    dkv_block<D, MODE_DK, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse, delta, dqkv, S, nq, nkv,
+    dkv_block<D, MODE_DK, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse2, delta, dqkv, S, nq, nkv,
                               scale);
   else
-    dkv_block<D, MODE_DV, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse, delta, dqkv, S, nq, nkv,
+    dkv_block<D, MODE_DV, DT>(smem, sL, sDl, kblk, g, b, qkv, dout, lse2, delta, dqkv, S, nq, nkv,
                               scale);
 }
 
@@ -931,20 +949,20 @@ void launch_fwd16(const void* qkv, void* o, float* lse, int B, int S, int nq, in
 }
 
 template <typename T>
-void launch_delta(const void* o, const void* dout, float* delta, int B, int S, int nq, int d,
-                  hipStream_t st) {
+void launch_delta(const void* o, const void* dout, const float* lse, float* delta, float* lse2,
+                  int B, int S, int nq, int d, hipStream_t st) {
   const size_t rows = (size_t)B * S * nq;
   dim3 grid((unsigned)((rows * (d / 8) + 255) / 256)), block(256);
   if (d == 128)
     hipLaunchKernelGGL((attn_delta_kernel<T, 128>), grid, block, 0, st, (const T*)o,
-                       (const T*)dout, delta, B, S, nq);
+                       (const T*)dout, lse, delta, lse2, B, S, nq);
   else
     hipLaunchKernelGGL((attn_delta_kernel<T, 64>), grid, block, 0, st, (const T*)o,
-                       (const T*)dout, delta, B, S, nq);
+                       (const T*)dout, lse, delta, lse2, B, S, nq);
 }
 
 template <int DT>
-int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv,
+int launch_bwd16(const void* qkv, const float* lse2, const void* dout, void* dqkv,
                  const float* delta, int B, int S, int nq, int nkv, int d, float scale,
                  hipStream_t st) {
   const bf16_t* q = (const bf16_t*)qkv;
@@ -954,10 +972,10 @@ int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv
     ProfScope ps("attn_bwd_dq", st);
     dim3 grid((unsigned)((S + 127) / 128 * nq * B)), block(256);
     if (d == 128)
-      hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+      hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
                          nq, nkv, scale);
     else
-      hipLaunchKernelGGL((attn_dq_kernel<64, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+      hipLaunchKernelGGL((attn_dq_kernel<64, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
                          nq, nkv, scale);
   }
   SLIDE_TRY(check_launch("attn_bwd_dq"));
@@ -965,10 +983,10 @@ int launch_bwd16(const void* qkv, const float* lse, const void* dout, void* dqkv
     ProfScope ps("attn_bwd_dkv", st);
     dim3 grid((unsigned)((S + 127) / 128 * 2 * nkv * B)), block(256);
     if (d == 128)
-      hipLaunchKernelGGL((attn_dkdv_kernel<128, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+      hipLaunchKernelGGL((attn_dkdv_kernel<128, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
                          nq, nkv, scale);
     else
-      hipLaunchKernelGGL((attn_dkdv_kernel<64, DT>), grid, block, 0, st, q, g, lse, delta, out, S,
+      hipLaunchKernelGGL((attn_dkdv_kernel<64, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
                          nq, nkv, scale);
   }
   return check_launch("attn_bwd_dkv");
@@ -995,22 +1013,24 @@ int attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, in
   return check_launch("attn_fwd");
 }
 
-size_t attention_bwd_ws(int B, int S, int nq) { return align_up((size_t)B * nq * S * 4, 256); }
+// D = rowsum(dO * O) and the log-sum-exps in log2 units, fp32 [B, nq, S] each
+size_t attention_bwd_ws(int B, int S, int nq) { return 2 * align_up((size_t)B * nq * S * 4, 256); }
 
 int attention_bwd(const void* qkv, const void* o, const float* lse, const void* dout, void* dqkv,
                   int B, int S, int nq, int nkv, int d, int dtype, void* ws, hipStream_t st) {
   if (B == 0 || S == 0) return SLIDE_OK;
   float* delta = (float*)ws;
+  float* lse2 = (float*)((char*)ws + attention_bwd_ws(B, S, nq) / 2);
   const float scale = 1.0f / sqrtf((float)d);
   {
     ProfScope ps("attn_delta", st);
-    SLIDE_DISPATCH(dtype, T, launch_delta<T>(o, dout, delta, B, S, nq, d, st));
+    SLIDE_DISPATCH(dtype, T, launch_delta<T>(o, dout, lse, delta, lse2, B, S, nq, d, st));
   }
   SLIDE_TRY(check_launch("attn_delta"));
   if (dtype == SLIDE_BF16)
-    return launch_bwd16<SLIDE_BF16>(qkv, lse, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
+    return launch_bwd16<SLIDE_BF16>(qkv, lse2, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
   if (dtype == SLIDE_F16)
-    return launch_bwd16<SLIDE_F16>(qkv, lse, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
+    return launch_bwd16<SLIDE_F16>(qkv, lse2, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
   {
     ProfScope ps("attn_bwd_dq", st);
     dim3 grid((S + 63) / 64, nq, B), block(64);
