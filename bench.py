@@ -72,7 +72,8 @@ def kernel_bytes(spec, B, S):
             "swiglu_fwd": 3 * N * F * 2, "swiglu_bwd": 5 * N * F * 2,
             "rope_fwd": 2 * N * (QR - spec.n_kv_heads * d) * 2,
             "rope_bwd": 2 * N * (QR - spec.n_kv_heads * d) * 2,
-            "attn_delta": 2 * N * OD * 2 + N * spec.n_heads * 4}
+            # O and dO read; per query and head D written, lse read, lse * log2(e) written
+            "attn_delta": 2 * N * OD * 2 + N * spec.n_heads * 12}
 
 
 def cpu_baseline(w, B1=2, S1=1024, n_ce=1024, ad_frac=1.0):

@@ -57,7 +57,7 @@ def test_hbm_bytes_of_the_memory_bound_kernels():
     assert b["swiglu_fwd"] == 3 * N * F * 2                  # read g, u; write m
     assert b["swiglu_bwd"] == 5 * N * F * 2                  # read dm, g, u; write dg, du
     assert b["rope_fwd"] == 2 * N * 40 * 128 * 2             # q and k heads, read and written
-    assert b["attn_delta"] == 2 * N * 4096 * 2 + N * 32 * 4
+    assert b["attn_delta"] == 2 * N * 4096 * 2 + N * 32 * 12
 
 
 def test_step_host_bytes():
