@@ -279,20 +279,42 @@ __global__ __launch_bounds__(64) void rmsnorm_dw_partial_kernel(const T* __restr
   V8<float>::store(part + (size_t)blockIdx.y * H + j, acc);
 }
 
-// Sum of nparts rows of H floats, per column: 64 columns per workgroup, the parts split over 4
-// slices (slice s takes parts s, s + 4, ...), combined in slice order (deterministic).
+// Sum of nparts rows of H floats (H a multiple of 4), per column: 64 columns per workgroup as 16
+// groups of 4 (16-byte loads); the parts split over 16 slices (slice s takes parts s, s + 16,
+// ..., with up to 8 loads in flight per thread, summed in increasing part order), the slices
+// combined in slice order: the result is deterministic.
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, T* out,
                                                           int nparts, int H) {
-  __shared__ float red[4][64];
-  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + c;
-  float acc = 0.f;
-  if (j < H)
-    for (int p = sl; p < nparts; p += 4) acc += part[(size_t)p * H + j];
-  red[sl][c] = acc;
+  __shared__ float red[16][64];
+  const int cg = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int j = blockIdx.x * 64 + cg * 4;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < H) {
+    for (int p0 = sl; p0 < nparts; p0 += 16 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p0 + 16 * u < nparts) v[u] = *(const float4*)(part + (size_t)(p0 + 16 * u) * H + j);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p0 + 16 * u < nparts) {
+          a[0] += v[u].x;
+          a[1] += v[u].y;
+          a[2] += v[u].z;
+          a[3] += v[u].w;
+        }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[sl][cg * 4 + e] = a[e];
   __syncthreads();
-  if (sl == 0 && j < H) Elem<T>::store(out + j, ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
+  if (threadIdx.x < 64 && blockIdx.x * 64 + (int)threadIdx.x < H) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][threadIdx.x];
+    Elem<T>::store(out + blockIdx.x * 64 + threadIdx.x, t);
+  }
 }
 
 // ---------------------------------------------------------------- RoPE
