@@ -382,6 +382,12 @@ int slide_gpu_adamw(float* p, const void* g, int g_dtype, float* m, float* v,
  * fp32 master weights (summary, section 2B: FP32 -> BF16/FP16 conversion in the shared host
  * buffers). SLIDE_E_ARG for a null pointer or another dtype. Blocks until done. */
 int slide_cpu_convert_f32(const float* src, void* dst, int dst_dtype, size_t n, int n_threads);
+/* The same conversion on the GPU, for 16-bit copies of fp32 weights that already live in HBM
+ * (the optimizer-resident baseline): src fp32 [n] and dst [n] in dst_dtype (SLIDE_BF16 or
+ * SLIDE_F16) device memory, rounded to nearest-even (the bits of slide_cpu_convert_f32 for every
+ * non-NaN input; NaN stays NaN). Asynchronous on `stream`; SLIDE_E_ARG for a null pointer with
+ * n > 0 or another dtype. */
+int slide_convert_f32(const float* src, void* dst, int dst_dtype, size_t n, void* stream);
 
 /* The host-DRAM roofline of the CPU optimizer (summary, section 2B: the optimizer state lives
  * in host memory, so the update of a layer is bound by host memory bandwidth): a STREAM triad

@@ -97,6 +97,7 @@ SIGNATURES = {
                                  ctypes.POINTER(AdamWHp), I]),
     "slide_gpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), P]),
     "slide_cpu_convert_f32": (I, [P, P, I, SZ, I]),
+    "slide_convert_f32": (I, [P, P, I, SZ, P]),
     "slide_host_triad": (I, [SZ, I, I, ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_double)]),
     "slide_nonfinite_count": (I, [P, I, SZ, P, P]),

@@ -24,7 +24,7 @@ __all__ = [
     "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows",
-    "slide_cpu_adamw_rows_packed", "slide_copy_rows", "slide_gpu_adamw",
+    "slide_cpu_adamw_rows_packed", "slide_copy_rows", "slide_gpu_adamw", "slide_convert_f32",
     "slide_cpu_convert_f32", "slide_host_triad", "StateTier",
     "slide_tier_region_bytes",
     "slide_nonfinite_count",
@@ -328,6 +328,11 @@ def slide_gpu_adamw(p, g, g_dtype, m, v, p_bf16_out, n, step, hp, stream=None):
 def slide_cpu_convert_f32(src, dst, dst_dtype, n, n_threads=0):
     """fp32 host array -> bf16 / fp16 bit patterns (round to nearest-even)."""
     call("slide_cpu_convert_f32", _p(src), _p(dst), dst_dtype, n, n_threads)
+
+
+def slide_convert_f32(src, dst, dst_dtype, n, stream=None):
+    """fp32 device tensor -> bf16 / fp16 device tensor (round to nearest-even), on stream."""
+    call("slide_convert_f32", _p(src), _p(dst), dst_dtype, n, _s(stream))
 
 
 def slide_host_triad(n, n_threads=0, reps=3):

@@ -432,6 +432,15 @@ extern "C" int slide_copy_rows(const void* src, const int32_t* src_rows, int64_t
                    (hipStream_t)stream);
 }
 
+extern "C" int slide_convert_f32(const float* src, void* dst, int dst_dtype, size_t n,
+                                 void* stream) {
+  SLIDE_REQUIRE(dst_dtype == SLIDE_BF16 || dst_dtype == SLIDE_F16, SLIDE_E_ARG,
+                "convert_f32: dst_dtype %d is not a 16-bit type", dst_dtype);
+  if (n == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(src && dst, SLIDE_E_ARG, "convert_f32: null pointer");
+  return convert_from_f32(src, dst, n, dst_dtype, (hipStream_t)stream);
+}
+
 extern "C" size_t slide_embed_bwd_workspace_bytes(int N, int V) { return embed_bwd_ws(N < 0 ? 0 : N, V); }
 
 extern "C" int slide_embed_bwd(const void* dx, const int32_t* tokens, void* dE, int N, int H, int V,

@@ -514,6 +514,10 @@ __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
+__global__ void fill_u16_kernel(uint16_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 template <typename T>
 __global__ void convert_f32_kernel(const float* __restrict__ src, T* __restrict__ dst, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -728,9 +732,10 @@ int fill_zero(void* p, size_t n, int dtype, hipStream_t st) {
   if (n == 0) return SLIDE_OK;
   if (dtype != SLIDE_F32) {
     // a 16-bit zero is the all-zero bit pattern: fill as fp32 words plus a possible odd tail
-    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n / 2, 256)), dim3(256), 0, st, (float*)p, n / 2, 0.f);
+    if (n >= 2)
+      hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n / 2, 256)), dim3(256), 0, st, (float*)p, n / 2, 0.f);
     if (n & 1)
-      hipLaunchKernelGGL(convert_f32_kernel<bf16_t>, dim3(1), dim3(1), 0, st, (const float*)p, (bf16_t*)p + (n - 1), (size_t)1);
+      hipLaunchKernelGGL(fill_u16_kernel, dim3(1), dim3(1), 0, st, (uint16_t*)p + (n - 1), (size_t)1);
   } else {
     hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, (float*)p, n, 0.f);
   }

@@ -87,12 +87,14 @@ class ResidentTrainer:
 
     # ------------------------------------------------------------------ parameters
     def _set(self, blk, t, row=None):
-        """fp32 master of a block (or of one layer row) and its compute copy."""
+        """fp32 master of a block (or of one layer row) and its compute copy, rounded by the
+        library (the offloaded engine rounds its copies with the same rule on the host)."""
         dst_m = blk.master if row is None else blk.master[row]
         dst_m.copy_(t.reshape(dst_m.shape))
         if self.spec.dtype == "bf16":
             dst = blk.dev if row is None else blk.dev[row]
-            dst.copy_(dst_m.to(torch.bfloat16))
+            B.slide_convert_f32(dst_m, dst, self.code, blk.n,
+                                torch.cuda.current_stream(self.device))
 
     def load_params(self, embed, layers, w_final, lm_head):
         """fp32 master weights (numpy or torch; layers in slot packing order); moments and the

@@ -256,3 +256,35 @@ def test_nonfinite_count_exact(dtype, n):
     torch.cuda.synchronize()
     print(f"  count {int(cnt.item())} expected {want}", flush=True)
     assert int(cnt.item()) == want
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_convert_f32_matches_oracle_rounding(dtype):
+    """The GPU fp32 -> 16-bit conversion rounds to nearest-even exactly as the oracle's rounding
+    and the host conversion do, for every non-NaN input: random bit patterns cover every exponent
+    (subnormals and overflow to infinity included), plus signed zeros, infinities, ties and the
+    half-precision limits; NaN stays NaN. The length spans many workgroups with a ragged tail."""
+    print(f"convert_f32 {dtype}", flush=True)
+    from oracle import adamw as oa
+    code = sl.dtype_code(dtype)
+    rng = np.random.default_rng(11)
+    n = 70_001
+    x = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.float32).copy()
+    special = [0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.4e38, -3.4e38, 1e-40, -1e-45, 65504.0,
+               65520.0, 1.00390625, 1.01171875, 1.0 + 2.0**-11, np.nan]
+    x[:len(special)] = np.array(special, np.float32)
+    ref = oa.bf16_round_bits(x) if dtype == "bf16" else oa.f16_round_bits(x)
+    host_out = np.zeros(n, np.uint16)
+    sl.slide_cpu_convert_f32(x, host_out, code, n, 4)
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    sl.slide_convert_f32(torch.from_numpy(x).to(DEV), out, code, n, stream())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    nan_in = np.isnan(x)
+    exp_mask, man_mask = (0x7F80, 0x007F) if dtype == "bf16" else (0x7C00, 0x03FF)
+    got_nan = ((got & exp_mask) == exp_mask) & ((got & man_mask) != 0)
+    assert np.array_equal(got_nan, nan_in)
+    assert np.array_equal(got[~nan_in], ref[~nan_in])
+    assert np.array_equal(got[~nan_in], host_out[~nan_in])
+    with pytest.raises(sl.SlideError):
+        sl.slide_convert_f32(torch.from_numpy(x).to(DEV), out, sl.SLIDE_F32, n, stream())
