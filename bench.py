@@ -171,6 +171,11 @@ def _parse():
     ap.add_argument("--embed-split", action="store_true",
                     help="update the embedding's rows that no token selects during the step and "
                          "only the selected rows after the backward")
+    ap.add_argument("--gap-ms", type=float, default=0.0,
+                    help="layer-kernels-8b only: leave the GPU idle this long after each layer "
+                         "(the host-bound step's duty cycle: the GPU waits on the CPU between "
+                         "layers); the kernel table then shows the kernels at the clocks such "
+                         "a duty cycle runs at, and ms_per_step is the kernels' sum")
     ap.add_argument("--adam-threads", type=int, default=0,
                     help="CPU AdamW threads (default: cores - 3, leaving cores to the engine thread and the HIP runtime)")
     return ap.parse_args()
@@ -922,6 +927,9 @@ def run_layer_kernels(args):
     e0.record(st)
     for _ in range(args.steps):
         one()
+        if args.gap_ms > 0:
+            torch.cuda.synchronize()
+            time.sleep(args.gap_ms * 1e-3)
     e1.record(st)
     torch.cuda.synchronize()
     sl.slide_prof_enable(False)
@@ -932,6 +940,8 @@ def run_layer_kernels(args):
     kernels = _kernel_table(sl.slide_prof_read(), alg, exe, kernel_bytes(spec, Bb, S))
     lt = sum(k["total_ms"] for n, k in kernels.items() if n in alg) * 1e-3
     l_alg = sum(alg[n] * k["launches"] for n, k in kernels.items() if n in alg)
+    if args.gap_ms > 0:   # the idle gaps are not the layer's time
+        ms = sum(k["total_ms"] for k in kernels.values()) / args.steps
     # the calibration copy: 1 GiB read and 1 GiB written by the runtime's copy kernel
     del saved, ws
     nbytes = 1 << 30
@@ -957,7 +967,7 @@ def run_layer_kernels(args):
         "data": "synthetic",
         "config": {"workload": "layer-kernels-8b", "hidden": c.hidden, "heads": c.n_heads,
                    "kv_heads": c.n_kv_heads, "head_dim": c.head_dim, "ffn": c.ffn,
-                   "global_batch": Bb, "seq_len": S},
+                   "global_batch": Bb, "seq_len": S, "idle_gap_ms": args.gap_ms},
         "layer_mfma_util_pct": round(100 * l_alg / lt / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": _roofline(kernels, alg, profiled=_is_profiled_launch(c, Bb * S, args.dtype)),
         "kernels": kernels,
