@@ -134,11 +134,13 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3-8b-shaped",
                     choices=["llama3-8b-shaped", "123b-shaped-slice", "lmhead-ce-128k",
-                             "critical-batch-sweep", "layer-kernels-8b"],
+                             "critical-batch-sweep", "layer-kernels-8b", "host-link-engines"],
                     help="llama3-8b-shaped (default: the headline step), 123b-shaped-slice, "
                          "lmhead-ce-128k (the chunked CE alone), critical-batch-sweep, "
                          "layer-kernels-8b (one 8B-shaped layer's kernels alone, plus a 1 GiB "
-                         "device copy that calibrates HBM byte counters)")
+                         "device copy that calibrates HBM byte counters), host-link-engines (one "
+                         "8B layer's bytes over the host link on each copy engine, and through "
+                         "hipMemcpyAsync)")
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences of 1024 tokens per step of the llama3-8b-shaped workload "
                          "(default 8); at the critical batch the CPU updates hide behind the "
@@ -976,6 +978,53 @@ def run_layer_kernels(args):
     }
 
 
+def run_host_link_engines(args):
+    """One 8B layer's bf16 weights (436 MB) between pinned host memory and HBM on each of the
+    GPU's copy engines, both directions, against hipMemcpyAsync on a side stream (the slot ring's
+    copies): the host link's rate depends on the engine a copy lands on."""
+    import torch
+    import layer_sliding_offloaded_fwd_amd as sl
+    from seeded_inputs import L8B
+    c = L8B.layer
+    cfg = sl.layer_cfg(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, "bf16")
+    nbytes = sl.slide_layer_param_count(cfg) * 2
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dev.fill_(1)
+    host.fill_(2)
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    d2h, h2d, info = sl.slide_host_link_engine_rates(dev, host, nbytes, reps)
+    s = torch.cuda.Stream()
+    rt = {}
+    for name, dst, src in (("d2h", host, dev), ("h2d", dev, host)):
+        best = 1e30
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record(s)
+                dst.copy_(src, non_blocking=True)
+                e1.record(s)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        rt[name] = best
+    eng = {e: {"d2h_ms": round(d2h[e], 3), "h2d_ms": round(h2d[e], 3),
+               "d2h_gbs": round(nbytes / d2h[e] / 1e6, 1) if d2h[e] > 0 else None,
+               "h2d_gbs": round(nbytes / h2d[e] / 1e6, 1) if h2d[e] > 0 else None}
+           for e in range(32) if d2h[e] > 0 or h2d[e] > 0}
+    for e, r in eng.items():
+        print(f"[bench] engine {e:2d}: d2h {r['d2h_ms']:7.2f} ms ({r['d2h_gbs']} GB/s)  "
+              f"h2d {r['h2d_ms']:7.2f} ms ({r['h2d_gbs']} GB/s)", file=sys.stderr, flush=True)
+    return {"metric": "host-link copy time per copy engine (1 GPU)", "unit": "ms",
+            "value": round(rt["d2h"], 3), "n_gpus": 1, "steps": reps, "warmup": 0,
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+            "data": "synthetic",
+            "config": {"workload": "host-link-engines", "bytes_per_copy": nbytes},
+            "engines": eng, "n_host_optimized_engines": info[0], "n_xgmi_engines": info[1],
+            "preferred_mask_d2h": hex(info[2]), "preferred_mask_h2d": hex(info[3]),
+            "hipMemcpyAsync_ms": {k: round(v, 3) for k, v in rt.items()}}
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -998,6 +1047,9 @@ def main():
         return
     if args.workload == "layer-kernels-8b":
         print(json.dumps(run_layer_kernels(args)))
+        return
+    if args.workload == "host-link-engines":
+        print(json.dumps(run_host_link_engines(args)))
         return
     if args.workload == "123b-shaped-slice":
         layers = args.layers or L123B.n_layers

@@ -305,6 +305,18 @@ int slide_slot_ring_state(slide_ring* r, int slot, int* state, int* layer);
 /* Find the slot currently holding `layer` (LOADING / IN_USE / FLUSHING), or -1. */
 int slide_slot_ring_find(slide_ring* r, int layer, int* slot_out);
 int slide_slot_ring_destroy(slide_ring* r);
+
+/* Host-link diagnostic (summary, section 2A: layers and gradients cross the host link
+ * asynchronously; the ring's copies run on whichever copy engine the runtime picks): the best of
+ * `reps` times (ms) of one nbytes copy between `dev` (device memory) and `host` (pinned host
+ * memory) on each copy engine of the GPU, device to host into d2h_ms[e] and host to device into
+ * h2d_ms[e] for engine e < 32 (-1 where an engine is absent or refuses). info4 receives the
+ * number of host-optimized engines, the number of engines optimized for copies between GPUs,
+ * and the runtime's preferred engine masks for device to host and host to device. Overwrites
+ * both buffers; synchronizes the device first and blocks until done. SLIDE_E_ARG for null or
+ * unpinned buffers, SLIDE_E_TIMEOUT if a copy does not finish within its bound. */
+int slide_host_link_engine_rates(void* dev, void* host, size_t nbytes, int reps, double* d2h_ms,
+                                 double* h2d_ms, uint32_t* info4);
 /* Host engine only: make the next `count` copies fail (fail_mode 1) or never complete
  * (fail_mode 2). Returns SLIDE_E_UNSUPPORTED for the HIP engine. */
 int slide_slot_ring_inject_fault(slide_ring* r, int fail_mode, int count);

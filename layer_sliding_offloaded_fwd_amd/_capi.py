@@ -97,6 +97,9 @@ SIGNATURES = {
                                  ctypes.POINTER(AdamWHp), I]),
     "slide_gpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), P]),
     "slide_cpu_convert_f32": (I, [P, P, I, SZ, I]),
+    "slide_host_link_engine_rates": (I, [P, P, SZ, I, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_uint32)]),
     "slide_convert_f32": (I, [P, P, I, SZ, P]),
     "slide_host_triad": (I, [SZ, I, I, ctypes.POINTER(ctypes.c_double),
                              ctypes.POINTER(ctypes.c_double)]),

@@ -25,6 +25,7 @@ __all__ = [
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows",
     "slide_cpu_adamw_rows_packed", "slide_copy_rows", "slide_gpu_adamw", "slide_convert_f32",
+    "slide_host_link_engine_rates",
     "slide_cpu_convert_f32", "slide_host_triad", "StateTier",
     "slide_tier_region_bytes",
     "slide_nonfinite_count",
@@ -333,6 +334,16 @@ def slide_cpu_convert_f32(src, dst, dst_dtype, n, n_threads=0):
 def slide_convert_f32(src, dst, dst_dtype, n, stream=None):
     """fp32 device tensor -> bf16 / fp16 device tensor (round to nearest-even), on stream."""
     call("slide_convert_f32", _p(src), _p(dst), dst_dtype, n, _s(stream))
+
+
+def slide_host_link_engine_rates(dev, host, nbytes, reps=3):
+    """Per copy engine: best time (ms) of an nbytes copy device -> host and host -> device
+    between `dev` (device tensor) and `host` (pinned tensor); -1 where absent. Returns
+    (d2h_ms[32], h2d_ms[32], (n_host_engines, n_xgmi_engines, pref_d2h_mask, pref_h2d_mask))."""
+    d2h, h2d = (ctypes.c_double * 32)(), (ctypes.c_double * 32)()
+    info = (ctypes.c_uint32 * 4)()
+    call("slide_host_link_engine_rates", _p(dev), _p(host), nbytes, reps, d2h, h2d, info)
+    return list(d2h), list(h2d), tuple(info)
 
 
 def slide_host_triad(n, n_threads=0, reps=3):

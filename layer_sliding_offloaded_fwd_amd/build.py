@@ -20,7 +20,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "pointwise.hip", "ce.hip", "layer.hip",
                "adamw_gpu.hip"]
-HIP_HOST_SOURCES = ["common.cpp", "ring.cpp"]   # host code that calls the HIP runtime
+HIP_HOST_SOURCES = ["common.cpp", "ring.cpp", "linkprobe.cpp"]   # host code on the HIP runtime
 CPU_SOURCES = ["adamw.cpp", "tier.cpp"]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -59,7 +59,8 @@ def build(verbose=False, jobs=None):
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread"])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread",
+          "-lhsa-runtime64"])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -288,3 +288,23 @@ def test_convert_f32_matches_oracle_rounding(dtype):
     assert np.array_equal(got[~nan_in], host_out[~nan_in])
     with pytest.raises(sl.SlideError):
         sl.slide_convert_f32(torch.from_numpy(x).to(DEV), out, sl.SLIDE_F32, n, stream())
+
+
+def test_host_link_engine_rates_time_every_engine():
+    """The host-link diagnostic times a copy on every copy engine in both directions (16 MB),
+    reports the engine counts and preferred masks, moves the bytes it claims to (the host buffer
+    ends up holding the device bytes after the device-to-host copies) and refuses unpinned host
+    memory."""
+    print("host_link_engine_rates 16 MB", flush=True)
+    n = 16 << 20
+    dev = torch.full((n,), 7, dtype=torch.uint8, device=DEV)
+    host = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
+    d2h, h2d, info = sl.slide_host_link_engine_rates(dev, host, n, 1)
+    timed = [e for e in range(32) if d2h[e] > 0 and h2d[e] > 0]
+    assert len(timed) >= 1 and info[0] + info[1] >= len(timed)
+    assert all(t == -1.0 for e, t in enumerate(d2h) if e not in timed and h2d[e] < 0)
+    if info[2]:
+        assert any(info[2] >> e & 1 for e in timed)
+    assert bool(torch.all(host == 7))   # the last copy before the h2d pass was device -> host
+    with pytest.raises(sl.SlideError):
+        sl.slide_host_link_engine_rates(dev, np.zeros(n, np.uint8), n, 1)
