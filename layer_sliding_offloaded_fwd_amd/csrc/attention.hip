@@ -26,7 +26,8 @@
 //    the query blocks on or after the diagonal, so dK and dV are summed without atomics (the
 //    result is deterministic). dQ runs as its own kernel. Every grid is flat and ordered
 //    heaviest block first.
-//  * D_i = rowsum(dO_i * O_i) is precomputed by a small kernel.
+//  * D_i = rowsum(dO_i * O_i) is formed in the dQ kernel's prologue (which holds the dO rows) and
+//    written, with the log-sum-exps in log2 units, for the dK/dV kernel.
 // fp32 path (the small fp32 configuration): straightforward SIMT kernels, one thread per query
 // (forward, dQ) or per key (dK/dV).
 #include "attention.h"
@@ -486,8 +487,10 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 template <int D, int DT>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                       const bf16_t* __restrict__ dout,
-                                                      const float* __restrict__ lse2v,
-                                                      const float* __restrict__ delta,
+                                                      const bf16_t* __restrict__ o,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ delta_out,
+                                                      float* __restrict__ lse2_out,
                                                       bf16_t* __restrict__ dqkv, int S, int nq,
                                                       int nkv, float scale) {
   constexpr int NKK = D / 16, NDB = D / 32, PER = 2 * tile_loads_per_wave<D>();
@@ -516,8 +519,28 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const bf16_t* __restric
     df[kk] = q < S ? *(const bf16x8_t*)(dobase + (size_t)q * OS + h * D + kk * 16 + hf * 8) : zero8();
   }
   const ColOffs<D> co(lane);
-  const float lse2 = q < S ? lse2v[((size_t)b * nq + h) * S + q] : 0.f;
-  const float dl = q < S ? delta[((size_t)b * nq + h) * S + q] : 0.f;
+  // D = rowsum(dO * O) of this lane's query: the lane holds half of its dO row (d = 16 kk + 8 hf
+  // .. + 7), reads O at the same places, and the lane 32 away adds the other half. D and the
+  // log-sum-exp in log2 units go to the workspace for the dK/dV kernel, which runs after this.
+  float dsum = 0.f;
+  if (q < S) {
+    const bf16_t* orow = o + ((size_t)b * S + q) * OS + h * D + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const auto ov = __builtin_bit_cast(short8_t, *(const bf16x8_t*)(orow + kk * 16));
+      const auto dv = __builtin_bit_cast(short8_t, df[kk]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dsum += Bits16<DT>::to_f((uint16_t)ov[i]) * Bits16<DT>::to_f((uint16_t)dv[i]);
+    }
+  }
+  const float dl = halves_sum(dsum);
+  const size_t at = ((size_t)b * nq + h) * S + q;
+  const float lse2 = q < S ? lse[at] * kLog2e : 0.f;
+  if (hf == 0 && q < S) {
+    delta_out[at] = dl;
+    lse2_out[at] = lse2;
+  }
 
   f32x16_t dq[NDB];
 #pragma unroll
@@ -962,8 +985,8 @@ void launch_delta(const void* o, const void* dout, const float* lse, float* delt
 }
 
 template <int DT>
-int launch_bwd16(const void* qkv, const float* lse2, const void* dout, void* dqkv,
-                 const float* delta, int B, int S, int nq, int nkv, int d, float scale,
+int launch_bwd16(const void* qkv, const void* o, const float* lse, const void* dout, void* dqkv,
+                 float* delta, float* lse2, int B, int S, int nq, int nkv, int d, float scale,
                  hipStream_t st) {
   const bf16_t* q = (const bf16_t*)qkv;
   const bf16_t* g = (const bf16_t*)dout;
@@ -972,11 +995,11 @@ int launch_bwd16(const void* qkv, const float* lse2, const void* dout, void* dqk
     ProfScope ps("attn_bwd_dq", st);
     dim3 grid((unsigned)((S + 127) / 128 * nq * B)), block(256);
     if (d == 128)
-      hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
-                         nq, nkv, scale);
+      hipLaunchKernelGGL((attn_dq_kernel<128, DT>), grid, block, 0, st, q, g,
+                         (const bf16_t*)o, lse, delta, lse2, out, S, nq, nkv, scale);
     else
-      hipLaunchKernelGGL((attn_dq_kernel<64, DT>), grid, block, 0, st, q, g, lse2, delta, out, S,
-                         nq, nkv, scale);
+      hipLaunchKernelGGL((attn_dq_kernel<64, DT>), grid, block, 0, st, q, g, (const bf16_t*)o,
+                         lse, delta, lse2, out, S, nq, nkv, scale);
   }
   SLIDE_TRY(check_launch("attn_bwd_dq"));
   {
@@ -1022,15 +1045,18 @@ int attention_bwd(const void* qkv, const void* o, const float* lse, const void* 
   float* delta = (float*)ws;
   float* lse2 = (float*)((char*)ws + attention_bwd_ws(B, S, nq) / 2);
   const float scale = 1.0f / sqrtf((float)d);
+  // 16-bit: the dQ kernel forms D and the log2-unit log-sum-exps itself
+  if (dtype == SLIDE_BF16)
+    return launch_bwd16<SLIDE_BF16>(qkv, o, lse, dout, dqkv, delta, lse2, B, S, nq, nkv, d,
+                                    scale, st);
+  if (dtype == SLIDE_F16)
+    return launch_bwd16<SLIDE_F16>(qkv, o, lse, dout, dqkv, delta, lse2, B, S, nq, nkv, d, scale,
+                                   st);
   {
     ProfScope ps("attn_delta", st);
     SLIDE_DISPATCH(dtype, T, launch_delta<T>(o, dout, lse, delta, lse2, B, S, nq, d, st));
   }
   SLIDE_TRY(check_launch("attn_delta"));
-  if (dtype == SLIDE_BF16)
-    return launch_bwd16<SLIDE_BF16>(qkv, lse2, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
-  if (dtype == SLIDE_F16)
-    return launch_bwd16<SLIDE_F16>(qkv, lse2, dout, dqkv, delta, B, S, nq, nkv, d, scale, st);
   {
     ProfScope ps("attn_bwd_dq", st);
     dim3 grid((S + 63) / 64, nq, B), block(64);
