@@ -5,7 +5,7 @@ import numpy as np
 import torch
 
 DEV = "cuda:0"
-# fp16 (not stated by the pages or the task): the bf16 bound scaled by the ratio of the unit
+# fp16 (not stated by the pages): the bf16 bound scaled by the ratio of the unit
 # roundoffs, 2^-11 / 2^-8 = 1/8, since every rounding point is the same and only the format
 # changes
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2.5e-3}
