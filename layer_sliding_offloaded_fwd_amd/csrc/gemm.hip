@@ -305,18 +305,20 @@ __global__ __launch_bounds__(TL::NT, 1) void gemm_bf16_kernel(GemmArgs g) {
 // dW) runs this kernel.
 namespace pipe {
 
-constexpr int BM = 256, BN = 256;
-
-// NT threads in a WGM x (waves / WGM) wave grid; NS stages of BK-deep k-tiles in LDS
-// (BK = 32: 32 KB per stage, BK = 64: 64 KB).
-template <int NT_, int WGM_, int NS_, int BK_>
+// BM x BN output tiles computed by NT threads in a WGM x (waves / WGM) wave grid; NS stages of
+// BK-deep k-tiles of both operands in LDS ((BM + BN) * BK * 2 bytes a stage); MINB workgroups
+// share a compute unit.
+template <int NT_, int WGM_, int NS_, int BK_, int BM_ = 256, int BN_ = 256, int MINB_ = 1>
 struct PCfg {
+  static constexpr int BM = BM_, BN = BN_, MINB = MINB_;
   static constexpr int NT = NT_, NW = NT / 64, WGM = WGM_, WGN = NW / WGM, NS = NS_, BK = BK_;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 32, NJ = WTN / 32;
-  static constexpr int SE = 256 * BK;         // elements per operand and stage
-  static constexpr int LPS = BK / NW;         // this wave's loads per stage (both operands)
+  static constexpr int SEA = BM * BK, SEB = BN * BK;   // elements of each operand in a stage
+  static constexpr int SE2 = SEA + SEB;
+  static constexpr int LPS = SE2 / 512 / NW;  // this wave's 1 KB loads per stage (both operands)
   static constexpr int KS = BK / 16;          // MFMA k steps per stage
-  static_assert(NS * 2 * SE * 2 <= 160 * 1024, "LDS");
+  static_assert(NS * SE2 * 2 * MINB <= 160 * 1024, "LDS");
+  static_assert(SEA % (512 * NW) == 0 && SEB % (512 * NW) == 0, "whole loads per wave");
   static_assert(KS % 2 == 0, "fragment sets alternate within a stage");
 };
 
@@ -336,15 +338,17 @@ __device__ __forceinline__ int swzk(int r) {
 // (0, 4, 10, 14)[k % 4], branch-free (k differs between lanes)
 __device__ __forceinline__ int swzt(int k) { return (0xEA40 >> ((k & 3) << 2)) & 15; }
 
-// Issue this wave's loads of one operand for one stage: BK / 2 wave-loads of 1 KB cover the
-// stage, BK / 2 / NW of them per wave.
-template <bool KMAJ, int NW, int BK>
+// Issue this wave's loads of one operand (R rows of the tile) for one stage: R * BK / 512
+// wave-loads of 1 KB cover the stage, 1 / NW of them per wave. An operand read along M (N) keeps
+// a 256-element row per k, 32 swizzled chunks.
+template <bool KMAJ, int NW, int BK, int R>
 __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ P, int ld,
                                       int row0, int rows_total, int k0, int K, int wave,
                                       int lane) {
   constexpr int LPR = BK / 8;       // lanes per K-major row (16 bytes each)
+  static_assert(KMAJ || R == 256, "outer-k stages hold 256 rows");
 #pragma unroll
-  for (int q = 0; q < BK / 2 / NW; ++q) {
+  for (int q = 0; q < R * BK / 512 / NW; ++q) {
     const int instr = wave + NW * q;
     const void* src = zero_page;
     if constexpr (KMAJ) {
@@ -367,9 +371,10 @@ __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ 
 // per load of the stage and advances it by a per-load byte step (0 for a lane outside the
 // matrix, which keeps reading the zero page) each time a stage is issued. Stages are issued in
 // order; a stage that reaches past K goes through the bounds-checked issue() instead.
-template <bool KMAJ, int NW, int BK>
+template <bool KMAJ, int NW, int BK, int R>
 struct Streamer {
-  static constexpr int NL = BK / 2 / NW;   // this wave's loads per stage of one operand
+  static constexpr int NL = R * BK / 512 / NW;   // this wave's loads per stage of one operand
+  static_assert(KMAJ || R == 256, "outer-k stages hold 256 rows");
   const char* ptr[NL];
   int step[NL];
   int dst0;                                // element offset of this wave's first load in a stage
@@ -482,11 +487,12 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
                                                 f32x16_t (&acc)[PC::MI][PC::NJ], float* lds,
                                                 int m0, int n0, int wm, int wn, int lane) {
   constexpr int WTM = PC::WTM, WTN = PC::WTN, MI = PC::MI, NJ = PC::NJ, NT = PC::NT;
+  constexpr int BM = PC::BM, BN = PC::BN;
   constexpr int CPR = BN / 4;                 // 4-column chunks per row
   constexpr int PER = WTM * CPR / NT;         // chunks per thread and pass
   constexpr bool F32 = EPI == EPI_STORE_F32 || EPI == EPI_ACCUM_F32;
   static_assert(WTM * CPR % NT == 0, "whole chunks per thread");
-  static_assert(WTM * BN * 4 <= PC::NS * 2 * PC::SE * 2, "one wave row of fp32 fits the stages");
+  static_assert(WTM * BN * 4 <= PC::NS * PC::SE2 * 2, "one wave row of fp32 fits the stages");
   const int hl = lane >> 5;
   const bool c_f32 = F32 || (EPI == EPI_CE_DZ && g.c_dtype == SLIDE_F32);
   const bool vec = (g.ldc % 4 == 0) && ((uintptr_t)g.C % (c_f32 ? 16 : 8) == 0) &&
@@ -510,12 +516,12 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
       }
     }
   }
-  // A plain bf16 store of a tile inside an aligned matrix: one pass. The whole 256 x 256 tile,
-  // rounded to bf16 (the only rounding either way), fits the 128 KB of stages, so every wave
-  // writes at once and each thread then stores 16-byte row chunks.
+  // A plain bf16 store of a tile inside an aligned matrix: one pass. The whole tile, rounded to
+  // bf16 (the only rounding either way), fits the stages, so every wave writes at once and each
+  // thread then stores 16-byte row chunks.
   if constexpr (EPI == EPI_STORE_BF16) {
     if (g.ldc % 8 == 0 && (uintptr_t)g.C % 16 == 0 && m0 + BM <= g.M && n0 + BN <= g.N) {
-      static_assert(BM * BN * 2 <= PC::NS * 2 * PC::SE * 2, "a bf16 tile fits the stages");
+      static_assert(BM * BN * 2 <= PC::NS * PC::SE2 * 2, "a bf16 tile fits the stages");
       constexpr int CPR8 = BN / 8, PER8 = BM * CPR8 / NT;
       bf16_t* lb = (bf16_t*)lds;
       __syncthreads();   // the main loop's LDS reads are done
@@ -721,11 +727,12 @@ struct StageTag {
 }  // namespace pipe
 
 template <class PC, bool AK, bool BKM, int EPI, int SITE, int DT>
-__global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
+__global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g) {
   using namespace pipe;
   constexpr int NS = PC::NS, NW = PC::NW, WGM = PC::WGM, WTM = PC::WTM, WTN = PC::WTN;
-  constexpr int MI = PC::MI, NJ = PC::NJ, BK = PC::BK, SE = PC::SE, KS = PC::KS;
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * 2 * SE];
+  constexpr int MI = PC::MI, NJ = PC::NJ, BK = PC::BK, SE2 = PC::SE2, KS = PC::KS;
+  constexpr int BM = PC::BM, BN = PC::BN;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * SE2];
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
@@ -753,10 +760,10 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = (g.K + BK - 1) / BK;
-  auto stage_a = [&](int b) { return smem + b * 2 * SE; };
-  auto stage_b = [&](int b) { return smem + b * 2 * SE + SE; };
-  Streamer<AK, NW, BK> sta;
-  Streamer<BKM, NW, BK> stb;
+  auto stage_a = [&](int b) { return smem + b * SE2; };
+  auto stage_b = [&](int b) { return smem + b * SE2 + PC::SEA; };
+  Streamer<AK, NW, BK, BM> sta;
+  Streamer<BKM, NW, BK, BN> stb;
   sta.init(A, g.lda, m0, g.M, wave, lane);
   stb.init(B, g.ldb, n0, g.N, wave, lane);
   auto issue_stage = [&](int kt) {   // stages are issued in order 0, 1, 2, ...
@@ -765,8 +772,8 @@ __global__ __launch_bounds__(PC::NT, 1) void gemm_pipe_kernel(GemmArgs g) {
       sta.issue_next(stage_a(b));
       stb.issue_next(stage_b(b));
     } else {                         // the last, partial stage: bounds-checked per lane
-      issue<AK, NW, BK>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
-      issue<BKM, NW, BK>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
+      issue<AK, NW, BK, BM>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
+      issue<BKM, NW, BK, BN>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
     }
   };
   // Wait until stage kt has landed (this wave's loads; the barrier that follows covers the
@@ -972,8 +979,8 @@ inline bool use_large(const GemmArgs& g) {
 template <bool AK, bool BKM, int EPI, int SITE, int DT>
 void launch_one(const GemmArgs& g, hipStream_t st) {
   if (use_large(g)) {
-    const int tiles = ((g.M + pipe::BM - 1) / pipe::BM) * ((g.N + pipe::BN - 1) / pipe::BN);
     using PC = typename PipeFor<AK, BKM>::type;
+    const int tiles = ((g.M + PC::BM - 1) / PC::BM) * ((g.N + PC::BN - 1) / PC::BN);
     hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles), dim3(PC::NT),
                        0, st, g);
   } else {
