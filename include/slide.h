@@ -224,6 +224,31 @@ int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w, cons
 int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
                int ldb, int b_kmajor, void* C, int ldc, int c_dtype, const void* R, int ldr,
                float alpha, int accumulate, int dtype, void* stream);
+/* SwiGLU of the layer's MLP (An Efficient Heterogeneous Co-Design for Fine-Tuning on a Single
+ * GPU, the summary's section 2C names SwiGLU among the kernels the system rewrote; the formula is
+ * the Llama MLP's): gu [N][2F] holds g in columns 0 .. F-1 and u in F .. 2F-1 of each row,
+ * m [N][F] = silu(g) * u with silu(g) = g / (1 + exp(-g)), computed in fp32 from the stored
+ * 16-bit (or fp32) values and rounded once. F must be a positive multiple of 8 and every pointer
+ * 16-byte aligned; device pointers, caller-owned; stream-ordered. */
+int slide_swiglu_fwd(const void* gu, void* m, int N, int F, int dtype, void* stream);
+/* Backward: dgu [N][2F] = (dm * u * s * (1 + g (1 - s)), dm * g * s) with s = sigmoid(g). */
+int slide_swiglu_bwd(const void* dm, const void* gu, void* dgu, int N, int F, int dtype,
+                     void* stream);
+/* The gate/up projection fused with SwiGLU: gu = x w_gu^T (x [M][K] row stride ldx, w_gu
+ * [2F][K] row stride ldw with the F gate rows first) and m = SwiGLU(gu), both written. For
+ * 16-bit dtypes on problems large enough for the pipelined GEMM one launch does both (each tile
+ * computes 128 gate and the matching 128 up columns); otherwise slide_gemm's kernel and the
+ * elementwise kernel run. The bits are the same either way: m is computed from the 16-bit g, u. */
+int slide_gemm_swiglu_fwd(int M, int F, int K, const void* x, int ldx, const void* w_gu, int ldw,
+                          void* gu, void* m, int dtype, void* stream);
+/* The down projection's input gradient fused with SwiGLU's backward: dm = dy w_down (dy [M][K]
+ * row stride lddy, w_down [K][F] row stride ldw), dgu = SwiGLU backward of dm at gu; dm itself is
+ * not stored by the fused launch. ws (ws_bytes >= slide_gemm_swiglu_bwd_workspace_bytes, 0 when
+ * the fused launch applies) holds dm otherwise. */
+size_t slide_gemm_swiglu_bwd_workspace_bytes(int M, int F, int dtype);
+int slide_gemm_swiglu_bwd(int M, int F, int K, const void* dy, int lddy, const void* w_down,
+                          int ldw, const void* gu, void* dgu, int dtype, void* ws,
+                          size_t ws_bytes, void* stream);
 /* Causal GQA attention on a packed qkv buffer [B*S, (nq+2nkv)*d] (RoPE already applied).
  * o [B*S, nq*d]; lse fp32 [B, nq, S]. */
 int slide_attention_fwd(const void* qkv, void* o, float* lse, int B, int S, int nq, int nkv,

@@ -21,7 +21,8 @@ __all__ = [
     "slide_embed_fwd",
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
-    "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm",
+    "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm", "slide_swiglu_fwd", "slide_swiglu_bwd",
+    "slide_gemm_swiglu_fwd", "slide_gemm_swiglu_bwd_workspace_bytes", "slide_gemm_swiglu_bwd",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows",
     "slide_cpu_adamw_rows_packed", "slide_copy_rows", "slide_gpu_adamw", "slide_convert_f32",
@@ -198,6 +199,29 @@ def slide_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, c_dtype, R=N
                alpha=1.0, accumulate=False, dtype=SLIDE_BF16, stream=None):
     call("slide_gemm", M, N, K, _p(A), lda, int(a_kmajor), _p(B), ldb, int(b_kmajor), _p(C), ldc,
          c_dtype, _p(R), ldr, ctypes.c_float(alpha), int(accumulate), dtype, _s(stream))
+
+
+def slide_swiglu_fwd(gu, m, N, F, dtype, stream=None):
+    call("slide_swiglu_fwd", _p(gu), _p(m), N, F, dtype, _s(stream))
+
+
+def slide_swiglu_bwd(dm, gu, dgu, N, F, dtype, stream=None):
+    call("slide_swiglu_bwd", _p(dm), _p(gu), _p(dgu), N, F, dtype, _s(stream))
+
+
+def slide_gemm_swiglu_fwd(M, F, K, x, ldx, w_gu, ldw, gu, m, dtype, stream=None):
+    call("slide_gemm_swiglu_fwd", M, F, K, _p(x), ldx, _p(w_gu), ldw, _p(gu), _p(m), dtype,
+         _s(stream))
+
+
+def slide_gemm_swiglu_bwd_workspace_bytes(M, F, dtype):
+    return int(lib().slide_gemm_swiglu_bwd_workspace_bytes(M, F, dtype))
+
+
+def slide_gemm_swiglu_bwd(M, F, K, dy, lddy, w_down, ldw, gu, dgu, dtype, ws=None, ws_bytes=0,
+                          stream=None):
+    call("slide_gemm_swiglu_bwd", M, F, K, _p(dy), lddy, _p(w_down), ldw, _p(gu), _p(dgu), dtype,
+         _p(ws), ws_bytes, _s(stream))
 
 
 def slide_attention_fwd(qkv, o, lse, B, S, nq, nkv, d, dtype, stream=None):

@@ -5,7 +5,7 @@
 namespace slide {
 
 enum { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_ACCUM_F32 = 3,
-       EPI_CE_STATS = 4, EPI_CE_DZ = 5 };
+       EPI_CE_STATS = 4, EPI_CE_DZ = 5, EPI_SWIGLU_FWD = 6, EPI_SWIGLU_BWD = 7 };
 
 // Fused epilogues of the LM-head cross-entropy's logits GEMM (C = z^T, [vocab rows][tokens]):
 //   CE_STATS: per token column, the max and sum of exp(z - max) over each block of kCeRowsPerPart
@@ -14,7 +14,16 @@ enum { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_RESID = 2, EPI_ACCUM_F32 = 3,
 //   CE_DZ: dz = (exp(z - lse_t) - [c0 + row == y_t]) * inv_nv for valid targets, else 0, stored
 //     in C (the storage type) for columns up to ldc (columns past N get 0).
 constexpr int kCeRowsPerPart = 64;
-enum { SPECIAL_NONE = 0, SPECIAL_CE_STATS = 1, SPECIAL_CE_DZ = 2 };
+enum { SPECIAL_NONE = 0, SPECIAL_CE_STATS = 1, SPECIAL_CE_DZ = 2, SPECIAL_SWIGLU_FWD = 3,
+       SPECIAL_SWIGLU_BWD = 4 };
+
+// Fused SwiGLU epilogues of the MLP GEMMs (16-bit operands, pipelined kernel):
+//   SWIGLU_FWD (gate/up projection, A and B K-major, B = W_gu [2F][K] with the gate rows first):
+//     each tile holds 128 gate and the matching 128 up columns; it stores them into C = gu
+//     [M][2F] (ldc) and m = silu(g) u of the 16-bit g and u into aux_out [M][F].
+//   SWIGLU_BWD (down projection's input gradient, N = F): the 16-bit dm of each tile is not
+//     stored; with g, u read from aux_in = gu [M][2F] (ld 2F) it gives dg, du into C = dgu
+//     [M][2F] (ldc).
 
 // Call sites of the layer and the LM head. Each site with its usual layout gets its own kernel
 // symbol (the site is a template tag with no effect on the code), so that profilers report the
@@ -54,9 +63,27 @@ struct GemmArgs {
   float* zt;             // [N] target logit (CE_STATS)
   int c0;                // first vocabulary row of this chunk
   int V;                 // vocabulary size
+  // SwiGLU epilogues
+  int ffn;               // F
+  void* aux_out;         // m (SWIGLU_FWD)
+  const void* aux_in;    // gu (SWIGLU_BWD)
 };
 
 int gemm_check(const GemmArgs& g);
 int gemm_launch(const GemmArgs& g, hipStream_t st);
+
+// The MLP's gate/up projection and SwiGLU: gu[M][2F] = x[M][K] W_gu^T (W_gu [2F][K], gate rows
+// first, row stride ldw), m[M][F] = silu(g) u. One fused launch when the pipelined kernel
+// applies, else the GEMM and the elementwise kernel; the results are the same bits either way.
+int gemm_swiglu_fwd(int M, int F, int K, const void* x, int ldx, const void* w, int ldw, void* gu,
+                    void* m, int dtype, const char* name, int site, hipStream_t st);
+// The down projection's input gradient and SwiGLU's backward: dm = dy[M][K] W_d (W_d [K][F]),
+// dgu[M][2F] = (dm * u * silu'(g), dm * silu(g)) from gu. dm_ws ([M][F], 16-byte aligned) is
+// written only when the fused launch does not apply.
+int gemm_swiglu_bwd(int M, int F, int K, const void* dy, int lddy, const void* w, int ldw,
+                    const void* gu, void* dgu, void* dm_ws, int dtype, const char* name, int site,
+                    hipStream_t st);
+// whether gemm_swiglu_bwd writes dm_ws for these sizes
+bool gemm_swiglu_bwd_needs_dm(int M, int F, int dtype);
 
 }  // namespace slide

@@ -16,6 +16,8 @@
 // Tiles are ordered XCD-aware and grouped along M for L2 reuse.
 // fp32 path (the small fp32 configuration): a plain LDS-tiled SIMT kernel, 64x64 per workgroup.
 #include "gemm.h"
+#include "pointwise.h"
+#include "swiglu.h"
 
 namespace slide {
 
@@ -344,7 +346,7 @@ __device__ __forceinline__ int swzt(int k) { return (0xEA40 >> ((k & 3) << 2)) &
 template <bool KMAJ, int NW, int BK, int R>
 __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ P, int ld,
                                       int row0, int rows_total, int k0, int K, int wave,
-                                      int lane) {
+                                      int lane, int split = 0) {
   constexpr int LPR = BK / 8;       // lanes per K-major row (16 bytes each)
   static_assert(KMAJ || R == 256, "outer-k stages hold 256 rows");
 #pragma unroll
@@ -354,8 +356,14 @@ __device__ __forceinline__ void issue(bf16_t* stage, const bf16_t* __restrict__ 
     if constexpr (KMAJ) {
       const int r = instr * (64 / LPR) + lane / LPR;
       const int c = (lane % LPR) ^ swzk<BK>(r);
-      const int gr = row0 + r, gk = k0 + c * 8;
-      if (gr < rows_total && gk < K) src = P + (size_t)gr * ld + gk;
+      int gr = row0 + r;
+      bool ok = gr < rows_total;
+      if (split) {   // rows R/2 .. R - 1 of the tile come from the matrix's second half
+        gr = row0 + r % (R / 2) + (r >= R / 2 ? split : 0);
+        ok = row0 + r % (R / 2) < split;
+      }
+      const int gk = k0 + c * 8;
+      if (ok && gk < K) src = P + (size_t)gr * ld + gk;
     } else {
       const int kr = instr * 2 + (lane >> 5);
       const int c = (lane & 31) ^ swzt(kr);
@@ -380,7 +388,7 @@ struct Streamer {
   int dst0;                                // element offset of this wave's first load in a stage
 
   __device__ __forceinline__ void init(const bf16_t* __restrict__ P, int ld, int row0,
-                                       int rows_total, int wave, int lane) {
+                                       int rows_total, int wave, int lane, int split = 0) {
     constexpr int LPR = BK / 8;
     dst0 = wave * 512;
 #pragma unroll
@@ -391,8 +399,13 @@ struct Streamer {
       if constexpr (KMAJ) {
         const int r = instr * (64 / LPR) + lane / LPR;
         const int c = (lane % LPR) ^ swzk<BK>(r);
-        ok = row0 + r < rows_total;
-        off = (size_t)(row0 + r) * ld + c * 8;
+        int gr = row0 + r;
+        ok = gr < rows_total;
+        if (split) {   // as in issue()
+          gr = row0 + r % (R / 2) + (r >= R / 2 ? split : 0);
+          ok = row0 + r % (R / 2) < split;
+        }
+        off = (size_t)gr * ld + c * 8;
       } else {
         const int kr = instr * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swzt(kr);
@@ -473,6 +486,117 @@ __device__ __forceinline__ void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
                : "memory");
 }
 
+// 8 16-bit values (one 16-byte chunk) of gate and up -> 8 values of silu(g) u
+template <int DT>
+__device__ __forceinline__ uint4 swiglu_fwd8(const uint4& gv, const uint4& uv) {
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack16<DT>(swiglu_fwd_1(lo16<DT>(gw[i]), lo16<DT>(uw[i])),
+                      swiglu_fwd_1(hi16<DT>(gw[i]), hi16<DT>(uw[i])));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// dm, g, u chunks -> dg, du chunks
+template <int DT>
+__device__ __forceinline__ void swiglu_bwd8(const uint4& dv, const uint4& gv, const uint4& uv,
+                                            uint4& dgv, uint4& duv) {
+  const uint32_t dw_[4] = {dv.x, dv.y, dv.z, dv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
+                 uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t og[4], ou[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float g0, u0, g1, u1;
+    swiglu_bwd_1(lo16<DT>(dw_[i]), lo16<DT>(gw[i]), lo16<DT>(uw[i]), g0, u0);
+    swiglu_bwd_1(hi16<DT>(dw_[i]), hi16<DT>(gw[i]), hi16<DT>(uw[i]), g1, u1);
+    og[i] = pack16<DT>(g0, g1);
+    ou[i] = pack16<DT>(u0, u1);
+  }
+  dgv = make_uint4(og[0], og[1], og[2], og[3]);
+  duv = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+}
+
+// The SwiGLU epilogues: the tile rounded to 16 bits into LDS, as the plain 16-bit store does
+// (so g, u and dm carry the bits the separate kernels would read), then 16-byte chunks.
+//   forward: a tile's columns 0 .. BN/2 - 1 are gate columns n0 .., the rest the matching up
+//     columns; both go to gu and silu(g) u to m.
+//   backward: columns n0 .. of dm; g and u are read from gu (row stride 2F) a group of chunks at
+//     a time, all issued before the first is waited for.
+template <int EPI, class PC, int DT>
+__device__ __forceinline__ void swiglu_epilogue(const GemmArgs& g,
+                                                f32x16_t (&acc)[PC::MI][PC::NJ], float* lds,
+                                                int m0, int n0, int wm, int wn, int lane) {
+  constexpr int WTM = PC::WTM, WTN = PC::WTN, MI = PC::MI, NJ = PC::NJ, NT = PC::NT;
+  constexpr int BM = PC::BM, BN = PC::BN;
+  static_assert(BM * BN * 2 <= PC::NS * PC::SE2 * 2, "a 16-bit tile fits the stages");
+  const int hl = lane >> 5;
+  bf16_t* lb = (bf16_t*)lds;
+  __syncthreads();   // the main loop's LDS reads are done
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm * WTM + i * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+        const int c = (wn * WTN + j * 32 + (lane & 31)) ^ (hl << 5);
+        lb[r * BN + c] = Bits16<DT>::from_f(acc[i][j][e] * g.alpha);
+      }
+  __syncthreads();
+  auto chunk = [&](int r, int c) {
+    return *(const uint4*)(lb + r * BN + (c ^ (((r >> 2) & 1) << 5)));
+  };
+  const int F = g.ffn;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    constexpr int CPH = BN / 2 / 8, PER = BM * CPH / NT;
+    static_assert(BM * CPH % NT == 0, "whole chunks per thread");
+    bf16_t* gu = (bf16_t*)g.C;
+    bf16_t* mo = (bf16_t*)g.aux_out;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int k = threadIdx.x + NT * q;
+      const int r = k / CPH, cc = k % CPH;
+      const int gr = m0 + r, col = n0 + cc * 8;
+      if (gr < g.M && col < F) {
+        const uint4 gv = chunk(r, cc * 8), uv = chunk(r, BN / 2 + cc * 8);
+        *(uint4*)(gu + (size_t)gr * g.ldc + col) = gv;
+        *(uint4*)(gu + (size_t)gr * g.ldc + F + col) = uv;
+        *(uint4*)(mo + (size_t)gr * F + col) = swiglu_fwd8<DT>(gv, uv);
+      }
+    }
+  } else {
+    constexpr int CPR = BN / 8, PER = BM * CPR / NT, GRP = 4;
+    static_assert(BM * CPR % NT == 0 && PER % GRP == 0, "whole groups per thread");
+    const bf16_t* gu = (const bf16_t*)g.aux_in;
+    bf16_t* dgu = (bf16_t*)g.C;
+#pragma unroll
+    for (int q0 = 0; q0 < PER; q0 += GRP) {
+      uint4 gv[GRP], uv[GRP];
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int k = threadIdx.x + NT * (q0 + j);
+        const int gr = m0 + k / CPR, col = n0 + (k % CPR) * 8;
+        if (gr < g.M && col < F) {
+          gv[j] = *(const uint4*)(gu + (size_t)gr * 2 * F + col);
+          uv[j] = *(const uint4*)(gu + (size_t)gr * 2 * F + F + col);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int k = threadIdx.x + NT * (q0 + j);
+        const int r = k / CPR, cc = k % CPR;
+        const int gr = m0 + r, col = n0 + cc * 8;
+        if (gr < g.M && col < F) {
+          uint4 dgv, duv;
+          swiglu_bwd8<DT>(chunk(r, cc * 8), gv[j], uv[j], dgv, duv);
+          *(uint4*)(dgu + (size_t)gr * g.ldc + col) = dgv;
+          *(uint4*)(dgu + (size_t)gr * g.ldc + F + col) = duv;
+        }
+      }
+    }
+  }
+}
+
 // Stores through LDS. The accumulators of a 32 x 32 MFMA block give each lane one column, so
 // direct stores are one element per lane. Instead, in pass h the waves of wave row h write
 // alpha * acc as fp32 into LDS (WTM x BN floats; the 32-column half is flipped for rows with bit 2
@@ -492,6 +616,10 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
   constexpr int PER = WTM * CPR / NT;         // chunks per thread and pass
   constexpr bool F32 = EPI == EPI_STORE_F32 || EPI == EPI_ACCUM_F32;
   static_assert(WTM * CPR % NT == 0, "whole chunks per thread");
+  if constexpr (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
+    swiglu_epilogue<EPI, PC, DT>(g, acc, lds, m0, n0, wm, wn, lane);
+    return;
+  }
   static_assert(WTM * BN * 4 <= PC::NS * PC::SE2 * 2, "one wave row of fp32 fits the stages");
   const int hl = lane >> 5;
   const bool c_f32 = F32 || (EPI == EPI_CE_DZ && g.c_dtype == SLIDE_F32);
@@ -734,7 +862,12 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
   constexpr int BM = PC::BM, BN = PC::BN;
   __shared__ __attribute__((aligned(1024))) bf16_t smem[NS * SE2];
 
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  // SwiGLU forward: a tile's B rows are BN / 2 gate rows and the matching up rows (F later)
+  constexpr bool SPLIT = EPI == EPI_SWIGLU_FWD;
+  static_assert(!SPLIT || (AK && BKM), "split tiles read a K-major B");
+  const int split = SPLIT ? g.ffn : 0;
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = SPLIT ? (g.ffn + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
   int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
   if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
   constexpr int GM = 4;
@@ -743,7 +876,7 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
   const int gsize = min(tiles_m - first_m, GM);
   const int in_group = logical % (GM * tiles_n);
   const int tm = first_m + in_group % gsize, tn = in_group / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * (SPLIT ? BN / 2 : BN);
 
   const bf16_t* A = (const bf16_t*)g.A;
   const bf16_t* B = (const bf16_t*)g.B;
@@ -765,7 +898,7 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
   Streamer<AK, NW, BK, BM> sta;
   Streamer<BKM, NW, BK, BN> stb;
   sta.init(A, g.lda, m0, g.M, wave, lane);
-  stb.init(B, g.ldb, n0, g.N, wave, lane);
+  stb.init(B, g.ldb, n0, g.N, wave, lane, split);
   auto issue_stage = [&](int kt) {   // stages are issued in order 0, 1, 2, ...
     const int b = kt % NS;
     if ((kt + 1) * BK <= g.K) {
@@ -773,7 +906,7 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
       stb.issue_next(stage_b(b));
     } else {                         // the last, partial stage: bounds-checked per lane
       issue<AK, NW, BK, BM>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
-      issue<BKM, NW, BK, BN>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane);
+      issue<BKM, NW, BK, BN>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane, split);
     }
   };
   // Wait until stage kt has landed (this wave's loads; the barrier that follows covers the
@@ -977,12 +1110,21 @@ inline bool use_large(const GemmArgs& g) {
 }
 
 template <bool AK, bool BKM, int EPI, int SITE, int DT>
+void launch_pipe(const GemmArgs& g, hipStream_t st) {
+  using PC = typename PipeFor<AK, BKM>::type;
+  const int tiles_n = EPI == EPI_SWIGLU_FWD ? (g.ffn + PC::BN / 2 - 1) / (PC::BN / 2)
+                                            : (g.N + PC::BN - 1) / PC::BN;
+  const int tiles = ((g.M + PC::BM - 1) / PC::BM) * tiles_n;
+  hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles), dim3(PC::NT),
+                     0, st, g);
+}
+
+template <bool AK, bool BKM, int EPI, int SITE, int DT>
 void launch_one(const GemmArgs& g, hipStream_t st) {
-  if (use_large(g)) {
-    using PC = typename PipeFor<AK, BKM>::type;
-    const int tiles = ((g.M + PC::BM - 1) / PC::BM) * ((g.N + PC::BN - 1) / PC::BN);
-    hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles), dim3(PC::NT),
-                       0, st, g);
+  if constexpr (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
+    launch_pipe<AK, BKM, EPI, SITE, DT>(g, st);   // callers checked use_large
+  } else if (use_large(g)) {
+    launch_pipe<AK, BKM, EPI, SITE, DT>(g, st);
   } else {
     const int tiles = ((g.M + TileS::BM - 1) / TileS::BM) * ((g.N + TileS::BN - 1) / TileS::BN);
     hipLaunchKernelGGL((gemm_bf16_kernel<TileS, AK, BKM, EPI, SITE, DT>), dim3(tiles),
@@ -1025,6 +1167,8 @@ void launch_16(const GemmArgs& g, hipStream_t st, int epi) {
   SLIDE_SITE(SITE_CE_DZ, true, true, EPI_CE_DZ)
   SLIDE_SITE(SITE_CE_DH, false, false, EPI_ACCUM_F32)
   SLIDE_SITE(SITE_CE_DW, true, false, EPI_STORE_BF16)
+  SLIDE_SITE(SITE_GATE_UP, true, true, EPI_SWIGLU_FWD)
+  SLIDE_SITE(SITE_DOWN_DX, true, false, EPI_SWIGLU_BWD)
 #undef SLIDE_SITE
   if (g.a_kmajor && g.b_kmajor) launch_generic<true, true, DT>(g, st, epi);
   else if (g.a_kmajor) launch_generic<true, false, DT>(g, st, epi);
@@ -1037,6 +1181,8 @@ void launch_16(const GemmArgs& g, hipStream_t st, int epi) {
 int gemm_epilogue_of(const GemmArgs& g) {
   if (g.special == SPECIAL_CE_STATS) return EPI_CE_STATS;
   if (g.special == SPECIAL_CE_DZ) return EPI_CE_DZ;
+  if (g.special == SPECIAL_SWIGLU_FWD) return EPI_SWIGLU_FWD;
+  if (g.special == SPECIAL_SWIGLU_BWD) return EPI_SWIGLU_BWD;
   if (g.accumulate) return EPI_ACCUM_F32;
   if (g.R) return EPI_RESID;
   return g.c_dtype == SLIDE_F32 ? EPI_STORE_F32 : EPI_STORE_BF16;
@@ -1073,11 +1219,20 @@ int gemm_check(const GemmArgs& g) {
 
 int gemm_launch(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return SLIDE_OK;
-  // the cross-entropy epilogues exist for the logits GEMM's own instantiation only
-  SLIDE_REQUIRE(g.special == SPECIAL_NONE ||
+  // the cross-entropy and SwiGLU epilogues exist for their GEMMs' own instantiations only
+  SLIDE_REQUIRE(g.special == SPECIAL_NONE || g.special == SPECIAL_SWIGLU_FWD ||
+                    g.special == SPECIAL_SWIGLU_BWD ||
                     (g.dtype != SLIDE_F32 && g.a_kmajor && g.b_kmajor &&
                      g.site == (g.special == SPECIAL_CE_STATS ? SITE_CE_STATS : SITE_CE_DZ)),
                 SLIDE_E_ARG, "gemm: cross-entropy epilogue with another site or layout");
+  SLIDE_REQUIRE(g.special != SPECIAL_SWIGLU_FWD ||
+                    (g.dtype != SLIDE_F32 && g.a_kmajor && g.b_kmajor && g.site == SITE_GATE_UP &&
+                     use_large(g) && g.N == 2 * g.ffn && g.aux_out),
+                SLIDE_E_ARG, "gemm: SwiGLU forward epilogue with another site, layout or size");
+  SLIDE_REQUIRE(g.special != SPECIAL_SWIGLU_BWD ||
+                    (g.dtype != SLIDE_F32 && g.a_kmajor && !g.b_kmajor && g.site == SITE_DOWN_DX &&
+                     use_large(g) && g.N == g.ffn && g.aux_in),
+                SLIDE_E_ARG, "gemm: SwiGLU backward epilogue with another site, layout or size");
   ProfScope ps(g.name ? g.name : "gemm", st);
   const int epi = gemm_epilogue_of(g);
   if (g.dtype == SLIDE_BF16) {
@@ -1095,6 +1250,49 @@ int gemm_launch(const GemmArgs& g, hipStream_t st) {
   return check_launch(g.name ? g.name : "gemm");
 }
 
+int gemm_swiglu_fwd(int M, int F, int K, const void* x, int ldx, const void* w, int ldw, void* gu,
+                    void* m, int dtype, const char* name, int site, hipStream_t st) {
+  GemmArgs g{M, 2 * F, K, x, ldx, true, w, ldw, true, gu, 2 * F, dtype, nullptr, 0, 1.0f,
+             false, dtype, name, site};
+  if (dtype == SLIDE_F32 || !use_large(g)) {
+    SLIDE_TRY(gemm_launch(g, st));
+    return swiglu_fwd(gu, m, M, F, dtype, st);
+  }
+  SLIDE_REQUIRE(F % 8 == 0 && aligned16(gu) && aligned16(m), SLIDE_E_ARG,
+                "gemm_swiglu_fwd: F must be a multiple of 8 and gu, m 16-byte aligned");
+  g.special = SPECIAL_SWIGLU_FWD;
+  g.ffn = F;
+  g.aux_out = m;
+  return gemm_launch(g, st);
+}
+
+bool gemm_swiglu_bwd_needs_dm(int M, int F, int dtype) {
+  GemmArgs g{};
+  g.M = M;
+  g.N = F;
+  return dtype == SLIDE_F32 || !use_large(g);
+}
+
+int gemm_swiglu_bwd(int M, int F, int K, const void* dy, int lddy, const void* w, int ldw,
+                    const void* gu, void* dgu, void* dm_ws, int dtype, const char* name, int site,
+                    hipStream_t st) {
+  GemmArgs g{M, F, K, dy, lddy, true, w, ldw, false, dm_ws, F, dtype, nullptr, 0, 1.0f, false,
+             dtype, name, site};
+  if (gemm_swiglu_bwd_needs_dm(M, F, dtype)) {
+    SLIDE_REQUIRE(dm_ws, SLIDE_E_ARG, "gemm_swiglu_bwd: these sizes need the dm workspace");
+    SLIDE_TRY(gemm_launch(g, st));
+    return swiglu_bwd(dm_ws, gu, dgu, M, F, dtype, st);
+  }
+  SLIDE_REQUIRE(F % 8 == 0 && aligned16(gu) && aligned16(dgu), SLIDE_E_ARG,
+                "gemm_swiglu_bwd: F must be a multiple of 8 and gu, dgu 16-byte aligned");
+  g.C = dgu;
+  g.ldc = 2 * F;
+  g.special = SPECIAL_SWIGLU_BWD;
+  g.ffn = F;
+  g.aux_in = gu;
+  return gemm_launch(g, st);
+}
+
 }  // namespace slide
 
 extern "C" int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
@@ -1104,4 +1302,46 @@ extern "C" int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kma
                     R, ldr, alpha, accumulate != 0, dtype, "gemm", slide::SITE_GENERIC};
   SLIDE_TRY(slide::gemm_check(g));
   return slide::gemm_launch(g, (hipStream_t)stream);
+}
+
+extern "C" int slide_gemm_swiglu_fwd(int M, int F, int K, const void* x, int ldx, const void* w_gu,
+                                     int ldw, void* gu, void* m, int dtype, void* stream) {
+  SLIDE_REQUIRE(slide::dtype_valid(dtype), SLIDE_E_ARG, "gemm_swiglu_fwd: bad dtype");
+  SLIDE_REQUIRE(M >= 0 && K >= 0 && F > 0 && F % 8 == 0, SLIDE_E_SHAPE,
+                "gemm_swiglu_fwd: M %d, K %d must be >= 0 and F %d a positive multiple of 8", M,
+                K, F);
+  SLIDE_REQUIRE(m && slide::aligned16(m) && slide::aligned16(gu), SLIDE_E_ARG,
+                "gemm_swiglu_fwd: gu and m must be non-null and 16-byte aligned");
+  slide::GemmArgs g{M, 2 * F, K, x, ldx, true, w_gu, ldw, true, gu, 2 * F, dtype, nullptr, 0,
+                    1.0f, false, dtype, "gemm_swiglu_fwd", slide::SITE_GATE_UP};
+  SLIDE_TRY(slide::gemm_check(g));
+  if (M == 0) return SLIDE_OK;
+  return slide::gemm_swiglu_fwd(M, F, K, x, ldx, w_gu, ldw, gu, m, dtype, "gemm_swiglu_fwd",
+                                slide::SITE_GATE_UP, (hipStream_t)stream);
+}
+
+extern "C" size_t slide_gemm_swiglu_bwd_workspace_bytes(int M, int F, int dtype) {
+  if (M <= 0 || F <= 0 || !slide::dtype_valid(dtype)) return 0;
+  if (!slide::gemm_swiglu_bwd_needs_dm(M, F, dtype)) return 0;
+  return slide::align_up((size_t)M * F * slide::dtype_size(dtype), 256);
+}
+
+extern "C" int slide_gemm_swiglu_bwd(int M, int F, int K, const void* dy, int lddy,
+                                     const void* w_down, int ldw, const void* gu, void* dgu,
+                                     int dtype, void* ws, size_t ws_bytes, void* stream) {
+  SLIDE_REQUIRE(slide::dtype_valid(dtype), SLIDE_E_ARG, "gemm_swiglu_bwd: bad dtype");
+  SLIDE_REQUIRE(M >= 0 && K >= 0 && F > 0 && F % 8 == 0, SLIDE_E_SHAPE,
+                "gemm_swiglu_bwd: M %d, K %d must be >= 0 and F %d a positive multiple of 8", M,
+                K, F);
+  SLIDE_REQUIRE(gu && dgu && slide::aligned16(gu) && slide::aligned16(dgu), SLIDE_E_ARG,
+                "gemm_swiglu_bwd: gu and dgu must be non-null and 16-byte aligned");
+  const size_t need = slide_gemm_swiglu_bwd_workspace_bytes(M, F, dtype);
+  SLIDE_REQUIRE(ws_bytes >= need && (need == 0 || (ws && slide::aligned16(ws))), SLIDE_E_WORKSPACE,
+                "gemm_swiglu_bwd: workspace %zu < %zu", ws_bytes, need);
+  slide::GemmArgs g{M, F, K, dy, lddy, true, w_down, ldw, false, dgu, 2 * F, dtype, nullptr, 0,
+                    1.0f, false, dtype, "gemm_swiglu_bwd", slide::SITE_DOWN_DX};
+  SLIDE_TRY(slide::gemm_check(g));
+  if (M == 0) return SLIDE_OK;
+  return slide::gemm_swiglu_bwd(M, F, K, dy, lddy, w_down, ldw, gu, dgu, need ? ws : nullptr,
+                                dtype, "gemm_swiglu_bwd", slide::SITE_DOWN_DX, (hipStream_t)stream);
 }

@@ -146,9 +146,8 @@ int forward(const Dims& d, const slide_layer_cfg& c, const void* w, const void* 
   SLIDE_TRY(gemm(d.N, d.H, d.OD, ws.o, d.OD, true, at(w, off[2], ts), d.OD, true, ws.x2, d.H, x,
                  d.dt, "gemm_o", SITE_O, st));
   SLIDE_TRY(rmsnorm_fwd(ws.x2, at(w, off[3], ts), ws.r2, nullptr, d.N, d.H, c.rms_eps, d.dt, st));
-  SLIDE_TRY(gemm(d.N, 2 * d.F, d.H, ws.r2, d.H, true, at(w, off[4], ts), d.H, true, ws.gu,
-                 2 * d.F, nullptr, d.dt, "gemm_gate_up", SITE_GATE_UP, st));
-  SLIDE_TRY(swiglu_fwd(ws.gu, ws.m, d.N, d.F, d.dt, st));
+  SLIDE_TRY(gemm_swiglu_fwd(d.N, d.F, d.H, ws.r2, d.H, at(w, off[4], ts), d.H, ws.gu, ws.m, d.dt,
+                            "gemm_gate_up", SITE_GATE_UP, st));
   if (y)
     SLIDE_TRY(gemm(d.N, d.H, d.F, ws.m, d.F, true, at(w, off[5], ts), d.F, true, y, d.H, ws.x2,
                    d.dt, "gemm_down", SITE_DOWN, st));
@@ -163,11 +162,10 @@ int backward(const Dims& d, const slide_layer_cfg& c, const void* w, const void*
   const int N = d.N, H = d.H, F = d.F;
   if (recompute) SLIDE_TRY(forward(d, c, w, x, nullptr, ws, st));
   // MLP half
-  SLIDE_TRY(gemm(N, F, H, dy, H, true, at(w, off[5], ts), F, false, ws.dm, F, nullptr, d.dt,
-                 "gemm_down_dx", SITE_DOWN_DX, st));
+  SLIDE_TRY(gemm_swiglu_bwd(N, F, H, dy, H, at(w, off[5], ts), F, ws.gu, ws.dgu, ws.dm, d.dt,
+                            "gemm_down_dx", SITE_DOWN_DX, st));
   SLIDE_TRY(gemm(H, F, N, dy, H, false, ws.m, F, false, at(g, off[5], ts), F, nullptr, d.dt,
                  "gemm_down_dw", SITE_DOWN_DW, st));
-  SLIDE_TRY(swiglu_bwd(ws.dm, ws.gu, ws.dgu, N, F, d.dt, st));
   SLIDE_TRY(gemm(N, H, 2 * F, ws.dgu, 2 * F, true, at(w, off[4], ts), H, false, ws.dr2, H,
                  nullptr, d.dt, "gemm_gate_up_dx", SITE_GATE_UP_DX, st));
   SLIDE_TRY(gemm(2 * F, H, N, ws.dgu, 2 * F, false, ws.r2, H, false, at(g, off[4], ts), H,
@@ -404,6 +402,31 @@ extern "C" int slide_rope(void* qkv, int B, int S, int nq, int nkv, int d, float
   float* sn = c.take<float>((size_t)S * (d / 2));
   SLIDE_TRY(rope_tables(cs, sn, S, d, theta, (hipStream_t)stream));
   return rope_apply(qkv, cs, sn, B, S, nq, nkv, d, inverse, dtype, (hipStream_t)stream);
+}
+
+namespace {
+int swiglu_args(const void* a, const void* b, const void* c, int N, int F, int dtype,
+                const char* what) {
+  SLIDE_REQUIRE(dtype_valid(dtype), SLIDE_E_ARG, "%s: bad dtype", what);
+  SLIDE_REQUIRE(N >= 0 && F > 0 && F % 8 == 0, SLIDE_E_SHAPE,
+                "%s: N %d must be >= 0 and F %d a positive multiple of 8", what, N, F);
+  if (N == 0) return SLIDE_OK;
+  SLIDE_REQUIRE(a && b && c, SLIDE_E_ARG, "%s: null pointer", what);
+  SLIDE_REQUIRE(aligned16(a) && aligned16(b) && aligned16(c), SLIDE_E_ARG,
+                "%s: pointers must be 16-byte aligned", what);
+  return SLIDE_OK;
+}
+}  // namespace
+
+extern "C" int slide_swiglu_fwd(const void* gu, void* m, int N, int F, int dtype, void* stream) {
+  SLIDE_TRY(swiglu_args(gu, m, m, N, F, dtype, "swiglu_fwd"));
+  return swiglu_fwd(gu, m, N, F, dtype, (hipStream_t)stream);
+}
+
+extern "C" int slide_swiglu_bwd(const void* dm, const void* gu, void* dgu, int N, int F, int dtype,
+                                void* stream) {
+  SLIDE_TRY(swiglu_args(dm, gu, dgu, N, F, dtype, "swiglu_bwd"));
+  return swiglu_bwd(dm, gu, dgu, N, F, dtype, (hipStream_t)stream);
 }
 
 extern "C" int slide_embed_fwd(const void* E, const int32_t* tokens, void* x, int N, int H, int V,

@@ -8,6 +8,7 @@
 // reductions, 16-byte vector accesses (8 bf16 or 2x4 fp32) so every wave reads whole 128-byte
 // lines. All arithmetic is fp32; bf16 is converted on load and rounded (nearest-even) on store.
 #include "pointwise.h"
+#include "swiglu.h"
 
 namespace slide {
 namespace {
@@ -360,7 +361,6 @@ __global__ __launch_bounds__(256) void rope_kernel(T* qkv, const float* __restri
 }
 
 // ---------------------------------------------------------------- SwiGLU
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const T* __restrict__ gu,
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const T* __restrict__ g
   V8<T>::load(gu + t * 2 * F + j, g);
   V8<T>::load(gu + t * 2 * F + F + j, u);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = g[i] * sigmoidf_(g[i]) * u[i];
+  for (int i = 0; i < 8; ++i) o[i] = swiglu_fwd_1(g[i], u[i]);
   V8<T>::store(m + idx, o);
 }
 
@@ -388,11 +388,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ d
   V8<T>::load(gu + t * 2 * F + F + j, u);
   V8<T>::load(dm + idx, d);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float sg = sigmoidf_(g[i]);
-    du[i] = d[i] * g[i] * sg;
-    dg[i] = d[i] * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
-  }
+  for (int i = 0; i < 8; ++i) swiglu_bwd_1(d[i], g[i], u[i], dg[i], du[i]);
   V8<T>::store(dgu + t * 2 * F + j, dg);
   V8<T>::store(dgu + t * 2 * F + F + j, du);
 }

@@ -81,6 +81,59 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     assert_close(host(C4), ref, "f32", "C = A B (fp32 output)", tol=1e-5)
 
 
+# (M, F, K): fused launches (both directions) with ragged rows, a ragged last tile (F % 128 and
+# F % 256 != 0) and a partial k-tile; the same with full tiles and a steady k loop; a size below
+# the pipelined kernel's threshold (the GEMM and the elementwise kernel run instead)
+SWIGLU_SHAPES = [(2088, 4040, 136), (2048, 4096, 520), (300, 264, 72)]
+
+
+def _bits(t):
+    return t.view(torch.int16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,F,K", SWIGLU_SHAPES)
+def test_gemm_swiglu_fused_equals_separate_and_oracle(dtype, M, F, K):
+    print(f"gemm+swiglu {dtype} M={M} F={F} K={K}", flush=True)
+    rng = _rng(7)
+    code = sl.dtype_code(dtype)
+    x = _round(rng.standard_normal((M, K)), dtype)
+    w = _round(rng.standard_normal((2 * F, K)) / np.sqrt(K), dtype)
+    dx, dw = dev(x, dtype), dev(w, dtype)
+    gu1, m1 = empty((M, 2 * F), dtype), empty((M, F), dtype)
+    sl.slide_gemm_swiglu_fwd(M, F, K, dx, K, dw, K, gu1, m1, code, stream())
+    gu2, m2 = empty((M, 2 * F), dtype), empty((M, F), dtype)
+    sl.slide_gemm(M, 2 * F, K, dx, K, True, dw, K, True, gu2, 2 * F, code, dtype=code,
+                  stream=stream())
+    sl.slide_swiglu_fwd(gu2, m2, M, F, code, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(gu1), _bits(gu2)), "fused gu differs from the plain GEMM's"
+    assert torch.equal(_bits(m1), _bits(m2)), "fused m differs from the elementwise kernel's"
+    ref = x @ w.T
+    assert_close(host(gu1), ref, dtype, "gu = x W_gu^T", tol=GEMM_TOL[dtype])
+    assert_close(host(m1), om.swiglu_fwd(ref[:, :F], ref[:, F:]), dtype, "m = SwiGLU(gu)")
+
+    # backward: dm = dy W_d (W_d [K][F]), then SwiGLU's backward at the stored gu
+    dy = _round(rng.standard_normal((M, K)), dtype)
+    wd = _round(rng.standard_normal((K, F)) / np.sqrt(K), dtype)
+    ddy, dwd = dev(dy, dtype), dev(wd, dtype)
+    need = sl.slide_gemm_swiglu_bwd_workspace_bytes(M, F, code)
+    dgu1 = empty((M, 2 * F), dtype)
+    buf = ws(need) if need else None
+    sl.slide_gemm_swiglu_bwd(M, F, K, ddy, K, dwd, F, gu1, dgu1, code, buf, need, stream())
+    dm2, dgu2 = empty((M, F), dtype), empty((M, 2 * F), dtype)
+    sl.slide_gemm(M, F, K, ddy, K, True, dwd, F, False, dm2, F, code, dtype=code, stream=stream())
+    sl.slide_swiglu_bwd(dm2, gu1, dgu2, M, F, code, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(dgu1), _bits(dgu2)), "fused dgu differs from the separate kernels'"
+    g, u = host(gu1)[:, :F], host(gu1)[:, F:]
+    dg_ref, du_ref = om.swiglu_bwd(dy @ wd, g, u)
+    got = host(dgu1)
+    assert_close(got[:, :F], dg_ref, dtype, "dg")
+    assert_close(got[:, F:], du_ref, dtype, "du")
+    print(f"  fused launch: {need == 0}", flush=True)
+
+
 # N = 300 and 517: several 64-row partial sums of the weight gradient, the last one ragged
 @pytest.mark.parametrize("dtype,H,N", [("bf16", 4096, 37), ("f32", 256, 37), ("bf16", 264, 300),
                                        ("f32", 200, 517), ("f16", 4096, 37), ("f16", 264, 300)])
