@@ -7,11 +7,7 @@
 
 namespace slide {
 
-// sigmoid with the hardware reciprocal (about 1 ulp) instead of a correctly rounded division,
-// whose ten-instruction sequence dominated the fused GEMM epilogue
-__device__ __forceinline__ float swiglu_sigmoid(float a) {
-  return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-}
+__device__ __forceinline__ float swiglu_sigmoid(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
 // The results leave as fp32 values: without this the compiler folds a final multiply and the
 // narrowing to fp16 into one mixed-precision FMA (one rounding instead of two) in some callers
