@@ -224,6 +224,17 @@ int slide_rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* w, cons
 int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
                int ldb, int b_kmajor, void* C, int ldc, int c_dtype, const void* R, int ldr,
                float alpha, int accumulate, int dtype, void* stream);
+/* slide_gemm with a workspace of slide_gemm_tail_workspace_bytes() (or NULL): when the last
+ * wave of 256 x 256 tiles would occupy at most half of the compute units, those tiles are
+ * computed as two halves of K each, whose fp32 partial sums a second launch adds (the first
+ * half's plus the second's) before the usual epilogue. Results then differ from slide_gemm's
+ * only in the rounding of that one addition; they are deterministic. The layer backward's GEMMs
+ * use this with a slice of the layer workspace. */
+size_t slide_gemm_tail_workspace_bytes(void);
+int slide_gemm_ws(int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
+                  int ldb, int b_kmajor, void* C, int ldc, int c_dtype, const void* R, int ldr,
+                  float alpha, int accumulate, int dtype, void* ws, size_t ws_bytes,
+                  void* stream);
 /* SwiGLU of the layer's MLP (An Efficient Heterogeneous Co-Design for Fine-Tuning on a Single
  * GPU, the summary's section 2C names SwiGLU among the kernels the system rewrote; the formula is
  * the Llama MLP's): gu [N][2F] holds g in columns 0 .. F-1 and u in F .. 2F-1 of each row,

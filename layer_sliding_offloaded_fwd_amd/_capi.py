@@ -71,6 +71,8 @@ SIGNATURES = {
     "slide_rmsnorm_bwd_noalloc_max_bytes": (SZ, []),
     "slide_rmsnorm_bwd_noalloc": (I, [P, P, P, P, P, P, I, I, F, I, P]),
     "slide_gemm": (I, [I, I, I, P, I, I, P, I, I, P, I, I, P, I, F, I, I, P]),
+    "slide_gemm_tail_workspace_bytes": (SZ, []),
+    "slide_gemm_ws": (I, [I, I, I, P, I, I, P, I, I, P, I, I, P, I, F, I, I, P, SZ, P]),
     "slide_swiglu_fwd": (I, [P, P, I, I, I, P]),
     "slide_swiglu_bwd": (I, [P, P, P, I, I, I, P]),
     "slide_gemm_swiglu_fwd": (I, [I, I, I, P, I, P, I, P, P, I, P]),

@@ -21,7 +21,8 @@ __all__ = [
     "slide_embed_fwd",
     "slide_embed_bwd_workspace_bytes", "slide_embed_bwd", "slide_rmsnorm_fwd",
     "slide_rmsnorm_bwd_workspace_bytes", "slide_rmsnorm_bwd", "slide_rmsnorm_bwd_noalloc",
-    "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm", "slide_swiglu_fwd", "slide_swiglu_bwd",
+    "slide_rmsnorm_bwd_noalloc_max_bytes", "slide_gemm", "slide_gemm_tail_workspace_bytes",
+    "slide_gemm_ws", "slide_swiglu_fwd", "slide_swiglu_bwd",
     "slide_gemm_swiglu_fwd", "slide_gemm_swiglu_bwd_workspace_bytes", "slide_gemm_swiglu_bwd",
     "slide_attention_fwd", "slide_attention_bwd_workspace_bytes", "slide_attention_bwd",
     "slide_rope", "SlotRing", "slide_cpu_adamw", "slide_cpu_adamw_rows",
@@ -199,6 +200,18 @@ def slide_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, c_dtype, R=N
                alpha=1.0, accumulate=False, dtype=SLIDE_BF16, stream=None):
     call("slide_gemm", M, N, K, _p(A), lda, int(a_kmajor), _p(B), ldb, int(b_kmajor), _p(C), ldc,
          c_dtype, _p(R), ldr, ctypes.c_float(alpha), int(accumulate), dtype, _s(stream))
+
+
+def slide_gemm_tail_workspace_bytes():
+    return int(lib().slide_gemm_tail_workspace_bytes())
+
+
+def slide_gemm_ws(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, c_dtype, R=None, ldr=0,
+                  alpha=1.0, accumulate=False, dtype=SLIDE_BF16, ws=None, ws_bytes=0,
+                  stream=None):
+    call("slide_gemm_ws", M, N, K, _p(A), lda, int(a_kmajor), _p(B), ldb, int(b_kmajor), _p(C),
+         ldc, c_dtype, _p(R), ldr, ctypes.c_float(alpha), int(accumulate), dtype, _p(ws),
+         ws_bytes, _s(stream))
 
 
 def slide_swiglu_fwd(gu, m, N, F, dtype, stream=None):

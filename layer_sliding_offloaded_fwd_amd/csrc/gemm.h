@@ -67,7 +67,16 @@ struct GemmArgs {
   int ffn;               // F
   void* aux_out;         // m (SWIGLU_FWD)
   const void* aux_in;    // gu (SWIGLU_BWD)
+  // Optional fp32 workspace for the last, partial wave of tiles (see gemm_launch); the launcher
+  // sets tail_split, the number of trailing tiles computed as two K halves.
+  float* tail_ws;
+  size_t tail_ws_bytes;
+  int tail_split;
 };
+
+// Workspace that lets gemm_launch split a partial last wave of up to kTailMaxTiles tiles
+constexpr int kTailMaxTiles = 128;
+constexpr size_t kTailWsBytes = (size_t)kTailMaxTiles * 2 * 256 * 256 * 4;
 
 int gemm_check(const GemmArgs& g);
 int gemm_launch(const GemmArgs& g, hipStream_t st);

@@ -15,6 +15,8 @@
 //     8x8 blocks and transposed in registers before the LDS write.
 // Tiles are ordered XCD-aware and grouped along M for L2 reuse.
 // fp32 path (the small fp32 configuration): a plain LDS-tiled SIMT kernel, 64x64 per workgroup.
+#include <atomic>
+
 #include "gemm.h"
 #include "pointwise.h"
 #include "swiglu.h"
@@ -388,7 +390,8 @@ struct Streamer {
   int dst0;                                // element offset of this wave's first load in a stage
 
   __device__ __forceinline__ void init(const bf16_t* __restrict__ P, int ld, int row0,
-                                       int rows_total, int wave, int lane, int split = 0) {
+                                       int rows_total, int wave, int lane, int split = 0,
+                                       int k0 = 0) {
     constexpr int LPR = BK / 8;
     dst0 = wave * 512;
 #pragma unroll
@@ -405,12 +408,12 @@ struct Streamer {
           gr = row0 + r % (R / 2) + (r >= R / 2 ? split : 0);
           ok = row0 + r % (R / 2) < split;
         }
-        off = (size_t)gr * ld + c * 8;
+        off = (size_t)gr * ld + k0 + c * 8;
       } else {
         const int kr = instr * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swzt(kr);
         ok = row0 + c * 8 < rows_total;
-        off = (size_t)kr * ld + row0 + c * 8;
+        off = (size_t)(k0 + kr) * ld + row0 + c * 8;
       }
       ptr[q] = ok ? (const char*)(P + off) : (const char*)zero_page;
       step[q] = ok ? (KMAJ ? BK * 2 : BK * ld * 2) : 0;
@@ -846,6 +849,19 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& g,
   }
 }
 
+// Tile (tm, tn) of a logical tile index: groups of GM tile rows walked column by column, so that
+// consecutive tiles share B columns and a group's A rows stay in L2.
+__device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  constexpr int GM = 4;
+  const int group = logical / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = logical % (GM * tiles_n);
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
 // compile-time selector of the steady-state or the checked stage body
 template <bool V>
 struct StageTag {
@@ -854,7 +870,9 @@ struct StageTag {
 
 }  // namespace pipe
 
-template <class PC, bool AK, bool BKM, int EPI, int SITE, int DT>
+// HALF = true: the launch for the tail tiles of a split GEMM (see launch_pipe); workgroup w
+// computes K half w % 2 of tail tile w / 2 and stores its fp32 partial sums.
+template <class PC, bool AK, bool BKM, int EPI, int SITE, int DT, bool HALF = false>
 __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g) {
   using namespace pipe;
   constexpr int NS = PC::NS, NW = PC::NW, WGM = PC::WGM, WTM = PC::WTM, WTN = PC::WTN;
@@ -868,15 +886,26 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
   const int split = SPLIT ? g.ffn : 0;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = SPLIT ? (g.ffn + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-  int wg = blockIdx.x, nwg = gridDim.x, logical = wg;
-  if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
-  constexpr int GM = 4;
-  const int group = logical / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int in_group = logical % (GM * tiles_n);
-  const int tm = first_m + in_group % gsize, tn = in_group / gsize;
+  // Whole tiles in an XCD-aware order (workgroup w runs on XCD w % 8, so each XCD takes a
+  // contiguous range of tiles); a split GEMM's tail tiles follow the whole ones (HALF launch).
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int n_full = tiles_m * tiles_n - g.tail_split;
+  int logical = wg, half = 0;
+  if constexpr (HALF) {
+    logical = n_full + (wg >> 1);
+    half = wg & 1;
+  } else if ((nwg & 7) == 0) {
+    logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  }
+  int tm, tn;
+  tile_coords(logical, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * (SPLIT ? BN / 2 : BN);
+  int kb = 0, ke = g.K;              // this workgroup's K range
+  if constexpr (HALF) {
+    const int mid = (g.K + BK - 1) / BK / 2 * BK;
+    if (half == 0) ke = mid;
+    else kb = mid;
+  }
 
   const bf16_t* A = (const bf16_t*)g.A;
   const bf16_t* B = (const bf16_t*)g.B;
@@ -892,21 +921,21 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = (g.K + BK - 1) / BK;
+  const int nk = (ke - kb + BK - 1) / BK;
   auto stage_a = [&](int b) { return smem + b * SE2; };
   auto stage_b = [&](int b) { return smem + b * SE2 + PC::SEA; };
   Streamer<AK, NW, BK, BM> sta;
   Streamer<BKM, NW, BK, BN> stb;
-  sta.init(A, g.lda, m0, g.M, wave, lane);
-  stb.init(B, g.ldb, n0, g.N, wave, lane, split);
+  sta.init(A, g.lda, m0, g.M, wave, lane, 0, kb);
+  stb.init(B, g.ldb, n0, g.N, wave, lane, split, kb);
   auto issue_stage = [&](int kt) {   // stages are issued in order 0, 1, 2, ...
     const int b = kt % NS;
-    if ((kt + 1) * BK <= g.K) {
+    if (kb + (kt + 1) * BK <= ke) {
       sta.issue_next(stage_a(b));
       stb.issue_next(stage_b(b));
     } else {                         // the last, partial stage: bounds-checked per lane
-      issue<AK, NW, BK, BM>(stage_a(b), A, g.lda, m0, g.M, kt * BK, g.K, wave, lane);
-      issue<BKM, NW, BK, BN>(stage_b(b), B, g.ldb, n0, g.N, kt * BK, g.K, wave, lane, split);
+      issue<AK, NW, BK, BM>(stage_a(b), A, g.lda, m0, g.M, kb + kt * BK, ke, wave, lane);
+      issue<BKM, NW, BK, BN>(stage_b(b), B, g.ldb, n0, g.N, kb + kt * BK, ke, wave, lane, split);
     }
   };
   // Wait until stage kt has landed (this wave's loads; the barrier that follows covers the
@@ -1008,15 +1037,55 @@ __global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_pipe_kernel(GemmArgs g)
     }
   };
   // iterations whose stage kt + NS is a full stage
-  const int n_steady = max(0, g.K / BK - NS);
+  const int n_steady = max(0, (ke - kb) / BK - NS);
   int kt = 0;
   for (; kt < n_steady; ++kt) run_stage(kt, StageTag<true>{});
   for (; kt < nk; ++kt) run_stage(kt, StageTag<false>{});
 
-  if constexpr (EPI != EPI_CE_STATS)
+  if constexpr (HALF) {   // a K half of a tail tile: its fp32 partial sums, in register order
+    float* p = g.tail_ws + ((size_t)wg * (BM * BN));
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          p[(((wave * MI + i) * NJ + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    (void)half;
+  } else if constexpr (EPI != EPI_CE_STATS)
     staged_epilogue<EPI, PC, DT>(g, acc, (float*)smem, m0, n0, wm, wn, lane);
   else
     gemm_epilogue<EPI, MI, NJ, DT>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+}
+
+// The tail tiles of a split launch: the two K halves' partial sums added in a fixed order (the
+// first half's plus the second's), then the tile's usual epilogue.
+template <class PC, int EPI, int DT>
+__global__ __launch_bounds__(PC::NT, PC::MINB) void gemm_tail_combine_kernel(GemmArgs g) {
+  using namespace pipe;
+  constexpr int NW = PC::NW, WGM = PC::WGM, MI = PC::MI, NJ = PC::NJ, BM = PC::BM, BN = PC::BN;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[PC::NS * PC::SE2];
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int n_full = tiles_m * tiles_n - g.tail_split;
+  int tm, tn;
+  tile_coords(n_full + (int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_assert(NW == PC::NT / 64, "waves");
+  const float* p0 = g.tail_ws + (size_t)blockIdx.x * 2 * (BM * BN);
+  const float* p1 = p0 + BM * BN;
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const size_t at = (size_t)(((wave * MI + i) * NJ + j) * 16 + e) * 64 + lane;
+        acc[i][j][e] = p0[at] + p1[at];
+      }
+  staged_epilogue<EPI, PC, DT>(g, acc, (float*)smem, tm * BM, tn * BN, wave % WGM, wave / WGM,
+                               lane);
 }
 
 // ------------------------------------------------------------------ fp32 SIMT GEMM
@@ -1109,14 +1178,50 @@ inline bool use_large(const GemmArgs& g) {
   return tiles >= 128;
 }
 
+// compute units of the current device (cached per device)
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <bool AK, bool BKM, int EPI, int SITE, int DT>
-void launch_pipe(const GemmArgs& g, hipStream_t st) {
+void launch_pipe(const GemmArgs& g_in, hipStream_t st) {
   using PC = typename PipeFor<AK, BKM>::type;
+  GemmArgs g = g_in;
   const int tiles_n = EPI == EPI_SWIGLU_FWD ? (g.ffn + PC::BN / 2 - 1) / (PC::BN / 2)
                                             : (g.N + PC::BN - 1) / PC::BN;
   const int tiles = ((g.M + PC::BM - 1) / PC::BM) * tiles_n;
-  hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles), dim3(PC::NT),
-                     0, st, g);
+  // A last wave of at most half the compute units would leave the others idle for a whole tile:
+  // with a workspace, the whole waves run first, then the tail tiles as two K halves each (one
+  // workgroup per half, so the halves fill the compute units), then a launch that adds them.
+  g.tail_split = 0;
+  constexpr bool CAN_SPLIT = EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32 || EPI == EPI_RESID ||
+                             EPI == EPI_ACCUM_F32;
+  const int cus = cu_count();
+  if (CAN_SPLIT && g.tail_ws && cus > 0 && tiles > cus && g.K >= 4 * PC::BK) {
+    const int tail = tiles % cus;
+    if (tail > 0 && 2 * tail <= cus && tail <= kTailMaxTiles &&
+        (size_t)tail * 2 * PC::BM * PC::BN * 4 <= g.tail_ws_bytes)
+      g.tail_split = tail;
+  }
+  hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT>), dim3(tiles - g.tail_split),
+                     dim3(PC::NT), 0, st, g);
+  if constexpr (CAN_SPLIT) {
+    if (g.tail_split) {
+      hipLaunchKernelGGL((gemm_pipe_kernel<PC, AK, BKM, EPI, SITE, DT, true>),
+                         dim3(2 * g.tail_split), dim3(PC::NT), 0, st, g);
+      hipLaunchKernelGGL((gemm_tail_combine_kernel<PC, EPI, DT>), dim3(g.tail_split),
+                         dim3(PC::NT), 0, st, g);
+    }
+  }
 }
 
 template <bool AK, bool BKM, int EPI, int SITE, int DT>
@@ -1301,6 +1406,21 @@ extern "C" int slide_gemm(int M, int N, int K, const void* A, int lda, int a_kma
   slide::GemmArgs g{M, N, K, A, lda, a_kmajor != 0, B, ldb, b_kmajor != 0, C, ldc, c_dtype,
                     R, ldr, alpha, accumulate != 0, dtype, "gemm", slide::SITE_GENERIC};
   SLIDE_TRY(slide::gemm_check(g));
+  return slide::gemm_launch(g, (hipStream_t)stream);
+}
+
+extern "C" size_t slide_gemm_tail_workspace_bytes(void) { return slide::kTailWsBytes; }
+
+extern "C" int slide_gemm_ws(int M, int N, int K, const void* A, int lda, int a_kmajor,
+                             const void* B, int ldb, int b_kmajor, void* C, int ldc, int c_dtype,
+                             const void* R, int ldr, float alpha, int accumulate, int dtype,
+                             void* ws, size_t ws_bytes, void* stream) {
+  slide::GemmArgs g{M, N, K, A, lda, a_kmajor != 0, B, ldb, b_kmajor != 0, C, ldc, c_dtype,
+                    R, ldr, alpha, accumulate != 0, dtype, "gemm", slide::SITE_GENERIC};
+  SLIDE_TRY(slide::gemm_check(g));
+  SLIDE_REQUIRE(!ws || slide::aligned16(ws), SLIDE_E_ARG, "gemm_ws: workspace must be 16-byte aligned");
+  g.tail_ws = (float*)ws;
+  g.tail_ws_bytes = ws ? ws_bytes : 0;
   return slide::gemm_launch(g, (hipStream_t)stream);
 }
 

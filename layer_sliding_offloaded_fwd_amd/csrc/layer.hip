@@ -73,6 +73,7 @@ struct Ws {
   float *lse, *cos_t, *sin_t;
   void *dm, *dgu, *dr2, *dx2, *dO, *dqkv, *dr;
   void *rms_ws, *attn_ws;
+  float* tail_ws;
   size_t bytes;
 };
 
@@ -109,6 +110,7 @@ size_t carve_bwd(void* base, const Dims& d, Ws& w) {
   w.dr = T(N * d.H);
   w.rms_ws = c.take<char>(rmsnorm_bwd_ws(d.N, d.H));
   w.attn_ws = c.take<char>(attention_bwd_ws(d.B, d.S, d.nq));
+  w.tail_ws = d.dt == SLIDE_F32 ? nullptr : (float*)c.take<char>(kTailWsBytes);
   return align_up(c.used, 256);
 }
 
@@ -124,10 +126,15 @@ Ws carve(void* base, const Dims& d, bool bwd) {
 inline const void* at(const void* p, size_t elems, size_t ts) { return (const char*)p + elems * ts; }
 inline void* at(void* p, size_t elems, size_t ts) { return (char*)p + elems * ts; }
 
+// tail_ws (kTailWsBytes, or null) lets a GEMM whose last wave of tiles is at most half full
+// split those tiles over K
 int gemm(int M, int N, int K, const void* A, int lda, bool ak, const void* B, int ldb, bool bk,
-         void* C, int ldc, const void* R, int dt, const char* name, int site, hipStream_t st) {
+         void* C, int ldc, const void* R, int dt, const char* name, int site, hipStream_t st,
+         float* tail_ws = nullptr) {
   GemmArgs g{M, N, K, A, lda, ak, B, ldb, bk, C, ldc, dt, R, R ? ldc : 0, 1.0f, false, dt, name,
              site};
+  g.tail_ws = tail_ws;
+  g.tail_ws_bytes = tail_ws ? kTailWsBytes : 0;
   return gemm_launch(g, st);
 }
 
@@ -165,25 +172,25 @@ int backward(const Dims& d, const slide_layer_cfg& c, const void* w, const void*
   SLIDE_TRY(gemm_swiglu_bwd(N, F, H, dy, H, at(w, off[5], ts), F, ws.gu, ws.dgu, ws.dm, d.dt,
                             "gemm_down_dx", SITE_DOWN_DX, st));
   SLIDE_TRY(gemm(H, F, N, dy, H, false, ws.m, F, false, at(g, off[5], ts), F, nullptr, d.dt,
-                 "gemm_down_dw", SITE_DOWN_DW, st));
+                 "gemm_down_dw", SITE_DOWN_DW, st, ws.tail_ws));
   SLIDE_TRY(gemm(N, H, 2 * F, ws.dgu, 2 * F, true, at(w, off[4], ts), H, false, ws.dr2, H,
-                 nullptr, d.dt, "gemm_gate_up_dx", SITE_GATE_UP_DX, st));
+                 nullptr, d.dt, "gemm_gate_up_dx", SITE_GATE_UP_DX, st, ws.tail_ws));
   SLIDE_TRY(gemm(2 * F, H, N, ws.dgu, 2 * F, false, ws.r2, H, false, at(g, off[4], ts), H,
-                 nullptr, d.dt, "gemm_gate_up_dw", SITE_GATE_UP_DW, st));
+                 nullptr, d.dt, "gemm_gate_up_dw", SITE_GATE_UP_DW, st, ws.tail_ws));
   SLIDE_TRY(rmsnorm_bwd(ws.dr2, ws.x2, at(w, off[3], ts), dy, ws.dx2, at(g, off[3], ts), N, H,
                         c.rms_eps, d.dt, ws.rms_ws, st));
   // attention half
   SLIDE_TRY(gemm(N, d.OD, H, ws.dx2, H, true, at(w, off[2], ts), d.OD, false, ws.dO, d.OD,
-                 nullptr, d.dt, "gemm_o_dx", SITE_O_DX, st));
+                 nullptr, d.dt, "gemm_o_dx", SITE_O_DX, st, ws.tail_ws));
   SLIDE_TRY(gemm(H, d.OD, N, ws.dx2, H, false, ws.o, d.OD, false, at(g, off[2], ts), d.OD,
-                 nullptr, d.dt, "gemm_o_dw", SITE_O_DW, st));
+                 nullptr, d.dt, "gemm_o_dw", SITE_O_DW, st, ws.tail_ws));
   SLIDE_TRY(attention_bwd(ws.qkv, ws.o, ws.lse, ws.dO, ws.dqkv, d.B, d.S, d.nq, d.nkv, d.d,
                           d.dt, ws.attn_ws, st));
   SLIDE_TRY(rope_apply(ws.dqkv, ws.cos_t, ws.sin_t, d.B, d.S, d.nq, d.nkv, d.d, 1, d.dt, st));
   SLIDE_TRY(gemm(N, H, d.QR, ws.dqkv, d.QR, true, at(w, off[1], ts), H, false, ws.dr, H, nullptr,
-                 d.dt, "gemm_qkv_dx", SITE_QKV_DX, st));
+                 d.dt, "gemm_qkv_dx", SITE_QKV_DX, st, ws.tail_ws));
   SLIDE_TRY(gemm(d.QR, H, N, ws.dqkv, d.QR, false, ws.r, H, false, at(g, off[1], ts), H, nullptr,
-                 d.dt, "gemm_qkv_dw", SITE_QKV_DW, st));
+                 d.dt, "gemm_qkv_dw", SITE_QKV_DW, st, ws.tail_ws));
   SLIDE_TRY(rmsnorm_bwd(ws.dr, x, at(w, off[0], ts), ws.dx2, dx, at(g, off[0], ts), N, H,
                         c.rms_eps, d.dt, ws.rms_ws, st));
   return SLIDE_OK;

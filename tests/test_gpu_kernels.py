@@ -81,6 +81,50 @@ def test_gemm_layouts_and_ragged_tails(dtype, ak, bk, M, N, K):
     assert_close(host(C4), ref, "f32", "C = A B (fp32 output)", tol=1e-5)
 
 
+# Tile counts just past whole waves of the 256 compute units (384 = 1.5 waves), so the last
+# 128 tiles run as two K halves each when a workspace is given; one shape with ragged edges.
+TAIL_SHAPES = [(6144, 4096, 264), (6100, 4090, 264)]
+
+
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, True), (False, False)])
+@pytest.mark.parametrize("M,N,K", TAIL_SHAPES)
+def test_gemm_split_tail_matches_oracle_and_unsplit(ak, bk, M, N, K):
+    print(f"gemm tail split a_kmajor={ak} b_kmajor={bk} M={M} N={N} K={K}", flush=True)
+    dtype, code = "bf16", sl.SLIDE_BF16
+    rng = _rng(3)
+    A = _round(rng.standard_normal((M, K)), dtype)
+    B = _round(rng.standard_normal((K, N)), dtype)
+    R = _round(rng.standard_normal((M, N)), dtype)
+    ref = A @ B
+    lda = K if ak else _r8(M)
+    ldb = K if bk else _r8(N)
+    dA = dev(A if ak else np.pad(A.T, ((0, 0), (0, lda - M))), dtype)
+    dB = dev(B.T.copy() if bk else np.pad(B, ((0, 0), (0, ldb - N))), dtype)
+    nb = sl.slide_gemm_tail_workspace_bytes()
+    buf = ws(nb)
+    C1, C2 = empty((M, N), dtype), empty((M, N), dtype)
+    sl.slide_gemm_ws(M, N, K, dA, lda, ak, dB, ldb, bk, C1, N, code, dtype=code, ws=buf,
+                     ws_bytes=nb, stream=stream())
+    sl.slide_gemm(M, N, K, dA, lda, ak, dB, ldb, bk, C2, N, code, dtype=code, stream=stream())
+    R1 = empty((M, N), dtype)
+    sl.slide_gemm_ws(M, N, K, dA, lda, ak, dB, ldb, bk, R1, N, code, R=dev(R, dtype), ldr=N,
+                     alpha=0.5, dtype=code, ws=buf, ws_bytes=nb, stream=stream())
+    F1 = torch.full((M, N), 1.0, dtype=torch.float32, device=DEV)
+    sl.slide_gemm_ws(M, N, K, dA, lda, ak, dB, ldb, bk, F1, N, sl.SLIDE_F32, accumulate=True,
+                     dtype=code, ws=buf, ws_bytes=nb, stream=stream())
+    torch.cuda.synchronize()
+    assert_close(host(C1), ref, dtype, "C = A B (split tail)", tol=GEMM_TOL[dtype])
+    assert_close(host(R1), 0.5 * ref + R, dtype, "C = R + 0.5 A B (split tail)",
+                 tol=GEMM_TOL[dtype])
+    assert_close(host(F1), 1.0 + ref, "f32", "C += A B (split tail, fp32)", tol=1e-5)
+    # tiles outside the tail are computed exactly as without the split; the tail's 128 tiles
+    # differ at most by the rounding of the one addition of the two halves
+    ndiff = int((_bits(C1) != _bits(C2)).sum())
+    print(f"  elements differing from the unsplit GEMM: {ndiff}", flush=True)
+    assert ndiff <= 128 * 256 * 256
+    assert_close(host(C1), host(C2), dtype, "split vs unsplit", tol=1e-2)
+
+
 # (M, F, K): fused launches (both directions) with ragged rows, a ragged last tile (F % 128 and
 # F % 256 != 0) and a partial k-tile; the same with full tiles and a steady k loop; a size below
 # the pipelined kernel's threshold (the GEMM and the elementwise kernel run instead)
