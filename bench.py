@@ -156,6 +156,9 @@ def _parse():
                          "backward")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers of the 123b slice (default 12, fewer if host RAM is short)")
+    ap.add_argument("--copy-engine", default="hsa", choices=["hip", "hsa"],
+                    help="slot-ring copies on two host-optimised copy engines chosen through "
+                         "the HSA runtime (default) or through hipMemcpyAsync")
     ap.add_argument("--activations", default="hbm", choices=["hbm", "recompute", "host"],
                     help="forward state for the backward: intermediates kept in HBM (default), "
                          "layer inputs kept and the forward recomputed, or layer inputs slid to "
@@ -344,8 +347,14 @@ def host_roofline(w, threads, step_s):
     host_bytes = adam_bytes + h2d + d2h
     bound_s = host_bytes / (triad_best * 1e9)
     link = host_link(2 * n)
-    link_s = max(h2d / (link["h2d_both_gbs"] * 1e9), d2h / (link["d2h_both_gbs"] * 1e9))
-    link.update(step_bound_ms=round(link_s * 1e3, 1), frac=round(link_s / step_s, 4))
+    # both directions at once at the probe's rate, scaled (per direction) from the engine the
+    # runtime used to the best engine where the probe's own copy ran slower than that
+    f_up = max(1.0, link["engine_best_h2d_gbs"] / link["h2d_alone_gbs"])
+    f_dn = max(1.0, link["engine_best_d2h_gbs"] / link["d2h_alone_gbs"])
+    link_s = max(h2d / (link["h2d_both_gbs"] * f_up * 1e9), d2h / (link["d2h_both_gbs"] * f_dn * 1e9))
+    placed_s = max(h2d / (link["h2d_both_gbs"] * 1e9), d2h / (link["d2h_both_gbs"] * 1e9))
+    link.update(step_bound_ms=round(link_s * 1e3, 1), frac=round(link_s / step_s, 4),
+                frac_as_placed=round(placed_s / step_s, 4))
     return {"bound": "host_dram", "adamw_bytes": adam_bytes, "h2d_bytes": h2d, "d2h_bytes": d2h,
             "peak_triad_gbs": round(triad_best, 1), "triad_median_gbs": round(triad_med, 1),
             "triad_threads": threads,
@@ -365,9 +374,10 @@ def host_link(nbytes, reps=3):
     """Host-link rates of the slot-ring copies, measured alone: one layer's bf16 weights
     (nbytes) between pinned host memory and HBM with hipMemcpyAsync on side streams, each
     direction alone and both at once (the backward's weight reloads run beside its gradient
-    flushes). Best of `reps`. The step's link bound is its upload and flush bytes at the rates of
-    both directions at once."""
+    flushes), each copy timed with events on its own stream. Best of `reps`. The step's link
+    bound is its upload and flush bytes at the rates of both directions at once."""
     import torch
+    import layer_sliding_offloaded_fwd_amd as sl
     h_src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     h_dst = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     d_dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -375,25 +385,41 @@ def host_link(nbytes, reps=3):
     up, down = torch.cuda.Stream(), torch.cuda.Stream()
 
     def timed(h2d, d2h):
-        best = float("inf")
+        """(up GB/s, down GB/s), best of reps, each direction timed on its own stream"""
+        best = [float("inf"), float("inf")]
         for _ in range(reps):
             torch.cuda.synchronize()
-            a = time.perf_counter()
-            if h2d:
-                with torch.cuda.stream(up):
-                    d_dst.copy_(h_src, non_blocking=True)
-            if d2h:
-                with torch.cuda.stream(down):
-                    h_dst.copy_(d_src, non_blocking=True)
+            ev = []
+            for on, st, dst, src in ((h2d, up, d_dst, h_src), (d2h, down, h_dst, d_src)):
+                if not on:
+                    ev.append(None)
+                    continue
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(st):
+                    e0.record(st)
+                    dst.copy_(src, non_blocking=True)
+                    e1.record(st)
+                ev.append((e0, e1))
             torch.cuda.synchronize()
-            best = min(best, time.perf_counter() - a)
-        return nbytes / best / 1e9
+            for i, e in enumerate(ev):
+                if e:
+                    best[i] = min(best[i], e[0].elapsed_time(e[1]) * 1e-3)
+        return tuple(nbytes / t / 1e9 if t < float("inf") else 0.0 for t in best)
 
     timed(True, True)   # warm-up
-    h2d_alone, d2h_alone, both = timed(True, False), timed(False, True), timed(True, True)
+    h2d_alone, d2h_alone = timed(True, False)[0], timed(False, True)[1]
+    h2d_both, d2h_both = timed(True, True)
+    # The rate a copy gets depends on the copy engine the runtime places it on (the engines built
+    # for copies between GPUs run the host link at a fraction of the host-optimised ones' rate),
+    # and hipMemcpyAsync's placement can stay on a slow engine for a while. The link's own rate
+    # is that of the best engine, timed one engine at a time.
+    d2h_ms, h2d_ms, _ = sl.slide_host_link_engine_rates(d_src, h_dst, nbytes, 1)
+    best = lambda ms: max((nbytes / (t * 1e-3) / 1e9 for t in ms if t > 0), default=0.0)
     return {"bytes_per_copy": nbytes, "h2d_alone_gbs": round(h2d_alone, 1),
-            "d2h_alone_gbs": round(d2h_alone, 1), "h2d_both_gbs": round(both, 1),
-            "d2h_both_gbs": round(both, 1)}
+            "d2h_alone_gbs": round(d2h_alone, 1), "h2d_both_gbs": round(h2d_both, 1),
+            "d2h_both_gbs": round(d2h_both, 1),
+            "engine_best_h2d_gbs": round(best(h2d_ms), 1),
+            "engine_best_d2h_gbs": round(best(d2h_ms), 1)}
 
 
 def run_step(w, args):
@@ -426,7 +452,8 @@ def run_step(w, args):
     eng = SlideEngine(spec, w.batch, w.seq, n_slots=w.ring_slots, ce_chunk=w.ce_chunk,
                       hp=AdamW(), adam_threads=threads, timeline=True,
                       activations=args.activations, keep_records=args.steps + args.warmup,
-                      embed_split=args.embed_split, **tier_kw)
+                      embed_split=args.embed_split, copy_engine=args.copy_engine, **tier_kw)
+    copy_engine = eng.copy_engine     # "hip" if the HSA ring could not be created
     eng.init_random(seed=0, std=0.02,
                     progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
     toks = [draw_tokens(w.batch, w.seq, w.vocab, seed=1 + i)
@@ -535,7 +562,7 @@ def run_step(w, args):
                    "ffn": c.ffn, "vocab": w.vocab, "global_batch": w.batch, "seq_len": w.seq,
                    "ring_slots": w.ring_slots, "ce_chunk": w.ce_chunk,
                    "parallelism": "single GPU, layers streamed from host",
-                   "adam_threads": threads,
+                   "adam_threads": threads, "copy_engine": copy_engine,
                    "activations": {"hbm": "intermediates kept in HBM (no recompute)",
                                    "recompute": "layer inputs kept in HBM, forward recomputed",
                                    "host": "layer inputs slid to host memory, forward "

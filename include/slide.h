@@ -289,8 +289,14 @@ enum { SLIDE_SLOT_FREE = 0, SLIDE_SLOT_LOADING = 1, SLIDE_SLOT_IN_USE = 2,
        SLIDE_SLOT_FLUSHING = 3 };
 /* engine: SLIDE_ENGINE_HIP moves data with hipMemcpyAsync on the h2d / d2h streams;
  * SLIDE_ENGINE_HOST treats dev_base as host memory and copies with memcpy on a host thread
- * (events become host flags), which lets the state machine run and be tested without a GPU. */
-enum { SLIDE_ENGINE_HIP = 0, SLIDE_ENGINE_HOST = 1 };
+ * (events become host flags), which lets the state machine run and be tested without a GPU;
+ * SLIDE_ENGINE_HSA copies on two chosen host-optimised copy engines (one per direction) through
+ * the HSA runtime, from a host thread per direction that waits on the host for the HIP events
+ * a copy depends on and for the copy's completion (the h2d / d2h streams are unused). With it,
+ * slide_slot_ring_acquire blocks the calling thread until the slot's load, and any flush still
+ * reading the slot, has completed (at most 60 s, then SLIDE_E_TIMEOUT); no GPU queue waits on
+ * the host. dev_base must be device memory and the host buffers pinned memory. */
+enum { SLIDE_ENGINE_HIP = 0, SLIDE_ENGINE_HOST = 1, SLIDE_ENGINE_HSA = 2 };
 int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_bytes, size_t g_bytes,
                            void* dev_base, void* h2d_stream, void* d2h_stream, int engine);
 /* Pick the next FREE slot (round-robin), start the copy host_w -> slot weights, mark LOADING.
@@ -340,6 +346,11 @@ int slide_slot_ring_reuse(slide_ring* r, int layer, int* slot_out);
 int slide_slot_ring_state(slide_ring* r, int slot, int* state, int* layer);
 /* Find the slot currently holding `layer` (LOADING / IN_USE / FLUSHING), or -1. */
 int slide_slot_ring_find(slide_ring* r, int layer, int* slot_out);
+/* Host time (CLOCK_MONOTONIC seconds) at which the flush named by ticket landed, for the
+ * host-timed engines (HOST, HSA; SLIDE_E_UNSUPPORTED for HIP). SLIDE_E_STATE before it has
+ * landed; SLIDE_E_ARG for an unknown ticket or one whose record was reused (the last 1024
+ * flushes are kept). */
+int slide_slot_ring_ticket_time(slide_ring* r, uint64_t ticket, double* t_done);
 int slide_slot_ring_destroy(slide_ring* r);
 
 /* Host-link diagnostic (summary, section 2A: layers and gradients cross the host link

@@ -10,7 +10,7 @@ SLIDE_E_STATE, SLIDE_E_TIMEOUT, SLIDE_E_UNSUPPORTED, SLIDE_E_NONFINITE = -5, -6,
 SLIDE_E_IO = -9
 SLIDE_TIER_DIRECT, SLIDE_TIER_UNLINK = 1, 2
 SLIDE_F32, SLIDE_BF16, SLIDE_F16 = 0, 1, 2
-SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST = 0, 1
+SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_ENGINE_HSA = 0, 1, 2
 SLOT_FREE, SLOT_LOADING, SLOT_IN_USE, SLOT_FLUSHING = 0, 1, 2, 3
 ERROR_NAMES = {0: "SLIDE_OK", -1: "SLIDE_E_ARG", -2: "SLIDE_E_SHAPE", -3: "SLIDE_E_WORKSPACE",
                -4: "SLIDE_E_HIP", -5: "SLIDE_E_STATE", -6: "SLIDE_E_TIMEOUT",
@@ -94,6 +94,7 @@ SIGNATURES = {
     "slide_slot_ring_state": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
     "slide_slot_ring_find": (I, [P, I, ctypes.POINTER(I)]),
     "slide_slot_ring_destroy": (I, [P]),
+    "slide_slot_ring_ticket_time": (I, [P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_double)]),
     "slide_slot_ring_inject_fault": (I, [P, I, I]),
     "slide_cpu_adamw": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64, ctypes.POINTER(AdamWHp), I]),
     "slide_cpu_adamw_scalar_for_test": (I, [P, P, I, P, P, P, SZ, ctypes.c_int64,

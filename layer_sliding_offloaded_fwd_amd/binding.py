@@ -7,12 +7,13 @@ runs in libslide's kernels; a non-zero status raises SlideError carrying slide_l
 import ctypes
 
 from ._capi import (AdamWHp, CeCfg, LayerCfg, SlideError, call, lib, SLIDE_BF16, SLIDE_F16,
-                    SLIDE_F32, SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_TIER_DIRECT,
+                    SLIDE_F32, SLIDE_ENGINE_HIP, SLIDE_ENGINE_HOST, SLIDE_ENGINE_HSA,
+                    SLIDE_TIER_DIRECT,
                     SLIDE_TIER_UNLINK)
 
 __all__ = [
     "LayerCfg", "CeCfg", "AdamWHp", "SlideError", "SLIDE_BF16", "SLIDE_F16", "SLIDE_F32",
-    "SLIDE_ENGINE_HIP",
+    "SLIDE_ENGINE_HIP", "SLIDE_ENGINE_HSA",
     "SLIDE_ENGINE_HOST", "slide_layer_param_count", "slide_layer_param_offsets",
     "slide_layer_workspace_bytes", "slide_layer_fwd", "slide_layer_bwd",
     "slide_layer_saved_bytes", "slide_layer_fwd_save", "slide_layer_bwd_saved",
@@ -308,6 +309,12 @@ class SlotRing:
 
     def release(self, slot, compute_stream=None):
         call("slide_slot_ring_release", self._h, slot, _s(compute_stream))
+
+    def ticket_time(self, ticket):
+        """Host time (time.perf_counter's clock) at which a flush landed (host-timed engines)."""
+        t = ctypes.c_double()
+        call("slide_slot_ring_ticket_time", self._h, ctypes.c_uint64(ticket), ctypes.byref(t))
+        return t.value
 
     def state(self, slot):
         st = ctypes.c_int()

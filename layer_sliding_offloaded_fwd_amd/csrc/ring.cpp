@@ -12,7 +12,20 @@
 //   release  records an event on the compute stream (the next load into the slot waits on it)
 // The host engine runs the same state machine on host memory with a copy thread, so the
 // bookkeeping and its failure paths can be exercised without a GPU.
+//
+// The HSA engine moves the same bytes on chosen copy engines. hipMemcpyAsync lets the runtime
+// pick the engine, and on this GPU the engines built for copies between GPUs run the host link
+// at a quarter of the host-optimised ones' rate or less; whole steps' gradient copies have landed
+// there. Here a host thread per direction runs the copies in order with
+// hsa_amd_memory_async_copy_on_engine: before a copy it waits on the host for the HIP events
+// the HIP engine would make the copy stream wait for (the slot's release for a load, the
+// compute stream's work for a flush), and it waits on the host for the copy's completion
+// signal. No GPU queue ever waits on a host-written value; instead acquire blocks the calling
+// thread until the slot's load (and any flush still reading it) has completed, as the host
+// engine's acquire does. Every host wait is bounded.
 #include <hip/hip_runtime.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
 #include <string.h>
 
 #include <atomic>
@@ -35,11 +48,21 @@ using slide::fail;
 namespace {
 
 constexpr int kTicketPool = 1024;
+// Copy engines of the HSA engine: two of the host-optimised ones (engines 0-3 run the host link
+// at ~57 GB/s in both directions on this GPU, the others at 7-13 GB/s device to host), one per
+// direction so that uploads and gradient copies run side by side.
+constexpr int kHsaEngineH2D = 1, kHsaEngineD2H = 0;
 
 // ------------------------------------------------------------------ host engine pieces
 struct HostEvent {
   std::atomic<int> st{1};  // 0 pending, 1 done, 2 failed
+  double t_done = 0;       // CLOCK_MONOTONIC seconds at completion (HSA engine)
 };
+
+double mono_now() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
 
 struct HostCopyQueue {
   struct Job {
@@ -100,7 +123,115 @@ struct HostCopyQueue {
         continue;
       }
       memcpy(j.dst, j.src, j.n);
+      j.done->t_done = mono_now();
       j.done->st.store(1);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ HSA engine pieces
+constexpr int kHsaWaitMs = 60000;   // bound of every host wait of the HSA engine's threads
+
+// The HSA agent that owns a pointer (the GPU for device memory, the CPU for pinned host memory).
+bool agent_of(const void* p, hsa_agent_t* agent) {
+  hsa_amd_pointer_info_t info;
+  memset(&info, 0, sizeof info);
+  info.size = sizeof info;
+  if (hsa_amd_pointer_info(p, &info, nullptr, nullptr, nullptr) != HSA_STATUS_SUCCESS)
+    return false;
+  if (info.type != HSA_EXT_POINTER_TYPE_HSA && info.type != HSA_EXT_POINTER_TYPE_LOCKED)
+    return false;
+  *agent = info.agentOwner;
+  return true;
+}
+
+struct HsaCopyQueue {
+  struct Job {
+    hipEvent_t gpu_wait = nullptr;   // GPU work to finish first (HIP event)
+    bool own_gpu_wait = false;       // destroy the event once waited for
+    void* dst;
+    const void* src;
+    size_t n;
+    bool to_device;
+    std::shared_ptr<HostEvent> done;
+  };
+  hsa_agent_t gpu{};
+  uint32_t engine = 0;               // hsa_amd_sdma_engine_id_t bit
+  hsa_signal_t sig{};
+  std::mutex mu;
+  std::condition_variable cv;
+  std::deque<Job> q;
+  bool stop = false;
+  std::thread th;
+
+  HsaCopyQueue(hsa_agent_t g, uint32_t eng) : gpu(g), engine(eng) {
+    hsa_signal_create(1, 0, nullptr, &sig);
+    th = std::thread([this] { run(); });
+  }
+  ~HsaCopyQueue() {
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      stop = true;
+    }
+    cv.notify_all();
+    th.join();
+    if (sig.handle) hsa_signal_destroy(sig);
+  }
+  void push(Job j) {
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      q.push_back(std::move(j));
+    }
+    cv.notify_all();
+  }
+  // 0 done, 1 failed, 2 ran out of time
+  int wait_gpu(hipEvent_t e) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+      const hipError_t r = hipEventQuery(e);
+      if (r == hipSuccess) return 0;
+      if (r != hipErrorNotReady) return 1;
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(kHsaWaitMs)) return 2;
+      // a copy takes milliseconds: polling every 200 us starts it at most that late, and leaves
+      // the cores to the CPU optimizer
+      std::this_thread::sleep_for(std::chrono::microseconds(200));
+    }
+  }
+  int copy(const Job& j) {
+    hsa_agent_t host_agent;
+    if (!agent_of(j.to_device ? j.src : j.dst, &host_agent)) return 1;
+    hsa_signal_store_relaxed(sig, 1);
+    const hsa_status_t st =
+        j.to_device
+            ? hsa_amd_memory_async_copy_on_engine(j.dst, gpu, j.src, host_agent, j.n, 0, nullptr,
+                                                  sig, (hsa_amd_sdma_engine_id_t)engine, true)
+            : hsa_amd_memory_async_copy_on_engine(j.dst, host_agent, j.src, gpu, j.n, 0, nullptr,
+                                                  sig, (hsa_amd_sdma_engine_id_t)engine, true);
+    if (st != HSA_STATUS_SUCCESS) return 1;
+    for (int w = 0; w < kHsaWaitMs / 100; ++w)   // 100 ms per wait
+      if (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1, 100000000,
+                                    HSA_WAIT_STATE_BLOCKED) < 1)
+        return 0;
+    return 2;
+  }
+  void run() {
+    for (;;) {
+      Job j;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv.wait(lk, [&] { return stop || !q.empty(); });
+        if (stop && q.empty()) return;
+        j = std::move(q.front());
+        q.pop_front();
+      }
+      int rc = 0;
+      if (j.gpu_wait) {
+        rc = wait_gpu(j.gpu_wait);
+        if (j.own_gpu_wait) hipEventDestroy(j.gpu_wait);
+      }
+      if (rc == 0) rc = copy(j);
+      j.done->t_done = mono_now();
+      j.done->st.store(rc == 0 ? 1 : 2);
     }
   }
 };
@@ -137,6 +268,9 @@ struct slide_ring {
   std::vector<uint64_t> ticket_id;
   // host engine
   std::unique_ptr<HostCopyQueue> hq_h2d, hq_d2h;
+  // HSA engine
+  std::unique_ptr<HsaCopyQueue> sq_h2d, sq_d2h;
+  bool hsa_up = false;
   int fault_mode = 0, fault_count = 0;
 
   char* w_ptr(int s) { return base + (size_t)s * (wb + gb); }
@@ -147,6 +281,8 @@ struct slide_ring {
     --fault_count;
     return fault_mode;
   }
+
+  bool host_events() const { return engine != SLIDE_ENGINE_HIP; }
 
   // record an event "now" on a compute stream (host engine: host compute is synchronous)
   int record_compute(Ev& e, void* stream) {
@@ -169,7 +305,7 @@ struct slide_ring {
     auto t0 = std::chrono::steady_clock::now();
     for (;;) {
       int st;
-      if (engine == SLIDE_ENGINE_HOST) {
+      if (host_events()) {
         st = e.host->st.load();
         if (st == 2) return fail(SLIDE_E_HIP, "slot ring: %s: copy failed", what);
         if (st == 1) return SLIDE_OK;
@@ -216,8 +352,16 @@ extern "C" int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_by
   if (w_bytes == 0) return fail(SLIDE_E_ARG, "slot ring create: w_bytes must be > 0");
   if ((w_bytes % 256) || (g_bytes % 256))
     return fail(SLIDE_E_ARG, "slot ring create: w_bytes and g_bytes must be multiples of 256");
-  if (engine != SLIDE_ENGINE_HIP && engine != SLIDE_ENGINE_HOST)
+  if (engine != SLIDE_ENGINE_HIP && engine != SLIDE_ENGINE_HOST && engine != SLIDE_ENGINE_HSA)
     return fail(SLIDE_E_ARG, "slot ring create: unknown engine %d", engine);
+  hsa_agent_t gpu{};
+  if (engine == SLIDE_ENGINE_HSA) {
+    if (hsa_init() != HSA_STATUS_SUCCESS) return fail(SLIDE_E_HIP, "slot ring create: hsa_init failed");
+    if (!agent_of(dev_base, &gpu)) {
+      hsa_shut_down();
+      return fail(SLIDE_E_ARG, "slot ring create: dev_base is not device memory known to HSA");
+    }
+  }
   auto* r = new slide_ring();
   r->n = n_slots;
   r->wb = w_bytes;
@@ -232,6 +376,11 @@ extern "C" int slide_slot_ring_create(slide_ring** out, int n_slots, size_t w_by
   if (engine == SLIDE_ENGINE_HOST) {
     r->hq_h2d.reset(new HostCopyQueue());
     r->hq_d2h.reset(new HostCopyQueue());
+  }
+  if (engine == SLIDE_ENGINE_HSA) {
+    r->hsa_up = true;
+    r->sq_h2d.reset(new HsaCopyQueue(gpu, 1u << kHsaEngineH2D));
+    r->sq_d2h.reset(new HsaCopyQueue(gpu, 1u << kHsaEngineD2H));
   }
   *out = r;
   return SLIDE_OK;
@@ -278,6 +427,20 @@ int load_part(slide_ring* r, int layer, const void* host_w, size_t off, size_t n
     sl.load_ev.host = j.done;
     sl.load_ev.valid = true;
     r->hq_h2d->push(std::move(j));
+  } else if (r->engine == SLIDE_ENGINE_HSA) {
+    HsaCopyQueue::Job j;
+    // the slot's release event stays valid until the slot is released again, which needs
+    // this load to complete first (acquire waits for it)
+    if (first && sl.free_ev.valid) j.gpu_wait = sl.free_ev.hip;
+    j.dst = dst;
+    j.src = src;
+    j.n = n;
+    j.to_device = true;
+    j.done = std::make_shared<HostEvent>();
+    j.done->st.store(0);
+    sl.load_ev.host = j.done;
+    sl.load_ev.valid = true;
+    r->sq_h2d->push(std::move(j));
   } else {
     if (first && sl.free_ev.valid && hipStreamWaitEvent(r->h2d, sl.free_ev.hip, 0) != hipSuccess)
       return fail(SLIDE_E_HIP, "slot ring %s: hipStreamWaitEvent failed", what);
@@ -339,12 +502,14 @@ extern "C" int slide_slot_ring_acquire(slide_ring* r, int slot, void* compute_st
   if (sl.state != SLIDE_SLOT_LOADING)
     return fail(SLIDE_E_STATE, "slot ring acquire: slot %d is %s, expected LOADING", slot,
                 state_name(sl.state));
-  if (r->engine == SLIDE_ENGINE_HOST) {
+  if (r->host_events()) {
     Ev le = sl.load_ev, fe = sl.flush_ev;
     lk.unlock();
-    // host compute runs synchronously, so the stream-side wait becomes a bounded host wait
-    rc = r->host_wait(le, 10000, "acquire (load)");
-    if (rc == SLIDE_OK) rc = r->host_wait(fe, 10000, "acquire (pending flush)");
+    // host compute runs synchronously (host engine), and no GPU queue waits on a host-signalled
+    // copy (HSA engine): the stream-side wait becomes a bounded host wait
+    const int limit = r->engine == SLIDE_ENGINE_HSA ? kHsaWaitMs : 10000;
+    rc = r->host_wait(le, limit, "acquire (load)");
+    if (rc == SLIDE_OK) rc = r->host_wait(fe, limit, "acquire (pending flush)");
     if (rc) return rc;
     lk.lock();
   } else {
@@ -394,6 +559,21 @@ int flush_part(slide_ring* r, int slot, void* host_g, size_t off, size_t n,
     te.host = j.done;
     te.valid = true;
     r->hq_d2h->push(std::move(j));
+  } else if (r->engine == SLIDE_ENGINE_HSA) {
+    Ev cdone;
+    if ((rc = r->record_compute(cdone, compute_stream))) return rc;
+    HsaCopyQueue::Job j;
+    j.gpu_wait = cdone.hip;
+    j.own_gpu_wait = true;
+    j.dst = dst;
+    j.src = src;
+    j.n = n;
+    j.to_device = false;
+    j.done = std::make_shared<HostEvent>();
+    j.done->st.store(0);
+    te.host = j.done;
+    te.valid = true;
+    r->sq_d2h->push(std::move(j));
   } else {
     Ev cdone;
     if ((rc = r->record_compute(cdone, compute_stream))) return rc;
@@ -490,8 +670,34 @@ extern "C" int slide_slot_ring_inject_fault(slide_ring* r, int fail_mode, int co
   return SLIDE_OK;
 }
 
+extern "C" int slide_slot_ring_ticket_time(slide_ring* r, uint64_t ticket, double* t_done) {
+  if (!r || !t_done) return fail(SLIDE_E_ARG, "slot ring ticket_time: null pointer");
+  if (r->engine == SLIDE_ENGINE_HIP)
+    return fail(SLIDE_E_UNSUPPORTED, "slot ring ticket_time: host-timed engines only");
+  std::lock_guard<std::mutex> lk(r->mu);
+  if (ticket == 0 || ticket >= r->next_ticket || r->ticket_id[ticket % kTicketPool] != ticket)
+    return fail(SLIDE_E_ARG, "slot ring ticket_time: unknown or recycled ticket %llu",
+                (unsigned long long)ticket);
+  const Ev& e = r->ticket_ev[ticket % kTicketPool];
+  if (!e.host || e.host->st.load() != 1)
+    return fail(SLIDE_E_STATE, "slot ring ticket_time: ticket %llu has not landed",
+                (unsigned long long)ticket);
+  *t_done = e.host->t_done;
+  return SLIDE_OK;
+}
+
 extern "C" int slide_slot_ring_destroy(slide_ring* r) {
   if (!r) return fail(SLIDE_E_ARG, "slot ring destroy: null handle");
+  if (r->engine == SLIDE_ENGINE_HSA) {
+    // the copy threads finish their queued copies (each bounded) and exit
+    r->sq_h2d.reset();
+    r->sq_d2h.reset();
+    for (auto& s : r->slots)
+      if (s.free_ev.hip) hipEventDestroy(s.free_ev.hip);
+    if (r->hsa_up) hsa_shut_down();
+    delete r;
+    return SLIDE_OK;
+  }
   if (r->engine == SLIDE_ENGINE_HIP) {
     auto drop = [](Ev& e) {
       if (e.hip) hipEventDestroy(e.hip);

@@ -29,6 +29,7 @@ import json
 import mmap
 import os
 import threading
+import sys
 import time
 from dataclasses import dataclass, field
 
@@ -78,7 +79,8 @@ def pinned_bytes(n, esize, min_bytes=0):
 
 class _Job:
     __slots__ = ("name", "wait", "p", "g", "m", "v", "out", "n", "post", "done", "t_start",
-                 "t_end", "t_ready", "step", "priority", "seq", "tier", "nonfinite", "off",
+                 "t_end", "t_ready", "t_landed", "step", "priority", "seq", "tier", "nonfinite",
+                 "off",
                  "rows", "row_len", "adam_t", "hp", "cancelled", "packed")
 
     def __init__(self, name, wait, p, g, m, v, out, n, step, priority, post=None, tier=None,
@@ -100,6 +102,7 @@ class _Job:
         self.seq = 0
         self.done = threading.Event()
         self.t_start = self.t_end = self.t_ready = 0.0
+        self.t_landed = None   # host time its gradient copy landed (host-timed copy engines)
 
 
 class _PinnedPool:
@@ -193,7 +196,8 @@ class SlideEngine:
                  save_activations=True, activations=None, x_slots=4, state_tier=None,
                  tier_layers=None, tier_chunk=0, tier_io_threads=8, check_finite=False,
                  keep_records=64, on_gradient=None, embed_split=False, loss_scale=2.0 ** 16,
-                 scale_growth_interval=2000, min_loss_scale=1.0, boundary_parts=8):
+                 scale_growth_interval=2000, min_loss_scale=1.0, boundary_parts=8,
+                 copy_engine="hsa"):
         """activations: where the forward's state for the backward lives.
           "hbm" (default): every layer's intermediates stay in HBM; no recompute.
           "recompute": only each layer's input stays in HBM; the backward re-runs the forward.
@@ -211,6 +215,12 @@ class SlideEngine:
           is flushed; the CPU worker then refuses the update of a block whose gradient is not
           finite (SlideError SLIDE_E_NONFINITE, raised by the next wait), so the fp32 master
           weights are never overwritten from it.
+        copy_engine: "hsa" (default: the slot ring's copies on two host-optimised copy engines
+          chosen through the HSA runtime, ordered by host threads; the ring's acquire then
+          blocks until the slot's load is in) or "hip" (hipMemcpyAsync, which picks the copy
+          engine itself and has put whole steps' gradient copies on engines that run the host
+          link at a quarter of its rate). If the HSA ring cannot be created, the engine falls
+          back to "hip" with a warning; copy_engine then says which one runs.
         keep_records: how many of the latest steps' records (events, job timings) are kept for
           analyse(); older ones are dropped, so a long run does not accumulate them.
         loss_scale, scale_growth_interval, min_loss_scale: dynamic loss scaling of fp16 compute
@@ -363,8 +373,20 @@ class SlideEngine:
             self.nf_dev = torch.zeros(len(names), dtype=torch.int32, device=dev)
             self.nf_host = self.pinned.tensor(len(names), torch.int32)
         self.ring_mem = torch.empty(self.n_slots * 2 * self.w_bytes, dtype=torch.uint8, device=dev)
-        self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
-                               self.h2d, self.d2h)
+        if copy_engine not in ("hip", "hsa"):
+            raise ValueError(f"copy_engine must be 'hip' or 'hsa', not {copy_engine!r}")
+        self.copy_engine = copy_engine
+        if copy_engine == "hsa":
+            try:
+                self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
+                                       self.h2d, self.d2h, engine=B.SLIDE_ENGINE_HSA)
+            except B.SlideError as e:
+                print(f"[slide] HSA copy engines unavailable ({e}); using hipMemcpyAsync",
+                      file=sys.stderr, flush=True)
+                self.copy_engine = "hip"
+        if self.copy_engine == "hip":
+            self.ring = B.SlotRing(self.n_slots, self.w_bytes, self.w_bytes, self.ring_mem,
+                                   self.h2d, self.d2h, engine=B.SLIDE_ENGINE_HIP)
         if activations == "host":
             # a ring of x_slots device buffers: layer input i lives in slot i % x_slots; the
             # inputs a later layer's output would overwrite are copied to pinned host memory
@@ -619,6 +641,8 @@ class SlideEngine:
         if isinstance(job.wait, int):
             try:
                 self.ring.wait_flush(job.wait, 0)
+                if self.copy_engine == "hsa" and job.t_landed is None:
+                    job.t_landed = self.ring.ticket_time(job.wait)
                 return True
             except B.SlideError as e:
                 if e.code == -6:   # SLIDE_E_TIMEOUT: still in flight
@@ -1188,7 +1212,8 @@ class SlideEngine:
                 ticket = self.ring.flush(s, self.layers[i].grad_host, c)
             if self.timeline:
                 rec["layers"].setdefault(i, {})["bwd"] = (e_a, e_b)
-                rec["layers"][i]["d2h_end"] = self._ev(self.d2h)
+                if self.copy_engine == "hip":   # else: the landed times of the layer's jobs
+                    rec["layers"][i]["d2h_end"] = self._ev(self.d2h)
             if i == 0 and self.l0_parts is not None:
                 rec["jobs"].extend(self._submit_parts(self.layers[0], tickets, "layer0", 0))
             else:
@@ -1282,8 +1307,10 @@ class SlideEngine:
             prev = -1e30
             for i in range(self.L - 1, -1, -1):
                 lr = rec["layers"].get(i, {})
-                if "bwd" in lr and "d2h_end" in lr:
-                    start, end = max(gms(lr["bwd"][1]), prev), gms(lr["d2h_end"])
+                landed = self._landed_at(rec, i)
+                if "bwd" in lr and ("d2h_end" in lr or landed is not None):
+                    end = gms(lr["d2h_end"]) if landed is None else (landed - origin) * 1e3
+                    start = max(gms(lr["bwd"][1]), prev)
                     prev = end
                     d2h.append(("#", f"step{rec['step']} layer{i} grads", start, end))
             for j in rec["jobs"] + rec["other_jobs"]:
@@ -1342,6 +1369,14 @@ class SlideEngine:
                 gaps.append(a["ev_end"].elapsed_time(f0[0]))
         return float(np.median(gaps)) if gaps else None
 
+    def _landed_at(self, rec, i):
+        """Host time at which layer i's gradient copies of this step had all landed, from the
+        copy threads' clocks (copy_engine "hsa"); None where GPU events time the copies."""
+        if self.copy_engine != "hsa":
+            return None
+        ts = [j.t_landed for j in rec["jobs"] if j.name == f"layer{i}"]
+        return max(ts) if ts and all(t is not None for t in ts) else None
+
     def analyse(self, recs):
         """Timeline of recorded steps (timeline=True): per-layer backward, gradient D2H and CPU
         update times; the pages' per-layer overlap predicate T_bwd >= T_d2h + T_update (figure 4
@@ -1372,7 +1407,8 @@ class SlideEngine:
             for i in range(L - 1, -1, -1):
                 lr = rec["layers"][i]
                 bs, be = to_host(lr["bwd"][0]), to_host(lr["bwd"][1])
-                d_end = to_host(lr["d2h_end"])
+                landed = self._landed_at(rec, i)
+                d_end = to_host(lr["d2h_end"]) if landed is None else landed
                 d_start = max(be, prev_end)   # the copy starts after its backward and the
                 prev_end = d_end              # previous copy on the D2H stream
                 parts = jobs[f"layer{i}"]

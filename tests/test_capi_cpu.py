@@ -416,9 +416,15 @@ def test_ring_sliding_schedule_moves_the_right_bytes():
         ring.release(s)
         if i - 3 >= 0:
             loaded[i - 3] = ring.load(i - 3, host_w[i - 3])
+    import time
     for i, t in tickets:
         ring.wait_flush(t, 5000)
         assert np.all(host_g[i] == 100 + i)
+        # the copy thread's completion time is on time.perf_counter's clock
+        assert 0 < ring.ticket_time(t) <= time.perf_counter()
+    with pytest.raises(sl.SlideError) as e:
+        ring.ticket_time(tickets[-1][1] + 1)
+    assert e.value.code == _capi.SLIDE_E_ARG
     ring.close()
 
 

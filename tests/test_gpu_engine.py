@@ -163,6 +163,40 @@ def test_offload_and_overlap_do_not_change_results():
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
+def test_hsa_copy_engine_changes_no_bit_and_times_the_copies():
+    """The slot ring's copies on chosen copy engines through the HSA runtime (copy_engine="hsa",
+    the default) move the same bytes in the same order as hipMemcpyAsync ("hip"): the same losses and fp32 masters to
+    the bit, overlapped and serialized; the timeline's gradient copies are timed from the copy
+    threads' clocks."""
+    print("copy engine: hsa vs hip", flush=True)
+    la, pa = _run(3, False, steps=3, copy_engine="hip")
+    lb, pb = _run(3, False, steps=3, copy_engine="hsa")
+    lc, pc = _run(1, True, steps=2, copy_engine="hip")
+    ld, pd = _run(1, True, steps=2, copy_engine="hsa")
+    assert la == lb and lc == ld and la[:2] == lc
+    for ref, other in ((pa, pb), (pc, pd)):
+        for k in ("embed", "w_final", "lm_head"):
+            assert np.array_equal(ref[k].view(np.uint32), other[k].view(np.uint32)), k
+        for x, y in zip(ref["layers"], other["layers"]):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    params = model_params(SMALL, seed=0, gain_std=0.1)
+    eng = SlideEngine(_spec(SMALL), SMALL.batch, SMALL.seq, n_slots=3, hp=HP, adam_threads=3,
+                      ce_chunk=256, timeline=True, copy_engine="hsa")
+    try:
+        eng.load_params(params["embed"].f32, _flat_layers(params, SMALL), params["w_final"].f32,
+                        params["lm_head"].f32)
+        for s in range(2):
+            eng.step(tokens(SMALL.batch, SMALL.seq, SMALL.vocab, seed=10 + s))
+        eng.wait_updates()
+        ana = eng.analyse(list(eng.records)[-1:])
+        assert all(r["t_d2h_ms"] >= 0 for r in ana["layers"])
+        assert sum(r["t_d2h_ms"] for r in ana["layers"]) > 0
+        tl = eng.timeline_of(list(eng.records)[-1:])
+        assert len(tl["d2h"]) == SMALL.n_layers
+    finally:
+        eng.close()
+
+
 def test_bf16_model_loss_matches_oracle():
     w = SMALL
     print(f"engine step {w.name}", flush=True)
