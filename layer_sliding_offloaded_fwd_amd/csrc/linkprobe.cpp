@@ -97,6 +97,9 @@ extern "C" int slide_host_link_engine_rates(void* dev, void* host, size_t nbytes
       }
     }
   }
+  // a copy that did not finish in time may still write its signal: leave that signal (and the
+  // runtime reference) alive rather than free them under it
+  if (rc == SLIDE_E_TIMEOUT) return rc;
   if (sig.handle) hsa_signal_destroy(sig);
   hsa_shut_down();
   return rc;
