@@ -50,8 +50,10 @@ namespace {
 constexpr int kTicketPool = 1024;
 // Copy engines of the HSA engine: two of the host-optimised ones (engines 0-3 run the host link
 // at ~57 GB/s in both directions on this GPU, the others at 7-13 GB/s device to host), one per
-// direction so that uploads and gradient copies run side by side.
-constexpr int kHsaEngineH2D = 1, kHsaEngineD2H = 0;
+// direction so that uploads and gradient copies run side by side, and neither of them engine 0,
+// which also carries the runtime's own copies (with gradient copies on engine 0 the batch-32
+// step's copies took 357 ms per step against 284-300 ms on engines 1, 2 or 3).
+constexpr int kHsaEngineH2D = 3, kHsaEngineD2H = 1;
 
 // ------------------------------------------------------------------ host engine pieces
 struct HostEvent {
