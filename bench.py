@@ -154,6 +154,9 @@ def _parse():
                     help="sequences of 1024 tokens per step of the llama3-8b-shaped workload "
                          "(default 8); at the critical batch the CPU updates hide behind the "
                          "backward")
+    ap.add_argument("--slots", type=int, default=0,
+                    help="HBM slots of the layer ring for the llama3-8b-shaped workload (default "
+                         "3; with one slot per layer the backward re-uploads no layer)")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers of the 123b slice (default 12, fewer if host RAM is short)")
     ap.add_argument("--copy-engine", default="hsa", choices=["hip", "hsa"],
@@ -1114,6 +1117,8 @@ def main():
         print(json.dumps(result))
         return
     w = dataclasses.replace(L8B, batch=args.batch) if args.batch else L8B
+    if args.slots:
+        w = dataclasses.replace(w, ring_slots=args.slots)
     result = run_step(w, args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
