@@ -164,6 +164,9 @@ struct HsaCopyQueue {
   std::condition_variable cv;
   std::deque<Job> q;
   bool stop = false;
+  // A copy that ran out of time may still be in flight and would signal sig later: no further
+  // copy is issued on this queue (every later job fails), and sig is never destroyed under it.
+  bool broken = false;
   std::thread th;
 
   HsaCopyQueue(hsa_agent_t g, uint32_t eng) : gpu(g), engine(eng) {
@@ -177,7 +180,7 @@ struct HsaCopyQueue {
     }
     cv.notify_all();
     th.join();
-    if (sig.handle) hsa_signal_destroy(sig);
+    if (sig.handle && !broken) hsa_signal_destroy(sig);
   }
   void push(Job j) {
     {
@@ -226,12 +229,15 @@ struct HsaCopyQueue {
         j = std::move(q.front());
         q.pop_front();
       }
-      int rc = 0;
+      int rc = broken ? 1 : 0;
       if (j.gpu_wait) {
-        rc = wait_gpu(j.gpu_wait);
+        if (rc == 0) rc = wait_gpu(j.gpu_wait);
         if (j.own_gpu_wait) hipEventDestroy(j.gpu_wait);
       }
-      if (rc == 0) rc = copy(j);
+      if (rc == 0) {
+        rc = copy(j);
+        if (rc == 2) broken = true;
+      }
       j.done->t_done = mono_now();
       j.done->st.store(rc == 0 ? 1 : 2);
     }
